@@ -1,0 +1,285 @@
+"""Pins of each oracle step against closed forms, special cases, invariants
+and brute force on tiny inputs.  Each test is chosen so that a plausible
+slip in the oracle (a dropped term, a wrong sign or index, a transposed
+operand, a wrong tie rule) fails it."""
+import json
+import math
+import os
+import itertools
+
+import numpy as np
+import pytest
+import scipy.special
+
+from oracle import csa2_ref as R
+from oracle import formats as F
+
+GOLD = os.path.join(os.path.dirname(__file__), "golden")
+
+
+# ------------------------------------------------------------------ a1
+def test_compress_m1_identity():
+    rng = np.random.default_rng(1)
+    h = rng.standard_normal((6, 512))
+    assert np.array_equal(R.compress(h, None, 1), h)
+
+
+def test_compress_special_cases():
+    rng = np.random.default_rng(2)
+    h = rng.standard_normal((8, 512))
+    # constant logits -> plain mean of each pair
+    z = np.full((8, 512), 0.7)
+    assert np.allclose(R.compress(h, z, 2), h.reshape(4, 2, 512).mean(1), rtol=0, atol=1e-15)
+    # a dominant logit picks its row
+    z = np.zeros((8, 512))
+    z[1::2] = 800.0
+    assert np.allclose(R.compress(h, z, 2), h[1::2], rtol=0, atol=0)
+    # per-channel weights: channel c uses its own logit column
+    z = rng.standard_normal((8, 512)) * 3
+    x = R.compress(h, z, 4)
+    w = scipy.special.softmax(z.reshape(2, 4, 512), axis=1)
+    assert np.allclose(x, (w * h.reshape(2, 4, 512)).sum(1), rtol=1e-14, atol=1e-14)
+    # convex combination: inside the per-channel range of its rows
+    hh = h.reshape(2, 4, 512)
+    assert np.all(x <= hh.max(1) + 1e-12) and np.all(x >= hh.min(1) - 1e-12)
+
+
+def test_compress_v4_worked_example():
+    g = json.load(open(os.path.join(GOLD, "v4_pooling_example.json")))
+    v = np.array(g["vectors"])                       # 4 tokens, 2 channels
+    w = np.array(g["printed_weights"])
+    z = np.repeat(np.log(w)[:, None], 2, axis=1)     # softmax(log w) = w (sum w = 1)
+    x = R.compress(v, z, 4)
+    assert np.allclose(x[0], g["printed_entry"], atol=1e-12)
+    # the printed weights are not the softmax of the printed logits
+    true = scipy.special.softmax(np.array(g["printed_logits"]))
+    assert not np.allclose(true, w, atol=0.01)
+
+
+# ------------------------------------------------------------------ a2
+def test_main_kv_quant_exact_when_representable():
+    rng = np.random.default_rng(3)
+    n = 64
+    sc = rng.integers(0x08, 0x7F, size=(n, 32))               # normal E4M3 scales
+    codes = rng.integers(0, 16, size=(n, 512)).astype(np.uint8)
+    codes[:, ::16] = 0x7                                        # group max = 6 * s
+    x = (F.e2m1_value(codes).reshape(n, 32, 16) * F.e4m3fn_value(sc)[:, :, None]).reshape(n, 512)
+    c, s = R.quant_main_kv(x)
+    assert np.array_equal(s, sc)
+    assert np.array_equal(R.dequant_main_kv(c, s), x)
+    # the largest magnitude the format holds (report section 2.4.4)
+    x = np.zeros((1, 512))
+    x[0, 5] = -2688.0
+    c, s = R.quant_main_kv(x)
+    assert R.dequant_main_kv(c, s)[0, 5] == -2688.0
+
+
+def test_main_kv_quant_brute_force():
+    rng = np.random.default_rng(4)
+    x = rng.standard_normal((8, 512)) * np.exp(rng.uniform(-6, 6, (8, 1)))
+    c, s = R.quant_main_kv(x)
+    allsc = F.e4m3fn_value(np.arange(0x7F))
+    e2 = F.e2m1_value(np.arange(16))
+    for j in range(8):
+        for g in range(32):
+            grp = x[j, 16 * g:16 * g + 16]
+            a = np.abs(grp).max() / 6
+            # scale: nearest E4M3 value to max/6 (tie -> even code)
+            d = np.abs(allsc - a)
+            best = np.flatnonzero(d == d.min())
+            want = best[0] if len(best) == 1 else [b for b in best if b % 2 == 0][0]
+            assert s[j, g] == want
+            sv = allsc[want]
+            nib = F.unpack_nibbles(c[j])[16 * g:16 * g + 16]
+            for ch in range(16):
+                r = grp[ch] / sv
+                dd = np.abs(np.clip(r, -6, 6) - e2)
+                assert dd[nib[ch]] == dd.min()
+                assert (nib[ch] >= 8) == (grp[ch] < 0)
+
+
+def test_main_kv_quant_zero_group():
+    x = np.zeros((2, 512))
+    x[1, :16] = 1e-6                       # max/6 rounds to E4M3 zero
+    c, s = R.quant_main_kv(x)
+    assert np.all(c == 0) and np.all(s == 0)
+
+
+# ------------------------------------------------------------------ a3
+def test_projection_orientation():
+    rng = np.random.default_rng(5)
+    xhat = rng.standard_normal((3, 512))
+    w = rng.standard_normal((128, 512))
+    k = R.project_indexer_k(xhat, w)
+    assert k.shape == (3, 128)
+    # output dim d reads row d of w
+    assert np.isclose(k[2, 7], sum(w[7, c] * xhat[2, c] for c in range(512)), rtol=1e-12)
+
+
+def test_mxfp4_special_cases():
+    k = np.zeros((4, 128))
+    k[0, :32] = 3.0          # floor(log2 3) = 1 -> X = 2^-1, 3 / X = 6: exact
+    k[0, 32:64] = -1.0       # X = 2^-2, -4: exact
+    k[1, :32] = 8.0          # power of two: X = 2, 4: exact
+    k[1, 32:64] = 7.99       # X = 1, 7.99 clips to 6
+    k[2, :] = np.arange(128) / 16.0
+    c, s = R.quant_mxfp4(k)
+    d = R.dequant_mxfp4(c, s)
+    assert np.all(d[0, :32] == 3.0) and np.all(d[0, 32:64] == -1.0)
+    assert s[0, 0] == 126 and s[0, 1] == 125
+    assert np.all(d[1, :32] == 8.0) and s[1, 0] == 128
+    assert np.all(d[1, 32:64] == 6.0)
+    assert s[3, 0] == 0 and np.all(c[3] == 0)                 # all-zero block
+    # every element is a nearest representable value of k / X
+    for g in range(4):
+        X = F.e8m0_value(s[2, g])
+        blk = k[2, 32 * g:32 * g + 32]
+        assert X == 2.0 ** (math.floor(math.log2(np.abs(blk).max())) - 2)
+        e2 = F.e2m1_value(np.arange(16))
+        for ch, nib in enumerate(F.unpack_nibbles(c[2])[32 * g:32 * g + 32]):
+            dd = np.abs(np.clip(blk[ch] / X, -6, 6) - e2)
+            assert dd[nib] == dd.min()
+
+
+# ------------------------------------------------------------------ a4
+def _score_loops(q, w, k):
+    out = []
+    for j in range(k.shape[0]):
+        tot = 0.0
+        for h in range(q.shape[0]):
+            dot = 0.0
+            for c in range(q.shape[1]):
+                dot += q[h, c] * k[j, c]
+            tot += w[h] * (dot if dot > 0 else 0.0)
+        out.append(tot)
+    return np.array(out)
+
+
+def test_scores_brute_force_tiny():
+    rng = np.random.default_rng(6)
+    q = rng.standard_normal((32, 128))
+    w = rng.uniform(0, 1, 32)
+    k = rng.standard_normal((5, 128))
+    assert np.allclose(R.index_scores(q, w, k), _score_loops(q, w, k), rtol=1e-12)
+
+
+def test_scores_identities():
+    rng = np.random.default_rng(7)
+    q = rng.standard_normal((32, 128))
+    w = rng.uniform(0, 1, 32)
+    k = rng.standard_normal((40, 128))
+    s = R.index_scores(q, w, k)
+    assert np.all(s >= 0)
+    # relu(x) - relu(-x) = x: the difference is the plain weighted dot
+    lin = (k @ q.T) @ w
+    assert np.allclose(s - R.index_scores(-q, w, k), lin, rtol=1e-10, atol=1e-10)
+    # one head with unit weight is relu(q_h . k)
+    e = np.zeros(32); e[9] = 1.0
+    assert np.allclose(R.index_scores(q, e, k), np.maximum(k @ q[9], 0), rtol=1e-13)
+    # positive homogeneity in q and linearity in w
+    assert np.allclose(R.index_scores(2.5 * q, w, k), 2.5 * s, rtol=1e-13)
+    assert np.allclose(R.index_scores(q, 3 * w, k), 3 * s, rtol=1e-13)
+
+
+# ------------------------------------------------------------------ a5
+def test_topk_textbook_sort_with_ties():
+    rng = np.random.default_rng(8)
+    s = rng.integers(0, 6, 60).astype(float)          # many exact ties
+    for k in (1, 5, 17, 60, 100):
+        want = sorted(sorted(range(60), key=lambda j: (-s[j], j))[:k])
+        assert list(R.topk(s, k)) == want
+    # duplicates: the lowest index wins
+    s = np.array([1.0, 3.0, 3.0, 3.0, 2.0])
+    assert list(R.topk(s, 2)) == [1, 2]
+    # explicit ids (a candidate pool)
+    ids = np.array([10, 20, 30, 40, 50])
+    assert list(R.topk(s, 2, ids)) == [20, 30]
+
+
+def test_topk_subset_enumeration():
+    # brute force: the selected set has the largest score sum among all
+    # k-subsets, and the lowest index sum among those
+    rng = np.random.default_rng(9)
+    s = rng.integers(0, 4, 9).astype(float)
+    k = 4
+    best = max(itertools.combinations(range(9), k), key=lambda c: (sum(s[list(c)]), -sum(c)))
+    assert list(R.topk(s, k)) == sorted(best)
+
+
+# ------------------------------------------------------------------ a6
+def test_block_pool_tiny_brute_force():
+    s = np.array([0, 9, 1, 1, 5, 5, 5, 5, 2, 9, 0, 0, 7], dtype=float)
+    # blocks of 4: maxima [9, 5, 9, 7] -> top 2 by (max desc, id asc) = blocks 0, 2
+    assert list(R.block_pool(s, block=4, n_blocks=2)) == [0, 1, 2, 3, 8, 9, 10, 11]
+    # top 3 adds block 3, which is partial (only position 12 visible)
+    assert list(R.block_pool(s, block=4, n_blocks=3)) == [0, 1, 2, 3, 8, 9, 10, 11, 12]
+    assert list(R.block_pool(s, block=4, n_blocks=10)) == list(range(13))
+
+
+def test_block_pool_invariants():
+    rng = np.random.default_rng(10)
+    n = 40000
+    s = rng.standard_normal(n) ** 2
+    s[1000:1040] = s.max()                      # a run of exact ties
+    pool = R.block_pool(s, 8, 2048)
+    assert pool.size == 16384
+    assert np.all(np.diff(pool) > 0)
+    assert set(R.topk(s, 512)) <= set(pool)
+    bm = R.block_max(s, 8)
+    inpool = np.zeros(bm.size, bool); inpool[pool // 8] = True
+    assert bm[inpool].min() >= bm[~inpool].max()
+    # Reindex with the Full layer's own scores reproduces the Full top-512
+    assert np.array_equal(R.topk(s[pool], 512, pool), R.topk(s, 512))
+
+
+# ------------------------------------------------------------------ a9
+def test_attend_special_cases():
+    rng = np.random.default_rng(11)
+    q = rng.standard_normal((64, 512)) / math.sqrt(512)
+    v = rng.standard_normal((1, 512))
+    o, lse = R.attend(q, v)
+    assert np.allclose(o, np.repeat(v, 64, 0), rtol=0, atol=1e-15)
+    assert np.allclose(lse, q @ v[0], rtol=1e-14)
+    v = rng.standard_normal((30, 512))
+    o, lse = R.attend(np.zeros((64, 512)), v)
+    assert np.allclose(o, np.repeat(v.mean(0, keepdims=True), 64, 0), atol=1e-14)
+    assert np.allclose(lse, math.log(30))
+
+
+def test_attend_library_softmax_and_permutation():
+    rng = np.random.default_rng(12)
+    q = rng.standard_normal((64, 512)) / math.sqrt(512)
+    v = rng.standard_normal((50, 512))
+    o, lse = R.attend(q, v)
+    p = scipy.special.softmax(q @ v.T, axis=1)
+    assert np.allclose(o, p @ v, rtol=1e-12, atol=1e-13)
+    assert np.allclose(lse, scipy.special.logsumexp(q @ v.T, axis=1), rtol=1e-13)
+    perm = rng.permutation(50)
+    o2, lse2 = R.attend(q, v[perm])
+    assert np.allclose(o, o2, rtol=1e-12, atol=1e-14) and np.allclose(lse, lse2, rtol=1e-13)
+
+
+def test_attend_split_merge():
+    rng = np.random.default_rng(13)
+    q = rng.standard_normal((64, 512)) / math.sqrt(512)
+    v = rng.standard_normal((100, 512)) * 3
+    o, lse = R.attend(q, v)
+    parts = [R.attend(q, v[a:b]) for a, b in ((0, 37), (37, 64), (64, 100))]
+    L = np.stack([p[1] for p in parts])
+    m = L.max(0)
+    wts = np.exp(L - m)
+    merged = sum(wts[i][:, None] * parts[i][0] for i in range(3)) / wts.sum(0)[:, None]
+    assert np.allclose(merged, o, rtol=1e-12, atol=1e-13)
+    assert np.allclose(m + np.log(wts.sum(0)), lse, rtol=1e-13)
+
+
+def test_gather_rows_skips_padding_and_appends_swa():
+    rng = np.random.default_rng(14)
+    x = rng.standard_normal((10, 512))
+    c, s = R.quant_main_kv(x)
+    swa_c = rng.integers(0, 0x7E, (3, 512)).astype(np.uint8)
+    swa_s = np.array([0.5, 2.0, 0.25])
+    rows = R.gather_rows(c, s, np.array([4, -1, 2]), swa_c, swa_s)
+    assert rows.shape == (5, 512)
+    assert np.array_equal(rows[0], R.dequant_main_kv(c[4], s[4]))
+    assert np.array_equal(rows[3], F.e4m3fn_value(swa_c[1]) * 2.0)
