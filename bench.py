@@ -1,0 +1,173 @@
+"""Benchmark of one decode step of the CSA2 global branch on one MI355X.
+
+Default workload: hierarchical decoder decode at 1M context (batch 4,
+N = 2^20 FP4 entries per sequence): the Full layer scans all entries,
+builds the 2048 x 8 block pool and its top-512 and attends; 4 Reindex
+layers rescore the pool with their own queries, take their top-512 and
+attend.  A step is that whole 5-layer pass; tokens/s = batch / step time.
+Inputs are seeded synthetic tensors already resident in HBM.
+
+Prints one JSON line with the metric, a roofline entry for the dominant
+kernel (the Full layer's index scan, timed with HIP events on its stream
+inside the timed region) and the fp64 oracle's speed on a bounded sample
+of the same workload on the host cores.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+from long_context_sparse_csa2_amd import synth  # noqa: E402
+from long_context_sparse_csa2_amd.pipeline import Step  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, AMD datasheet
+SCAN_BYTES_PER_ENTRY = 68      # MXFP4 indexer K: 64 B codes + 4 B E8M0 scales
+METRIC = "decode tokens/s at 1M ctx (indexer+top-512+FP4 sparse attn); % of roofline"
+
+
+def step_bytes(wl):
+    """Algorithmic HBM bytes of one step: indexer K of every scanned entry,
+    288 B per gathered main-KV row, 516 B per SWA row, queries and outputs."""
+    Q = wl.Q
+    n_attend = len(wl.layers)
+    b = Q * wl.N * SCAN_BYTES_PER_ENTRY
+    b += sum(Q * wl.n_blocks * wl.block * SCAN_BYTES_PER_ENTRY for m in wl.layers if m == "reindex")
+    b += n_attend * Q * (wl.k * 288 + wl.swa * 516 + 64 * 512 * 2 + 64 * 512 * 4)
+    return b
+
+
+def cpu_baseline(wl, step, seconds_target=15.0):
+    """The fp64 oracle, as it stands, on one sequence of the workload: the
+    whole step (Full scan, pool, top-512, attention, every Reindex layer).
+    Returns tokens/s for that one-sequence sample."""
+    from threadpoolctl import threadpool_info
+    from oracle import csa2_ref as R
+
+    b = 0
+    kv_c = step.cache.kv_codes[b].cpu().numpy()
+    kv_s = step.cache.kv_scales[b].cpu().numpy()
+    ik_c = step.cache.ik_codes[b].cpu().numpy()
+    ik_s = step.cache.ik_scales[b].cpu().numpy()
+    layers = []
+    for li in range(len(wl.layers)):
+        L = step.layers[li]
+        layers.append(dict(q_idx=L["q_idx"][b].float().cpu().numpy().astype(np.float64),
+                           w=L["w"][b].cpu().numpy().astype(np.float64),
+                           q_attn=L["q_attn"][b].float().cpu().numpy().astype(np.float64),
+                           swa_c=L["swa_codes"][b].cpu().numpy(),
+                           swa_s=L["swa_scale"][b].cpu().numpy().astype(np.float64)))
+    runs, t_total = 0, 0.0
+    while t_total < seconds_target and runs < 5:
+        t0 = time.perf_counter()
+        khat = R.dequant_mxfp4(ik_c, ik_s)
+        pool = None
+        for li, mode in enumerate(wl.layers):
+            L = layers[li]
+            if mode == "full":
+                s = R.index_scores(L["q_idx"], L["w"], khat)
+                if wl.hierarchical:
+                    pool = R.block_pool(s, wl.block, wl.n_blocks)
+                idx = R.topk(s, wl.k)
+            elif mode == "reindex":
+                s = R.index_scores(L["q_idx"], L["w"], khat[pool])
+                idx = R.topk(s, wl.k, pool)
+            rows = R.gather_rows(kv_c, kv_s, idx, L["swa_c"], L["swa_s"])
+            R.attend(L["q_attn"], rows)
+        t_total += time.perf_counter() - t0
+        runs += 1
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    return {"value": runs / t_total, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"one of {wl.B} sequences, whole {len(wl.layers)}-layer step, "
+                      f"{runs} run(s) in {t_total:.1f} s; numpy fp64 (BLAS matmul on "
+                      f"{threads} threads, elementwise steps on 1)"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default="c2", choices=sorted(synth.WORKLOADS))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
+              "the path would shard by sequence across GPUs, which is not built here",
+              file=sys.stderr)
+        sys.exit(2)
+
+    dev = torch.device("cuda:0")
+    wl = synth.WORKLOADS[args.config]
+    print(f"[bench] building {wl.name} ({wl.note}) cache on {dev}", file=sys.stderr, flush=True)
+    step = Step(wl, dev)
+    torch.cuda.synchronize()
+    print("[bench] warmup", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        step.run()
+    torch.cuda.synchronize()
+
+    events = {}
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record()
+    for _ in range(args.steps):
+        step.run(events=events)
+    t1.record()
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / args.steps
+    per_call = {k: float(np.mean([a.elapsed_time(b) for a, b in v])) * 1e3 for k, v in events.items()}
+    calls = {k: len(v) // args.steps for k, v in events.items()}
+    print(f"[bench] {ms:.3f} ms/step; per call (us): "
+          + ", ".join(f"{k}={v:.1f}x{calls[k]}" for k, v in per_call.items()), file=sys.stderr,
+          flush=True)
+
+    scan_us = per_call["index_score_full"]
+    scan_bytes = wl.Q * wl.N * SCAN_BYTES_PER_ENTRY
+    achieved = scan_bytes / (scan_us * 1e-6) / 1e9
+    traffic = None
+    tfile = os.path.join(ROOT, "profiles", f"traffic_index_score_{wl.name}.json")
+    if os.path.exists(tfile):
+        traffic = json.load(open(tfile)).get("bytes_per_launch")
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                "kernel": "k_index_score (Full-layer scan)",
+                "bytes_per_launch": scan_bytes, "avg_launch_us": round(scan_us, 2)}
+    step_b = step_bytes(wl)
+    out = {
+        "metric": METRIC,
+        "value": round(wl.B / (ms * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{wl.name}: {wl.note}", "batch": wl.B, "entries": wl.N,
+                   "raw_tokens": wl.T, "m": wl.m, "layers": wl.layers, "top_k": wl.k,
+                   "pool_blocks": wl.n_blocks if wl.hierarchical else 0, "swa": wl.swa},
+        "roofline": roofline,
+        "step_roofline": {"bytes": step_b, "us_at_peak": round(step_b / (HBM_PEAK_GBS * 1e3), 2),
+                          "frac": round(step_b / (HBM_PEAK_GBS * 1e9) / (ms * 1e-3), 4)},
+        "per_call_us": {k: round(v, 2) for k, v in per_call.items()},
+        "calls_per_step": calls,
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline(wl, step)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,247 @@
+/*
+ * csa2.h -- C ABI of libcsa2: the global-attention hot path of Compressed
+ * Sparse Attention 2 (CSA2) for AMD Instinct MI355X (gfx950).
+ *
+ * The operation is the one described in "DeepSeek-V4.1-Flash: Pushing the
+ * Limits of KV Cache Compression" (report digest), section 2.3 (CSA2),
+ * 2.3.1 (Full / Reindex / Reuse modes), 2.3.2 (Hierarchical Sparse Indexer,
+ * Fig. 5) and 2.4.4 (FP4 main KV cache), with the sizes of the mer.dev
+ * commentary on that report (section 1 setup: 512-d latent, 64 query heads of
+ * dim 512, a 32 x 128 indexer, top-k 512, 2048 blocks of 8 positions, SWA
+ * window 128; section 2: 356 bytes per entry).
+ *
+ * Conventions for every entry point
+ *   - All array arguments are DEVICE pointers unless marked (host).  The
+ *     caller owns every buffer; the library never allocates or frees device
+ *     memory and keeps no state except a thread-local error string.
+ *   - Every call enqueues its kernels on `stream` (a hipStream_t, may be 0
+ *     for the null stream) and returns without synchronising.
+ *   - bf16 values are passed as uint16_t bit patterns.
+ *   - Arguments are validated on the host before anything is launched.  A
+ *     bad argument returns CSA2_EINVAL (or CSA2_EUNSUPPORTED for a size the
+ *     library does not implement, CSA2_EWORKSPACE for a short workspace)
+ *     and sets csa2_last_error().  Launch failures return CSA2_EHIP.
+ *   - The contents of device arrays (indices, cache bytes) are not checked;
+ *     out-of-range indices are undefined behaviour.
+ *   - No exception or abort crosses the ABI.  Calls are thread-safe.
+ *
+ * Cache layout (one KV-producing layer, B sequences, `cap` entries each,
+ * structure of arrays, entry (b, j) at flat index b * cap + j):
+ *   kv_codes  [B][cap][256] u8  E2M1 main-KV codes, channel 2c in the low nibble
+ *   kv_scales [B][cap][32]  u8  E4M3FN scale of channels 16g..16g+15
+ *   ik_codes  [B][cap][64]  u8  E2M1 indexer-K codes, dim 2c in the low nibble
+ *   ik_scales [B][cap][4]   u8  E8M0 scale of dims 32g..32g+31
+ * = 288 B main KV + 68 B indexer K = 356 B per entry (commentary, section 2).
+ * The bytes are the cache's whole state: saving and restoring it is a copy.
+ */
+#ifndef CSA2_H
+#define CSA2_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  CSA2_OK = 0,
+  CSA2_EINVAL = 1,        /* bad argument (null pointer, size, alignment)  */
+  CSA2_EUNSUPPORTED = 2,  /* a size or mode outside what the library does  */
+  CSA2_EWORKSPACE = 3,    /* workspace smaller than csa2_workspace_bytes()  */
+  CSA2_EHIP = 4           /* the HIP runtime reported an error              */
+} csa2_status;
+
+/* Fixed sizes of the path (commentary, section 1 setup). */
+#define CSA2_D_LATENT 512   /* main-KV latent channels                        */
+#define CSA2_H_INDEX 32     /* indexer heads                                  */
+#define CSA2_D_INDEX 128    /* indexer head dim                               */
+#define CSA2_H_ATTN 64      /* attention query heads (head dim = CSA2_D_LATENT) */
+#define CSA2_MAX_K 2048     /* largest top-k / block count accepted           */
+#define CSA2_MAX_SWA 128    /* largest SWA window per query                   */
+#define CSA2_MAX_COLS (1 << 24) /* largest score row the selectors accept     */
+
+/* Workspace query selectors. */
+#define CSA2_OP_TOPK 1
+#define CSA2_OP_POOL 2
+#define CSA2_OP_ATTEND 3
+
+/* One KV-producing layer's cache for B sequences (host struct holding device
+ * pointers).  Every pointer must be 16-byte aligned. */
+typedef struct {
+  uint8_t* kv_codes;
+  uint8_t* kv_scales;
+  uint8_t* ik_codes;
+  uint8_t* ik_scales;
+  int64_t cap;            /* entries per sequence (the batch stride) */
+} csa2_cache;
+
+/* Name of a status code (static string). */
+const char* csa2_status_string(int status);
+
+/* Detail of the last failed call on this thread ("" if none). */
+const char* csa2_last_error(void);
+
+/*
+ * (1) Compress, quantise and project: steps a1-a3 of the path.
+ *
+ * Report section 2.3: CSA2 compresses every m raw entries into one with no
+ * overlap between the sources of adjacent entries and no absolute position
+ * embedding, and obtains the indexer K by projecting the main-KV entry;
+ * section 2.4.4: the main KV is stored as E2M1 with one E4M3 scale per 16
+ * channels (no second-level scale), the indexer K as OCP MXFP4.
+ *
+ * For each sequence b and entry j in [0, T/m):
+ *   x[c]  = sum_t softmax_t(z[b][jm+t][c]) * h[b][jm+t][c]     (t < m)
+ *           (x = h when m == 1; the softmax form follows the commentary,
+ *            section 4.1)
+ *   s_g   = E4M3FN(RNE, saturating)(max_{c in g} |x[c]| / 6), 16-channel g
+ *   code  = E2M1(RNE, saturating)(x[c] / s_g), all +0 when s_g == 0
+ *   k[d]  = sum_c w_ik[d][c] * xhat[c]     (xhat = the dequantised main KV)
+ *   MXFP4: X = 2^(floor(log2 max|k_g|) - 2) as E8M0 per 32 dims, E2M1(k / X)
+ * and writes entry e0 + j of sequence b of `dst`.
+ *
+ *   h      [B][T][512] bf16  raw latents
+ *   z      [B][T][512] bf16  compression logits; may be NULL iff m == 1
+ *   B, T   sequences and raw tokens per sequence; T % m == 0
+ *   m      compression ratio, 1 <= m <= 16
+ *   w_ik   [128][512] bf16   indexer-K projection (output dim x input channel)
+ *   dst    cache written at entries [e0, e0 + T/m); requires e0 + T/m <= cap
+ */
+csa2_status csa2_compress_quant(const uint16_t* h, const uint16_t* z, int B, int64_t T, int m,
+                                const uint16_t* w_ik, const csa2_cache* dst, int64_t e0,
+                                void* stream);
+
+/*
+ * (2) Lightning-indexer scores: step a4 (full scan) and a7 (Reindex scoring
+ * of a candidate pool).
+ *
+ * Report section 2.3 (indexer Q and K score the main-KV entries), section
+ * 2.3.2 (the first Full layer scores every causally visible entry; Reindex
+ * layers score only the pool); score form of the commentary, section 4.1:
+ *   score(q, j) = sum_{h<32} w[q][h] * max(0, sum_{c<128} q_idx[q][h][c] * khat_j[c])
+ * with khat the dequantised MXFP4 indexer K.  Accumulation is fp32.
+ *
+ *   q_idx  [Q][32][128] bf16   indexer queries
+ *   w      [Q][32] fp32        per-head weights
+ *   q_seq  [Q] int32           sequence (cache row block) of each query
+ *   n_vis  [Q] int64           columns to score for each query (<= n_cols)
+ *   cand   NULL: column c scores entry c (c < n_vis[q]).
+ *          else [Q][ld_cand] int32 entry ids: column c scores entry
+ *          cand[q][c] (c < n_vis[q]); entries must be in [0, cap).
+ *   ld_cand  row stride of cand (ignored when cand is NULL)
+ *   Q      queries
+ *   n_cols (host) upper bound of n_vis[q], sets the launch size
+ *   src    the cache
+ *   scores [Q][ld] fp32; columns >= n_vis[q] are not written
+ */
+csa2_status csa2_index_score(const uint16_t* q_idx, const float* w, const int32_t* q_seq,
+                             const int64_t* n_vis, const int32_t* cand, int64_t ld_cand, int Q,
+                             int64_t n_cols, const csa2_cache* src, float* scores, int64_t ld,
+                             void* stream);
+
+/*
+ * (3a) Per-query top-k: step a5 (and the selection half of a7).
+ *
+ * Selects, for each query, the min(k, n_valid[q]) columns with the largest
+ * score, ties broken towards the lower column (report section 2.3 and Fig. 5:
+ * top-512 per query; the tie rule is this library's reading).  Scores are
+ * compared as fp32 values (+0 and -0 equal); NaN is not allowed.
+ *
+ *   scores   [Q][ld] fp32
+ *   n_valid  [Q] int64    columns 0..n_valid[q]-1 are candidates
+ *   col_ids  NULL: the id of column c is c.  Else [Q][ld] int32 entry ids,
+ *            strictly ascending over each query's valid columns (the pool
+ *            that csa2_block_pool writes has this form), so that the lower
+ *            column is also the lower entry id.
+ *   n_cols   (host) upper bound of n_valid[q], <= CSA2_MAX_COLS
+ *   k        1 <= k <= CSA2_MAX_K
+ *   out      [Q][k] int32 selected ids, ascending, padded with -1
+ *   ws       workspace of csa2_workspace_bytes(CSA2_OP_TOPK, Q, n_cols, k) bytes
+ */
+csa2_status csa2_select_topk(const float* scores, int64_t ld, int Q, const int64_t* n_valid,
+                             const int32_t* col_ids, int64_t n_cols, int k, int32_t* out,
+                             void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * (3b) Hierarchical candidate pool: step a6.
+ *
+ * Report section 2.3.2 and Fig. 5: the first Full layer of the decoder gives
+ * every block of positions the maximum index score among them, keeps the
+ * blocks with the highest scores, and collects their positions into a pool
+ * (2048 blocks x 8 positions = 16384 candidates) that later Reindex layers
+ * search.  Here: aligned blocks [8b, 8b+8) of the first n_valid[q] columns,
+ * a partial last block uses its valid columns; blocks ranked by (max desc,
+ * block id asc); the first min(n_blocks, #blocks) are kept.
+ *
+ *   scores, ld, Q, n_valid, n_cols  as for csa2_select_topk (col_ids = identity)
+ *   block     positions per block; must be 8
+ *   n_blocks  1 <= n_blocks <= CSA2_MAX_K
+ *   pool      [Q][n_blocks * block] int32 pooled positions, ascending, -1 padded
+ *   pool_len  [Q] int64 number of valid pool entries
+ *   ws        csa2_workspace_bytes(CSA2_OP_POOL, Q, n_cols, n_blocks) bytes
+ */
+csa2_status csa2_block_pool(const float* scores, int64_t ld, int Q, const int64_t* n_valid,
+                            int64_t n_cols, int block, int n_blocks, int32_t* pool,
+                            int64_t* pool_len, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * (4 + 5) Gather and sparse attention: steps a8 and a9.
+ *
+ * Report section 2.3: each query attends to its selected main-KV entries
+ * together with the layer-local sliding-window KV; the 512-d latent is
+ * shared by all 64 heads and used as both key and value (MLA style);
+ * section 2.4.4: main KV dequantised from FP4 before attention, SWA KV FP8.
+ * For query q and head h, over the rows
+ *   main:  xhat_j for j = idx[q][i] (i < k, idx == -1 skipped),
+ *          from sequence q_seq[q] of `src`
+ *   SWA:   sigma_r * e_r for r in [swa_start[q], swa_start[q] + swa_len[q]),
+ *          row r of sequence q_seq[q] of the SWA arrays
+ *   l = q[q][h] . row,  p = softmax(l),  out[q][h] = sum p * row,
+ *   lse[q][h] = log sum exp(l).
+ * q is used as given (the 1/sqrt(512) softmax scale is folded in by the
+ * caller).  Logits accumulate in fp32 from exact bf16 operands; the
+ * probability-weighted sum uses fp16 probabilities and fp16 values
+ * (exact for FP4 main KV) with fp32 accumulation.
+ *
+ *   q          [Q][64][512] bf16
+ *   q_seq      [Q] int32
+ *   Q          queries
+ *   src        the cache
+ *   idx        [Q][k] int32 selected entries (-1 = none); 0 <= k <= CSA2_MAX_K
+ *   swa_codes  [B][T_swa][512] u8 E4M3FN; may be NULL iff every swa_len is 0
+ *   swa_scale  [B][T_swa] fp32
+ *   T_swa      SWA rows per sequence
+ *   swa_start  [Q] int64, swa_len [Q] int32 (0 <= swa_len <= CSA2_MAX_SWA);
+ *              the window is clipped to [0, T_swa)
+ *   out        [Q][64][512] fp32
+ *   lse        [Q][64] fp32, or NULL.  A query with no rows gets out = 0,
+ *              lse = -inf.
+ *   ws         csa2_workspace_bytes(CSA2_OP_ATTEND, Q, 0, k) bytes
+ */
+csa2_status csa2_sparse_attend(const uint16_t* q, const int32_t* q_seq, int Q, const csa2_cache* src,
+                               const int32_t* idx, int k, const uint8_t* swa_codes,
+                               const float* swa_scale, int64_t T_swa, const int64_t* swa_start,
+                               const int32_t* swa_len, float* out, float* lse, void* ws,
+                               size_t ws_bytes, void* stream);
+
+/* Workspace bytes an operation needs (0 if it needs none).
+ *   op      CSA2_OP_TOPK (n_cols, k), CSA2_OP_POOL (n_cols, k = n_blocks),
+ *           CSA2_OP_ATTEND (k = entries per query)
+ */
+size_t csa2_workspace_bytes(int op, int Q, int64_t n_cols, int k);
+
+/*
+ * Device self-test of the hardware conversion and matrix instructions the
+ * kernels rely on (FP4 -> bf16/fp16 scaled conversion, MFMA operand
+ * layouts), against plain integer/bit code on the same device.  Writes
+ * `n` int32 failure counters to `counts` (device); all zero means pass.
+ * Returns the number of counters it writes when counts is NULL.
+ */
+int csa2_selftest(int32_t* counts, int n, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CSA2_H */

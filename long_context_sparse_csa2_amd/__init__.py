@@ -1,0 +1,222 @@
+"""Python binding of libcsa2, the MI355X (gfx950) CSA2 global-attention path.
+
+Every function here only marshals arguments (torch tensors -> device
+pointers, the current HIP stream) and calls the C ABI of the same name in
+include/csa2.h; all computation runs in the library's HIP kernels.  PyTorch
+supplies device memory and streams.  If libcsa2.so is missing the functions
+raise: there is no CPU fallback.
+"""
+
+import ctypes
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libcsa2.so")
+
+CSA2_OP_TOPK, CSA2_OP_POOL, CSA2_OP_ATTEND = 1, 2, 3
+STATUS = {0: "CSA2_OK", 1: "CSA2_EINVAL", 2: "CSA2_EUNSUPPORTED", 3: "CSA2_EWORKSPACE", 4: "CSA2_EHIP"}
+EXPORTS = ("csa2_status_string", "csa2_last_error", "csa2_compress_quant", "csa2_index_score",
+           "csa2_select_topk", "csa2_block_pool", "csa2_sparse_attend", "csa2_workspace_bytes",
+           "csa2_selftest")
+
+
+class Csa2Error(RuntimeError):
+    def __init__(self, fn, status, detail):
+        super().__init__(f"{fn}: {STATUS.get(status, status)}: {detail}")
+        self.status = status
+
+
+class _Cache(ctypes.Structure):
+    _fields_ = [("kv_codes", ctypes.c_void_p), ("kv_scales", ctypes.c_void_p),
+                ("ik_codes", ctypes.c_void_p), ("ik_scales", ctypes.c_void_p),
+                ("cap", ctypes.c_int64)]
+
+
+_lib = None
+
+
+def lib():
+    """Load libcsa2.so once (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: run __graft_entry__.build() "
+                              "(python -c 'import __graft_entry__ as g; g.build()')")
+        L = ctypes.CDLL(LIB_PATH)
+        P, I, I64, SZ = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_size_t
+        L.csa2_status_string.restype = ctypes.c_char_p
+        L.csa2_status_string.argtypes = [I]
+        L.csa2_last_error.restype = ctypes.c_char_p
+        L.csa2_last_error.argtypes = []
+        L.csa2_compress_quant.restype = I
+        L.csa2_compress_quant.argtypes = [P, P, I, I64, I, P, ctypes.POINTER(_Cache), I64, P]
+        L.csa2_index_score.restype = I
+        L.csa2_index_score.argtypes = [P, P, P, P, P, I64, I, I64, ctypes.POINTER(_Cache), P, I64, P]
+        L.csa2_select_topk.restype = I
+        L.csa2_select_topk.argtypes = [P, I64, I, P, P, I64, I, P, P, SZ, P]
+        L.csa2_block_pool.restype = I
+        L.csa2_block_pool.argtypes = [P, I64, I, P, I64, I, I, P, P, P, SZ, P]
+        L.csa2_sparse_attend.restype = I
+        L.csa2_sparse_attend.argtypes = [P, P, I, ctypes.POINTER(_Cache), P, I, P, P, I64, P, P,
+                                         P, P, P, SZ, P]
+        L.csa2_workspace_bytes.restype = SZ
+        L.csa2_workspace_bytes.argtypes = [I, I, I64, I]
+        L.csa2_selftest.restype = I
+        L.csa2_selftest.argtypes = [P, I, P]
+        _lib = L
+    return _lib
+
+
+# ------------------------------------------------------------ helpers
+def _ptr(t):
+    if t is None:
+        return None
+    if not t.is_contiguous():
+        raise ValueError("tensor arguments must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream, ref):
+    if stream is not None:
+        return ctypes.c_void_p(stream)
+    if ref is not None and ref.is_cuda:
+        return ctypes.c_void_p(torch.cuda.current_stream(ref.device).cuda_stream)
+    return ctypes.c_void_p(0)
+
+
+def _check(fn, st):
+    if st != 0:
+        raise Csa2Error(fn, st, lib().csa2_last_error().decode())
+
+
+def _dtype(t, dt, name):
+    if t is not None and t.dtype != dt:
+        raise TypeError(f"{name} must be {dt}, got {t.dtype}")
+
+
+class Cache:
+    """One KV-producing layer's global KV for B sequences: four device arrays
+    (structure of arrays, 356 bytes per entry) allocated by torch."""
+
+    def __init__(self, B, cap, device):
+        self.B, self.cap = B, cap
+        self.kv_codes = torch.empty(B, cap, 256, dtype=torch.uint8, device=device)
+        self.kv_scales = torch.empty(B, cap, 32, dtype=torch.uint8, device=device)
+        self.ik_codes = torch.empty(B, cap, 64, dtype=torch.uint8, device=device)
+        self.ik_scales = torch.empty(B, cap, 4, dtype=torch.uint8, device=device)
+
+    def c_struct(self):
+        return _Cache(self.kv_codes.data_ptr(), self.kv_scales.data_ptr(),
+                      self.ik_codes.data_ptr(), self.ik_scales.data_ptr(), self.cap)
+
+    def view(self, b0, b1):
+        """The same cache restricted to sequences b0..b1-1 (no copy)."""
+        v = Cache.__new__(Cache)
+        v.B, v.cap = b1 - b0, self.cap
+        for name, arr in self.arrays().items():
+            setattr(v, name, arr[b0:b1])
+        return v
+
+    def arrays(self):
+        return dict(kv_codes=self.kv_codes, kv_scales=self.kv_scales,
+                    ik_codes=self.ik_codes, ik_scales=self.ik_scales)
+
+    @property
+    def nbytes(self):
+        return sum(a.numel() for a in self.arrays().values())
+
+
+# ------------------------------------------------------------ entry points
+def csa2_workspace_bytes(op, Q, n_cols, k):
+    return int(lib().csa2_workspace_bytes(op, Q, n_cols, k))
+
+
+def csa2_compress_quant(h, z, m, w_ik, cache, e0=0, stream=None):
+    """h, z: [B, T, 512] bf16 (z None iff m == 1); w_ik [128, 512] bf16."""
+    _dtype(h, torch.bfloat16, "h"); _dtype(z, torch.bfloat16, "z"); _dtype(w_ik, torch.bfloat16, "w_ik")
+    B, T = h.shape[0], h.shape[1]
+    cs = cache.c_struct()
+    st = lib().csa2_compress_quant(_ptr(h), _ptr(z), B, T, m, _ptr(w_ik), ctypes.byref(cs), e0,
+                                   _stream(stream, h))
+    _check("csa2_compress_quant", st)
+
+
+def csa2_index_score(q_idx, w, q_seq, n_vis, cand, n_cols, cache, scores, stream=None):
+    """q_idx [Q, 32, 128] bf16, w [Q, 32] f32, q_seq [Q] i32, n_vis [Q] i64,
+    cand None or [Q, P] i32, scores [Q, ld] f32."""
+    _dtype(q_idx, torch.bfloat16, "q_idx"); _dtype(w, torch.float32, "w")
+    _dtype(q_seq, torch.int32, "q_seq"); _dtype(n_vis, torch.int64, "n_vis")
+    _dtype(cand, torch.int32, "cand"); _dtype(scores, torch.float32, "scores")
+    Q = q_idx.shape[0]
+    ld_cand = cand.shape[1] if cand is not None else 0
+    cs = cache.c_struct()
+    st = lib().csa2_index_score(_ptr(q_idx), _ptr(w), _ptr(q_seq), _ptr(n_vis), _ptr(cand),
+                                ld_cand, Q, n_cols, ctypes.byref(cs), _ptr(scores),
+                                scores.shape[1], _stream(stream, q_idx))
+    _check("csa2_index_score", st)
+
+
+def csa2_select_topk(scores, n_valid, col_ids, n_cols, k, out, ws=None, stream=None):
+    """scores [Q, ld] f32, n_valid [Q] i64, col_ids None or [Q, ld] i32,
+    out [Q, k] i32; ws a uint8 tensor of csa2_workspace_bytes(TOPK, ...)."""
+    _dtype(scores, torch.float32, "scores"); _dtype(n_valid, torch.int64, "n_valid")
+    _dtype(col_ids, torch.int32, "col_ids"); _dtype(out, torch.int32, "out")
+    Q = scores.shape[0]
+    wsb = ws.numel() * ws.element_size() if ws is not None else 0
+    st = lib().csa2_select_topk(_ptr(scores), scores.shape[1], Q, _ptr(n_valid), _ptr(col_ids),
+                                n_cols, k, _ptr(out), _ptr(ws), wsb, _stream(stream, scores))
+    _check("csa2_select_topk", st)
+
+
+def csa2_block_pool(scores, n_valid, n_cols, n_blocks, pool, pool_len, ws=None, block=8,
+                    stream=None):
+    """pool [Q, n_blocks * block] i32, pool_len [Q] i64."""
+    _dtype(scores, torch.float32, "scores"); _dtype(n_valid, torch.int64, "n_valid")
+    _dtype(pool, torch.int32, "pool"); _dtype(pool_len, torch.int64, "pool_len")
+    Q = scores.shape[0]
+    wsb = ws.numel() * ws.element_size() if ws is not None else 0
+    st = lib().csa2_block_pool(_ptr(scores), scores.shape[1], Q, _ptr(n_valid), n_cols, block,
+                               n_blocks, _ptr(pool), _ptr(pool_len), _ptr(ws), wsb,
+                               _stream(stream, scores))
+    _check("csa2_block_pool", st)
+
+
+def csa2_sparse_attend(q, q_seq, cache, idx, swa_codes, swa_scale, swa_start, swa_len, out,
+                       lse=None, ws=None, stream=None):
+    """q [Q, 64, 512] bf16, idx [Q, k] i32 (or None with k = 0),
+    swa_codes [B, T_swa, 512] u8, swa_scale [B, T_swa] f32, swa_start [Q] i64,
+    swa_len [Q] i32, out [Q, 64, 512] f32, lse [Q, 64] f32 or None."""
+    _dtype(q, torch.bfloat16, "q"); _dtype(q_seq, torch.int32, "q_seq")
+    _dtype(idx, torch.int32, "idx"); _dtype(swa_codes, torch.uint8, "swa_codes")
+    _dtype(swa_scale, torch.float32, "swa_scale"); _dtype(swa_start, torch.int64, "swa_start")
+    _dtype(swa_len, torch.int32, "swa_len"); _dtype(out, torch.float32, "out")
+    _dtype(lse, torch.float32, "lse")
+    Q = q.shape[0]
+    k = idx.shape[1] if idx is not None else 0
+    T_swa = swa_codes.shape[1] if swa_codes is not None else 0
+    wsb = ws.numel() * ws.element_size() if ws is not None else 0
+    cs = cache.c_struct()
+    st = lib().csa2_sparse_attend(_ptr(q), _ptr(q_seq), Q, ctypes.byref(cs), _ptr(idx), k,
+                                  _ptr(swa_codes), _ptr(swa_scale), T_swa, _ptr(swa_start),
+                                  _ptr(swa_len), _ptr(out), _ptr(lse), _ptr(ws), wsb,
+                                  _stream(stream, q))
+    _check("csa2_sparse_attend", st)
+
+
+def csa2_selftest(device="cuda"):
+    """Run the device self-test; returns the list of failure counters."""
+    n = lib().csa2_selftest(None, 0, None)
+    counts = torch.zeros(n, dtype=torch.int32, device=device)
+    st = lib().csa2_selftest(_ptr(counts), n, _stream(None, counts))
+    if st != 0:
+        raise RuntimeError(f"csa2_selftest launch failed ({st})")
+    torch.cuda.synchronize(counts.device)
+    return counts.cpu().tolist()
+
+
+def workspace(op, Q, n_cols, k, device):
+    """A uint8 device tensor of the size csa2_workspace_bytes asks for (or None)."""
+    n = csa2_workspace_bytes(op, Q, n_cols, k)
+    return torch.empty(n, dtype=torch.uint8, device=device) if n else None

@@ -1,0 +1,196 @@
+// C ABI of libcsa2: host-side validation and dispatch to the kernels.
+// Every check runs before anything is launched; see include/csa2.h for the
+// contract of each entry point.
+#include "csa2.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+
+#include "launch.h"
+
+namespace {
+
+thread_local char g_err[512];
+
+csa2_status fail(csa2_status st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+bool al(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+
+csa2_status hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return CSA2_OK;
+  return fail(CSA2_EHIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+csa2_status check_cache(const csa2_cache* c) {
+  if (!c) return fail(CSA2_EINVAL, "cache is NULL");
+  if (!c->kv_codes || !c->kv_scales || !c->ik_codes || !c->ik_scales)
+    return fail(CSA2_EINVAL, "cache has a NULL array");
+  if (!al(c->kv_codes, 16) || !al(c->kv_scales, 16) || !al(c->ik_codes, 16) ||
+      !al(c->ik_scales, 16))
+    return fail(CSA2_EINVAL, "cache arrays must be 16-byte aligned");
+  if (c->cap <= 0) return fail(CSA2_EINVAL, "cache cap=%lld must be > 0", (long long)c->cap);
+  return CSA2_OK;
+}
+
+#define REQ(cond, ...)                                   \
+  do {                                                   \
+    if (!(cond)) return fail(CSA2_EINVAL, __VA_ARGS__);  \
+  } while (0)
+
+}  // namespace
+
+extern "C" {
+
+const char* csa2_status_string(int s) {
+  switch (s) {
+    case CSA2_OK: return "CSA2_OK";
+    case CSA2_EINVAL: return "CSA2_EINVAL";
+    case CSA2_EUNSUPPORTED: return "CSA2_EUNSUPPORTED";
+    case CSA2_EWORKSPACE: return "CSA2_EWORKSPACE";
+    case CSA2_EHIP: return "CSA2_EHIP";
+    default: return "CSA2_UNKNOWN";
+  }
+}
+
+const char* csa2_last_error(void) { return g_err; }
+
+csa2_status csa2_compress_quant(const uint16_t* h, const uint16_t* z, int B, int64_t T, int m,
+                                const uint16_t* w_ik, const csa2_cache* dst, int64_t e0,
+                                void* stream) {
+  g_err[0] = 0;
+  REQ(h && w_ik, "h and w_ik must not be NULL");
+  const csa2_status cs = check_cache(dst);
+  if (cs != CSA2_OK) return cs;
+  REQ(B > 0 && B <= 65535, "B=%d must be in [1, 65535]", B);
+  REQ(T > 0, "T=%lld must be > 0", (long long)T);
+  REQ(m >= 1 && m <= 16, "m=%d must be in [1, 16]", m);
+  REQ(T % m == 0, "T=%lld is not a multiple of m=%d", (long long)T, m);
+  REQ(m == 1 || z, "z must be given when m > 1");
+  REQ(e0 >= 0 && e0 + T / m <= dst->cap, "entries [%lld, %lld) exceed cap=%lld", (long long)e0,
+      (long long)(e0 + T / m), (long long)dst->cap);
+  REQ(al(h, 16) && (!z || al(z, 16)) && al(w_ik, 16), "h, z, w_ik must be 16-byte aligned");
+  return hip_status(csa2::launch_compress_quant(h, m == 1 ? nullptr : z, B, T, m, w_ik,
+                                                dst->kv_codes, dst->kv_scales, dst->ik_codes,
+                                                dst->ik_scales, dst->cap, e0,
+                                                (hipStream_t)stream),
+                    "csa2_compress_quant launch");
+}
+
+csa2_status csa2_index_score(const uint16_t* q_idx, const float* w, const int32_t* q_seq,
+                             const int64_t* n_vis, const int32_t* cand, int64_t ld_cand, int Q,
+                             int64_t n_cols, const csa2_cache* src, float* scores, int64_t ld,
+                             void* stream) {
+  g_err[0] = 0;
+  REQ(q_idx && w && q_seq && n_vis && scores, "q_idx, w, q_seq, n_vis, scores must not be NULL");
+  const csa2_status cs = check_cache(src);
+  if (cs != CSA2_OK) return cs;
+  REQ(Q > 0, "Q=%d must be > 0", Q);
+  REQ(n_cols >= 0, "n_cols=%lld must be >= 0", (long long)n_cols);
+  REQ(ld >= n_cols, "ld=%lld < n_cols=%lld", (long long)ld, (long long)n_cols);
+  REQ(!cand || ld_cand >= n_cols, "ld_cand=%lld < n_cols=%lld", (long long)ld_cand,
+      (long long)n_cols);
+  REQ(cand || n_cols <= src->cap, "n_cols=%lld exceeds cap=%lld", (long long)n_cols,
+      (long long)src->cap);
+  REQ(al(q_idx, 16) && al(w, 4) && al(scores, 4), "q_idx must be 16-byte aligned");
+  if (n_cols == 0) return CSA2_OK;
+  REQ((n_cols + 1023) / 1024 * (int64_t)Q < (int64_t)1 << 31, "launch too large");
+  return hip_status(csa2::launch_index_score(q_idx, w, q_seq, n_vis, cand, ld_cand, Q, n_cols,
+                                             src->ik_codes, src->ik_scales, src->cap, scores, ld,
+                                             (hipStream_t)stream),
+                    "csa2_index_score launch");
+}
+
+static csa2_status select_common(const float* scores, int64_t ld, int Q, const int64_t* n_valid,
+                                 int64_t n_cols, int kk, void* ws, size_t ws_bytes, int mode) {
+  REQ(scores && n_valid, "scores and n_valid must not be NULL");
+  REQ(Q > 0, "Q=%d must be > 0", Q);
+  REQ(kk >= 1 && kk <= CSA2_MAX_K, "k=%d must be in [1, %d]", kk, CSA2_MAX_K);
+  REQ(n_cols >= 0 && n_cols <= CSA2_MAX_COLS, "n_cols=%lld must be in [0, %d]",
+      (long long)n_cols, CSA2_MAX_COLS);
+  REQ(ld >= n_cols && ld > 0, "ld=%lld < n_cols=%lld", (long long)ld, (long long)n_cols);
+  REQ(al(scores, 4), "scores must be 4-byte aligned");
+  const size_t need = csa2::select_ws_bytes(Q, n_cols, mode);
+  if (need > 0 && (!ws || ws_bytes < need))
+    return fail(CSA2_EWORKSPACE, "workspace %zu bytes < %zu needed", ws ? ws_bytes : (size_t)0,
+                need);
+  REQ(!ws || al(ws, 16), "ws must be 16-byte aligned");
+  return CSA2_OK;
+}
+
+csa2_status csa2_select_topk(const float* scores, int64_t ld, int Q, const int64_t* n_valid,
+                             const int32_t* col_ids, int64_t n_cols, int k, int32_t* out,
+                             void* ws, size_t ws_bytes, void* stream) {
+  g_err[0] = 0;
+  REQ(out, "out must not be NULL");
+  const csa2_status st = select_common(scores, ld, Q, n_valid, n_cols, k, ws, ws_bytes, 0);
+  if (st != CSA2_OK) return st;
+  return hip_status(csa2::launch_select(scores, ld, Q, n_valid, col_ids, n_cols, k, 0, out, k,
+                                        nullptr, ws, (hipStream_t)stream),
+                    "csa2_select_topk launch");
+}
+
+csa2_status csa2_block_pool(const float* scores, int64_t ld, int Q, const int64_t* n_valid,
+                            int64_t n_cols, int block, int n_blocks, int32_t* pool,
+                            int64_t* pool_len, void* ws, size_t ws_bytes, void* stream) {
+  g_err[0] = 0;
+  REQ(pool && pool_len, "pool and pool_len must not be NULL");
+  if (block != 8) return fail(CSA2_EUNSUPPORTED, "block=%d: only blocks of 8 positions", block);
+  const csa2_status st = select_common(scores, ld, Q, n_valid, n_cols, n_blocks, ws, ws_bytes, 1);
+  if (st != CSA2_OK) return st;
+  return hip_status(csa2::launch_select(scores, ld, Q, n_valid, nullptr, n_cols, n_blocks, 1, pool,
+                                        (int64_t)n_blocks * 8, pool_len, ws,
+                                        (hipStream_t)stream),
+                    "csa2_block_pool launch");
+}
+
+csa2_status csa2_sparse_attend(const uint16_t* q, const int32_t* q_seq, int Q, const csa2_cache* src,
+                               const int32_t* idx, int k, const uint8_t* swa_codes,
+                               const float* swa_scale, int64_t T_swa, const int64_t* swa_start,
+                               const int32_t* swa_len, float* out, float* lse, void* ws,
+                               size_t ws_bytes, void* stream) {
+  g_err[0] = 0;
+  REQ(q && q_seq && out && swa_start && swa_len,
+      "q, q_seq, out, swa_start, swa_len must not be NULL");
+  const csa2_status cs = check_cache(src);
+  if (cs != CSA2_OK) return cs;
+  REQ(k >= 0 && k <= CSA2_MAX_K, "k=%d must be in [0, %d]", k, CSA2_MAX_K);
+  REQ(k == 0 || idx, "idx must not be NULL when k > 0");
+  REQ(T_swa >= 0, "T_swa must be >= 0");
+  REQ(T_swa == 0 || (swa_codes && swa_scale), "swa_codes / swa_scale NULL with T_swa > 0");
+  REQ(al(q, 16) && al(out, 16) && (!swa_codes || al(swa_codes, 16)),
+      "q, out, swa_codes must be 16-byte aligned");
+  REQ(!ws || al(ws, 16), "ws must be 16-byte aligned");
+  REQ(Q > 0 && Q <= (1 << 24), "Q=%d must be in [1, 2^24]", Q);
+  return hip_status(csa2::launch_attend(q, q_seq, Q, src->kv_codes, src->kv_scales, src->cap, idx,
+                                        k, swa_codes, swa_scale, T_swa, swa_start, swa_len, out,
+                                        lse, ws, ws_bytes, (hipStream_t)stream),
+                    "csa2_sparse_attend launch");
+}
+
+size_t csa2_workspace_bytes(int op, int Q, int64_t n_cols, int k) {
+  if (Q <= 0) return 0;
+  switch (op) {
+    case CSA2_OP_TOPK: return csa2::select_ws_bytes(Q, n_cols < 0 ? 0 : n_cols, 0);
+    case CSA2_OP_POOL: return csa2::select_ws_bytes(Q, n_cols < 0 ? 0 : n_cols, 1);
+    case CSA2_OP_ATTEND: return csa2::attend_ws_bytes(Q, k < 0 ? 0 : k);
+    default: return 0;
+  }
+}
+
+int csa2_selftest(int32_t* counts, int n, void* stream) {
+  const int c = csa2::selftest_count();
+  if (!counts) return c;
+  if (n < c) return -1;
+  return csa2::launch_selftest(counts, (hipStream_t)stream) == hipSuccess ? 0 : -2;
+}
+
+}  // extern "C"

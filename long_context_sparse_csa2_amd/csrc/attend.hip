@@ -1,0 +1,357 @@
+// Steps a8 + a9: gather the selected FP4 main-KV rows and the FP8 SWA rows
+// of each query and run 64-head attention over them with the latent used as
+// both key and value, with an online softmax.
+//
+// Report digest "DeepSeek-V4.1-Flash", section 2.3: every query attends to
+// its selected main-KV entries together with the layer's sliding-window KV;
+// the 512-d latent is shared by the heads (MLA style) and is both key and
+// value; section 2.4.4: main KV is dequantised from FP4 before attention,
+// SWA KV stays FP8.
+//
+// Design.  A workgroup owns (query, 16 heads, a run of 64-row chunks).
+// Main-KV chunks and SWA chunks are separate, so every chunk has one row
+// type and the MFMAs stay in uniform control flow.  Per chunk:
+//   S = Q K^T   16 heads x 64 rows, 16x16x32 bf16 MFMA; each wave takes 16
+//               rows and each lane streams the 64 code bytes (or 128 FP8
+//               bytes) of one row quarter straight from HBM into the B
+//               operand, converting FP4 with the gfx950 conversion at scale
+//               1 and applying the E4M3 group scale in fp32 (exact);
+//               the query tile sits in registers for the whole run.
+//   softmax     running max / sum per head, reductions through LDS.
+//   O += P V    16 heads x 512 dims, 16x16x32 fp16 MFMA: P (fp16) and V^T
+//               (fp16, exact for FP4 values) are staged in LDS; wave w owns
+//               output dims 128w..128w+127.
+// Decode (few queries) splits the chunks of a query over several
+// workgroups and merges the partial (max, sum, O) by log-sum-exp in a second
+// kernel; prefill runs one workgroup per (query, head group) over all
+// chunks and writes the result directly.
+#include "common.h"
+#include "launch.h"
+
+namespace csa2 {
+
+constexpr int AT_ROWS = 64;        // rows per chunk
+constexpr int AT_HG = 16;          // heads per workgroup
+constexpr int AT_PAD = 8;          // fp16 padding of an LDS row
+constexpr int AT_MAX_SWA = 128;
+constexpr int AT_TARGET_WG = 1024; // workgroups a decode launch aims for
+
+__global__ __launch_bounds__(256) void k_attend(
+    const uint16_t* __restrict__ qv, const int32_t* __restrict__ q_seq,
+    const uint8_t* __restrict__ kv_codes, const uint8_t* __restrict__ kv_scales, int64_t cap,
+    const int32_t* __restrict__ idx, int k, const uint8_t* __restrict__ swa_codes,
+    const float* __restrict__ swa_scale, int64_t T_swa, const int64_t* __restrict__ swa_start,
+    const int32_t* __restrict__ swa_len, float* __restrict__ out, float* __restrict__ lse,
+    float* __restrict__ part_o, float* __restrict__ part_ml, int nsplit, int cps) {
+  __shared__ __align__(16) _Float16 vt[D_LAT][AT_ROWS + AT_PAD];   // V^T of the chunk
+  __shared__ __align__(16) _Float16 pl[AT_HG][AT_ROWS + AT_PAD];   // P of the chunk
+  __shared__ float red_m[4][AT_HG], red_l[4][AT_HG];
+  __shared__ int64_t rowoff[AT_ROWS];                               // entry / SWA row, -1 = none
+  __shared__ float rowsig[AT_ROWS];
+
+  const int sp = blockIdx.x % nsplit;
+  const int hq = blockIdx.x / nsplit;
+  const int hg = hq & 3, q = hq >> 2;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int r16 = lane & 15, qd = lane >> 4;
+  const int64_t seq = q_seq[q];
+  const int64_t sst = swa_start[q];
+  int64_t sl64 = swa_len[q];
+  if (sst < 0 || sst >= T_swa) sl64 = 0;                     // window clipped to [0, T_swa)
+  else if (sl64 > T_swa - sst) sl64 = T_swa - sst;
+  const int sl = sl64 < 0 ? 0 : (sl64 > AT_MAX_SWA ? AT_MAX_SWA : (int)sl64);
+  const int nmc = (k + AT_ROWS - 1) / AT_ROWS;
+  const int nch = nmc + (sl + AT_ROWS - 1) / AT_ROWS;
+  const int ch_beg = sp * cps;
+  const int ch_end = min(ch_beg + cps, nch);
+
+  // query tile: head hg*16 + r16, dims 128*qd + 8s .. +7 for step s
+  bf16x8_t a[16];
+  {
+    const uint16_t* qp = qv + ((int64_t)q * H_ATT + hg * AT_HG + r16) * D_LAT + qd * 128;
+#pragma unroll
+    for (int s = 0; s < 16; ++s) a[s] = *(const bf16x8_t*)(qp + 8 * s);
+  }
+  f32x4_t o[8];
+#pragma unroll
+  for (int t = 0; t < 8; ++t) o[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  float m_run[4], l_run[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) { m_run[j] = -INFINITY; l_run[j] = 0.f; }
+
+  for (int ch = ch_beg; ch < ch_end; ++ch) {
+    const bool is_main = ch < nmc;                 // uniform over the workgroup
+    const int rbase = is_main ? ch * AT_ROWS : (ch - nmc) * AT_ROWS;
+    if (tid < AT_ROWS) {
+      const int r = rbase + tid;
+      int64_t off = -1;
+      float sg = 1.f;
+      if (is_main) {
+        if (r < k) {
+          const int e = idx[(int64_t)q * k + r];
+          if (e >= 0) off = seq * cap + e;
+        }
+      } else if (r < sl) {
+        off = seq * T_swa + sst + r;
+        sg = swa_scale[off];
+      }
+      rowoff[tid] = off;
+      rowsig[tid] = sg;
+    }
+    __syncthreads();
+
+    // ---- S = Q K^T for rows 16*wave .. +15 (lane column r16)
+    const int lr = wave * 16 + r16;
+    const int64_t myoff = rowoff[lr];
+    const bool valid = myoff >= 0;
+    f32x4_t sacc = {0.f, 0.f, 0.f, 0.f};
+    if (is_main) {
+      const int64_t ent = valid ? myoff : seq * cap;
+      const u32x4_t* cp = (const u32x4_t*)(kv_codes + ent * 256 + qd * 64);
+      const u32x4_t w0 = cp[0], w1 = cp[1], w2 = cp[2], w3 = cp[3];
+      const uint64_t sc = *(const uint64_t*)(kv_scales + ent * 32 + qd * 8);
+      const u32x4_t wq[4] = {w0, w1, w2, w3};
+#pragma unroll
+      for (int s = 0; s < 16; ++s) {
+        const float scl = e4m3_val((uint32_t)(sc >> (8 * (s >> 1))) & 0xFFu);
+        sacc = mfma16_bf16(a[s], fp4x8_to_bf16_scaled(wq[s >> 2][s & 3], scl), sacc);
+      }
+    } else {
+      const int64_t rr = valid ? myoff : seq * T_swa + sst;
+      const u32x4_t* cp = (const u32x4_t*)(swa_codes + rr * 512 + qd * 128);
+#pragma unroll
+      for (int s2 = 0; s2 < 8; ++s2) {
+        const u32x4_t wv = cp[s2];
+        sacc = mfma16_bf16(a[2 * s2], fp8x8_to_bf16(wv[0], wv[1]), sacc);
+        sacc = mfma16_bf16(a[2 * s2 + 1], fp8x8_to_bf16(wv[2], wv[3]), sacc);
+      }
+      const float sg = rowsig[lr];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) sacc[j] *= sg;
+    }
+    if (!valid) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) sacc[j] = -INFINITY;
+    }
+
+    // ---- stage V^T (fp16): thread owns rows 2rp, 2rp+1 and dims 64db .. +63
+    {
+      const int rp = tid & 31, db = tid >> 5;
+      const int64_t off0 = rowoff[2 * rp], off1 = rowoff[2 * rp + 1];
+      _Float16* vcol = &vt[db * 64][2 * rp];
+      auto put8 = [&](int dim0, f16x8_t x0, f16x8_t x1) {
+#pragma unroll
+        for (int b = 0; b < 8; ++b) {
+          f16x2_t pr;
+          pr[0] = off0 >= 0 ? x0[b] : (_Float16)0.f;
+          pr[1] = off1 >= 0 ? x1[b] : (_Float16)0.f;
+          *(f16x2_t*)(vcol + (dim0 + b) * (AT_ROWS + AT_PAD)) = pr;
+        }
+      };
+      if (is_main) {
+        const int64_t e0 = off0 >= 0 ? off0 : seq * cap, e1 = off1 >= 0 ? off1 : seq * cap;
+        const u32x4_t* c0p = (const u32x4_t*)(kv_codes + e0 * 256 + db * 32);
+        const u32x4_t* c1p = (const u32x4_t*)(kv_codes + e1 * 256 + db * 32);
+        const uint32_t s0 = *(const uint32_t*)(kv_scales + e0 * 32 + db * 4);
+        const uint32_t s1 = *(const uint32_t*)(kv_scales + e1 * 32 + db * 4);
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2) {
+          const u32x4_t a0 = c0p[h2], b0 = c1p[h2];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {            // 8 dims per word, 2 words per scale group
+            const int wi = 4 * h2 + i;
+            put8(8 * wi, fp4x8_to_f16_scaled(a0[i], e4m3_val((s0 >> (8 * (wi >> 1))) & 0xFFu)),
+                 fp4x8_to_f16_scaled(b0[i], e4m3_val((s1 >> (8 * (wi >> 1))) & 0xFFu)));
+          }
+        }
+      } else {
+        const int64_t r0 = off0 >= 0 ? off0 : seq * T_swa + sst;
+        const int64_t r1 = off1 >= 0 ? off1 : seq * T_swa + sst;
+        const float g0 = rowsig[2 * rp], g1 = rowsig[2 * rp + 1];
+        const uint32_t* c0p = (const uint32_t*)(swa_codes + r0 * 512 + db * 64);
+        const uint32_t* c1p = (const uint32_t*)(swa_codes + r1 * 512 + db * 64);
+#pragma unroll 2
+        for (int i = 0; i < 8; ++i) {              // 8 dims = two words per step
+          const uint32_t x0l = c0p[2 * i], x0h = c0p[2 * i + 1];
+          const uint32_t x1l = c1p[2 * i], x1h = c1p[2 * i + 1];
+          f16x8_t y0, y1;
+#pragma unroll
+          for (int b = 0; b < 4; ++b) {
+            y0[b] = (_Float16)(e4m3_val((x0l >> (8 * b)) & 0xFFu) * g0);
+            y0[4 + b] = (_Float16)(e4m3_val((x0h >> (8 * b)) & 0xFFu) * g0);
+            y1[b] = (_Float16)(e4m3_val((x1l >> (8 * b)) & 0xFFu) * g1);
+            y1[4 + b] = (_Float16)(e4m3_val((x1h >> (8 * b)) & 0xFFu) * g1);
+          }
+          put8(8 * i, y0, y1);
+        }
+      }
+    }
+
+    // ---- online softmax over this chunk
+    float cm[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      float v = sacc[j];
+      v = fmaxf(v, __shfl_xor(v, 1));
+      v = fmaxf(v, __shfl_xor(v, 2));
+      v = fmaxf(v, __shfl_xor(v, 4));
+      v = fmaxf(v, __shfl_xor(v, 8));
+      cm[j] = v;
+    }
+    if (r16 == 0) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) red_m[wave][4 * qd + j] = cm[j];
+    }
+    __syncthreads();
+    float alpha[4], p[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int hh = 4 * qd + j;
+      const float cmax = fmaxf(fmaxf(red_m[0][hh], red_m[1][hh]), fmaxf(red_m[2][hh], red_m[3][hh]));
+      const float m_new = fmaxf(m_run[j], cmax);
+      if (m_new == -INFINITY) {
+        alpha[j] = 1.f;
+        p[j] = 0.f;
+      } else {
+        alpha[j] = expf(m_run[j] - m_new);            // 0 when m_run is -inf
+        p[j] = valid ? expf(sacc[j] - m_new) : 0.f;
+      }
+      m_run[j] = m_new;
+      pl[hh][lr] = (_Float16)p[j];
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      float v = p[j];
+      v += __shfl_xor(v, 1);
+      v += __shfl_xor(v, 2);
+      v += __shfl_xor(v, 4);
+      v += __shfl_xor(v, 8);
+      if (r16 == 0) red_l[wave][4 * qd + j] = v;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int hh = 4 * qd + j;
+      l_run[j] = l_run[j] * alpha[j] + ((red_l[0][hh] + red_l[1][hh]) + (red_l[2][hh] + red_l[3][hh]));
+#pragma unroll
+      for (int t = 0; t < 8; ++t) o[t][j] *= alpha[j];
+    }
+
+    // ---- O += P V for dims 128*wave .. +127
+    const f16x8_t pa0 = *(const f16x8_t*)&pl[r16][qd * 8];
+    const f16x8_t pa1 = *(const f16x8_t*)&pl[r16][32 + qd * 8];
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      const int dim = wave * 128 + 16 * t + r16;
+      const f16x8_t vb0 = *(const f16x8_t*)&vt[dim][qd * 8];
+      const f16x8_t vb1 = *(const f16x8_t*)&vt[dim][32 + qd * 8];
+      o[t] = mfma16_f16(pa0, vb0, o[t]);
+      o[t] = mfma16_f16(pa1, vb1, o[t]);
+    }
+    __syncthreads();
+  }
+
+  // ---- write the result (single split) or the partial state
+  const int head0 = hg * AT_HG + 4 * qd;
+  if (nsplit == 1) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float inv = l_run[j] > 0.f ? 1.f / l_run[j] : 0.f;
+      float* op = out + ((int64_t)q * H_ATT + head0 + j) * D_LAT + wave * 128 + r16;
+#pragma unroll
+      for (int t = 0; t < 8; ++t) op[16 * t] = o[t][j] * inv;
+      if (lse && wave == 0 && r16 == 0)
+        lse[(int64_t)q * H_ATT + head0 + j] = l_run[j] > 0.f ? m_run[j] + logf(l_run[j]) : -INFINITY;
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int64_t slot = ((int64_t)q * nsplit + sp) * H_ATT + head0 + j;
+      float* op = part_o + slot * D_LAT + wave * 128 + r16;
+#pragma unroll
+      for (int t = 0; t < 8; ++t) op[16 * t] = o[t][j];
+      if (wave == 0 && r16 == 0) {
+        part_ml[2 * slot] = m_run[j];
+        part_ml[2 * slot + 1] = l_run[j];
+      }
+    }
+  }
+}
+
+// Merge the per-split partial states of one (query, head) by log-sum-exp.
+__global__ __launch_bounds__(128) void k_attend_combine(const float* __restrict__ part_o,
+                                                        const float* __restrict__ part_ml,
+                                                        int nsplit, float* __restrict__ out,
+                                                        float* __restrict__ lse) {
+  const int qh = blockIdx.x;              // q * 64 + head
+  const int q = qh / H_ATT, h = qh % H_ATT;
+  float M = -INFINITY;
+  for (int s = 0; s < nsplit; ++s) {
+    const int64_t slot = ((int64_t)q * nsplit + s) * H_ATT + h;
+    if (part_ml[2 * slot + 1] > 0.f) M = fmaxf(M, part_ml[2 * slot]);
+  }
+  float L = 0.f;
+  f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+  const int d0 = threadIdx.x * 4;
+  for (int s = 0; s < nsplit; ++s) {
+    const int64_t slot = ((int64_t)q * nsplit + s) * H_ATT + h;
+    const float l = part_ml[2 * slot + 1];
+    if (!(l > 0.f)) continue;
+    const float wgt = expf(part_ml[2 * slot] - M);
+    L += l * wgt;
+    const f32x4_t v = *(const f32x4_t*)(part_o + slot * D_LAT + d0);
+    acc += v * wgt;
+  }
+  const float inv = L > 0.f ? 1.f / L : 0.f;
+  *(f32x4_t*)(out + (int64_t)qh * D_LAT + d0) = acc * inv;
+  if (lse && threadIdx.x == 0) lse[qh] = L > 0.f ? M + logf(L) : -INFINITY;
+}
+
+// ------------------------------------------------------------ host side
+static void attend_plan(int Q, int k, int& nsplit, int& cps) {
+  const int nch = (k + AT_ROWS - 1) / AT_ROWS + AT_MAX_SWA / AT_ROWS;
+  const int groups = Q * (H_ATT / AT_HG);
+  int want = (AT_TARGET_WG + groups - 1) / groups;
+  if (want < 1) want = 1;
+  cps = (nch + want - 1) / want;
+  if (cps < 1) cps = 1;
+  nsplit = (nch + cps - 1) / cps;
+  if (nsplit < 1) nsplit = 1;
+}
+
+static size_t attend_ws_for(int Q, int nsplit) {
+  if (nsplit <= 1) return 0;
+  return (size_t)Q * nsplit * H_ATT * (D_LAT + 2) * sizeof(float);
+}
+
+size_t attend_ws_bytes(int Q, int k) {
+  int nsplit, cps;
+  attend_plan(Q, k, nsplit, cps);
+  return attend_ws_for(Q, nsplit);
+}
+
+hipError_t launch_attend(const uint16_t* q, const int32_t* q_seq, int Q, const uint8_t* kv_codes,
+                         const uint8_t* kv_scales, int64_t cap, const int32_t* idx, int k,
+                         const uint8_t* swa_codes, const float* swa_scale, int64_t T_swa,
+                         const int64_t* swa_start, const int32_t* swa_len, float* out, float* lse,
+                         void* ws, size_t ws_bytes, hipStream_t stream) {
+  int nsplit, cps;
+  attend_plan(Q, k, nsplit, cps);
+  const int nch = (k + AT_ROWS - 1) / AT_ROWS + AT_MAX_SWA / AT_ROWS;
+  while (nsplit > 1 && (ws == nullptr || attend_ws_for(Q, nsplit) > ws_bytes)) {
+    ++cps;                                   // fewer, longer splits until the partials fit
+    nsplit = (nch + cps - 1) / cps;
+  }
+  if (nsplit <= 1) { nsplit = 1; cps = nch; }
+  float* part_o = (float*)ws;
+  float* part_ml = nsplit > 1 ? part_o + (size_t)Q * nsplit * H_ATT * D_LAT : nullptr;
+  hipLaunchKernelGGL(k_attend, dim3((unsigned)(Q * (H_ATT / AT_HG) * nsplit)), dim3(256), 0,
+                     stream, q, q_seq, kv_codes, kv_scales, cap, idx, k, swa_codes, swa_scale,
+                     T_swa, swa_start, swa_len, out, lse, part_o, part_ml, nsplit, cps);
+  if (nsplit > 1)
+    hipLaunchKernelGGL(k_attend_combine, dim3((unsigned)(Q * H_ATT)), dim3(128), 0, stream,
+                       (const float*)part_o, (const float*)part_ml, nsplit, out, lse);
+  return hipGetLastError();
+}
+
+}  // namespace csa2

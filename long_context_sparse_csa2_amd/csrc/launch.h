@@ -1,0 +1,37 @@
+// Internal launchers behind the C ABI (validated arguments only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace csa2 {
+
+hipError_t launch_compress_quant(const uint16_t* h, const uint16_t* z, int B, int64_t T, int m,
+                                 const uint16_t* w_ik, uint8_t* kv_codes, uint8_t* kv_scales,
+                                 uint8_t* ik_codes, uint8_t* ik_scales, int64_t cap, int64_t e0,
+                                 hipStream_t stream);
+
+hipError_t launch_index_score(const uint16_t* q_idx, const float* w, const int32_t* q_seq,
+                              const int64_t* n_vis, const int32_t* cand, int64_t ld_cand, int Q,
+                              int64_t n_cols, const uint8_t* ik_codes, const uint8_t* ik_scales,
+                              int64_t cap, float* scores, int64_t ld, hipStream_t stream);
+
+// Selection: mode 0 = top-k of columns (levels down to 0), mode 1 = block
+// pool (levels down to 1, blocks of 8).
+size_t select_ws_bytes(int Q, int64_t n_cols, int mode);
+hipError_t launch_select(const float* scores, int64_t ld, int Q, const int64_t* n_valid,
+                         const int32_t* col_ids, int64_t n_cols, int kk, int mode, int32_t* out,
+                         int64_t out_ld, int64_t* out_len, void* ws, hipStream_t stream);
+
+size_t attend_ws_bytes(int Q, int k);
+hipError_t launch_attend(const uint16_t* q, const int32_t* q_seq, int Q, const uint8_t* kv_codes,
+                         const uint8_t* kv_scales, int64_t cap, const int32_t* idx, int k,
+                         const uint8_t* swa_codes, const float* swa_scale, int64_t T_swa,
+                         const int64_t* swa_start, const int32_t* swa_len, float* out, float* lse,
+                         void* ws, size_t ws_bytes, hipStream_t stream);
+
+int selftest_count();
+hipError_t launch_selftest(int32_t* counts, hipStream_t stream);
+
+}  // namespace csa2

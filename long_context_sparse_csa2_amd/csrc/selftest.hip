@@ -1,0 +1,106 @@
+// Device self-test of the gfx950 instructions the kernels depend on, each
+// checked against plain integer/bit code on the same device:
+//   0  FP4 -> bf16 with a power-of-two scale in the conversion (E8M0 path)
+//   1  FP4 -> bf16 times each E4M3 scale (main-KV path, fp32 multiply)
+//   2  MFMA 32x32x16 bf16 row/column placement of A, B and D
+//   3  MFMA 16x16x32 bf16 placement
+//   4  MFMA 16x16x32 fp16 placement
+//   5  FP4 -> fp16 times each E4M3 scale (packed fp16 multiply)
+// Each counter holds the number of mismatching values (0 = pass).
+#include "common.h"
+#include "launch.h"
+
+namespace csa2 {
+
+constexpr int ST_COUNT = 6;
+
+__device__ __forceinline__ int st_a(int m, int k) { return ((m * 7 + k * 3) % 9) - 4; }
+__device__ __forceinline__ int st_b(int k, int n) { return ((k * 5 + n * 11) % 7) - 3; }
+
+__global__ __launch_bounds__(64) void k_selftest(int32_t* counts) {
+  const int l = threadIdx.x;
+  int bad_pow2 = 0, bad_bf = 0, bad_f16 = 0;
+  const float pow2[6] = {1.0f, 0.5f, 0x1p-9f, 0x1p-20f, 0x1p20f, 0x1p-126f};
+  for (int v = 0; v < 256; ++v) {
+    const uint32_t w = (uint32_t)v | ((uint32_t)((v ^ l) & 255) << 8) |
+                       ((uint32_t)((v + 3 * l) & 255) << 16) | ((uint32_t)((v * 5 + l) & 255) << 24);
+    for (int si = 0; si < 6; ++si) {
+      const bf16x8_t hw = fp4x8_to_bf16_pow2(w, pow2[si]);
+      for (int i = 0; i < 8; ++i) {
+        const float got = (float)hw[i];
+        const float want = fp4_scaled_soft(w, i, pow2[si]);
+        bad_pow2 += !(got == want && signbit(got) == signbit(want));
+      }
+    }
+    // every positive finite E4M3FN scale; lane l takes codes l, l + 64
+    for (int sc = l + 1; sc < 0x7F; sc += 64) {
+      const float s = e4m3_val((uint32_t)sc);
+      const bf16x8_t hb = fp4x8_to_bf16_scaled(w, s);
+      const f16x8_t hh = fp4x8_to_f16_scaled(w, s);
+      for (int i = 0; i < 8; ++i) {
+        const float want = fp4_scaled_soft(w, i, s);
+        const float gb = (float)hb[i], gh = (float)hh[i];
+        bad_bf += !(gb == want);
+        bad_f16 += !(gh == want);
+      }
+    }
+  }
+  atomicAdd(&counts[0], bad_pow2);
+  atomicAdd(&counts[1], bad_bf);
+  atomicAdd(&counts[5], bad_f16);
+
+  {  // 32x32x16 bf16
+    bf16x8_t a, b;
+    for (int t = 0; t < 8; ++t) {
+      a[t] = (__bf16)(float)st_a(l % 32, 8 * (l / 32) + t);
+      b[t] = (__bf16)(float)st_b(8 * (l / 32) + t, l % 32);
+    }
+    f32x16_t d = {};
+    d = mfma32_bf16(a, b, d);
+    int bad = 0;
+    for (int j = 0; j < 16; ++j) {
+      const int m = 8 * (j / 4) + 4 * (l / 32) + (j % 4), n = l % 32;
+      int ref = 0;
+      for (int kk = 0; kk < 16; ++kk) ref += st_a(m, kk) * st_b(kk, n);
+      bad += d[j] != (float)ref;
+    }
+    atomicAdd(&counts[2], bad);
+  }
+  {  // 16x16x32 bf16 and fp16
+    bf16x8_t a, b;
+    f16x8_t ah, bh;
+    for (int t = 0; t < 8; ++t) {
+      const float av = (float)st_a(l % 16, 8 * (l / 16) + t);
+      const float bv = (float)st_b(8 * (l / 16) + t, l % 16);
+      a[t] = (__bf16)av; b[t] = (__bf16)bv;
+      ah[t] = (_Float16)av; bh[t] = (_Float16)bv;
+    }
+    f32x4_t d = {}, dh = {};
+    d = mfma16_bf16(a, b, d);
+    dh = mfma16_f16(ah, bh, dh);
+    int bad = 0, badh = 0;
+    for (int j = 0; j < 4; ++j) {
+      const int m = 4 * (l / 16) + j, n = l % 16;
+      int ref = 0;
+      for (int kk = 0; kk < 32; ++kk) ref += st_a(m, kk) * st_b(kk, n);
+      bad += d[j] != (float)ref;
+      badh += dh[j] != (float)ref;
+    }
+    atomicAdd(&counts[3], bad);
+    atomicAdd(&counts[4], badh);
+  }
+}
+
+__global__ void k_zero_i32(int32_t* p, int n) {
+  if ((int)threadIdx.x < n) p[threadIdx.x] = 0;
+}
+
+int selftest_count() { return ST_COUNT; }
+
+hipError_t launch_selftest(int32_t* counts, hipStream_t stream) {
+  hipLaunchKernelGGL(k_zero_i32, dim3(1), dim3(64), 0, stream, counts, ST_COUNT);
+  hipLaunchKernelGGL(k_selftest, dim3(1), dim3(64), 0, stream, counts);
+  return hipGetLastError();
+}
+
+}  // namespace csa2

@@ -1,0 +1,114 @@
+"""One decode (or prefill) step of the CSA2 global branch, composed from the
+C-ABI calls: the layer schedule of a workload run layer by layer.
+
+Report digest "DeepSeek-V4.1-Flash", section 2.3.1: a Full layer produces
+main KV and indexer K and runs the indexer; a Reindex layer rescores the
+shared keys with its own indexer query and picks its own top-k; a Reuse
+layer attends with the latest top-k indices and runs no indexer.  Section
+2.3.2: in the decoder the first Full layer also builds the 2048 x 8 block
+pool that the Reindex layers search.  Layers run one after another (layer
+l + 1's queries would depend on layer l's output in the model).
+
+Buffers are allocated once with torch; `run()` only enqueues kernels.
+"""
+
+import torch
+
+from . import (Cache, CSA2_OP_ATTEND, CSA2_OP_POOL, CSA2_OP_TOPK, csa2_block_pool,
+               csa2_compress_quant, csa2_index_score, csa2_select_topk, csa2_sparse_attend,
+               workspace)
+from .synth import Workload
+
+
+def build_cache(wl: Workload, device, seq_chunk=1):
+    """Draw each sequence's raw latents on the device and compress them into a
+    fresh cache (steps a1-a3), a few sequences at a time to bound memory."""
+    cache = Cache(wl.B, wl.N, device)
+    w_ik = wl.w_ik(device)
+    for b0 in range(0, wl.B, seq_chunk):
+        b1 = min(wl.B, b0 + seq_chunk)
+        h, z = wl.latents(device, b0, b1)
+        sub = cache.view(b0, b1)
+        csa2_compress_quant(h, z, wl.m, w_ik, sub)
+        del h, z
+    return cache, w_ik
+
+
+class Step:
+    """All layers of one step of a workload over a built cache."""
+
+    def __init__(self, wl: Workload, device, cache=None):
+        self.wl = wl
+        self.device = device
+        if cache is None:
+            cache, _ = build_cache(wl, device)
+        self.cache = cache
+        g = wl.query_geometry()
+        self.q_seq = g["q_seq"].to(device)
+        self.n_vis = g["n_vis"].to(device)
+        self.swa_start = g["swa_start"].to(device)
+        self.swa_len = g["swa_len"].to(device)
+        Q, N, k = wl.Q, wl.N, wl.k
+        self.layers = [wl.layer_inputs(li, device) for li in range(len(wl.layers))]
+        self.scores = torch.empty(Q, N, dtype=torch.float32, device=device)
+        self.idx = torch.empty(Q, k, dtype=torch.int32, device=device)
+        self.ws_topk = workspace(CSA2_OP_TOPK, Q, N, k, device)
+        self.ws_attend = workspace(CSA2_OP_ATTEND, Q, 0, k, device)
+        self.out = [torch.empty(Q, 64, 512, dtype=torch.float32, device=device) for _ in wl.layers]
+        self.lse = [torch.empty(Q, 64, dtype=torch.float32, device=device) for _ in wl.layers]
+        self.idx_per_layer = [None] * len(wl.layers)
+        self.scores_per_layer = [None] * len(wl.layers)
+        if wl.hierarchical:
+            P = wl.n_blocks * wl.block
+            self.P = P
+            self.pool = torch.empty(Q, P, dtype=torch.int32, device=device)
+            self.pool_len = torch.empty(Q, dtype=torch.int64, device=device)
+            self.ws_pool = workspace(CSA2_OP_POOL, Q, N, wl.n_blocks, device)
+            self.pool_scores = torch.empty(Q, P, dtype=torch.float32, device=device)
+            self.ws_topk_pool = workspace(CSA2_OP_TOPK, Q, P, k, device)
+            self.idx_r = [torch.empty(Q, k, dtype=torch.int32, device=device) for _ in wl.layers]
+
+    def run(self, keep=False, events=None):
+        """Enqueue every layer of the step.  keep=True also keeps each
+        layer's indices and scores (for checking).  `events`, a dict, gets
+        (start, end) torch.cuda.Event pairs recorded around each call on the
+        current stream, keyed by call name."""
+        wl = self.wl
+        idx = self.idx
+
+        def timed(name, fn, *a, **kw):
+            if events is None:
+                return fn(*a, **kw)
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn(*a, **kw)
+            e1.record()
+            events.setdefault(name, []).append((e0, e1))
+
+        for li, mode in enumerate(wl.layers):
+            L = self.layers[li]
+            if mode == "full":
+                timed("index_score_full", csa2_index_score, L["q_idx"], L["w"], self.q_seq,
+                      self.n_vis, None, wl.N, self.cache, self.scores)
+                if wl.hierarchical:
+                    timed("block_pool", csa2_block_pool, self.scores, self.n_vis, wl.N,
+                          wl.n_blocks, self.pool, self.pool_len, self.ws_pool, block=wl.block)
+                timed("select_topk_full", csa2_select_topk, self.scores, self.n_vis, None, wl.N,
+                      wl.k, self.idx, self.ws_topk)
+                idx = self.idx
+            elif mode == "reindex":
+                idx = self.idx_r[li]
+                timed("index_score_pool", csa2_index_score, L["q_idx"], L["w"], self.q_seq,
+                      self.pool_len, self.pool, self.P, self.cache, self.pool_scores)
+                timed("select_topk_pool", csa2_select_topk, self.pool_scores, self.pool_len,
+                      self.pool, self.P, wl.k, idx, self.ws_topk_pool)
+            if keep:
+                self.idx_per_layer[li] = idx.clone()
+                if mode == "full":
+                    self.scores_per_layer[li] = self.scores.clone()
+                elif mode == "reindex":
+                    self.scores_per_layer[li] = self.pool_scores.clone()
+            timed("sparse_attend", csa2_sparse_attend, L["q_attn"], self.q_seq, self.cache, idx,
+                  L["swa_codes"], L["swa_scale"], self.swa_start, self.swa_len, self.out[li],
+                  self.lse[li], self.ws_attend)

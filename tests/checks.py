@@ -1,0 +1,250 @@
+"""Parity checks of the HIP path against the fp64 oracle.
+
+Each check takes the GPU's outputs (copied to the host) and the inputs both
+sides saw, recomputes the step with the oracle and asserts the bar:
+  * m = 1 main-KV codes and scales: bit-exact.
+  * indexer-K codes (fp32 projection on the GPU) and m = 2 main-KV codes
+    (fp32 pooling on the GPU): equal, except where the oracle's value lies
+    within the GPU arithmetic's error bound of a rounding threshold; there
+    the GPU's code must be one of the two codes the threshold separates.
+  * scores: |s - r| <= 1e-3 * max(|r|, 1e-3 * max_j |r_j|).
+  * top-k and pool computed from the GPU's own fp32 scores: bit-exact
+    against the oracle's selection on the same fp32 values; against the
+    oracle's fp64 scores, the sets may differ only in entries whose fp64
+    score is within 1e-5 relative of the k-th score.
+  * attention: max|o - o_ref| / max|o_ref| <= 2e-3; per head
+    |lse - lse_ref| <= 1e-4 + 32 * 2^-24 * max_j sum_c |q_c v_jc| (the logits
+    accumulate 16 MFMA K-steps in fp32, so their error scales with the
+    magnitude of the products, not with the lse).
+Stages hand off the GPU's own results (cache bytes, pool, indices) to the
+oracle's next stage, since a near-tie swap changes which rows are read.
+"""
+import numpy as np
+import torch
+
+from oracle import csa2_ref as R
+from oracle import formats as F
+
+SCORE_RTOL = 1e-3
+TIE_RTOL = 1e-5
+ATT_TOL = 2e-3
+LSE_ATOL = 1e-4
+
+E2M1_MIDS = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0])
+_E4M3_POS = F.e4m3fn_value(np.arange(0x7F))
+E4M3_MIDS = (_E4M3_POS[1:] + _E4M3_POS[:-1]) / 2
+
+
+def host(t):
+    return t.detach().cpu().numpy()
+
+
+def bf16_to_f64(t):
+    return t.detach().cpu().float().numpy().astype(np.float64)
+
+
+# ----------------------------------------------------------------- codes
+def _near(vals, mids, tol):
+    """|vals| within tol of any midpoint (elementwise)."""
+    a = np.abs(vals)[..., None]
+    return (np.abs(a - mids) <= tol[..., None]).any(-1)
+
+
+def check_codes_with_margin(ref_vals, delta, gpu_codes, gpu_scales, ref_codes, ref_scales,
+                            group, scale_value, scale_mids, elem_div_scale=True):
+    """Compare GPU nibble codes / scale bytes with the oracle's under the
+    margin rule.  ref_vals [n, C] are the oracle's pre-quantisation values,
+    delta [n, C] the GPU error bound; scale_value maps scale bytes to
+    values; scale_mids are the rounding thresholds of the scale (None for
+    E8M0: thresholds are powers of two)."""
+    n, C = ref_vals.shape
+    G = C // group
+    rv = ref_vals.reshape(n, G, group)
+    dl = delta.reshape(n, G, group)
+    amax = np.abs(rv).max(-1)
+    dmax = dl.max(-1)
+    bad_scale = gpu_scales != ref_scales
+    if bad_scale.any():
+        if scale_mids is None:                       # E8M0: floor(log2 amax) boundary
+            p = np.exp2(np.round(np.log2(np.maximum(amax, 1e-300))))
+            ok = np.abs(amax - p) <= dmax
+        else:                                        # E4M3: amax / 6 near a midpoint
+            ok = _near(amax / 6.0, scale_mids, dmax / 6.0)
+        assert ok[bad_scale].all(), f"{int((bad_scale & ~ok).sum())} scale bytes differ beyond the margin"
+    # element codes, judged against the scale the GPU chose
+    s = scale_value(gpu_scales)[..., None]
+    gc = F.unpack_nibbles(gpu_codes).reshape(n, G, group)
+    rc = F.unpack_nibbles(ref_codes).reshape(n, G, group)
+    safe = np.where(s > 0, s, 1.0)
+    want = np.where(s > 0, F.e2m1_encode(rv / safe), 0)
+    # canonical zero: +0 and -0 are the same value
+    mag = lambda c: np.where((c & 7) == 0, 0, c)
+    diff = mag(gc) != mag(want)
+    if diff.any():
+        near = _near(rv / safe, E2M1_MIDS, dl / safe)
+        adj = np.abs(F.e2m1_value(gc) - F.e2m1_value(want)) <= 2.0 + 1e-12
+        ok = near & adj
+        assert ok[diff].all(), f"{int((diff & ~ok).sum())} codes differ beyond the margin"
+    return int(diff.sum()), int(bad_scale.sum())
+
+
+def check_main_kv(x_ref, m, gpu_kv_codes, gpu_kv_scales, h_abs_max):
+    """a1 + a2: oracle pooled x (fp64) quantised vs the GPU's bytes."""
+    rc, rs = R.quant_main_kv(x_ref)
+    if m == 1:
+        assert np.array_equal(gpu_kv_scales, rs), "main-KV scales differ (m=1 must be exact)"
+        g = F.unpack_nibbles(gpu_kv_codes)
+        r = F.unpack_nibbles(rc)
+        assert np.array_equal(g, r), f"main-KV codes differ at {int((g != r).sum())} channels (m=1)"
+        return 0, 0
+    # fp32 pooling: a few ulp of the largest input of the group of m rows
+    delta = np.asarray(h_abs_max, np.float64) * 2.0 ** -18
+    return check_codes_with_margin(x_ref, delta, gpu_kv_codes, gpu_kv_scales, rc, rs, 16,
+                                   F.e4m3fn_value, E4M3_MIDS)
+
+
+def check_indexer_k(gpu_kv_codes, gpu_kv_scales, w_ik, gpu_ik_codes, gpu_ik_scales):
+    """a3, stage-wise: the oracle projects the GPU's stored main KV."""
+    xhat = R.dequant_main_kv(gpu_kv_codes, gpu_kv_scales)
+    k = R.project_indexer_k(xhat, w_ik)
+    rc, rs = R.quant_mxfp4(k)
+    # fp32 accumulation of 512 exact products: bound n * 2^-24 * sum|terms|, doubled
+    delta = (np.abs(xhat) @ np.abs(w_ik).T) * (2 * 512 * 2.0 ** -24)
+    return check_codes_with_margin(k, delta, gpu_ik_codes, gpu_ik_scales, rc, rs, 32,
+                                   F.e8m0_value, None)
+
+
+# ---------------------------------------------------------------- scores
+def check_scores(gpu, ref):
+    gpu = np.asarray(gpu, np.float64)
+    ref = np.asarray(ref, np.float64)
+    if ref.size == 0:
+        return 0.0
+    floor = 1e-3 * np.abs(ref).max()
+    tol = SCORE_RTOL * np.maximum(np.abs(ref), floor)
+    err = np.abs(gpu - ref)
+    assert np.all(err <= tol), f"scores: max rel err {float((err / np.maximum(np.abs(ref), floor)).max()):.3e}"
+    return float((err / np.maximum(np.abs(ref), floor)).max())
+
+
+def check_topk_exact(gpu_idx, scores_f32, k, ids=None):
+    """The GPU selection equals the oracle's selection on the same fp32 scores."""
+    want = R.topk(np.asarray(scores_f32, np.float64), k, ids)
+    got = np.sort(gpu_idx[gpu_idx >= 0])
+    assert got.size == min(k, len(scores_f32)), f"count {got.size} != {min(k, len(scores_f32))}"
+    assert np.array_equal(got, want), f"top-k differs in {np.setxor1d(got, want).size} ids"
+    assert np.all(gpu_idx[got.size:] == -1), "padding after the selected ids must be -1"
+    assert np.all(np.diff(gpu_idx[:got.size]) > 0), "selected ids must be ascending"
+
+
+def check_topk_tolerance(gpu_idx, ref_scores, k, ids=None):
+    """Against fp64 scores: only near-ties (within 1e-5 of the k-th) may swap."""
+    ref_scores = np.asarray(ref_scores, np.float64)
+    ids = np.arange(ref_scores.size) if ids is None else np.asarray(ids)
+    want = R.topk(ref_scores, k, ids)
+    got = np.sort(gpu_idx[gpu_idx >= 0])
+    assert got.size == want.size
+    sd = np.setxor1d(got, want)
+    if sd.size:
+        kth = R.kth_score(ref_scores, k)
+        pos = {int(e): i for i, e in enumerate(ids)}
+        s = np.array([ref_scores[pos[int(e)]] for e in sd])
+        assert np.all(np.abs(s - kth) <= TIE_RTOL * abs(kth)), "top-k swap beyond the tie tolerance"
+    return int(sd.size)
+
+
+def check_pool_exact(gpu_pool, gpu_len, scores_f32, block, n_blocks):
+    want = R.block_pool(np.asarray(scores_f32, np.float64), block, n_blocks)
+    assert int(gpu_len) == want.size, f"pool_len {int(gpu_len)} != {want.size}"
+    assert np.array_equal(gpu_pool[:want.size], want), "pool differs"
+    assert np.all(gpu_pool[want.size:] == -1)
+
+
+# ------------------------------------------------------------- attention
+def check_attention(o_gpu, lse_gpu, q, rows):
+    o_ref, lse_ref = R.attend(q, rows)
+    scale = np.abs(o_ref).max()
+    err = np.abs(o_gpu - o_ref).max() / scale
+    assert err <= ATT_TOL, f"attention err {err:.3e}"
+    mag = (np.abs(q) @ np.abs(rows).T).max(axis=1)              # per head
+    ltol = LSE_ATOL + 32 * 2.0 ** -24 * mag
+    lerr = np.abs(lse_gpu - lse_ref)
+    assert np.all(lerr <= ltol), f"lse err {float(lerr.max()):.3e} (tol {float(ltol.min()):.3e})"
+    return float(err), float(lerr.max())
+
+
+def swa_rows(swa_codes, swa_scale, start, length):
+    if length <= 0:
+        return None, None
+    return swa_codes[start:start + length], swa_scale[start:start + length]
+
+
+# ------------------------------------------------------------- one step
+def check_step(step, full_scores=True, q_sample=None, entry_sample=None, seed=0):
+    """Check every layer of an executed Step (run with keep=True) against the
+    oracle, stage by stage.  full_scores=False compares scores on a sample of
+    entries only (large workloads)."""
+    wl = step.wl
+    rng = np.random.default_rng(seed)
+    cache = {k: v for k, v in step.cache.arrays().items()}
+    q_seq = host(step.q_seq)
+    n_vis = host(step.n_vis)
+    swa_start = host(step.swa_start)
+    swa_len = host(step.swa_len)
+    Q = wl.Q
+    qs = np.arange(Q) if q_sample is None else np.asarray(q_sample)
+    seqs = sorted(set(int(q_seq[q]) for q in qs))
+    # cache of the sequences involved, on the host
+    kv_c = {b: host(cache["kv_codes"][b]) for b in seqs}
+    kv_s = {b: host(cache["kv_scales"][b]) for b in seqs}
+    ik_c = {b: host(cache["ik_codes"][b]) for b in seqs}
+    ik_s = {b: host(cache["ik_scales"][b]) for b in seqs}
+    khat = {}
+    report = {}
+    for li, mode in enumerate(wl.layers):
+        L = step.layers[li]
+        q_idx = bf16_to_f64(L["q_idx"])
+        w = host(L["w"]).astype(np.float64)
+        q_att = bf16_to_f64(L["q_attn"])
+        sw_c = host(L["swa_codes"])
+        sw_s = host(L["swa_scale"]).astype(np.float64)
+        idx = host(step.idx_per_layer[li])
+        sc_gpu = host(step.scores_per_layer[li]) if step.scores_per_layer[li] is not None else None
+        if mode == "reindex":
+            pool = host(step.pool)
+            plen = host(step.pool_len)
+        for q in qs:
+            b = int(q_seq[q])
+            nv = int(n_vis[q])
+            if mode == "full":
+                s_g = sc_gpu[q, :nv]
+                if full_scores:
+                    if b not in khat:
+                        khat[b] = R.dequant_mxfp4(ik_c[b], ik_s[b])
+                    ref = R.index_scores(q_idx[q], w[q], khat[b][:nv])
+                    check_scores(s_g, ref)
+                    check_topk_tolerance(idx[q], ref, wl.k)
+                else:
+                    ent = rng.choice(nv, size=min(nv, entry_sample or 4096), replace=False)
+                    ref = R.index_scores(q_idx[q], w[q], R.dequant_mxfp4(ik_c[b][ent], ik_s[b][ent]))
+                    check_scores(s_g[ent], ref)
+                    sel = idx[q][idx[q] >= 0]
+                    ref_sel = R.index_scores(q_idx[q], w[q], R.dequant_mxfp4(ik_c[b][sel], ik_s[b][sel]))
+                    check_scores(s_g[sel], ref_sel)
+                check_topk_exact(idx[q], s_g, wl.k)
+                if wl.hierarchical:
+                    check_pool_exact(host(step.pool[q]), host(step.pool_len[q]), s_g, wl.block,
+                                     wl.n_blocks)
+            elif mode == "reindex":
+                pl = int(plen[q])
+                ids = pool[q, :pl]
+                s_g = sc_gpu[q, :pl]
+                ref = R.index_scores(q_idx[q], w[q], R.dequant_mxfp4(ik_c[b][ids], ik_s[b][ids]))
+                check_scores(s_g, ref)
+                check_topk_exact(idx[q], s_g, wl.k, ids)
+                check_topk_tolerance(idx[q], ref, wl.k, ids)
+            # attention over the GPU's own selection (a8 + a9)
+            sc, ss = swa_rows(sw_c[b], sw_s[b], int(swa_start[q]), int(swa_len[q]))
+            rows = R.gather_rows(kv_c[b], kv_s[b], idx[q], sc, ss)
+            check_attention(host(step.out[li][q]), host(step.lse[li][q]), q_att[q], rows)
+    return report

@@ -1,0 +1,116 @@
+"""The C-ABI library loads, exports every function include/csa2.h declares,
+and rejects bad arguments on the host before any HIP call (no GPU needed)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import long_context_sparse_csa2_amd as C
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "csa2.h")
+FAKE = ctypes.c_void_p(0x10000)      # aligned, never dereferenced: every call below fails validation
+
+
+def declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(csa2_[a-z_]+)\s*\(", src)))
+
+
+def test_exports_every_declared_symbol():
+    L = C.lib()
+    names = declared()
+    assert set(names) == set(C.EXPORTS)
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_status_strings():
+    L = C.lib()
+    assert L.csa2_status_string(0) == b"CSA2_OK"
+    assert L.csa2_status_string(4) == b"CSA2_EHIP"
+    assert L.csa2_status_string(99) == b"CSA2_UNKNOWN"
+
+
+def _cache(cap=100, ptr=0x10000):
+    return C._Cache(ptr, ptr, ptr, ptr, cap)
+
+
+def test_compress_validation():
+    L = C.lib()
+    cs = _cache(cap=100)
+    # null h
+    assert L.csa2_compress_quant(None, None, 1, 64, 1, FAKE, ctypes.byref(cs), 0, None) == 1
+    # T not a multiple of m
+    assert L.csa2_compress_quant(FAKE, FAKE, 1, 63, 2, FAKE, ctypes.byref(cs), 0, None) == 1
+    assert b"multiple" in L.csa2_last_error()
+    # m > 1 without logits
+    assert L.csa2_compress_quant(FAKE, None, 1, 64, 2, FAKE, ctypes.byref(cs), 0, None) == 1
+    # past the cache capacity
+    assert L.csa2_compress_quant(FAKE, None, 1, 101, 1, FAKE, ctypes.byref(cs), 0, None) == 1
+    assert L.csa2_compress_quant(FAKE, None, 1, 60, 1, FAKE, ctypes.byref(cs), 41, None) == 1
+    # misaligned cache array
+    bad = _cache(ptr=0x10004)
+    assert L.csa2_compress_quant(FAKE, None, 1, 8, 1, FAKE, ctypes.byref(bad), 0, None) == 1
+    assert b"aligned" in L.csa2_last_error()
+    # m out of range
+    assert L.csa2_compress_quant(FAKE, FAKE, 1, 34, 17, FAKE, ctypes.byref(cs), 0, None) == 1
+
+
+def test_index_score_validation():
+    L = C.lib()
+    cs = _cache(cap=100)
+    P = FAKE
+    assert L.csa2_index_score(None, P, P, P, None, 0, 1, 10, ctypes.byref(cs), P, 10, None) == 1
+    assert L.csa2_index_score(P, P, P, P, None, 0, 0, 10, ctypes.byref(cs), P, 10, None) == 1
+    assert L.csa2_index_score(P, P, P, P, None, 0, 1, 10, ctypes.byref(cs), P, 9, None) == 1
+    assert L.csa2_index_score(P, P, P, P, None, 0, 1, 101, ctypes.byref(cs), P, 101, None) == 1
+    assert L.csa2_index_score(P, P, P, P, P, 5, 1, 10, ctypes.byref(cs), P, 10, None) == 1
+    # nothing to score: returns OK without launching
+    assert L.csa2_index_score(P, P, P, P, None, 0, 1, 0, ctypes.byref(cs), P, 10, None) == 0
+
+
+def test_select_and_pool_validation():
+    L = C.lib()
+    P = FAKE
+    for k in (0, -1, 2049):
+        assert L.csa2_select_topk(P, 100, 1, P, None, 100, k, P, None, 0, None) == 1
+    assert L.csa2_select_topk(P, 100, 1, P, None, 101, 5, P, None, 0, None) == 1
+    assert L.csa2_select_topk(P, 1 << 25, 1, P, None, (1 << 24) + 1, 5, P, None, 0, None) == 1
+    # workspace needed above 16384 columns
+    assert L.csa2_select_topk(P, 20000, 1, P, None, 20000, 5, P, None, 0, None) == 3
+    need = C.csa2_workspace_bytes(C.CSA2_OP_TOPK, 1, 20000, 5)
+    assert need == 4 * 2500
+    assert L.csa2_select_topk(P, 20000, 1, P, None, 20000, 5, P, P, need - 1, None) == 3
+    assert L.csa2_block_pool(P, 100, 1, P, 100, 16, 4, P, P, P, 1 << 20, None) == 2
+    assert L.csa2_block_pool(P, 100, 1, P, 100, 8, 0, P, P, P, 1 << 20, None) == 1
+    assert L.csa2_block_pool(P, 100, 1, P, 100, 8, 4, None, P, P, 1 << 20, None) == 1
+
+
+def test_attend_validation():
+    L = C.lib()
+    cs = _cache()
+    P = FAKE
+    assert L.csa2_sparse_attend(None, P, 1, ctypes.byref(cs), P, 8, P, P, 4, P, P, P, None, None, 0, None) == 1
+    assert L.csa2_sparse_attend(P, P, 1, ctypes.byref(cs), None, 8, P, P, 4, P, P, P, None, None, 0, None) == 1
+    assert L.csa2_sparse_attend(P, P, 1, ctypes.byref(cs), P, 4096, P, P, 4, P, P, P, None, None, 0, None) == 1
+    assert L.csa2_sparse_attend(P, P, 1, ctypes.byref(cs), P, 8, None, None, 4, P, P, P, None, None, 0, None) == 1
+    assert L.csa2_sparse_attend(P, P, 0, ctypes.byref(cs), P, 8, P, P, 4, P, P, P, None, None, 0, None) == 1
+    assert L.csa2_sparse_attend(P, P, 1, None, P, 8, P, P, 4, P, P, P, None, None, 0, None) == 1
+
+
+def test_workspace_sizes():
+    # top-k / pool: the 8-way maxima levels up to the first one with <= 16384 groups
+    n = 1 << 20
+    assert C.csa2_workspace_bytes(C.CSA2_OP_TOPK, 4, n, 512) == 4 * 4 * (n // 8 + n // 64)
+    assert C.csa2_workspace_bytes(C.CSA2_OP_TOPK, 4, 16384, 512) == 0
+    assert C.csa2_workspace_bytes(C.CSA2_OP_POOL, 4, 16384, 2048) == 4 * 4 * 2048
+    # attention: partial (max, sum, O) per split for small batches, none for large
+    assert C.csa2_workspace_bytes(C.CSA2_OP_ATTEND, 4, 0, 512) > 0
+    assert C.csa2_workspace_bytes(C.CSA2_OP_ATTEND, 4096, 0, 512) == 0
+
+
+def test_selftest_counter_query():
+    assert C.lib().csa2_selftest(None, 0, None) == 6

@@ -1,0 +1,257 @@
+"""Per-operation parity of the HIP kernels against the fp64 oracle, through
+the C ABI, at sizes the oracle finishes in seconds (several tiles plus a
+ragged tail) and on the edge cases (empty, ragged, ties, k > n, masked rows,
+empty SWA window, split and unsplit attention)."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import long_context_sparse_csa2_amd as C
+from long_context_sparse_csa2_amd import synth
+from oracle import csa2_ref as R
+from oracle import formats as F
+from tests import checks
+
+pytestmark = pytest.mark.gpu
+DEV = torch.device("cuda:0")
+
+
+def _latents(B, T, seed, scale_rows=True):
+    g = torch.Generator().manual_seed(seed)
+    h = torch.randn(B, T, 512, generator=g)
+    if scale_rows:   # spread magnitudes over many binades to exercise every scale code
+        h = h * torch.exp(torch.empty(B, T, 1).uniform_(-9, 6, generator=g))
+    z = torch.randn(B, T, 512, generator=g) * 2
+    return h.to(torch.bfloat16), z.to(torch.bfloat16)
+
+
+def _build(B, T, m, seed):
+    h, z = _latents(B, T, seed)
+    w = (torch.randn(128, 512, generator=torch.Generator().manual_seed(seed + 7)) / math.sqrt(512)).to(torch.bfloat16)
+    cache = C.Cache(B, T // m, DEV)
+    C.csa2_compress_quant(h.to(DEV), z.to(DEV) if m > 1 else None, m, w.to(DEV), cache)
+    torch.cuda.synchronize()
+    return h, z, w, cache
+
+
+def test_selftest():
+    assert C.csa2_selftest(DEV) == [0] * 6
+
+
+@pytest.mark.parametrize("m,T", [(1, 1000), (2, 2000), (4, 4 * 77)])
+def test_compress_quant(m, T):
+    B = 2
+    h, z, w, cache = _build(B, T, m, seed=10 + m)
+    w64 = checks.bf16_to_f64(w)
+    for b in range(B):
+        h64 = checks.bf16_to_f64(h[b])
+        z64 = checks.bf16_to_f64(z[b])
+        x = R.compress(h64, z64, m)
+        hmax = np.abs(h64).reshape(-1, m, 512).max(1)
+        kv_c, kv_s = checks.host(cache.kv_codes[b]), checks.host(cache.kv_scales[b])
+        checks.check_main_kv(x, m, kv_c, kv_s, hmax)
+        checks.check_indexer_k(kv_c, kv_s, w64, checks.host(cache.ik_codes[b]),
+                               checks.host(cache.ik_scales[b]))
+
+
+def test_compress_offset_and_tail():
+    # e0 offset and an entry count that is not a multiple of the 32-entry tile
+    h, z = _latents(1, 45, 3)
+    w = (torch.randn(128, 512, generator=torch.Generator().manual_seed(5)) / 22.6).to(torch.bfloat16)
+    cache = C.Cache(1, 100, DEV)
+    cache.kv_codes.fill_(0xAB)
+    C.csa2_compress_quant(h.to(DEV), None, 1, w.to(DEV), cache, e0=50)
+    torch.cuda.synchronize()
+    kv = checks.host(cache.kv_codes[0])
+    assert np.all(kv[:50] == 0xAB) and np.all(kv[95:] == 0xAB)
+    rc, rs = R.quant_main_kv(checks.bf16_to_f64(h[0]))
+    assert np.array_equal(kv[50:95], rc)
+    assert np.array_equal(checks.host(cache.kv_scales[0])[50:95], rs)
+
+
+def _scores_inputs(Q, seed):
+    g = torch.Generator().manual_seed(seed)
+    q = torch.randn(Q, 32, 128, generator=g).to(torch.bfloat16)
+    w = torch.rand(Q, 32, generator=g)
+    return q, w
+
+
+def test_index_score_full_and_pool():
+    B, T = 2, 3000
+    _, _, _, cache = _build(B, T, 1, seed=21)
+    Q = 3
+    q, w = _scores_inputs(Q, 22)
+    q_seq = torch.tensor([0, 1, 1], dtype=torch.int32)
+    n_vis = torch.tensor([3000, 2999, 1], dtype=torch.int64)
+    scores = torch.full((Q, 3008), -7.0, device=DEV)
+    C.csa2_index_score(q.to(DEV), w.to(DEV), q_seq.to(DEV), n_vis.to(DEV), None, 3000, cache, scores)
+    torch.cuda.synchronize()
+    s = checks.host(scores)
+    q64, w64 = checks.bf16_to_f64(q), w.double().numpy()
+    for i in range(Q):
+        b, nv = int(q_seq[i]), int(n_vis[i])
+        khat = R.dequant_mxfp4(checks.host(cache.ik_codes[b]), checks.host(cache.ik_scales[b]))
+        checks.check_scores(s[i, :nv], R.index_scores(q64[i], w64[i], khat[:nv]))
+        assert np.all(s[i, nv:] == -7.0)          # unscored columns untouched
+    # candidate mode (Reindex): arbitrary ascending entry ids
+    rng = np.random.default_rng(0)
+    cand = np.full((Q, 700), -1, dtype=np.int32)
+    lens = [700, 333, 0]
+    for i in range(Q):
+        cand[i, :lens[i]] = np.sort(rng.choice(2999, lens[i], replace=False))
+    ps = torch.full((Q, 700), -7.0, device=DEV)
+    C.csa2_index_score(q.to(DEV), w.to(DEV), q_seq.to(DEV), torch.tensor(lens, dtype=torch.int64).to(DEV),
+                       torch.from_numpy(cand).to(DEV), 700, cache, ps)
+    torch.cuda.synchronize()
+    p = checks.host(ps)
+    for i in range(Q):
+        b = int(q_seq[i])
+        ids = cand[i, :lens[i]]
+        khat = R.dequant_mxfp4(checks.host(cache.ik_codes[b])[ids], checks.host(cache.ik_scales[b])[ids])
+        checks.check_scores(p[i, :lens[i]], R.index_scores(q64[i], w64[i], khat))
+        assert np.all(p[i, lens[i]:] == -7.0)
+
+
+def _rand_scores(Q, n, seed, ties=True):
+    rng = np.random.default_rng(seed)
+    s = (rng.standard_normal((Q, n)) ** 2).astype(np.float32)
+    if ties:
+        s[:, ::7] = np.float32(1.5)                    # many exact ties
+        s[:, 3::11] = 0.0
+        s[:, 5::13] = -0.0
+    return s
+
+
+def _topk(s, nv, k, col_ids=None):
+    Q, ld = s.shape
+    n_cols = int(max(nv)) if len(nv) else 0
+    ws = C.workspace(C.CSA2_OP_TOPK, Q, n_cols, k, DEV)
+    out = torch.empty(Q, k, dtype=torch.int32, device=DEV)
+    C.csa2_select_topk(torch.from_numpy(s).to(DEV), torch.tensor(nv, dtype=torch.int64).to(DEV),
+                       None if col_ids is None else torch.from_numpy(col_ids).to(DEV), n_cols, k,
+                       out, ws)
+    torch.cuda.synchronize()
+    return checks.host(out)
+
+
+@pytest.mark.parametrize("n,k", [(1, 1), (100, 512), (511, 512), (512, 512), (513, 512),
+                                 (5000, 7), (20000, 512), (70000, 2048), (200000, 512)])
+def test_select_topk(n, k):
+    Q = 3
+    s = _rand_scores(Q, n, seed=n + k)
+    nv = [n, max(0, n - 5), n // 2]
+    out = _topk(s, nv, k)
+    for i in range(Q):
+        checks.check_topk_exact(out[i], s[i, :nv[i]], k)
+
+
+def test_select_topk_all_equal_and_empty():
+    s = np.zeros((2, 3000), np.float32)
+    out = _topk(s, [3000, 0], 512)
+    assert np.array_equal(out[0], np.arange(512))
+    assert np.all(out[1] == -1)
+
+
+def test_select_topk_col_ids():
+    Q, n = 2, 16384
+    rng = np.random.default_rng(3)
+    s = _rand_scores(Q, n, seed=4)
+    ids = np.stack([np.sort(rng.choice(1 << 20, n, replace=False)) for _ in range(Q)]).astype(np.int32)
+    nv = [n, 9000]
+    out = _topk(s, nv, 512, ids)
+    for i in range(Q):
+        checks.check_topk_exact(out[i], s[i, :nv[i]], 512, ids[i, :nv[i]])
+
+
+@pytest.mark.parametrize("n", [3, 2048, 16384 + 3, 16384 * 8 + 5, 300000])
+def test_block_pool(n):
+    Q = 2
+    s = _rand_scores(Q, n, seed=n)
+    nv = [n, max(1, n - 9)]
+    ws = C.workspace(C.CSA2_OP_POOL, Q, n, 2048, DEV)
+    pool = torch.empty(Q, 16384, dtype=torch.int32, device=DEV)
+    plen = torch.empty(Q, dtype=torch.int64, device=DEV)
+    C.csa2_block_pool(torch.from_numpy(s).to(DEV), torch.tensor(nv, dtype=torch.int64).to(DEV), n,
+                      2048, pool, plen, ws)
+    torch.cuda.synchronize()
+    for i in range(Q):
+        checks.check_pool_exact(checks.host(pool[i]), checks.host(plen[i]), s[i, :nv[i]], 8, 2048)
+
+
+def _swa(nseq, T_swa, seed):
+    g = torch.Generator().manual_seed(seed)
+    lat = torch.randn(nseq, T_swa, 512, generator=g)
+    scale = lat.abs().amax(2) / 448
+    codes = (lat / scale[..., None]).to(torch.float8_e4m3fn).view(torch.uint8)
+    return codes, scale
+
+
+@pytest.mark.parametrize("Q,k", [(2, 512), (3, 100), (300, 64)])
+def test_sparse_attend(Q, k):
+    B, N = 2, 1500
+    _, _, _, cache = _build(B, N, 1, seed=31 + Q)
+    rng = np.random.default_rng(Q)
+    g = torch.Generator().manual_seed(Q)
+    q = (torch.randn(Q, 64, 512, generator=g) / math.sqrt(512)).to(torch.bfloat16)
+    q_seq = rng.integers(0, B, Q).astype(np.int32)
+    idx = np.stack([rng.choice(N, k, replace=False) for _ in range(Q)]).astype(np.int32)
+    idx[0, ::5] = -1                                  # masked selections
+    T_swa = 200
+    swa_c, swa_s = _swa(B, T_swa, 9)
+    start = rng.integers(0, T_swa - 128, Q).astype(np.int64)
+    slen = rng.integers(0, 129, Q).astype(np.int32)
+    slen[0] = 128
+    slen[-1] = 0                                      # no window at all
+    out = torch.empty(Q, 64, 512, device=DEV)
+    lse = torch.empty(Q, 64, device=DEV)
+    ws = C.workspace(C.CSA2_OP_ATTEND, Q, 0, k, DEV)
+    C.csa2_sparse_attend(q.to(DEV), torch.from_numpy(q_seq).to(DEV), cache, torch.from_numpy(idx).to(DEV),
+                         swa_c.to(DEV), swa_s.to(DEV), torch.from_numpy(start).to(DEV),
+                         torch.from_numpy(slen).to(DEV), out, lse, ws)
+    torch.cuda.synchronize()
+    o, l = checks.host(out), checks.host(lse)
+    q64 = checks.bf16_to_f64(q)
+    kv_c = checks.host(cache.kv_codes)
+    kv_s = checks.host(cache.kv_scales)
+    sc_np, ss_np = swa_c.numpy(), swa_s.double().numpy()
+    for i in range(min(Q, 40)):
+        b = q_seq[i]
+        rows = R.gather_rows(kv_c[b], kv_s[b], idx[i], sc_np[b, start[i]:start[i] + slen[i]],
+                             ss_np[b, start[i]:start[i] + slen[i]])
+        checks.check_attention(o[i], l[i], q64[i], rows)
+
+
+def test_sparse_attend_no_rows():
+    _, _, _, cache = _build(1, 64, 1, seed=2)
+    q = torch.zeros(1, 64, 512, dtype=torch.bfloat16, device=DEV)
+    idx = torch.full((1, 8), -1, dtype=torch.int32, device=DEV)
+    out = torch.full((1, 64, 512), 5.0, device=DEV)
+    lse = torch.zeros(1, 64, device=DEV)
+    z64 = torch.zeros(1, dtype=torch.int64, device=DEV)
+    z32 = torch.zeros(1, dtype=torch.int32, device=DEV)
+    C.csa2_sparse_attend(q, z32, cache, idx, None, None, z64, z32, out, lse,
+                         C.workspace(C.CSA2_OP_ATTEND, 1, 0, 8, DEV))
+    torch.cuda.synchronize()
+    assert torch.all(out == 0) and torch.all(torch.isinf(lse)) and torch.all(lse < 0)
+
+
+def test_c0_step():
+    from long_context_sparse_csa2_amd.pipeline import Step
+    step = Step(synth.WORKLOADS["c0"], DEV)
+    step.run(keep=True)
+    torch.cuda.synchronize()
+    checks.check_step(step, full_scores=True)
+
+
+def test_determinism():
+    from long_context_sparse_csa2_amd.pipeline import Step
+    step = Step(synth.scaled(synth.WORKLOADS["c2"], B=2, T=40000), DEV)
+    step.run(keep=True)
+    a = [t.clone() for t in step.out] + [x.clone() for x in step.idx_per_layer]
+    step.run(keep=True)
+    b = list(step.out) + list(step.idx_per_layer)
+    torch.cuda.synchronize()
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
