@@ -96,6 +96,10 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default="c2", choices=sorted(synth.WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--eager", action="store_true", help="launch every call from Python "
+                    "instead of replaying the step's HIP graphs")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device copy (reference for HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
@@ -104,6 +108,15 @@ def main():
         sys.exit(2)
 
     dev = torch.device("cuda:0")
+    if args.copy_calibration:
+        n = 1 << 30
+        a = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "launches": 3}))
+        return
     wl = synth.WORKLOADS[args.config]
     print(f"[bench] building {wl.name} ({wl.note}) cache on {dev}", file=sys.stderr, flush=True)
     step = Step(wl, dev)
@@ -113,23 +126,42 @@ def main():
         step.run()
     torch.cuda.synchronize()
 
+    # eager pass with per-call events (breakdown of the step)
     events = {}
+    for _ in range(3):
+        step.run(events=events)
+    torch.cuda.synchronize()
+    per_call = {k: float(np.mean([a.elapsed_time(b) for a, b in v])) * 1e3 for k, v in events.items()}
+    calls = {k: len(v) // 3 for k, v in events.items()}
+
+    # timed region: K steps; the Full-layer scan (first call of the step) is
+    # bracketed by HIP events on the stream it runs on
+    graphs = None if args.eager else step.capture(split_first=True)
+    scan_ev = []
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0.record()
     for _ in range(args.steps):
-        step.run(events=events)
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        if graphs:
+            e0.record(); graphs[0].replay(); e1.record(); graphs[1].replay()
+        else:
+            ops = step.ops()
+            e0.record(); ops[0][2](); e1.record()
+            for _, _, fn in ops[1:]:
+                fn()
+        scan_ev.append((e0, e1))
     t1.record()
     torch.cuda.synchronize()
     ms = t0.elapsed_time(t1) / args.steps
-    per_call = {k: float(np.mean([a.elapsed_time(b) for a, b in v])) * 1e3 for k, v in events.items()}
-    calls = {k: len(v) // args.steps for k, v in events.items()}
-    print(f"[bench] {ms:.3f} ms/step; per call (us): "
+    scan_us = float(np.mean([a.elapsed_time(b) for a, b in scan_ev])) * 1e3
+    print(f"[bench] {ms:.3f} ms/step ({'eager' if graphs is None else 'graph replay'}); "
+          f"scan {scan_us:.1f} us; eager per call (us): "
           + ", ".join(f"{k}={v:.1f}x{calls[k]}" for k, v in per_call.items()), file=sys.stderr,
           flush=True)
 
-    scan_us = per_call["index_score_full"]
     scan_bytes = wl.Q * wl.N * SCAN_BYTES_PER_ENTRY
     achieved = scan_bytes / (scan_us * 1e-6) / 1e9
     traffic = None
@@ -160,7 +192,8 @@ def main():
         "roofline": roofline,
         "step_roofline": {"bytes": step_b, "us_at_peak": round(step_b / (HBM_PEAK_GBS * 1e3), 2),
                           "frac": round(step_b / (HBM_PEAK_GBS * 1e9) / (ms * 1e-3), 4)},
-        "per_call_us": {k: round(v, 2) for k, v in per_call.items()},
+        "launch": "eager" if graphs is None else "hip graph replay",
+        "per_call_us_eager": {k: round(v, 2) for k, v in per_call.items()},
         "calls_per_step": calls,
     }
     if not args.no_cpu_baseline:

@@ -174,16 +174,26 @@ csa2_status csa2_select_topk(const float* scores, int64_t ld, int Q, const int64
  * a partial last block uses its valid columns; blocks ranked by (max desc,
  * block id asc); the first min(n_blocks, #blocks) are kept.
  *
+ * The same section has that Full layer also produce the top-k of its own
+ * attention from the full scan.  With k <= n_blocks that top-k lies inside
+ * the pool (an entry outside it has n_blocks blocks ranked above its own
+ * block, each holding an entry that beats or ties it with a lower id), so
+ * the call can return it too, selected among the pool's positions, which
+ * equals csa2_select_topk over all n_valid columns.
+ *
  *   scores, ld, Q, n_valid, n_cols  as for csa2_select_topk (col_ids = identity)
  *   block     positions per block; must be 8
  *   n_blocks  1 <= n_blocks <= CSA2_MAX_K
  *   pool      [Q][n_blocks * block] int32 pooled positions, ascending, -1 padded
  *   pool_len  [Q] int64 number of valid pool entries
+ *   k         0 (no top-k) or 1 <= k <= n_blocks
+ *   topk      [Q][k] int32 top-k positions, ascending, -1 padded (NULL iff k == 0)
  *   ws        csa2_workspace_bytes(CSA2_OP_POOL, Q, n_cols, n_blocks) bytes
  */
 csa2_status csa2_block_pool(const float* scores, int64_t ld, int Q, const int64_t* n_valid,
                             int64_t n_cols, int block, int n_blocks, int32_t* pool,
-                            int64_t* pool_len, void* ws, size_t ws_bytes, void* stream);
+                            int64_t* pool_len, int k, int32_t* topk, void* ws, size_t ws_bytes,
+                            void* stream);
 
 /*
  * (4 + 5) Gather and sparse attention: steps a8 and a9.

@@ -57,7 +57,7 @@ def lib():
         L.csa2_select_topk.restype = I
         L.csa2_select_topk.argtypes = [P, I64, I, P, P, I64, I, P, P, SZ, P]
         L.csa2_block_pool.restype = I
-        L.csa2_block_pool.argtypes = [P, I64, I, P, I64, I, I, P, P, P, SZ, P]
+        L.csa2_block_pool.argtypes = [P, I64, I, P, I64, I, I, P, P, I, P, P, SZ, P]
         L.csa2_sparse_attend.restype = I
         L.csa2_sparse_attend.argtypes = [P, P, I, ctypes.POINTER(_Cache), P, I, P, P, I64, P, P,
                                          P, P, P, SZ, P]
@@ -171,14 +171,17 @@ def csa2_select_topk(scores, n_valid, col_ids, n_cols, k, out, ws=None, stream=N
 
 
 def csa2_block_pool(scores, n_valid, n_cols, n_blocks, pool, pool_len, ws=None, block=8,
-                    stream=None):
-    """pool [Q, n_blocks * block] i32, pool_len [Q] i64."""
+                    topk=None, stream=None):
+    """pool [Q, n_blocks * block] i32, pool_len [Q] i64; topk None or
+    [Q, k] i32 (the Full layer's own top-k, selected inside the pool)."""
     _dtype(scores, torch.float32, "scores"); _dtype(n_valid, torch.int64, "n_valid")
     _dtype(pool, torch.int32, "pool"); _dtype(pool_len, torch.int64, "pool_len")
+    _dtype(topk, torch.int32, "topk")
     Q = scores.shape[0]
+    k = topk.shape[1] if topk is not None else 0
     wsb = ws.numel() * ws.element_size() if ws is not None else 0
     st = lib().csa2_block_pool(_ptr(scores), scores.shape[1], Q, _ptr(n_valid), n_cols, block,
-                               n_blocks, _ptr(pool), _ptr(pool_len), _ptr(ws), wsb,
+                               n_blocks, _ptr(pool), _ptr(pool_len), k, _ptr(topk), _ptr(ws), wsb,
                                _stream(stream, scores))
     _check("csa2_block_pool", st)
 

@@ -134,20 +134,23 @@ csa2_status csa2_select_topk(const float* scores, int64_t ld, int Q, const int64
   const csa2_status st = select_common(scores, ld, Q, n_valid, n_cols, k, ws, ws_bytes, 0);
   if (st != CSA2_OK) return st;
   return hip_status(csa2::launch_select(scores, ld, Q, n_valid, col_ids, n_cols, k, 0, out, k,
-                                        nullptr, ws, (hipStream_t)stream),
+                                        nullptr, 0, nullptr, ws, (hipStream_t)stream),
                     "csa2_select_topk launch");
 }
 
 csa2_status csa2_block_pool(const float* scores, int64_t ld, int Q, const int64_t* n_valid,
                             int64_t n_cols, int block, int n_blocks, int32_t* pool,
-                            int64_t* pool_len, void* ws, size_t ws_bytes, void* stream) {
+                            int64_t* pool_len, int k, int32_t* topk, void* ws, size_t ws_bytes,
+                            void* stream) {
   g_err[0] = 0;
   REQ(pool && pool_len, "pool and pool_len must not be NULL");
+  REQ(k >= 0 && k <= n_blocks, "k=%d must be in [0, n_blocks=%d]", k, n_blocks);
+  REQ(k == 0 || topk, "topk must not be NULL when k > 0");
   if (block != 8) return fail(CSA2_EUNSUPPORTED, "block=%d: only blocks of 8 positions", block);
   const csa2_status st = select_common(scores, ld, Q, n_valid, n_cols, n_blocks, ws, ws_bytes, 1);
   if (st != CSA2_OK) return st;
   return hip_status(csa2::launch_select(scores, ld, Q, n_valid, nullptr, n_cols, n_blocks, 1, pool,
-                                        (int64_t)n_blocks * 8, pool_len, ws,
+                                        (int64_t)n_blocks * 8, pool_len, k, topk, ws,
                                         (hipStream_t)stream),
                     "csa2_block_pool launch");
 }

@@ -22,7 +22,8 @@ hipError_t launch_index_score(const uint16_t* q_idx, const float* w, const int32
 size_t select_ws_bytes(int Q, int64_t n_cols, int mode);
 hipError_t launch_select(const float* scores, int64_t ld, int Q, const int64_t* n_valid,
                          const int32_t* col_ids, int64_t n_cols, int kk, int mode, int32_t* out,
-                         int64_t out_ld, int64_t* out_len, void* ws, hipStream_t stream);
+                         int64_t out_ld, int64_t* out_len, int k2, int32_t* out2, void* ws,
+                         hipStream_t stream);
 
 size_t attend_ws_bytes(int Q, int k);
 hipError_t launch_attend(const uint16_t* q, const int32_t* q_seq, int Q, const uint8_t* kv_codes,

@@ -68,47 +68,83 @@ class Step:
             self.ws_topk_pool = workspace(CSA2_OP_TOPK, Q, P, k, device)
             self.idx_r = [torch.empty(Q, k, dtype=torch.int32, device=device) for _ in wl.layers]
 
+    def ops(self):
+        """The step as an ordered list of (name, layer, thunk); each thunk
+        enqueues one C-ABI call on the current stream."""
+        wl = self.wl
+        out = []
+        idx = self.idx
+        for li, mode in enumerate(wl.layers):
+            L = self.layers[li]
+            if mode == "full":
+                out.append(("index_score_full", li, lambda L=L: csa2_index_score(
+                    L["q_idx"], L["w"], self.q_seq, self.n_vis, None, wl.N, self.cache, self.scores)))
+                if wl.hierarchical:
+                    # the pool and the layer's own top-k in one selection pass
+                    out.append(("block_pool_topk", li, lambda: csa2_block_pool(
+                        self.scores, self.n_vis, wl.N, wl.n_blocks, self.pool, self.pool_len,
+                        self.ws_pool, block=wl.block, topk=self.idx)))
+                else:
+                    out.append(("select_topk_full", li, lambda: csa2_select_topk(
+                        self.scores, self.n_vis, None, wl.N, wl.k, self.idx, self.ws_topk)))
+                idx = self.idx
+            elif mode == "reindex":
+                idx = self.idx_r[li]
+                out.append(("index_score_pool", li, lambda L=L: csa2_index_score(
+                    L["q_idx"], L["w"], self.q_seq, self.pool_len, self.pool, self.P, self.cache,
+                    self.pool_scores)))
+                out.append(("select_topk_pool", li, lambda idx=idx: csa2_select_topk(
+                    self.pool_scores, self.pool_len, self.pool, self.P, wl.k, idx,
+                    self.ws_topk_pool)))
+            out.append(("sparse_attend", li, lambda L=L, li=li, idx=idx: csa2_sparse_attend(
+                L["q_attn"], self.q_seq, self.cache, idx, L["swa_codes"], L["swa_scale"],
+                self.swa_start, self.swa_len, self.out[li], self.lse[li], self.ws_attend)))
+        return out
+
     def run(self, keep=False, events=None):
         """Enqueue every layer of the step.  keep=True also keeps each
         layer's indices and scores (for checking).  `events`, a dict, gets
         (start, end) torch.cuda.Event pairs recorded around each call on the
         current stream, keyed by call name."""
         wl = self.wl
-        idx = self.idx
-
-        def timed(name, fn, *a, **kw):
+        for name, li, fn in self.ops():
             if events is None:
-                return fn(*a, **kw)
-            e0 = torch.cuda.Event(enable_timing=True)
-            e1 = torch.cuda.Event(enable_timing=True)
-            e0.record()
-            fn(*a, **kw)
-            e1.record()
-            events.setdefault(name, []).append((e0, e1))
-
-        for li, mode in enumerate(wl.layers):
-            L = self.layers[li]
-            if mode == "full":
-                timed("index_score_full", csa2_index_score, L["q_idx"], L["w"], self.q_seq,
-                      self.n_vis, None, wl.N, self.cache, self.scores)
-                if wl.hierarchical:
-                    timed("block_pool", csa2_block_pool, self.scores, self.n_vis, wl.N,
-                          wl.n_blocks, self.pool, self.pool_len, self.ws_pool, block=wl.block)
-                timed("select_topk_full", csa2_select_topk, self.scores, self.n_vis, None, wl.N,
-                      wl.k, self.idx, self.ws_topk)
-                idx = self.idx
-            elif mode == "reindex":
-                idx = self.idx_r[li]
-                timed("index_score_pool", csa2_index_score, L["q_idx"], L["w"], self.q_seq,
-                      self.pool_len, self.pool, self.P, self.cache, self.pool_scores)
-                timed("select_topk_pool", csa2_select_topk, self.pool_scores, self.pool_len,
-                      self.pool, self.P, wl.k, idx, self.ws_topk_pool)
-            if keep:
-                self.idx_per_layer[li] = idx.clone()
+                fn()
+            else:
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                e0.record()
+                fn()
+                e1.record()
+                events.setdefault(name, []).append((e0, e1))
+            if keep and name == "sparse_attend":
+                mode = wl.layers[li]
+                self.idx_per_layer[li] = (self.idx_r[li] if mode == "reindex" else self.idx).clone()
                 if mode == "full":
                     self.scores_per_layer[li] = self.scores.clone()
                 elif mode == "reindex":
                     self.scores_per_layer[li] = self.pool_scores.clone()
-            timed("sparse_attend", csa2_sparse_attend, L["q_attn"], self.q_seq, self.cache, idx,
-                  L["swa_codes"], L["swa_scale"], self.swa_start, self.swa_len, self.out[li],
-                  self.lse[li], self.ws_attend)
+
+    def capture(self, split_first=True):
+        """Capture the step into HIP graphs: [first call] and [the rest]
+        (split_first) or one graph.  Returns the list of graphs; replaying
+        them in order is one step."""
+        ops = self.ops()
+        groups = [ops[:1], ops[1:]] if split_first else [ops]
+        graphs = []
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            for grp in groups:              # one eager pass on the capture stream first
+                for _, _, fn in grp:
+                    fn()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        for grp in groups:
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                for _, _, fn in grp:
+                    fn()
+            graphs.append(g)
+        torch.cuda.synchronize()
+        return graphs

@@ -84,9 +84,12 @@ def test_select_and_pool_validation():
     need = C.csa2_workspace_bytes(C.CSA2_OP_TOPK, 1, 20000, 5)
     assert need == 4 * 2500
     assert L.csa2_select_topk(P, 20000, 1, P, None, 20000, 5, P, P, need - 1, None) == 3
-    assert L.csa2_block_pool(P, 100, 1, P, 100, 16, 4, P, P, P, 1 << 20, None) == 2
-    assert L.csa2_block_pool(P, 100, 1, P, 100, 8, 0, P, P, P, 1 << 20, None) == 1
-    assert L.csa2_block_pool(P, 100, 1, P, 100, 8, 4, None, P, P, 1 << 20, None) == 1
+    assert L.csa2_block_pool(P, 100, 1, P, 100, 16, 4, P, P, 0, None, P, 1 << 20, None) == 2
+    assert L.csa2_block_pool(P, 100, 1, P, 100, 8, 0, P, P, 0, None, P, 1 << 20, None) == 1
+    assert L.csa2_block_pool(P, 100, 1, P, 100, 8, 4, None, P, 0, None, P, 1 << 20, None) == 1
+    # fused top-k: k above the block count, or no output buffer
+    assert L.csa2_block_pool(P, 100, 1, P, 100, 8, 4, P, P, 5, P, P, 1 << 20, None) == 1
+    assert L.csa2_block_pool(P, 100, 1, P, 100, 8, 4, P, P, 3, None, P, 1 << 20, None) == 1
 
 
 def test_attend_validation():

@@ -173,11 +173,30 @@ def test_block_pool(n):
     ws = C.workspace(C.CSA2_OP_POOL, Q, n, 2048, DEV)
     pool = torch.empty(Q, 16384, dtype=torch.int32, device=DEV)
     plen = torch.empty(Q, dtype=torch.int64, device=DEV)
+    topk = torch.empty(Q, 512, dtype=torch.int32, device=DEV)
     C.csa2_block_pool(torch.from_numpy(s).to(DEV), torch.tensor(nv, dtype=torch.int64).to(DEV), n,
-                      2048, pool, plen, ws)
+                      2048, pool, plen, ws, topk=topk)
     torch.cuda.synchronize()
     for i in range(Q):
         checks.check_pool_exact(checks.host(pool[i]), checks.host(plen[i]), s[i, :nv[i]], 8, 2048)
+        checks.check_topk_exact(checks.host(topk[i]), s[i, :nv[i]], 512)
+
+
+def test_block_pool_small_blocks_and_topk():
+    # few blocks, k equal to the block count, heavy ties
+    Q, n = 2, 5000
+    s = _rand_scores(Q, n, seed=77)
+    s[1, :] = 2.0
+    ws = C.workspace(C.CSA2_OP_POOL, Q, n, 64, DEV)
+    pool = torch.empty(Q, 64 * 8, dtype=torch.int32, device=DEV)
+    plen = torch.empty(Q, dtype=torch.int64, device=DEV)
+    topk = torch.empty(Q, 64, dtype=torch.int32, device=DEV)
+    C.csa2_block_pool(torch.from_numpy(s).to(DEV), torch.tensor([n, n], dtype=torch.int64).to(DEV),
+                      n, 64, pool, plen, ws, topk=topk)
+    torch.cuda.synchronize()
+    for i in range(Q):
+        checks.check_pool_exact(checks.host(pool[i]), checks.host(plen[i]), s[i], 8, 64)
+        checks.check_topk_exact(checks.host(topk[i]), s[i], 64)
 
 
 def _swa(nseq, T_swa, seed):
@@ -255,3 +274,25 @@ def test_determinism():
     torch.cuda.synchronize()
     for x, y in zip(a, b):
         assert torch.equal(x, y)
+
+
+def test_graph_replay_matches_eager():
+    """The step captured as HIP graphs (as bench.py replays it) gives the
+    eager result on every replay, with eager work in between."""
+    from long_context_sparse_csa2_amd.pipeline import Step
+    step = Step(synth.scaled(synth.WORKLOADS["c2"], B=2, T=50000), DEV)
+    step.run()
+    torch.cuda.synchronize()
+    ref = [t.clone() for t in step.out] + [step.pool.clone(), step.idx.clone()]
+    graphs = step.capture(split_first=True)
+    for rep in range(3):
+        for t in step.out:
+            t.zero_()                     # eager work between replays
+        step.pool.fill_(-5)
+        torch.cuda.synchronize()
+        for g in graphs:
+            g.replay()
+        torch.cuda.synchronize()
+        got = list(step.out) + [step.pool, step.idx]
+        for a, b in zip(ref, got):
+            assert torch.equal(a, b), f"replay {rep} differs"
