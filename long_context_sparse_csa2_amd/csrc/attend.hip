@@ -168,21 +168,13 @@ __global__ __launch_bounds__(256) void k_attend(
         const int64_t r0 = off0 >= 0 ? off0 : seq * T_swa + sst;
         const int64_t r1 = off1 >= 0 ? off1 : seq * T_swa + sst;
         const float g0 = rowsig[2 * rp], g1 = rowsig[2 * rp + 1];
-        const uint32_t* c0p = (const uint32_t*)(swa_codes + r0 * 512 + db * 64);
-        const uint32_t* c1p = (const uint32_t*)(swa_codes + r1 * 512 + db * 64);
-#pragma unroll 2
-        for (int i = 0; i < 8; ++i) {              // 8 dims = two words per step
-          const uint32_t x0l = c0p[2 * i], x0h = c0p[2 * i + 1];
-          const uint32_t x1l = c1p[2 * i], x1h = c1p[2 * i + 1];
-          f16x8_t y0, y1;
+        const u32x4_t* c0p = (const u32x4_t*)(swa_codes + r0 * 512 + db * 64);
+        const u32x4_t* c1p = (const u32x4_t*)(swa_codes + r1 * 512 + db * 64);
 #pragma unroll
-          for (int b = 0; b < 4; ++b) {
-            y0[b] = (_Float16)(e4m3_val((x0l >> (8 * b)) & 0xFFu) * g0);
-            y0[4 + b] = (_Float16)(e4m3_val((x0h >> (8 * b)) & 0xFFu) * g0);
-            y1[b] = (_Float16)(e4m3_val((x1l >> (8 * b)) & 0xFFu) * g1);
-            y1[4 + b] = (_Float16)(e4m3_val((x1h >> (8 * b)) & 0xFFu) * g1);
-          }
-          put8(8 * i, y0, y1);
+        for (int i2 = 0; i2 < 4; ++i2) {           // 16 dims per 16-byte load
+          const u32x4_t x0 = c0p[i2], x1 = c1p[i2];
+          put8(16 * i2, fp8x8_to_f16_scaled(x0[0], x0[1], g0), fp8x8_to_f16_scaled(x1[0], x1[1], g1));
+          put8(16 * i2 + 8, fp8x8_to_f16_scaled(x0[2], x0[3], g0), fp8x8_to_f16_scaled(x1[2], x1[3], g1));
         }
       }
     }
@@ -279,32 +271,47 @@ __global__ __launch_bounds__(256) void k_attend(
 }
 
 // Merge the per-split partial states of one (query, head) by log-sum-exp.
+// Every split wrote its state (an empty split: max -inf, sum 0, O = 0), so
+// the weighted sum runs without branches and its loads overlap.
+constexpr int AT_MAX_SPLITS = 64;
+
 __global__ __launch_bounds__(128) void k_attend_combine(const float* __restrict__ part_o,
                                                         const float* __restrict__ part_ml,
                                                         int nsplit, float* __restrict__ out,
                                                         float* __restrict__ lse) {
+  __shared__ float wgt[AT_MAX_SPLITS];
+  __shared__ float sums[2];
   const int qh = blockIdx.x;              // q * 64 + head
   const int q = qh / H_ATT, h = qh % H_ATT;
-  float M = -INFINITY;
-  for (int s = 0; s < nsplit; ++s) {
-    const int64_t slot = ((int64_t)q * nsplit + s) * H_ATT + h;
-    if (part_ml[2 * slot + 1] > 0.f) M = fmaxf(M, part_ml[2 * slot]);
+  const int tid = threadIdx.x;
+  float m = -INFINITY, l = 0.f;
+  if (tid < nsplit) {
+    const int64_t slot = ((int64_t)q * nsplit + tid) * H_ATT + h;
+    m = part_ml[2 * slot];
+    l = part_ml[2 * slot + 1];
+    if (!(l > 0.f)) m = -INFINITY;
   }
-  float L = 0.f;
+  float M = m;                            // max over the first wave (nsplit <= 64)
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
+  const float wv = (tid < nsplit && l > 0.f) ? expf(m - M) : 0.f;
+  float L = l * wv;
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) L += __shfl_xor(L, off);
+  if (tid < AT_MAX_SPLITS) wgt[tid] = wv;
+  if (tid == 0) { sums[0] = M; sums[1] = L; }
+  __syncthreads();
+  M = sums[0];
+  L = sums[1];
   f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-  const int d0 = threadIdx.x * 4;
-  for (int s = 0; s < nsplit; ++s) {
-    const int64_t slot = ((int64_t)q * nsplit + s) * H_ATT + h;
-    const float l = part_ml[2 * slot + 1];
-    if (!(l > 0.f)) continue;
-    const float wgt = expf(part_ml[2 * slot] - M);
-    L += l * wgt;
-    const f32x4_t v = *(const f32x4_t*)(part_o + slot * D_LAT + d0);
-    acc += v * wgt;
-  }
+  const int d0 = tid * 4;
+  const float* op = part_o + (((int64_t)q * nsplit) * H_ATT + h) * D_LAT + d0;
+  const int64_t sstride = (int64_t)H_ATT * D_LAT;
+#pragma unroll 8
+  for (int s2 = 0; s2 < nsplit; ++s2) acc += *(const f32x4_t*)(op + s2 * sstride) * wgt[s2];
   const float inv = L > 0.f ? 1.f / L : 0.f;
   *(f32x4_t*)(out + (int64_t)qh * D_LAT + d0) = acc * inv;
-  if (lse && threadIdx.x == 0) lse[qh] = L > 0.f ? M + logf(L) : -INFINITY;
+  if (lse && tid == 0) lse[qh] = L > 0.f ? M + logf(L) : -INFINITY;
 }
 
 // ------------------------------------------------------------ host side
@@ -316,6 +323,7 @@ static void attend_plan(int Q, int k, int& nsplit, int& cps) {
   cps = (nch + want - 1) / want;
   if (cps < 1) cps = 1;
   nsplit = (nch + cps - 1) / cps;
+  while (nsplit > AT_MAX_SPLITS) { ++cps; nsplit = (nch + cps - 1) / cps; }
   if (nsplit < 1) nsplit = 1;
 }
 

@@ -143,14 +143,31 @@ __device__ __forceinline__ float fp4_scaled_soft(uint32_t w, int i, float scale)
   return e2m1_val((w >> (4 * i)) & 15u) * scale;
 }
 
-// Eight E4M3FN bytes (two words, byte 0 first) to bf16 (exact).
+// Eight E4M3FN bytes (two words, byte 0 first) to bf16 with the gfx950 FP8
+// conversion at scale 1 (exact: every E4M3FN value is a bf16 value).
 __device__ __forceinline__ bf16x8_t fp8x8_to_bf16(uint32_t lo, uint32_t hi) {
+  const bf16x2_t p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, false);
+  const bf16x2_t p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, true);
+  const bf16x2_t p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, false);
+  const bf16x2_t p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, true);
   bf16x8_t r;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    r[i] = __builtin_bit_cast(__bf16, bf16_bits_exact(e4m3_val((lo >> (8 * i)) & 0xFFu)));
-    r[4 + i] = __builtin_bit_cast(__bf16, bf16_bits_exact(e4m3_val((hi >> (8 * i)) & 0xFFu)));
-  }
+  r[0] = p0[0]; r[1] = p0[1]; r[2] = p1[0]; r[3] = p1[1];
+  r[4] = p2[0]; r[5] = p2[1]; r[6] = p3[0]; r[7] = p3[1];
+  return r;
+}
+
+// Eight E4M3FN bytes times an fp32 scale to fp16: decoded to fp32 at scale
+// 1 (exact), multiplied in fp32, rounded once to fp16.
+__device__ __forceinline__ f16x8_t fp8x8_to_f16_scaled(uint32_t lo, uint32_t hi, float scale) {
+  const f32x2_t p0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(lo, 1.0f, false);
+  const f32x2_t p1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(lo, 1.0f, true);
+  const f32x2_t p2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(hi, 1.0f, false);
+  const f32x2_t p3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(hi, 1.0f, true);
+  f16x8_t r;
+  r[0] = (_Float16)(p0[0] * scale); r[1] = (_Float16)(p0[1] * scale);
+  r[2] = (_Float16)(p1[0] * scale); r[3] = (_Float16)(p1[1] * scale);
+  r[4] = (_Float16)(p2[0] * scale); r[5] = (_Float16)(p2[1] * scale);
+  r[6] = (_Float16)(p3[0] * scale); r[7] = (_Float16)(p3[1] * scale);
   return r;
 }
 
@@ -167,6 +184,33 @@ __device__ __forceinline__ f32x4_t mfma16_bf16(bf16x8_t a, bf16x8_t b, f32x4_t c
 }
 __device__ __forceinline__ f32x4_t mfma16_f16(f16x8_t a, f16x8_t b, f32x4_t c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+
+// ------------------------------------------------------------ wave scans
+// Inclusive scan over the 64 lanes of a wave with DPP: Hillis-Steele shifts
+// inside each 16-lane row, then the row_bcast:15 / row_bcast:31 steps carry
+// the row totals across rows.  `ident` is the identity of `op`.  Must be
+// called with every lane active.
+template <typename Op>
+__device__ __forceinline__ uint32_t wave_scan_dpp(uint32_t v, Op op, uint32_t ident) {
+  v = op(v, (uint32_t)__builtin_amdgcn_update_dpp((int)ident, (int)v, 0x111, 0xf, 0xf, false));
+  v = op(v, (uint32_t)__builtin_amdgcn_update_dpp((int)ident, (int)v, 0x112, 0xf, 0xf, false));
+  v = op(v, (uint32_t)__builtin_amdgcn_update_dpp((int)ident, (int)v, 0x114, 0xf, 0xf, false));
+  v = op(v, (uint32_t)__builtin_amdgcn_update_dpp((int)ident, (int)v, 0x118, 0xf, 0xf, false));
+  v = op(v, (uint32_t)__builtin_amdgcn_update_dpp((int)ident, (int)v, 0x142, 0xa, 0xf, false));
+  v = op(v, (uint32_t)__builtin_amdgcn_update_dpp((int)ident, (int)v, 0x143, 0xc, 0xf, false));
+  return v;
+}
+struct OpAdd { __device__ uint32_t operator()(uint32_t a, uint32_t b) const { return a + b; } };
+struct OpMax { __device__ uint32_t operator()(uint32_t a, uint32_t b) const { return a > b ? a : b; } };
+struct OpMin { __device__ uint32_t operator()(uint32_t a, uint32_t b) const { return a < b ? a : b; } };
+
+__device__ __forceinline__ uint32_t wave_incl_sum(uint32_t v) { return wave_scan_dpp(v, OpAdd(), 0u); }
+__device__ __forceinline__ uint32_t wave_max_all(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_readlane((int)wave_scan_dpp(v, OpMax(), 0u), 63);
+}
+__device__ __forceinline__ uint32_t wave_min_all(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_readlane((int)wave_scan_dpp(v, OpMin(), 0xFFFFFFFFu), 63);
 }
 
 // ------------------------------------------------------------ score keys

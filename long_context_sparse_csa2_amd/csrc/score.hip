@@ -24,16 +24,17 @@
 namespace csa2 {
 
 constexpr int SC_WAVES = 4;
-constexpr int SC_TPW = 8;                              // 32-entry tiles per wave
-constexpr int SC_COLS = SC_WAVES * SC_TPW * 32;        // columns per workgroup
 
-template <bool CAND>
+// TPW: 32-entry tiles per wave; DEPTH: tiles whose bytes are in flight ahead
+// of the one being multiplied.
+template <bool CAND, int TPW, int DEPTH>
 __global__ __launch_bounds__(256) void k_index_score(
     const uint16_t* __restrict__ q_idx, const float* __restrict__ w,
     const int32_t* __restrict__ q_seq, const int64_t* __restrict__ n_vis,
     const int32_t* __restrict__ cand, int64_t ld_cand, int64_t nchunk, int64_t n_cols,
     const uint8_t* __restrict__ ik_codes, const uint8_t* __restrict__ ik_scales, int64_t cap,
     float* __restrict__ scores, int64_t ld) {
+  constexpr int SC_COLS = SC_WAVES * TPW * 32;        // columns per workgroup
   const int q = (int)(blockIdx.x / nchunk);
   const int64_t cbase = (int64_t)(blockIdx.x % nchunk) * SC_COLS;
   const int64_t nv0 = n_vis[q];
@@ -66,18 +67,28 @@ __global__ __launch_bounds__(256) void k_index_score(
     scw = *(const uint32_t*)(ik_scales + (seq_base + e) * 4);
   };
 
-  u32x4_t n0, n1;
-  uint32_t nsc;
-  int64_t col0 = cbase + (int64_t)wave * 32;
-  if (col0 < nv) load(col0, n0, n1, nsc);
-#pragma unroll 1
-  for (int t = 0; t < SC_TPW; ++t) {
+  // ring of DEPTH + 1 tiles: slot t % (DEPTH + 1) holds tile t
+  u32x4_t r0[DEPTH + 1], r1[DEPTH + 1];
+  uint32_t rs[DEPTH + 1];
+  const int64_t step = SC_WAVES * 32;
+  const int64_t col_first = cbase + (int64_t)wave * 32;
+#pragma unroll
+  for (int t = 0; t < DEPTH; ++t) {
+    const int64_t c0 = col_first + t * step;
+    if (t < TPW && c0 < nv) load(c0, r0[t], r1[t], rs[t]);
+  }
+#pragma unroll
+  for (int t = 0; t < TPW; ++t) {
+    const int64_t col0 = col_first + t * step;
     if (col0 >= nv) break;
-    const u32x4_t c0 = n0, c1 = n1;
-    const uint32_t scw = nsc;
-    const int64_t nxt = col0 + SC_WAVES * 32;
-    if (t + 1 < SC_TPW && nxt < nv) load(nxt, n0, n1, nsc);
-
+    {
+      const int tn = t + DEPTH;
+      const int64_t cn = col_first + tn * step;
+      if (tn < TPW && cn < nv) load(cn, r0[tn % (DEPTH + 1)], r1[tn % (DEPTH + 1)], rs[tn % (DEPTH + 1)]);
+    }
+    const int sl = t % (DEPTH + 1);
+    const u32x4_t c0 = r0[sl], c1 = r1[sl];
+    const uint32_t scw = rs[sl];
     const float s_lo = e8m0_val((scw >> (16 * half)) & 0xFFu);
     const float s_hi = e8m0_val((scw >> (16 * half + 8)) & 0xFFu);
     f32x16_t acc = {};
@@ -95,22 +106,39 @@ __global__ __launch_bounds__(256) void k_index_score(
     part += __shfl_xor(part, 32);
     const int64_t c = col0 + r;
     if (half == 0 && c < nv) srow[c] = part;
-    col0 = nxt;
   }
+}
+
+template <bool CAND, int TPW, int DEPTH>
+static void launch_variant(dim3 grid, hipStream_t stream, const uint16_t* q_idx, const float* w,
+                           const int32_t* q_seq, const int64_t* n_vis, const int32_t* cand,
+                           int64_t ld_cand, int64_t nchunk, int64_t n_cols,
+                           const uint8_t* ik_codes, const uint8_t* ik_scales, int64_t cap,
+                           float* scores, int64_t ld) {
+  hipLaunchKernelGGL((k_index_score<CAND, TPW, DEPTH>), grid, dim3(256), 0, stream, q_idx, w,
+                     q_seq, n_vis, cand, ld_cand, nchunk, n_cols, ik_codes, ik_scales, cap, scores,
+                     ld);
 }
 
 hipError_t launch_index_score(const uint16_t* q_idx, const float* w, const int32_t* q_seq,
                               const int64_t* n_vis, const int32_t* cand, int64_t ld_cand, int Q,
                               int64_t n_cols, const uint8_t* ik_codes, const uint8_t* ik_scales,
                               int64_t cap, float* scores, int64_t ld, hipStream_t stream) {
-  const int64_t nchunk = (n_cols + SC_COLS - 1) / SC_COLS;
+  // long scans: 32 tiles per wave (4096 columns per workgroup) with two tiles
+  // in flight; short ones (a Reindex pool): one tile per wave, for more
+  // workgroups in flight (both measured best on MI355X)
+  const bool long_scan = n_cols * Q >= (int64_t)1 << 22;
+  const int tpw = long_scan ? 32 : 1;
+  const int64_t cols = (int64_t)SC_WAVES * tpw * 32;
+  const int64_t nchunk = (n_cols + cols - 1) / cols;
   const dim3 grid((unsigned)(nchunk * Q));
-  if (cand)
-    hipLaunchKernelGGL(k_index_score<true>, grid, dim3(256), 0, stream, q_idx, w, q_seq, n_vis,
-                       cand, ld_cand, nchunk, n_cols, ik_codes, ik_scales, cap, scores, ld);
-  else
-    hipLaunchKernelGGL(k_index_score<false>, grid, dim3(256), 0, stream, q_idx, w, q_seq, n_vis,
-                       cand, ld_cand, nchunk, n_cols, ik_codes, ik_scales, cap, scores, ld);
+  if (long_scan) {
+    if (cand) launch_variant<true, 32, 2>(grid, stream, q_idx, w, q_seq, n_vis, cand, ld_cand, nchunk, n_cols, ik_codes, ik_scales, cap, scores, ld);
+    else launch_variant<false, 32, 2>(grid, stream, q_idx, w, q_seq, n_vis, cand, ld_cand, nchunk, n_cols, ik_codes, ik_scales, cap, scores, ld);
+  } else {
+    if (cand) launch_variant<true, 1, 1>(grid, stream, q_idx, w, q_seq, n_vis, cand, ld_cand, nchunk, n_cols, ik_codes, ik_scales, cap, scores, ld);
+    else launch_variant<false, 1, 1>(grid, stream, q_idx, w, q_seq, n_vis, cand, ld_cand, nchunk, n_cols, ik_codes, ik_scales, cap, scores, ld);
+  }
   return hipGetLastError();
 }
 

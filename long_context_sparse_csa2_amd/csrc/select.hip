@@ -98,48 +98,47 @@ __global__ __launch_bounds__(256) void k_maxima(const float* __restrict__ scores
   }
 }
 
-// ------------------------------------------------------ block helpers
-// Inclusive scan of one value per thread over the 1024-thread block.
-__device__ __forceinline__ uint32_t block_incl_scan(uint32_t v, uint32_t* red) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const uint32_t y = __shfl_up(v, off);
-    if (lane >= off) v += y;
-  }
-  if (lane == 63) red[wave] = v;
-  __syncthreads();
-  uint32_t pre = 0;
-  for (int w = 0; w < wave; ++w) pre += red[w];
-  __syncthreads();
-  return v + pre;
-}
-
-__device__ __forceinline__ void block_minmax(uint32_t& mn, uint32_t& mx, uint32_t* red) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) {
-    mn = min(mn, __shfl_xor(mn, off));
-    mx = max(mx, __shfl_xor(mx, off));
-  }
-  if (lane == 0) { red[wave] = mn; red[16 + wave] = mx; }
-  __syncthreads();
-  mn = red[0];
-  mx = red[16];
-  for (int w = 1; w < SEL_THREADS / 64; ++w) { mn = min(mn, red[w]); mx = max(mx, red[16 + w]); }
-  __syncthreads();
-}
-
-// Candidates of one selection live in registers: slot i of thread t holds
-// candidate e = i * 1024 + t (valid iff e < cnt), so candidate order is
-// (slot, thread) order and every LDS access below is conflict-free.
-constexpr int SEL_PER = SEL_CAP / SEL_THREADS;     // 16 slots per thread
+// ------------------------------------------------------------ select
+// One workgroup of 1024 threads per query.  The candidates of one round
+// (at most SEL_CAP) live in registers: slot i of thread t holds candidate
+// e = 1024 i + t, so candidate order is (slot, thread) order, every LDS
+// access is conflict-free and the only per-candidate state is its key (its
+// id is recomputed from e and the parent list when needed).
+constexpr int SEL_PER = SEL_CAP / SEL_THREADS;     // 32 slots per thread
+constexpr int SEL_WAVES = SEL_THREADS / 64;
 constexpr int SEL_SMALL = 256;
+constexpr int SEL_BINS = 2048;
+constexpr int SEL_BPT = SEL_BINS / SEL_THREADS;    // histogram bins per thread
 
-// number of register slots that hold candidates (uniform over the block)
-__device__ __forceinline__ int used_slots(int cnt) { return (cnt + SEL_THREADS - 1) / SEL_THREADS; }
+struct SelShared {
+  uint32_t lists[2][SEL_KK_MAX];      // parent ids of this round / ids it keeps
+  uint32_t hist[SEL_BINS];
+  uint32_t small[SEL_SMALL];
+  uint32_t table[2][SEL_PER * SEL_WAVES];
+  uint32_t red[2][SEL_WAVES];
+  uint32_t bc[4][4];
+};
 
-// Threshold of the best kk of the cnt candidates (cnt > kk >= 1).
+// Inclusive block-wide sum; `total` gets the block total.  red must not be
+// reused by the caller until after the next barrier.
+__device__ __forceinline__ uint32_t block_scan(uint32_t v, uint32_t* red, uint32_t& total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const uint32_t incl = wave_incl_sum(v);
+  if (lane == 63) red[wave] = incl;
+  __syncthreads();
+  uint32_t pre = 0, tot = 0;
+#pragma unroll
+  for (int w = 0; w < SEL_WAVES; ++w) {
+    const uint32_t x = red[w];
+    pre += w < wave ? x : 0u;
+    tot += x;
+  }
+  total = tot;
+  return incl + pre;
+}
+
+// Threshold of the best kk of the cnt candidates (cnt > kk >= 1), given
+// their min and max keys.
 //
 // Search on the key interval [lo, hi] that holds the kk-th best key: each
 // pass bins the keys inside it by (key - lo) >> s, with s chosen so that at
@@ -148,99 +147,91 @@ __device__ __forceinline__ int used_slots(int cnt) { return (cnt + SEL_THREADS -
 // SEL_SMALL candidates their exact kk-th key is found by ranking them
 // against each other.  Result: keys above hi are in, keys inside [lo, hi]
 // are in for the first `tie_lim` of them in candidate (= id) order, keys
-// below lo are out.
-__device__ __forceinline__ void threshold_search(const uint32_t (&kr)[SEL_PER], int cnt, int kk, uint32_t* hist,
-                                 uint32_t* red, uint32_t* bc, uint32_t* small, uint32_t& lo_out,
-                                 uint32_t& hi_out, uint32_t& tie_out) {
+// below lo are out.  The histogram must be zero on entry and is left zero.
+__device__ __forceinline__ void threshold_search(const uint32_t (&kr)[SEL_PER], int cnt, int ns,
+                                                 int kk, uint32_t mn, uint32_t mx, SelShared& sh,
+                                                 uint32_t& lo_out, uint32_t& hi_out,
+                                                 uint32_t& tie_out) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int ns = used_slots(cnt);
-  uint32_t mn = 0xFFFFFFFFu, mx = 0u;
-#pragma unroll
-  for (int i = 0; i < SEL_PER; ++i) {
-    if (i >= ns) break;
-    if (i * SEL_THREADS + tid < cnt) {
-      mn = min(mn, kr[i]);
-      mx = max(mx, kr[i]);
-    }
-  }
-  block_minmax(mn, mx, red);
-
   uint32_t lo = mn, hi = mx;
   uint32_t krem = (uint32_t)kk;
   uint32_t incnt = (uint32_t)cnt;          // candidates with key in [lo, hi]
   uint32_t tie_lim;
+  int pass = 0;
   while (true) {
     if (lo == hi) { tie_lim = krem; break; }
     if (incnt <= (uint32_t)SEL_SMALL) {
       // gather the interval's keys and rank them exactly
-      if (tid == 0) bc[3] = 0u;
-      __syncthreads();
 #pragma unroll
       for (int i = 0; i < SEL_PER; ++i) {
-        if (i >= ns) break;
-        const uint32_t k = kr[i];
-        if (i * SEL_THREADS + tid < cnt && k >= lo && k <= hi) small[atomicAdd(&bc[3], 1u)] = k;
+        if (i < ns) {
+          const uint32_t k = kr[i];
+          if (i * SEL_THREADS + tid < cnt && k >= lo && k <= hi)
+            sh.small[atomicAdd(&sh.bc[3][3], 1u)] = k;
+        }
       }
       __syncthreads();
       if (tid < (int)incnt) {
-        const uint32_t mine = small[tid];
+        const uint32_t mine = sh.small[tid];
         uint32_t gt = 0, ge = 0;
         for (uint32_t j = 0; j < incnt; ++j) {
-          const uint32_t o = small[j];
+          const uint32_t o = sh.small[j];
           gt += o > mine;
           ge += o >= mine;
         }
-        if (gt < krem && ge >= krem) { bc[0] = mine; bc[1] = gt; }
+        if (gt < krem && ge >= krem) { sh.bc[2][0] = mine; sh.bc[2][1] = gt; }
       }
       __syncthreads();
-      const uint32_t t = bc[0], g = bc[1];
-      __syncthreads();
+      const uint32_t t = sh.bc[2][0], g = sh.bc[2][1];
+      if (tid == 0) sh.bc[3][3] = 0u;     // gather counter; next used after further barriers
       lo = hi = t;
       tie_lim = krem - g;
       break;
     }
     const uint32_t span = hi - lo;                                   // range - 1
     const int bits = 32 - __clz(span);
-    const int sh = bits > 11 ? bits - 11 : 0;
-    hist[tid] = 0u;
-    hist[tid + SEL_THREADS] = 0u;
-    __syncthreads();
+    const int shf = bits > 11 ? bits - 11 : 0;
 #pragma unroll
     for (int i = 0; i < SEL_PER; ++i) {
-      if (i >= ns) break;
-      const uint32_t k = kr[i];
-      const bool in = i * SEL_THREADS + tid < cnt && k >= lo && k <= hi;
-      const uint32_t bin = (k - lo) >> sh;
-      // lanes of a wave that share one bin (concentrated scores) add once
-      const uint64_t act = __ballot(in);
-      if (act) {
-        const int first = __ffsll((long long)act) - 1;
-        const uint32_t b0 = __builtin_amdgcn_readlane(bin, first);
-        const uint64_t same = __ballot(in && bin == b0);
-        if (same == act) {
-          if (lane == first) atomicAdd(&hist[b0], (uint32_t)__popcll(act));
-        } else if (in) {
-          atomicAdd(&hist[bin], 1u);
-        }
+      if (i < ns) {
+        const uint32_t k = kr[i];
+        const bool in = i * SEL_THREADS + tid < cnt && k >= lo && k <= hi;
+        if (in) atomicAdd(&sh.hist[(k - lo) >> shf], 1u);
       }
     }
     __syncthreads();
-    // thread t owns bins 2047-2t (hi) and 2046-2t (lo); counts from the top
-    const int bh = 2047 - 2 * tid, bl = bh - 1;
-    const uint32_t hh = hist[bh], hl = hist[bl];
-    const uint32_t incl = block_incl_scan(hh + hl, red);
-    const uint32_t excl = incl - hh - hl;
-    if (excl < krem && incl >= krem) {
-      if (excl + hh >= krem) { bc[0] = (uint32_t)bh; bc[1] = excl; bc[2] = hh; }
-      else { bc[0] = (uint32_t)bl; bc[1] = excl + hh; bc[2] = hl; }
+    // thread t owns SEL_BPT consecutive bins from the top, counted downwards
+    uint32_t hb[SEL_BPT];
+    uint32_t v = 0;
+#pragma unroll
+    for (int j = 0; j < SEL_BPT; ++j) {
+      hb[j] = sh.hist[SEL_BINS - 1 - SEL_BPT * tid - j];
+      sh.hist[SEL_BINS - 1 - SEL_BPT * tid - j] = 0u;                  // leave it zero
+      v += hb[j];
     }
+    uint32_t tot;
+    const uint32_t incl = block_scan(v, sh.red[pass & 1], tot);
+    uint32_t* bcp = sh.bc[pass & 1];
+    if (incl - v < krem && incl >= krem) {
+      uint32_t acc = incl - v;
+#pragma unroll
+      for (int j = 0; j < SEL_BPT; ++j) {
+        if (acc < krem && acc + hb[j] >= krem) {
+          bcp[0] = (uint32_t)(SEL_BINS - 1 - SEL_BPT * tid - j);
+          bcp[1] = acc;
+          bcp[2] = hb[j];
+        }
+        acc += hb[j];
+      }
+    }
+    if (tid == 0) sh.bc[3][3] = 0u;                                   // gather counter
     __syncthreads();
-    const uint32_t d = bc[0], above = bc[1], inbin = bc[2];
-    __syncthreads();
+    const uint32_t d = bcp[0], above = bcp[1], inbin = bcp[2];
+    ++pass;
     krem -= above;
-    const uint32_t nlo = lo + (d << sh);
-    const uint32_t top = (d << sh) + ((1u << sh) - 1u);
+    const uint32_t nlo = lo + (d << shf);
+    const uint32_t top = (d << shf) + ((1u << shf) - 1u);
     const uint32_t nhi = top >= span ? hi : lo + top;
     lo = nlo;
     hi = nhi;
@@ -252,70 +243,14 @@ __device__ __forceinline__ void threshold_search(const uint32_t (&kr)[SEL_PER], 
   tie_out = tie_lim;
 }
 
-// Write the ids of the selected candidates (all of them if sel_all) to
-// sel[0..) in candidate order; returns how many.  table holds 2 x 256 words.
-__device__ __forceinline__ int compact_ids(const uint32_t (&kr)[SEL_PER], const uint32_t (&ir)[SEL_PER], int cnt,
-                           bool sel_all, uint32_t lo, uint32_t hi, uint32_t tie_lim,
-                           uint32_t* sel, uint32_t* table, uint32_t* red) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  // the masks are recomputed in the second pass rather than kept (SGPR budget)
-  const int ns = used_slots(cnt);
-  if (tid < 256) table[tid] = 0u;
-  __syncthreads();
-#pragma unroll
-  for (int i = 0; i < SEL_PER; ++i) {
-    if (i >= ns) break;
-    const bool v = i * SEL_THREADS + tid < cnt;
-    const uint64_t gm = __ballot(v && (sel_all || kr[i] > hi));
-    const uint64_t tm = __ballot(v && !sel_all && kr[i] >= lo && kr[i] <= hi);
-    if (lane == 0) table[i * 16 + wave] = (uint32_t)__popcll(gm) | ((uint32_t)__popcll(tm) << 16);
-  }
-  __syncthreads();
-  // exclusive scan over the 256 (slot, wave) counts in candidate order
-  const uint32_t v = tid < 256 ? table[tid] : 0u;
-  const uint32_t incl = block_incl_scan(v, red);
-  if (tid < 256) table[256 + tid] = incl - v;
-  if (tid == 255) red[31] = incl;
-  __syncthreads();
-  const uint32_t total = red[31];
-#pragma unroll
-  for (int i = 0; i < SEL_PER; ++i) {
-    if (i >= ns) break;
-    const bool v2 = i * SEL_THREADS + tid < cnt;
-    const bool g = v2 && (sel_all || kr[i] > hi);
-    const bool t = v2 && !sel_all && kr[i] >= lo && kr[i] <= hi;
-    const uint64_t gm = __ballot(g);
-    const uint64_t tm = __ballot(t);
-    const uint32_t pre = table[256 + i * 16 + wave];
-    const uint32_t gb = (pre & 0xFFFFu) + (uint32_t)__popcll(gm & below);
-    const uint32_t tb = (pre >> 16) + (uint32_t)__popcll(tm & below);
-    if (g || (t && tb < tie_lim)) sel[gb + min(tb, tie_lim)] = ir[i];
-  }
-  __syncthreads();
-  const uint32_t ng = total & 0xFFFFu, nt = total >> 16;
-  return (int)(ng + min(nt, tie_lim));
-}
-
-// ------------------------------------------------------------ select
-// mode 0: top-kk columns -> out[q][0..kk) ids (col_ids mapped), -1 padded.
-// mode 1: best kk blocks of 8 -> out[q][0..8kk) positions, out_len[q]; then,
-//         if k2 > 0, the top-k2 positions inside that pool -> out2[q][0..k2).
-//         (With k2 <= kk the top-k2 of all columns lies inside the pool.)
 __global__ __launch_bounds__(SEL_THREADS) void k_select(
     const float* __restrict__ scores, int64_t ld, const int64_t* __restrict__ n_valid,
     const int32_t* __restrict__ col_ids, int64_t n_cols, LevelDesc d,
     const uint32_t* __restrict__ ws, int kk, int mode, int32_t* __restrict__ out, int64_t out_ld,
     int64_t* __restrict__ out_len, int k2, int32_t* __restrict__ out2) {
-  __shared__ uint32_t sel[SEL_KK_MAX];
-  __shared__ uint32_t hist[2048];
-  __shared__ uint32_t small[SEL_SMALL];
-  __shared__ uint32_t table[512];
-  __shared__ uint32_t red[32];
-  __shared__ uint32_t bc[4];
-
+  __shared__ SelShared sh;
   const int q = blockIdx.x;
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int64_t n0 = n_valid[q];
   const int64_t n = n0 < 0 ? 0 : (n0 < n_cols ? n0 : n_cols);
   const float* srow = scores + (int64_t)q * ld;
@@ -331,80 +266,135 @@ __global__ __launch_bounds__(SEL_THREADS) void k_select(
     }
     return;
   }
-  auto level_key = [&](int lvl, int64_t g) __attribute__((always_inline)) -> uint32_t {
-    return lvl == 0 ? f32_key(srow[g]) : ws[d.off[lvl] + (int64_t)q * d.stride[lvl] + g];
-  };
-  uint32_t kr[SEL_PER], ir[SEL_PER];
-  // candidates of level lvl: all its groups (first == true) or the children
-  // of the cnt groups listed in sel[] (ascending)
-  auto load = [&](int lvl, bool first, int pcnt) __attribute__((always_inline)) -> int {
-    int c;
-    if (first) {
-      c = (int)groups_at(n, lvl);
-    } else {
-      const int64_t gc = groups_at(n, lvl);
-      const int64_t rem = gc - 8 * (int64_t)sel[pcnt - 1];
-      c = 8 * (pcnt - 1) + (rem < 8 ? (int)rem : 8);
-    }
 #pragma unroll
-    for (int i = 0; i < SEL_PER; ++i) {
-      if (i >= used_slots(c)) break;
-      const int e = i * SEL_THREADS + tid;
-      uint32_t id = 0, key = 0;
-      if (e < c) {
-        id = first ? (uint32_t)e : sel[e >> 3] * 8u + (uint32_t)(e & 7);
-        key = level_key(lvl, id);
-      }
-      kr[i] = key;
-      ir[i] = id;
-    }
-    __syncthreads();                      // sel[] may be overwritten after this
-    return c;
-  };
-  // keep the best `want` of the loaded candidates in sel[] (ids ascending)
-  auto keep = [&](int c, int want) __attribute__((always_inline)) -> int {
-    uint32_t lo = 0, hi = 0, tl = 0;
-    const bool all = c <= want;
-    if (!all) threshold_search(kr, c, want, hist, red, bc, small, lo, hi, tl);
-    return compact_ids(kr, ir, c, all, lo, hi, tl, sel, table, red);
-  };
+  for (int j = 0; j < SEL_BPT; ++j) sh.hist[SEL_BPT * tid + j] = 0u;
+  if (tid == 0) sh.bc[3][3] = 0u;
 
+  uint32_t kr[SEL_PER];
+  int cur = 0;                      // sh.lists[cur]: parents of the round being loaded
   int lvl = 0;
   while (groups_at(n, lvl) > SEL_CAP) ++lvl;
   if (lvl < stop) lvl = stop;
-  int cnt = load(lvl, true, 0);
-  while (true) {
-    cnt = keep(cnt, kk);
-    if (lvl == stop) break;
-    --lvl;
-    cnt = load(lvl, false, cnt);
-  }
+  bool first = true;
+  int pcnt = 0;
+  int cnt = 0;
+  uint32_t rb = 0;                  // alternates the reduction buffers between rounds
 
-  if (mode == 0) {
-    for (int i = tid; i < kk; i += SEL_THREADS) {
-      int32_t v = -1;
-      if (i < cnt) v = col_ids ? col_ids[(int64_t)q * ld + sel[i]] : (int32_t)sel[i];
-      orow[i] = v;
+  while (true) {
+    // ---- load the candidates of level lvl and their key range
+    const uint32_t* par = sh.lists[cur];
+    if (first) {
+      cnt = (int)groups_at(n, lvl);
+    } else {
+      const int64_t rem = groups_at(n, lvl) - 8 * (int64_t)par[pcnt - 1];
+      cnt = 8 * (pcnt - 1) + (rem < 8 ? (int)rem : 8);
     }
-    return;
-  }
-  for (int i = tid; i < kk * 8; i += SEL_THREADS) {
-    int32_t v = -1;
-    if (i < cnt * 8) {
-      const int64_t p = (int64_t)sel[i >> 3] * 8 + (i & 7);
-      if (p < n) v = (int32_t)p;
+    const int ns = (cnt + SEL_THREADS - 1) / SEL_THREADS;
+    uint32_t mn = 0xFFFFFFFFu, mx = 0u;
+#pragma unroll
+    for (int i = 0; i < SEL_PER; ++i) {
+      if (i < ns) {
+        const int e = i * SEL_THREADS + tid;
+        uint32_t key = 0;
+        if (e < cnt) {
+          const uint32_t id = first ? (uint32_t)e : par[e >> 3] * 8u + (uint32_t)(e & 7);
+          key = lvl == 0 ? f32_key(srow[id]) : ws[d.off[lvl] + (int64_t)q * d.stride[lvl] + id];
+          mn = min(mn, key);
+          mx = max(mx, key);
+        }
+        kr[i] = key;
+      }
     }
-    orow[i] = v;
-  }
-  if (tid == 0) {
-    const int64_t rem = n - 8 * (int64_t)sel[cnt - 1];
-    out_len[q] = (int64_t)8 * (cnt - 1) + (rem < 8 ? rem : 8);
-  }
-  if (k2 > 0) {                          // the Full layer's own top-k, from inside its pool
-    cnt = load(0, false, cnt);
-    cnt = keep(cnt, k2);
-    for (int i = tid; i < k2; i += SEL_THREADS)
-      out2[(int64_t)q * k2 + i] = i < cnt ? (int32_t)sel[i] : -1;
+    const int want = (lvl == 0 && mode == 1) ? k2 : kk;
+    // ---- threshold (skipped when everything is kept)
+    uint32_t lo = 0, hi = 0, tl = 0;
+    const bool all = cnt <= want;
+    if (!all) {
+      mn = wave_min_all(mn);
+      mx = wave_max_all(mx);
+      if (lane == 0) { sh.red[rb][wave] = mn; sh.table[rb][wave] = mx; }
+      __syncthreads();
+#pragma unroll
+      for (int w = 0; w < SEL_WAVES; ++w) { mn = min(mn, sh.red[rb][w]); mx = max(mx, sh.table[rb][w]); }
+      threshold_search(kr, cnt, ns, want, mn, mx, sh, lo, hi, tl);
+    }
+    // ---- order-preserving compaction of the kept ids into sh.lists[cur ^ 1]
+    uint32_t* tab = sh.table[rb ^ 1];
+#pragma unroll
+    for (int i = 0; i < SEL_PER; ++i) {
+      if (i < ns) {
+        const bool v = i * SEL_THREADS + tid < cnt;
+        const uint64_t gm = __ballot(v && (all || kr[i] > hi));
+        const uint64_t tm = __ballot(v && !all && kr[i] >= lo && kr[i] <= hi);
+        if (lane == 0) tab[i * SEL_WAVES + wave] = (uint32_t)__popcll(gm) | ((uint32_t)__popcll(tm) << 16);
+      }
+    }
+    __syncthreads();
+    const int nt = ns * SEL_WAVES;                       // (slot, wave) counts in candidate order
+    const uint32_t tv = tid < nt ? tab[tid] : 0u;
+    uint32_t tot;
+    const uint32_t tinc = block_scan(tv, sh.red[rb ^ 1], tot);
+    __syncthreads();                                     // every thread has read tab
+    if (tid < nt) tab[tid] = tinc - tv;
+    __syncthreads();
+    uint32_t* keep = sh.lists[cur ^ 1];
+    const uint64_t below = lane == 0 ? 0ull : (~0ull >> (64 - lane));
+#pragma unroll
+    for (int i = 0; i < SEL_PER; ++i) {
+      if (i < ns) {
+        const int e = i * SEL_THREADS + tid;
+        const bool v = e < cnt;
+        const bool g = v && (all || kr[i] > hi);
+        const bool t = v && !all && kr[i] >= lo && kr[i] <= hi;
+        const uint64_t gm = __ballot(g);
+        const uint64_t tm = __ballot(t);
+        const uint32_t pre = tab[i * SEL_WAVES + wave];
+        const uint32_t gb = (pre & 0xFFFFu) + (uint32_t)__popcll(gm & below);
+        const uint32_t tb = (pre >> 16) + (uint32_t)__popcll(tm & below);
+        if (g || (t && tb < tl)) {
+          const uint32_t id = first ? (uint32_t)e : par[e >> 3] * 8u + (uint32_t)(e & 7);
+          keep[gb + min(tb, tl)] = id;
+        }
+      }
+    }
+    const uint32_t ng = tot & 0xFFFFu, ntie = tot >> 16;
+    const int kept = all ? cnt : (int)(ng + min(ntie, tl));
+    __syncthreads();
+    cur ^= 1;
+    rb ^= 1;
+    first = false;
+    pcnt = kept;
+    const uint32_t* sel = sh.lists[cur];
+
+    if (lvl == stop && mode == 0) {
+      for (int i = tid; i < kk; i += SEL_THREADS) {
+        int32_t o = -1;
+        if (i < kept) o = col_ids ? col_ids[(int64_t)q * ld + sel[i]] : (int32_t)sel[i];
+        orow[i] = o;
+      }
+      return;
+    }
+    if (lvl == 1 && mode == 1) {           // the pool: positions of the kept blocks
+      for (int i = tid; i < kk * 8; i += SEL_THREADS) {
+        int32_t o = -1;
+        if (i < kept * 8) {
+          const int64_t p = (int64_t)sel[i >> 3] * 8 + (i & 7);
+          if (p < n) o = (int32_t)p;
+        }
+        orow[i] = o;
+      }
+      if (tid == 0) {
+        const int64_t rem = n - 8 * (int64_t)sel[kept - 1];
+        out_len[q] = (int64_t)8 * (kept - 1) + (rem < 8 ? rem : 8);
+      }
+      if (k2 <= 0) return;
+    }
+    if (lvl == 0 && mode == 1) {           // the Full layer's own top-k, from inside its pool
+      for (int i = tid; i < k2; i += SEL_THREADS)
+        out2[(int64_t)q * k2 + i] = i < kept ? (int32_t)sel[i] : -1;
+      return;
+    }
+    --lvl;
   }
 }
 

@@ -6,13 +6,15 @@
 //   3  MFMA 16x16x32 bf16 placement
 //   4  MFMA 16x16x32 fp16 placement
 //   5  FP4 -> fp16 times each E4M3 scale (packed fp16 multiply)
+//   6  DPP wave scan / max / min against a lane loop
+//   7  E4M3FN -> bf16 / fp16 (times scales) for all 256 codes but NaN
 // Each counter holds the number of mismatching values (0 = pass).
 #include "common.h"
 #include "launch.h"
 
 namespace csa2 {
 
-constexpr int ST_COUNT = 6;
+constexpr int ST_COUNT = 8;
 
 __device__ __forceinline__ int st_a(int m, int k) { return ((m * 7 + k * 3) % 9) - 4; }
 __device__ __forceinline__ int st_b(int k, int n) { return ((k * 5 + n * 11) % 7) - 3; }
@@ -44,6 +46,42 @@ __global__ __launch_bounds__(64) void k_selftest(int32_t* counts) {
         bad_f16 += !(gh == want);
       }
     }
+  }
+  {  // DPP wave scans
+    const uint32_t x = (uint32_t)((l * 37 + 11) % 101);
+    const uint32_t inc = wave_incl_sum(x);
+    const uint32_t mxv = wave_max_all(x), mnv = wave_min_all(x + 5);
+    uint32_t ref = 0, rmx = 0, rmn = 0xFFFFFFFFu;
+    for (int j = 0; j < 64; ++j) {
+      const uint32_t y = (uint32_t)((j * 37 + 11) % 101);
+      if (j <= l) ref += y;
+      rmx = y > rmx ? y : rmx;
+      rmn = y + 5 < rmn ? y + 5 : rmn;
+    }
+    atomicAdd(&counts[6], (int)(inc != ref) + (int)(mxv != rmx) + (int)(mnv != rmn));
+  }
+  {  // FP8 E4M3FN conversions: lane l checks codes 4l .. 4l+3 in every byte position
+    int bad8 = 0;
+    const float scales[3] = {1.0f, 0.0137f, 3.5f};
+    for (int rot = 0; rot < 4; ++rot) {
+      uint32_t lo = 0, hi = 0;
+      for (int b = 0; b < 4; ++b) {
+        lo |= (uint32_t)((4 * l + ((b + rot) & 3)) & 255) << (8 * b);
+        hi |= (uint32_t)((4 * l + ((b + rot + 2) & 3)) & 255) << (8 * b);
+      }
+      const bf16x8_t vb = fp8x8_to_bf16(lo, hi);
+      for (int si = 0; si < 3; ++si) {
+        const f16x8_t vh = fp8x8_to_f16_scaled(lo, hi, scales[si]);
+        for (int i = 0; i < 8; ++i) {
+          const uint32_t c = ((i < 4 ? lo : hi) >> (8 * (i & 3))) & 255u;
+          if ((c & 0x7Fu) == 0x7Fu) continue;                   // NaN codes
+          const float want = e4m3_val(c);
+          if (si == 0) bad8 += !((float)vb[i] == want && signbit((float)vb[i]) == signbit(want));
+          bad8 += (float)vh[i] != (float)(_Float16)(want * scales[si]);
+        }
+      }
+    }
+    atomicAdd(&counts[7], bad8);
   }
   atomicAdd(&counts[0], bad_pow2);
   atomicAdd(&counts[1], bad_bf);

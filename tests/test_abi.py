@@ -116,4 +116,4 @@ def test_workspace_sizes():
 
 
 def test_selftest_counter_query():
-    assert C.lib().csa2_selftest(None, 0, None) == 6
+    assert C.lib().csa2_selftest(None, 0, None) == 8
