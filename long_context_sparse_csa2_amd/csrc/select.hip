@@ -99,12 +99,11 @@ __global__ __launch_bounds__(256) void k_maxima(const float* __restrict__ scores
 }
 
 // ------------------------------------------------------------ select
-// One workgroup of 1024 threads per query.  The candidates of one round
-// (at most SEL_CAP) live in registers: slot i of thread t holds candidate
-// e = 1024 i + t, so candidate order is (slot, thread) order, every LDS
-// access is conflict-free and the only per-candidate state is its key (its
-// id is recomputed from e and the parent list when needed).
-constexpr int SEL_PER = SEL_CAP / SEL_THREADS;     // 32 slots per thread
+// One workgroup of 1024 threads per query.  The candidates of one round (at
+// most SEL_CAP, in id order) live in registers, thread-major: thread t holds
+// candidates 16t .. 16t + 15, loaded with 16-byte vector loads, so the
+// order-preserving compaction is one block scan of per-thread counts.
+constexpr int SEL_PER = SEL_CAP / SEL_THREADS;     // 16 candidates per thread
 constexpr int SEL_WAVES = SEL_THREADS / 64;
 constexpr int SEL_SMALL = 256;
 constexpr int SEL_BINS = 2048;
@@ -114,8 +113,8 @@ struct SelShared {
   uint32_t lists[2][SEL_KK_MAX];      // parent ids of this round / ids it keeps
   uint32_t hist[SEL_BINS];
   uint32_t small[SEL_SMALL];
-  uint32_t table[2][SEL_PER * SEL_WAVES];
   uint32_t red[2][SEL_WAVES];
+  uint32_t mm[2][SEL_WAVES];
   uint32_t bc[4][4];
 };
 
@@ -138,7 +137,7 @@ __device__ __forceinline__ uint32_t block_scan(uint32_t v, uint32_t* red, uint32
 }
 
 // Threshold of the best kk of the cnt candidates (cnt > kk >= 1), given
-// their min and max keys.
+// their min and max keys; nv = this thread's candidate count.
 //
 // Search on the key interval [lo, hi] that holds the kk-th best key: each
 // pass bins the keys inside it by (key - lo) >> s, with s chosen so that at
@@ -148,12 +147,11 @@ __device__ __forceinline__ uint32_t block_scan(uint32_t v, uint32_t* red, uint32
 // against each other.  Result: keys above hi are in, keys inside [lo, hi]
 // are in for the first `tie_lim` of them in candidate (= id) order, keys
 // below lo are out.  The histogram must be zero on entry and is left zero.
-__device__ __forceinline__ void threshold_search(const uint32_t (&kr)[SEL_PER], int cnt, int ns,
+__device__ __forceinline__ void threshold_search(const uint32_t (&kr)[SEL_PER], int nv, int cnt,
                                                  int kk, uint32_t mn, uint32_t mx, SelShared& sh,
                                                  uint32_t& lo_out, uint32_t& hi_out,
                                                  uint32_t& tie_out) {
   const int tid = threadIdx.x;
-  const int lane = tid & 63;
   uint32_t lo = mn, hi = mx;
   uint32_t krem = (uint32_t)kk;
   uint32_t incnt = (uint32_t)cnt;          // candidates with key in [lo, hi]
@@ -162,26 +160,24 @@ __device__ __forceinline__ void threshold_search(const uint32_t (&kr)[SEL_PER], 
   while (true) {
     if (lo == hi) { tie_lim = krem; break; }
     if (incnt <= (uint32_t)SEL_SMALL) {
-      // gather the interval's keys and rank them exactly
+      // gather the interval's keys, rank each against all (4 threads each)
 #pragma unroll
       for (int i = 0; i < SEL_PER; ++i) {
-        if (i < ns) {
-          const uint32_t k = kr[i];
-          if (i * SEL_THREADS + tid < cnt && k >= lo && k <= hi)
-            sh.small[atomicAdd(&sh.bc[3][3], 1u)] = k;
-        }
+        const uint32_t k = kr[i];
+        if (i < nv && k >= lo && k <= hi) sh.small[atomicAdd(&sh.bc[3][3], 1u)] = k;
       }
       __syncthreads();
-      if (tid < (int)incnt) {
-        const uint32_t mine = sh.small[tid];
-        uint32_t gt = 0, ge = 0;
-        for (uint32_t j = 0; j < incnt; ++j) {
-          const uint32_t o = sh.small[j];
-          gt += o > mine;
-          ge += o >= mine;
-        }
-        if (gt < krem && ge >= krem) { sh.bc[2][0] = mine; sh.bc[2][1] = gt; }
+      const int c = tid >> 2, part = tid & 3;
+      const uint32_t mine = c < (int)incnt ? sh.small[c] : 0u;
+      uint32_t gt = 0, ge = 0;
+      for (uint32_t j = part; j < incnt; j += 4) {
+        const uint32_t o = sh.small[j];
+        gt += o > mine;
+        ge += o >= mine;
       }
+      gt += __shfl_xor(gt, 1); ge += __shfl_xor(ge, 1);
+      gt += __shfl_xor(gt, 2); ge += __shfl_xor(ge, 2);
+      if (part == 0 && c < (int)incnt && gt < krem && ge >= krem) { sh.bc[2][0] = mine; sh.bc[2][1] = gt; }
       __syncthreads();
       const uint32_t t = sh.bc[2][0], g = sh.bc[2][1];
       if (tid == 0) sh.bc[3][3] = 0u;     // gather counter; next used after further barriers
@@ -194,11 +190,8 @@ __device__ __forceinline__ void threshold_search(const uint32_t (&kr)[SEL_PER], 
     const int shf = bits > 11 ? bits - 11 : 0;
 #pragma unroll
     for (int i = 0; i < SEL_PER; ++i) {
-      if (i < ns) {
-        const uint32_t k = kr[i];
-        const bool in = i * SEL_THREADS + tid < cnt && k >= lo && k <= hi;
-        if (in) atomicAdd(&sh.hist[(k - lo) >> shf], 1u);
-      }
+      const uint32_t k = kr[i];
+      if (i < nv && k >= lo && k <= hi) atomicAdd(&sh.hist[(k - lo) >> shf], 1u);
     }
     __syncthreads();
     // thread t owns SEL_BPT consecutive bins from the top, counted downwards
@@ -243,11 +236,59 @@ __device__ __forceinline__ void threshold_search(const uint32_t (&kr)[SEL_PER], 
   tie_out = tie_lim;
 }
 
+// 16 consecutive keys of a level array (uint32 keys) or of the scores (fp32,
+// turned into keys) starting at index base, of which the first `n` are valid;
+// vec: the array and base are 16-byte aligned.
+__device__ __forceinline__ void load16(const uint32_t* lv, const float* sc, int64_t base, int n,
+                                       bool vec, uint32_t (&kr)[SEL_PER]) {
+  if (vec && n >= 16) {
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      if (sc) {
+        const f32x4_t x = *(const f32x4_t*)(sc + base + 4 * v);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) kr[4 * v + j] = f32_key(x[j]);
+      } else {
+        const u32x4_t x = *(const u32x4_t*)(lv + base + 4 * v);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) kr[4 * v + j] = x[j];
+      }
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < SEL_PER; ++i)
+      kr[i] = i < n ? (sc ? f32_key(sc[base + i]) : lv[base + i]) : 0u;
+  }
+}
+
+// 8 consecutive keys (one parent's children) into kr[off .. off + 8).
+__device__ __forceinline__ void load8(const uint32_t* lv, const float* sc, int64_t base, int n,
+                                      bool vec, uint32_t (&kr)[SEL_PER], int off) {
+  if (vec && n >= 8) {
+#pragma unroll
+    for (int v = 0; v < 2; ++v) {
+      if (sc) {
+        const f32x4_t x = *(const f32x4_t*)(sc + base + 4 * v);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) kr[off + 4 * v + j] = f32_key(x[j]);
+      } else {
+        const u32x4_t x = *(const u32x4_t*)(lv + base + 4 * v);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) kr[off + 4 * v + j] = x[j];
+      }
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      kr[off + i] = i < n ? (sc ? f32_key(sc[base + i]) : lv[base + i]) : 0u;
+  }
+}
+
 __global__ __launch_bounds__(SEL_THREADS) void k_select(
     const float* __restrict__ scores, int64_t ld, const int64_t* __restrict__ n_valid,
     const int32_t* __restrict__ col_ids, int64_t n_cols, LevelDesc d,
     const uint32_t* __restrict__ ws, int kk, int mode, int32_t* __restrict__ out, int64_t out_ld,
-    int64_t* __restrict__ out_len, int k2, int32_t* __restrict__ out2) {
+    int64_t* __restrict__ out_len, int k2, int32_t* __restrict__ out2, int vec) {
   __shared__ SelShared sh;
   const int q = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -278,32 +319,42 @@ __global__ __launch_bounds__(SEL_THREADS) void k_select(
   bool first = true;
   int pcnt = 0;
   int cnt = 0;
-  uint32_t rb = 0;                  // alternates the reduction buffers between rounds
+  int rb = 0;                       // alternates the reduction buffers between rounds
 
   while (true) {
-    // ---- load the candidates of level lvl and their key range
+    // ---- load the candidates of level lvl (thread t: 16t .. 16t+15) and their key range
     const uint32_t* par = sh.lists[cur];
+    const int64_t gl = groups_at(n, lvl);
     if (first) {
-      cnt = (int)groups_at(n, lvl);
+      cnt = (int)gl;
     } else {
-      const int64_t rem = groups_at(n, lvl) - 8 * (int64_t)par[pcnt - 1];
+      const int64_t rem = gl - 8 * (int64_t)par[pcnt - 1];
       cnt = 8 * (pcnt - 1) + (rem < 8 ? (int)rem : 8);
     }
-    const int ns = (cnt + SEL_THREADS - 1) / SEL_THREADS;
+    const int e0 = SEL_PER * tid;
+    const int nv = cnt - e0 < 0 ? 0 : (cnt - e0 > SEL_PER ? SEL_PER : cnt - e0);
+    const uint32_t* lv = lvl == 0 ? nullptr : ws + d.off[lvl] + (int64_t)q * d.stride[lvl];
+    const float* sc = lvl == 0 ? srow : nullptr;
+    const bool vok = lvl > 0 || vec;                 // 16-byte aligned rows
+    uint32_t p0 = 0, p1 = 0;
+    if (nv > 0) {
+      if (first) {
+        load16(lv, sc, e0, nv, vok, kr);
+      } else {
+        // candidates 16t .. 16t+15 are the children of parents 2t and 2t+1
+        p0 = par[e0 >> 3];
+        p1 = nv > 8 ? par[(e0 >> 3) + 1] : 0u;
+        const int64_t b0 = (int64_t)p0 * 8, b1 = (int64_t)p1 * 8;
+        const int n0c = nv < 8 ? nv : 8;
+        const int n1c = nv > 8 ? nv - 8 : 0;
+        load8(lv, sc, b0, n0c, vok, kr, 0);
+        load8(lv, sc, b1, n1c, vok, kr, 8);
+      }
+    }
     uint32_t mn = 0xFFFFFFFFu, mx = 0u;
 #pragma unroll
     for (int i = 0; i < SEL_PER; ++i) {
-      if (i < ns) {
-        const int e = i * SEL_THREADS + tid;
-        uint32_t key = 0;
-        if (e < cnt) {
-          const uint32_t id = first ? (uint32_t)e : par[e >> 3] * 8u + (uint32_t)(e & 7);
-          key = lvl == 0 ? f32_key(srow[id]) : ws[d.off[lvl] + (int64_t)q * d.stride[lvl] + id];
-          mn = min(mn, key);
-          mx = max(mx, key);
-        }
-        kr[i] = key;
-      }
+      if (i < nv) { mn = min(mn, kr[i]); mx = max(mx, kr[i]); }
     }
     const int want = (lvl == 0 && mode == 1) ? k2 : kk;
     // ---- threshold (skipped when everything is kept)
@@ -312,53 +363,43 @@ __global__ __launch_bounds__(SEL_THREADS) void k_select(
     if (!all) {
       mn = wave_min_all(mn);
       mx = wave_max_all(mx);
-      if (lane == 0) { sh.red[rb][wave] = mn; sh.table[rb][wave] = mx; }
+      if (lane == 0) { sh.red[rb][wave] = mn; sh.mm[rb][wave] = mx; }
       __syncthreads();
 #pragma unroll
-      for (int w = 0; w < SEL_WAVES; ++w) { mn = min(mn, sh.red[rb][w]); mx = max(mx, sh.table[rb][w]); }
-      threshold_search(kr, cnt, ns, want, mn, mx, sh, lo, hi, tl);
+      for (int w = 0; w < SEL_WAVES; ++w) { mn = min(mn, sh.red[rb][w]); mx = max(mx, sh.mm[rb][w]); }
+      threshold_search(kr, nv, cnt, want, mn, mx, sh, lo, hi, tl);
     }
     // ---- order-preserving compaction of the kept ids into sh.lists[cur ^ 1]
-    uint32_t* tab = sh.table[rb ^ 1];
+    uint32_t ngt = 0, ntie = 0;
 #pragma unroll
     for (int i = 0; i < SEL_PER; ++i) {
-      if (i < ns) {
-        const bool v = i * SEL_THREADS + tid < cnt;
-        const uint64_t gm = __ballot(v && (all || kr[i] > hi));
-        const uint64_t tm = __ballot(v && !all && kr[i] >= lo && kr[i] <= hi);
-        if (lane == 0) tab[i * SEL_WAVES + wave] = (uint32_t)__popcll(gm) | ((uint32_t)__popcll(tm) << 16);
+      if (i < nv) {
+        ngt += all || kr[i] > hi;
+        ntie += !all && kr[i] >= lo && kr[i] <= hi;
       }
     }
-    __syncthreads();
-    const int nt = ns * SEL_WAVES;                       // (slot, wave) counts in candidate order
-    const uint32_t tv = tid < nt ? tab[tid] : 0u;
+    const uint32_t packed = ngt | (ntie << 16);           // both sums stay below 2^16
     uint32_t tot;
-    const uint32_t tinc = block_scan(tv, sh.red[rb ^ 1], tot);
-    __syncthreads();                                     // every thread has read tab
-    if (tid < nt) tab[tid] = tinc - tv;
-    __syncthreads();
+    const uint32_t excl = block_scan(packed, sh.red[rb ^ 1], tot) - packed;
+    const uint32_t gt_before = excl & 0xFFFFu, tie_before = excl >> 16;
     uint32_t* keep = sh.lists[cur ^ 1];
-    const uint64_t below = lane == 0 ? 0ull : (~0ull >> (64 - lane));
+    uint32_t pos = gt_before + min(tie_before, tl);
+    uint32_t tr = tie_before;
+    const bool map_cols = lvl == stop && mode == 0 && col_ids;
 #pragma unroll
     for (int i = 0; i < SEL_PER; ++i) {
-      if (i < ns) {
-        const int e = i * SEL_THREADS + tid;
-        const bool v = e < cnt;
-        const bool g = v && (all || kr[i] > hi);
-        const bool t = v && !all && kr[i] >= lo && kr[i] <= hi;
-        const uint64_t gm = __ballot(g);
-        const uint64_t tm = __ballot(t);
-        const uint32_t pre = tab[i * SEL_WAVES + wave];
-        const uint32_t gb = (pre & 0xFFFFu) + (uint32_t)__popcll(gm & below);
-        const uint32_t tb = (pre >> 16) + (uint32_t)__popcll(tm & below);
-        if (g || (t && tb < tl)) {
-          const uint32_t id = first ? (uint32_t)e : par[e >> 3] * 8u + (uint32_t)(e & 7);
-          keep[gb + min(tb, tl)] = id;
+      if (i < nv) {
+        const bool g = all || kr[i] > hi;
+        const bool t = !all && kr[i] >= lo && kr[i] <= hi;
+        if (g || (t && tr < tl)) {
+          const int e = e0 + i;
+          uint32_t id = first ? (uint32_t)e : (i < 8 ? p0 : p1) * 8u + (uint32_t)(e & 7);
+          keep[pos++] = id;
         }
+        tr += t;
       }
     }
-    const uint32_t ng = tot & 0xFFFFu, ntie = tot >> 16;
-    const int kept = all ? cnt : (int)(ng + min(ntie, tl));
+    const int kept = all ? cnt : (int)((tot & 0xFFFFu) + min(tot >> 16, tl));
     __syncthreads();
     cur ^= 1;
     rb ^= 1;
@@ -369,7 +410,7 @@ __global__ __launch_bounds__(SEL_THREADS) void k_select(
     if (lvl == stop && mode == 0) {
       for (int i = tid; i < kk; i += SEL_THREADS) {
         int32_t o = -1;
-        if (i < kept) o = col_ids ? col_ids[(int64_t)q * ld + sel[i]] : (int32_t)sel[i];
+        if (i < kept) o = map_cols ? col_ids[(int64_t)q * ld + sel[i]] : (int32_t)sel[i];
         orow[i] = o;
       }
       return;
@@ -408,7 +449,7 @@ static LevelDesc make_levels(int Q, int64_t n_cols, int mode) {
   int64_t off = 0;
   for (int l = 1; l <= L; ++l) {
     d.off[l] = off;
-    d.stride[l] = groups_at(n_cols, l);
+    d.stride[l] = (groups_at(n_cols, l) + 3) / 4 * 4;    // 16-byte aligned rows
     off += (int64_t)Q * d.stride[l];
   }
   return d;
@@ -427,14 +468,14 @@ hipError_t launch_select(const float* scores, int64_t ld, int Q, const int64_t* 
                          hipStream_t stream) {
   const LevelDesc d = make_levels(Q, n_cols, mode);
   const int64_t nchunk = (n_cols + 4095) / 4096;
+  const int vec = (ld % 4 == 0) && (((uintptr_t)scores & 15) == 0);   // 16-byte row starts
   if (d.nlev > 0 && nchunk > 0) {
-    const int vec = (ld % 4 == 0) && (((uintptr_t)scores & 15) == 0);   // 16-byte row starts
     hipLaunchKernelGGL(k_maxima, dim3((unsigned)(nchunk * Q)), dim3(256), 0, stream, scores, ld,
                        n_valid, n_cols, nchunk, d, (uint32_t*)ws, vec);
   }
   hipLaunchKernelGGL(k_select, dim3((unsigned)Q), dim3(SEL_THREADS), 0, stream, scores, ld,
                      n_valid, col_ids, n_cols, d, (const uint32_t*)ws, kk, mode, out, out_ld,
-                     out_len, k2, out2);
+                     out_len, k2, out2, vec);
   return hipGetLastError();
 }
 
