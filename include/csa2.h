@@ -227,7 +227,11 @@ csa2_status csa2_block_pool(const float* scores, int64_t ld, int Q, const int64_
  *   out        [Q][64][512] fp32
  *   lse        [Q][64] fp32, or NULL.  A query with no rows gets out = 0,
  *              lse = -inf.
- *   ws         csa2_workspace_bytes(CSA2_OP_ATTEND, Q, 0, k) bytes
+ *   ws         csa2_workspace_bytes(CSA2_OP_ATTEND, Q, 0, k) bytes (partial
+ *              states of the row splits).  With a smaller or NULL workspace the
+ *              call uses fewer splits (at worst one workgroup per query and
+ *              head group), with the same result.  Calls that share one
+ *              workspace must not overlap.
  */
 csa2_status csa2_sparse_attend(const uint16_t* q, const int32_t* q_seq, int Q, const csa2_cache* src,
                                const int32_t* idx, int k, const uint8_t* swa_codes,

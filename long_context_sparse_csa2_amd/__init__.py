@@ -220,6 +220,8 @@ def csa2_selftest(device="cuda"):
 
 
 def workspace(op, Q, n_cols, k, device):
-    """A uint8 device tensor of the size csa2_workspace_bytes asks for (or None)."""
+    """A zero-filled uint8 device tensor of the size csa2_workspace_bytes asks
+    for (or None).  The attention workspace must start zeroed (it holds the
+    split-merge semaphores, which every call leaves at zero)."""
     n = csa2_workspace_bytes(op, Q, n_cols, k)
-    return torch.empty(n, dtype=torch.uint8, device=device) if n else None
+    return torch.zeros(n, dtype=torch.uint8, device=device) if n else None

@@ -23,8 +23,10 @@
 //               output dims 128w..128w+127.
 // Decode (few queries) splits the chunks of a query over several
 // workgroups and merges the partial (max, sum, O) by log-sum-exp in a second
-// kernel; prefill runs one workgroup per (query, head group) over all
-// chunks and writes the result directly.
+// kernel (merging in the last workgroup to finish needs an agent-scope fence,
+// which writes back the whole L2 of its XCD on MI355X and measured 4x slower).
+// Prefill runs one workgroup per (query, head group) over all chunks and
+// writes the result directly.
 #include "common.h"
 #include "launch.h"
 
@@ -36,7 +38,7 @@ constexpr int AT_PAD = 8;          // fp16 padding of an LDS row
 constexpr int AT_MAX_SWA = 128;
 constexpr int AT_TARGET_WG = 1024; // workgroups a decode launch aims for
 
-__global__ __launch_bounds__(256) void k_attend(
+__global__ __launch_bounds__(256, 2) void k_attend(
     const uint16_t* __restrict__ qv, const int32_t* __restrict__ q_seq,
     const uint8_t* __restrict__ kv_codes, const uint8_t* __restrict__ kv_scales, int64_t cap,
     const int32_t* __restrict__ idx, int k, const uint8_t* __restrict__ swa_codes,
@@ -100,6 +102,29 @@ __global__ __launch_bounds__(256) void k_attend(
     }
     __syncthreads();
 
+    // ---- issue this thread's V^T staging loads before the QK^T work: rows
+    //      2rp, 2rp+1, dims 64db .. +63 (main: 32 code bytes + 4 scale bytes
+    //      per row; SWA: 64 FP8 bytes per row)
+    const int rp = tid & 31, db = tid >> 5;
+    const int64_t voff0 = rowoff[2 * rp], voff1 = rowoff[2 * rp + 1];
+    u32x4_t va[4], vb[4];
+    uint32_t vs0 = 0, vs1 = 0;
+    if (is_main) {
+      const int64_t e0 = voff0 >= 0 ? voff0 : seq * cap, e1 = voff1 >= 0 ? voff1 : seq * cap;
+      const u32x4_t* c0p = (const u32x4_t*)(kv_codes + e0 * 256 + db * 32);
+      const u32x4_t* c1p = (const u32x4_t*)(kv_codes + e1 * 256 + db * 32);
+      va[0] = c0p[0]; va[1] = c0p[1]; vb[0] = c1p[0]; vb[1] = c1p[1];
+      vs0 = *(const uint32_t*)(kv_scales + e0 * 32 + db * 4);
+      vs1 = *(const uint32_t*)(kv_scales + e1 * 32 + db * 4);
+    } else {
+      const int64_t r0 = voff0 >= 0 ? voff0 : seq * T_swa + sst;
+      const int64_t r1 = voff1 >= 0 ? voff1 : seq * T_swa + sst;
+      const u32x4_t* c0p = (const u32x4_t*)(swa_codes + r0 * 512 + db * 64);
+      const u32x4_t* c1p = (const u32x4_t*)(swa_codes + r1 * 512 + db * 64);
+#pragma unroll
+      for (int i2 = 0; i2 < 4; ++i2) { va[i2] = c0p[i2]; vb[i2] = c1p[i2]; }
+    }
+
     // ---- S = Q K^T for rows 16*wave .. +15 (lane column r16)
     const int lr = wave * 16 + r16;
     const int64_t myoff = rowoff[lr];
@@ -134,47 +159,36 @@ __global__ __launch_bounds__(256) void k_attend(
       for (int j = 0; j < 4; ++j) sacc[j] = -INFINITY;
     }
 
-    // ---- stage V^T (fp16): thread owns rows 2rp, 2rp+1 and dims 64db .. +63
+    // ---- stage V^T (fp16) from the loaded bytes
     {
-      const int rp = tid & 31, db = tid >> 5;
-      const int64_t off0 = rowoff[2 * rp], off1 = rowoff[2 * rp + 1];
       _Float16* vcol = &vt[db * 64][2 * rp];
       auto put8 = [&](int dim0, f16x8_t x0, f16x8_t x1) {
 #pragma unroll
         for (int b = 0; b < 8; ++b) {
           f16x2_t pr;
-          pr[0] = off0 >= 0 ? x0[b] : (_Float16)0.f;
-          pr[1] = off1 >= 0 ? x1[b] : (_Float16)0.f;
+          pr[0] = voff0 >= 0 ? x0[b] : (_Float16)0.f;
+          pr[1] = voff1 >= 0 ? x1[b] : (_Float16)0.f;
           *(f16x2_t*)(vcol + (dim0 + b) * (AT_ROWS + AT_PAD)) = pr;
         }
       };
       if (is_main) {
-        const int64_t e0 = off0 >= 0 ? off0 : seq * cap, e1 = off1 >= 0 ? off1 : seq * cap;
-        const u32x4_t* c0p = (const u32x4_t*)(kv_codes + e0 * 256 + db * 32);
-        const u32x4_t* c1p = (const u32x4_t*)(kv_codes + e1 * 256 + db * 32);
-        const uint32_t s0 = *(const uint32_t*)(kv_scales + e0 * 32 + db * 4);
-        const uint32_t s1 = *(const uint32_t*)(kv_scales + e1 * 32 + db * 4);
 #pragma unroll
         for (int h2 = 0; h2 < 2; ++h2) {
-          const u32x4_t a0 = c0p[h2], b0 = c1p[h2];
 #pragma unroll
           for (int i = 0; i < 4; ++i) {            // 8 dims per word, 2 words per scale group
             const int wi = 4 * h2 + i;
-            put8(8 * wi, fp4x8_to_f16_scaled(a0[i], e4m3_val((s0 >> (8 * (wi >> 1))) & 0xFFu)),
-                 fp4x8_to_f16_scaled(b0[i], e4m3_val((s1 >> (8 * (wi >> 1))) & 0xFFu)));
+            put8(8 * wi, fp4x8_to_f16_scaled(va[h2][i], e4m3_val((vs0 >> (8 * (wi >> 1))) & 0xFFu)),
+                 fp4x8_to_f16_scaled(vb[h2][i], e4m3_val((vs1 >> (8 * (wi >> 1))) & 0xFFu)));
           }
         }
       } else {
-        const int64_t r0 = off0 >= 0 ? off0 : seq * T_swa + sst;
-        const int64_t r1 = off1 >= 0 ? off1 : seq * T_swa + sst;
         const float g0 = rowsig[2 * rp], g1 = rowsig[2 * rp + 1];
-        const u32x4_t* c0p = (const u32x4_t*)(swa_codes + r0 * 512 + db * 64);
-        const u32x4_t* c1p = (const u32x4_t*)(swa_codes + r1 * 512 + db * 64);
 #pragma unroll
         for (int i2 = 0; i2 < 4; ++i2) {           // 16 dims per 16-byte load
-          const u32x4_t x0 = c0p[i2], x1 = c1p[i2];
-          put8(16 * i2, fp8x8_to_f16_scaled(x0[0], x0[1], g0), fp8x8_to_f16_scaled(x1[0], x1[1], g1));
-          put8(16 * i2 + 8, fp8x8_to_f16_scaled(x0[2], x0[3], g0), fp8x8_to_f16_scaled(x1[2], x1[3], g1));
+          put8(16 * i2, fp8x8_to_f16_scaled(va[i2][0], va[i2][1], g0),
+               fp8x8_to_f16_scaled(vb[i2][0], vb[i2][1], g1));
+          put8(16 * i2 + 8, fp8x8_to_f16_scaled(va[i2][2], va[i2][3], g0),
+               fp8x8_to_f16_scaled(vb[i2][2], vb[i2][3], g1));
         }
       }
     }
@@ -255,17 +269,17 @@ __global__ __launch_bounds__(256) void k_attend(
       if (lse && wave == 0 && r16 == 0)
         lse[(int64_t)q * H_ATT + head0 + j] = l_run[j] > 0.f ? m_run[j] + logf(l_run[j]) : -INFINITY;
     }
-  } else {
+    return;
+  }
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int64_t slot = ((int64_t)q * nsplit + sp) * H_ATT + head0 + j;
-      float* op = part_o + slot * D_LAT + wave * 128 + r16;
+  for (int j = 0; j < 4; ++j) {
+    const int64_t slot = ((int64_t)q * nsplit + sp) * H_ATT + head0 + j;
+    float* op = part_o + slot * D_LAT + wave * 128 + r16;
 #pragma unroll
-      for (int t = 0; t < 8; ++t) op[16 * t] = o[t][j];
-      if (wave == 0 && r16 == 0) {
-        part_ml[2 * slot] = m_run[j];
-        part_ml[2 * slot + 1] = l_run[j];
-      }
+    for (int t = 0; t < 8; ++t) op[16 * t] = o[t][j];
+    if (wave == 0 && r16 == 0) {
+      part_ml[2 * slot] = m_run[j];
+      part_ml[2 * slot + 1] = l_run[j];
     }
   }
 }
@@ -327,6 +341,7 @@ static void attend_plan(int Q, int k, int& nsplit, int& cps) {
   if (nsplit < 1) nsplit = 1;
 }
 
+// workspace: [partial O: Q * nsplit * 64 * 512 fp32][partial (max, sum)]
 static size_t attend_ws_for(int Q, int nsplit) {
   if (nsplit <= 1) return 0;
   return (size_t)Q * nsplit * H_ATT * (D_LAT + 2) * sizeof(float);
