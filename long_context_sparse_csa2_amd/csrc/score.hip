@@ -124,21 +124,34 @@ hipError_t launch_index_score(const uint16_t* q_idx, const float* w, const int32
                               const int64_t* n_vis, const int32_t* cand, int64_t ld_cand, int Q,
                               int64_t n_cols, const uint8_t* ik_codes, const uint8_t* ik_scales,
                               int64_t cap, float* scores, int64_t ld, hipStream_t stream) {
-  // long scans: 32 tiles per wave (4096 columns per workgroup) with two tiles
-  // in flight; short ones (a Reindex pool): one tile per wave, for more
-  // workgroups in flight (both measured best on MI355X)
-  const bool long_scan = n_cols * Q >= (int64_t)1 << 22;
-  const int tpw = long_scan ? 32 : 1;
+  // Tiles per wave: the largest of 32, 16, 8, 2, 1 that still launches at
+  // least 1024 workgroups (4 per CU); long scans keep two tiles in flight.
+  // (Swept on MI355X: 1M-entry scans want 32 tiles x 2 in flight, 64K-entry
+  // scans 8-16, 16K-entry Reindex pools 1-2.)
+  int tpw = 1;
+  for (int t : {32, 16, 8, 2}) {
+    const int64_t wgs = (int64_t)Q * ((n_cols + 128 * t - 1) / (128 * t));
+    if (wgs >= 1024) { tpw = t; break; }
+  }
   const int64_t cols = (int64_t)SC_WAVES * tpw * 32;
   const int64_t nchunk = (n_cols + cols - 1) / cols;
   const dim3 grid((unsigned)(nchunk * Q));
-  if (long_scan) {
-    if (cand) launch_variant<true, 32, 2>(grid, stream, q_idx, w, q_seq, n_vis, cand, ld_cand, nchunk, n_cols, ik_codes, ik_scales, cap, scores, ld);
-    else launch_variant<false, 32, 2>(grid, stream, q_idx, w, q_seq, n_vis, cand, ld_cand, nchunk, n_cols, ik_codes, ik_scales, cap, scores, ld);
-  } else {
-    if (cand) launch_variant<true, 1, 1>(grid, stream, q_idx, w, q_seq, n_vis, cand, ld_cand, nchunk, n_cols, ik_codes, ik_scales, cap, scores, ld);
-    else launch_variant<false, 1, 1>(grid, stream, q_idx, w, q_seq, n_vis, cand, ld_cand, nchunk, n_cols, ik_codes, ik_scales, cap, scores, ld);
+#define CSA2_SCORE_CASE(T, D)                                                                       \
+  case T:                                                                                          \
+    if (cand) launch_variant<true, T, D>(grid, stream, q_idx, w, q_seq, n_vis, cand, ld_cand,      \
+                                         nchunk, n_cols, ik_codes, ik_scales, cap, scores, ld);    \
+    else launch_variant<false, T, D>(grid, stream, q_idx, w, q_seq, n_vis, cand, ld_cand, nchunk,  \
+                                     n_cols, ik_codes, ik_scales, cap, scores, ld);                \
+    break;
+  switch (tpw) {
+    CSA2_SCORE_CASE(32, 2)
+    CSA2_SCORE_CASE(16, 2)
+    CSA2_SCORE_CASE(8, 2)
+    CSA2_SCORE_CASE(2, 1)
+    default:
+    CSA2_SCORE_CASE(1, 1)
   }
+#undef CSA2_SCORE_CASE
   return hipGetLastError();
 }
 

@@ -27,7 +27,6 @@
 
 namespace csa2 {
 
-constexpr int SEL_THREADS = 1024;
 constexpr int SEL_KK_MAX = 2048;
 
 struct LevelDesc {
@@ -99,27 +98,27 @@ __global__ __launch_bounds__(256) void k_maxima(const float* __restrict__ scores
 }
 
 // ------------------------------------------------------------ select
-// One workgroup of 1024 threads per query.  The candidates of one round (at
+// One workgroup of NT threads (1024, or 256 for small rounds) per query.  The candidates of one round (at
 // most SEL_CAP, in id order) live in registers, thread-major: thread t holds
 // candidates 16t .. 16t + 15, loaded with 16-byte vector loads, so the
 // order-preserving compaction is one block scan of per-thread counts.
-constexpr int SEL_PER = SEL_CAP / SEL_THREADS;     // 16 candidates per thread
-constexpr int SEL_WAVES = SEL_THREADS / 64;
+constexpr int SEL_PER = 16;                        // candidates per thread
 constexpr int SEL_SMALL = 256;
 constexpr int SEL_BINS = 2048;
-constexpr int SEL_BPT = SEL_BINS / SEL_THREADS;    // histogram bins per thread
 
+template <int NT>
 struct SelShared {
   uint32_t lists[2][SEL_KK_MAX];      // parent ids of this round / ids it keeps
   uint32_t hist[SEL_BINS];
   uint32_t small[SEL_SMALL];
-  uint32_t red[2][SEL_WAVES];
-  uint32_t mm[2][SEL_WAVES];
+  uint32_t red[2][(NT / 64)];
+  uint32_t mm[2][(NT / 64)];
   uint32_t bc[4][4];
 };
 
 // Inclusive block-wide sum; `total` gets the block total.  red must not be
 // reused by the caller until after the next barrier.
+template <int NT>
 __device__ __forceinline__ uint32_t block_scan(uint32_t v, uint32_t* red, uint32_t& total) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const uint32_t incl = wave_incl_sum(v);
@@ -127,7 +126,7 @@ __device__ __forceinline__ uint32_t block_scan(uint32_t v, uint32_t* red, uint32
   __syncthreads();
   uint32_t pre = 0, tot = 0;
 #pragma unroll
-  for (int w = 0; w < SEL_WAVES; ++w) {
+  for (int w = 0; w < (NT / 64); ++w) {
     const uint32_t x = red[w];
     pre += w < wave ? x : 0u;
     tot += x;
@@ -147,8 +146,9 @@ __device__ __forceinline__ uint32_t block_scan(uint32_t v, uint32_t* red, uint32
 // against each other.  Result: keys above hi are in, keys inside [lo, hi]
 // are in for the first `tie_lim` of them in candidate (= id) order, keys
 // below lo are out.  The histogram must be zero on entry and is left zero.
+template <int NT>
 __device__ __forceinline__ void threshold_search(const uint32_t (&kr)[SEL_PER], int nv, int cnt,
-                                                 int kk, uint32_t mn, uint32_t mx, SelShared& sh,
+                                                 int kk, uint32_t mn, uint32_t mx, SelShared<NT>& sh,
                                                  uint32_t& lo_out, uint32_t& hi_out,
                                                  uint32_t& tie_out) {
   const int tid = threadIdx.x;
@@ -167,16 +167,17 @@ __device__ __forceinline__ void threshold_search(const uint32_t (&kr)[SEL_PER], 
         if (i < nv && k >= lo && k <= hi) sh.small[atomicAdd(&sh.bc[3][3], 1u)] = k;
       }
       __syncthreads();
-      const int c = tid >> 2, part = tid & 3;
+      constexpr int RS = NT / SEL_SMALL;           // threads ranking one candidate
+      const int c = tid / RS, part = tid % RS;
       const uint32_t mine = c < (int)incnt ? sh.small[c] : 0u;
       uint32_t gt = 0, ge = 0;
-      for (uint32_t j = part; j < incnt; j += 4) {
+      for (uint32_t j = part; j < incnt; j += RS) {
         const uint32_t o = sh.small[j];
         gt += o > mine;
         ge += o >= mine;
       }
-      gt += __shfl_xor(gt, 1); ge += __shfl_xor(ge, 1);
-      gt += __shfl_xor(gt, 2); ge += __shfl_xor(ge, 2);
+#pragma unroll
+      for (int off = 1; off < RS; off <<= 1) { gt += __shfl_xor(gt, off); ge += __shfl_xor(ge, off); }
       if (part == 0 && c < (int)incnt && gt < krem && ge >= krem) { sh.bc[2][0] = mine; sh.bc[2][1] = gt; }
       __syncthreads();
       const uint32_t t = sh.bc[2][0], g = sh.bc[2][1];
@@ -194,24 +195,24 @@ __device__ __forceinline__ void threshold_search(const uint32_t (&kr)[SEL_PER], 
       if (i < nv && k >= lo && k <= hi) atomicAdd(&sh.hist[(k - lo) >> shf], 1u);
     }
     __syncthreads();
-    // thread t owns SEL_BPT consecutive bins from the top, counted downwards
-    uint32_t hb[SEL_BPT];
+    // thread t owns (SEL_BINS / NT) consecutive bins from the top, counted downwards
+    uint32_t hb[(SEL_BINS / NT)];
     uint32_t v = 0;
 #pragma unroll
-    for (int j = 0; j < SEL_BPT; ++j) {
-      hb[j] = sh.hist[SEL_BINS - 1 - SEL_BPT * tid - j];
-      sh.hist[SEL_BINS - 1 - SEL_BPT * tid - j] = 0u;                  // leave it zero
+    for (int j = 0; j < (SEL_BINS / NT); ++j) {
+      hb[j] = sh.hist[SEL_BINS - 1 - (SEL_BINS / NT) * tid - j];
+      sh.hist[SEL_BINS - 1 - (SEL_BINS / NT) * tid - j] = 0u;                  // leave it zero
       v += hb[j];
     }
     uint32_t tot;
-    const uint32_t incl = block_scan(v, sh.red[pass & 1], tot);
+    const uint32_t incl = block_scan<NT>(v, sh.red[pass & 1], tot);
     uint32_t* bcp = sh.bc[pass & 1];
     if (incl - v < krem && incl >= krem) {
       uint32_t acc = incl - v;
 #pragma unroll
-      for (int j = 0; j < SEL_BPT; ++j) {
+      for (int j = 0; j < (SEL_BINS / NT); ++j) {
         if (acc < krem && acc + hb[j] >= krem) {
-          bcp[0] = (uint32_t)(SEL_BINS - 1 - SEL_BPT * tid - j);
+          bcp[0] = (uint32_t)(SEL_BINS - 1 - (SEL_BINS / NT) * tid - j);
           bcp[1] = acc;
           bcp[2] = hb[j];
         }
@@ -284,12 +285,13 @@ __device__ __forceinline__ void load8(const uint32_t* lv, const float* sc, int64
   }
 }
 
-__global__ __launch_bounds__(SEL_THREADS) void k_select(
+template <int NT>
+__global__ __launch_bounds__(NT) void k_select(
     const float* __restrict__ scores, int64_t ld, const int64_t* __restrict__ n_valid,
     const int32_t* __restrict__ col_ids, int64_t n_cols, LevelDesc d,
     const uint32_t* __restrict__ ws, int kk, int mode, int32_t* __restrict__ out, int64_t out_ld,
     int64_t* __restrict__ out_len, int k2, int32_t* __restrict__ out2, int vec) {
-  __shared__ SelShared sh;
+  __shared__ SelShared<NT> sh;
   const int q = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int64_t n0 = n_valid[q];
@@ -300,21 +302,21 @@ __global__ __launch_bounds__(SEL_THREADS) void k_select(
   const int64_t out_w = mode == 0 ? kk : (int64_t)kk * 8;
 
   if (n == 0) {
-    for (int64_t i = tid; i < out_w; i += SEL_THREADS) orow[i] = -1;
+    for (int64_t i = tid; i < out_w; i += NT) orow[i] = -1;
     if (mode == 1) {
       if (tid == 0) out_len[q] = 0;
-      for (int i = tid; i < k2; i += SEL_THREADS) out2[(int64_t)q * k2 + i] = -1;
+      for (int i = tid; i < k2; i += NT) out2[(int64_t)q * k2 + i] = -1;
     }
     return;
   }
 #pragma unroll
-  for (int j = 0; j < SEL_BPT; ++j) sh.hist[SEL_BPT * tid + j] = 0u;
+  for (int j = 0; j < (SEL_BINS / NT); ++j) sh.hist[(SEL_BINS / NT) * tid + j] = 0u;
   if (tid == 0) sh.bc[3][3] = 0u;
 
   uint32_t kr[SEL_PER];
   int cur = 0;                      // sh.lists[cur]: parents of the round being loaded
   int lvl = 0;
-  while (groups_at(n, lvl) > SEL_CAP) ++lvl;
+  while (groups_at(n, lvl) > (int64_t)NT * SEL_PER) ++lvl;
   if (lvl < stop) lvl = stop;
   bool first = true;
   int pcnt = 0;
@@ -366,8 +368,8 @@ __global__ __launch_bounds__(SEL_THREADS) void k_select(
       if (lane == 0) { sh.red[rb][wave] = mn; sh.mm[rb][wave] = mx; }
       __syncthreads();
 #pragma unroll
-      for (int w = 0; w < SEL_WAVES; ++w) { mn = min(mn, sh.red[rb][w]); mx = max(mx, sh.mm[rb][w]); }
-      threshold_search(kr, nv, cnt, want, mn, mx, sh, lo, hi, tl);
+      for (int w = 0; w < (NT / 64); ++w) { mn = min(mn, sh.red[rb][w]); mx = max(mx, sh.mm[rb][w]); }
+      threshold_search<NT>(kr, nv, cnt, want, mn, mx, sh, lo, hi, tl);
     }
     // ---- order-preserving compaction of the kept ids into sh.lists[cur ^ 1]
     uint32_t ngt = 0, ntie = 0;
@@ -380,7 +382,7 @@ __global__ __launch_bounds__(SEL_THREADS) void k_select(
     }
     const uint32_t packed = ngt | (ntie << 16);           // both sums stay below 2^16
     uint32_t tot;
-    const uint32_t excl = block_scan(packed, sh.red[rb ^ 1], tot) - packed;
+    const uint32_t excl = block_scan<NT>(packed, sh.red[rb ^ 1], tot) - packed;
     const uint32_t gt_before = excl & 0xFFFFu, tie_before = excl >> 16;
     uint32_t* keep = sh.lists[cur ^ 1];
     uint32_t pos = gt_before + min(tie_before, tl);
@@ -408,7 +410,7 @@ __global__ __launch_bounds__(SEL_THREADS) void k_select(
     const uint32_t* sel = sh.lists[cur];
 
     if (lvl == stop && mode == 0) {
-      for (int i = tid; i < kk; i += SEL_THREADS) {
+      for (int i = tid; i < kk; i += NT) {
         int32_t o = -1;
         if (i < kept) o = map_cols ? col_ids[(int64_t)q * ld + sel[i]] : (int32_t)sel[i];
         orow[i] = o;
@@ -416,7 +418,7 @@ __global__ __launch_bounds__(SEL_THREADS) void k_select(
       return;
     }
     if (lvl == 1 && mode == 1) {           // the pool: positions of the kept blocks
-      for (int i = tid; i < kk * 8; i += SEL_THREADS) {
+      for (int i = tid; i < kk * 8; i += NT) {
         int32_t o = -1;
         if (i < kept * 8) {
           const int64_t p = (int64_t)sel[i >> 3] * 8 + (i & 7);
@@ -431,7 +433,7 @@ __global__ __launch_bounds__(SEL_THREADS) void k_select(
       if (k2 <= 0) return;
     }
     if (lvl == 0 && mode == 1) {           // the Full layer's own top-k, from inside its pool
-      for (int i = tid; i < k2; i += SEL_THREADS)
+      for (int i = tid; i < k2; i += NT)
         out2[(int64_t)q * k2 + i] = i < kept ? (int32_t)sel[i] : -1;
       return;
     }
@@ -473,9 +475,15 @@ hipError_t launch_select(const float* scores, int64_t ld, int Q, const int64_t* 
     hipLaunchKernelGGL(k_maxima, dim3((unsigned)(nchunk * Q)), dim3(256), 0, stream, scores, ld,
                        n_valid, n_cols, nchunk, d, (uint32_t*)ws, vec);
   }
-  hipLaunchKernelGGL(k_select, dim3((unsigned)Q), dim3(SEL_THREADS), 0, stream, scores, ld,
-                     n_valid, col_ids, n_cols, d, (const uint32_t*)ws, kk, mode, out, out_ld,
-                     out_len, k2, out2, vec);
+  // one round over at most 4096 candidates: 256-thread workgroups, several per CU
+  if (mode == 0 && n_cols <= 256 * SEL_PER)
+    hipLaunchKernelGGL(k_select<256>, dim3((unsigned)Q), dim3(256), 0, stream, scores, ld, n_valid,
+                       col_ids, n_cols, d, (const uint32_t*)ws, kk, mode, out, out_ld, out_len, k2,
+                       out2, vec);
+  else
+    hipLaunchKernelGGL(k_select<1024>, dim3((unsigned)Q), dim3(1024), 0, stream, scores, ld,
+                       n_valid, col_ids, n_cols, d, (const uint32_t*)ws, kk, mode, out, out_ld,
+                       out_len, k2, out2, vec);
   return hipGetLastError();
 }
 
