@@ -37,6 +37,7 @@ constexpr int AT_HG = 16;          // heads per workgroup
 constexpr int AT_PAD = 8;          // fp16 padding of an LDS row
 constexpr int AT_MAX_SWA = 128;
 constexpr int AT_TARGET_WG = 1024; // workgroups a decode launch aims for
+constexpr int AT_WIDE_MIN_Q = 256;  // from this many queries on, one workgroup per query
 
 __global__ __launch_bounds__(256, 2) void k_attend(
     const uint16_t* __restrict__ qv, const int32_t* __restrict__ q_seq,
@@ -348,6 +349,7 @@ static size_t attend_ws_for(int Q, int nsplit) {
 }
 
 size_t attend_ws_bytes(int Q, int k) {
+  if (Q >= AT_WIDE_MIN_Q) return 0;
   int nsplit, cps;
   attend_plan(Q, k, nsplit, cps);
   return attend_ws_for(Q, nsplit);
@@ -358,6 +360,10 @@ hipError_t launch_attend(const uint16_t* q, const int32_t* q_seq, int Q, const u
                          const uint8_t* swa_codes, const float* swa_scale, int64_t T_swa,
                          const int64_t* swa_start, const int32_t* swa_len, float* out, float* lse,
                          void* ws, size_t ws_bytes, hipStream_t stream) {
+  // many queries (prefill): one workgroup per query over all heads
+  if (Q >= AT_WIDE_MIN_Q)
+    return launch_attend_wide(q, q_seq, Q, kv_codes, kv_scales, cap, idx, k, swa_codes, swa_scale,
+                              T_swa, swa_start, swa_len, out, lse, stream);
   int nsplit, cps;
   attend_plan(Q, k, nsplit, cps);
   const int nch = (k + AT_ROWS - 1) / AT_ROWS + AT_MAX_SWA / AT_ROWS;

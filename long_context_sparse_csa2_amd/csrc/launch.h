@@ -32,6 +32,12 @@ hipError_t launch_attend(const uint16_t* q, const int32_t* q_seq, int Q, const u
                          const int64_t* swa_start, const int32_t* swa_len, float* out, float* lse,
                          void* ws, size_t ws_bytes, hipStream_t stream);
 
+hipError_t launch_attend_wide(const uint16_t* q, const int32_t* q_seq, int Q,
+                              const uint8_t* kv_codes, const uint8_t* kv_scales, int64_t cap,
+                              const int32_t* idx, int k, const uint8_t* swa_codes,
+                              const float* swa_scale, int64_t T_swa, const int64_t* swa_start,
+                              const int32_t* swa_len, float* out, float* lse, hipStream_t stream);
+
 int selftest_count();
 hipError_t launch_selftest(int32_t* counts, hipStream_t stream);
 

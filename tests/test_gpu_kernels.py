@@ -207,9 +207,11 @@ def _swa(nseq, T_swa, seed):
     return codes, scale
 
 
-@pytest.mark.parametrize("Q,k", [(2, 512), (3, 100), (300, 64)])
+@pytest.mark.parametrize("Q,k", [(2, 512), (3, 100), (255, 513), (256, 2048), (300, 64), (260, 1)])
 def test_sparse_attend(Q, k):
-    B, N = 2, 1500
+    """Decode-sized batches take the split-row kernel, 256 queries and more
+    the one-workgroup-per-query kernel; both against the oracle."""
+    B, N = 2, max(1500, k + 300)
     _, _, _, cache = _build(B, N, 1, seed=31 + Q)
     rng = np.random.default_rng(Q)
     g = torch.Generator().manual_seed(Q)
@@ -235,23 +237,25 @@ def test_sparse_attend(Q, k):
     kv_c = checks.host(cache.kv_codes)
     kv_s = checks.host(cache.kv_scales)
     sc_np, ss_np = swa_c.numpy(), swa_s.double().numpy()
-    for i in range(min(Q, 40)):
+    check_q = sorted(set(range(min(Q, 24))) | set(rng.integers(0, Q, 16).tolist()) | {Q - 1})
+    for i in check_q:
         b = q_seq[i]
         rows = R.gather_rows(kv_c[b], kv_s[b], idx[i], sc_np[b, start[i]:start[i] + slen[i]],
                              ss_np[b, start[i]:start[i] + slen[i]])
         checks.check_attention(o[i], l[i], q64[i], rows)
 
 
-def test_sparse_attend_no_rows():
+@pytest.mark.parametrize("Q", [1, 256])
+def test_sparse_attend_no_rows(Q):
     _, _, _, cache = _build(1, 64, 1, seed=2)
-    q = torch.zeros(1, 64, 512, dtype=torch.bfloat16, device=DEV)
-    idx = torch.full((1, 8), -1, dtype=torch.int32, device=DEV)
-    out = torch.full((1, 64, 512), 5.0, device=DEV)
-    lse = torch.zeros(1, 64, device=DEV)
-    z64 = torch.zeros(1, dtype=torch.int64, device=DEV)
-    z32 = torch.zeros(1, dtype=torch.int32, device=DEV)
+    q = torch.zeros(Q, 64, 512, dtype=torch.bfloat16, device=DEV)
+    idx = torch.full((Q, 8), -1, dtype=torch.int32, device=DEV)
+    out = torch.full((Q, 64, 512), 5.0, device=DEV)
+    lse = torch.zeros(Q, 64, device=DEV)
+    z64 = torch.zeros(Q, dtype=torch.int64, device=DEV)
+    z32 = torch.zeros(Q, dtype=torch.int32, device=DEV)
     C.csa2_sparse_attend(q, z32, cache, idx, None, None, z64, z32, out, lse,
-                         C.workspace(C.CSA2_OP_ATTEND, 1, 0, 8, DEV))
+                         C.workspace(C.CSA2_OP_ATTEND, Q, 0, 8, DEV))
     torch.cuda.synchronize()
     assert torch.all(out == 0) and torch.all(torch.isinf(lse)) and torch.all(lse < 0)
 
