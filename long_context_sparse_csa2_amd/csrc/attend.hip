@@ -8,49 +8,49 @@
 // value; section 2.4.4: main KV is dequantised from FP4 before attention,
 // SWA KV stays FP8.
 //
-// Design.  A workgroup owns (query, 16 heads, a run of 64-row chunks).
-// Main-KV chunks and SWA chunks are separate, so every chunk has one row
-// type and the MFMAs stay in uniform control flow.  Per chunk:
-//   S = Q K^T   16 heads x 64 rows, 16x16x32 bf16 MFMA; each wave takes 16
-//               rows and each lane streams the 64 code bytes (or 128 FP8
-//               bytes) of one row quarter straight from HBM into the B
-//               operand, converting FP4 with the gfx950 conversion at scale
-//               1 and applying the E4M3 group scale in fp32 (exact);
-//               the query tile sits in registers for the whole run.
-//   softmax     running max / sum per head, reductions through LDS.
-//   O += P V    16 heads x 512 dims, 16x16x32 fp16 MFMA: P (fp16) and V^T
-//               (fp16, exact for FP4 values) are staged in LDS; wave w owns
-//               output dims 128w..128w+127.
+// Design.  A workgroup of 256 threads owns (query, 16 heads, a run of
+// 64-row chunks).  Main-KV chunks and SWA chunks are separate, so every
+// chunk has one row type and the MFMAs stay in uniform control flow.
+//   query     the 16 heads' rows are converted once to fp16 in LDS, each
+//             head scaled by a power of two (undone on the scores).
+//   staging   thread t loads the (t & 63)-th row's quarter t >> 6 straight
+//             from HBM (its own idx lookup, no barrier in between) and
+//             writes it dequantised to fp16 in LDS (see attend_stage.h).
+//   S = Q K^T 16 heads x 64 rows, 16x16x32 fp16 MFMA, wave w rows 16w..+15.
+//   softmax   running max / sum per head, reductions through LDS.
+//   O += P V  16 heads x 512 dims, 16x16x32 fp16 MFMA, wave w dims
+//             128w..+127; V columns come from the staged rows through
+//             transposing LDS reads.
 // Decode (few queries) splits the chunks of a query over several
 // workgroups and merges the partial (max, sum, O) by log-sum-exp in a second
 // kernel (merging in the last workgroup to finish needs an agent-scope fence,
 // which writes back the whole L2 of its XCD on MI355X and measured 4x slower).
-// Prefill runs one workgroup per (query, head group) over all chunks and
-// writes the result directly.
 #include "common.h"
 #include "launch.h"
+#include "attend_stage.h"
 
 namespace csa2 {
 
-constexpr int AT_ROWS = 64;        // rows per chunk
 constexpr int AT_HG = 16;          // heads per workgroup
 constexpr int AT_PAD = 8;          // fp16 padding of an LDS row
 constexpr int AT_MAX_SWA = 128;
 constexpr int AT_TARGET_WG = 1024; // workgroups a decode launch aims for
 constexpr int AT_WIDE_MIN_Q = 256;  // from this many queries on, one workgroup per query
 
-__global__ __launch_bounds__(256, 2) void k_attend(
+__global__ __launch_bounds__(256, 1) void k_attend(
     const uint16_t* __restrict__ qv, const int32_t* __restrict__ q_seq,
     const uint8_t* __restrict__ kv_codes, const uint8_t* __restrict__ kv_scales, int64_t cap,
     const int32_t* __restrict__ idx, int k, const uint8_t* __restrict__ swa_codes,
     const float* __restrict__ swa_scale, int64_t T_swa, const int64_t* __restrict__ swa_start,
     const int32_t* __restrict__ swa_len, float* __restrict__ out, float* __restrict__ lse,
     float* __restrict__ part_o, float* __restrict__ part_ml, int nsplit, int cps) {
-  __shared__ __align__(16) _Float16 vt[D_LAT][AT_ROWS + AT_PAD];   // V^T of the chunk
-  __shared__ __align__(16) _Float16 pl[AT_HG][AT_ROWS + AT_PAD];   // P of the chunk
+  __shared__ __align__(16) _Float16 kv[2][CH_ROWS * KV_LD];         // K (+ V of main rows), V of SWA rows
+  __shared__ __align__(16) _Float16 qs[AT_HG][D_LAT + AT_PAD];     // fp16 query rows
+  __shared__ __align__(16) _Float16 pl[AT_HG][CH_ROWS + AT_PAD];   // P of the chunk
   __shared__ float red_m[4][AT_HG], red_l[4][AT_HG];
-  __shared__ int64_t rowoff[AT_ROWS];                               // entry / SWA row, -1 = none
-  __shared__ float rowsig[AT_ROWS];
+  __shared__ int64_t rowoff[CH_ROWS];                               // entry / SWA row, -1 = none
+  __shared__ float rowsig[CH_ROWS];
+  __shared__ float qinv[AT_HG];                                     // 2^-e of each head
 
   const int sp = blockIdx.x % nsplit;
   const int hq = blockIdx.x / nsplit;
@@ -63,30 +63,52 @@ __global__ __launch_bounds__(256, 2) void k_attend(
   if (sst < 0 || sst >= T_swa) sl64 = 0;                     // window clipped to [0, T_swa)
   else if (sl64 > T_swa - sst) sl64 = T_swa - sst;
   const int sl = sl64 < 0 ? 0 : (sl64 > AT_MAX_SWA ? AT_MAX_SWA : (int)sl64);
-  const int nmc = (k + AT_ROWS - 1) / AT_ROWS;
-  const int nch = nmc + (sl + AT_ROWS - 1) / AT_ROWS;
+  const int nmc = (k + CH_ROWS - 1) / CH_ROWS;
+  const int nch = nmc + (sl + CH_ROWS - 1) / CH_ROWS;
   const int ch_beg = sp * cps;
   const int ch_end = min(ch_beg + cps, nch);
 
-  // query tile: head hg*16 + r16, dims 128*qd + 8s .. +7 for step s
-  bf16x8_t a[16];
+  // ---- query: thread t converts head t >> 4, dims 32 (t & 15) .. +31
   {
-    const uint16_t* qp = qv + ((int64_t)q * H_ATT + hg * AT_HG + r16) * D_LAT + qd * 128;
+    const int hh = tid >> 4, part = tid & 15;
+    const bf16x8_t* qp = (const bf16x8_t*)(qv + ((int64_t)q * H_ATT + hg * AT_HG + hh) * D_LAT +
+                                           part * 32);
+    bf16x8_t x[4];
 #pragma unroll
-    for (int s = 0; s < 16; ++s) a[s] = *(const bf16x8_t*)(qp + 8 * s);
+    for (int i = 0; i < 4; ++i) x[i] = qp[i];
+    float mx = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) mx = fmaxf(mx, fabsf((float)x[i][j]));
+#pragma unroll
+    for (int off = 1; off < 16; off <<= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+    const int e = q_exponent(mx);
+    const float f = ldexpf(1.f, e);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      f16x8_t y;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) y[j] = (_Float16)((float)x[i][j] * f);
+      *(f16x8_t*)&qs[hh][part * 32 + 8 * i] = y;
+    }
+    if (part == 0) qinv[hh] = ldexpf(1.f, -e);
   }
+
+  f16x8_t a[16];                  // query tile: head r16, dims 32 s + 8 qd .. +7 for step s
   f32x4_t o[8];
 #pragma unroll
   for (int t = 0; t < 8; ++t) o[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  float m_run[4], l_run[4];
+  float m_run[4], l_run[4], hinv[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) { m_run[j] = -INFINITY; l_run[j] = 0.f; }
 
   for (int ch = ch_beg; ch < ch_end; ++ch) {
     const bool is_main = ch < nmc;                 // uniform over the workgroup
-    const int rbase = is_main ? ch * AT_ROWS : (ch - nmc) * AT_ROWS;
-    if (tid < AT_ROWS) {
-      const int r = rbase + tid;
+    const int rbase = is_main ? ch * CH_ROWS : (ch - nmc) * CH_ROWS;
+    // ---- stage: thread t takes row t & 63, quarter t >> 6
+    {
+      const int r = rbase + (tid & 63);
       int64_t off = -1;
       float sg = 1.f;
       if (is_main) {
@@ -98,101 +120,30 @@ __global__ __launch_bounds__(256, 2) void k_attend(
         off = seq * T_swa + sst + r;
         sg = swa_scale[off];
       }
-      rowoff[tid] = off;
-      rowsig[tid] = sg;
+      const bool valid = off >= 0;
+      const int64_t rd = valid ? off : (is_main ? seq * cap : seq * T_swa + sst);   // a readable row
+      RawShare<256> raw;
+      load_share<256>(raw, is_main, rd, tid >> 6, kv_codes, kv_scales, swa_codes);
+      if (tid < CH_ROWS) { rowoff[tid] = off; rowsig[tid] = sg; }
+      store_share<256>(raw, is_main, valid, sg, kv[0], kv[1], tid & 63, tid >> 6);
     }
     __syncthreads();
-
-    // ---- issue this thread's V^T staging loads before the QK^T work: rows
-    //      2rp, 2rp+1, dims 64db .. +63 (main: 32 code bytes + 4 scale bytes
-    //      per row; SWA: 64 FP8 bytes per row)
-    const int rp = tid & 31, db = tid >> 5;
-    const int64_t voff0 = rowoff[2 * rp], voff1 = rowoff[2 * rp + 1];
-    u32x4_t va[4], vb[4];
-    uint32_t vs0 = 0, vs1 = 0;
-    if (is_main) {
-      const int64_t e0 = voff0 >= 0 ? voff0 : seq * cap, e1 = voff1 >= 0 ? voff1 : seq * cap;
-      const u32x4_t* c0p = (const u32x4_t*)(kv_codes + e0 * 256 + db * 32);
-      const u32x4_t* c1p = (const u32x4_t*)(kv_codes + e1 * 256 + db * 32);
-      va[0] = c0p[0]; va[1] = c0p[1]; vb[0] = c1p[0]; vb[1] = c1p[1];
-      vs0 = *(const uint32_t*)(kv_scales + e0 * 32 + db * 4);
-      vs1 = *(const uint32_t*)(kv_scales + e1 * 32 + db * 4);
-    } else {
-      const int64_t r0 = voff0 >= 0 ? voff0 : seq * T_swa + sst;
-      const int64_t r1 = voff1 >= 0 ? voff1 : seq * T_swa + sst;
-      const u32x4_t* c0p = (const u32x4_t*)(swa_codes + r0 * 512 + db * 64);
-      const u32x4_t* c1p = (const u32x4_t*)(swa_codes + r1 * 512 + db * 64);
+    if (ch == ch_beg) {
 #pragma unroll
-      for (int i2 = 0; i2 < 4; ++i2) { va[i2] = c0p[i2]; vb[i2] = c1p[i2]; }
+      for (int s = 0; s < 16; ++s) a[s] = *(const f16x8_t*)&qs[r16][32 * s + 8 * qd];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) hinv[j] = qinv[4 * qd + j];
     }
 
     // ---- S = Q K^T for rows 16*wave .. +15 (lane column r16)
     const int lr = wave * 16 + r16;
-    const int64_t myoff = rowoff[lr];
-    const bool valid = myoff >= 0;
     f32x4_t sacc = {0.f, 0.f, 0.f, 0.f};
-    if (is_main) {
-      const int64_t ent = valid ? myoff : seq * cap;
-      const u32x4_t* cp = (const u32x4_t*)(kv_codes + ent * 256 + qd * 64);
-      const u32x4_t w0 = cp[0], w1 = cp[1], w2 = cp[2], w3 = cp[3];
-      const uint64_t sc = *(const uint64_t*)(kv_scales + ent * 32 + qd * 8);
-      const u32x4_t wq[4] = {w0, w1, w2, w3};
 #pragma unroll
-      for (int s = 0; s < 16; ++s) {
-        const float scl = e4m3_val((uint32_t)(sc >> (8 * (s >> 1))) & 0xFFu);
-        sacc = mfma16_bf16(a[s], fp4x8_to_bf16_scaled(wq[s >> 2][s & 3], scl), sacc);
-      }
-    } else {
-      const int64_t rr = valid ? myoff : seq * T_swa + sst;
-      const u32x4_t* cp = (const u32x4_t*)(swa_codes + rr * 512 + qd * 128);
+    for (int s = 0; s < 16; ++s) sacc = mfma16_f16(a[s], qk_b(kv[0], lr, s, qd), sacc);
+    const bool valid = rowoff[lr] >= 0;
+    const float rs = is_main ? 1.f : rowsig[lr];
 #pragma unroll
-      for (int s2 = 0; s2 < 8; ++s2) {
-        const u32x4_t wv = cp[s2];
-        sacc = mfma16_bf16(a[2 * s2], fp8x8_to_bf16(wv[0], wv[1]), sacc);
-        sacc = mfma16_bf16(a[2 * s2 + 1], fp8x8_to_bf16(wv[2], wv[3]), sacc);
-      }
-      const float sg = rowsig[lr];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) sacc[j] *= sg;
-    }
-    if (!valid) {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) sacc[j] = -INFINITY;
-    }
-
-    // ---- stage V^T (fp16) from the loaded bytes
-    {
-      _Float16* vcol = &vt[db * 64][2 * rp];
-      auto put8 = [&](int dim0, f16x8_t x0, f16x8_t x1) {
-#pragma unroll
-        for (int b = 0; b < 8; ++b) {
-          f16x2_t pr;
-          pr[0] = voff0 >= 0 ? x0[b] : (_Float16)0.f;
-          pr[1] = voff1 >= 0 ? x1[b] : (_Float16)0.f;
-          *(f16x2_t*)(vcol + (dim0 + b) * (AT_ROWS + AT_PAD)) = pr;
-        }
-      };
-      if (is_main) {
-#pragma unroll
-        for (int h2 = 0; h2 < 2; ++h2) {
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {            // 8 dims per word, 2 words per scale group
-            const int wi = 4 * h2 + i;
-            put8(8 * wi, fp4x8_to_f16_scaled(va[h2][i], e4m3_val((vs0 >> (8 * (wi >> 1))) & 0xFFu)),
-                 fp4x8_to_f16_scaled(vb[h2][i], e4m3_val((vs1 >> (8 * (wi >> 1))) & 0xFFu)));
-          }
-        }
-      } else {
-        const float g0 = rowsig[2 * rp], g1 = rowsig[2 * rp + 1];
-#pragma unroll
-        for (int i2 = 0; i2 < 4; ++i2) {           // 16 dims per 16-byte load
-          put8(16 * i2, fp8x8_to_f16_scaled(va[i2][0], va[i2][1], g0),
-               fp8x8_to_f16_scaled(vb[i2][0], vb[i2][1], g1));
-          put8(16 * i2 + 8, fp8x8_to_f16_scaled(va[i2][2], va[i2][3], g0),
-               fp8x8_to_f16_scaled(vb[i2][2], vb[i2][3], g1));
-        }
-      }
-    }
+    for (int j = 0; j < 4; ++j) sacc[j] = valid ? sacc[j] * hinv[j] * rs : -INFINITY;
 
     // ---- online softmax over this chunk
     float cm[4];
@@ -245,15 +196,14 @@ __global__ __launch_bounds__(256, 2) void k_attend(
     }
 
     // ---- O += P V for dims 128*wave .. +127
+    const _Float16* vrows = is_main ? kv[0] : kv[1];
     const f16x8_t pa0 = *(const f16x8_t*)&pl[r16][qd * 8];
     const f16x8_t pa1 = *(const f16x8_t*)&pl[r16][32 + qd * 8];
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
-      const int dim = wave * 128 + 16 * t + r16;
-      const f16x8_t vb0 = *(const f16x8_t*)&vt[dim][qd * 8];
-      const f16x8_t vb1 = *(const f16x8_t*)&vt[dim][32 + qd * 8];
-      o[t] = mfma16_f16(pa0, vb0, o[t]);
-      o[t] = mfma16_f16(pa1, vb1, o[t]);
+      const int n0 = wave * 128 + 16 * t;
+      o[t] = mfma16_f16(pa0, pv_b(vrows, 0, n0, lane), o[t]);
+      o[t] = mfma16_f16(pa1, pv_b(vrows, 32, n0, lane), o[t]);
     }
     __syncthreads();
   }
@@ -331,7 +281,7 @@ __global__ __launch_bounds__(128) void k_attend_combine(const float* __restrict_
 
 // ------------------------------------------------------------ host side
 static void attend_plan(int Q, int k, int& nsplit, int& cps) {
-  const int nch = (k + AT_ROWS - 1) / AT_ROWS + AT_MAX_SWA / AT_ROWS;
+  const int nch = (k + CH_ROWS - 1) / CH_ROWS + AT_MAX_SWA / CH_ROWS;
   const int groups = Q * (H_ATT / AT_HG);
   int want = (AT_TARGET_WG + groups - 1) / groups;
   if (want < 1) want = 1;
@@ -366,7 +316,7 @@ hipError_t launch_attend(const uint16_t* q, const int32_t* q_seq, int Q, const u
                               T_swa, swa_start, swa_len, out, lse, stream);
   int nsplit, cps;
   attend_plan(Q, k, nsplit, cps);
-  const int nch = (k + AT_ROWS - 1) / AT_ROWS + AT_MAX_SWA / AT_ROWS;
+  const int nch = (k + CH_ROWS - 1) / CH_ROWS + AT_MAX_SWA / CH_ROWS;
   while (nsplit > 1 && (ws == nullptr || attend_ws_for(Q, nsplit) > ws_bytes)) {
     ++cps;                                   // fewer, longer splits until the partials fit
     nsplit = (nch + cps - 1) / cps;

@@ -98,12 +98,20 @@ __global__ __launch_bounds__(256) void k_maxima(const float* __restrict__ scores
 }
 
 // ------------------------------------------------------------ select
-// One workgroup of NT threads (1024, or 256 for small rounds) per query.  The candidates of one round (at
-// most SEL_CAP, in id order) live in registers, thread-major: thread t holds
-// candidates 16t .. 16t + 15, loaded with 16-byte vector loads, so the
-// order-preserving compaction is one block scan of per-thread counts.
+// One workgroup of NT threads (1024, or 256 for small rounds) per query.
+// The candidates of one round (at most SEL_CAP, in id order) live in
+// registers, thread-major: thread t holds candidates 16t .. 16t + 15 (in the
+// first round 16 consecutive groups, later the 8 children of parents 2t and
+// 2t + 1), so the order-preserving compaction is one block scan of
+// per-thread counts.
+//
+// Floor.  A round keeps its best kk parents; each kept parent's maximum
+// child has the parent's key, so when the next round wants at most as many
+// as were kept, its answer lies among the children whose key is at least
+// the smallest kept key (the floor) and the children below it are dropped
+// before the threshold search.
 constexpr int SEL_PER = 16;                        // candidates per thread
-constexpr int SEL_SMALL = 256;
+constexpr int SEL_SMALL = 64;                      // intervals this small are ranked exactly
 constexpr int SEL_BINS = 2048;
 
 template <int NT>
@@ -113,6 +121,7 @@ struct SelShared {
   uint32_t small[SEL_SMALL];
   uint32_t red[2][(NT / 64)];
   uint32_t mm[2][(NT / 64)];
+  uint32_t cn[2][(NT / 64)];
   uint32_t bc[4][4];
 };
 
@@ -135,8 +144,17 @@ __device__ __forceinline__ uint32_t block_scan(uint32_t v, uint32_t* red, uint32
   return incl + pre;
 }
 
-// Threshold of the best kk of the cnt candidates (cnt > kk >= 1), given
-// their min and max keys; nv = this thread's candidate count.
+// Bit i set iff candidate i is considered and its key lies in [lo, hi].
+__device__ __forceinline__ uint32_t range_mask(const uint32_t (&kr)[SEL_PER], uint32_t cmask,
+                                               uint32_t lo, uint32_t hi) {
+  uint32_t m = 0;
+#pragma unroll
+  for (int i = 0; i < SEL_PER; ++i) m |= (kr[i] >= lo && kr[i] <= hi) ? (1u << i) : 0u;
+  return m & cmask;
+}
+
+// Threshold of the best kk of the m considered candidates (m > kk >= 1),
+// given their min and max keys; cmask = this thread's considered ones.
 //
 // Search on the key interval [lo, hi] that holds the kk-th best key: each
 // pass bins the keys inside it by (key - lo) >> s, with s chosen so that at
@@ -145,31 +163,39 @@ __device__ __forceinline__ uint32_t block_scan(uint32_t v, uint32_t* red, uint32
 // SEL_SMALL candidates their exact kk-th key is found by ranking them
 // against each other.  Result: keys above hi are in, keys inside [lo, hi]
 // are in for the first `tie_lim` of them in candidate (= id) order, keys
-// below lo are out.  The histogram must be zero on entry and is left zero.
+// below lo are out.  The histogram must be zero on entry and is left zero;
+// so is the gather counter sh.bc[3][3].
 template <int NT>
-__device__ __forceinline__ void threshold_search(const uint32_t (&kr)[SEL_PER], int nv, int cnt,
-                                                 int kk, uint32_t mn, uint32_t mx, SelShared<NT>& sh,
-                                                 uint32_t& lo_out, uint32_t& hi_out,
-                                                 uint32_t& tie_out) {
-  const int tid = threadIdx.x;
+__device__ __forceinline__ void threshold_search(const uint32_t (&kr)[SEL_PER], uint32_t cmask,
+                                                 int m, int kk, uint32_t mn, uint32_t mx,
+                                                 SelShared<NT>& sh, uint32_t& lo_out,
+                                                 uint32_t& hi_out, uint32_t& tie_out) {
+  const int tid = threadIdx.x, lane = tid & 63;
   uint32_t lo = mn, hi = mx;
   uint32_t krem = (uint32_t)kk;
-  uint32_t incnt = (uint32_t)cnt;          // candidates with key in [lo, hi]
+  uint32_t incnt = (uint32_t)m;            // considered candidates with key in [lo, hi]
   uint32_t tie_lim;
   int pass = 0;
   while (true) {
     if (lo == hi) { tie_lim = krem; break; }
+    const uint32_t imask = range_mask(kr, cmask, lo, hi);
     if (incnt <= (uint32_t)SEL_SMALL) {
-      // gather the interval's keys, rank each against all (4 threads each)
+      // gather the interval's keys: wave prefix of per-thread counts, one
+      // LDS atomic per wave for the wave's base
+      const uint32_t c = (uint32_t)__popc(imask);
+      const uint32_t incl = wave_incl_sum(c);
+      uint32_t base = 0;
+      if (lane == 63) base = atomicAdd(&sh.bc[3][3], incl);
+      base = (uint32_t)__builtin_amdgcn_readlane((int)base, 63);
+      uint32_t pos = base + incl - c;
 #pragma unroll
-      for (int i = 0; i < SEL_PER; ++i) {
-        const uint32_t k = kr[i];
-        if (i < nv && k >= lo && k <= hi) sh.small[atomicAdd(&sh.bc[3][3], 1u)] = k;
-      }
+      for (int i = 0; i < SEL_PER; ++i)
+        if ((imask >> i) & 1u) sh.small[pos++] = kr[i];
       __syncthreads();
-      constexpr int RS = NT / SEL_SMALL;           // threads ranking one candidate
-      const int c = tid / RS, part = tid % RS;
-      const uint32_t mine = c < (int)incnt ? sh.small[c] : 0u;
+      // rank each gathered key against all of them, RS threads per key
+      constexpr int RS = NT / SEL_SMALL;
+      const int ci = tid / RS, part = tid % RS;
+      const uint32_t mine = ci < (int)incnt ? sh.small[ci] : 0u;
       uint32_t gt = 0, ge = 0;
       for (uint32_t j = part; j < incnt; j += RS) {
         const uint32_t o = sh.small[j];
@@ -178,7 +204,7 @@ __device__ __forceinline__ void threshold_search(const uint32_t (&kr)[SEL_PER], 
       }
 #pragma unroll
       for (int off = 1; off < RS; off <<= 1) { gt += __shfl_xor(gt, off); ge += __shfl_xor(ge, off); }
-      if (part == 0 && c < (int)incnt && gt < krem && ge >= krem) { sh.bc[2][0] = mine; sh.bc[2][1] = gt; }
+      if (part == 0 && ci < (int)incnt && gt < krem && ge >= krem) { sh.bc[2][0] = mine; sh.bc[2][1] = gt; }
       __syncthreads();
       const uint32_t t = sh.bc[2][0], g = sh.bc[2][1];
       if (tid == 0) sh.bc[3][3] = 0u;     // gather counter; next used after further barriers
@@ -190,10 +216,8 @@ __device__ __forceinline__ void threshold_search(const uint32_t (&kr)[SEL_PER], 
     const int bits = 32 - __clz(span);
     const int shf = bits > 11 ? bits - 11 : 0;
 #pragma unroll
-    for (int i = 0; i < SEL_PER; ++i) {
-      const uint32_t k = kr[i];
-      if (i < nv && k >= lo && k <= hi) atomicAdd(&sh.hist[(k - lo) >> shf], 1u);
-    }
+    for (int i = 0; i < SEL_PER; ++i)
+      if ((imask >> i) & 1u) atomicAdd(&sh.hist[(kr[i] - lo) >> shf], 1u);
     __syncthreads();
     // thread t owns (SEL_BINS / NT) consecutive bins from the top, counted downwards
     uint32_t hb[(SEL_BINS / NT)];
@@ -219,7 +243,6 @@ __device__ __forceinline__ void threshold_search(const uint32_t (&kr)[SEL_PER], 
         acc += hb[j];
       }
     }
-    if (tid == 0) sh.bc[3][3] = 0u;                                   // gather counter
     __syncthreads();
     const uint32_t d = bcp[0], above = bcp[1], inbin = bcp[2];
     ++pass;
@@ -237,51 +260,20 @@ __device__ __forceinline__ void threshold_search(const uint32_t (&kr)[SEL_PER], 
   tie_out = tie_lim;
 }
 
-// 16 consecutive keys of a level array (uint32 keys) or of the scores (fp32,
-// turned into keys) starting at index base, of which the first `n` are valid;
-// vec: the array and base are 16-byte aligned.
-__device__ __forceinline__ void load16(const uint32_t* lv, const float* sc, int64_t base, int n,
-                                       bool vec, uint32_t (&kr)[SEL_PER]) {
-  if (vec && n >= 16) {
+// Raw words of 8 consecutive entries b .. b+7 of a level array or a score
+// row into raw[off .. off + 8).  vec: the 8 words lie inside the row and
+// start 16-byte aligned (two vector loads); otherwise word j is read at
+// min(b + j, len - 1) and the caller masks the ones at or past len.
+__device__ __forceinline__ void load_run8(const uint32_t* src, int64_t b, int64_t len, bool vec,
+                                          uint32_t (&raw)[SEL_PER], int off) {
+  if (vec) {
+    const u32x4_t x0 = *(const u32x4_t*)(src + b);
+    const u32x4_t x1 = *(const u32x4_t*)(src + b + 4);
 #pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      if (sc) {
-        const f32x4_t x = *(const f32x4_t*)(sc + base + 4 * v);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) kr[4 * v + j] = f32_key(x[j]);
-      } else {
-        const u32x4_t x = *(const u32x4_t*)(lv + base + 4 * v);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) kr[4 * v + j] = x[j];
-      }
-    }
+    for (int j = 0; j < 4; ++j) { raw[off + j] = x0[j]; raw[off + 4 + j] = x1[j]; }
   } else {
 #pragma unroll
-    for (int i = 0; i < SEL_PER; ++i)
-      kr[i] = i < n ? (sc ? f32_key(sc[base + i]) : lv[base + i]) : 0u;
-  }
-}
-
-// 8 consecutive keys (one parent's children) into kr[off .. off + 8).
-__device__ __forceinline__ void load8(const uint32_t* lv, const float* sc, int64_t base, int n,
-                                      bool vec, uint32_t (&kr)[SEL_PER], int off) {
-  if (vec && n >= 8) {
-#pragma unroll
-    for (int v = 0; v < 2; ++v) {
-      if (sc) {
-        const f32x4_t x = *(const f32x4_t*)(sc + base + 4 * v);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) kr[off + 4 * v + j] = f32_key(x[j]);
-      } else {
-        const u32x4_t x = *(const u32x4_t*)(lv + base + 4 * v);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) kr[off + 4 * v + j] = x[j];
-      }
-    }
-  } else {
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-      kr[off + i] = i < n ? (sc ? f32_key(sc[base + i]) : lv[base + i]) : 0u;
+    for (int j = 0; j < 8; ++j) raw[off + j] = src[b + j < len ? b + j : len - 1];
   }
 }
 
@@ -290,7 +282,7 @@ __global__ __launch_bounds__(NT) void k_select(
     const float* __restrict__ scores, int64_t ld, const int64_t* __restrict__ n_valid,
     const int32_t* __restrict__ col_ids, int64_t n_cols, LevelDesc d,
     const uint32_t* __restrict__ ws, int kk, int mode, int32_t* __restrict__ out, int64_t out_ld,
-    int64_t* __restrict__ out_len, int k2, int32_t* __restrict__ out2, int vec) {
+    int64_t* __restrict__ out_len, int k2, int32_t* __restrict__ out2, int vec0) {
   __shared__ SelShared<NT> sh;
   const int q = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -313,20 +305,20 @@ __global__ __launch_bounds__(NT) void k_select(
   for (int j = 0; j < (SEL_BINS / NT); ++j) sh.hist[(SEL_BINS / NT) * tid + j] = 0u;
   if (tid == 0) sh.bc[3][3] = 0u;
 
-  uint32_t kr[SEL_PER];
   int cur = 0;                      // sh.lists[cur]: parents of the round being loaded
   int lvl = 0;
   while (groups_at(n, lvl) > (int64_t)NT * SEL_PER) ++lvl;
   if (lvl < stop) lvl = stop;
   bool first = true;
   int pcnt = 0;
-  int cnt = 0;
   int rb = 0;                       // alternates the reduction buffers between rounds
+  uint32_t floor_key = 0;           // children below it cannot be in this round's answer
 
   while (true) {
-    // ---- load the candidates of level lvl (thread t: 16t .. 16t+15) and their key range
+    // ---- candidates of level lvl (thread t: 16t .. 16t+15), every load in flight at once
     const uint32_t* par = sh.lists[cur];
     const int64_t gl = groups_at(n, lvl);
+    int cnt;
     if (first) {
       cnt = (int)gl;
     } else {
@@ -335,79 +327,93 @@ __global__ __launch_bounds__(NT) void k_select(
     }
     const int e0 = SEL_PER * tid;
     const int nv = cnt - e0 < 0 ? 0 : (cnt - e0 > SEL_PER ? SEL_PER : cnt - e0);
-    const uint32_t* lv = lvl == 0 ? nullptr : ws + d.off[lvl] + (int64_t)q * d.stride[lvl];
-    const float* sc = lvl == 0 ? srow : nullptr;
-    const bool vok = lvl > 0 || vec;                 // 16-byte aligned rows
+    const bool is_score = lvl == 0;
+    const uint32_t* src = is_score ? (const uint32_t*)srow
+                                   : ws + d.off[lvl] + (int64_t)q * d.stride[lvl];
+    const bool vok = !is_score || vec0;              // level rows are padded to 16 words
+    uint32_t kr[SEL_PER];
+#pragma unroll
+    for (int i = 0; i < SEL_PER; ++i) kr[i] = 0u;
     uint32_t p0 = 0, p1 = 0;
     if (nv > 0) {
-      if (first) {
-        load16(lv, sc, e0, nv, vok, kr);
-      } else {
+      int64_t b0 = e0, b1 = e0 + 8;
+      if (!first) {
         // candidates 16t .. 16t+15 are the children of parents 2t and 2t+1
         p0 = par[e0 >> 3];
-        p1 = nv > 8 ? par[(e0 >> 3) + 1] : 0u;
-        const int64_t b0 = (int64_t)p0 * 8, b1 = (int64_t)p1 * 8;
-        const int n0c = nv < 8 ? nv : 8;
-        const int n1c = nv > 8 ? nv - 8 : 0;
-        load8(lv, sc, b0, n0c, vok, kr, 0);
-        load8(lv, sc, b1, n1c, vok, kr, 8);
+        p1 = nv > 8 ? par[(e0 >> 3) + 1] : p0;
+        b0 = (int64_t)p0 * 8;
+        b1 = (int64_t)p1 * 8;
+      }
+      load_run8(src, b0, gl, vok, kr, 0);
+      load_run8(src, b1, gl, vok, kr, 8);
+      if (is_score) {
+#pragma unroll
+        for (int i = 0; i < SEL_PER; ++i) kr[i] = f32_key(__uint_as_float(kr[i]));
       }
     }
-    uint32_t mn = 0xFFFFFFFFu, mx = 0u;
+    // ---- considered candidates: valid and at or above the floor
+    uint32_t cmask = 0, mn = 0xFFFFFFFFu, mx = 0u;
 #pragma unroll
     for (int i = 0; i < SEL_PER; ++i) {
-      if (i < nv) { mn = min(mn, kr[i]); mx = max(mx, kr[i]); }
+      const bool c = i < nv && kr[i] >= floor_key;
+      cmask |= c ? (1u << i) : 0u;
+      mn = c ? min(mn, kr[i]) : mn;
+      mx = c ? max(mx, kr[i]) : mx;
     }
     const int want = (lvl == 0 && mode == 1) ? k2 : kk;
-    // ---- threshold (skipped when everything is kept)
+    mn = wave_min_all(mn);
+    mx = wave_max_all(mx);
+    const uint32_t wc = (uint32_t)__builtin_amdgcn_readlane((int)wave_incl_sum((uint32_t)__popc(cmask)), 63);
+    if (lane == 0) { sh.red[rb][wave] = mn; sh.mm[rb][wave] = mx; sh.cn[rb][wave] = wc; }
+    __syncthreads();
+    int m = 0;
+#pragma unroll
+    for (int w = 0; w < (NT / 64); ++w) {
+      mn = min(mn, sh.red[rb][w]);
+      mx = max(mx, sh.mm[rb][w]);
+      m += (int)sh.cn[rb][w];
+    }
+    // ---- threshold (skipped when every considered candidate is kept)
     uint32_t lo = 0, hi = 0, tl = 0;
-    const bool all = cnt <= want;
-    if (!all) {
-      mn = wave_min_all(mn);
-      mx = wave_max_all(mx);
-      if (lane == 0) { sh.red[rb][wave] = mn; sh.mm[rb][wave] = mx; }
-      __syncthreads();
-#pragma unroll
-      for (int w = 0; w < (NT / 64); ++w) { mn = min(mn, sh.red[rb][w]); mx = max(mx, sh.mm[rb][w]); }
-      threshold_search<NT>(kr, nv, cnt, want, mn, mx, sh, lo, hi, tl);
-    }
+    const bool all = m <= want;
+    if (!all) threshold_search<NT>(kr, cmask, m, want, mn, mx, sh, lo, hi, tl);
     // ---- order-preserving compaction of the kept ids into sh.lists[cur ^ 1]
-    uint32_t ngt = 0, ntie = 0;
-#pragma unroll
-    for (int i = 0; i < SEL_PER; ++i) {
-      if (i < nv) {
-        ngt += all || kr[i] > hi;
-        ntie += !all && kr[i] >= lo && kr[i] <= hi;
-      }
+    uint32_t gm = cmask, tm = 0;
+    if (!all) {
+      gm = range_mask(kr, cmask, hi + 1u, 0xFFFFFFFFu);
+      if (hi == 0xFFFFFFFFu) gm = 0;
+      tm = range_mask(kr, cmask, lo, hi);
     }
+    const uint32_t ngt = (uint32_t)__popc(gm), ntie = (uint32_t)__popc(tm);
     const uint32_t packed = ngt | (ntie << 16);           // both sums stay below 2^16
     uint32_t tot;
     const uint32_t excl = block_scan<NT>(packed, sh.red[rb ^ 1], tot) - packed;
     const uint32_t gt_before = excl & 0xFFFFu, tie_before = excl >> 16;
+    // this thread's ties in id order while the tie limit lasts
+    uint32_t take = tl > tie_before ? tl - tie_before : 0u;
+    uint32_t tk = 0, trest = tm;
+    while (take > 0 && trest != 0) {
+      tk |= trest & (0u - trest);
+      trest &= trest - 1u;
+      --take;
+    }
+    const uint32_t km = gm | tk;
     uint32_t* keep = sh.lists[cur ^ 1];
     uint32_t pos = gt_before + min(tie_before, tl);
-    uint32_t tr = tie_before;
-    const bool map_cols = lvl == stop && mode == 0 && col_ids;
 #pragma unroll
     for (int i = 0; i < SEL_PER; ++i) {
-      if (i < nv) {
-        const bool g = all || kr[i] > hi;
-        const bool t = !all && kr[i] >= lo && kr[i] <= hi;
-        if (g || (t && tr < tl)) {
-          const int e = e0 + i;
-          uint32_t id = first ? (uint32_t)e : (i < 8 ? p0 : p1) * 8u + (uint32_t)(e & 7);
-          keep[pos++] = id;
-        }
-        tr += t;
+      if ((km >> i) & 1u) {
+        keep[pos++] = first ? (uint32_t)(e0 + i) : (i < 8 ? p0 : p1) * 8u + (uint32_t)(i & 7);
       }
     }
-    const int kept = all ? cnt : (int)((tot & 0xFFFFu) + min(tot >> 16, tl));
+    const int kept = all ? m : (int)((tot & 0xFFFFu) + min(tot >> 16, tl));
     __syncthreads();
     cur ^= 1;
     rb ^= 1;
     first = false;
     pcnt = kept;
     const uint32_t* sel = sh.lists[cur];
+    const bool map_cols = lvl == stop && mode == 0 && col_ids;
 
     if (lvl == stop && mode == 0) {
       for (int i = tid; i < kk; i += NT) {
@@ -438,6 +444,8 @@ __global__ __launch_bounds__(NT) void k_select(
       return;
     }
     --lvl;
+    const int want_next = (lvl == 0 && mode == 1) ? k2 : kk;
+    floor_key = kept >= want_next ? (all ? mn : lo) : 0u;
   }
 }
 
@@ -451,7 +459,7 @@ static LevelDesc make_levels(int Q, int64_t n_cols, int mode) {
   int64_t off = 0;
   for (int l = 1; l <= L; ++l) {
     d.off[l] = off;
-    d.stride[l] = (groups_at(n_cols, l) + 3) / 4 * 4;    // 16-byte aligned rows
+    d.stride[l] = (groups_at(n_cols, l) + 15) / 16 * 16; // 64-byte aligned rows
     off += (int64_t)Q * d.stride[l];
   }
   return d;
@@ -470,10 +478,12 @@ hipError_t launch_select(const float* scores, int64_t ld, int Q, const int64_t* 
                          hipStream_t stream) {
   const LevelDesc d = make_levels(Q, n_cols, mode);
   const int64_t nchunk = (n_cols + 4095) / 4096;
-  const int vec = (ld % 4 == 0) && (((uintptr_t)scores & 15) == 0);   // 16-byte row starts
+  const bool al16 = ((uintptr_t)scores & 15) == 0;
+  const int vec_max = (ld % 4 == 0) && al16;    // 16-byte row starts
+  const int vec = (ld % 16 == 0) && al16;       // every run of 8 / 16 scores inside its row
   if (d.nlev > 0 && nchunk > 0) {
     hipLaunchKernelGGL(k_maxima, dim3((unsigned)(nchunk * Q)), dim3(256), 0, stream, scores, ld,
-                       n_valid, n_cols, nchunk, d, (uint32_t*)ws, vec);
+                       n_valid, n_cols, nchunk, d, (uint32_t*)ws, vec_max);
   }
   // one round over at most 4096 candidates: 256-thread workgroups, several per CU
   if (mode == 0 && n_cols <= 256 * SEL_PER)

@@ -82,7 +82,7 @@ def test_select_and_pool_validation():
     # workspace needed above 16384 columns
     assert L.csa2_select_topk(P, 20000, 1, P, None, 20000, 5, P, None, 0, None) == 3
     need = C.csa2_workspace_bytes(C.CSA2_OP_TOPK, 1, 20000, 5)
-    assert need == 4 * 2500
+    assert need == 4 * 2512                 # 2500 block maxima, rows padded to 16 words
     assert L.csa2_select_topk(P, 20000, 1, P, None, 20000, 5, P, P, need - 1, None) == 3
     assert L.csa2_block_pool(P, 100, 1, P, 100, 16, 4, P, P, 0, None, P, 1 << 20, None) == 2
     assert L.csa2_block_pool(P, 100, 1, P, 100, 8, 0, P, P, 0, None, P, 1 << 20, None) == 1
