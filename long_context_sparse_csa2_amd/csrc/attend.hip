@@ -68,6 +68,27 @@ __global__ __launch_bounds__(256, 1) void k_attend(
   const int ch_beg = sp * cps;
   const int ch_end = min(ch_beg + cps, nch);
 
+  // this thread's staging row (row t & 63 of chunk ch): flat row, -1 = none
+  auto row_of = [&](int ch, float& sg) __attribute__((always_inline)) {
+    const bool main_ch = ch < nmc;
+    const int r = (main_ch ? ch * CH_ROWS : (ch - nmc) * CH_ROWS) + (tid & 63);
+    int64_t off = -1;
+    sg = 1.f;
+    if (main_ch) {
+      if (r < k) {
+        const int e = idx[(int64_t)q * k + r];
+        if (e >= 0) off = seq * cap + e;
+      }
+    } else if (r < sl) {
+      off = seq * T_swa + sst + r;
+      sg = swa_scale[off];
+    }
+    return off;
+  };
+  // the first chunk's row id is in flight before the query work
+  float nsg = 1.f;
+  int64_t noff = ch_beg < ch_end ? row_of(ch_beg, nsg) : -1;
+
   // ---- query: thread t converts head t >> 4, dims 32 (t & 15) .. +31
   {
     const int hh = tid >> 4, part = tid & 15;
@@ -81,8 +102,7 @@ __global__ __launch_bounds__(256, 1) void k_attend(
     for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int j = 0; j < 8; ++j) mx = fmaxf(mx, fabsf((float)x[i][j]));
-#pragma unroll
-    for (int off = 1; off < 16; off <<= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+    mx = row16_max(mx);                          // the 16 threads of head hh
     const int e = q_exponent(mx);
     const float f = ldexpf(1.f, e);
 #pragma unroll
@@ -105,21 +125,10 @@ __global__ __launch_bounds__(256, 1) void k_attend(
 
   for (int ch = ch_beg; ch < ch_end; ++ch) {
     const bool is_main = ch < nmc;                 // uniform over the workgroup
-    const int rbase = is_main ? ch * CH_ROWS : (ch - nmc) * CH_ROWS;
     // ---- stage: thread t takes row t & 63, quarter t >> 6
     {
-      const int r = rbase + (tid & 63);
-      int64_t off = -1;
-      float sg = 1.f;
-      if (is_main) {
-        if (r < k) {
-          const int e = idx[(int64_t)q * k + r];
-          if (e >= 0) off = seq * cap + e;
-        }
-      } else if (r < sl) {
-        off = seq * T_swa + sst + r;
-        sg = swa_scale[off];
-      }
+      float sg = nsg;
+      const int64_t off = ch == ch_beg ? noff : row_of(ch, sg);
       const bool valid = off >= 0;
       const int64_t rd = valid ? off : (is_main ? seq * cap : seq * T_swa + sst);   // a readable row
       RawShare<256> raw;
@@ -148,14 +157,7 @@ __global__ __launch_bounds__(256, 1) void k_attend(
     // ---- online softmax over this chunk
     float cm[4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      float v = sacc[j];
-      v = fmaxf(v, __shfl_xor(v, 1));
-      v = fmaxf(v, __shfl_xor(v, 2));
-      v = fmaxf(v, __shfl_xor(v, 4));
-      v = fmaxf(v, __shfl_xor(v, 8));
-      cm[j] = v;
-    }
+    for (int j = 0; j < 4; ++j) cm[j] = row16_max(sacc[j]);      // over the 16 rows of the wave
     if (r16 == 0) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) red_m[wave][4 * qd + j] = cm[j];
@@ -179,11 +181,7 @@ __global__ __launch_bounds__(256, 1) void k_attend(
     }
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      float v = p[j];
-      v += __shfl_xor(v, 1);
-      v += __shfl_xor(v, 2);
-      v += __shfl_xor(v, 4);
-      v += __shfl_xor(v, 8);
+      const float v = row16_sum(p[j]);
       if (r16 == 0) red_l[wave][4 * qd + j] = v;
     }
     __syncthreads();
@@ -236,47 +234,53 @@ __global__ __launch_bounds__(256, 1) void k_attend(
 }
 
 // Merge the per-split partial states of one (query, head) by log-sum-exp.
-// Every split wrote its state (an empty split: max -inf, sum 0, O = 0), so
-// the weighted sum runs without branches and its loads overlap.
+// Every split wrote its state (an empty split: max -inf, sum 0, O = 0).  A
+// thread owns 4 dims; it loads the states of 16 splits at a time, all
+// loads in flight together (indices past the last split re-read the last
+// one with weight 0), then folds them into a running (max, sum, O).
 constexpr int AT_MAX_SPLITS = 64;
+constexpr int AT_MERGE_BATCH = 16;
 
 __global__ __launch_bounds__(128) void k_attend_combine(const float* __restrict__ part_o,
                                                         const float* __restrict__ part_ml,
                                                         int nsplit, float* __restrict__ out,
                                                         float* __restrict__ lse) {
-  __shared__ float wgt[AT_MAX_SPLITS];
-  __shared__ float sums[2];
   const int qh = blockIdx.x;              // q * 64 + head
   const int q = qh / H_ATT, h = qh % H_ATT;
-  const int tid = threadIdx.x;
-  float m = -INFINITY, l = 0.f;
-  if (tid < nsplit) {
-    const int64_t slot = ((int64_t)q * nsplit + tid) * H_ATT + h;
-    m = part_ml[2 * slot];
-    l = part_ml[2 * slot + 1];
-    if (!(l > 0.f)) m = -INFINITY;
-  }
-  float M = m;                            // max over the first wave (nsplit <= 64)
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
-  const float wv = (tid < nsplit && l > 0.f) ? expf(m - M) : 0.f;
-  float L = l * wv;
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) L += __shfl_xor(L, off);
-  if (tid < AT_MAX_SPLITS) wgt[tid] = wv;
-  if (tid == 0) { sums[0] = M; sums[1] = L; }
-  __syncthreads();
-  M = sums[0];
-  L = sums[1];
+  const int d0 = threadIdx.x * 4;
+  const int64_t slot0 = (int64_t)q * nsplit * H_ATT + h;    // split s: slot0 + s * H_ATT
+  float M = -INFINITY, L = 0.f;
   f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-  const int d0 = tid * 4;
-  const float* op = part_o + (((int64_t)q * nsplit) * H_ATT + h) * D_LAT + d0;
-  const int64_t sstride = (int64_t)H_ATT * D_LAT;
-#pragma unroll 8
-  for (int s2 = 0; s2 < nsplit; ++s2) acc += *(const f32x4_t*)(op + s2 * sstride) * wgt[s2];
+  for (int s0 = 0; s0 < nsplit; s0 += AT_MERGE_BATCH) {
+    f32x2_t ml[AT_MERGE_BATCH];
+    f32x4_t ov[AT_MERGE_BATCH];
+#pragma unroll
+    for (int i = 0; i < AT_MERGE_BATCH; ++i) {
+      const int si = s0 + i < nsplit ? s0 + i : nsplit - 1;
+      const int64_t slot = slot0 + (int64_t)si * H_ATT;
+      ml[i] = *(const f32x2_t*)(part_ml + 2 * slot);
+      ov[i] = *(const f32x4_t*)(part_o + slot * D_LAT + d0);
+    }
+    float bm = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < AT_MERGE_BATCH; ++i)
+      if (s0 + i < nsplit && ml[i][1] > 0.f) bm = fmaxf(bm, ml[i][0]);
+    const float nM = fmaxf(M, bm);
+    if (nM == -INFINITY) continue;                      // nothing attended so far
+    const float sc = expf(M - nM);                      // 0 while M is -inf
+    L *= sc;
+    acc *= sc;
+#pragma unroll
+    for (int i = 0; i < AT_MERGE_BATCH; ++i) {
+      const float w = (s0 + i < nsplit && ml[i][1] > 0.f) ? expf(ml[i][0] - nM) : 0.f;
+      L += ml[i][1] * w;
+      acc += ov[i] * w;
+    }
+    M = nM;
+  }
   const float inv = L > 0.f ? 1.f / L : 0.f;
   *(f32x4_t*)(out + (int64_t)qh * D_LAT + d0) = acc * inv;
-  if (lse && tid == 0) lse[qh] = L > 0.f ? M + logf(L) : -INFINITY;
+  if (lse && threadIdx.x == 0) lse[qh] = L > 0.f ? M + logf(L) : -INFINITY;
 }
 
 // ------------------------------------------------------------ host side

@@ -158,12 +158,7 @@ __global__ __launch_bounds__(AW_THREADS, 1) void k_attend_wide(
     float cm[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      float v = fmaxf(sacc[0][j], sacc[1][j]);
-      v = fmaxf(v, __shfl_xor(v, 1));
-      v = fmaxf(v, __shfl_xor(v, 2));
-      v = fmaxf(v, __shfl_xor(v, 4));
-      v = fmaxf(v, __shfl_xor(v, 8));
-      cm[j] = v;
+      cm[j] = row16_max(fmaxf(sacc[0][j], sacc[1][j]));
     }
     if (r16 == 0) {
 #pragma unroll
@@ -189,11 +184,7 @@ __global__ __launch_bounds__(AW_THREADS, 1) void k_attend_wide(
           pl[hh][half * 32 + rt * 16 + r16] = (_Float16)p;
         }
       }
-      psum += __shfl_xor(psum, 1);
-      psum += __shfl_xor(psum, 2);
-      psum += __shfl_xor(psum, 4);
-      psum += __shfl_xor(psum, 8);
-      l_run[j] = l_run[j] * alpha[j] + psum;        // this wave's rows only
+      l_run[j] = l_run[j] * alpha[j] + row16_sum(psum);   // this wave's rows only
       m_run[j] = m_new;
     }
     __syncthreads();

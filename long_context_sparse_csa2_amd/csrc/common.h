@@ -171,6 +171,12 @@ __device__ __forceinline__ f16x8_t fp8x8_to_f16_scaled(uint32_t lo, uint32_t hi,
   return r;
 }
 
+// max(x, 0) as one integer max on the bit pattern: every float with the
+// sign bit set (including -0) becomes +0, the rest is unchanged.
+__device__ __forceinline__ float relu_f32(float x) {
+  return __int_as_float(max(__float_as_int(x), 0));
+}
+
 // ------------------------------------------------------------------ MFMA
 // 32x32x16 bf16: A lane l holds A[l%32][8(l/32) .. +7]; B lane l holds
 // B[8(l/32) .. +7][l%32]; D lane l element j is D[8(j/4) + 4(l/32) + j%4][l%32].
@@ -211,6 +217,29 @@ __device__ __forceinline__ uint32_t wave_max_all(uint32_t v) {
 }
 __device__ __forceinline__ uint32_t wave_min_all(uint32_t v) {
   return (uint32_t)__builtin_amdgcn_readlane((int)wave_scan_dpp(v, OpMin(), 0xFFFFFFFFu), 63);
+}
+
+// Max / sum over the 16 lanes of a DPP row (lanes 16r .. 16r + 15), every
+// lane getting the result: xor-1 and xor-2 quad permutations, then the
+// half-row and row mirrors (each step pairs groups that already agree, so
+// all 16 lanes end with the same value).
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xf, 0xf, false));
+}
+__device__ __forceinline__ float row16_max(float v) {
+  v = fmaxf(v, dpp_mov<0xb1>(v));     // quad_perm [1,0,3,2]
+  v = fmaxf(v, dpp_mov<0x4e>(v));     // quad_perm [2,3,0,1]
+  v = fmaxf(v, dpp_mov<0x141>(v));    // row_half_mirror
+  v = fmaxf(v, dpp_mov<0x140>(v));    // row_mirror
+  return v;
+}
+__device__ __forceinline__ float row16_sum(float v) {
+  v += dpp_mov<0xb1>(v);
+  v += dpp_mov<0x4e>(v);
+  v += dpp_mov<0x141>(v);
+  v += dpp_mov<0x140>(v);
+  return v;
 }
 
 // ------------------------------------------------------------ score keys

@@ -102,7 +102,7 @@ __global__ __launch_bounds__(256) void k_index_score(
     acc = mfma32_bf16(a[7], fp4x8_to_bf16_pow2(c1[3], s_hi), acc);
     float part = 0.f;
 #pragma unroll
-    for (int j = 0; j < 16; ++j) part += wr[j] * fmaxf(acc[j], 0.f);
+    for (int j = 0; j < 16; ++j) part += wr[j] * relu_f32(acc[j]);
     part += __shfl_xor(part, 32);
     const int64_t c = col0 + r;
     if (half == 0 && c < nv) srow[c] = part;

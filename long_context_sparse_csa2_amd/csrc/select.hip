@@ -145,11 +145,12 @@ __device__ __forceinline__ uint32_t block_scan(uint32_t v, uint32_t* red, uint32
 }
 
 // Bit i set iff candidate i is considered and its key lies in [lo, hi].
-__device__ __forceinline__ uint32_t range_mask(const uint32_t (&kr)[SEL_PER], uint32_t cmask,
+template <int PER>
+__device__ __forceinline__ uint32_t range_mask(const uint32_t (&kr)[PER], uint32_t cmask,
                                                uint32_t lo, uint32_t hi) {
   uint32_t m = 0;
 #pragma unroll
-  for (int i = 0; i < SEL_PER; ++i) m |= (kr[i] >= lo && kr[i] <= hi) ? (1u << i) : 0u;
+  for (int i = 0; i < PER; ++i) m |= (kr[i] >= lo && kr[i] <= hi) ? (1u << i) : 0u;
   return m & cmask;
 }
 
@@ -165,8 +166,8 @@ __device__ __forceinline__ uint32_t range_mask(const uint32_t (&kr)[SEL_PER], ui
 // are in for the first `tie_lim` of them in candidate (= id) order, keys
 // below lo are out.  The histogram must be zero on entry and is left zero;
 // so is the gather counter sh.bc[3][3].
-template <int NT>
-__device__ __forceinline__ void threshold_search(const uint32_t (&kr)[SEL_PER], uint32_t cmask,
+template <int NT, int PER>
+__device__ __forceinline__ void threshold_search(const uint32_t (&kr)[PER], uint32_t cmask,
                                                  int m, int kk, uint32_t mn, uint32_t mx,
                                                  SelShared<NT>& sh, uint32_t& lo_out,
                                                  uint32_t& hi_out, uint32_t& tie_out) {
@@ -178,7 +179,7 @@ __device__ __forceinline__ void threshold_search(const uint32_t (&kr)[SEL_PER], 
   int pass = 0;
   while (true) {
     if (lo == hi) { tie_lim = krem; break; }
-    const uint32_t imask = range_mask(kr, cmask, lo, hi);
+    const uint32_t imask = range_mask<PER>(kr, cmask, lo, hi);
     if (incnt <= (uint32_t)SEL_SMALL) {
       // gather the interval's keys: wave prefix of per-thread counts, one
       // LDS atomic per wave for the wave's base
@@ -189,7 +190,7 @@ __device__ __forceinline__ void threshold_search(const uint32_t (&kr)[SEL_PER], 
       base = (uint32_t)__builtin_amdgcn_readlane((int)base, 63);
       uint32_t pos = base + incl - c;
 #pragma unroll
-      for (int i = 0; i < SEL_PER; ++i)
+      for (int i = 0; i < PER; ++i)
         if ((imask >> i) & 1u) sh.small[pos++] = kr[i];
       __syncthreads();
       // rank each gathered key against all of them, RS threads per key
@@ -216,7 +217,7 @@ __device__ __forceinline__ void threshold_search(const uint32_t (&kr)[SEL_PER], 
     const int bits = 32 - __clz(span);
     const int shf = bits > 11 ? bits - 11 : 0;
 #pragma unroll
-    for (int i = 0; i < SEL_PER; ++i)
+    for (int i = 0; i < PER; ++i)
       if ((imask >> i) & 1u) atomicAdd(&sh.hist[(kr[i] - lo) >> shf], 1u);
     __syncthreads();
     // thread t owns (SEL_BINS / NT) consecutive bins from the top, counted downwards
@@ -260,6 +261,76 @@ __device__ __forceinline__ void threshold_search(const uint32_t (&kr)[SEL_PER], 
   tie_out = tie_lim;
 }
 
+// One keep-best-`want` round over the candidates this thread holds in
+// kr[0 .. nv) (thread-major: ids increase with the thread, then the slot):
+// candidates below floor_key are dropped, the threshold of the rest found
+// and the kept ids written in id order to `keep` (id_of(i) is slot i's id).
+// rb picks the reduction buffers (alternate it between rounds).  Ends with a
+// barrier; returns the kept count, the threshold interval's low end and the
+// smallest considered key (the next round's floor), and whether every
+// considered candidate was kept.
+struct RoundOut {
+  int kept;
+  uint32_t lo, mn;
+  bool all;
+};
+
+template <int NT, int PER, typename IdOf>
+__device__ __forceinline__ RoundOut select_round(const uint32_t (&kr)[PER], int nv, uint32_t floor_key,
+                                                 int want, SelShared<NT>& sh, int rb, uint32_t* keep,
+                                                 IdOf id_of) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  uint32_t cmask = 0, mn = 0xFFFFFFFFu, mx = 0u;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const bool c = i < nv && kr[i] >= floor_key;
+    cmask |= c ? (1u << i) : 0u;
+    mn = c ? min(mn, kr[i]) : mn;
+    mx = c ? max(mx, kr[i]) : mx;
+  }
+  mn = wave_min_all(mn);
+  mx = wave_max_all(mx);
+  const uint32_t wc = (uint32_t)__builtin_amdgcn_readlane((int)wave_incl_sum((uint32_t)__popc(cmask)), 63);
+  if (lane == 0) { sh.red[rb][wave] = mn; sh.mm[rb][wave] = mx; sh.cn[rb][wave] = wc; }
+  __syncthreads();
+  int m = 0;
+#pragma unroll
+  for (int w = 0; w < (NT / 64); ++w) {
+    mn = min(mn, sh.red[rb][w]);
+    mx = max(mx, sh.mm[rb][w]);
+    m += (int)sh.cn[rb][w];
+  }
+  uint32_t lo = 0, hi = 0, tl = 0;
+  const bool all = m <= want;
+  if (!all) threshold_search<NT, PER>(kr, cmask, m, want, mn, mx, sh, lo, hi, tl);
+  uint32_t gm = cmask, tm = 0;
+  if (!all) {
+    gm = hi == 0xFFFFFFFFu ? 0u : range_mask<PER>(kr, cmask, hi + 1u, 0xFFFFFFFFu);
+    tm = range_mask<PER>(kr, cmask, lo, hi);
+  }
+  const uint32_t ngt = (uint32_t)__popc(gm), ntie = (uint32_t)__popc(tm);
+  const uint32_t packed = ngt | (ntie << 16);           // both sums stay below 2^16
+  uint32_t tot;
+  const uint32_t excl = block_scan<NT>(packed, sh.red[rb ^ 1], tot) - packed;
+  const uint32_t gt_before = excl & 0xFFFFu, tie_before = excl >> 16;
+  // this thread's ties in id order while the tie limit lasts
+  uint32_t take = tl > tie_before ? tl - tie_before : 0u;
+  uint32_t tk = 0, trest = tm;
+  while (take > 0 && trest != 0) {
+    tk |= trest & (0u - trest);
+    trest &= trest - 1u;
+    --take;
+  }
+  const uint32_t km = gm | tk;
+  uint32_t pos = gt_before + min(tie_before, tl);
+#pragma unroll
+  for (int i = 0; i < PER; ++i)
+    if ((km >> i) & 1u) keep[pos++] = id_of(i);
+  const int kept = all ? m : (int)((tot & 0xFFFFu) + min(tot >> 16, tl));
+  __syncthreads();
+  return RoundOut{kept, lo, mn, all};
+}
+
 // Raw words of 8 consecutive entries b .. b+7 of a level array or a score
 // row into raw[off .. off + 8).  vec: the 8 words lie inside the row and
 // start 16-byte aligned (two vector loads); otherwise word j is read at
@@ -285,7 +356,7 @@ __global__ __launch_bounds__(NT) void k_select(
     int64_t* __restrict__ out_len, int k2, int32_t* __restrict__ out2, int vec0) {
   __shared__ SelShared<NT> sh;
   const int q = blockIdx.x;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x;
   const int64_t n0 = n_valid[q];
   const int64_t n = n0 < 0 ? 0 : (n0 < n_cols ? n0 : n_cols);
   const float* srow = scores + (int64_t)q * ld;
@@ -351,63 +422,12 @@ __global__ __launch_bounds__(NT) void k_select(
         for (int i = 0; i < SEL_PER; ++i) kr[i] = f32_key(__uint_as_float(kr[i]));
       }
     }
-    // ---- considered candidates: valid and at or above the floor
-    uint32_t cmask = 0, mn = 0xFFFFFFFFu, mx = 0u;
-#pragma unroll
-    for (int i = 0; i < SEL_PER; ++i) {
-      const bool c = i < nv && kr[i] >= floor_key;
-      cmask |= c ? (1u << i) : 0u;
-      mn = c ? min(mn, kr[i]) : mn;
-      mx = c ? max(mx, kr[i]) : mx;
-    }
     const int want = (lvl == 0 && mode == 1) ? k2 : kk;
-    mn = wave_min_all(mn);
-    mx = wave_max_all(mx);
-    const uint32_t wc = (uint32_t)__builtin_amdgcn_readlane((int)wave_incl_sum((uint32_t)__popc(cmask)), 63);
-    if (lane == 0) { sh.red[rb][wave] = mn; sh.mm[rb][wave] = mx; sh.cn[rb][wave] = wc; }
-    __syncthreads();
-    int m = 0;
-#pragma unroll
-    for (int w = 0; w < (NT / 64); ++w) {
-      mn = min(mn, sh.red[rb][w]);
-      mx = max(mx, sh.mm[rb][w]);
-      m += (int)sh.cn[rb][w];
-    }
-    // ---- threshold (skipped when every considered candidate is kept)
-    uint32_t lo = 0, hi = 0, tl = 0;
-    const bool all = m <= want;
-    if (!all) threshold_search<NT>(kr, cmask, m, want, mn, mx, sh, lo, hi, tl);
-    // ---- order-preserving compaction of the kept ids into sh.lists[cur ^ 1]
-    uint32_t gm = cmask, tm = 0;
-    if (!all) {
-      gm = range_mask(kr, cmask, hi + 1u, 0xFFFFFFFFu);
-      if (hi == 0xFFFFFFFFu) gm = 0;
-      tm = range_mask(kr, cmask, lo, hi);
-    }
-    const uint32_t ngt = (uint32_t)__popc(gm), ntie = (uint32_t)__popc(tm);
-    const uint32_t packed = ngt | (ntie << 16);           // both sums stay below 2^16
-    uint32_t tot;
-    const uint32_t excl = block_scan<NT>(packed, sh.red[rb ^ 1], tot) - packed;
-    const uint32_t gt_before = excl & 0xFFFFu, tie_before = excl >> 16;
-    // this thread's ties in id order while the tie limit lasts
-    uint32_t take = tl > tie_before ? tl - tie_before : 0u;
-    uint32_t tk = 0, trest = tm;
-    while (take > 0 && trest != 0) {
-      tk |= trest & (0u - trest);
-      trest &= trest - 1u;
-      --take;
-    }
-    const uint32_t km = gm | tk;
-    uint32_t* keep = sh.lists[cur ^ 1];
-    uint32_t pos = gt_before + min(tie_before, tl);
-#pragma unroll
-    for (int i = 0; i < SEL_PER; ++i) {
-      if ((km >> i) & 1u) {
-        keep[pos++] = first ? (uint32_t)(e0 + i) : (i < 8 ? p0 : p1) * 8u + (uint32_t)(i & 7);
-      }
-    }
-    const int kept = all ? m : (int)((tot & 0xFFFFu) + min(tot >> 16, tl));
-    __syncthreads();
+    const RoundOut ro = select_round<NT, SEL_PER>(
+        kr, nv, floor_key, want, sh, rb, sh.lists[cur ^ 1], [&](int i) __attribute__((always_inline)) {
+          return first ? (uint32_t)(e0 + i) : (i < 8 ? p0 : p1) * 8u + (uint32_t)(i & 7);
+        });
+    const int kept = ro.kept;
     cur ^= 1;
     rb ^= 1;
     first = false;
@@ -445,7 +465,7 @@ __global__ __launch_bounds__(NT) void k_select(
     }
     --lvl;
     const int want_next = (lvl == 0 && mode == 1) ? k2 : kk;
-    floor_key = kept >= want_next ? (all ? mn : lo) : 0u;
+    floor_key = kept >= want_next ? (ro.all ? ro.mn : ro.lo) : 0u;
   }
 }
 
@@ -486,11 +506,11 @@ hipError_t launch_select(const float* scores, int64_t ld, int Q, const int64_t* 
                        n_valid, n_cols, nchunk, d, (uint32_t*)ws, vec_max);
   }
   // one round over at most 4096 candidates: 256-thread workgroups, several per CU
-  if (mode == 0 && n_cols <= 256 * SEL_PER)
+  if (mode == 0 && n_cols <= 256 * SEL_PER) {
     hipLaunchKernelGGL(k_select<256>, dim3((unsigned)Q), dim3(256), 0, stream, scores, ld, n_valid,
                        col_ids, n_cols, d, (const uint32_t*)ws, kk, mode, out, out_ld, out_len, k2,
                        out2, vec);
-  else
+  } else
     hipLaunchKernelGGL(k_select<1024>, dim3((unsigned)Q), dim3(1024), 0, stream, scores, ld,
                        n_valid, col_ids, n_cols, d, (const uint32_t*)ws, kk, mode, out, out_ld,
                        out_len, k2, out2, vec);

@@ -137,7 +137,8 @@ def _topk(s, nv, k, col_ids=None):
 
 
 @pytest.mark.parametrize("n,k", [(1, 1), (100, 512), (511, 512), (512, 512), (513, 512),
-                                 (5000, 7), (20000, 512), (70000, 2048), (200000, 512)])
+                                 (5000, 7), (6000, 2048), (9001, 600), (16384, 1), (16384, 512),
+                                 (16384, 2048), (20000, 512), (70000, 2048), (200000, 512)])
 def test_select_topk(n, k):
     Q = 3
     s = _rand_scores(Q, n, seed=n + k)
@@ -147,10 +148,11 @@ def test_select_topk(n, k):
         checks.check_topk_exact(out[i], s[i, :nv[i]], k)
 
 
-def test_select_topk_all_equal_and_empty():
-    s = np.zeros((2, 3000), np.float32)
-    out = _topk(s, [3000, 0], 512)
-    assert np.array_equal(out[0], np.arange(512))
+@pytest.mark.parametrize("n", [3000, 10000])
+def test_select_topk_all_equal_and_empty(n):
+    s = np.zeros((2, n), np.float32)
+    out = _topk(s, [n, 0], 512)
+    assert np.array_equal(out[0], np.arange(512))      # ties go to the lowest ids
     assert np.all(out[1] == -1)
 
 
