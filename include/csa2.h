@@ -22,7 +22,12 @@
  *     library does not implement, CSA2_EWORKSPACE for a short workspace)
  *     and sets csa2_last_error().  Launch failures return CSA2_EHIP.
  *   - The contents of device arrays (indices, cache bytes) are not checked;
- *     out-of-range indices are undefined behaviour.
+ *     out-of-range indices are undefined behaviour.  With CSA2_CHECK=1 in
+ *     the environment, csa2_index_score (q_seq >= 0, candidate ids in
+ *     [0, cap)) and csa2_sparse_attend (q_seq >= 0, idx in [-1, cap)) first
+ *     range-check their index arrays on the device, synchronise the stream
+ *     and return CSA2_EINVAL naming the array if any value is out of range
+ *     (checked calls are synchronous and must not be graph-captured).
  *   - No exception or abort crosses the ABI.  Calls are thread-safe.
  *
  * Cache layout (one KV-producing layer, B sequences, `cap` entries each,

@@ -8,6 +8,8 @@
 #include <cstdarg>
 #include <cstdint>
 #include <cstdio>
+#include <cstdlib>
+#include <cstring>
 
 #include "launch.h"
 
@@ -40,6 +42,31 @@ csa2_status check_cache(const csa2_cache* c) {
   if (c->cap <= 0) return fail(CSA2_EINVAL, "cache cap=%lld must be > 0", (long long)c->cap);
   return CSA2_OK;
 }
+
+// CSA2_CHECK=1 in the environment: device index arrays are range-checked
+// (synchronously) before the kernels that use them run.
+bool device_checks() {
+  const char* v = getenv("CSA2_CHECK");
+  return v && strcmp(v, "1") == 0;
+}
+
+csa2_status check_indices(const char* what, const int32_t* a, int64_t rows, int64_t ld,
+                          const int64_t* len, int64_t ncols, int64_t lo, int64_t hi,
+                          void* stream) {
+  unsigned int bad = 0;
+  const hipError_t e = csa2::check_range(a, rows, ld, len, ncols, lo, hi, (hipStream_t)stream, &bad);
+  if (e != hipSuccess) return fail(CSA2_EHIP, "CSA2_CHECK %s: %s", what, hipGetErrorString(e));
+  if (bad)
+    return fail(CSA2_EINVAL, "CSA2_CHECK: %u value(s) of %s outside [%lld, %lld)", bad, what,
+                (long long)lo, (long long)hi);
+  return CSA2_OK;
+}
+
+#define CHECKED(call)                        \
+  do {                                       \
+    const csa2_status st_ = (call);          \
+    if (st_ != CSA2_OK) return st_;          \
+  } while (0)
 
 #define REQ(cond, ...)                                   \
   do {                                                   \
@@ -103,6 +130,11 @@ csa2_status csa2_index_score(const uint16_t* q_idx, const float* w, const int32_
   REQ(al(q_idx, 16) && al(w, 4) && al(scores, 4), "q_idx must be 16-byte aligned");
   if (n_cols == 0) return CSA2_OK;
   REQ((n_cols + 1023) / 1024 * (int64_t)Q < (int64_t)1 << 31, "launch too large");
+  if (device_checks()) {
+    CHECKED(check_indices("q_seq", q_seq, 1, Q, nullptr, Q, 0, INT32_MAX, stream));
+    if (cand)
+      CHECKED(check_indices("cand", cand, Q, ld_cand, n_vis, n_cols, 0, src->cap, stream));
+  }
   return hip_status(csa2::launch_index_score(q_idx, w, q_seq, n_vis, cand, ld_cand, Q, n_cols,
                                              src->ik_codes, src->ik_scales, src->cap, scores, ld,
                                              (hipStream_t)stream),
@@ -173,6 +205,10 @@ csa2_status csa2_sparse_attend(const uint16_t* q, const int32_t* q_seq, int Q, c
       "q, out, swa_codes must be 16-byte aligned");
   REQ(!ws || al(ws, 16), "ws must be 16-byte aligned");
   REQ(Q > 0 && Q <= (1 << 24), "Q=%d must be in [1, 2^24]", Q);
+  if (device_checks()) {
+    CHECKED(check_indices("q_seq", q_seq, 1, Q, nullptr, Q, 0, INT32_MAX, stream));
+    if (k > 0) CHECKED(check_indices("idx", idx, Q, k, nullptr, k, -1, src->cap, stream));
+  }
   return hip_status(csa2::launch_attend(q, q_seq, Q, src->kv_codes, src->kv_scales, src->cap, idx,
                                         k, swa_codes, swa_scale, T_swa, swa_start, swa_len, out,
                                         lse, ws, ws_bytes, (hipStream_t)stream),

@@ -38,6 +38,12 @@ hipError_t launch_attend_wide(const uint16_t* q, const int32_t* q_seq, int Q,
                               const float* swa_scale, int64_t T_swa, const int64_t* swa_start,
                               const int32_t* swa_len, float* out, float* lse, hipStream_t stream);
 
+// Counts the values of a[r][c] (r < rows, c < min(len[r], ncols)) outside
+// [lo, hi) into *bad (host); synchronises the stream.
+hipError_t check_range(const int32_t* a, int64_t rows, int64_t ld, const int64_t* len,
+                       int64_t ncols, int64_t lo, int64_t hi, hipStream_t stream,
+                       unsigned int* bad);
+
 int selftest_count();
 hipError_t launch_selftest(int32_t* counts, hipStream_t stream);
 

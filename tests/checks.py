@@ -120,7 +120,7 @@ def check_scores(gpu, ref):
     ref = np.asarray(ref, np.float64)
     if ref.size == 0:
         return 0.0
-    floor = 1e-3 * np.abs(ref).max()
+    floor = max(1e-3 * np.abs(ref).max(), np.finfo(np.float64).tiny)
     tol = SCORE_RTOL * np.maximum(np.abs(ref), floor)
     err = np.abs(gpu - ref)
     assert np.all(err <= tol), f"scores: max rel err {float((err / np.maximum(np.abs(ref), floor)).max()):.3e}"

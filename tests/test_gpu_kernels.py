@@ -114,6 +114,33 @@ def test_index_score_full_and_pool():
         assert np.all(p[i, lens[i]:] == -7.0)
 
 
+def test_index_score_many_queries():
+    """300 queries: a run sharing one sequence, then mixed sequences, ragged
+    and zero visible counts, a column count that is not a multiple of the
+    scan's tile."""
+    B, T, Q = 3, 1000, 300
+    _, _, _, cache = _build(B, T, 1, seed=23)
+    q, w = _scores_inputs(Q, 24)
+    rng = np.random.default_rng(5)
+    q_seq = np.zeros(Q, np.int32)
+    q_seq[160:] = rng.integers(0, B, Q - 160)          # mixed sequences from block 20 on
+    n_vis = (np.arange(Q) * 7 % (T + 1)).astype(np.int64)
+    n_vis[:40] = T
+    n_vis[41] = 0
+    scores = torch.full((Q, 1008), -7.0, device=DEV)
+    C.csa2_index_score(q.to(DEV), w.to(DEV), torch.from_numpy(q_seq).to(DEV),
+                       torch.from_numpy(n_vis).to(DEV), None, T, cache, scores)
+    torch.cuda.synchronize()
+    s = checks.host(scores)
+    q64, w64 = checks.bf16_to_f64(q), w.double().numpy()
+    khat = [R.dequant_mxfp4(checks.host(cache.ik_codes[b]), checks.host(cache.ik_scales[b])) for b in range(B)]
+    for i in range(Q):
+        nv = int(n_vis[i])
+        if nv:
+            checks.check_scores(s[i, :nv], R.index_scores(q64[i], w64[i], khat[q_seq[i]][:nv]))
+        assert np.all(s[i, nv:] == -7.0)
+
+
 def _rand_scores(Q, n, seed, ties=True):
     rng = np.random.default_rng(seed)
     s = (rng.standard_normal((Q, n)) ** 2).astype(np.float32)
@@ -260,6 +287,36 @@ def test_sparse_attend_no_rows(Q):
                          C.workspace(C.CSA2_OP_ATTEND, Q, 0, 8, DEV))
     torch.cuda.synchronize()
     assert torch.all(out == 0) and torch.all(torch.isinf(lse)) and torch.all(lse < 0)
+
+
+def test_check_mode_rejects_bad_indices(monkeypatch):
+    """CSA2_CHECK=1: out-of-range device indices are reported as CSA2_EINVAL
+    before any kernel reads through them; valid ones pass."""
+    B, N, Q, k = 2, 300, 2, 16
+    _, _, _, cache = _build(B, N, 1, seed=41)
+    q = torch.zeros(Q, 64, 512, dtype=torch.bfloat16, device=DEV)
+    q_seq = torch.tensor([0, 1], dtype=torch.int32, device=DEV)
+    z64 = torch.zeros(Q, dtype=torch.int64, device=DEV)
+    z32 = torch.zeros(Q, dtype=torch.int32, device=DEV)
+    out = torch.empty(Q, 64, 512, device=DEV)
+    ws = C.workspace(C.CSA2_OP_ATTEND, Q, 0, k, DEV)
+    idx = torch.arange(Q * k, dtype=torch.int32, device=DEV).reshape(Q, k)
+    monkeypatch.setenv("CSA2_CHECK", "1")
+    C.csa2_sparse_attend(q, q_seq, cache, idx, None, None, z64, z32, out, None, ws)
+    bad = idx.clone()
+    bad[1, 3] = N                                     # one past the cache capacity
+    with pytest.raises(C.Csa2Error, match="idx"):
+        C.csa2_sparse_attend(q, q_seq, cache, bad, None, None, z64, z32, out, None, ws)
+    qi, w = _scores_inputs(Q, 42)
+    cand = torch.zeros(Q, 40, dtype=torch.int32, device=DEV)
+    cand[0, 39] = -5                                  # outside [0, cap) but past n_vis[0]: ignored
+    nv = torch.tensor([39, 40], dtype=torch.int64, device=DEV)
+    sc = torch.empty(Q, 40, device=DEV)
+    C.csa2_index_score(qi.to(DEV), w.to(DEV), q_seq, nv, cand, 40, cache, sc)
+    cand[1, 10] = N
+    with pytest.raises(C.Csa2Error, match="cand"):
+        C.csa2_index_score(qi.to(DEV), w.to(DEV), q_seq, nv, cand, 40, cache, sc)
+    torch.cuda.synchronize()
 
 
 def test_c0_step():
