@@ -139,6 +139,27 @@ def index_scores(q_idx, w, khat):
     return np.maximum(dots, 0.0) @ np.asarray(w, dtype=np.float64)
 
 
+# ------------------------------------------------- f1 MXFP4 indexer query
+def quant_indexer_q(q_idx):
+    """MXFP4 form of the indexer query.  The report (section 2.4.4) says V4
+    already trains the indexer queries and keys for OCP MXFP4 so that the
+    index product runs as an FP4 matrix multiply; the commentary (section 5)
+    repeats it.  Reading: the rule of quant_mxfp4 (the OCP MX rule used for
+    the indexer K), applied per head to each 32-dim block of the bf16 query
+    as given.  [.., 32, 128] -> (codes [.., 32, 64] u8, scales [.., 32, 4] u8)."""
+    q = np.asarray(q_idx, dtype=np.float64)
+    c, s = quant_mxfp4(q.reshape(-1, D_INDEX))
+    return c.reshape(q.shape[:-1] + (D_INDEX // 2,)), s.reshape(q.shape[:-1] + (D_INDEX // MX_GROUP,))
+
+
+def index_scores_fp4q(q_idx, w, khat):
+    """Step a4 with the MXFP4 query: index_scores of the dequantised
+    quant_indexer_q(q_idx) against the dequantised indexer K.
+    q_idx [32, 128], w [32], khat [n, 128] -> fp64 [n]."""
+    c, s = quant_indexer_q(q_idx)
+    return index_scores(dequant_mxfp4(c, s), w, khat)
+
+
 # ---------------------------------------------------------------- a5 top-k
 def topk(scores, k, ids=None):
     """The min(k, n) candidates with the largest score; ties broken towards

@@ -181,6 +181,79 @@ def test_scores_identities():
     assert np.allclose(R.index_scores(q, 3 * w, k), 3 * s, rtol=1e-13)
 
 
+# ------------------------------------------------------------------ f1
+def test_fp4q_worked_example():
+    """MXFP4 query (report section 2.4.4; OCP MX rule), values worked by
+    hand: X = 2^(floor(log2 amax) - 2), RNE to E2M1 with ties to the even
+    code, saturation at 6."""
+    q = np.zeros((32, 128))
+    # head 3, block 1: amax 7 -> X = 1 (byte 127)
+    q[3, 32:39] = [5.0, -2.6, 0.3, 0.25, 7.0, -0.1, 1.25]
+    # head 0, block 0: amax 0.75 -> X = 2^-3 (byte 124); 0.0375 / X = 0.3 -> 0.5
+    # (a 16-dim block would give X = 2^-7 and 0.03125 instead)
+    q[0, 0] = 0.75
+    q[0, 20] = 0.0375
+    # head 31, block 3: amax 1e-3 -> X = 2^-12 (byte 115); 4.096 -> 4
+    q[31, 100] = -1e-3
+    c, s = R.quant_indexer_q(q)
+    assert c.shape == (32, 64) and s.shape == (32, 4)
+    # codes: 5 -> 4 (6), -2.6 -> -3 (13), 0.3 -> 0.5 (1), 0.25 -> 0 (0),
+    # 7 -> 6 (7), -0.1 -> -0 (8), 1.25 -> 1 (2); channel 2c in the low nibble
+    assert list(c[3, 16:20]) == [0xD6, 0x01, 0x87, 0x02]
+    assert s[3, 1] == 127 and s[0, 0] == 124 and s[31, 3] == 115
+    assert s[0, 3] == 0 and np.all(c[0, 48:64] == 0)           # all-zero block
+    d = R.dequant_mxfp4(c, s)
+    assert list(d[3, 32:39]) == [4.0, -3.0, 0.5, 0.0, 6.0, 0.0, 1.0]
+    assert d[0, 0] == 0.75 and d[0, 20] == 0.0625
+    assert d[31, 100] == -4.0 * 2.0 ** -12
+    # the score uses the quantised query: unit weight on head 3 against
+    # unit keys e_32 and -e_33 gives relu(4) and relu(3)
+    w = np.zeros(32); w[3] = 1.0
+    k = np.zeros((3, 128)); k[0, 32] = 1.0; k[1, 33] = -1.0; k[2, 32] = -1.0
+    assert list(R.index_scores_fp4q(q, w, k)) == [4.0, 3.0, 0.0]
+
+
+def test_fp4q_exact_when_representable():
+    """A query whose every (head, 32-dim block) is E2M1 values times its own
+    power of two, with |max| 6 or 4, is its own MXFP4 form, so the scores
+    equal the plain ones exactly.  The exponents differ by up to 2^40 from
+    block to block, so a block taken along the wrong axis (across heads) or
+    over 64 dims would crush the small blocks."""
+    rng = np.random.default_rng(11)
+    e2 = F.e2m1_value(np.arange(16))
+    codes = rng.integers(0, 16, size=(32, 4, 32))
+    codes[:, :, 0] = rng.choice([6, 7, 14, 15], size=(32, 4))      # |max| in {4, 6}
+    ex = rng.integers(-20, 21, size=(32, 4))
+    q = (e2[codes] * np.exp2(ex)[:, :, None]).reshape(32, 128)
+    c, s = R.quant_indexer_q(q)
+    assert np.array_equal(R.dequant_mxfp4(c, s), q)
+    w = rng.uniform(0, 1, 32)
+    k = rng.standard_normal((50, 128))
+    assert np.array_equal(R.index_scores_fp4q(q, w, k), R.index_scores(q, w, k))
+
+
+def test_fp4q_error_bound():
+    """Each quantised element lies within 2 X of the input (amax / X is in
+    [4, 8): half an E2M1 step is at most X below 6 X, saturation costs less
+    than 2 X above it), and the relu is 1-Lipschitz, so
+    |s_fp4 - s| <= sum_h w_h sum_c 2 X_hc |k_c|."""
+    rng = np.random.default_rng(12)
+    q = rng.standard_normal((32, 128)) * np.exp2(rng.integers(-6, 7, size=(32, 1)))
+    w = rng.uniform(0, 1, 32)
+    k = rng.standard_normal((64, 128))
+    c, s = R.quant_indexer_q(q)
+    X = np.repeat(F.e8m0_value(s), 32, axis=1)                   # [32, 128]
+    qh = R.dequant_mxfp4(c, s)
+    assert np.all(np.abs(qh - q) <= 2 * X)
+    assert np.all(np.abs(qh - q) <= X * (np.abs(q) <= 6 * X) + 2 * X * (np.abs(q) > 6 * X))
+    bound = (np.abs(k) @ (2 * X).T) @ w
+    err = np.abs(R.index_scores_fp4q(q, w, k) - R.index_scores(q, w, k))
+    assert np.all(err <= bound) and np.all(R.index_scores_fp4q(q, w, k) >= 0)
+    # the quantisation is scale-equivariant under powers of two
+    c2, s2 = R.quant_indexer_q(q * 2.0 ** 5)
+    assert np.array_equal(c2, c) and np.array_equal(s2.astype(int), s.astype(int) + 5)
+
+
 # ------------------------------------------------------------------ a5
 def test_topk_textbook_sort_with_ties():
     rng = np.random.default_rng(8)
