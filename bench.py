@@ -29,6 +29,7 @@ from long_context_sparse_csa2_amd.pipeline import Step  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, AMD datasheet
 MFMA_BF16_PEAK_TFLOPS = 2500.0 # MI355X dense bf16 matrix peak, AMD datasheet
+MFMA_FP4_PEAK_TFLOPS = 10100.0 # MI355X dense fp4 matrix peak, AMD datasheet
 SCAN_BYTES_PER_ENTRY = 68      # MXFP4 indexer K: 64 B codes + 4 B E8M0 scales
 SCAN_FLOPS_PER_ENTRY = 2 * 32 * 128   # 32 heads x 128 dims multiply-adds per (query, entry)
 METRIC = "decode tokens/s at 1M ctx (indexer+top-512+FP4 sparse attn); % of roofline"
@@ -49,13 +50,14 @@ def step_bytes(wl):
     return b
 
 
-def scan_traffic(cfg):
+def scan_traffic(cfg, fp4q=False):
     """HBM bytes (read + written) per scan launch from the committed
     rocprofv3 FETCH_SIZE / WRITE_SIZE summary, or None when there is none or
     the scan kernel's source has changed since the counters were taken."""
     import hashlib
     import re
-    f = os.path.join(ROOT, "profiles", f"index_score_{cfg}_hbm_traffic.md")
+    kind = "index_score_fp4q" if fp4q else "index_score"
+    f = os.path.join(ROOT, "profiles", f"{kind}_{cfg}_hbm_traffic.md")
     if not os.path.exists(f):
         return None
     txt = open(f).read()
@@ -73,8 +75,9 @@ def scan_roofline(wl, step, scan_us):
     """Roofline entry of the Full-layer scan.  Decode scans stream every
     visible entry's 68 B of indexer K once per query (HBM-bound); a prefill
     chunk scores thousands of queries against the same few thousand entries,
-    which stay in cache, so its bound is the bf16 MFMA work instead.  The
-    bound is whichever takes longer at its datasheet peak."""
+    which stay in cache, so its bound is the MFMA work instead (bf16 for the
+    bf16 query, fp4 for the MXFP4 query).  The bound is whichever takes
+    longer at its datasheet peak."""
     n_vis = step.n_vis.cpu().numpy()
     seqs = step.q_seq.cpu().numpy()
     pairs = int(n_vis.sum())
@@ -82,17 +85,19 @@ def scan_roofline(wl, step, scan_us):
     hbm_bytes = (pairs if len(seqs) == len(set(seqs.tolist())) else uniq) * SCAN_BYTES_PER_ENTRY
     flops = pairs * SCAN_FLOPS_PER_ENTRY
     t_hbm = hbm_bytes / (HBM_PEAK_GBS * 1e9)
-    t_mfma = flops / (MFMA_BF16_PEAK_TFLOPS * 1e12)
+    peak = MFMA_FP4_PEAK_TFLOPS if step.fp4q else MFMA_BF16_PEAK_TFLOPS
+    t_mfma = flops / (peak * 1e12)
     base = {"kernel": "k_index_score (Full-layer scan)", "avg_launch_us": round(scan_us, 2)}
     if t_hbm >= t_mfma:
         achieved = hbm_bytes / (scan_us * 1e-6) / 1e9
         return {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": scan_traffic(wl.name),
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": scan_traffic(wl.name, step.fp4q),
                 "bytes_per_launch": hbm_bytes, **base}
     achieved = flops / (scan_us * 1e-6) / 1e12
-    return {"bound": "mfma", "achieved": round(achieved, 1), "peak": MFMA_BF16_PEAK_TFLOPS,
-            "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
-            "traffic": scan_traffic(wl.name), "flops_per_launch": flops, **base}
+    return {"bound": "mfma", "achieved": round(achieved, 1), "peak": peak,
+            "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
+            "mfma_dtype": "fp4" if step.fp4q else "bf16",
+            "traffic": scan_traffic(wl.name, step.fp4q), "flops_per_launch": flops, **base}
 
 
 def cpu_baseline(wl, step, seconds_target=15.0):
@@ -115,6 +120,7 @@ def cpu_baseline(wl, step, seconds_target=15.0):
                            q_attn=L["q_attn"][b].float().cpu().numpy().astype(np.float64),
                            swa_c=L["swa_codes"][b].cpu().numpy(),
                            swa_s=L["swa_scale"][b].cpu().numpy().astype(np.float64)))
+    scores = R.index_scores_fp4q if step.fp4q else R.index_scores
     runs, t_total = 0, 0.0
     while t_total < seconds_target and runs < 5:
         t0 = time.perf_counter()
@@ -123,12 +129,12 @@ def cpu_baseline(wl, step, seconds_target=15.0):
         for li, mode in enumerate(wl.layers):
             L = layers[li]
             if mode == "full":
-                s = R.index_scores(L["q_idx"], L["w"], khat)
+                s = scores(L["q_idx"], L["w"], khat)
                 if wl.hierarchical:
                     pool = R.block_pool(s, wl.block, wl.n_blocks)
                 idx = R.topk(s, wl.k)
             elif mode == "reindex":
-                s = R.index_scores(L["q_idx"], L["w"], khat[pool])
+                s = scores(L["q_idx"], L["w"], khat[pool])
                 idx = R.topk(s, wl.k, pool)
             rows = R.gather_rows(kv_c, kv_s, idx, L["swa_c"], L["swa_s"])
             R.attend(L["q_attn"], rows)
@@ -147,6 +153,9 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default="c2", choices=sorted(synth.WORKLOADS))
+    ap.add_argument("--indexer-q", default="bf16", choices=["bf16", "mxfp4"],
+                    help="indexer query format: bf16 as given, or quantised to MXFP4 in the "
+                         "scan (csa2_index_score_fp4q)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--eager", action="store_true", help="launch every call from Python "
                     "instead of replaying the step's HIP graphs")
@@ -171,7 +180,7 @@ def main():
         return
     wl = synth.WORKLOADS[args.config]
     print(f"[bench] building {wl.name} ({wl.note}) cache on {dev}", file=sys.stderr, flush=True)
-    step = Step(wl, dev)
+    step = Step(wl, dev, fp4q=args.indexer_q == "mxfp4")
     torch.cuda.synchronize()
     print("[bench] warmup", file=sys.stderr, flush=True)
     for _ in range(args.warmup):
@@ -233,7 +242,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": f"{wl.name}: {wl.note}", "batch": wl.B, "entries": wl.N,
                    "raw_tokens": wl.T, "m": wl.m, "layers": wl.layers, "top_k": wl.k,
-                   "pool_blocks": wl.n_blocks if wl.hierarchical else 0, "swa": wl.swa},
+                   "pool_blocks": wl.n_blocks if wl.hierarchical else 0, "swa": wl.swa,
+                   "indexer_q": args.indexer_q},
         "roofline": roofline,
         "step_roofline": None if step_b is None else {
             "bytes": step_b, "us_at_peak": round(step_b / (HBM_PEAK_GBS * 1e3), 2),

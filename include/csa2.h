@@ -146,6 +146,28 @@ csa2_status csa2_index_score(const uint16_t* q_idx, const float* w, const int32_
                              void* stream);
 
 /*
+ * (2b) Lightning-indexer scores with an MXFP4 indexer query.
+ *
+ * Report section 2.4.4 (V4 already trains the indexer queries and keys for
+ * the OCP MXFP4 format so that index scoring runs as an FP4 matrix multiply);
+ * commentary section 5.  Same arguments, layouts, ownership and errors as
+ * csa2_index_score; the only difference is that each query is first
+ * quantised with the OCP MX rule the cache uses for the indexer K, per head
+ * and 32-dim block:
+ *   X = 2^(floor(log2 max|q_g|) - 2) as E8M0 (exponent clamped to
+ *   [-127, 127]; an all-zero block gets 2^-127 and +0 codes),
+ *   qhat[c] = X * E2M1(RNE, saturating at 6)(q[c] / X)
+ * and the score is
+ *   score(q, j) = sum_{h<32} w[q][h] * max(0, sum_{c<128} qhat[q][h][c] * khat_j[c])
+ * accumulated in fp32 (the FP4 x FP4 products are exact).  The quantised
+ * query is not written out.
+ */
+csa2_status csa2_index_score_fp4q(const uint16_t* q_idx, const float* w, const int32_t* q_seq,
+                                  const int64_t* n_vis, const int32_t* cand, int64_t ld_cand,
+                                  int Q, int64_t n_cols, const csa2_cache* src, float* scores,
+                                  int64_t ld, void* stream);
+
+/*
  * (3a) Per-query top-k: step a5 (and the selection half of a7).
  *
  * Selects, for each query, the min(k, n_valid[q]) columns with the largest

@@ -18,7 +18,7 @@ LIB_PATH = os.path.join(_PKG, "libcsa2.so")
 CSA2_OP_TOPK, CSA2_OP_POOL, CSA2_OP_ATTEND = 1, 2, 3
 STATUS = {0: "CSA2_OK", 1: "CSA2_EINVAL", 2: "CSA2_EUNSUPPORTED", 3: "CSA2_EWORKSPACE", 4: "CSA2_EHIP"}
 EXPORTS = ("csa2_status_string", "csa2_last_error", "csa2_compress_quant", "csa2_index_score",
-           "csa2_select_topk", "csa2_block_pool", "csa2_sparse_attend", "csa2_workspace_bytes",
+           "csa2_index_score_fp4q", "csa2_select_topk", "csa2_block_pool", "csa2_sparse_attend", "csa2_workspace_bytes",
            "csa2_selftest")
 
 
@@ -52,8 +52,9 @@ def lib():
         L.csa2_last_error.argtypes = []
         L.csa2_compress_quant.restype = I
         L.csa2_compress_quant.argtypes = [P, P, I, I64, I, P, ctypes.POINTER(_Cache), I64, P]
-        L.csa2_index_score.restype = I
-        L.csa2_index_score.argtypes = [P, P, P, P, P, I64, I, I64, ctypes.POINTER(_Cache), P, I64, P]
+        for fn in (L.csa2_index_score, L.csa2_index_score_fp4q):
+            fn.restype = I
+            fn.argtypes = [P, P, P, P, P, I64, I, I64, ctypes.POINTER(_Cache), P, I64, P]
         L.csa2_select_topk.restype = I
         L.csa2_select_topk.argtypes = [P, I64, I, P, P, I64, I, P, P, SZ, P]
         L.csa2_block_pool.restype = I
@@ -143,19 +144,22 @@ def csa2_compress_quant(h, z, m, w_ik, cache, e0=0, stream=None):
     _check("csa2_compress_quant", st)
 
 
-def csa2_index_score(q_idx, w, q_seq, n_vis, cand, n_cols, cache, scores, stream=None):
+def csa2_index_score(q_idx, w, q_seq, n_vis, cand, n_cols, cache, scores, stream=None,
+                     fp4q=False):
     """q_idx [Q, 32, 128] bf16, w [Q, 32] f32, q_seq [Q] i32, n_vis [Q] i64,
-    cand None or [Q, P] i32, scores [Q, ld] f32."""
+    cand None or [Q, P] i32, scores [Q, ld] f32.  fp4q=True calls
+    csa2_index_score_fp4q (the query quantised to MXFP4 first)."""
     _dtype(q_idx, torch.bfloat16, "q_idx"); _dtype(w, torch.float32, "w")
     _dtype(q_seq, torch.int32, "q_seq"); _dtype(n_vis, torch.int64, "n_vis")
     _dtype(cand, torch.int32, "cand"); _dtype(scores, torch.float32, "scores")
     Q = q_idx.shape[0]
     ld_cand = cand.shape[1] if cand is not None else 0
     cs = cache.c_struct()
-    st = lib().csa2_index_score(_ptr(q_idx), _ptr(w), _ptr(q_seq), _ptr(n_vis), _ptr(cand),
-                                ld_cand, Q, n_cols, ctypes.byref(cs), _ptr(scores),
-                                scores.shape[1], _stream(stream, q_idx))
-    _check("csa2_index_score", st)
+    name = "csa2_index_score_fp4q" if fp4q else "csa2_index_score"
+    st = getattr(lib(), name)(_ptr(q_idx), _ptr(w), _ptr(q_seq), _ptr(n_vis), _ptr(cand),
+                              ld_cand, Q, n_cols, ctypes.byref(cs), _ptr(scores),
+                              scores.shape[1], _stream(stream, q_idx))
+    _check(name, st)
 
 
 def csa2_select_topk(scores, n_valid, col_ids, n_cols, k, out, ws=None, stream=None):
@@ -221,7 +225,6 @@ def csa2_selftest(device="cuda"):
 
 def workspace(op, Q, n_cols, k, device):
     """A zero-filled uint8 device tensor of the size csa2_workspace_bytes asks
-    for (or None).  The attention workspace must start zeroed (it holds the
-    split-merge semaphores, which every call leaves at zero)."""
+    for, or None when the operation needs none."""
     n = csa2_workspace_bytes(op, Q, n_cols, k)
     return torch.zeros(n, dtype=torch.uint8, device=device) if n else None

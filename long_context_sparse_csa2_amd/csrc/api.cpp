@@ -112,11 +112,11 @@ csa2_status csa2_compress_quant(const uint16_t* h, const uint16_t* z, int B, int
                     "csa2_compress_quant launch");
 }
 
-csa2_status csa2_index_score(const uint16_t* q_idx, const float* w, const int32_t* q_seq,
-                             const int64_t* n_vis, const int32_t* cand, int64_t ld_cand, int Q,
-                             int64_t n_cols, const csa2_cache* src, float* scores, int64_t ld,
-                             void* stream) {
-  g_err[0] = 0;
+static csa2_status index_score_common(const uint16_t* q_idx, const float* w,
+                                      const int32_t* q_seq, const int64_t* n_vis,
+                                      const int32_t* cand, int64_t ld_cand, int Q, int64_t n_cols,
+                                      const csa2_cache* src, float* scores, int64_t ld,
+                                      void* stream, bool fp4q) {
   REQ(q_idx && w && q_seq && n_vis && scores, "q_idx, w, q_seq, n_vis, scores must not be NULL");
   const csa2_status cs = check_cache(src);
   if (cs != CSA2_OK) return cs;
@@ -137,8 +137,26 @@ csa2_status csa2_index_score(const uint16_t* q_idx, const float* w, const int32_
   }
   return hip_status(csa2::launch_index_score(q_idx, w, q_seq, n_vis, cand, ld_cand, Q, n_cols,
                                              src->ik_codes, src->ik_scales, src->cap, scores, ld,
-                                             (hipStream_t)stream),
-                    "csa2_index_score launch");
+                                             fp4q, (hipStream_t)stream),
+                    fp4q ? "csa2_index_score_fp4q launch" : "csa2_index_score launch");
+}
+
+csa2_status csa2_index_score(const uint16_t* q_idx, const float* w, const int32_t* q_seq,
+                             const int64_t* n_vis, const int32_t* cand, int64_t ld_cand, int Q,
+                             int64_t n_cols, const csa2_cache* src, float* scores, int64_t ld,
+                             void* stream) {
+  g_err[0] = 0;
+  return index_score_common(q_idx, w, q_seq, n_vis, cand, ld_cand, Q, n_cols, src, scores, ld,
+                            stream, false);
+}
+
+csa2_status csa2_index_score_fp4q(const uint16_t* q_idx, const float* w, const int32_t* q_seq,
+                                  const int64_t* n_vis, const int32_t* cand, int64_t ld_cand,
+                                  int Q, int64_t n_cols, const csa2_cache* src, float* scores,
+                                  int64_t ld, void* stream) {
+  g_err[0] = 0;
+  return index_score_common(q_idx, w, q_seq, n_vis, cand, ld_cand, Q, n_cols, src, scores, ld,
+                            stream, true);
 }
 
 static csa2_status select_common(const float* scores, int64_t ld, int Q, const int64_t* n_valid,

@@ -15,7 +15,8 @@ hipError_t launch_compress_quant(const uint16_t* h, const uint16_t* z, int B, in
 hipError_t launch_index_score(const uint16_t* q_idx, const float* w, const int32_t* q_seq,
                               const int64_t* n_vis, const int32_t* cand, int64_t ld_cand, int Q,
                               int64_t n_cols, const uint8_t* ik_codes, const uint8_t* ik_scales,
-                              int64_t cap, float* scores, int64_t ld, hipStream_t stream);
+                              int64_t cap, float* scores, int64_t ld, bool fp4q,
+                              hipStream_t stream);
 
 // Selection: mode 0 = top-k of columns (levels down to 0), mode 1 = block
 // pool (levels down to 1, blocks of 8).

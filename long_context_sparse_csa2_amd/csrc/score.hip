@@ -18,6 +18,20 @@
 // and the two lane halves are summed with one cross-lane exchange, so only
 // 4 bytes per entry are written.  The next tile's bytes are loaded before
 // the current tile's MFMAs issue.
+//
+// MXFP4-query variant (report section 2.4.4: V4 trains the indexer Q and K
+// for OCP MXFP4 so that the index product is an FP4 matrix multiply): the
+// workgroup first quantises the query with the OCP MX rule the compressor
+// applies to the indexer K (E8M0 X = 2^(floor(log2 amax) - 2) per head and
+// 32-dim block, E2M1 RNE saturating) into LDS; every tile is then two gfx950
+// scaled FP4 x FP4 MFMAs (32x32x64) on the raw key bytes, with no
+// conversion at all.  Lane half h passes the 32 dims of block 2h + c as the
+// K slice of MFMA c, for the query and the key alike (any permutation of K
+// shared by both operands leaves the product unchanged), so each lane still
+// streams 32 contiguous code bytes, and each lane's 32-element K slice is
+// exactly one MX block with one scale byte per operand.  Products of E2M1
+// values with power-of-two scales are exact; only the fp32 accumulation
+// rounds.
 #include "common.h"
 #include "launch.h"
 
@@ -25,18 +39,66 @@ namespace csa2 {
 
 constexpr int SC_WAVES = 4;
 
+typedef int i32x8_t __attribute__((ext_vector_type(8)));
+
+// MXFP4 query of one workgroup: codes of head h, dims 2c and 2c+1 in byte
+// c (low nibble first), and the E8M0 byte of each 32-dim block.
+struct QFp4Lds {
+  uint8_t codes[H_IDX][D_IDX / 2];
+  uint32_t scales[H_IDX];                             // block g in byte g
+};
+
+// The workgroup's 256 threads quantise the 32 x 128 query: thread t takes
+// head t / 8, block (t / 2) % 4, dims 16 (t % 2) .. +15 of that block; the
+// two threads of a block share their maxima.
+__device__ __forceinline__ void quant_query_fp4(const uint16_t* __restrict__ qrow, QFp4Lds& ql) {
+  const int t = threadIdx.x;
+  const int head = t >> 3, g = (t >> 1) & 3, sub = t & 1;
+  const uint16_t* src = qrow + head * D_IDX + 32 * g + 16 * sub;
+  const u32x4_t w0 = *(const u32x4_t*)src, w1 = *(const u32x4_t*)(src + 8);
+  float v[16];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    v[2 * i] = __uint_as_float(w0[i] << 16);
+    v[2 * i + 1] = __uint_as_float(w0[i] & 0xFFFF0000u);
+    v[8 + 2 * i] = __uint_as_float(w1[i] << 16);
+    v[8 + 2 * i + 1] = __uint_as_float(w1[i] & 0xFFFF0000u);
+  }
+  float amax = 0.f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(v[i]));
+  amax = fmaxf(amax, __shfl_xor(amax, 1));
+  int E = -127;
+  if (amax > 0.f) {
+    int ex;
+    (void)frexpf(amax, &ex);                          // floor(log2 amax) = ex - 1
+    E = ex - 1 - 2;                                   // minus emax of E2M1
+    E = E < -127 ? -127 : (E > 127 ? 127 : E);
+  }
+  uint32_t lo = 0, hi = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    lo |= e2m1_encode(ldexpf(v[i], -E), 1.0f) << (4 * i);
+    hi |= e2m1_encode(ldexpf(v[8 + i], -E), 1.0f) << (4 * i);
+  }
+  *(uint2*)&ql.codes[head][16 * g + 8 * sub] = make_uint2(lo, hi);
+  if (sub == 0) ((uint8_t*)&ql.scales[head])[g] = (uint8_t)(E + 127);
+}
+
 // TPW: 32-entry tiles per wave; DEPTH: tiles whose bytes are in flight ahead
-// of the one being multiplied.
-template <bool CAND, int TPW, int DEPTH>
+// of the one being multiplied.  Workgroup chunk c starts at column
+// c * chunk_stride (+ 32 per wave) and a wave's consecutive tiles are
+// tile_stride columns apart.
+template <bool CAND, bool FP4Q, int TPW, int DEPTH>
 __global__ __launch_bounds__(256) void k_index_score(
     const uint16_t* __restrict__ q_idx, const float* __restrict__ w,
     const int32_t* __restrict__ q_seq, const int64_t* __restrict__ n_vis,
-    const int32_t* __restrict__ cand, int64_t ld_cand, int64_t nchunk, int64_t n_cols,
+    const int32_t* __restrict__ cand, int64_t ld_cand, int64_t nchunk, int64_t chunk_stride,
+    int64_t tile_stride, int64_t n_cols,
     const uint8_t* __restrict__ ik_codes, const uint8_t* __restrict__ ik_scales, int64_t cap,
     float* __restrict__ scores, int64_t ld) {
-  constexpr int SC_COLS = SC_WAVES * TPW * 32;        // columns per workgroup
   const int q = (int)(blockIdx.x / nchunk);
-  const int64_t cbase = (int64_t)(blockIdx.x % nchunk) * SC_COLS;
+  const int64_t cbase = (int64_t)(blockIdx.x % nchunk) * chunk_stride;
   const int64_t nv0 = n_vis[q];
   const int64_t nv = nv0 < n_cols ? nv0 : n_cols;     // never past the launch's columns
   if (cbase >= nv) return;
@@ -44,11 +106,26 @@ __global__ __launch_bounds__(256) void k_index_score(
   const int r = lane & 31, half = lane >> 5;
   const int64_t seq_base = (int64_t)q_seq[q] * cap;
 
-  // A operand: head r, dims 64*half + 8s .. +7 for step s.
-  bf16x8_t a[8];
-  const uint16_t* qp = q_idx + ((int64_t)q * H_IDX + r) * D_IDX + half * 64;
+  // A operand.  bf16: head r, dims 64*half + 8s .. +7 for step s.  MXFP4:
+  // head r, blocks 2*half (MFMA 0) and 2*half + 1 (MFMA 1), scale bytes in
+  // bits 0-7 and 8-15 of qsc.
+  bf16x8_t a[FP4Q ? 1 : 8];
+  i32x8_t qa0 = {}, qa1 = {};
+  uint32_t qsc = 0;
+  if constexpr (FP4Q) {
+    __shared__ QFp4Lds ql;
+    quant_query_fp4(q_idx + (int64_t)q * H_IDX * D_IDX, ql);
+    __syncthreads();
+    const u32x4_t* cp = (const u32x4_t*)&ql.codes[r][32 * half];
+    const u32x4_t c0 = cp[0], c1 = cp[1];
+    qa0 = i32x8_t{(int)c0[0], (int)c0[1], (int)c0[2], (int)c0[3], 0, 0, 0, 0};
+    qa1 = i32x8_t{(int)c1[0], (int)c1[1], (int)c1[2], (int)c1[3], 0, 0, 0, 0};
+    qsc = ql.scales[r] >> (16 * half);
+  } else {
+    const uint16_t* qp = q_idx + ((int64_t)q * H_IDX + r) * D_IDX + half * 64;
 #pragma unroll
-  for (int s = 0; s < 8; ++s) a[s] = *(const bf16x8_t*)(qp + 8 * s);
+    for (int s = 0; s < 8; ++s) a[s] = *(const bf16x8_t*)(qp + 8 * s);
+  }
   // head weight of each accumulator row this lane holds
   float wr[16];
 #pragma unroll
@@ -59,7 +136,7 @@ __global__ __launch_bounds__(256) void k_index_score(
 
   auto load = [&](int64_t col0, u32x4_t& c0, u32x4_t& c1, uint32_t& scw) {
     const int64_t c = col0 + r;
-    const int64_t cc = c < nv ? c : col0;
+    const int64_t cc = c < nv ? c : nv - 1;           // past the end: re-read the last entry
     const int64_t e = CAND ? (int64_t)crow[cc] : cc;
     const uint8_t* cp = ik_codes + (seq_base + e) * 64 + half * 32;
     c0 = *(const u32x4_t*)cp;
@@ -70,12 +147,12 @@ __global__ __launch_bounds__(256) void k_index_score(
   // ring of DEPTH + 1 tiles: slot t % (DEPTH + 1) holds tile t
   u32x4_t r0[DEPTH + 1], r1[DEPTH + 1];
   uint32_t rs[DEPTH + 1];
-  const int64_t step = SC_WAVES * 32;
+  const int64_t step = tile_stride;
   const int64_t col_first = cbase + (int64_t)wave * 32;
 #pragma unroll
   for (int t = 0; t < DEPTH; ++t) {
     const int64_t c0 = col_first + t * step;
-    if (t < TPW && c0 < nv) load(c0, r0[t], r1[t], rs[t]);
+    if (t < TPW) load(c0, r0[t], r1[t], rs[t]);
   }
 #pragma unroll
   for (int t = 0; t < TPW; ++t) {
@@ -84,22 +161,35 @@ __global__ __launch_bounds__(256) void k_index_score(
     {
       const int tn = t + DEPTH;
       const int64_t cn = col_first + tn * step;
-      if (tn < TPW && cn < nv) load(cn, r0[tn % (DEPTH + 1)], r1[tn % (DEPTH + 1)], rs[tn % (DEPTH + 1)]);
+      if (tn < TPW) load(cn, r0[tn % (DEPTH + 1)], r1[tn % (DEPTH + 1)], rs[tn % (DEPTH + 1)]);
     }
     const int sl = t % (DEPTH + 1);
     const u32x4_t c0 = r0[sl], c1 = r1[sl];
     const uint32_t scw = rs[sl];
-    const float s_lo = e8m0_val((scw >> (16 * half)) & 0xFFu);
-    const float s_hi = e8m0_val((scw >> (16 * half + 8)) & 0xFFu);
     f32x16_t acc = {};
-    acc = mfma32_bf16(a[0], fp4x8_to_bf16_pow2(c0[0], s_lo), acc);
-    acc = mfma32_bf16(a[1], fp4x8_to_bf16_pow2(c0[1], s_lo), acc);
-    acc = mfma32_bf16(a[2], fp4x8_to_bf16_pow2(c0[2], s_lo), acc);
-    acc = mfma32_bf16(a[3], fp4x8_to_bf16_pow2(c0[3], s_lo), acc);
-    acc = mfma32_bf16(a[4], fp4x8_to_bf16_pow2(c1[0], s_hi), acc);
-    acc = mfma32_bf16(a[5], fp4x8_to_bf16_pow2(c1[1], s_hi), acc);
-    acc = mfma32_bf16(a[6], fp4x8_to_bf16_pow2(c1[2], s_hi), acc);
-    acc = mfma32_bf16(a[7], fp4x8_to_bf16_pow2(c1[3], s_hi), acc);
+    if constexpr (FP4Q) {
+      const uint32_t ksc = scw >> (16 * half);
+      const i32x8_t b0 = {(int)c0[0], (int)c0[1], (int)c0[2], (int)c0[3], 0, 0, 0, 0};
+      const i32x8_t b1 = {(int)c1[0], (int)c1[1], (int)c1[2], (int)c1[3], 0, 0, 0, 0};
+      // format 4 (E2M1) for both operands; scale operands are E8M0 bytes
+      acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(qa0, b0, acc, 4, 4, 0,
+                                                            (int)(qsc & 0xFFu), 0,
+                                                            (int)(ksc & 0xFFu));
+      acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(qa1, b1, acc, 4, 4, 0,
+                                                            (int)((qsc >> 8) & 0xFFu), 0,
+                                                            (int)((ksc >> 8) & 0xFFu));
+    } else {
+      const float s_lo = e8m0_val((scw >> (16 * half)) & 0xFFu);
+      const float s_hi = e8m0_val((scw >> (16 * half + 8)) & 0xFFu);
+      acc = mfma32_bf16(a[0], fp4x8_to_bf16_pow2(c0[0], s_lo), acc);
+      acc = mfma32_bf16(a[1], fp4x8_to_bf16_pow2(c0[1], s_lo), acc);
+      acc = mfma32_bf16(a[2], fp4x8_to_bf16_pow2(c0[2], s_lo), acc);
+      acc = mfma32_bf16(a[3], fp4x8_to_bf16_pow2(c0[3], s_lo), acc);
+      acc = mfma32_bf16(a[4], fp4x8_to_bf16_pow2(c1[0], s_hi), acc);
+      acc = mfma32_bf16(a[5], fp4x8_to_bf16_pow2(c1[1], s_hi), acc);
+      acc = mfma32_bf16(a[6], fp4x8_to_bf16_pow2(c1[2], s_hi), acc);
+      acc = mfma32_bf16(a[7], fp4x8_to_bf16_pow2(c1[3], s_hi), acc);
+    }
     float part = 0.f;
 #pragma unroll
     for (int j = 0; j < 16; ++j) part += wr[j] * relu_f32(acc[j]);
@@ -110,20 +200,28 @@ __global__ __launch_bounds__(256) void k_index_score(
 }
 
 template <bool CAND, int TPW, int DEPTH>
-static void launch_variant(dim3 grid, hipStream_t stream, const uint16_t* q_idx, const float* w,
+static void launch_variant(bool fp4q, dim3 grid, hipStream_t stream, const uint16_t* q_idx,
+                           const float* w,
                            const int32_t* q_seq, const int64_t* n_vis, const int32_t* cand,
-                           int64_t ld_cand, int64_t nchunk, int64_t n_cols,
+                           int64_t ld_cand, int64_t nchunk, int64_t chunk_stride,
+                           int64_t tile_stride, int64_t n_cols,
                            const uint8_t* ik_codes, const uint8_t* ik_scales, int64_t cap,
                            float* scores, int64_t ld) {
-  hipLaunchKernelGGL((k_index_score<CAND, TPW, DEPTH>), grid, dim3(256), 0, stream, q_idx, w,
-                     q_seq, n_vis, cand, ld_cand, nchunk, n_cols, ik_codes, ik_scales, cap, scores,
-                     ld);
+  if (fp4q)
+    hipLaunchKernelGGL((k_index_score<CAND, true, TPW, DEPTH>), grid, dim3(256), 0, stream, q_idx,
+                       w, q_seq, n_vis, cand, ld_cand, nchunk, chunk_stride, tile_stride, n_cols, ik_codes,
+                       ik_scales, cap, scores, ld);
+  else
+    hipLaunchKernelGGL((k_index_score<CAND, false, TPW, DEPTH>), grid, dim3(256), 0, stream, q_idx,
+                       w, q_seq, n_vis, cand, ld_cand, nchunk, chunk_stride, tile_stride, n_cols, ik_codes,
+                       ik_scales, cap, scores, ld);
 }
 
 hipError_t launch_index_score(const uint16_t* q_idx, const float* w, const int32_t* q_seq,
                               const int64_t* n_vis, const int32_t* cand, int64_t ld_cand, int Q,
                               int64_t n_cols, const uint8_t* ik_codes, const uint8_t* ik_scales,
-                              int64_t cap, float* scores, int64_t ld, hipStream_t stream) {
+                              int64_t cap, float* scores, int64_t ld, bool fp4q,
+                              hipStream_t stream) {
   // Tiles per wave: the largest of 32, 16, 8, 2, 1 that still launches at
   // least 1024 workgroups (4 per CU); long scans keep two tiles in flight.
   // (Swept on MI355X: 1M-entry scans want 32 tiles x 2 in flight, 64K-entry
@@ -136,12 +234,24 @@ hipError_t launch_index_score(const uint16_t* q_idx, const float* w, const int32
   const int64_t cols = (int64_t)SC_WAVES * tpw * 32;
   const int64_t nchunk = (n_cols + cols - 1) / cols;
   const dim3 grid((unsigned)(nchunk * Q));
-#define CSA2_SCORE_CASE(T, D)                                                                       \
-  case T:                                                                                          \
-    if (cand) launch_variant<true, T, D>(grid, stream, q_idx, w, q_seq, n_vis, cand, ld_cand,      \
-                                         nchunk, n_cols, ik_codes, ik_scales, cap, scores, ld);    \
-    else launch_variant<false, T, D>(grid, stream, q_idx, w, q_seq, n_vis, cand, ld_cand, nchunk,  \
-                                     n_cols, ik_codes, ik_scales, cap, scores, ld);                \
+  // Long scans (>= 128 chunks per query) interleave the workgroups' tiles:
+  // workgroup g takes 128-column slices g, g + nchunk, g + 2 nchunk, ..., so
+  // at any moment the workgroups of a query read one contiguous window
+  // instead of nchunk windows a fixed power-of-two stride apart (measured on
+  // MI355X: 2-7 % faster at 512K-1M entries, 3-5 % slower at 64K).
+  const bool inter = nchunk >= 128;
+  const int64_t cs = inter ? (int64_t)SC_WAVES * 32 : cols;
+  const int64_t ts = inter ? nchunk * SC_WAVES * 32 : (int64_t)SC_WAVES * 32;
+#define CSA2_SCORE_CASE(T, D)                                                          \
+  case T:                                                                             \
+    if (cand)                                                                         \
+      launch_variant<true, T, D>(fp4q, grid, stream, q_idx, w, q_seq, n_vis, cand,    \
+                                 ld_cand, nchunk, cs, ts, n_cols, ik_codes, ik_scales, \
+                                 cap, scores, ld);                                    \
+    else                                                                              \
+      launch_variant<false, T, D>(fp4q, grid, stream, q_idx, w, q_seq, n_vis, cand,   \
+                                  ld_cand, nchunk, cs, ts, n_cols, ik_codes, ik_scales, \
+                                  cap, scores, ld);                                   \
     break;
   switch (tpw) {
     CSA2_SCORE_CASE(32, 2)

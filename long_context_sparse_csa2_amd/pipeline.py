@@ -37,9 +37,12 @@ def build_cache(wl: Workload, device, seq_chunk=1):
 class Step:
     """All layers of one step of a workload over a built cache."""
 
-    def __init__(self, wl: Workload, device, cache=None):
+    def __init__(self, wl: Workload, device, cache=None, fp4q=False):
+        """fp4q=True scores with the MXFP4 indexer query
+        (csa2_index_score_fp4q) instead of the bf16 one."""
         self.wl = wl
         self.device = device
+        self.fp4q = fp4q
         if cache is None:
             cache, _ = build_cache(wl, device)
         self.cache = cache
@@ -78,7 +81,8 @@ class Step:
             L = self.layers[li]
             if mode == "full":
                 out.append(("index_score_full", li, lambda L=L: csa2_index_score(
-                    L["q_idx"], L["w"], self.q_seq, self.n_vis, None, wl.N, self.cache, self.scores)))
+                    L["q_idx"], L["w"], self.q_seq, self.n_vis, None, wl.N, self.cache, self.scores,
+                    fp4q=self.fp4q)))
                 if wl.hierarchical:
                     # the pool and the layer's own top-k in one selection pass
                     out.append(("block_pool_topk", li, lambda: csa2_block_pool(
@@ -92,7 +96,7 @@ class Step:
                 idx = self.idx_r[li]
                 out.append(("index_score_pool", li, lambda L=L: csa2_index_score(
                     L["q_idx"], L["w"], self.q_seq, self.pool_len, self.pool, self.P, self.cache,
-                    self.pool_scores)))
+                    self.pool_scores, fp4q=self.fp4q)))
                 out.append(("select_topk_pool", li, lambda idx=idx: csa2_select_topk(
                     self.pool_scores, self.pool_len, self.pool, self.P, wl.k, idx,
                     self.ws_topk_pool)))

@@ -16,7 +16,7 @@ FAKE = ctypes.c_void_p(0x10000)      # aligned, never dereferenced: every call b
 def declared():
     src = open(HEADER).read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"\b(csa2_[a-z_]+)\s*\(", src)))
+    return sorted(set(re.findall(r"\b(csa2_[a-z0-9_]+)\s*\(", src)))
 
 
 def test_exports_every_declared_symbol():
@@ -59,17 +59,19 @@ def test_compress_validation():
     assert L.csa2_compress_quant(FAKE, FAKE, 1, 34, 17, FAKE, ctypes.byref(cs), 0, None) == 1
 
 
-def test_index_score_validation():
+@pytest.mark.parametrize("entry", ["csa2_index_score", "csa2_index_score_fp4q"])
+def test_index_score_validation(entry):
     L = C.lib()
     cs = _cache(cap=100)
     P = FAKE
-    assert L.csa2_index_score(None, P, P, P, None, 0, 1, 10, ctypes.byref(cs), P, 10, None) == 1
-    assert L.csa2_index_score(P, P, P, P, None, 0, 0, 10, ctypes.byref(cs), P, 10, None) == 1
-    assert L.csa2_index_score(P, P, P, P, None, 0, 1, 10, ctypes.byref(cs), P, 9, None) == 1
-    assert L.csa2_index_score(P, P, P, P, None, 0, 1, 101, ctypes.byref(cs), P, 101, None) == 1
-    assert L.csa2_index_score(P, P, P, P, P, 5, 1, 10, ctypes.byref(cs), P, 10, None) == 1
+    f = getattr(L, entry)
+    assert f(None, P, P, P, None, 0, 1, 10, ctypes.byref(cs), P, 10, None) == 1
+    assert f(P, P, P, P, None, 0, 0, 10, ctypes.byref(cs), P, 10, None) == 1
+    assert f(P, P, P, P, None, 0, 1, 10, ctypes.byref(cs), P, 9, None) == 1
+    assert f(P, P, P, P, None, 0, 1, 101, ctypes.byref(cs), P, 101, None) == 1
+    assert f(P, P, P, P, P, 5, 1, 10, ctypes.byref(cs), P, 10, None) == 1
     # nothing to score: returns OK without launching
-    assert L.csa2_index_score(P, P, P, P, None, 0, 1, 0, ctypes.byref(cs), P, 10, None) == 0
+    assert f(P, P, P, P, None, 0, 1, 0, ctypes.byref(cs), P, 10, None) == 0
 
 
 def test_select_and_pool_validation():

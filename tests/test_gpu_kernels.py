@@ -114,6 +114,102 @@ def test_index_score_full_and_pool():
         assert np.all(p[i, lens[i]:] == -7.0)
 
 
+def _fp4q_special_queries(Q, seed):
+    """Indexer queries that exercise the MXFP4 query quantiser: per-block
+    magnitudes spread over 2^-30 .. 2^20, exact E2M1 ties (0.25, 0.75, 1.25,
+    1.75, 2.5, 3.5, 5 times the block scale), all-zero blocks, negative
+    zeros, blocks whose scale clamps at 2^-127, and saturation (|q| / X in
+    (6, 8))."""
+    q, w = _scores_inputs(Q, seed)
+    g = torch.Generator().manual_seed(seed + 1)
+    ex = torch.randint(-30, 21, (Q, 32, 4, 1), generator=g).float()
+    q = (q.float().reshape(Q, 32, 4, 32) * torch.exp2(ex)).reshape(Q, 32, 128)
+    ties = torch.tensor([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, -2.5, -0.25, 6.0])
+    q[0, 1, 32:42] = ties * 2.0 ** -7            # amax 6 X with X = 2^-7
+    q[0, 2, 64:96] = 0.0                          # all-zero block
+    q[0, 3, 0:32] = -0.0                          # negative zeros only
+    q[0, 4, 96:128] = 0.0
+    q[0, 4, 96] = 2.0 ** -130                     # scale clamps at 2^-127: 2^-130 / X = 1/8
+    q[0, 4, 97] = -2.0 ** -126                    # 2 X: exact
+    q[0, 5, 0:32] = 0.0
+    q[0, 5, 0] = 7.5                              # X = 1: saturates to 6
+    q[0, 5, 1] = -7.0
+    q[0, 5, 2] = 1.0
+    return q.to(torch.bfloat16), w
+
+
+def _oracle_scores_fp4q(q64, w64, khat):
+    return R.index_scores_fp4q(q64, w64, khat)
+
+
+@pytest.mark.parametrize("special", [False, True])
+def test_index_score_fp4q(special):
+    """MXFP4-query scoring (full scan and candidate pool) against the oracle's
+    quantised query."""
+    B, T, Q = 2, 3000, 5
+    _, _, _, cache = _build(B, T, 1, seed=31)
+    q, w = _fp4q_special_queries(Q, 32) if special else _scores_inputs(Q, 32)
+    q_seq = torch.tensor([0, 1, 1, 0, 1], dtype=torch.int32)
+    n_vis = torch.tensor([3000, 2999, 1, 257, 2049], dtype=torch.int64)
+    scores = torch.full((Q, 3008), -7.0, device=DEV)
+    C.csa2_index_score(q.to(DEV), w.to(DEV), q_seq.to(DEV), n_vis.to(DEV), None, 3000, cache,
+                       scores, fp4q=True)
+    torch.cuda.synchronize()
+    s = checks.host(scores)
+    q64, w64 = checks.bf16_to_f64(q), w.double().numpy()
+    khat = [R.dequant_mxfp4(checks.host(cache.ik_codes[b]), checks.host(cache.ik_scales[b])) for b in range(B)]
+    for i in range(Q):
+        b, nv = int(q_seq[i]), int(n_vis[i])
+        checks.check_scores(s[i, :nv], _oracle_scores_fp4q(q64[i], w64[i], khat[b][:nv]))
+        assert np.all(s[i, nv:] == -7.0)
+    # candidate mode
+    rng = np.random.default_rng(3)
+    P = 900
+    lens = [900, 333, 0, 1, 64]
+    cand = np.full((Q, P), -1, dtype=np.int32)
+    for i in range(Q):
+        cand[i, :lens[i]] = np.sort(rng.choice(2999, lens[i], replace=False))
+    ps = torch.full((Q, P), -7.0, device=DEV)
+    C.csa2_index_score(q.to(DEV), w.to(DEV), q_seq.to(DEV), torch.tensor(lens, dtype=torch.int64).to(DEV),
+                       torch.from_numpy(cand).to(DEV), P, cache, ps, fp4q=True)
+    torch.cuda.synchronize()
+    p = checks.host(ps)
+    for i in range(Q):
+        b = int(q_seq[i])
+        ids = cand[i, :lens[i]]
+        if lens[i]:
+            checks.check_scores(p[i, :lens[i]], _oracle_scores_fp4q(q64[i], w64[i], khat[b][ids]))
+        assert np.all(p[i, lens[i]:] == -7.0)
+
+
+def test_index_score_fp4q_many_queries():
+    """300 queries over mixed sequences and ragged visible counts, and the
+    top-512 of the resulting scores equal to the oracle's selection."""
+    B, T, Q = 3, 1000, 300
+    _, _, _, cache = _build(B, T, 1, seed=33)
+    q, w = _scores_inputs(Q, 34)
+    rng = np.random.default_rng(7)
+    q_seq = rng.integers(0, B, Q).astype(np.int32)
+    n_vis = (np.arange(Q) * 13 % (T + 1)).astype(np.int64)
+    n_vis[:10] = T
+    scores = torch.full((Q, 1008), -7.0, device=DEV)
+    C.csa2_index_score(q.to(DEV), w.to(DEV), torch.from_numpy(q_seq).to(DEV),
+                       torch.from_numpy(n_vis).to(DEV), None, T, cache, scores, fp4q=True)
+    torch.cuda.synchronize()
+    s = checks.host(scores)
+    q64, w64 = checks.bf16_to_f64(q), w.double().numpy()
+    khat = [R.dequant_mxfp4(checks.host(cache.ik_codes[b]), checks.host(cache.ik_scales[b])) for b in range(B)]
+    for i in range(Q):
+        nv = int(n_vis[i])
+        if nv:
+            checks.check_scores(s[i, :nv], _oracle_scores_fp4q(q64[i], w64[i], khat[q_seq[i]][:nv]))
+        assert np.all(s[i, nv:] == -7.0)
+    # the fp4-query scores feed the same selection
+    o = _topk(np.ascontiguousarray(s[:10]), n_vis[:10], 512)
+    for i in range(10):
+        checks.check_topk_exact(o[i], s[i, :T], 512)
+
+
 def test_index_score_many_queries():
     """300 queries: a run sharing one sequence, then mixed sequences, ragged
     and zero visible counts, a column count that is not a multiple of the
