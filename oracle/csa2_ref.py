@@ -240,6 +240,76 @@ def gather_rows(kv_codes, kv_scales, idx, swa_codes=None, swa_scale=None):
     return np.concatenate(rows, axis=0)
 
 
+# ------------------------------------- f2 decode-time append and state
+SWA_WINDOW = 128        # n_win: SWA rows kept per sequence (commentary section 1 setup)
+
+
+def quant_swa_row(x):
+    """FP8 SWA row: E4M3FN codes with one fp32 scale per row.  The V4 page
+    (Fig. 6, KV cache layout) keeps the SWA entries of the most recent
+    n_win tokens in each request's state block; the pages name the format
+    only as FP8.  Reading: sigma = max|x| / 448 and code = RNE_E4M3FN(x /
+    sigma), both quotients rounded to fp32 (the precision the kernel takes
+    this decision in); an all-zero row stores sigma = 0 and +0 codes.
+    x [.., 512] -> (codes [.., 512] u8, sigma [..] fp32)."""
+    x32 = np.asarray(x, dtype=np.float32)
+    amax = np.abs(x32).max(axis=-1)
+    sig = (amax / np.float32(448.0)).astype(np.float32)
+    safe = np.where(sig > 0, sig, np.float32(1.0)).astype(np.float32)
+    v = (x32 / safe[..., None]).astype(np.float32)
+    codes = np.where(sig[..., None] > 0, F.e4m3fn_encode(v.astype(np.float64)), 0)
+    return codes.astype(np.uint8), sig
+
+
+def new_state(m, W=SWA_WINDOW):
+    """Per-sequence state block (V4 page, Fig. 6): the raw latents and
+    compression logits of the tokens of a not yet complete group of m, the
+    SWA ring of the last W tokens, and the token count."""
+    return dict(m=m, W=W, n_tok=0,
+                tail_h=np.zeros((max(m - 1, 1), D_LATENT)), tail_z=np.zeros((max(m - 1, 1), D_LATENT)),
+                swa_codes=np.zeros((W, D_LATENT), np.uint8), swa_scale=np.zeros(W, np.float32))
+
+
+def append_token(state, cache, h, z, swa_x, w_ik):
+    """One decode token of one sequence.  Reading of the V4 page's Fig. 6:
+    token t (= the count so far) waits in the tail until it completes its
+    group of m; the m-th token's arrival compresses the group (steps a1-a3,
+    build_entries) into entry t // m of `cache` (a dict of the four entry
+    arrays, preallocated); every token's SWA row goes to ring slot t mod W.
+    h, z [512] (z ignored for m = 1), swa_x [512]; updates both in place."""
+    m, W, t = state["m"], state["W"], state["n_tok"]
+    s = t % m
+    if s == m - 1:
+        hh = np.concatenate([state["tail_h"][:m - 1], np.asarray(h, np.float64)[None]], axis=0)
+        zz = None if m == 1 else np.concatenate([state["tail_z"][:m - 1], np.asarray(z, np.float64)[None]], axis=0)
+        e = build_entries(hh, zz, m, w_ik)
+        for key in ("kv_codes", "kv_scales", "ik_codes", "ik_scales"):
+            cache[key][t // m] = e[key][0]
+    else:
+        state["tail_h"][s] = h
+        state["tail_z"][s] = z
+    c, sg = quant_swa_row(swa_x)
+    state["swa_codes"][t % W] = c
+    state["swa_scale"][t % W] = sg
+    state["n_tok"] = t + 1
+
+
+def decode_geometry(n_tok, m, W=SWA_WINDOW):
+    """What the next decode query of a sequence with n_tok tokens sees:
+    entries 0 .. n_tok // m - 1 (the complete groups; entry j covers tokens
+    jm .. jm + m - 1) and the SWA rows of the last min(W, n_tok) tokens,
+    which start at ring slot (n_tok - len) mod W.  -> (n_vis, swa_start, swa_len)."""
+    swa_len = min(W, n_tok)
+    return n_tok // m, (n_tok - swa_len) % W if W else 0, swa_len
+
+
+def swa_window(swa_codes, swa_scale, start, length):
+    """The SWA ring rows start, start + 1, ... (mod W), oldest first."""
+    W = len(swa_scale)
+    idx = (start + np.arange(length)) % W if length > 0 else np.zeros(0, np.int64)
+    return swa_codes[idx], swa_scale[idx]
+
+
 # ----------------------------------------- layer schedule (accounting model)
 ENCODER_GROUPS = 3          # each: 1 Full + 5 Reuse, m = 2
 DECODER_GROUPS = 5          # first: 1 Full + 3 Reuse; then 4 x (1 Reindex + 3 Reuse), m = 1

@@ -254,6 +254,95 @@ def test_fp4q_error_bound():
     assert np.array_equal(c2, c) and np.array_equal(s2.astype(int), s.astype(int) + 5)
 
 
+# ------------------------------------------------------------------ f2
+def test_swa_row_worked_example():
+    """FP8 SWA row: sigma = max|x| / 448 in fp32, codes RNE_E4M3FN(x / sigma)."""
+    x = np.zeros(512)
+    x[:5] = [3.5, -1.75, 2.0 ** -7, 0.3, -0.0]
+    c, sg = R.quant_swa_row(x)
+    assert sg == np.float32(2.0 ** -7)                 # 3.5 / 448 = 2^-7 exactly
+    # 3.5 / sigma = 448 -> 0x7E; -224 = -1.75 * 2^7 -> 0x80 | (14 << 3) | 6;
+    # 1 -> 0x38; 0.3 / 2^-7 = 38.4 -> 40 (1.25 * 2^5: (12 << 3) | 2); -0 -> 0
+    assert list(c[:5]) == [0x7E, 0xF6, 0x38, 0x62, 0x00]
+    assert np.all(c[5:] == 0)
+    z, zs = R.quant_swa_row(np.zeros(512))
+    assert zs == 0 and np.all(z == 0)
+    # sigma times the decoded code of the row maximum is the maximum itself
+    rng = np.random.default_rng(21)
+    rows = rng.standard_normal((20, 512)) * np.exp2(rng.integers(-20, 20, size=(20, 1)))
+    c, sg = R.quant_swa_row(rows)
+    dec = F.e4m3fn_value(c)
+    top = np.abs(rows).argmax(axis=1)
+    assert np.all(np.abs(dec[np.arange(20), top]) == 448.0)
+
+
+def test_swa_row_nearest_brute_force():
+    """Every code is a nearest E4M3FN value of fp32(x / sigma), ties to the
+    even code, with sigma = fp32(max|x| / 448)."""
+    rng = np.random.default_rng(22)
+    rows = rng.standard_normal((8, 512)).astype(np.float32)
+    c, sg = R.quant_swa_row(rows)
+    allc = np.arange(256)
+    allv = F.e4m3fn_value(allc)
+    fin = ~np.isnan(allv)
+    for r in range(8):
+        assert sg[r] == np.float32(np.abs(rows[r]).max() / np.float32(448))
+        v = (rows[r] / sg[r]).astype(np.float32).astype(np.float64)
+        d = np.abs(v[:, None] - allv[None, fin])
+        best = d.min(axis=1)
+        got = np.abs(v - F.e4m3fn_value(c[r]))
+        assert np.array_equal(got, best)
+
+
+def test_append_matches_batch_build():
+    """Appending T tokens one by one gives the entries that compressing the
+    complete groups in one call gives (steps a1-a3 are pinned on their own),
+    and leaves the incomplete group's tokens in the tail."""
+    rng = np.random.default_rng(23)
+    w_ik = rng.standard_normal((128, 512)) / 22.6
+    for m in (1, 2, 4):
+        T = 4 * m + (m - 1)
+        h = rng.standard_normal((T, 512))
+        z = rng.standard_normal((T, 512)) * 2
+        sw = rng.standard_normal((T, 512))
+        st = R.new_state(m, W=8)
+        cache = dict(kv_codes=np.zeros((8, 256), np.uint8), kv_scales=np.zeros((8, 32), np.uint8),
+                     ik_codes=np.zeros((8, 64), np.uint8), ik_scales=np.zeros((8, 4), np.uint8))
+        for t in range(T):
+            R.append_token(st, cache, h[t], z[t], sw[t], w_ik)
+        n = T // m
+        ref = R.build_entries(h[:n * m], None if m == 1 else z[:n * m], m, w_ik)
+        for key in ("kv_codes", "kv_scales", "ik_codes", "ik_scales"):
+            assert np.array_equal(cache[key][:n], ref[key]), (m, key)
+            assert np.all(cache[key][n:] == 0)
+        assert st["n_tok"] == T
+        if m > 1:
+            assert np.array_equal(st["tail_h"][:T - n * m], h[n * m:])
+            assert np.array_equal(st["tail_z"][:T - n * m], z[n * m:])
+
+
+def test_swa_ring_and_geometry():
+    """Geometry of the next query and the ring window, before, at and past
+    the wrap of a W = 8 ring; the window lists the last min(W, T) tokens'
+    rows oldest first."""
+    assert R.decode_geometry(0, 2, 8) == (0, 0, 0)
+    assert R.decode_geometry(5, 2, 8) == (2, 0, 5)      # entries 0, 1 = tokens 0-3
+    assert R.decode_geometry(8, 1, 8) == (8, 0, 8)
+    assert R.decode_geometry(13, 4, 8) == (3, 5, 8)     # tokens 5..12 in slots 5,6,7,0..4
+    rng = np.random.default_rng(24)
+    w_ik = rng.standard_normal((128, 512)) / 22.6
+    sw = rng.standard_normal((13, 512))
+    st = R.new_state(1, W=8)
+    cache = dict(kv_codes=np.zeros((16, 256), np.uint8), kv_scales=np.zeros((16, 32), np.uint8),
+                 ik_codes=np.zeros((16, 64), np.uint8), ik_scales=np.zeros((16, 4), np.uint8))
+    for t in range(13):
+        R.append_token(st, cache, sw[t], None, sw[t], w_ik)
+        _, start, ln = R.decode_geometry(t + 1, 1, 8)
+        wc, ws = R.swa_window(st["swa_codes"], st["swa_scale"], start, ln)
+        rc, rs = R.quant_swa_row(sw[t + 1 - ln:t + 1])
+        assert np.array_equal(wc, rc) and np.array_equal(ws, rs)
+
+
 # ------------------------------------------------------------------ a5
 def test_topk_textbook_sort_with_ties():
     rng = np.random.default_rng(8)
