@@ -100,6 +100,48 @@ def scan_roofline(wl, step, scan_us):
             "traffic": scan_traffic(wl.name, step.fp4q), "flops_per_launch": flops, **base}
 
 
+def time_append(wl, dev, calls=64):
+    """Decode-time append (csa2_decode_append) of one token per sequence for
+    the workload's batch and m, into a fresh state and a cache with room for
+    the appended entries: `calls` back-to-back calls captured in one HIP
+    graph, replayed between HIP events on the current stream.  Returns
+    microseconds per call."""
+    from long_context_sparse_csa2_amd import Cache, State, csa2_decode_append
+    B, m = wl.B, wl.m
+    cache = Cache(B, calls // m + 1, dev)
+    st = State(B, m, wl.swa, dev)
+    g = torch.Generator(device=dev).manual_seed(5)
+    h = torch.randn(calls, B, 512, device=dev, generator=g).to(torch.bfloat16)
+    z = torch.randn(calls, B, 512, device=dev, generator=g).to(torch.bfloat16) if m > 1 else None
+    sw = torch.randn(calls, B, 512, device=dev, generator=g).to(torch.bfloat16)
+    w_ik = wl.w_ik(dev)
+    n_vis = torch.empty(B, dtype=torch.int64, device=dev)
+    s0 = torch.empty(B, dtype=torch.int64, device=dev)
+    sl = torch.empty(B, dtype=torch.int32, device=dev)
+    def run():
+        for i in range(calls):
+            csa2_decode_append(h[i], z[i] if z is not None else None, sw[i], w_ik, cache, st,
+                               n_vis, s0, sl)
+    run()                                     # eager pass (loads the kernels)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(graph, stream=side):
+            run()
+    torch.cuda.current_stream().wait_stream(side)
+    st.n_tok.zero_()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    graph.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e3 / calls
+
+
 def cpu_baseline(wl, step, seconds_target=15.0):
     """The fp64 oracle, as it stands, on one sequence of the workload: the
     whole step (Full scan, pool, top-512, attention, every Reindex layer).
@@ -252,6 +294,10 @@ def main():
         "per_call_us_eager": {k: round(v, 2) for k, v in per_call.items()},
         "calls_per_step": calls,
     }
+    if not wl.prefill:
+        out["decode_append"] = {"us_per_call": round(time_append(wl, dev), 2), "batch": wl.B,
+                                "m": wl.m, "swa_window": wl.swa,
+                                "note": "csa2_decode_append, one HIP graph of 64 calls; not part of the step"}
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(wl, step)

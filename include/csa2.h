@@ -81,6 +81,18 @@ typedef struct {
   int64_t cap;            /* entries per sequence (the batch stride) */
 } csa2_cache;
 
+/* Per-sequence decode state of one KV-producing layer (host struct holding
+ * device pointers; every pointer 16-byte aligned).  Start from n_tok = 0. */
+typedef struct {
+  uint16_t* tail_h;       /* [B][m-1][512] bf16 raw latents of the incomplete group (m > 1) */
+  uint16_t* tail_z;       /* [B][m-1][512] bf16 their compression logits (m > 1)            */
+  int64_t* n_tok;         /* [B] tokens appended so far                                     */
+  uint8_t* swa_codes;     /* [B][W][512] E4M3FN SWA rows, a ring: token t in slot t mod W   */
+  float* swa_scale;       /* [B][W] fp32 row scale sigma                                    */
+  int64_t W;              /* ring slots (the SWA window), 0 <= W <= CSA2_MAX_SWA            */
+  int m;                  /* compression ratio of the layer, 1 <= m <= 16                   */
+} csa2_state;
+
 /* Name of a status code (static string). */
 const char* csa2_status_string(int status);
 
@@ -232,8 +244,9 @@ csa2_status csa2_block_pool(const float* scores, int64_t ld, int Q, const int64_
  * For query q and head h, over the rows
  *   main:  xhat_j for j = idx[q][i] (i < k, idx == -1 skipped),
  *          from sequence q_seq[q] of `src`
- *   SWA:   sigma_r * e_r for r in [swa_start[q], swa_start[q] + swa_len[q]),
- *          row r of sequence q_seq[q] of the SWA arrays
+ *   SWA:   sigma_r * e_r for the swa_len[q] rows r = (swa_start[q] + i) mod T_swa,
+ *          i = 0, 1, ..., of sequence q_seq[q] of the SWA arrays (the SWA
+ *          arrays are a ring of T_swa slots, as csa2_decode_append keeps it)
  *   l = q[q][h] . row,  p = softmax(l),  out[q][h] = sum p * row,
  *   lse[q][h] = log sum exp(l).
  * q is used as given (the 1/sqrt(512) softmax scale is folded in by the
@@ -250,7 +263,8 @@ csa2_status csa2_block_pool(const float* scores, int64_t ld, int Q, const int64_
  *   swa_scale  [B][T_swa] fp32
  *   T_swa      SWA rows per sequence
  *   swa_start  [Q] int64, swa_len [Q] int32 (0 <= swa_len <= CSA2_MAX_SWA);
- *              the window is clipped to [0, T_swa)
+ *              a window longer than T_swa is cut to T_swa rows, and a
+ *              swa_start outside [0, T_swa) gives no SWA rows
  *   out        [Q][64][512] fp32
  *   lse        [Q][64] fp32, or NULL.  A query with no rows gets out = 0,
  *              lse = -inf.
@@ -265,6 +279,45 @@ csa2_status csa2_sparse_attend(const uint16_t* q, const int32_t* q_seq, int Q, c
                                const float* swa_scale, int64_t T_swa, const int64_t* swa_start,
                                const int32_t* swa_len, float* out, float* lse, void* ws,
                                size_t ws_bytes, void* stream);
+
+/*
+ * (6) Decode-time append of one token per sequence.
+ *
+ * The V4 KV layout ("DeepSeek-V4" page, Fig. 6) keeps per request a
+ * fixed-size state block: the SWA entries of the most recent tokens and the
+ * uncompressed tail of tokens not yet ready for compression; the classical
+ * cache grows by one compressed entry per m tokens (report section 2.3:
+ * non-overlapping m-to-1 compression).  For each sequence b, with
+ * t = n_tok[b] before the call:
+ *   - if (t + 1) % m == 0, the m - 1 tail tokens followed by the new token
+ *     are compressed, quantised and projected exactly as csa2_compress_quant
+ *     does for one entry, and written as entry (t + 1) / m - 1 of `cache`
+ *     (not written if that entry is at or past cache->cap);
+ *     otherwise the new token's h and z go to tail slot t % m;
+ *   - the new token's SWA latent x = swa_new[b] is stored in ring slot t % W
+ *     as sigma = max|x| / 448 (fp32) and codes E4M3FN(RNE, saturating)(x /
+ *     sigma), both quotients rounded to fp32 (an all-zero row: sigma = 0,
+ *     +0 codes) -- the FP8 SWA row format csa2_sparse_attend reads;
+ *   - n_tok[b] = t + 1, and what the sequence's next query sees is written:
+ *     n_vis[b] = (t + 1) / m entries, swa_len[b] = min(W, t + 1) SWA rows
+ *     starting at ring slot swa_start[b] = (t + 1 - swa_len[b]) mod W.
+ *
+ *   h_new    [B][512] bf16 raw latent of the new token
+ *   z_new    [B][512] bf16 its compression logits; may be NULL iff m == 1
+ *   swa_new  [B][512] bf16 its SWA latent; may be NULL iff state->W == 0
+ *   B        sequences, 1 <= B <= 65535
+ *   w_ik     [128][512] bf16 indexer-K projection
+ *   cache    the layer's cache
+ *   state    the layer's state block
+ *   n_vis, swa_start, swa_len   [B] int64 / int64 / int32 outputs, each may
+ *            be NULL; with q_seq[q] = q they are csa2_index_score's n_vis
+ *            and csa2_sparse_attend's swa_start / swa_len (T_swa = W)
+ * Calls for one state must be ordered on one stream.
+ */
+csa2_status csa2_decode_append(const uint16_t* h_new, const uint16_t* z_new,
+                               const uint16_t* swa_new, int B, const uint16_t* w_ik,
+                               const csa2_cache* cache, const csa2_state* state, int64_t* n_vis,
+                               int64_t* swa_start, int32_t* swa_len, void* stream);
 
 /* Workspace bytes an operation needs (0 if it needs none).
  *   op      CSA2_OP_TOPK (n_cols, k), CSA2_OP_POOL (n_cols, k = n_blocks),

@@ -18,8 +18,8 @@ LIB_PATH = os.path.join(_PKG, "libcsa2.so")
 CSA2_OP_TOPK, CSA2_OP_POOL, CSA2_OP_ATTEND = 1, 2, 3
 STATUS = {0: "CSA2_OK", 1: "CSA2_EINVAL", 2: "CSA2_EUNSUPPORTED", 3: "CSA2_EWORKSPACE", 4: "CSA2_EHIP"}
 EXPORTS = ("csa2_status_string", "csa2_last_error", "csa2_compress_quant", "csa2_index_score",
-           "csa2_index_score_fp4q", "csa2_select_topk", "csa2_block_pool", "csa2_sparse_attend", "csa2_workspace_bytes",
-           "csa2_selftest")
+           "csa2_index_score_fp4q", "csa2_select_topk", "csa2_block_pool", "csa2_sparse_attend",
+           "csa2_decode_append", "csa2_workspace_bytes", "csa2_selftest")
 
 
 class Csa2Error(RuntimeError):
@@ -32,6 +32,12 @@ class _Cache(ctypes.Structure):
     _fields_ = [("kv_codes", ctypes.c_void_p), ("kv_scales", ctypes.c_void_p),
                 ("ik_codes", ctypes.c_void_p), ("ik_scales", ctypes.c_void_p),
                 ("cap", ctypes.c_int64)]
+
+
+class _State(ctypes.Structure):
+    _fields_ = [("tail_h", ctypes.c_void_p), ("tail_z", ctypes.c_void_p),
+                ("n_tok", ctypes.c_void_p), ("swa_codes", ctypes.c_void_p),
+                ("swa_scale", ctypes.c_void_p), ("W", ctypes.c_int64), ("m", ctypes.c_int)]
 
 
 _lib = None
@@ -62,6 +68,9 @@ def lib():
         L.csa2_sparse_attend.restype = I
         L.csa2_sparse_attend.argtypes = [P, P, I, ctypes.POINTER(_Cache), P, I, P, P, I64, P, P,
                                          P, P, P, SZ, P]
+        L.csa2_decode_append.restype = I
+        L.csa2_decode_append.argtypes = [P, P, P, I, P, ctypes.POINTER(_Cache),
+                                         ctypes.POINTER(_State), P, P, P, P]
         L.csa2_workspace_bytes.restype = SZ
         L.csa2_workspace_bytes.argtypes = [I, I, I64, I]
         L.csa2_selftest.restype = I
@@ -127,6 +136,33 @@ class Cache:
     @property
     def nbytes(self):
         return sum(a.numel() for a in self.arrays().values())
+
+
+class State:
+    """One KV-producing layer's decode state for B sequences (allocated by
+    torch, zeroed: n_tok = 0): the tail of the incomplete group of m tokens
+    and the SWA ring of W rows."""
+
+    def __init__(self, B, m, W, device):
+        self.B, self.m, self.W = B, m, W
+        t = max(m - 1, 1)
+        self.tail_h = torch.zeros(B, t, 512, dtype=torch.bfloat16, device=device)
+        self.tail_z = torch.zeros(B, t, 512, dtype=torch.bfloat16, device=device)
+        self.n_tok = torch.zeros(B, dtype=torch.int64, device=device)
+        self.swa_codes = torch.zeros(B, max(W, 1), 512, dtype=torch.uint8, device=device)
+        self.swa_scale = torch.zeros(B, max(W, 1), dtype=torch.float32, device=device)
+
+    def view(self, b0, b1):
+        """The same state restricted to sequences b0..b1-1 (no copy)."""
+        v = State.__new__(State)
+        v.B, v.m, v.W = b1 - b0, self.m, self.W
+        for name in ("tail_h", "tail_z", "n_tok", "swa_codes", "swa_scale"):
+            setattr(v, name, getattr(self, name)[b0:b1])
+        return v
+
+    def c_struct(self):
+        return _State(self.tail_h.data_ptr(), self.tail_z.data_ptr(), self.n_tok.data_ptr(),
+                      self.swa_codes.data_ptr(), self.swa_scale.data_ptr(), self.W, self.m)
 
 
 # ------------------------------------------------------------ entry points
@@ -228,3 +264,18 @@ def workspace(op, Q, n_cols, k, device):
     for, or None when the operation needs none."""
     n = csa2_workspace_bytes(op, Q, n_cols, k)
     return torch.zeros(n, dtype=torch.uint8, device=device) if n else None
+
+
+def csa2_decode_append(h_new, z_new, swa_new, w_ik, cache, state, n_vis=None, swa_start=None,
+                       swa_len=None, stream=None):
+    """h_new, z_new (None iff m == 1), swa_new: [B, 512] bf16; w_ik [128, 512]
+    bf16; n_vis / swa_start [B] int64 and swa_len [B] int32 outputs or None."""
+    for t, n in ((h_new, "h_new"), (z_new, "z_new"), (swa_new, "swa_new"), (w_ik, "w_ik")):
+        _dtype(t, torch.bfloat16, n)
+    _dtype(n_vis, torch.int64, "n_vis"); _dtype(swa_start, torch.int64, "swa_start")
+    _dtype(swa_len, torch.int32, "swa_len")
+    cs, ss = cache.c_struct(), state.c_struct()
+    st = lib().csa2_decode_append(_ptr(h_new), _ptr(z_new), _ptr(swa_new), h_new.shape[0],
+                                  _ptr(w_ik), ctypes.byref(cs), ctypes.byref(ss), _ptr(n_vis),
+                                  _ptr(swa_start), _ptr(swa_len), _stream(stream, h_new))
+    _check("csa2_decode_append", st)

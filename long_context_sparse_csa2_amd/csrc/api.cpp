@@ -112,6 +112,45 @@ csa2_status csa2_compress_quant(const uint16_t* h, const uint16_t* z, int B, int
                     "csa2_compress_quant launch");
 }
 
+csa2_status csa2_decode_append(const uint16_t* h_new, const uint16_t* z_new,
+                               const uint16_t* swa_new, int B, const uint16_t* w_ik,
+                               const csa2_cache* cache, const csa2_state* state, int64_t* n_vis,
+                               int64_t* swa_start, int32_t* swa_len, void* stream) {
+  g_err[0] = 0;
+  REQ(h_new && w_ik && state, "h_new, w_ik, state must not be NULL");
+  const csa2_status cs = check_cache(cache);
+  if (cs != CSA2_OK) return cs;
+  const int m = state->m;
+  const int64_t W = state->W;
+  REQ(B > 0 && B <= 65535, "B=%d must be in [1, 65535]", B);
+  REQ(m >= 1 && m <= 16, "state->m=%d must be in [1, 16]", m);
+  REQ(W >= 0 && W <= CSA2_MAX_SWA, "state->W=%lld must be in [0, %d]", (long long)W,
+      CSA2_MAX_SWA);
+  REQ(state->n_tok, "state->n_tok must not be NULL");
+  REQ(m == 1 || (z_new && state->tail_h && state->tail_z),
+      "z_new, state->tail_h and state->tail_z must be given when m > 1");
+  REQ(W == 0 || (swa_new && state->swa_codes && state->swa_scale),
+      "swa_new, state->swa_codes and state->swa_scale must be given when W > 0");
+  REQ(al(h_new, 16) && (!z_new || al(z_new, 16)) && (!swa_new || al(swa_new, 16)) &&
+          al(w_ik, 16) && (!state->tail_h || al(state->tail_h, 16)) &&
+          (!state->tail_z || al(state->tail_z, 16)) && al(state->n_tok, 8) &&
+          (!state->swa_codes || al(state->swa_codes, 16)) &&
+          (!state->swa_scale || al(state->swa_scale, 4)),
+      "h_new, z_new, swa_new, w_ik and the state arrays must be 16-byte aligned");
+  hipStream_t st = (hipStream_t)stream;
+  const uint16_t* zn = m == 1 ? nullptr : z_new;
+  CHECKED(hip_status(csa2::launch_append_compress(h_new, zn, B, m, state->tail_h, state->tail_z,
+                                                  state->n_tok, w_ik, cache->kv_codes,
+                                                  cache->kv_scales, cache->ik_codes,
+                                                  cache->ik_scales, cache->cap, st),
+                     "csa2_decode_append compress launch"));
+  return hip_status(csa2::launch_append_state(h_new, zn, W > 0 ? swa_new : nullptr, B, m,
+                                              state->tail_h, state->tail_z, state->n_tok,
+                                              state->swa_codes, state->swa_scale, W, n_vis,
+                                              swa_start, swa_len, st),
+                    "csa2_decode_append state launch");
+}
+
 static csa2_status index_score_common(const uint16_t* q_idx, const float* w,
                                       const int32_t* q_seq, const int64_t* n_vis,
                                       const int32_t* cand, int64_t ld_cand, int Q, int64_t n_cols,

@@ -49,8 +49,8 @@ __global__ __launch_bounds__(AW_THREADS, 1) void k_attend_wide(
   const int64_t seq = q_seq[q];
   const int64_t sst = swa_start[q];
   int64_t sl64 = swa_len[q];
-  if (sst < 0 || sst >= T_swa) sl64 = 0;
-  else if (sl64 > T_swa - sst) sl64 = T_swa - sst;
+  if (sst < 0 || sst >= T_swa) sl64 = 0;                     // ring: start must be a slot
+  else if (sl64 > T_swa) sl64 = T_swa;                       // at most one lap
   const int sl = sl64 < 0 ? 0 : (sl64 > AW_MAX_SWA ? AW_MAX_SWA : (int)sl64);
   const int nmc = (k + CH_ROWS - 1) / CH_ROWS;
   const int nch = nmc + (sl + CH_ROWS - 1) / CH_ROWS;
@@ -72,7 +72,7 @@ __global__ __launch_bounds__(AW_THREADS, 1) void k_attend_wide(
       if (e >= 0) off = seq * cap + e;
     } else {
       const int r = (ch - nmc) * CH_ROWS + srow;
-      if (r < sl) off = seq * T_swa + sst + r;
+      if (r < sl) off = seq * T_swa + (sst + r < T_swa ? sst + r : sst + r - T_swa);
     }
     return off;
   };

@@ -15,17 +15,46 @@ constexpr int CQ_ENT = 32;          // entries per workgroup
 constexpr int CQ_XPAD = 8;          // bf16 padding of an LDS latent row
 constexpr int CQ_KPAD = 4;          // fp32 padding of an LDS indexer-K row
 
+// APPEND = false: entry j of sequence b pools rows jm .. jm + m - 1 of
+// h[b] / z[b] ([B][T][512]) and is written at entry e0 + j.
+// APPEND = true (decode-time append, one workgroup per sequence, n_ent = 1):
+// the token count n_tok[b] says whether the new token (row b of h_new /
+// z_new) completes a group of m; if it does, the group is the m - 1 tokens
+// waiting in the tail (h / z as [B][m - 1][512]) followed by the new one,
+// and it becomes entry (n_tok[b] + 1) / m - 1.  Nothing is written when no
+// group completes or the entry would fall at or past cap.
+template <bool APPEND>
 __global__ __launch_bounds__(256) void k_compress_quant(
     const uint16_t* __restrict__ h, const uint16_t* __restrict__ z, int64_t T, int m,
     int64_t n_ent, const uint16_t* __restrict__ w_ik, uint8_t* __restrict__ kv_codes,
     uint8_t* __restrict__ kv_scales, uint8_t* __restrict__ ik_codes,
-    uint8_t* __restrict__ ik_scales, int64_t cap, int64_t e0) {
+    uint8_t* __restrict__ ik_scales, int64_t cap, int64_t e0,
+    const uint16_t* __restrict__ h_new, const uint16_t* __restrict__ z_new,
+    const int64_t* __restrict__ n_tok) {
   __shared__ __align__(16) uint16_t xs[CQ_ENT][D_LAT + CQ_XPAD];   // dequantised main KV, bf16
   __shared__ __align__(16) float ks[CQ_ENT][D_IDX + CQ_KPAD];      // projected indexer K
 
   const int b = blockIdx.y;
   const int64_t j0 = (int64_t)blockIdx.x * CQ_ENT;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  if constexpr (APPEND) {
+    const int64_t t = n_tok[b];                    // tokens before the new one
+    if ((t + 1) % m != 0 || (t + 1) / m > cap) return;
+    e0 = (t + 1) / m - 1;
+  }
+  // raw row t (< m) of entry j
+  auto hrow = [&](int64_t j, int t) -> const uint16_t* {
+    if constexpr (APPEND)
+      return t == m - 1 ? h_new + (int64_t)b * D_LAT : h + ((int64_t)b * (m - 1) + t) * D_LAT;
+    else
+      return h + ((int64_t)b * T + j * m + t) * D_LAT;
+  };
+  auto zrow = [&](int64_t j, int t) -> const uint16_t* {
+    if constexpr (APPEND)
+      return t == m - 1 ? z_new + (int64_t)b * D_LAT : z + ((int64_t)b * (m - 1) + t) * D_LAT;
+    else
+      return z + ((int64_t)b * T + j * m + t) * D_LAT;
+  };
 
   // ---- phase 1: pooling + main-KV quantisation; wave w owns entries 8w..8w+7,
   //      lane l owns channels 8l..8l+7 (two lanes per 16-channel scale group).
@@ -37,9 +66,8 @@ __global__ __launch_bounds__(256) void k_compress_quant(
       continue;
     }
     float x[8];
-    const int64_t row0 = (int64_t)b * T + j * m;
     if (m == 1) {
-      const u32x4_t v = *(const u32x4_t*)(h + row0 * D_LAT + lane * 8);
+      const u32x4_t v = *(const u32x4_t*)(hrow(j, 0) + lane * 8);
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
         x[2 * c] = __uint_as_float(v[c] << 16);
@@ -50,7 +78,7 @@ __global__ __launch_bounds__(256) void k_compress_quant(
 #pragma unroll
       for (int c = 0; c < 8; ++c) { zmax[c] = -INFINITY; num[c] = 0.f; den[c] = 0.f; }
       for (int t = 0; t < m; ++t) {
-        const u32x4_t zv = *(const u32x4_t*)(z + (row0 + t) * D_LAT + lane * 8);
+        const u32x4_t zv = *(const u32x4_t*)(zrow(j, t) + lane * 8);
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
           zmax[2 * c] = fmaxf(zmax[2 * c], __uint_as_float(zv[c] << 16));
@@ -58,8 +86,8 @@ __global__ __launch_bounds__(256) void k_compress_quant(
         }
       }
       for (int t = 0; t < m; ++t) {
-        const u32x4_t zv = *(const u32x4_t*)(z + (row0 + t) * D_LAT + lane * 8);
-        const u32x4_t hv = *(const u32x4_t*)(h + (row0 + t) * D_LAT + lane * 8);
+        const u32x4_t zv = *(const u32x4_t*)(zrow(j, t) + lane * 8);
+        const u32x4_t hv = *(const u32x4_t*)(hrow(j, t) + lane * 8);
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
           const float e0v = expf(__uint_as_float(zv[c] << 16) - zmax[2 * c]);
@@ -156,8 +184,20 @@ hipError_t launch_compress_quant(const uint16_t* h, const uint16_t* z, int B, in
                                  hipStream_t stream) {
   const int64_t n_ent = T / m;
   const dim3 grid((unsigned)((n_ent + CQ_ENT - 1) / CQ_ENT), (unsigned)B);
-  hipLaunchKernelGGL(k_compress_quant, grid, dim3(256), 0, stream, h, z, T, m, n_ent, w_ik,
-                     kv_codes, kv_scales, ik_codes, ik_scales, cap, e0);
+  hipLaunchKernelGGL(k_compress_quant<false>, grid, dim3(256), 0, stream, h, z, T, m, n_ent, w_ik,
+                     kv_codes, kv_scales, ik_codes, ik_scales, cap, e0, nullptr, nullptr,
+                     nullptr);
+  return hipGetLastError();
+}
+
+hipError_t launch_append_compress(const uint16_t* h_new, const uint16_t* z_new, int B, int m,
+                                  const uint16_t* tail_h, const uint16_t* tail_z,
+                                  const int64_t* n_tok, const uint16_t* w_ik, uint8_t* kv_codes,
+                                  uint8_t* kv_scales, uint8_t* ik_codes, uint8_t* ik_scales,
+                                  int64_t cap, hipStream_t stream) {
+  hipLaunchKernelGGL(k_compress_quant<true>, dim3(1, (unsigned)B), dim3(256), 0, stream, tail_h,
+                     tail_z, (int64_t)m, m, (int64_t)1, w_ik, kv_codes, kv_scales, ik_codes,
+                     ik_scales, cap, (int64_t)0, h_new, z_new, n_tok);
   return hipGetLastError();
 }
 

@@ -179,9 +179,12 @@ def check_attention(o_gpu, lse_gpu, q, rows):
 
 
 def swa_rows(swa_codes, swa_scale, start, length):
+    """The SWA window as the attention reads it: a ring of T_swa slots."""
+    T = len(swa_scale)
+    length = min(length, T) if 0 <= start < T else 0
     if length <= 0:
         return None, None
-    return swa_codes[start:start + length], swa_scale[start:start + length]
+    return R.swa_window(swa_codes, swa_scale, start, length)
 
 
 # ------------------------------------------------------------- one step

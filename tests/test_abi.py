@@ -106,6 +106,38 @@ def test_attend_validation():
     assert L.csa2_sparse_attend(P, P, 1, None, P, 8, P, P, 4, P, P, P, None, None, 0, None) == 1
 
 
+def test_decode_append_validation():
+    L = C.lib()
+    cs = _cache()
+    P = FAKE
+    ok = dict(tail_h=0x10000, tail_z=0x10000, n_tok=0x10000, swa_codes=0x10000, swa_scale=0x10000)
+
+    def state(**kw):
+        d = dict(ok, W=8, m=2)
+        d.update(kw)
+        return C._State(d["tail_h"], d["tail_z"], d["n_tok"], d["swa_codes"], d["swa_scale"],
+                        d["W"], d["m"])
+
+    def call(h=P, z=P, sw=P, B=2, w=P, cache=cs, st=None):
+        st = state() if st is None else st
+        return L.csa2_decode_append(h, z, sw, B, w, ctypes.byref(cache), ctypes.byref(st),
+                                    None, None, None, None)
+
+    assert call(h=None) == 1
+    assert call(w=None) == 1
+    assert call(B=0) == 1 and call(B=65536) == 1
+    assert call(st=state(m=0)) == 1 and call(st=state(m=17)) == 1
+    assert call(st=state(W=129)) == 1 and call(st=state(W=-1)) == 1
+    assert call(st=state(n_tok=0)) == 1
+    assert call(z=None) == 1                                  # m = 2 needs the logits
+    assert call(st=state(tail_h=0)) == 1
+    assert call(sw=None) == 1                                 # W > 0 needs the SWA latent
+    assert call(st=state(swa_codes=0)) == 1
+    assert call(h=ctypes.c_void_p(0x10008)) == 1              # misaligned
+    assert b"aligned" in L.csa2_last_error()
+    assert call(cache=_cache(ptr=0x10004)) == 1
+
+
 def test_workspace_sizes():
     # top-k / pool: the 8-way maxima levels up to the first one with <= 16384 groups
     n = 1 << 20

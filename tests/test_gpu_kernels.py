@@ -346,9 +346,10 @@ def test_sparse_attend(Q, k):
     idx[0, ::5] = -1                                  # masked selections
     T_swa = 200
     swa_c, swa_s = _swa(B, T_swa, 9)
-    start = rng.integers(0, T_swa - 128, Q).astype(np.int64)
+    start = rng.integers(0, T_swa, Q).astype(np.int64)   # windows past slot T_swa - 1 wrap
     slen = rng.integers(0, 129, Q).astype(np.int32)
     slen[0] = 128
+    start[1 % Q], slen[1 % Q] = T_swa - 1, 128        # wraps after its first row
     slen[-1] = 0                                      # no window at all
     out = torch.empty(Q, 64, 512, device=DEV)
     lse = torch.empty(Q, 64, device=DEV)
@@ -365,8 +366,8 @@ def test_sparse_attend(Q, k):
     check_q = sorted(set(range(min(Q, 24))) | set(rng.integers(0, Q, 16).tolist()) | {Q - 1})
     for i in check_q:
         b = q_seq[i]
-        rows = R.gather_rows(kv_c[b], kv_s[b], idx[i], sc_np[b, start[i]:start[i] + slen[i]],
-                             ss_np[b, start[i]:start[i] + slen[i]])
+        wc, ws_ = checks.swa_rows(sc_np[b], ss_np[b], int(start[i]), int(slen[i]))
+        rows = R.gather_rows(kv_c[b], kv_s[b], idx[i], wc, ws_)
         checks.check_attention(o[i], l[i], q64[i], rows)
 
 
