@@ -279,12 +279,16 @@ def test_select_topk_all_equal_and_empty(n):
     assert np.all(out[1] == -1)
 
 
-def test_select_topk_col_ids():
-    Q, n = 2, 16384
+@pytest.mark.parametrize("n", [16384, 3001, 700, 20000])
+def test_select_topk_col_ids(n):
+    """Mapped columns: one round with the ids loaded beside the scores (row
+    stride a multiple of 16 or not, 256- and 1024-thread selectors) and the
+    multi-round case past 16,384 columns, which maps the ids at the end."""
+    Q = 2
     rng = np.random.default_rng(3)
     s = _rand_scores(Q, n, seed=4)
     ids = np.stack([np.sort(rng.choice(1 << 20, n, replace=False)) for _ in range(Q)]).astype(np.int32)
-    nv = [n, 9000]
+    nv = [n, min(n, 9000) - 1]
     out = _topk(s, nv, 512, ids)
     for i in range(Q):
         checks.check_topk_exact(out[i], s[i, :nv[i]], 512, ids[i, :nv[i]])
