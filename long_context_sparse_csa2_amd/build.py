@@ -9,7 +9,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libcsa2.so")
-SOURCES = ["compress.hip", "append.hip", "score.hip", "select.hip", "attend.hip", "attend_wide.hip",
+SOURCES = ["compress.hip", "score.hip", "select.hip", "attend.hip", "attend_wide.hip",
            "selftest.hip", "check.hip", "api.cpp"]
 ARCH = "gfx950"
 FLAGS = [

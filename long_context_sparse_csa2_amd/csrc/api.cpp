@@ -139,16 +139,12 @@ csa2_status csa2_decode_append(const uint16_t* h_new, const uint16_t* z_new,
       "h_new, z_new, swa_new, w_ik and the state arrays must be 16-byte aligned");
   hipStream_t st = (hipStream_t)stream;
   const uint16_t* zn = m == 1 ? nullptr : z_new;
-  CHECKED(hip_status(csa2::launch_append_compress(h_new, zn, B, m, state->tail_h, state->tail_z,
-                                                  state->n_tok, w_ik, cache->kv_codes,
-                                                  cache->kv_scales, cache->ik_codes,
-                                                  cache->ik_scales, cache->cap, st),
-                     "csa2_decode_append compress launch"));
-  return hip_status(csa2::launch_append_state(h_new, zn, W > 0 ? swa_new : nullptr, B, m,
-                                              state->tail_h, state->tail_z, state->n_tok,
-                                              state->swa_codes, state->swa_scale, W, n_vis,
-                                              swa_start, swa_len, st),
-                    "csa2_decode_append state launch");
+  return hip_status(csa2::launch_append(h_new, zn, W > 0 ? swa_new : nullptr, B, m,
+                                        state->tail_h, state->tail_z, state->n_tok, w_ik,
+                                        cache->kv_codes, cache->kv_scales, cache->ik_codes,
+                                        cache->ik_scales, cache->cap, state->swa_codes,
+                                        state->swa_scale, W, n_vis, swa_start, swa_len, st),
+                    "csa2_decode_append launch");
 }
 
 static csa2_status index_score_common(const uint16_t* q_idx, const float* w,

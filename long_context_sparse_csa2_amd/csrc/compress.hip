@@ -1,5 +1,7 @@
 // Steps a1-a3: m-to-1 softmax pooling, FP4 main-KV quantisation, indexer-K
-// projection and MXFP4 quantisation, one workgroup per 32 entries.
+// projection and MXFP4 quantisation, one workgroup per 32 entries; and the
+// decode-time append, which runs the same steps on the group a new token
+// completes.
 //
 // Report digest "DeepSeek-V4.1-Flash", section 2.3: non-overlapping
 // compression, indexer K projected from the main-KV entry; section 2.4.4:
@@ -15,46 +17,29 @@ constexpr int CQ_ENT = 32;          // entries per workgroup
 constexpr int CQ_XPAD = 8;          // bf16 padding of an LDS latent row
 constexpr int CQ_KPAD = 4;          // fp32 padding of an LDS indexer-K row
 
-// APPEND = false: entry j of sequence b pools rows jm .. jm + m - 1 of
-// h[b] / z[b] ([B][T][512]) and is written at entry e0 + j.
-// APPEND = true (decode-time append, one workgroup per sequence, n_ent = 1):
-// the token count n_tok[b] says whether the new token (row b of h_new /
-// z_new) completes a group of m; if it does, the group is the m - 1 tokens
-// waiting in the tail (h / z as [B][m - 1][512]) followed by the new one,
-// and it becomes entry (n_tok[b] + 1) / m - 1.  Nothing is written when no
-// group completes or the entry would fall at or past cap.
-template <bool APPEND>
-__global__ __launch_bounds__(256) void k_compress_quant(
-    const uint16_t* __restrict__ h, const uint16_t* __restrict__ z, int64_t T, int m,
-    int64_t n_ent, const uint16_t* __restrict__ w_ik, uint8_t* __restrict__ kv_codes,
-    uint8_t* __restrict__ kv_scales, uint8_t* __restrict__ ik_codes,
-    uint8_t* __restrict__ ik_scales, int64_t cap, int64_t e0,
-    const uint16_t* __restrict__ h_new, const uint16_t* __restrict__ z_new,
-    const int64_t* __restrict__ n_tok) {
+// The compressor for entries j0 .. j0 + 31 of sequence b (those below
+// n_ent), written at entries e0 + j.  hrow(j, t) / zrow(j, t) give raw row
+// t (< m) of entry j.  ONE_ENTRY (the decode append, one valid entry) loads
+// the whole projection operand at once instead of eight steps at a time.
+template <bool ONE_ENTRY, typename HRow, typename ZRow>
+__device__ __forceinline__ void compress_entries(HRow hrow, ZRow zrow, int m, int64_t n_ent,
+                                                 int64_t j0, int b, int64_t e0,
+                                                 const uint16_t* __restrict__ w_ik,
+                                                 uint8_t* __restrict__ kv_codes,
+                                                 uint8_t* __restrict__ kv_scales,
+                                                 uint8_t* __restrict__ ik_codes,
+                                                 uint8_t* __restrict__ ik_scales, int64_t cap) {
   __shared__ __align__(16) uint16_t xs[CQ_ENT][D_LAT + CQ_XPAD];   // dequantised main KV, bf16
   __shared__ __align__(16) float ks[CQ_ENT][D_IDX + CQ_KPAD];      // projected indexer K
-
-  const int b = blockIdx.y;
-  const int64_t j0 = (int64_t)blockIdx.x * CQ_ENT;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  if constexpr (APPEND) {
-    const int64_t t = n_tok[b];                    // tokens before the new one
-    if ((t + 1) % m != 0 || (t + 1) / m > cap) return;
-    e0 = (t + 1) / m - 1;
+  // the projection operand (wave w: output dims 32w..32w+31), for a single
+  // entry loaded up front so that its latency overlaps the pooling
+  const uint16_t* wrow = w_ik + (int64_t)(wave * 32 + (lane & 31)) * D_LAT + (lane >> 5) * 8;
+  bf16x8_t wpre[ONE_ENTRY ? D_LAT / 16 : 1];
+  if constexpr (ONE_ENTRY) {
+#pragma unroll
+    for (int s = 0; s < D_LAT / 16; ++s) wpre[s] = *(const bf16x8_t*)(wrow + 16 * s);
   }
-  // raw row t (< m) of entry j
-  auto hrow = [&](int64_t j, int t) -> const uint16_t* {
-    if constexpr (APPEND)
-      return t == m - 1 ? h_new + (int64_t)b * D_LAT : h + ((int64_t)b * (m - 1) + t) * D_LAT;
-    else
-      return h + ((int64_t)b * T + j * m + t) * D_LAT;
-  };
-  auto zrow = [&](int64_t j, int t) -> const uint16_t* {
-    if constexpr (APPEND)
-      return t == m - 1 ? z_new + (int64_t)b * D_LAT : z + ((int64_t)b * (m - 1) + t) * D_LAT;
-    else
-      return z + ((int64_t)b * T + j * m + t) * D_LAT;
-  };
 
   // ---- phase 1: pooling + main-KV quantisation; wave w owns entries 8w..8w+7,
   //      lane l owns channels 8l..8l+7 (two lanes per 16-channel scale group).
@@ -130,13 +115,18 @@ __global__ __launch_bounds__(256) void k_compress_quant(
   //      MFMA; wave w computes output dims 32w..32w+31.
   {
     const int r = lane & 31, kh = lane >> 5;
-    const uint16_t* wrow = w_ik + (int64_t)(wave * 32 + r) * D_LAT + kh * 8;
     f32x16_t acc = {};
+    if constexpr (ONE_ENTRY) {
+#pragma unroll
+      for (int s = 0; s < D_LAT / 16; ++s)
+        acc = mfma32_bf16(*(const bf16x8_t*)&xs[r][16 * s + kh * 8], wpre[s], acc);
+    } else {
 #pragma unroll 8
-    for (int s = 0; s < D_LAT / 16; ++s) {
-      const bf16x8_t a = *(const bf16x8_t*)&xs[r][16 * s + kh * 8];
-      const bf16x8_t bb = *(const bf16x8_t*)(wrow + 16 * s);
-      acc = mfma32_bf16(a, bb, acc);
+      for (int s = 0; s < D_LAT / 16; ++s) {
+        const bf16x8_t a = *(const bf16x8_t*)&xs[r][16 * s + kh * 8];
+        const bf16x8_t bb = *(const bf16x8_t*)(wrow + 16 * s);
+        acc = mfma32_bf16(a, bb, acc);
+      }
     }
 #pragma unroll
     for (int jj = 0; jj < 16; ++jj) ks[8 * (jj >> 2) + 4 * kh + (jj & 3)][wave * 32 + r] = acc[jj];
@@ -178,26 +168,133 @@ __global__ __launch_bounds__(256) void k_compress_quant(
   }
 }
 
+__global__ __launch_bounds__(256) void k_compress_quant(
+    const uint16_t* __restrict__ h, const uint16_t* __restrict__ z, int64_t T, int m,
+    int64_t n_ent, const uint16_t* __restrict__ w_ik, uint8_t* __restrict__ kv_codes,
+    uint8_t* __restrict__ kv_scales, uint8_t* __restrict__ ik_codes,
+    uint8_t* __restrict__ ik_scales, int64_t cap, int64_t e0) {
+  const int b = blockIdx.y;
+  compress_entries<false>(
+      [&](int64_t j, int t) { return h + ((int64_t)b * T + j * m + t) * D_LAT; },
+      [&](int64_t j, int t) { return z + ((int64_t)b * T + j * m + t) * D_LAT; }, m, n_ent,
+      (int64_t)blockIdx.x * CQ_ENT, b, e0, w_ik, kv_codes, kv_scales, ik_codes, ik_scales, cap);
+}
+
 hipError_t launch_compress_quant(const uint16_t* h, const uint16_t* z, int B, int64_t T, int m,
                                  const uint16_t* w_ik, uint8_t* kv_codes, uint8_t* kv_scales,
                                  uint8_t* ik_codes, uint8_t* ik_scales, int64_t cap, int64_t e0,
                                  hipStream_t stream) {
   const int64_t n_ent = T / m;
   const dim3 grid((unsigned)((n_ent + CQ_ENT - 1) / CQ_ENT), (unsigned)B);
-  hipLaunchKernelGGL(k_compress_quant<false>, grid, dim3(256), 0, stream, h, z, T, m, n_ent, w_ik,
-                     kv_codes, kv_scales, ik_codes, ik_scales, cap, e0, nullptr, nullptr,
-                     nullptr);
+  hipLaunchKernelGGL(k_compress_quant, grid, dim3(256), 0, stream, h, z, T, m, n_ent, w_ik,
+                     kv_codes, kv_scales, ik_codes, ik_scales, cap, e0);
   return hipGetLastError();
 }
 
-hipError_t launch_append_compress(const uint16_t* h_new, const uint16_t* z_new, int B, int m,
-                                  const uint16_t* tail_h, const uint16_t* tail_z,
-                                  const int64_t* n_tok, const uint16_t* w_ik, uint8_t* kv_codes,
-                                  uint8_t* kv_scales, uint8_t* ik_codes, uint8_t* ik_scales,
-                                  int64_t cap, hipStream_t stream) {
-  hipLaunchKernelGGL(k_compress_quant<true>, dim3(1, (unsigned)B), dim3(256), 0, stream, tail_h,
-                     tail_z, (int64_t)m, m, (int64_t)1, w_ik, kv_codes, kv_scales, ik_codes,
-                     ik_scales, cap, (int64_t)0, h_new, z_new, n_tok);
+// ------------------------------------------------------------ decode append
+// Decode-time append: the per-sequence state block of the V4 KV layout
+// ("DeepSeek-V4" page, Fig. 6: a fixed-size block per request holding the
+// SWA entries of the most recent tokens and the uncompressed tail that is
+// not yet ready for compression).  One workgroup per sequence, one token:
+//   - with t = n_tok[b] tokens before it, the new token completes a group of
+//     m iff (t + 1) % m == 0; then the m - 1 tail tokens followed by the new
+//     one are compressed exactly as above into entry (t + 1) / m - 1 (not
+//     written at or past cap);
+//   - otherwise the token's raw latent and logits go to tail slot t % m;
+//   - its SWA latent x becomes one FP8 row in ring slot t % W: sigma =
+//     max|x| / 448 and codes E4M3FN(x / sigma), both quotients IEEE fp32
+//     (all-zero row: sigma = 0, +0 codes);
+//   - the next query's geometry is written and the count advances.
+__device__ __forceinline__ void append_state_wave(
+    int64_t t, int b, const uint16_t* __restrict__ h_new, const uint16_t* __restrict__ z_new,
+    const uint16_t* __restrict__ swa_new, int m, uint16_t* __restrict__ tail_h,
+    uint16_t* __restrict__ tail_z, int64_t* __restrict__ n_tok, uint8_t* __restrict__ swa_codes,
+    float* __restrict__ swa_scale, int64_t W, int64_t* __restrict__ n_vis,
+    int64_t* __restrict__ swa_start, int32_t* __restrict__ swa_len) {
+  const int lane = threadIdx.x & 63;                  // lane l owns channels 8l .. 8l + 7
+  const int s = (int)(t % m);
+  if (s < m - 1) {                                    // the group is not complete: keep the token
+    const int64_t src = (int64_t)b * D_LAT + lane * 8;
+    const int64_t dst = ((int64_t)b * (m - 1) + s) * D_LAT + lane * 8;
+    *(u32x4_t*)(tail_h + dst) = *(const u32x4_t*)(h_new + src);
+    *(u32x4_t*)(tail_z + dst) = *(const u32x4_t*)(z_new + src);
+  }
+  if (W > 0) {
+    const u32x4_t v = *(const u32x4_t*)(swa_new + (int64_t)b * D_LAT + lane * 8);
+    float x[8];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      x[2 * c] = __uint_as_float(v[c] << 16);
+      x[2 * c + 1] = __uint_as_float(v[c] & 0xFFFF0000u);
+    }
+    float amax = 0.f;
+#pragma unroll
+    for (int c = 0; c < 8; ++c) amax = fmaxf(amax, fabsf(x[c]));
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
+    const float sig = amax / 448.0f;                  // IEEE division, as every quotient here
+    uint32_t lo = 0, hi = 0;
+    if (sig > 0.f) {
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        const float q = x[c] / sig;
+        const uint32_t code = e4m3_encode_pos(fabsf(q)) | (q < 0.f ? 0x80u : 0u);
+        if (c < 4) lo |= code << (8 * c); else hi |= code << (8 * (c - 4));
+      }
+    }
+    const int64_t slot = (int64_t)b * W + t % W;
+    *(uint2*)(swa_codes + slot * D_LAT + lane * 8) = make_uint2(lo, hi);
+    if (lane == 0) swa_scale[slot] = sig;
+  }
+  if (lane == 0) {
+    const int64_t n = t + 1;
+    const int64_t len = n < W ? n : W;
+    if (n_vis) n_vis[b] = n / m;
+    if (swa_start) swa_start[b] = W > 0 ? (n - len) % W : 0;
+    if (swa_len) swa_len[b] = (int32_t)len;
+    n_tok[b] = n;
+  }
+}
+
+__global__ __launch_bounds__(256) void k_append(
+    const uint16_t* __restrict__ h_new, const uint16_t* __restrict__ z_new,
+    const uint16_t* __restrict__ swa_new, int m, uint16_t* __restrict__ tail_h,
+    uint16_t* __restrict__ tail_z, int64_t* __restrict__ n_tok, const uint16_t* __restrict__ w_ik,
+    uint8_t* __restrict__ kv_codes, uint8_t* __restrict__ kv_scales,
+    uint8_t* __restrict__ ik_codes, uint8_t* __restrict__ ik_scales, int64_t cap,
+    uint8_t* __restrict__ swa_codes, float* __restrict__ swa_scale, int64_t W,
+    int64_t* __restrict__ n_vis, int64_t* __restrict__ swa_start, int32_t* __restrict__ swa_len) {
+  const int b = blockIdx.x;
+  const int64_t t = n_tok[b];                         // tokens before the new one
+  __syncthreads();                                    // read by every thread before it changes
+  // the last wave files the token (its loads overlap the compressor's)
+  if (threadIdx.x >= 192)
+    append_state_wave(t, b, h_new, z_new, swa_new, m, tail_h, tail_z, n_tok, swa_codes,
+                      swa_scale, W, n_vis, swa_start, swa_len);
+  if ((t + 1) % m == 0 && (t + 1) / m <= cap) {
+    const uint16_t* th = tail_h;
+    const uint16_t* tz = tail_z;
+    compress_entries<true>(
+        [&](int64_t, int r) {
+          return r == m - 1 ? h_new + (int64_t)b * D_LAT : th + ((int64_t)b * (m - 1) + r) * D_LAT;
+        },
+        [&](int64_t, int r) {
+          return r == m - 1 ? z_new + (int64_t)b * D_LAT : tz + ((int64_t)b * (m - 1) + r) * D_LAT;
+        },
+        m, (int64_t)1, (int64_t)0, b, (t + 1) / m - 1, w_ik, kv_codes, kv_scales, ik_codes,
+        ik_scales, cap);
+  }
+}
+
+hipError_t launch_append(const uint16_t* h_new, const uint16_t* z_new, const uint16_t* swa_new,
+                         int B, int m, uint16_t* tail_h, uint16_t* tail_z, int64_t* n_tok,
+                         const uint16_t* w_ik, uint8_t* kv_codes, uint8_t* kv_scales,
+                         uint8_t* ik_codes, uint8_t* ik_scales, int64_t cap, uint8_t* swa_codes,
+                         float* swa_scale, int64_t W, int64_t* n_vis, int64_t* swa_start,
+                         int32_t* swa_len, hipStream_t stream) {
+  hipLaunchKernelGGL(k_append, dim3((unsigned)B), dim3(256), 0, stream, h_new, z_new, swa_new, m,
+                     tail_h, tail_z, n_tok, w_ik, kv_codes, kv_scales, ik_codes, ik_scales, cap,
+                     swa_codes, swa_scale, W, n_vis, swa_start, swa_len);
   return hipGetLastError();
 }
 

@@ -12,17 +12,12 @@ hipError_t launch_compress_quant(const uint16_t* h, const uint16_t* z, int B, in
                                  uint8_t* ik_codes, uint8_t* ik_scales, int64_t cap, int64_t e0,
                                  hipStream_t stream);
 
-hipError_t launch_append_compress(const uint16_t* h_new, const uint16_t* z_new, int B, int m,
-                                  const uint16_t* tail_h, const uint16_t* tail_z,
-                                  const int64_t* n_tok, const uint16_t* w_ik, uint8_t* kv_codes,
-                                  uint8_t* kv_scales, uint8_t* ik_codes, uint8_t* ik_scales,
-                                  int64_t cap, hipStream_t stream);
-
-hipError_t launch_append_state(const uint16_t* h_new, const uint16_t* z_new,
-                               const uint16_t* swa_new, int B, int m, uint16_t* tail_h,
-                               uint16_t* tail_z, int64_t* n_tok, uint8_t* swa_codes,
-                               float* swa_scale, int64_t W, int64_t* n_vis, int64_t* swa_start,
-                               int32_t* swa_len, hipStream_t stream);
+hipError_t launch_append(const uint16_t* h_new, const uint16_t* z_new, const uint16_t* swa_new,
+                         int B, int m, uint16_t* tail_h, uint16_t* tail_z, int64_t* n_tok,
+                         const uint16_t* w_ik, uint8_t* kv_codes, uint8_t* kv_scales,
+                         uint8_t* ik_codes, uint8_t* ik_scales, int64_t cap, uint8_t* swa_codes,
+                         float* swa_scale, int64_t W, int64_t* n_vis, int64_t* swa_start,
+                         int32_t* swa_len, hipStream_t stream);
 
 hipError_t launch_index_score(const uint16_t* q_idx, const float* w, const int32_t* q_seq,
                               const int64_t* n_vis, const int32_t* cand, int64_t ld_cand, int Q,
