@@ -33,6 +33,7 @@ MFMA_FP4_PEAK_TFLOPS = 10100.0 # MI355X dense fp4 matrix peak, AMD datasheet
 SCAN_BYTES_PER_ENTRY = 68      # MXFP4 indexer K: 64 B codes + 4 B E8M0 scales
 SCAN_FLOPS_PER_ENTRY = 2 * 32 * 128   # 32 heads x 128 dims multiply-adds per (query, entry)
 METRIC = "decode tokens/s at 1M ctx (indexer+top-512+FP4 sparse attn); % of roofline"
+PREFILL_METRIC = "prefill raw tokens/s (causal indexer+top-512+FP4 sparse attn); % of roofline"
 
 
 def step_bytes(wl):
@@ -142,12 +143,55 @@ def time_append(wl, dev, calls=64):
     return e0.elapsed_time(e1) * 1e3 / calls
 
 
+def cpu_baseline_prefill(wl, step, seconds_target=15.0):
+    """The fp64 oracle on a sample of a prefill's queries, spread over the
+    causal range: per query, every layer (scores over its visible entries,
+    top-512, attention with its SWA window).  One query stands for m raw
+    tokens, so tokens/s = m x queries / s (the work grows with the position,
+    and the sample is spread evenly, so its mean matches the whole run's)."""
+    from threadpoolctl import threadpool_info
+    from oracle import csa2_ref as R
+    ik_c = step.cache.ik_codes[0].cpu().numpy()
+    ik_s = step.cache.ik_scales[0].cpu().numpy()
+    kv_c = step.cache.kv_codes[0].cpu().numpy()
+    kv_s = step.cache.kv_scales[0].cpu().numpy()
+    n_vis = step.n_vis.cpu().numpy()
+    s0, sl = step.swa_start.cpu().numpy(), step.swa_len.cpu().numpy()
+    khat = R.dequant_mxfp4(ik_c, ik_s)
+    scores = R.index_scores_fp4q if step.fp4q else R.index_scores
+    order = np.random.default_rng(0).permutation(wl.Q)     # spread over the causal range
+    done, t_total = 0, 0.0
+    while t_total < seconds_target and done < len(order):
+        q = int(order[done])
+        t0 = time.perf_counter()
+        idx = None
+        for li, mode in enumerate(wl.layers):
+            L = step.layers[li]
+            if mode == "full":
+                s = scores(L["q_idx"][q].float().cpu().numpy().astype(np.float64),
+                           L["w"][q].cpu().numpy().astype(np.float64), khat[:int(n_vis[q])])
+                idx = R.topk(s, wl.k)
+            sc = L["swa_codes"][0, int(s0[q]):int(s0[q]) + int(sl[q])].cpu().numpy()
+            ss = L["swa_scale"][0, int(s0[q]):int(s0[q]) + int(sl[q])].cpu().numpy().astype(np.float64)
+            rows = R.gather_rows(kv_c, kv_s, idx, sc, ss)
+            R.attend(L["q_attn"][q].float().cpu().numpy().astype(np.float64), rows)
+        t_total += time.perf_counter() - t0
+        done += 1
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    return {"value": wl.m * done / t_total, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"{done} of {wl.Q} queries drawn evenly over the causal range, all "
+                      f"{len(wl.layers)} layers each, {t_total:.1f} s; m = {wl.m} raw tokens per "
+                      f"query; numpy fp64 (BLAS matmul on {threads} threads)"}
+
+
 def cpu_baseline(wl, step, seconds_target=15.0):
     """The fp64 oracle, as it stands, on one sequence of the workload: the
     whole step (Full scan, pool, top-512, attention, every Reindex layer).
     Returns tokens/s for that one-sequence sample."""
     from threadpoolctl import threadpool_info
     from oracle import csa2_ref as R
+    if wl.prefill:
+        return cpu_baseline_prefill(wl, step, seconds_target)
 
     b = 0
     kv_c = step.cache.kv_codes[b].cpu().numpy()
@@ -240,7 +284,10 @@ def main():
     # timed region: K steps; the Full-layer scan (first call of the step) is
     # launched directly and bracketed by HIP events on the stream it runs on,
     # the rest of the step replays as one HIP graph
-    graphs = None if args.eager else step.capture(split_first=True)
+    chunked = len(step.chunks) > 1
+    # a chunked prefill launches eagerly (its calls run for milliseconds) and
+    # times every chunk's scan; the other workloads replay HIP graphs
+    graphs = None if (args.eager or chunked) else step.capture(split_first=True)
     scan_ev = []
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
@@ -249,19 +296,32 @@ def main():
     for _ in range(args.steps):
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
+        if chunked:
+            pairs = []
+            for op in step.ops():
+                if op.name == "index_score_full":
+                    a = torch.cuda.Event(enable_timing=True)
+                    b = torch.cuda.Event(enable_timing=True)
+                    a.record(); op.fn(); b.record()
+                    pairs.append((a, b))
+                else:
+                    op.fn()
+            scan_ev.append(pairs)
+            continue
         if graphs:
             ops = step.ops()
             e0.record(); ops[0][2](); e1.record(); graphs[1].replay()
         else:
             ops = step.ops()
             e0.record(); ops[0][2](); e1.record()
-            for _, _, fn in ops[1:]:
-                fn()
-        scan_ev.append((e0, e1))
+            for op in ops[1:]:
+                op.fn()
+        scan_ev.append([(e0, e1)])
     t1.record()
     torch.cuda.synchronize()
     ms = t0.elapsed_time(t1) / args.steps
-    scan_us = float(np.mean([a.elapsed_time(b) for a, b in scan_ev])) * 1e3
+    # scan time per step: the Full-layer scans of the step (one launch, or one per chunk)
+    scan_us = float(np.mean([sum(a.elapsed_time(b) for a, b in st) for st in scan_ev])) * 1e3
     print(f"[bench] {ms:.3f} ms/step ({'eager' if graphs is None else 'graph replay'}); "
           f"scan {scan_us:.1f} us; eager per call (us): "
           + ", ".join(f"{k}={v:.1f}x{calls[k]}" for k, v in per_call.items()), file=sys.stderr,
@@ -270,8 +330,8 @@ def main():
     roofline = scan_roofline(wl, step, scan_us)
     step_b = step_bytes(wl)
     out = {
-        "metric": METRIC,
-        "value": round(wl.B / (ms * 1e-3), 1),
+        "metric": PREFILL_METRIC if wl.prefill else METRIC,
+        "value": round((wl.T if wl.prefill else wl.B) / (ms * 1e-3), 1),
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
@@ -285,7 +345,7 @@ def main():
         "config": {"workload": f"{wl.name}: {wl.note}", "batch": wl.B, "entries": wl.N,
                    "raw_tokens": wl.T, "m": wl.m, "layers": wl.layers, "top_k": wl.k,
                    "pool_blocks": wl.n_blocks if wl.hierarchical else 0, "swa": wl.swa,
-                   "indexer_q": args.indexer_q},
+                   "indexer_q": args.indexer_q, "query_chunk": wl.q_chunk if wl.prefill else 0},
         "roofline": roofline,
         "step_roofline": None if step_b is None else {
             "bytes": step_b, "us_at_peak": round(step_b / (HBM_PEAK_GBS * 1e3), 2),

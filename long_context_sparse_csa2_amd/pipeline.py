@@ -9,8 +9,17 @@ layer attends with the latest top-k indices and runs no indexer.  Section
 pool that the Reindex layers search.  Layers run one after another (layer
 l + 1's queries would depend on layer l's output in the model).
 
+A long encoder prefill (the commentary, section 4 item 4: the encoder's
+indexer stays quadratic, outside the hierarchy) runs its queries in chunks
+of `q_chunk`: per chunk, every layer scores the chunk's queries against
+their causally visible entries, selects and attends, so the score buffer is
+q_chunk x N instead of N x N.  Each query's result does not depend on the
+chunk it runs in.
+
 Buffers are allocated once with torch; `run()` only enqueues kernels.
 """
+
+from collections import namedtuple
 
 import torch
 
@@ -18,6 +27,9 @@ from . import (Cache, CSA2_OP_ATTEND, CSA2_OP_POOL, CSA2_OP_TOPK, csa2_block_poo
                csa2_compress_quant, csa2_index_score, csa2_select_topk, csa2_sparse_attend,
                workspace)
 from .synth import Workload
+
+# one C-ABI call of a step: its name, layer, thunk and query rows [i0, i1)
+Op = namedtuple("Op", "name layer fn rows")
 
 
 def build_cache(wl: Workload, device, seq_chunk=1):
@@ -52,11 +64,13 @@ class Step:
         self.swa_start = g["swa_start"].to(device)
         self.swa_len = g["swa_len"].to(device)
         Q, N, k = wl.Q, wl.N, wl.k
+        qc = wl.q_chunk if (wl.prefill and 0 < wl.q_chunk < Q) else Q
+        self.chunks = [(i0, min(Q, i0 + qc)) for i0 in range(0, Q, qc)]
         self.layers = [wl.layer_inputs(li, device) for li in range(len(wl.layers))]
-        self.scores = torch.empty(Q, N, dtype=torch.float32, device=device)
-        self.idx = torch.empty(Q, k, dtype=torch.int32, device=device)
-        self.ws_topk = workspace(CSA2_OP_TOPK, Q, N, k, device)
-        self.ws_attend = workspace(CSA2_OP_ATTEND, Q, 0, k, device)
+        self.scores = torch.empty(qc, N, dtype=torch.float32, device=device)
+        self.idx = torch.empty(qc, k, dtype=torch.int32, device=device)
+        self.ws_topk = workspace(CSA2_OP_TOPK, qc, N, k, device)
+        self.ws_attend = workspace(CSA2_OP_ATTEND, qc, 0, k, device)
         self.out = [torch.empty(Q, 64, 512, dtype=torch.float32, device=device) for _ in wl.layers]
         self.lse = [torch.empty(Q, 64, dtype=torch.float32, device=device) for _ in wl.layers]
         self.idx_per_layer = [None] * len(wl.layers)
@@ -72,62 +86,91 @@ class Step:
             self.idx_r = [torch.empty(Q, k, dtype=torch.int32, device=device) for _ in wl.layers]
 
     def ops(self):
-        """The step as an ordered list of (name, layer, thunk); each thunk
-        enqueues one C-ABI call on the current stream."""
+        """The step as an ordered list of Op(name, layer, thunk, rows); each
+        thunk enqueues one C-ABI call on the current stream.  A chunked
+        prefill runs all layers for one chunk of queries before the next."""
         wl = self.wl
         out = []
-        idx = self.idx
-        for li, mode in enumerate(wl.layers):
-            L = self.layers[li]
-            if mode == "full":
-                out.append(("index_score_full", li, lambda L=L: csa2_index_score(
-                    L["q_idx"], L["w"], self.q_seq, self.n_vis, None, wl.N, self.cache, self.scores,
-                    fp4q=self.fp4q)))
-                if wl.hierarchical:
-                    # the pool and the layer's own top-k in one selection pass
-                    out.append(("block_pool_topk", li, lambda: csa2_block_pool(
-                        self.scores, self.n_vis, wl.N, wl.n_blocks, self.pool, self.pool_len,
-                        self.ws_pool, block=wl.block, topk=self.idx)))
-                else:
-                    out.append(("select_topk_full", li, lambda: csa2_select_topk(
-                        self.scores, self.n_vis, None, wl.N, wl.k, self.idx, self.ws_topk)))
-                idx = self.idx
-            elif mode == "reindex":
-                idx = self.idx_r[li]
-                out.append(("index_score_pool", li, lambda L=L: csa2_index_score(
-                    L["q_idx"], L["w"], self.q_seq, self.pool_len, self.pool, self.P, self.cache,
-                    self.pool_scores, fp4q=self.fp4q)))
-                out.append(("select_topk_pool", li, lambda idx=idx: csa2_select_topk(
-                    self.pool_scores, self.pool_len, self.pool, self.P, wl.k, idx,
-                    self.ws_topk_pool)))
-            out.append(("sparse_attend", li, lambda L=L, li=li, idx=idx: csa2_sparse_attend(
-                L["q_attn"], self.q_seq, self.cache, idx, L["swa_codes"], L["swa_scale"],
-                self.swa_start, self.swa_len, self.out[li], self.lse[li], self.ws_attend)))
+        for (i0, i1) in self.chunks:
+            n = i1 - i0
+            rows = slice(i0, i1)
+            # columns the chunk can see: causal prefill query i sees i + 1 entries
+            n_cols = i1 if wl.prefill else wl.N
+            q_seq, n_vis = self.q_seq[rows], self.n_vis[rows]
+            swa_start, swa_len = self.swa_start[rows], self.swa_len[rows]
+            scores, idx_full = self.scores[:n], self.idx[:n]
+            idx = idx_full
+            for li, mode in enumerate(wl.layers):
+                L = {key: v[rows] if key in ("q_idx", "w", "q_attn") else v
+                     for key, v in self.layers[li].items()}
+                if mode == "full":
+                    out.append(Op("index_score_full", li, lambda L=L, q_seq=q_seq, n_vis=n_vis,
+                                  n_cols=n_cols, scores=scores: csa2_index_score(
+                        L["q_idx"], L["w"], q_seq, n_vis, None, n_cols, self.cache, scores,
+                        fp4q=self.fp4q), (i0, i1)))
+                    if wl.hierarchical:
+                        # the pool and the layer's own top-k in one selection pass
+                        out.append(Op("block_pool_topk", li, lambda: csa2_block_pool(
+                            self.scores, self.n_vis, wl.N, wl.n_blocks, self.pool, self.pool_len,
+                            self.ws_pool, block=wl.block, topk=self.idx), (i0, i1)))
+                    else:
+                        out.append(Op("select_topk_full", li, lambda n_vis=n_vis, n_cols=n_cols,
+                                      scores=scores, idx=idx_full: csa2_select_topk(
+                            scores, n_vis, None, n_cols, wl.k, idx, self.ws_topk), (i0, i1)))
+                    idx = idx_full
+                elif mode == "reindex":
+                    idx = self.idx_r[li]
+                    out.append(Op("index_score_pool", li, lambda L=L: csa2_index_score(
+                        L["q_idx"], L["w"], self.q_seq, self.pool_len, self.pool, self.P,
+                        self.cache, self.pool_scores, fp4q=self.fp4q), (i0, i1)))
+                    out.append(Op("select_topk_pool", li, lambda idx=idx: csa2_select_topk(
+                        self.pool_scores, self.pool_len, self.pool, self.P, wl.k, idx,
+                        self.ws_topk_pool), (i0, i1)))
+                out.append(Op("sparse_attend", li, lambda L=L, li=li, idx=idx, q_seq=q_seq,
+                              swa_start=swa_start, swa_len=swa_len, rows=rows: csa2_sparse_attend(
+                    L["q_attn"], q_seq, self.cache, idx, L["swa_codes"], L["swa_scale"],
+                    swa_start, swa_len, self.out[li][rows], self.lse[li][rows], self.ws_attend),
+                    (i0, i1)))
         return out
 
-    def run(self, keep=False, events=None):
+    def run(self, keep=False, events=None, keep_rows=None):
         """Enqueue every layer of the step.  keep=True also keeps each
-        layer's indices and scores (for checking).  `events`, a dict, gets
+        layer's indices and scores (for checking): of every query, or with
+        keep_rows (ascending query ids) of those queries only, row j of the
+        kept arrays then being query keep_rows[j].  `events`, a dict, gets
         (start, end) torch.cuda.Event pairs recorded around each call on the
         current stream, keyed by call name."""
         wl = self.wl
-        for name, li, fn in self.ops():
+        Q = wl.Q
+        kept = torch.arange(Q) if keep_rows is None else torch.as_tensor(keep_rows, dtype=torch.int64)
+        nk = len(kept)
+        for op in self.ops():
+            name, li, (i0, i1) = op.name, op.layer, op.rows
             if events is None:
-                fn()
+                op.fn()
             else:
                 e0 = torch.cuda.Event(enable_timing=True)
                 e1 = torch.cuda.Event(enable_timing=True)
                 e0.record()
-                fn()
+                op.fn()
                 e1.record()
                 events.setdefault(name, []).append((e0, e1))
             if keep and name == "sparse_attend":
                 mode = wl.layers[li]
-                self.idx_per_layer[li] = (self.idx_r[li] if mode == "reindex" else self.idx).clone()
-                if mode == "full":
-                    self.scores_per_layer[li] = self.scores.clone()
-                elif mode == "reindex":
-                    self.scores_per_layer[li] = self.pool_scores.clone()
+                src_idx = self.idx_r[li] if mode == "reindex" else self.idx
+                sel = ((kept >= i0) & (kept < i1)).nonzero().flatten()   # kept rows in this chunk
+                dst = sel.to(self.device)
+                src_rows = (kept[sel] - i0).to(self.device)
+                if self.idx_per_layer[li] is None:
+                    self.idx_per_layer[li] = torch.empty(nk, wl.k, dtype=torch.int32,
+                                                         device=self.device)
+                self.idx_per_layer[li][dst] = src_idx.index_select(0, src_rows)
+                if mode in ("full", "reindex"):
+                    src = self.scores if mode == "full" else self.pool_scores
+                    if self.scores_per_layer[li] is None:
+                        self.scores_per_layer[li] = torch.empty(nk, src.shape[1], dtype=torch.float32,
+                                                                device=self.device)
+                    self.scores_per_layer[li][dst] = src.index_select(0, src_rows)
 
     def capture(self, split_first=True):
         """Capture the step into HIP graphs: [first call] and [the rest]
@@ -140,15 +183,15 @@ class Step:
         side.wait_stream(torch.cuda.current_stream())
         with torch.cuda.stream(side):
             for grp in groups:              # one eager pass on the capture stream first
-                for _, _, fn in grp:
-                    fn()
+                for op in grp:
+                    op.fn()
         torch.cuda.current_stream().wait_stream(side)
         torch.cuda.synchronize()
         for grp in groups:
             g = torch.cuda.CUDAGraph()
             with torch.cuda.graph(g):
-                for _, _, fn in grp:
-                    fn()
+                for op in grp:
+                    op.fn()
             graphs.append(g)
         torch.cuda.synchronize()
         return graphs

@@ -45,6 +45,8 @@ class Workload:
     hierarchical  whether the Full layer builds the 2048 x 8 candidate pool
     prefill     causal prefill (one sequence, one query per entry) instead of
                 one decode query per sequence
+    q_chunk     prefill queries per chunk (0: all at once)
+    draw_device draw the per-layer inputs on the device (large prefills)
     """
     name: str
     seed: int
@@ -58,6 +60,8 @@ class Workload:
     swa: int = 128
     block: int = 8
     n_blocks: int = 2048
+    q_chunk: int = 0
+    draw_device: bool = False
     note: str = ""
 
     @property
@@ -96,16 +100,18 @@ class Workload:
         """Per-layer queries and SWA rows (drawn on the CPU, then moved)."""
         Q = self.Q
         out = {}
-        g = _gen(self.seed, "q_idx", layer, "cpu")
-        out["q_idx"] = torch.randn(Q, 32, 128, dtype=torch.float32, generator=g).to(torch.bfloat16)
-        g = _gen(self.seed, "w", layer, "cpu")
-        out["w"] = torch.rand(Q, 32, dtype=torch.float32, generator=g)
-        g = _gen(self.seed, "q_attn", layer, "cpu")
-        out["q_attn"] = (torch.randn(Q, 64, 512, dtype=torch.float32, generator=g)
+        dd = device if self.draw_device else "cpu"
+        g = _gen(self.seed, "q_idx", layer, dd)
+        out["q_idx"] = torch.randn(Q, 32, 128, dtype=torch.float32, generator=g,
+                                   device=dd).to(torch.bfloat16)
+        g = _gen(self.seed, "w", layer, dd)
+        out["w"] = torch.rand(Q, 32, dtype=torch.float32, generator=g, device=dd)
+        g = _gen(self.seed, "q_attn", layer, dd)
+        out["q_attn"] = (torch.randn(Q, 64, 512, dtype=torch.float32, generator=g, device=dd)
                          / math.sqrt(512.0)).to(torch.bfloat16)
         nseq = 1 if self.prefill else self.B
-        g = _gen(self.seed, "swa", layer, "cpu")
-        lat = torch.randn(nseq, self.T_swa, 512, dtype=torch.float32, generator=g)
+        g = _gen(self.seed, "swa", layer, dd)
+        lat = torch.randn(nseq, self.T_swa, 512, dtype=torch.float32, generator=g, device=dd)
         scale = lat.abs().amax(dim=2) / 448.0
         codes = (lat / scale[..., None]).to(torch.float8_e4m3fn).view(torch.uint8)
         out["swa_codes"] = codes
@@ -150,6 +156,11 @@ WORKLOADS = {
     "c4": Workload("c4", 4, B=8, T=1 << 20, m=2,
                    layers=["full", "reuse", "reuse", "reuse", "reuse", "reuse"],
                    note="encoder long-context decode with reuse, 1M raw tokens, m=2, batch 8"),
+    # long encoder prefill in query chunks: one encoder group (Full + 5 Reuse)
+    "p64k": Workload("p64k", 5, B=1, T=1 << 16, m=2,
+                     layers=["full", "reuse", "reuse", "reuse", "reuse", "reuse"], prefill=True,
+                     q_chunk=4096, draw_device=True,
+                     note="encoder group prefill of 65,536 raw tokens (m=2) in 4096-query chunks"),
 }
 
 
