@@ -310,6 +310,48 @@ def swa_window(swa_codes, swa_scale, start, length):
     return swa_codes[idx], swa_scale[idx]
 
 
+# ------------------------------------ f4 RoPE around attention, bf16 cast
+def rope_rotate(x, pos, dims, theta):
+    """RoPE on the last `dims` of the 512 channels of each row.  Reading (the
+    pages fix neither the channels, the pairing nor the base): the RoFormer
+    rule on adjacent pairs, pair i = channels (512 - dims + 2i, 512 - dims +
+    2i + 1) turned by the angle pos * theta^(-2i / dims):
+        (a, b) -> (a cos - b sin, a sin + b cos).
+    x [.., 512]; pos a scalar (one position for all rows) -> fp64 [.., 512]."""
+    x = np.array(x, dtype=np.float64, copy=True)
+    if dims == 0:
+        return x
+    i = np.arange(dims // 2)
+    ang = float(pos) * np.asarray(theta, dtype=np.float64) ** (-2.0 * i / dims)
+    c, s = np.cos(ang), np.sin(ang)
+    a = x[..., D_LATENT - dims::2].copy()
+    b = x[..., D_LATENT - dims + 1::2].copy()
+    x[..., D_LATENT - dims::2] = a * c - b * s
+    x[..., D_LATENT - dims + 1::2] = a * s + b * c
+    return x
+
+
+def bf16_round(x):
+    """Round to bf16 (8 significant bits), to nearest, ties to even."""
+    x = np.asarray(x, dtype=np.float64)
+    m, e = np.frexp(x)                      # x = m 2^e, |m| in [0.5, 1)
+    return np.ldexp(np.rint(np.ldexp(m, 8)), e - 8)
+
+
+def attend_rope(q, rows, pos, dims, theta):
+    """Fused RoPE - attention - inverse RoPE - cast, as the report (section
+    3.2) names FlashMLA's kernel.  The cache holds post-RoPE latents (section
+    2.4.4: quantised after RoPE), so the rows are used as stored; the query's
+    RoPE channels are turned by its position first; the output, a
+    probability-weighted mix of rows that carry their own rotations, has its
+    RoPE channels turned back by the query's position (reading: the second
+    RoPE of the fused kernel is this inverse rotation); the result is cast to
+    bf16.  -> (o_bf16 [64, 512] as fp64, o before the cast, lse [64])."""
+    o, lse = attend(rope_rotate(q, pos, dims, theta), rows)
+    o = rope_rotate(o, -float(pos), dims, theta)
+    return bf16_round(o), o, lse
+
+
 # ----------------------------------------- layer schedule (accounting model)
 ENCODER_GROUPS = 3          # each: 1 Full + 5 Reuse, m = 2
 DECODER_GROUPS = 5          # first: 1 Full + 3 Reuse; then 4 x (1 Reindex + 3 Reuse), m = 1

@@ -343,6 +343,64 @@ def test_swa_ring_and_geometry():
         assert np.array_equal(wc, rc) and np.array_equal(ws, rs)
 
 
+# ------------------------------------------------------------------ f4
+def test_rope_worked_example_and_identities():
+    """RoPE on the last `dims` channels, adjacent pairs, angle pos *
+    theta^(-2i/dims): values worked by hand for dims = 4, theta = 100."""
+    x = np.zeros(512)
+    x[508], x[510], x[100] = 1.0, 2.0, 7.0
+    y = R.rope_rotate(x, np.pi / 2, 4, 100.0)
+    # pair 0 (508, 509) turns by pi/2: (1, 0) -> (0, 1); pair 1 (510, 511) by
+    # pi/20: (2, 0) -> (2 cos, 2 sin); channel 100 is not a RoPE channel
+    assert abs(y[508]) < 1e-15 and y[509] == 1.0
+    assert np.isclose(y[510], 2 * np.cos(np.pi / 20), rtol=1e-15)
+    assert np.isclose(y[511], 2 * np.sin(np.pi / 20), rtol=1e-15)
+    assert y[100] == 7.0 and np.count_nonzero(np.abs(y) > 1e-15) == 4
+    rng = np.random.default_rng(31)
+    v = rng.standard_normal((5, 512))
+    assert np.array_equal(R.rope_rotate(v, 0, 64, 1e4), v)
+    assert np.array_equal(R.rope_rotate(v, 123, 0, 1e4), v)
+    a = R.rope_rotate(R.rope_rotate(v, 1000, 64, 1e4), 234567, 64, 1e4)
+    assert np.allclose(a, R.rope_rotate(v, 235567, 64, 1e4), rtol=0, atol=1e-9)
+    r = R.rope_rotate(v, 98765, 64, 1e4)
+    assert np.array_equal(r[:, :448], v[:, :448])
+    pn = lambda z: z[:, 448::2] ** 2 + z[:, 449::2] ** 2
+    assert np.allclose(pn(r), pn(v), rtol=1e-12)
+    # dot products depend only on the position difference
+    q, k = rng.standard_normal(512), rng.standard_normal(512)
+    d1 = R.rope_rotate(q, 500, 64, 1e4) @ R.rope_rotate(k, 530, 64, 1e4)
+    d2 = R.rope_rotate(q, 70000, 64, 1e4) @ R.rope_rotate(k, 70030, 64, 1e4)
+    assert np.isclose(d1, d2, rtol=1e-9)
+
+
+def test_bf16_round():
+    assert list(R.bf16_round([1.0, 1 + 2 ** -8, 1 + 3 * 2 ** -8, -(1 + 2 ** -8 + 2 ** -20)])) == \
+        [1.0, 1.0, 1 + 2 ** -6, -(1 + 2 ** -7)]        # ties to even, otherwise nearest
+    x = np.random.default_rng(32).standard_normal(1000) * 100
+    r = R.bf16_round(x)
+    assert np.all(np.abs(r - x) <= np.abs(x) * 2.0 ** -8)
+    assert np.array_equal(R.bf16_round(r), r)
+
+
+def test_attend_rope_undoes_the_rows_rotation():
+    """Rows that are a value set rotated by the query's own position give
+    exactly the attention over the unrotated values (before the cast):
+    dot products are rotation-invariant and the inverse RoPE undoes the
+    rotation the mix carries.  A sign slip in either rotation breaks it."""
+    rng = np.random.default_rng(33)
+    q = rng.standard_normal((64, 512)) / np.sqrt(512)
+    v = rng.standard_normal((40, 512))
+    for pos in (0, 17, 1 << 20):
+        rows = R.rope_rotate(v, pos, 64, 1e4)
+        ob, o, lse = R.attend_rope(q, rows, pos, 64, 1e4)
+        o_ref, lse_ref = R.attend(q, v)
+        assert np.allclose(o, o_ref, rtol=0, atol=1e-11) and np.allclose(lse, lse_ref, atol=1e-11)
+        assert np.array_equal(ob, R.bf16_round(o))
+    # no RoPE channels: plain attention
+    ob, o, lse = R.attend_rope(q, v, 5, 0, 1e4)
+    assert np.array_equal(o, R.attend(q, v)[0])
+
+
 # ------------------------------------------------------------------ a5
 def test_topk_textbook_sort_with_ties():
     rng = np.random.default_rng(8)
