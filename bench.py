@@ -143,6 +143,45 @@ def time_append(wl, dev, calls=64):
     return e0.elapsed_time(e1) * 1e3 / calls
 
 
+def time_attend_rope(step, dev, calls=20):
+    """The fused RoPE - attention - inverse RoPE - bf16 cast
+    (csa2_sparse_attend_rope, 64 rotated channels, theta 10000) on the step's
+    first layer (its queries, selection and SWA windows), next to the plain
+    csa2_sparse_attend on the same inputs: `calls` launches of each captured
+    in a HIP graph and replayed between HIP events.  Returns microseconds per
+    call (rope, plain)."""
+    from long_context_sparse_csa2_amd import csa2_sparse_attend, csa2_sparse_attend_rope
+    wl = step.wl
+    L = step.layers[0]
+    Q = wl.Q if not step.chunks or len(step.chunks) == 1 else step.chunks[0][1]
+    rows = slice(0, Q)
+    pos = (torch.arange(Q, dtype=torch.int64, device=dev) * 7919 + (1 << 20) - 1)
+    out_b = torch.empty(Q, 64, 512, dtype=torch.bfloat16, device=dev)
+    out_f = torch.empty(Q, 64, 512, dtype=torch.float32, device=dev)
+    args = (L["q_attn"][rows], step.q_seq[rows], step.cache, step.idx[:Q], L["swa_codes"],
+            L["swa_scale"], step.swa_start[rows], step.swa_len[rows])
+    res = []
+    for fn in (lambda: csa2_sparse_attend_rope(*args, pos, 64, 10000.0, out_b, None, step.ws_attend),
+               lambda: csa2_sparse_attend(*args, out_f, None, step.ws_attend)):
+        fn()
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            with torch.cuda.graph(g, stream=side):
+                for _ in range(calls):
+                    fn()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(); g.replay(); e1.record()
+        torch.cuda.synchronize()
+        res.append(e0.elapsed_time(e1) * 1e3 / calls)
+    return res
+
+
 def cpu_baseline_prefill(wl, step, seconds_target=15.0):
     """The fp64 oracle on a sample of a prefill's queries, spread over the
     causal range: per query, every layer (scores over its visible entries,
@@ -354,6 +393,11 @@ def main():
         "per_call_us_eager": {k: round(v, 2) for k, v in per_call.items()},
         "calls_per_step": calls,
     }
+    rope_us, plain_us = time_attend_rope(step, dev)
+    out["attend_rope"] = {"us_per_call": round(rope_us, 2), "plain_us_per_call": round(plain_us, 2),
+                          "queries": step.chunks[0][1], "rope_dims": 64,
+                          "note": "csa2_sparse_attend_rope (bf16 out) vs csa2_sparse_attend "
+                                  "(fp32 out) on the first layer's inputs; not part of the step"}
     if not wl.prefill:
         out["decode_append"] = {"us_per_call": round(time_append(wl, dev), 2), "batch": wl.B,
                                 "m": wl.m, "swa_window": wl.swa,

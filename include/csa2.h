@@ -65,6 +65,7 @@ typedef enum {
 #define CSA2_MAX_K 2048     /* largest top-k / block count accepted           */
 #define CSA2_MAX_SWA 128    /* largest SWA window per query                   */
 #define CSA2_MAX_COLS (1 << 24) /* largest score row the selectors accept     */
+#define CSA2_MAX_ROPE 64    /* most RoPE channels of csa2_sparse_attend_rope  */
 
 /* Workspace query selectors. */
 #define CSA2_OP_TOPK 1
@@ -279,6 +280,42 @@ csa2_status csa2_sparse_attend(const uint16_t* q, const int32_t* q_seq, int Q, c
                                const float* swa_scale, int64_t T_swa, const int64_t* swa_start,
                                const int32_t* swa_len, float* out, float* lse, void* ws,
                                size_t ws_bytes, void* stream);
+
+/* Rotary position embedding of csa2_sparse_attend_rope (host struct). */
+typedef struct {
+  const int64_t* q_pos;   /* [Q] position of each query (device); may be NULL iff dims == 0 */
+  int dims;               /* rotated channels: the last `dims` of the 512, even, 0..64      */
+  float theta;            /* frequency base, finite and > 1 (e.g. 10000)                    */
+} csa2_rope;
+
+/*
+ * (5b) Fused RoPE - attention - inverse RoPE - cast.
+ *
+ * The report (section 3.2) runs attention as one fused kernel with RoPE,
+ * the attention, a second RoPE and the output cast (FlashMLA's); section
+ * 2.4.4: the cache holds latents quantised after RoPE.  Same rows, masks,
+ * workspace and errors as csa2_sparse_attend, with:
+ *   - pair i of channels (512 - dims + 2i, 512 - dims + 2i + 1) of every
+ *     head of q turned by the angle q_pos[q] * theta^(-2i/dims) before the
+ *     products: (a, b) -> (a cos - b sin, a sin + b cos);
+ *   - the same channels of each head's output turned back by the opposite
+ *     angle after the softmax-weighted sum;
+ *   - out written as bf16 (round to nearest even) of the fp32 result.
+ * Angles are formed and reduced modulo 2 pi in fp64, then used in fp32;
+ * the rotated query enters the fp16 products as two fp16 terms (high and
+ * low) on its last 64 channels, so its logits keep fp32 accuracy.
+ *
+ *   rope   the rotation (host struct)
+ *   out    [Q][64][512] bf16
+ *   lse    [Q][64] fp32 or NULL (unchanged by the rotations)
+ */
+csa2_status csa2_sparse_attend_rope(const uint16_t* q, const int32_t* q_seq, int Q,
+                                    const csa2_cache* src, const int32_t* idx, int k,
+                                    const uint8_t* swa_codes, const float* swa_scale,
+                                    int64_t T_swa, const int64_t* swa_start,
+                                    const int32_t* swa_len, const csa2_rope* rope,
+                                    uint16_t* out, float* lse, void* ws, size_t ws_bytes,
+                                    void* stream);
 
 /*
  * (6) Decode-time append of one token per sequence.

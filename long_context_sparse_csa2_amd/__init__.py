@@ -19,7 +19,8 @@ CSA2_OP_TOPK, CSA2_OP_POOL, CSA2_OP_ATTEND = 1, 2, 3
 STATUS = {0: "CSA2_OK", 1: "CSA2_EINVAL", 2: "CSA2_EUNSUPPORTED", 3: "CSA2_EWORKSPACE", 4: "CSA2_EHIP"}
 EXPORTS = ("csa2_status_string", "csa2_last_error", "csa2_compress_quant", "csa2_index_score",
            "csa2_index_score_fp4q", "csa2_select_topk", "csa2_block_pool", "csa2_sparse_attend",
-           "csa2_decode_append", "csa2_workspace_bytes", "csa2_selftest")
+           "csa2_sparse_attend_rope", "csa2_decode_append", "csa2_workspace_bytes",
+           "csa2_selftest")
 
 
 class Csa2Error(RuntimeError):
@@ -32,6 +33,10 @@ class _Cache(ctypes.Structure):
     _fields_ = [("kv_codes", ctypes.c_void_p), ("kv_scales", ctypes.c_void_p),
                 ("ik_codes", ctypes.c_void_p), ("ik_scales", ctypes.c_void_p),
                 ("cap", ctypes.c_int64)]
+
+
+class _Rope(ctypes.Structure):
+    _fields_ = [("q_pos", ctypes.c_void_p), ("dims", ctypes.c_int), ("theta", ctypes.c_float)]
 
 
 class _State(ctypes.Structure):
@@ -68,6 +73,9 @@ def lib():
         L.csa2_sparse_attend.restype = I
         L.csa2_sparse_attend.argtypes = [P, P, I, ctypes.POINTER(_Cache), P, I, P, P, I64, P, P,
                                          P, P, P, SZ, P]
+        L.csa2_sparse_attend_rope.restype = I
+        L.csa2_sparse_attend_rope.argtypes = [P, P, I, ctypes.POINTER(_Cache), P, I, P, P, I64, P,
+                                              P, ctypes.POINTER(_Rope), P, P, P, SZ, P]
         L.csa2_decode_append.restype = I
         L.csa2_decode_append.argtypes = [P, P, P, I, P, ctypes.POINTER(_Cache),
                                          ctypes.POINTER(_State), P, P, P, P]
@@ -279,3 +287,26 @@ def csa2_decode_append(h_new, z_new, swa_new, w_ik, cache, state, n_vis=None, sw
                                   _ptr(w_ik), ctypes.byref(cs), ctypes.byref(ss), _ptr(n_vis),
                                   _ptr(swa_start), _ptr(swa_len), _stream(stream, h_new))
     _check("csa2_decode_append", st)
+
+
+def csa2_sparse_attend_rope(q, q_seq, cache, idx, swa_codes, swa_scale, swa_start, swa_len,
+                            q_pos, dims, theta, out, lse=None, ws=None, stream=None):
+    """As csa2_sparse_attend, with the query's last `dims` channels turned by
+    q_pos [Q] i64 (theta^(-2i/dims) per pair) before and the output's turned
+    back after; out [Q, 64, 512] bf16."""
+    _dtype(q, torch.bfloat16, "q"); _dtype(q_seq, torch.int32, "q_seq")
+    _dtype(idx, torch.int32, "idx"); _dtype(swa_codes, torch.uint8, "swa_codes")
+    _dtype(swa_scale, torch.float32, "swa_scale"); _dtype(swa_start, torch.int64, "swa_start")
+    _dtype(swa_len, torch.int32, "swa_len"); _dtype(out, torch.bfloat16, "out")
+    _dtype(lse, torch.float32, "lse"); _dtype(q_pos, torch.int64, "q_pos")
+    Q = q.shape[0]
+    k = idx.shape[1] if idx is not None else 0
+    T_swa = swa_codes.shape[1] if swa_codes is not None else 0
+    wsb = ws.numel() * ws.element_size() if ws is not None else 0
+    cs = cache.c_struct()
+    rp = _Rope(q_pos.data_ptr() if q_pos is not None else None, dims, theta)
+    st = lib().csa2_sparse_attend_rope(_ptr(q), _ptr(q_seq), Q, ctypes.byref(cs), _ptr(idx), k,
+                                       _ptr(swa_codes), _ptr(swa_scale), T_swa, _ptr(swa_start),
+                                       _ptr(swa_len), ctypes.byref(rp), _ptr(out), _ptr(lse),
+                                       _ptr(ws), wsb, _stream(stream, q))
+    _check("csa2_sparse_attend_rope", st)

@@ -8,6 +8,7 @@
 #include <cstdarg>
 #include <cstdint>
 #include <cstdio>
+#include <cmath>
 #include <cstdlib>
 #include <cstring>
 
@@ -240,13 +241,13 @@ csa2_status csa2_block_pool(const float* scores, int64_t ld, int Q, const int64_
                     "csa2_block_pool launch");
 }
 
-csa2_status csa2_sparse_attend(const uint16_t* q, const int32_t* q_seq, int Q, const csa2_cache* src,
-                               const int32_t* idx, int k, const uint8_t* swa_codes,
-                               const float* swa_scale, int64_t T_swa, const int64_t* swa_start,
-                               const int32_t* swa_len, float* out, float* lse, void* ws,
-                               size_t ws_bytes, void* stream) {
-  g_err[0] = 0;
-  REQ(q && q_seq && out && swa_start && swa_len,
+static csa2_status attend_common(const uint16_t* q, const int32_t* q_seq, int Q,
+                                 const csa2_cache* src, const int32_t* idx, int k,
+                                 const uint8_t* swa_codes, const float* swa_scale, int64_t T_swa,
+                                 const int64_t* swa_start, const int32_t* swa_len, float* out,
+                                 float* lse, void* ws, size_t ws_bytes,
+                                 const csa2::RopeArgs& rp, void* stream) {
+  REQ(q && q_seq && (out || rp.out_bf16) && swa_start && swa_len,
       "q, q_seq, out, swa_start, swa_len must not be NULL");
   const csa2_status cs = check_cache(src);
   if (cs != CSA2_OK) return cs;
@@ -254,7 +255,8 @@ csa2_status csa2_sparse_attend(const uint16_t* q, const int32_t* q_seq, int Q, c
   REQ(k == 0 || idx, "idx must not be NULL when k > 0");
   REQ(T_swa >= 0, "T_swa must be >= 0");
   REQ(T_swa == 0 || (swa_codes && swa_scale), "swa_codes / swa_scale NULL with T_swa > 0");
-  REQ(al(q, 16) && al(out, 16) && (!swa_codes || al(swa_codes, 16)),
+  REQ(al(q, 16) && (!out || al(out, 16)) && (!rp.out_bf16 || al(rp.out_bf16, 16)) &&
+          (!swa_codes || al(swa_codes, 16)),
       "q, out, swa_codes must be 16-byte aligned");
   REQ(!ws || al(ws, 16), "ws must be 16-byte aligned");
   REQ(Q > 0 && Q <= (1 << 24), "Q=%d must be in [1, 2^24]", Q);
@@ -264,8 +266,42 @@ csa2_status csa2_sparse_attend(const uint16_t* q, const int32_t* q_seq, int Q, c
   }
   return hip_status(csa2::launch_attend(q, q_seq, Q, src->kv_codes, src->kv_scales, src->cap, idx,
                                         k, swa_codes, swa_scale, T_swa, swa_start, swa_len, out,
-                                        lse, ws, ws_bytes, (hipStream_t)stream),
-                    "csa2_sparse_attend launch");
+                                        lse, ws, ws_bytes, rp, (hipStream_t)stream),
+                    rp.out_bf16 ? "csa2_sparse_attend_rope launch" : "csa2_sparse_attend launch");
+}
+
+csa2_status csa2_sparse_attend(const uint16_t* q, const int32_t* q_seq, int Q, const csa2_cache* src,
+                               const int32_t* idx, int k, const uint8_t* swa_codes,
+                               const float* swa_scale, int64_t T_swa, const int64_t* swa_start,
+                               const int32_t* swa_len, float* out, float* lse, void* ws,
+                               size_t ws_bytes, void* stream) {
+  g_err[0] = 0;
+  REQ(out, "out must not be NULL");
+  const csa2::RopeArgs none = {nullptr, 0, 0.f, nullptr, {}};
+  return attend_common(q, q_seq, Q, src, idx, k, swa_codes, swa_scale, T_swa, swa_start, swa_len,
+                       out, lse, ws, ws_bytes, none, stream);
+}
+
+csa2_status csa2_sparse_attend_rope(const uint16_t* q, const int32_t* q_seq, int Q,
+                                    const csa2_cache* src, const int32_t* idx, int k,
+                                    const uint8_t* swa_codes, const float* swa_scale,
+                                    int64_t T_swa, const int64_t* swa_start,
+                                    const int32_t* swa_len, const csa2_rope* rope,
+                                    uint16_t* out, float* lse, void* ws, size_t ws_bytes,
+                                    void* stream) {
+  g_err[0] = 0;
+  REQ(rope && out, "rope and out must not be NULL");
+  REQ(rope->dims >= 0 && rope->dims <= CSA2_MAX_ROPE && rope->dims % 2 == 0,
+      "rope->dims=%d must be even and in [0, %d]", rope->dims, CSA2_MAX_ROPE);
+  REQ(rope->dims == 0 || rope->q_pos, "rope->q_pos must not be NULL when rope->dims > 0");
+  REQ(rope->dims == 0 || (rope->theta > 1.0f && rope->theta < INFINITY),
+      "rope->theta must be finite and > 1");
+  REQ(!rope->q_pos || al(rope->q_pos, 8), "rope->q_pos must be 8-byte aligned");
+  csa2::RopeArgs rp = {rope->q_pos, rope->dims, rope->theta, out, {}};
+  for (int i = 0; i < rope->dims / 2; ++i)
+    rp.freq[i] = std::pow((double)rope->theta, -2.0 * (double)i / (double)rope->dims);
+  return attend_common(q, q_seq, Q, src, idx, k, swa_codes, swa_scale, T_swa, swa_start, swa_len,
+                       nullptr, lse, ws, ws_bytes, rp, stream);
 }
 
 size_t csa2_workspace_bytes(int op, int Q, int64_t n_cols, int k) {

@@ -43,7 +43,7 @@ __global__ __launch_bounds__(256, 1) void k_attend(
     const int32_t* __restrict__ idx, int k, const uint8_t* __restrict__ swa_codes,
     const float* __restrict__ swa_scale, int64_t T_swa, const int64_t* __restrict__ swa_start,
     const int32_t* __restrict__ swa_len, float* __restrict__ out, float* __restrict__ lse,
-    float* __restrict__ part_o, float* __restrict__ part_ml, int nsplit, int cps) {
+    float* __restrict__ part_o, float* __restrict__ part_ml, int nsplit, int cps, RopeArgs rp) {
   __shared__ __align__(16) _Float16 kv[2][CH_ROWS * KV_LD];         // K (+ V of main rows), V of SWA rows
   __shared__ __align__(16) _Float16 qs[AT_HG][D_LAT + AT_PAD];     // fp16 query rows
   __shared__ __align__(16) _Float16 pl[AT_HG][CH_ROWS + AT_PAD];   // P of the chunk
@@ -51,6 +51,8 @@ __global__ __launch_bounds__(256, 1) void k_attend(
   __shared__ int64_t rowoff[CH_ROWS];                               // entry / SWA row, -1 = none
   __shared__ float rowsig[CH_ROWS];
   __shared__ float qinv[AT_HG];                                     // 2^-e of each head
+  __shared__ f32x2_t rcs[ROPE_MAX_PAIRS];                           // RoPE (cos, sin) per pair
+  __shared__ __align__(16) _Float16 qs_lo[AT_HG][ROPE_MAX_DIMS + AT_PAD];  // low fp16 terms, last 64 dims
 
   const int sp = blockIdx.x % nsplit;
   const int hq = blockIdx.x / nsplit;
@@ -97,25 +99,38 @@ __global__ __launch_bounds__(256, 1) void k_attend(
     bf16x8_t x[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) x[i] = qp[i];
-    float mx = 0.f;
+    rope_table<256>(rp, q, rcs);                   // while the query bytes are in flight
+    float xf[32];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j = 0; j < 8; ++j) mx = fmaxf(mx, fabsf((float)x[i][j]));
+      for (int j = 0; j < 8; ++j) xf[8 * i + j] = (float)x[i][j];
+#pragma unroll
+    for (int p2 = 0; p2 < 16; ++p2)
+      rope_pair(xf[2 * p2], xf[2 * p2 + 1], part * 32 + 2 * p2, rp.dims, rcs, 1.f);
+    float mx = 0.f;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) mx = fmaxf(mx, fabsf(xf[i]));
     mx = row16_max(mx);                          // the 16 threads of head hh
     const int e = q_exponent(mx);
     const float f = ldexpf(1.f, e);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      f16x8_t y;
+      f16x8_t y, ylo;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) y[j] = (_Float16)((float)x[i][j] * f);
+      for (int j = 0; j < 8; ++j) {
+        const float v = xf[8 * i + j] * f;
+        y[j] = (_Float16)v;
+        ylo[j] = (_Float16)(v - (float)y[j]);          // exact difference, rounded once
+      }
       *(f16x8_t*)&qs[hh][part * 32 + 8 * i] = y;
+      if (rp.dims > 0 && part >= 14) *(f16x8_t*)&qs_lo[hh][(part - 14) * 32 + 8 * i] = ylo;
     }
     if (part == 0) qinv[hh] = ldexpf(1.f, -e);
   }
 
   f16x8_t a[16];                  // query tile: head r16, dims 32 s + 8 qd .. +7 for step s
+  f16x8_t alo[2];                 // with RoPE: low terms of steps 14 and 15
   f32x4_t o[8];
 #pragma unroll
   for (int t = 0; t < 8; ++t) o[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
@@ -140,6 +155,10 @@ __global__ __launch_bounds__(256, 1) void k_attend(
     if (ch == ch_beg) {
 #pragma unroll
       for (int s = 0; s < 16; ++s) a[s] = *(const f16x8_t*)&qs[r16][32 * s + 8 * qd];
+      if (rp.dims > 0) {
+#pragma unroll
+        for (int s = 0; s < 2; ++s) alo[s] = *(const f16x8_t*)&qs_lo[r16][32 * s + 8 * qd];
+      }
 #pragma unroll
       for (int j = 0; j < 4; ++j) hinv[j] = qinv[4 * qd + j];
     }
@@ -149,6 +168,10 @@ __global__ __launch_bounds__(256, 1) void k_attend(
     f32x4_t sacc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int s = 0; s < 16; ++s) sacc = mfma16_f16(a[s], qk_b(kv[0], lr, s, qd), sacc);
+    if (rp.dims > 0) {                             // the rotated query's low terms
+#pragma unroll
+      for (int s = 0; s < 2; ++s) sacc = mfma16_f16(alo[s], qk_b(kv[0], lr, 14 + s, qd), sacc);
+    }
     const bool valid = rowoff[lr] >= 0;
     const float rs = is_main ? 1.f : rowsig[lr];
 #pragma unroll
@@ -212,9 +235,16 @@ __global__ __launch_bounds__(256, 1) void k_attend(
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const float inv = l_run[j] > 0.f ? 1.f / l_run[j] : 0.f;
-      float* op = out + ((int64_t)q * H_ATT + head0 + j) * D_LAT + wave * 128 + r16;
+      const int64_t row = ((int64_t)q * H_ATT + head0 + j) * D_LAT + wave * 128 + r16;
 #pragma unroll
-      for (int t = 0; t < 8; ++t) op[16 * t] = o[t][j] * inv;
+      for (int t = 0; t < 8; ++t) {
+        float v = o[t][j] * inv;
+        const int d = wave * 128 + 16 * t + r16;
+        if (rp.dims > 0 && wave * 128 + 16 * t + 15 >= D_LAT - rp.dims)   // uniform per wave
+          v = rope_out_lane(v, d, rp.dims, rcs);
+        if (rp.out_bf16) rp.out_bf16[row + 16 * t] = bf16_rne(v);
+        else out[row + 16 * t] = v;
+      }
       if (lse && wave == 0 && r16 == 0)
         lse[(int64_t)q * H_ATT + head0 + j] = l_run[j] > 0.f ? m_run[j] + logf(l_run[j]) : -INFINITY;
     }
@@ -244,11 +274,12 @@ constexpr int AT_MERGE_BATCH = 16;
 __global__ __launch_bounds__(128) void k_attend_combine(const float* __restrict__ part_o,
                                                         const float* __restrict__ part_ml,
                                                         int nsplit, float* __restrict__ out,
-                                                        float* __restrict__ lse) {
+                                                        float* __restrict__ lse, RopeArgs rp) {
   const int qh = blockIdx.x;              // q * 64 + head
   const int q = qh / H_ATT, h = qh % H_ATT;
   const int d0 = threadIdx.x * 4;
   const int64_t slot0 = (int64_t)q * nsplit * H_ATT + h;    // split s: slot0 + s * H_ATT
+  const int64_t pos = rp.dims > 0 ? rp.q_pos[q] : 0;        // in flight with the partials
   float M = -INFINITY, L = 0.f;
   f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
   for (int s0 = 0; s0 < nsplit; s0 += AT_MERGE_BATCH) {
@@ -279,7 +310,26 @@ __global__ __launch_bounds__(128) void k_attend_combine(const float* __restrict_
     M = nM;
   }
   const float inv = L > 0.f ? 1.f / L : 0.f;
-  *(f32x4_t*)(out + (int64_t)qh * D_LAT + d0) = acc * inv;
+  f32x4_t v = acc * inv;
+  if (rp.dims > 0 && d0 + 3 >= D_LAT - rp.dims) {
+#pragma unroll
+    for (int p2 = 0; p2 < 2; ++p2) {
+      const int d = d0 + 2 * p2, base = D_LAT - rp.dims;
+      if (d >= base) {
+        const f32x2_t cs = rope_cs(pos, (d - base) >> 1, rp);
+        const float a = v[2 * p2], b = v[2 * p2 + 1];
+        v[2 * p2] = a * cs[0] + b * cs[1];               // turned back by the query's angle
+        v[2 * p2 + 1] = b * cs[0] - a * cs[1];
+      }
+    }
+  }
+  if (rp.out_bf16) {
+    const uint32_t lo = (uint32_t)bf16_rne(v[0]) | ((uint32_t)bf16_rne(v[1]) << 16);
+    const uint32_t hi = (uint32_t)bf16_rne(v[2]) | ((uint32_t)bf16_rne(v[3]) << 16);
+    *(uint2*)(rp.out_bf16 + (int64_t)qh * D_LAT + d0) = make_uint2(lo, hi);
+  } else {
+    *(f32x4_t*)(out + (int64_t)qh * D_LAT + d0) = v;
+  }
   if (lse && threadIdx.x == 0) lse[qh] = L > 0.f ? M + logf(L) : -INFINITY;
 }
 
@@ -313,11 +363,11 @@ hipError_t launch_attend(const uint16_t* q, const int32_t* q_seq, int Q, const u
                          const uint8_t* kv_scales, int64_t cap, const int32_t* idx, int k,
                          const uint8_t* swa_codes, const float* swa_scale, int64_t T_swa,
                          const int64_t* swa_start, const int32_t* swa_len, float* out, float* lse,
-                         void* ws, size_t ws_bytes, hipStream_t stream) {
+                         void* ws, size_t ws_bytes, const RopeArgs& rp, hipStream_t stream) {
   // many queries (prefill): one workgroup per query over all heads
   if (Q >= AT_WIDE_MIN_Q)
     return launch_attend_wide(q, q_seq, Q, kv_codes, kv_scales, cap, idx, k, swa_codes, swa_scale,
-                              T_swa, swa_start, swa_len, out, lse, stream);
+                              T_swa, swa_start, swa_len, out, lse, rp, stream);
   int nsplit, cps;
   attend_plan(Q, k, nsplit, cps);
   const int nch = (k + CH_ROWS - 1) / CH_ROWS + AT_MAX_SWA / CH_ROWS;
@@ -330,10 +380,10 @@ hipError_t launch_attend(const uint16_t* q, const int32_t* q_seq, int Q, const u
   float* part_ml = nsplit > 1 ? part_o + (size_t)Q * nsplit * H_ATT * D_LAT : nullptr;
   hipLaunchKernelGGL(k_attend, dim3((unsigned)(Q * (H_ATT / AT_HG) * nsplit)), dim3(256), 0,
                      stream, q, q_seq, kv_codes, kv_scales, cap, idx, k, swa_codes, swa_scale,
-                     T_swa, swa_start, swa_len, out, lse, part_o, part_ml, nsplit, cps);
+                     T_swa, swa_start, swa_len, out, lse, part_o, part_ml, nsplit, cps, rp);
   if (nsplit > 1)
     hipLaunchKernelGGL(k_attend_combine, dim3((unsigned)(Q * H_ATT)), dim3(128), 0, stream,
-                       (const float*)part_o, (const float*)part_ml, nsplit, out, lse);
+                       (const float*)part_o, (const float*)part_ml, nsplit, out, lse, rp);
   return hipGetLastError();
 }
 

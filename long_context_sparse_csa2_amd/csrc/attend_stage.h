@@ -20,6 +20,7 @@
 #pragma once
 
 #include "common.h"
+#include "launch.h"
 
 namespace csa2 {
 
@@ -161,6 +162,73 @@ __device__ __forceinline__ int q_exponent(float mx) {
   if (!(mx > 0.f) || !(mx < INFINITY)) return 0;
   int e = 13 - ilogbf(mx);
   return e < -126 ? -126 : (e > 126 ? 126 : e);
+}
+
+// Rotary position embedding around the attention (RopeArgs, launch.h).  The
+// rotated channels are at most the last 64 (the width of the query steps 14
+// and 15, which carry a second, low fp16 term of the rotated query so that
+// the logits keep fp32 accuracy).
+constexpr int ROPE_MAX_DIMS = 64;
+constexpr int ROPE_MAX_PAIRS = ROPE_MAX_DIMS / 2;
+
+static_assert(ROPE_MAX_PAIRS <= 32, "RopeArgs::freq holds 32 pairs");
+
+// cos and sin of pair i's angle at position pos: the angle pos * freq[i] is
+// formed and reduced modulo 2 pi in fp64 (it reaches 10^6 radians at 1M
+// positions), then its cos and sin are taken in fp32.
+__device__ inline f32x2_t rope_cs(int64_t pos, int i, const RopeArgs& rp) {
+  const double two_pi = 6.283185307179586476925;
+  double ang = (double)pos * rp.freq[i];
+  ang -= two_pi * rint(ang * (1.0 / two_pi));
+  float sn, cs;
+  sincosf((float)ang, &sn, &cs);
+  return f32x2_t{cs, sn};
+}
+
+// The table of one query's (cos, sin) per pair, filled by the workgroup's
+// NT threads (with a barrier) when there is a rotation.
+template <int NT>
+__device__ __forceinline__ void rope_table(const RopeArgs& rp, int q, f32x2_t* tab) {
+  if (rp.dims > 0) {                                  // uniform: a kernel argument
+    const int64_t pos = rp.q_pos[q];
+    for (int i = threadIdx.x; i < rp.dims / 2; i += NT) tab[i] = rope_cs(pos, i, rp);
+    __syncthreads();
+  }
+}
+
+// Turn the pair (x[0], x[1]) = channels (d, d + 1), d even, by the table's
+// angle (sign +1) or its opposite (sign -1), if d is a RoPE channel.
+__device__ __forceinline__ void rope_pair(float& a, float& b, int d, int dims, const f32x2_t* tab,
+                                          float sign) {
+  const int base = D_LAT - dims;
+  if (dims > 0 && d >= base) {
+    const f32x2_t cs = tab[(d - base) >> 1];
+    const float sn = sign * cs[1];
+    const float na = a * cs[0] - b * sn, nb = a * sn + b * cs[0];
+    a = na;
+    b = nb;
+  }
+}
+
+// fp32 -> bf16 bits, round to nearest even (finite values).
+__device__ __forceinline__ uint16_t bf16_rne(float v) {
+  const uint32_t u = __float_as_uint(v);
+  return (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
+}
+
+// One output value of channel d held by this lane, whose pair partner
+// (channel d ^ 1) the neighbouring lane (lane ^ 1) holds: turned back by
+// the query's angle when d is a RoPE channel.  Every lane of the wave must
+// call it (it exchanges values).
+__device__ __forceinline__ float rope_out_lane(float v, int d, int dims, const f32x2_t* tab) {
+  const float w = __shfl_xor(v, 1);
+  const int base = D_LAT - dims;
+  if (dims > 0 && d >= base) {
+    const f32x2_t cs = tab[(d - base) >> 1];
+    // inverse turn: (a, b) -> (a cos + b sin, b cos - a sin)
+    v = (d & 1) ? v * cs[0] - w * cs[1] : v * cs[0] + w * cs[1];
+  }
+  return v;
 }
 
 }  // namespace csa2

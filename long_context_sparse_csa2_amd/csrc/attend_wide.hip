@@ -34,13 +34,15 @@ __global__ __launch_bounds__(AW_THREADS, 1) void k_attend_wide(
     const uint8_t* __restrict__ kv_codes, const uint8_t* __restrict__ kv_scales, int64_t cap,
     const int32_t* __restrict__ idx, int k, const uint8_t* __restrict__ swa_codes,
     const float* __restrict__ swa_scale, int64_t T_swa, const int64_t* __restrict__ swa_start,
-    const int32_t* __restrict__ swa_len, float* __restrict__ out, float* __restrict__ lse) {
+    const int32_t* __restrict__ swa_len, float* __restrict__ out, float* __restrict__ lse,
+    RopeArgs rp) {
   __shared__ __align__(16) _Float16 kv[2][CH_ROWS * KV_LD];        // K (+ V of main rows), V of SWA rows
   __shared__ __align__(16) _Float16 pl[H_ATT][CH_ROWS + AW_PAD];  // P of the chunk
   __shared__ int64_t rowoff[CH_ROWS];
   __shared__ float rowsig[CH_ROWS];
   __shared__ float red_m[2][H_ATT];
   __shared__ float red_l[2][H_ATT];
+  __shared__ f32x2_t rcs[ROPE_MAX_PAIRS];                          // RoPE (cos, sin) per pair
 
   const int q = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -79,17 +81,31 @@ __global__ __launch_bounds__(AW_THREADS, 1) void k_attend_wide(
 
   // ---- query tile of head group hg (head 16 hg + r16, dims 32 s + 8 qd .. +7)
   f16x8_t a[16];
+  f16x8_t alo[2];                 // with RoPE: low terms of steps 14 and 15
   float hinv[4];
   {
     const uint16_t* qp = qv + ((int64_t)q * H_ATT + hg * 16 + r16) * D_LAT + 8 * qd;
     bf16x8_t x[16];
 #pragma unroll
     for (int s = 0; s < 16; ++s) x[s] = *(const bf16x8_t*)(qp + 32 * s);
+    rope_table<AW_THREADS>(rp, q, rcs);            // while the query bytes are in flight
+    float xf[16][8];
+#pragma unroll
+    for (int s = 0; s < 16; ++s)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) xf[s][j] = (float)x[s][j];
+    if (rp.dims > 0) {
+#pragma unroll
+      for (int s = 0; s < 16; ++s)
+#pragma unroll
+        for (int p2 = 0; p2 < 4; ++p2)
+          rope_pair(xf[s][2 * p2], xf[s][2 * p2 + 1], 32 * s + 8 * qd + 2 * p2, rp.dims, rcs, 1.f);
+    }
     float mx = 0.f;
 #pragma unroll
     for (int s = 0; s < 16; ++s)
 #pragma unroll
-      for (int j = 0; j < 8; ++j) mx = fmaxf(mx, fabsf((float)x[s][j]));
+      for (int j = 0; j < 8; ++j) mx = fmaxf(mx, fabsf(xf[s][j]));
     mx = fmaxf(mx, __shfl_xor(mx, 16));
     mx = fmaxf(mx, __shfl_xor(mx, 32));
     const int e = q_exponent(mx);
@@ -97,7 +113,13 @@ __global__ __launch_bounds__(AW_THREADS, 1) void k_attend_wide(
 #pragma unroll
     for (int s = 0; s < 16; ++s)
 #pragma unroll
-      for (int j = 0; j < 8; ++j) a[s][j] = (_Float16)((float)x[s][j] * f);
+      for (int j = 0; j < 8; ++j) a[s][j] = (_Float16)(xf[s][j] * f);
+    // the rotated query is no longer exact in fp16: its last 64 dims carry a
+    // second, low fp16 term (the exact fp32 difference, rounded once)
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) alo[s][j] = (_Float16)(xf[14 + s][j] * f - (float)a[14 + s][j]);
 #pragma unroll
     for (int j = 0; j < 4; ++j) hinv[j] = ldexpf(1.f, -__shfl(e, 4 * qd + j));
   }
@@ -147,6 +169,10 @@ __global__ __launch_bounds__(AW_THREADS, 1) void k_attend_wide(
       f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int s = 0; s < 16; ++s) acc = mfma16_f16(a[s], qk_b(kv[0], row, s, qd), acc);
+      if (rp.dims > 0) {
+#pragma unroll
+        for (int s = 0; s < 2; ++s) acc = mfma16_f16(alo[s], qk_b(kv[0], row, 14 + s, qd), acc);
+      }
       const bool valid = rowoff[row] >= 0;
       const float rs = is_main ? 1.f : rowsig[row];
 #pragma unroll
@@ -219,9 +245,16 @@ __global__ __launch_bounds__(AW_THREADS, 1) void k_attend_wide(
     const int hh = hg * 16 + 4 * qd + j;
     const float L = red_l[0][hh] + red_l[1][hh];
     const float inv = L > 0.f ? 1.f / L : 0.f;
-    float* op = out + ((int64_t)q * H_ATT + hh) * D_LAT + half * 256 + r16;
+    const int64_t row = ((int64_t)q * H_ATT + hh) * D_LAT + half * 256 + r16;
 #pragma unroll
-    for (int t = 0; t < 16; ++t) op[16 * t] = o[t][j] * inv;
+    for (int t = 0; t < 16; ++t) {
+      float v = o[t][j] * inv;
+      const int d = half * 256 + 16 * t + r16;
+      if (rp.dims > 0 && half * 256 + 16 * t + 15 >= D_LAT - rp.dims)   // uniform per wave
+        v = rope_out_lane(v, d, rp.dims, rcs);
+      if (rp.out_bf16) rp.out_bf16[row + 16 * t] = bf16_rne(v);
+      else out[row + 16 * t] = v;
+    }
     if (lse && half == 0 && r16 == 0)
       lse[(int64_t)q * H_ATT + hh] = L > 0.f ? m_run[j] + logf(L) : -INFINITY;
   }
@@ -231,10 +264,11 @@ hipError_t launch_attend_wide(const uint16_t* q, const int32_t* q_seq, int Q,
                               const uint8_t* kv_codes, const uint8_t* kv_scales, int64_t cap,
                               const int32_t* idx, int k, const uint8_t* swa_codes,
                               const float* swa_scale, int64_t T_swa, const int64_t* swa_start,
-                              const int32_t* swa_len, float* out, float* lse, hipStream_t stream) {
+                              const int32_t* swa_len, float* out, float* lse, const RopeArgs& rp,
+                              hipStream_t stream) {
   hipLaunchKernelGGL(k_attend_wide, dim3((unsigned)Q), dim3(AW_THREADS), 0, stream, q, q_seq,
                      kv_codes, kv_scales, cap, idx, k, swa_codes, swa_scale, T_swa, swa_start,
-                     swa_len, out, lse);
+                     swa_len, out, lse, rp);
   return hipGetLastError();
 }
 

@@ -7,6 +7,22 @@
 
 namespace csa2 {
 
+// Rotary position embedding around the attention, the fused RoPE -
+// attention - inverse RoPE - cast kernel the report names (section 3.2):
+// with dims > 0 the query's pair i = channels (512 - dims + 2i, +1) turns by
+// q_pos[q] * theta^(-2i / dims) before the products and the output's by the
+// opposite angle after them; out_bf16 != nullptr writes the output as bf16
+// (rounded to nearest even) in place of fp32.  dims = 0 and out_bf16 =
+// nullptr is the plain attention.  freq[i] = theta^(-2i / dims) in fp64,
+// filled on the host.
+struct RopeArgs {
+  const int64_t* q_pos;
+  int dims;
+  float theta;
+  uint16_t* out_bf16;
+  double freq[32];
+};
+
 hipError_t launch_compress_quant(const uint16_t* h, const uint16_t* z, int B, int64_t T, int m,
                                  const uint16_t* w_ik, uint8_t* kv_codes, uint8_t* kv_scales,
                                  uint8_t* ik_codes, uint8_t* ik_scales, int64_t cap, int64_t e0,
@@ -38,13 +54,14 @@ hipError_t launch_attend(const uint16_t* q, const int32_t* q_seq, int Q, const u
                          const uint8_t* kv_scales, int64_t cap, const int32_t* idx, int k,
                          const uint8_t* swa_codes, const float* swa_scale, int64_t T_swa,
                          const int64_t* swa_start, const int32_t* swa_len, float* out, float* lse,
-                         void* ws, size_t ws_bytes, hipStream_t stream);
+                         void* ws, size_t ws_bytes, const RopeArgs& rp, hipStream_t stream);
 
 hipError_t launch_attend_wide(const uint16_t* q, const int32_t* q_seq, int Q,
                               const uint8_t* kv_codes, const uint8_t* kv_scales, int64_t cap,
                               const int32_t* idx, int k, const uint8_t* swa_codes,
                               const float* swa_scale, int64_t T_swa, const int64_t* swa_start,
-                              const int32_t* swa_len, float* out, float* lse, hipStream_t stream);
+                              const int32_t* swa_len, float* out, float* lse, const RopeArgs& rp,
+                              hipStream_t stream);
 
 // Counts the values of a[r][c] (r < rows, c < min(len[r], ncols)) outside
 // [lo, hi) into *bad (host); synchronises the stream.

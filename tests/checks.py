@@ -178,6 +178,26 @@ def check_attention(o_gpu, lse_gpu, q, rows):
     return float(err), float(lerr.max())
 
 
+def check_attention_bf16(o_gpu_bf16, lse_gpu, o_ref, lse_ref, q, rows):
+    """bf16 output of the fused RoPE kernel against the oracle's output
+    before its cast: the fp32 error bound of check_attention, plus the bf16
+    rounding of the fp32 value (8 significant bits: at most 2^-8 of its
+    magnitude)."""
+    o = np.asarray(o_gpu_bf16, np.float64)
+    scale = np.abs(o_ref).max()
+    if scale == 0:
+        assert np.all(o == 0), "non-zero attention output over zero rows"
+        scale = 1.0
+    tol = ATT_TOL * scale * (1 + 2.0 ** -8) + 2.0 ** -8 * np.abs(o_ref)
+    err = np.abs(o - o_ref)
+    assert np.all(err <= tol), f"bf16 attention err {float((err / scale).max()):.3e}"
+    mag = (np.abs(q) @ np.abs(rows).T).max(axis=1)
+    ltol = LSE_ATOL + 32 * 2.0 ** -24 * mag
+    lerr = np.abs(lse_gpu - lse_ref)
+    assert np.all(lerr <= ltol), f"lse err {float(lerr.max()):.3e}"
+    return float((err / scale).max())
+
+
 def swa_rows(swa_codes, swa_scale, start, length):
     """The SWA window as the attention reads it: a ring of T_swa slots."""
     T = len(swa_scale)

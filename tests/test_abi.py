@@ -106,6 +106,28 @@ def test_attend_validation():
     assert L.csa2_sparse_attend(P, P, 1, None, P, 8, P, P, 4, P, P, P, None, None, 0, None) == 1
 
 
+def test_attend_rope_validation():
+    L = C.lib()
+    cs = _cache()
+    P = FAKE
+
+    def call(rope, out=P):
+        r = None if rope is None else ctypes.byref(rope)
+        return L.csa2_sparse_attend_rope(P, P, 1, ctypes.byref(cs), P, 8, P, P, 4, P, P, r, out,
+                                         None, None, 0, None)
+
+    assert call(None) == 1
+    assert call(C._Rope(0x10000, 64, 1e4), out=None) == 1
+    assert call(C._Rope(0x10000, 63, 1e4)) == 1              # odd
+    assert call(C._Rope(0x10000, 66, 1e4)) == 1              # past the last 64 channels
+    assert call(C._Rope(0x10000, -2, 1e4)) == 1
+    assert call(C._Rope(None, 64, 1e4)) == 1                 # positions needed
+    assert call(C._Rope(0x10000, 64, 1.0)) == 1              # base must exceed 1
+    assert call(C._Rope(0x10000, 64, float("inf"))) == 1
+    assert call(C._Rope(0x10004, 64, 1e4)) == 1              # misaligned positions
+    assert b"q_pos" in L.csa2_last_error()
+
+
 def test_decode_append_validation():
     L = C.lib()
     cs = _cache()

@@ -375,6 +375,58 @@ def test_sparse_attend(Q, k):
         checks.check_attention(o[i], l[i], q64[i], rows)
 
 
+def _bf16_bits_to_f64(t):
+    return checks.host(t.view(torch.int16).to(torch.int32) << 16).view(np.float32).astype(np.float64)
+
+
+@pytest.mark.parametrize("Q,dims,split", [(3, 64, True), (1, 64, False), (2, 32, True),
+                                          (300, 64, False), (260, 2, False)])
+def test_sparse_attend_rope(Q, dims, split):
+    """Fused RoPE - attention - inverse RoPE - bf16 cast against the oracle:
+    the decode kernel with its split merge (split) or in one workgroup per
+    head group (no workspace), and the one-workgroup-per-query kernel (Q >=
+    256); positions from 0 to past 2^20 (angles up to 10^6 radians)."""
+    B, N, k = 2, 1500, 200
+    _, _, _, cache = _build(B, N, 1, seed=71 + Q)
+    rng = np.random.default_rng(Q + dims)
+    g = torch.Generator().manual_seed(Q + 1)
+    q = (torch.randn(Q, 64, 512, generator=g) / math.sqrt(512)).to(torch.bfloat16)
+    q_seq = rng.integers(0, B, Q).astype(np.int32)
+    idx = np.stack([rng.choice(N, k, replace=False) for _ in range(Q)]).astype(np.int32)
+    idx[0, ::7] = -1
+    T_swa = 200
+    swa_c, swa_s = _swa(B, T_swa, 11)
+    start = rng.integers(0, T_swa, Q).astype(np.int64)
+    slen = rng.integers(0, 129, Q).astype(np.int32)
+    pos = rng.integers(0, (1 << 20) + 5000, Q).astype(np.int64)
+    pos[0] = 0
+    theta = 10000.0
+    out = torch.empty(Q, 64, 512, dtype=torch.bfloat16, device=DEV)
+    lse = torch.empty(Q, 64, device=DEV)
+    ws = C.workspace(C.CSA2_OP_ATTEND, Q, 0, k, DEV) if split else None
+    args = (q.to(DEV), torch.from_numpy(q_seq).to(DEV), cache, torch.from_numpy(idx).to(DEV),
+            swa_c.to(DEV), swa_s.to(DEV), torch.from_numpy(start).to(DEV),
+            torch.from_numpy(slen).to(DEV))
+    C.csa2_sparse_attend_rope(*args, torch.from_numpy(pos).to(DEV), dims, theta, out, lse, ws)
+    # no rotation: the plain kernel's fp32 output rounded to bf16, bit for bit
+    out0 = torch.empty_like(out)
+    C.csa2_sparse_attend_rope(*args, None, 0, theta, out0, None, ws)
+    plain = torch.empty(Q, 64, 512, device=DEV)
+    C.csa2_sparse_attend(*args, plain, None, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(out0, plain.to(torch.bfloat16))
+    o, l = _bf16_bits_to_f64(out), checks.host(lse)
+    q64 = checks.bf16_to_f64(q)
+    kv_c, kv_s = checks.host(cache.kv_codes), checks.host(cache.kv_scales)
+    sc_np, ss_np = swa_c.numpy(), swa_s.double().numpy()
+    for i in sorted(set(range(min(Q, 12))) | {Q - 1}):
+        b = q_seq[i]
+        wc, ws_ = checks.swa_rows(sc_np[b], ss_np[b], int(start[i]), int(slen[i]))
+        rows = R.gather_rows(kv_c[b], kv_s[b], idx[i], wc, ws_)
+        _, o_ref, lse_ref = R.attend_rope(q64[i], rows, int(pos[i]), dims, theta)
+        checks.check_attention_bf16(o[i], l[i], o_ref, lse_ref, R.rope_rotate(q64[i], int(pos[i]), dims, theta), rows)
+
+
 @pytest.mark.parametrize("Q", [1, 256])
 def test_sparse_attend_no_rows(Q):
     _, _, _, cache = _build(1, 64, 1, seed=2)
