@@ -6,8 +6,12 @@
 // scale per row.
 //
 // The rows of one 64-row chunk are dequantised once to fp16 and written
-// row-major to LDS (row stride KV_LD halves: 1056 bytes, 8 banks apart, so
-// the reads below are conflict-free):
+// row-major to LDS.  The row stride KV_LD is 536 halves = 268 words, 12 banks
+// apart modulo the 64 banks: the 16 rows of a QK^T operand read (16 bytes
+// per lane) land on 16 disjoint 4-bank groups, the 4 rows x 4 column groups
+// of a transposing PV read (8 bytes per lane) on 16 disjoint 2-bank pairs,
+// and the 16 rows of a staging write on 16 disjoint groups.  (A stride 8
+// banks apart put rows r and r + 8 of a QK^T read on the same banks.)
 //   main rows  E2M1 x E4M3 products are exact in fp16 (at most 6 significant
 //              bits, magnitudes in [2^-10, 2688]); they serve as K and V.
 //   SWA rows   the E4M3 values unscaled (exact) serve as K, the row scale
@@ -28,7 +32,7 @@ typedef short i16x4_t __attribute__((ext_vector_type(4)));
 typedef _Float16 f16x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int CH_ROWS = 64;             // rows per chunk
-constexpr int KV_LD = D_LAT + 16;       // fp16 row stride of a staged chunk
+constexpr int KV_LD = D_LAT + 24;       // fp16 row stride of a staged chunk
 
 // One thread's share of a chunk row: NT threads cover 64 rows, NT / 64
 // threads per row, DIMS consecutive dims each.

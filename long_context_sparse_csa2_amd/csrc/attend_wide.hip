@@ -16,7 +16,9 @@
 //            w & 3, row half w >> 2); the query tile sits in registers as
 //            fp16, each head scaled by a power of two (undone on S)
 //   softmax  running max per head shared through LDS; each wave keeps the
-//            sum of its own rows (same reference max), added at the end
+//            sum of its own rows (same reference max), added at the end; the
+//            reference max only moves when a chunk beats it by more than
+//            e^8, so the rescaling of O is skipped in most chunks
 //   O += P V fp16 MFMA 16x16x32; wave w = (head group, 256-dim half); V
 //            columns through transposing LDS reads of the staged rows
 #include "common.h"
@@ -28,6 +30,7 @@ namespace csa2 {
 constexpr int AW_THREADS = 512;
 constexpr int AW_PAD = 8;              // fp16 padding of pl rows
 constexpr int AW_MAX_SWA = 128;        // largest SWA window per query
+constexpr float AW_LAZY = 8.f;         // slack of the softmax reference max (natural log)
 
 __global__ __launch_bounds__(AW_THREADS, 1) void k_attend_wide(
     const uint16_t* __restrict__ qv, const int32_t* __restrict__ q_seq,
@@ -192,10 +195,16 @@ __global__ __launch_bounds__(AW_THREADS, 1) void k_attend_wide(
     }
     __syncthreads();
     float alpha[4];
+    bool moved = false;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int hh = hg * 16 + 4 * qd + j;
-      const float m_new = fmaxf(m_run[j], fmaxf(red_m[0][hh], red_m[1][hh]));
+      // the reference max of a head moves only when a chunk exceeds it by
+      // more than AW_LAZY (P then stays below e^AW_LAZY, far inside fp16), so
+      // O is rescaled only in the few chunks where some max moved
+      const float m_chunk = fmaxf(red_m[0][hh], red_m[1][hh]);
+      const float m_new = m_chunk > m_run[j] + AW_LAZY ? m_chunk : m_run[j];
+      moved |= m_new != m_run[j];
       float psum = 0.f;
       if (m_new == -INFINITY) {
         alpha[j] = 1.f;
@@ -217,10 +226,12 @@ __global__ __launch_bounds__(AW_THREADS, 1) void k_attend_wide(
 
     // ---- O += P V: heads of group hg, dims 256*half .. +255 (16 tiles)
     // (the O rows of this lane are the same heads as its S rows: 16hg + 4qd + j)
+    if (__builtin_amdgcn_ballot_w64(moved) != 0) {        // uniform over the wave
 #pragma unroll
-    for (int t = 0; t < 16; ++t) {
+      for (int t = 0; t < 16; ++t) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) o[t][j] *= alpha[j];
+        for (int j = 0; j < 4; ++j) o[t][j] *= alpha[j];
+      }
     }
     const _Float16* vrows = is_main ? kv[0] : kv[1];
     const f16x8_t pa0 = *(const f16x8_t*)&pl[hg * 16 + r16][qd * 8];
