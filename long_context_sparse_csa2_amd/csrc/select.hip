@@ -99,253 +99,263 @@ __global__ __launch_bounds__(256) void k_maxima(const float* __restrict__ scores
 
 // ------------------------------------------------------------ select
 // One workgroup of NT threads (1024, or 256 for small rounds) per query.
-// The candidates of one round (at most SEL_CAP, in id order) live in
-// registers, thread-major: thread t holds candidates 16t .. 16t + 15 (in the
-// first round 16 consecutive groups, later the 8 children of parents 2t and
-// 2t + 1), so the order-preserving compaction is one block scan of
-// per-thread counts.
+// The candidates of one round (at most 64 * SEL_PER per wave, in id order)
+// live in registers slot-major: slot i of lane l in wave w holds candidate
+// c = 1024 w + 64 i + l, with key 0 for "no candidate" (no fp32 value maps to
+// key 0).  The candidates of one slot across a wave are then consecutive,
+// so an order-preserving compaction is a ballot and a masked bit count per
+// slot, and the only block-wide step is a prefix over per-wave totals.  A
+// round's block-wide bookkeeping (histogram scans) runs in one wave while
+// the others wait at the barrier.
 //
 // Floor.  A round keeps its best kk parents; each kept parent's maximum
 // child has the parent's key, so when the next round wants at most as many
 // as were kept, its answer lies among the children whose key is at least
-// the smallest kept key (the floor) and the children below it are dropped
-// before the threshold search.
-constexpr int SEL_PER = 16;                        // candidates per thread
+// the smallest kept key (the floor), and the children below it are dropped
+// before the threshold search.  The children's keys then lie between the
+// floor and the best parent's key, so that round needs no min / max pass.
+constexpr int SEL_PER = 16;                        // candidate slots per lane
 constexpr int SEL_SMALL = 64;                      // intervals this small are ranked exactly
 constexpr int SEL_BINS = 2048;
 
 template <int NT>
 struct SelShared {
-  uint32_t lists[2][SEL_KK_MAX];      // parent ids of this round / ids it keeps
-  uint32_t hist[SEL_BINS];
+  uint32_t lists[2][SEL_KK_MAX + 64]; // parent ids of this round / ids it keeps (+ 64 spare slots)
+  uint32_t hist[SEL_BINS + 64];        // + one dummy bin per lane for keys outside the interval
   uint32_t small[SEL_SMALL];
-  uint32_t red[2][(NT / 64)];
-  uint32_t mm[2][(NT / 64)];
-  uint32_t cn[2][(NT / 64)];
-  uint32_t bc[4][4];
+  uint32_t wred[3][NT / 64];          // per-wave min, max, count
+  uint32_t wcnt[NT / 64];             // per-wave kept counts (above | ties << 16)
+  uint32_t bc[2][4];                  // histogram pass results, alternating
+  uint32_t sres[3];                   // small interval: threshold, keys above it, keys equal
+  uint32_t gather;                    // small-interval gather counter
 };
 
-// Inclusive block-wide sum; `total` gets the block total.  red must not be
-// reused by the caller until after the next barrier.
-template <int NT>
-__device__ __forceinline__ uint32_t block_scan(uint32_t v, uint32_t* red, uint32_t& total) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const uint32_t incl = wave_incl_sum(v);
-  if (lane == 63) red[wave] = incl;
-  __syncthreads();
-  uint32_t pre = 0, tot = 0;
+// Number of set bits of m below this lane.
+__device__ __forceinline__ uint32_t lanes_below(uint64_t m) {
+  return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+}
+
+// Wave 0's scan of the histogram, from the top bin down: lane l sums bins
+// [SEL_BINS - 32 (l + 1), SEL_BINS - 32 l) in groups of 4, the lane whose
+// range holds the krem-th best key finds its group and re-reads it to find
+// the bin, and every lane then zeroes its bins.  out = (bin, keys above it,
+// keys in it, total).
+__device__ __forceinline__ void hist_scan(uint32_t* hist, uint32_t krem, uint32_t* out) {
+  const int lane = threadIdx.x & 63;
+  const int base = SEL_BINS - 32 * (lane + 1);
+  uint32_t g[8], s = 0;
 #pragma unroll
-  for (int w = 0; w < (NT / 64); ++w) {
-    const uint32_t x = red[w];
-    pre += w < wave ? x : 0u;
-    tot += x;
+  for (int v = 0; v < 8; ++v) {
+    const u32x4_t x = *(const u32x4_t*)&hist[base + 4 * v];
+    g[v] = x[0] + x[1] + x[2] + x[3];
+    s += g[v];
   }
-  total = tot;
-  return incl + pre;
-}
-
-// Bit i set iff candidate i is considered and its key lies in [lo, hi].
-template <int PER>
-__device__ __forceinline__ uint32_t range_mask(const uint32_t (&kr)[PER], uint32_t cmask,
-                                               uint32_t lo, uint32_t hi) {
-  uint32_t m = 0;
+  const uint32_t incl = wave_incl_sum(s);
+  const uint32_t excl = incl - s;
+  if (lane == 63) out[3] = incl;
+  if (excl < krem && incl >= krem) {
+    uint32_t acc = excl, gv = 0, gacc = 0;
 #pragma unroll
-  for (int i = 0; i < PER; ++i) m |= (kr[i] >= lo && kr[i] <= hi) ? (1u << i) : 0u;
-  return m & cmask;
-}
-
-// Threshold of the best kk of the m considered candidates (m > kk >= 1),
-// given their min and max keys; cmask = this thread's considered ones.
-//
-// Search on the key interval [lo, hi] that holds the kk-th best key: each
-// pass bins the keys inside it by (key - lo) >> s, with s chosen so that at
-// most 2048 bins cover the interval, keeps the bin holding the krem-th best
-// key and shrinks the interval to it.  Once the interval holds at most
-// SEL_SMALL candidates their exact kk-th key is found by ranking them
-// against each other.  Result: keys above hi are in, keys inside [lo, hi]
-// are in for the first `tie_lim` of them in candidate (= id) order, keys
-// below lo are out.  The histogram must be zero on entry and is left zero;
-// so is the gather counter sh.bc[3][3].
-template <int NT, int PER>
-__device__ __forceinline__ void threshold_search(const uint32_t (&kr)[PER], uint32_t cmask,
-                                                 int m, int kk, uint32_t mn, uint32_t mx,
-                                                 SelShared<NT>& sh, uint32_t& lo_out,
-                                                 uint32_t& hi_out, uint32_t& tie_out) {
-  const int tid = threadIdx.x, lane = tid & 63;
-  uint32_t lo = mn, hi = mx;
-  uint32_t krem = (uint32_t)kk;
-  uint32_t incnt = (uint32_t)m;            // considered candidates with key in [lo, hi]
-  uint32_t tie_lim;
-  int pass = 0;
-  while (true) {
-    if (lo == hi) { tie_lim = krem; break; }
-    const uint32_t imask = range_mask<PER>(kr, cmask, lo, hi);
-    if (incnt <= (uint32_t)SEL_SMALL) {
-      // gather the interval's keys: wave prefix of per-thread counts, one
-      // LDS atomic per wave for the wave's base
-      const uint32_t c = (uint32_t)__popc(imask);
-      const uint32_t incl = wave_incl_sum(c);
-      uint32_t base = 0;
-      if (lane == 63) base = atomicAdd(&sh.bc[3][3], incl);
-      base = (uint32_t)__builtin_amdgcn_readlane((int)base, 63);
-      uint32_t pos = base + incl - c;
-#pragma unroll
-      for (int i = 0; i < PER; ++i)
-        if ((imask >> i) & 1u) sh.small[pos++] = kr[i];
-      __syncthreads();
-      // rank each gathered key against all of them, RS threads per key
-      constexpr int RS = NT / SEL_SMALL;
-      const int ci = tid / RS, part = tid % RS;
-      const uint32_t mine = ci < (int)incnt ? sh.small[ci] : 0u;
-      uint32_t gt = 0, ge = 0;
-      for (uint32_t j = part; j < incnt; j += RS) {
-        const uint32_t o = sh.small[j];
-        gt += o > mine;
-        ge += o >= mine;
-      }
-#pragma unroll
-      for (int off = 1; off < RS; off <<= 1) { gt += __shfl_xor(gt, off); ge += __shfl_xor(ge, off); }
-      if (part == 0 && ci < (int)incnt && gt < krem && ge >= krem) { sh.bc[2][0] = mine; sh.bc[2][1] = gt; }
-      __syncthreads();
-      const uint32_t t = sh.bc[2][0], g = sh.bc[2][1];
-      if (tid == 0) sh.bc[3][3] = 0u;     // gather counter; next used after further barriers
-      lo = hi = t;
-      tie_lim = krem - g;
-      break;
+    for (int v = 7; v >= 0; --v) {
+      if (acc < krem && acc + g[v] >= krem) { gv = (uint32_t)v; gacc = acc; }
+      acc += g[v];
     }
-    const uint32_t span = hi - lo;                                   // range - 1
-    const int bits = 32 - __clz(span);
-    const int shf = bits > 11 ? bits - 11 : 0;
+    const u32x4_t bb = *(const u32x4_t*)&hist[base + 4 * gv];
+    acc = gacc;
+    uint32_t bin = 0, above = 0, inbin = 0;
 #pragma unroll
-    for (int i = 0; i < PER; ++i)
-      if ((imask >> i) & 1u) atomicAdd(&sh.hist[(kr[i] - lo) >> shf], 1u);
-    __syncthreads();
-    // thread t owns (SEL_BINS / NT) consecutive bins from the top, counted downwards
-    uint32_t hb[(SEL_BINS / NT)];
-    uint32_t v = 0;
-#pragma unroll
-    for (int j = 0; j < (SEL_BINS / NT); ++j) {
-      hb[j] = sh.hist[SEL_BINS - 1 - (SEL_BINS / NT) * tid - j];
-      sh.hist[SEL_BINS - 1 - (SEL_BINS / NT) * tid - j] = 0u;                  // leave it zero
-      v += hb[j];
+    for (int j = 3; j >= 0; --j) {
+      if (acc < krem && acc + bb[j] >= krem) { bin = 4 * gv + (uint32_t)j; above = acc; inbin = bb[j]; }
+      acc += bb[j];
     }
-    uint32_t tot;
-    const uint32_t incl = block_scan<NT>(v, sh.red[pass & 1], tot);
-    uint32_t* bcp = sh.bc[pass & 1];
-    if (incl - v < krem && incl >= krem) {
-      uint32_t acc = incl - v;
-#pragma unroll
-      for (int j = 0; j < (SEL_BINS / NT); ++j) {
-        if (acc < krem && acc + hb[j] >= krem) {
-          bcp[0] = (uint32_t)(SEL_BINS - 1 - (SEL_BINS / NT) * tid - j);
-          bcp[1] = acc;
-          bcp[2] = hb[j];
-        }
-        acc += hb[j];
-      }
-    }
-    __syncthreads();
-    const uint32_t d = bcp[0], above = bcp[1], inbin = bcp[2];
-    ++pass;
-    krem -= above;
-    const uint32_t nlo = lo + (d << shf);
-    const uint32_t top = (d << shf) + ((1u << shf) - 1u);
-    const uint32_t nhi = top >= span ? hi : lo + top;
-    lo = nlo;
-    hi = nhi;
-    incnt = inbin;
-    if (inbin == krem) { tie_lim = krem; break; }                    // the whole bin is in
+    out[0] = (uint32_t)base + bin;
+    out[1] = above;
+    out[2] = inbin;
   }
-  lo_out = lo;
-  hi_out = hi;
-  tie_out = tie_lim;
+#pragma unroll
+  for (int v = 0; v < 8; ++v) *(u32x4_t*)&hist[base + 4 * v] = u32x4_t{0u, 0u, 0u, 0u};
 }
 
-// One keep-best-`want` round over the candidates this thread holds in
-// kr[0 .. nv) (thread-major: ids increase with the thread, then the slot):
-// candidates below floor_key are dropped, the threshold of the rest found
-// and the kept ids written in id order to `keep` (id_of(i) is slot i's id).
-// rb picks the reduction buffers (alternate it between rounds).  Ends with a
-// barrier; returns the kept count, the threshold interval's low end and the
-// smallest considered key (the next round's floor), and whether every
-// considered candidate was kept.
+// One keep-best-`want` round over the candidates in kr (slot-major, key 0 =
+// none).  known: every candidate's key lies in [kmn, kmx] (kmn >= 1) and the
+// min / max / count pass is skipped.  The kept ids go to `keep` in id order
+// (id_of(i) is slot i's id).  Ends with a barrier; returns the kept count,
+// the low end of the threshold interval, bounds of the considered keys, and
+// whether every considered candidate was kept.
 struct RoundOut {
   int kept;
-  uint32_t lo, mn;
+  uint32_t lo, mn, mx;
   bool all;
 };
 
-template <int NT, int PER, typename IdOf>
-__device__ __forceinline__ RoundOut select_round(const uint32_t (&kr)[PER], int nv, uint32_t floor_key,
-                                                 int want, SelShared<NT>& sh, int rb, uint32_t* keep,
-                                                 IdOf id_of) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  uint32_t cmask = 0, mn = 0xFFFFFFFFu, mx = 0u;
+template <int NT, typename IdOf>
+__device__ __forceinline__ RoundOut select_round(const uint32_t (&kr)[SEL_PER], bool known,
+                                                 uint32_t kmn, uint32_t kmx, int want,
+                                                 SelShared<NT>& sh, uint32_t* keep, IdOf id_of) {
+  constexpr int NW = NT / 64;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  uint32_t mn = kmn, mx = kmx;
+  uint32_t m = 0xFFFFFFFFu;                       // considered count (unknown when known)
+  if (!known) {
+    uint32_t mnm1 = 0xFFFFFFFFu, mxx = 0u, cnt = 0u;
 #pragma unroll
-  for (int i = 0; i < PER; ++i) {
-    const bool c = i < nv && kr[i] >= floor_key;
-    cmask |= c ? (1u << i) : 0u;
-    mn = c ? min(mn, kr[i]) : mn;
-    mx = c ? max(mx, kr[i]) : mx;
+    for (int i = 0; i < SEL_PER; ++i) {
+      mnm1 = min(mnm1, kr[i] - 1u);               // key 0 wraps to the top
+      mxx = max(mxx, kr[i]);
+      cnt += kr[i] != 0u ? 1u : 0u;
+    }
+    mnm1 = wave_min_all(mnm1);
+    mxx = wave_max_all(mxx);
+    cnt = (uint32_t)__builtin_amdgcn_readlane((int)wave_incl_sum(cnt), 63);
+    if (lane == 0) { sh.wred[0][wave] = mnm1; sh.wred[1][wave] = mxx; sh.wred[2][wave] = cnt; }
+    __syncthreads();
+    uint32_t a = 0xFFFFFFFFu, b = 0u, c = 0u;
+    if (lane < NW) { a = sh.wred[0][lane]; b = sh.wred[1][lane]; c = sh.wred[2][lane]; }
+    mn = wave_min_all(a) + 1u;
+    mx = wave_max_all(b);
+    m = (uint32_t)__builtin_amdgcn_readlane((int)wave_incl_sum(c), 63);
   }
-  mn = wave_min_all(mn);
-  mx = wave_max_all(mx);
-  const uint32_t wc = (uint32_t)__builtin_amdgcn_readlane((int)wave_incl_sum((uint32_t)__popc(cmask)), 63);
-  if (lane == 0) { sh.red[rb][wave] = mn; sh.mm[rb][wave] = mx; sh.cn[rb][wave] = wc; }
-  __syncthreads();
-  int m = 0;
-#pragma unroll
-  for (int w = 0; w < (NT / 64); ++w) {
-    mn = min(mn, sh.red[rb][w]);
-    mx = max(mx, sh.mm[rb][w]);
-    m += (int)sh.cn[rb][w];
-  }
-  uint32_t lo = 0, hi = 0, tl = 0;
-  const bool all = m <= want;
-  if (!all) threshold_search<NT, PER>(kr, cmask, m, want, mn, mx, sh, lo, hi, tl);
-  uint32_t gm = cmask, tm = 0;
+  bool all = m <= (uint32_t)want;
+  uint32_t lo = mn, hi = mx, tl = 0;
+  bool ties_all = true;                 // every key in [lo, hi] is kept
   if (!all) {
-    gm = hi == 0xFFFFFFFFu ? 0u : range_mask<PER>(kr, cmask, hi + 1u, 0xFFFFFFFFu);
-    tm = range_mask<PER>(kr, cmask, lo, hi);
-  }
-  const uint32_t ngt = (uint32_t)__popc(gm), ntie = (uint32_t)__popc(tm);
-  const uint32_t packed = ngt | (ntie << 16);           // both sums stay below 2^16
-  uint32_t tot;
-  const uint32_t excl = block_scan<NT>(packed, sh.red[rb ^ 1], tot) - packed;
-  const uint32_t gt_before = excl & 0xFFFFu, tie_before = excl >> 16;
-  // this thread's ties in id order while the tie limit lasts
-  uint32_t take = tl > tie_before ? tl - tie_before : 0u;
-  uint32_t tk = 0, trest = tm;
-  while (take > 0 && trest != 0) {
-    tk |= trest & (0u - trest);
-    trest &= trest - 1u;
-    --take;
-  }
-  const uint32_t km = gm | tk;
-  uint32_t pos = gt_before + min(tie_before, tl);
+    uint32_t krem = (uint32_t)want;
+    uint32_t incnt = m;                           // candidates with key in [lo, hi]
+    int pass = 0;
+    while (true) {
+      if (lo == hi) { tl = krem; ties_all = incnt == krem; break; }
+      const uint32_t span = hi - lo;
+      if (incnt <= (uint32_t)SEL_SMALL) {
+        // gather the interval's keys (any order); a slot holding some takes
+        // its place with one LDS atomic
 #pragma unroll
-  for (int i = 0; i < PER; ++i)
-    if ((km >> i) & 1u) keep[pos++] = id_of(i);
-  const int kept = all ? m : (int)((tot & 0xFFFFu) + min(tot >> 16, tl));
-  __syncthreads();
-  return RoundOut{kept, lo, mn, all};
-}
-
-// Raw words of 8 consecutive entries b .. b+7 of a level array or a score
-// row into raw[off .. off + 8).  vec: the 8 words lie inside the row and
-// start 16-byte aligned (two vector loads); otherwise word j is read at
-// min(b + j, len - 1) and the caller masks the ones at or past len.
-__device__ __forceinline__ void load_run8(const uint32_t* src, int64_t b, int64_t len, bool vec,
-                                          uint32_t (&raw)[SEL_PER], int off) {
-  if (vec) {
-    const u32x4_t x0 = *(const u32x4_t*)(src + b);
-    const u32x4_t x1 = *(const u32x4_t*)(src + b + 4);
+        for (int i = 0; i < SEL_PER; ++i) {
+          const bool in = kr[i] - lo <= span;
+          const uint64_t mk = __ballot(in);
+          if (mk) {
+            uint32_t base = 0;
+            if (lane == 0) base = atomicAdd(&sh.gather, (uint32_t)__popcll(mk));
+            base = (uint32_t)__builtin_amdgcn_readlane((int)base, 0);
+            if (in) sh.small[base + lanes_below(mk)] = kr[i];
+          }
+        }
+        __syncthreads();
+        // rank each gathered key against all of them, RS threads per key
+        constexpr int RS = NT / SEL_SMALL;
+        const int ci = tid / RS, part = tid % RS;
+        const uint32_t mine = ci < (int)incnt ? sh.small[ci] : 0u;
+        uint32_t gt = 0, ge = 0;
+        for (uint32_t j = part; j < incnt; j += RS) {
+          const uint32_t o = sh.small[j];
+          gt += o > mine;
+          ge += o >= mine;
+        }
 #pragma unroll
-    for (int j = 0; j < 4; ++j) { raw[off + j] = x0[j]; raw[off + 4 + j] = x1[j]; }
+        for (int off = 1; off < RS; off <<= 1) { gt += __shfl_xor(gt, off); ge += __shfl_xor(ge, off); }
+        if (part == 0 && ci < (int)incnt && gt < krem && ge >= krem) {
+          sh.sres[0] = mine;
+          sh.sres[1] = gt;
+          sh.sres[2] = ge - gt;
+        }
+        __syncthreads();
+        const uint32_t t = sh.sres[0], g = sh.sres[1], eq = sh.sres[2];
+        if (tid == 0) sh.gather = 0u;             // next used after further barriers
+        lo = hi = t;
+        tl = krem - g;
+        ties_all = eq == tl;
+        break;
+      }
+      const int bits = 32 - __clz(span);
+      const int shf = bits > 11 ? bits - 11 : 0;
+      if (pass == 0) {
+        // every candidate lies in [lo, hi]; key 0 (none) goes to the lane's
+        // own dummy bin (one shared dummy would serialise the atomics)
+#pragma unroll
+        for (int i = 0; i < SEL_PER; ++i) {
+          const uint32_t d = kr[i] - lo;
+          atomicAdd(&sh.hist[d <= span ? d >> shf : (uint32_t)(SEL_BINS + lane)], 1u);
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < SEL_PER; ++i) {
+          const uint32_t d = kr[i] - lo;
+          if (d <= span) atomicAdd(&sh.hist[d >> shf], 1u);
+        }
+      }
+      __syncthreads();
+      uint32_t* bcp = sh.bc[pass & 1];
+      if (wave == 0) hist_scan(sh.hist, krem, bcp);
+      __syncthreads();
+      const uint32_t total = bcp[3];
+      ++pass;
+      if (total <= krem) { all = true; break; }   // first pass of a known round: all fit
+      const uint32_t d = bcp[0], above = bcp[1], inbin = bcp[2];
+      krem -= above;
+      const uint32_t nlo = lo + (d << shf);
+      const uint32_t top = (d << shf) + ((1u << shf) - 1u);
+      const uint32_t nhi = top >= span ? hi : lo + top;
+      lo = nlo;
+      hi = nhi;
+      incnt = inbin;
+      if (inbin == krem) { tl = krem; break; }    // the whole bin is in (ties_all)
+    }
+  }
+  // ---- order-preserving compaction.  Usually every key in [lo, hi] is in
+  // (the whole bin, or no tie straddles the k-th key) and the kept keys are
+  // those >= lo; otherwise the keys above hi and the first tl keys inside
+  // [lo, hi] in id order.
+  const uint32_t span = hi - lo;
+  const bool fast = all || ties_all;
+  uint32_t ngt = 0, ntie = 0;
+  if (fast) {
+#pragma unroll
+    for (int i = 0; i < SEL_PER; ++i) ngt += (uint32_t)__popcll(__ballot(kr[i] >= lo));
   } else {
 #pragma unroll
-    for (int j = 0; j < 8; ++j) raw[off + j] = src[b + j < len ? b + j : len - 1];
+    for (int i = 0; i < SEL_PER; ++i) {
+      ngt += (uint32_t)__popcll(__ballot(kr[i] > hi));
+      ntie += (uint32_t)__popcll(__ballot(kr[i] - lo <= span));
+    }
   }
+  if (lane == 0) sh.wcnt[wave] = ngt | (ntie << 16);    // both stay below 2^16
+  __syncthreads();
+  const uint32_t incl = wave_incl_sum(lane < NW ? sh.wcnt[lane] : 0u);
+  const uint32_t tot = (uint32_t)__builtin_amdgcn_readlane((int)incl, 63);
+  const uint32_t before = wave > 0 ? (uint32_t)__builtin_amdgcn_readlane((int)incl, wave - 1) : 0u;
+  const uint32_t gt_before = before & 0xFFFFu, tie_before = before >> 16;
+  if (fast) {
+    uint32_t pos = gt_before;
+#pragma unroll
+    for (int i = 0; i < SEL_PER; ++i) {
+      const bool in = kr[i] >= lo;                  // lo >= 1: key 0 is never in
+      const uint64_t km = __ballot(in);
+      const uint32_t at = in ? pos + lanes_below(km) : (uint32_t)(SEL_KK_MAX + lane);  // spare
+      keep[at] = id_of(i);
+      pos += (uint32_t)__popcll(km);
+    }
+  } else {
+    uint32_t take = tl > tie_before ? tl - tie_before : 0u;
+    uint32_t pos = gt_before + min(tie_before, tl);
+#pragma unroll
+    for (int i = 0; i < SEL_PER; ++i) {
+      const bool tie = kr[i] - lo <= span;
+      const uint64_t tm = __ballot(tie);
+      const uint32_t nt = (uint32_t)__popcll(tm);
+      bool tk = tie;
+      if (nt > take) tk = tie && lanes_below(tm) < take;
+      take = nt > take ? 0u : take - nt;
+      const bool in = kr[i] > hi || tk;
+      const uint64_t km = __ballot(in);
+      if (km) {
+        if (in) keep[pos + lanes_below(km)] = id_of(i);
+        pos += (uint32_t)__popcll(km);
+      }
+    }
+  }
+  const int kept = fast ? (int)(tot & 0xFFFFu) : (int)((tot & 0xFFFFu) + min(tot >> 16, tl));
+  __syncthreads();
+  return RoundOut{kept, lo, mn, mx, all};
 }
 
 template <int NT>
@@ -353,17 +363,42 @@ __global__ __launch_bounds__(NT) void k_select(
     const float* __restrict__ scores, int64_t ld, const int64_t* __restrict__ n_valid,
     const int32_t* __restrict__ col_ids, int64_t n_cols, LevelDesc d,
     const uint32_t* __restrict__ ws, int kk, int mode, int32_t* __restrict__ out, int64_t out_ld,
-    int64_t* __restrict__ out_len, int k2, int32_t* __restrict__ out2, int vec0) {
+    int64_t* __restrict__ out_len, int k2, int32_t* __restrict__ out2) {
   __shared__ SelShared<NT> sh;
   const int q = blockIdx.x;
-  const int tid = threadIdx.x;
-  const int64_t n0 = n_valid[q];
-  const int64_t n = n0 < 0 ? 0 : (n0 < n_cols ? n0 : n_cols);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const float* srow = scores + (int64_t)q * ld;
   int32_t* orow = out + (int64_t)q * out_ld;
   const int stop = mode;
   const int64_t out_w = mode == 0 ? kk : (int64_t)kk * 8;
+  const int cap = NT * SEL_PER;
+  const int cbase = 64 * SEL_PER * wave + lane;          // candidate of slot 0
 
+  // first round's level as n_cols gives it; its loads go out before n_valid
+  // arrives (every index is clamped into the level's row)
+  auto level_of = [&](int64_t n) {
+    int l = 0;
+    while (groups_at(n, l) > (int64_t)cap) ++l;
+    return l < stop ? stop : l;
+  };
+  auto src_of = [&](int l) {
+    return l == 0 ? (const uint32_t*)srow : ws + d.off[l] + (int64_t)q * d.stride[l];
+  };
+  int lvl = level_of(n_cols);
+  uint32_t kr[SEL_PER];
+  auto load_first = [&](int l) {
+    const uint32_t* src = src_of(l);
+    const int64_t len64 = groups_at(n_cols, l);
+    const int last = (int)(len64 < cap ? len64 : cap) - 1;
+#pragma unroll
+    for (int i = 0; i < SEL_PER; ++i) {
+      const int c = cbase + 64 * i;
+      kr[i] = src[c < last ? c : last];
+    }
+  };
+  if (n_cols > 0) load_first(lvl);
+  const int64_t n0 = n_valid[q];
+  const int64_t n = n0 < 0 ? 0 : (n0 < n_cols ? n0 : n_cols);
   if (n == 0) {
     for (int64_t i = tid; i < out_w; i += NT) orow[i] = -1;
     if (mode == 1) {
@@ -372,66 +407,65 @@ __global__ __launch_bounds__(NT) void k_select(
     }
     return;
   }
+  {
+    const int ln = level_of(n);
+    if (ln != lvl) { lvl = ln; load_first(lvl); }
+  }
 #pragma unroll
   for (int j = 0; j < (SEL_BINS / NT); ++j) sh.hist[(SEL_BINS / NT) * tid + j] = 0u;
-  if (tid == 0) sh.bc[3][3] = 0u;
+  if (tid == 0) sh.gather = 0u;
 
   int cur = 0;                      // sh.lists[cur]: parents of the round being loaded
-  int lvl = 0;
-  while (groups_at(n, lvl) > (int64_t)NT * SEL_PER) ++lvl;
-  if (lvl < stop) lvl = stop;
   bool first = true;
   int pcnt = 0;
-  int rb = 0;                       // alternates the reduction buffers between rounds
   uint32_t floor_key = 0;           // children below it cannot be in this round's answer
+  uint32_t top_key = 0;             // the best key of the previous round
+  uint32_t pid[SEL_PER];            // child rounds: parent id of each slot
 
   while (true) {
-    // ---- candidates of level lvl (thread t: 16t .. 16t+15), every load in flight at once
-    const uint32_t* par = sh.lists[cur];
-    const int64_t gl = groups_at(n, lvl);
-    int cnt;
-    if (first) {
-      cnt = (int)gl;
-    } else {
-      const int64_t rem = gl - 8 * (int64_t)par[pcnt - 1];
-      cnt = 8 * (pcnt - 1) + (rem < 8 ? (int)rem : 8);
-    }
-    const int e0 = SEL_PER * tid;
-    const int nv = cnt - e0 < 0 ? 0 : (cnt - e0 > SEL_PER ? SEL_PER : cnt - e0);
+    const int gl = (int)groups_at(n, lvl);            // n <= 2^26 fits
     const bool is_score = lvl == 0;
-    const uint32_t* src = is_score ? (const uint32_t*)srow
-                                   : ws + d.off[lvl] + (int64_t)q * d.stride[lvl];
-    const bool vok = !is_score || vec0;              // level rows are padded to 16 words
-    uint32_t kr[SEL_PER];
+    if (first) {
 #pragma unroll
-    for (int i = 0; i < SEL_PER; ++i) kr[i] = 0u;
-    uint32_t p0 = 0, p1 = 0;
-    if (nv > 0) {
-      int64_t b0 = e0, b1 = e0 + 8;
-      if (!first) {
-        // candidates 16t .. 16t+15 are the children of parents 2t and 2t+1
-        p0 = par[e0 >> 3];
-        p1 = nv > 8 ? par[(e0 >> 3) + 1] : p0;
-        b0 = (int64_t)p0 * 8;
-        b1 = (int64_t)p1 * 8;
+      for (int i = 0; i < SEL_PER; ++i) {
+        const uint32_t k = is_score ? f32_key(__uint_as_float(kr[i])) : kr[i];
+        kr[i] = cbase + 64 * i < gl ? k : 0u;
       }
-      load_run8(src, b0, gl, vok, kr, 0);
-      load_run8(src, b1, gl, vok, kr, 8);
-      if (is_score) {
+    } else {
+      // slot i of this lane: child (lane & 7) of parent (c >> 3) in the kept
+      // list; pid = ~0 marks a slot without a child
+      const uint32_t* par = sh.lists[cur];
+      const uint32_t* src = src_of(lvl);
 #pragma unroll
-        for (int i = 0; i < SEL_PER; ++i) kr[i] = f32_key(__uint_as_float(kr[i]));
+      for (int i = 0; i < SEL_PER; ++i) {
+        const int p = (cbase + 64 * i) >> 3;
+        const uint32_t pp = p < pcnt ? par[p] : 0xFFFFFFFFu;
+        const uint32_t cid = pp * 8u + (uint32_t)(lane & 7);
+        const bool ok = pp != 0xFFFFFFFFu && cid < (uint32_t)gl;
+        pid[i] = ok ? pp : 0xFFFFFFFFu;
+        kr[i] = src[ok ? cid : 0u];
+      }
+      // all 16 gathers in flight before the first use (left to itself the
+      // compiler sinks each load to its use and serialises their latencies)
+      __builtin_amdgcn_s_waitcnt(0);
+#pragma unroll
+      for (int i = 0; i < SEL_PER; ++i) {
+        const uint32_t k = is_score ? f32_key(__uint_as_float(kr[i])) : kr[i];
+        kr[i] = pid[i] != 0xFFFFFFFFu && k >= floor_key ? k : 0u;
       }
     }
     const int want = (lvl == 0 && mode == 1) ? k2 : kk;
-    const RoundOut ro = select_round<NT, SEL_PER>(
-        kr, nv, floor_key, want, sh, rb, sh.lists[cur ^ 1], [&](int i) __attribute__((always_inline)) {
-          return first ? (uint32_t)(e0 + i) : (i < 8 ? p0 : p1) * 8u + (uint32_t)(i & 7);
+    const bool fr = first;
+    const RoundOut ro = select_round<NT>(
+        kr, !first, floor_key > 0u ? floor_key : 1u, top_key, want, sh, sh.lists[cur ^ 1],
+        [&](int i) __attribute__((always_inline)) {
+          return fr ? (uint32_t)(cbase + 64 * i) : pid[i] * 8u + (uint32_t)(lane & 7);
         });
     const int kept = ro.kept;
     cur ^= 1;
-    rb ^= 1;
     first = false;
     pcnt = kept;
+    top_key = ro.mx;
     const uint32_t* sel = sh.lists[cur];
     const bool map_cols = lvl == stop && mode == 0 && col_ids;
 
@@ -500,7 +534,6 @@ hipError_t launch_select(const float* scores, int64_t ld, int Q, const int64_t* 
   const int64_t nchunk = (n_cols + 4095) / 4096;
   const bool al16 = ((uintptr_t)scores & 15) == 0;
   const int vec_max = (ld % 4 == 0) && al16;    // 16-byte row starts
-  const int vec = (ld % 16 == 0) && al16;       // every run of 8 / 16 scores inside its row
   if (d.nlev > 0 && nchunk > 0) {
     hipLaunchKernelGGL(k_maxima, dim3((unsigned)(nchunk * Q)), dim3(256), 0, stream, scores, ld,
                        n_valid, n_cols, nchunk, d, (uint32_t*)ws, vec_max);
@@ -509,11 +542,11 @@ hipError_t launch_select(const float* scores, int64_t ld, int Q, const int64_t* 
   if (mode == 0 && n_cols <= 256 * SEL_PER) {
     hipLaunchKernelGGL(k_select<256>, dim3((unsigned)Q), dim3(256), 0, stream, scores, ld, n_valid,
                        col_ids, n_cols, d, (const uint32_t*)ws, kk, mode, out, out_ld, out_len, k2,
-                       out2, vec);
+                       out2);
   } else
     hipLaunchKernelGGL(k_select<1024>, dim3((unsigned)Q), dim3(1024), 0, stream, scores, ld,
                        n_valid, col_ids, n_cols, d, (const uint32_t*)ws, kk, mode, out, out_ld,
-                       out_len, k2, out2, vec);
+                       out_len, k2, out2);
   return hipGetLastError();
 }
 
