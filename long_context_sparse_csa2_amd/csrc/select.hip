@@ -99,10 +99,10 @@ __global__ __launch_bounds__(256) void k_maxima(const float* __restrict__ scores
 
 // ------------------------------------------------------------ select
 // One workgroup of NT threads (1024, or 256 for small rounds) per query.
-// The candidates of one round (at most 64 * SEL_PER per wave, in id order)
-// live in registers slot-major: slot i of lane l in wave w holds candidate
-// c = 1024 w + 64 i + l, with key 0 for "no candidate" (no fp32 value maps to
-// key 0).  The candidates of one slot across a wave are then consecutive,
+// The candidates of one round (PER slots per lane, at most NT * PER, in id
+// order) live in registers slot-major: slot i of lane l in wave w holds
+// candidate c = 64 PER w + 64 i + l, with key 0 for "no candidate" (no fp32
+// value maps to key 0).  The candidates of one slot across a wave are then consecutive,
 // so an order-preserving compaction is a ballot and a masked bit count per
 // slot, and the only block-wide step is a prefix over per-wave totals.  A
 // round's block-wide bookkeeping (histogram scans) runs in one wave while
@@ -114,7 +114,10 @@ __global__ __launch_bounds__(256) void k_maxima(const float* __restrict__ scores
 // the smallest kept key (the floor), and the children below it are dropped
 // before the threshold search.  The children's keys then lie between the
 // floor and the best parent's key, so that round needs no min / max pass.
-constexpr int SEL_PER = 16;                        // candidate slots per lane
+constexpr int SEL_PER = 16;                        // candidate slots per lane (small rounds)
+#ifndef SEL_NT
+#define SEL_NT 1024                                // threads of the 16,384-candidate selector
+#endif
 constexpr int SEL_SMALL = 64;                      // intervals this small are ranked exactly
 constexpr int SEL_BINS = 2048;
 
@@ -188,8 +191,8 @@ struct RoundOut {
   bool all;
 };
 
-template <int NT, typename IdOf>
-__device__ __forceinline__ RoundOut select_round(const uint32_t (&kr)[SEL_PER], bool known,
+template <int NT, int PER, typename IdOf>
+__device__ __forceinline__ RoundOut select_round(const uint32_t (&kr)[PER], bool known,
                                                  uint32_t kmn, uint32_t kmx, int want,
                                                  SelShared<NT>& sh, uint32_t* keep, IdOf id_of) {
   constexpr int NW = NT / 64;
@@ -200,7 +203,7 @@ __device__ __forceinline__ RoundOut select_round(const uint32_t (&kr)[SEL_PER], 
   if (!known) {
     uint32_t mnm1 = 0xFFFFFFFFu, mxx = 0u, cnt = 0u;
 #pragma unroll
-    for (int i = 0; i < SEL_PER; ++i) {
+    for (int i = 0; i < PER; ++i) {
       mnm1 = min(mnm1, kr[i] - 1u);               // key 0 wraps to the top
       mxx = max(mxx, kr[i]);
       cnt += kr[i] != 0u ? 1u : 0u;
@@ -230,7 +233,7 @@ __device__ __forceinline__ RoundOut select_round(const uint32_t (&kr)[SEL_PER], 
         // gather the interval's keys (any order); a slot holding some takes
         // its place with one LDS atomic
 #pragma unroll
-        for (int i = 0; i < SEL_PER; ++i) {
+        for (int i = 0; i < PER; ++i) {
           const bool in = kr[i] - lo <= span;
           const uint64_t mk = __ballot(in);
           if (mk) {
@@ -245,14 +248,16 @@ __device__ __forceinline__ RoundOut select_round(const uint32_t (&kr)[SEL_PER], 
         constexpr int RS = NT / SEL_SMALL;
         const int ci = tid / RS, part = tid % RS;
         const uint32_t mine = ci < (int)incnt ? sh.small[ci] : 0u;
-        uint32_t gt = 0, ge = 0;
-        for (uint32_t j = part; j < incnt; j += RS) {
+        uint32_t cnt = 0;                         // keys above mine | keys >= mine << 16
+#pragma unroll
+        for (int it = 0; it < SEL_SMALL / RS; ++it) {
+          const int j = part + it * RS;
           const uint32_t o = sh.small[j];
-          gt += o > mine;
-          ge += o >= mine;
+          cnt += j < (int)incnt ? (o > mine ? 1u : 0u) + (o >= mine ? 0x10000u : 0u) : 0u;
         }
 #pragma unroll
-        for (int off = 1; off < RS; off <<= 1) { gt += __shfl_xor(gt, off); ge += __shfl_xor(ge, off); }
+        for (int off = 1; off < RS; off <<= 1) cnt += (uint32_t)__shfl_xor((int)cnt, off);
+        const uint32_t gt = cnt & 0xFFFFu, ge = cnt >> 16;
         if (part == 0 && ci < (int)incnt && gt < krem && ge >= krem) {
           sh.sres[0] = mine;
           sh.sres[1] = gt;
@@ -272,13 +277,13 @@ __device__ __forceinline__ RoundOut select_round(const uint32_t (&kr)[SEL_PER], 
         // every candidate lies in [lo, hi]; key 0 (none) goes to the lane's
         // own dummy bin (one shared dummy would serialise the atomics)
 #pragma unroll
-        for (int i = 0; i < SEL_PER; ++i) {
+        for (int i = 0; i < PER; ++i) {
           const uint32_t d = kr[i] - lo;
           atomicAdd(&sh.hist[d <= span ? d >> shf : (uint32_t)(SEL_BINS + lane)], 1u);
         }
       } else {
 #pragma unroll
-        for (int i = 0; i < SEL_PER; ++i) {
+        for (int i = 0; i < PER; ++i) {
           const uint32_t d = kr[i] - lo;
           if (d <= span) atomicAdd(&sh.hist[d >> shf], 1u);
         }
@@ -310,10 +315,10 @@ __device__ __forceinline__ RoundOut select_round(const uint32_t (&kr)[SEL_PER], 
   uint32_t ngt = 0, ntie = 0;
   if (fast) {
 #pragma unroll
-    for (int i = 0; i < SEL_PER; ++i) ngt += (uint32_t)__popcll(__ballot(kr[i] >= lo));
+    for (int i = 0; i < PER; ++i) ngt += (uint32_t)__popcll(__ballot(kr[i] >= lo));
   } else {
 #pragma unroll
-    for (int i = 0; i < SEL_PER; ++i) {
+    for (int i = 0; i < PER; ++i) {
       ngt += (uint32_t)__popcll(__ballot(kr[i] > hi));
       ntie += (uint32_t)__popcll(__ballot(kr[i] - lo <= span));
     }
@@ -327,7 +332,7 @@ __device__ __forceinline__ RoundOut select_round(const uint32_t (&kr)[SEL_PER], 
   if (fast) {
     uint32_t pos = gt_before;
 #pragma unroll
-    for (int i = 0; i < SEL_PER; ++i) {
+    for (int i = 0; i < PER; ++i) {
       const bool in = kr[i] >= lo;                  // lo >= 1: key 0 is never in
       const uint64_t km = __ballot(in);
       const uint32_t at = in ? pos + lanes_below(km) : (uint32_t)(SEL_KK_MAX + lane);  // spare
@@ -338,7 +343,7 @@ __device__ __forceinline__ RoundOut select_round(const uint32_t (&kr)[SEL_PER], 
     uint32_t take = tl > tie_before ? tl - tie_before : 0u;
     uint32_t pos = gt_before + min(tie_before, tl);
 #pragma unroll
-    for (int i = 0; i < SEL_PER; ++i) {
+    for (int i = 0; i < PER; ++i) {
       const bool tie = kr[i] - lo <= span;
       const uint64_t tm = __ballot(tie);
       const uint32_t nt = (uint32_t)__popcll(tm);
@@ -358,12 +363,12 @@ __device__ __forceinline__ RoundOut select_round(const uint32_t (&kr)[SEL_PER], 
   return RoundOut{kept, lo, mn, mx, all};
 }
 
-template <int NT>
+template <int NT, int PER>
 __global__ __launch_bounds__(NT) void k_select(
     const float* __restrict__ scores, int64_t ld, const int64_t* __restrict__ n_valid,
     const int32_t* __restrict__ col_ids, int64_t n_cols, LevelDesc d,
     const uint32_t* __restrict__ ws, int kk, int mode, int32_t* __restrict__ out, int64_t out_ld,
-    int64_t* __restrict__ out_len, int k2, int32_t* __restrict__ out2) {
+    int64_t* __restrict__ out_len, int k2, int32_t* __restrict__ out2, int vec_out) {
   __shared__ SelShared<NT> sh;
   const int q = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -371,8 +376,8 @@ __global__ __launch_bounds__(NT) void k_select(
   int32_t* orow = out + (int64_t)q * out_ld;
   const int stop = mode;
   const int64_t out_w = mode == 0 ? kk : (int64_t)kk * 8;
-  const int cap = NT * SEL_PER;
-  const int cbase = 64 * SEL_PER * wave + lane;          // candidate of slot 0
+  const int cap = NT * PER;
+  const int cbase = 64 * PER * wave + lane;          // candidate of slot 0
 
   // first round's level as n_cols gives it; its loads go out before n_valid
   // arrives (every index is clamped into the level's row)
@@ -385,13 +390,13 @@ __global__ __launch_bounds__(NT) void k_select(
     return l == 0 ? (const uint32_t*)srow : ws + d.off[l] + (int64_t)q * d.stride[l];
   };
   int lvl = level_of(n_cols);
-  uint32_t kr[SEL_PER];
+  uint32_t kr[PER];
   auto load_first = [&](int l) {
     const uint32_t* src = src_of(l);
     const int64_t len64 = groups_at(n_cols, l);
     const int last = (int)(len64 < cap ? len64 : cap) - 1;
 #pragma unroll
-    for (int i = 0; i < SEL_PER; ++i) {
+    for (int i = 0; i < PER; ++i) {
       const int c = cbase + 64 * i;
       kr[i] = src[c < last ? c : last];
     }
@@ -415,19 +420,46 @@ __global__ __launch_bounds__(NT) void k_select(
   for (int j = 0; j < (SEL_BINS / NT); ++j) sh.hist[(SEL_BINS / NT) * tid + j] = 0u;
   if (tid == 0) sh.gather = 0u;
 
+  // pool output: positions of the kept blocks (sel, ascending) and its length
+  auto write_pool = [&](int kept, const uint32_t* sel) __attribute__((always_inline)) {
+    if (vec_out) {                       // one block's 8 positions as two 16-byte stores
+      for (int b = tid; b < kk; b += NT) {
+        const int64_t base = b < kept ? (int64_t)sel[b] * 8 : n;
+        uint32_t o[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) o[j] = base + j < n ? (uint32_t)(base + j) : 0xFFFFFFFFu;
+        *(u32x4_t*)(orow + 8 * b) = u32x4_t{o[0], o[1], o[2], o[3]};
+        *(u32x4_t*)(orow + 8 * b + 4) = u32x4_t{o[4], o[5], o[6], o[7]};
+      }
+    } else {
+      for (int i = tid; i < kk * 8; i += NT) {
+        int32_t o = -1;
+        if (i < kept * 8) {
+          const int64_t p = (int64_t)sel[i >> 3] * 8 + (i & 7);
+          if (p < n) o = (int32_t)p;
+        }
+        orow[i] = o;
+      }
+    }
+    if (tid == 0) {
+      const int64_t rem = n - 8 * (int64_t)sel[kept - 1];
+      out_len[q] = (int64_t)8 * (kept - 1) + (rem < 8 ? rem : 8);
+    }
+  };
+  bool pool_pending = false;
   int cur = 0;                      // sh.lists[cur]: parents of the round being loaded
   bool first = true;
   int pcnt = 0;
   uint32_t floor_key = 0;           // children below it cannot be in this round's answer
   uint32_t top_key = 0;             // the best key of the previous round
-  uint32_t pid[SEL_PER];            // child rounds: parent id of each slot
+  uint32_t pid[PER];            // child rounds: parent id of each slot
 
   while (true) {
     const int gl = (int)groups_at(n, lvl);            // n <= 2^26 fits
     const bool is_score = lvl == 0;
     if (first) {
 #pragma unroll
-      for (int i = 0; i < SEL_PER; ++i) {
+      for (int i = 0; i < PER; ++i) {
         const uint32_t k = is_score ? f32_key(__uint_as_float(kr[i])) : kr[i];
         kr[i] = cbase + 64 * i < gl ? k : 0u;
       }
@@ -437,26 +469,35 @@ __global__ __launch_bounds__(NT) void k_select(
       const uint32_t* par = sh.lists[cur];
       const uint32_t* src = src_of(lvl);
 #pragma unroll
-      for (int i = 0; i < SEL_PER; ++i) {
+      for (int i = 0; i < PER; ++i) {    // every parent read first, then every load
         const int p = (cbase + 64 * i) >> 3;
-        const uint32_t pp = p < pcnt ? par[p] : 0xFFFFFFFFu;
-        const uint32_t cid = pp * 8u + (uint32_t)(lane & 7);
-        const bool ok = pp != 0xFFFFFFFFu && cid < (uint32_t)gl;
-        pid[i] = ok ? pp : 0xFFFFFFFFu;
+        pid[i] = par[p < pcnt ? p : 0];
+      }
+#pragma unroll
+      for (int i = 0; i < PER; ++i) {
+        const int p = (cbase + 64 * i) >> 3;
+        const uint32_t cid = pid[i] * 8u + (uint32_t)(lane & 7);
+        const bool ok = p < pcnt && cid < (uint32_t)gl;
+        pid[i] = ok ? pid[i] : 0xFFFFFFFFu;
         kr[i] = src[ok ? cid : 0u];
       }
-      // all 16 gathers in flight before the first use (left to itself the
+      if (pool_pending) {                // the previous round's pool, while the gathers fly
+        write_pool(pcnt, par);
+        pool_pending = false;
+      }
+      // all gathers in flight before the first use (left to itself the
       // compiler sinks each load to its use and serialises their latencies)
       __builtin_amdgcn_s_waitcnt(0);
+      // children below the floor stay: the round's key bounds leave them out
 #pragma unroll
-      for (int i = 0; i < SEL_PER; ++i) {
+      for (int i = 0; i < PER; ++i) {
         const uint32_t k = is_score ? f32_key(__uint_as_float(kr[i])) : kr[i];
-        kr[i] = pid[i] != 0xFFFFFFFFu && k >= floor_key ? k : 0u;
+        kr[i] = pid[i] != 0xFFFFFFFFu ? k : 0u;
       }
     }
     const int want = (lvl == 0 && mode == 1) ? k2 : kk;
     const bool fr = first;
-    const RoundOut ro = select_round<NT>(
+    const RoundOut ro = select_round<NT, PER>(
         kr, !first, floor_key > 0u ? floor_key : 1u, top_key, want, sh, sh.lists[cur ^ 1],
         [&](int i) __attribute__((always_inline)) {
           return fr ? (uint32_t)(cbase + 64 * i) : pid[i] * 8u + (uint32_t)(lane & 7);
@@ -478,19 +519,11 @@ __global__ __launch_bounds__(NT) void k_select(
       return;
     }
     if (lvl == 1 && mode == 1) {           // the pool: positions of the kept blocks
-      for (int i = tid; i < kk * 8; i += NT) {
-        int32_t o = -1;
-        if (i < kept * 8) {
-          const int64_t p = (int64_t)sel[i >> 3] * 8 + (i & 7);
-          if (p < n) o = (int32_t)p;
-        }
-        orow[i] = o;
+      if (k2 <= 0) {
+        write_pool(kept, sel);
+        return;
       }
-      if (tid == 0) {
-        const int64_t rem = n - 8 * (int64_t)sel[kept - 1];
-        out_len[q] = (int64_t)8 * (kept - 1) + (rem < 8 ? rem : 8);
-      }
-      if (k2 <= 0) return;
+      pool_pending = true;                 // written while the next round loads
     }
     if (lvl == 0 && mode == 1) {           // the Full layer's own top-k, from inside its pool
       for (int i = tid; i < k2; i += NT)
@@ -534,19 +567,20 @@ hipError_t launch_select(const float* scores, int64_t ld, int Q, const int64_t* 
   const int64_t nchunk = (n_cols + 4095) / 4096;
   const bool al16 = ((uintptr_t)scores & 15) == 0;
   const int vec_max = (ld % 4 == 0) && al16;    // 16-byte row starts
+  const int vec_out = ((uintptr_t)out & 15) == 0 && out_ld % 4 == 0;   // 16-byte output rows
   if (d.nlev > 0 && nchunk > 0) {
     hipLaunchKernelGGL(k_maxima, dim3((unsigned)(nchunk * Q)), dim3(256), 0, stream, scores, ld,
                        n_valid, n_cols, nchunk, d, (uint32_t*)ws, vec_max);
   }
   // one round over at most 4096 candidates: 256-thread workgroups, several per CU
   if (mode == 0 && n_cols <= 256 * SEL_PER) {
-    hipLaunchKernelGGL(k_select<256>, dim3((unsigned)Q), dim3(256), 0, stream, scores, ld, n_valid,
+    hipLaunchKernelGGL((k_select<256, SEL_PER>), dim3((unsigned)Q), dim3(256), 0, stream, scores, ld, n_valid,
                        col_ids, n_cols, d, (const uint32_t*)ws, kk, mode, out, out_ld, out_len, k2,
-                       out2);
+                       out2, vec_out);
   } else
-    hipLaunchKernelGGL(k_select<1024>, dim3((unsigned)Q), dim3(1024), 0, stream, scores, ld,
+    hipLaunchKernelGGL((k_select<SEL_NT, SEL_CAP / SEL_NT>), dim3((unsigned)Q), dim3(SEL_NT), 0, stream, scores, ld,
                        n_valid, col_ids, n_cols, d, (const uint32_t*)ws, kk, mode, out, out_ld,
-                       out_len, k2, out2);
+                       out_len, k2, out2, vec_out);
   return hipGetLastError();
 }
 
