@@ -492,15 +492,17 @@ def test_determinism():
         assert torch.equal(x, y)
 
 
-def test_graph_replay_matches_eager():
-    """The step captured as HIP graphs (as bench.py replays it) gives the
-    eager result on every replay, with eager work in between."""
+@pytest.mark.parametrize("split_first", [True, False])
+def test_graph_replay_matches_eager(split_first):
+    """The step captured as HIP graphs (as bench.py replays it: one graph,
+    or the scan apart from the rest) gives the eager result on every replay,
+    with eager work in between."""
     from long_context_sparse_csa2_amd.pipeline import Step
     step = Step(synth.scaled(synth.WORKLOADS["c2"], B=2, T=50000), DEV)
     step.run()
     torch.cuda.synchronize()
     ref = [t.clone() for t in step.out] + [step.pool.clone(), step.idx.clone()]
-    graphs = step.capture(split_first=True)
+    graphs = step.capture(split_first=split_first)
     for rep in range(3):
         for t in step.out:
             t.zero_()                     # eager work between replays
