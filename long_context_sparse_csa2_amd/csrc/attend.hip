@@ -70,26 +70,49 @@ __global__ __launch_bounds__(256, 1) void k_attend(
   const int ch_beg = sp * cps;
   const int ch_end = min(ch_beg + cps, nch);
 
-  // this thread's staging row (row t & 63 of chunk ch): flat row, -1 = none
-  auto row_of = [&](int ch, float& sg) __attribute__((always_inline)) {
+  // This thread's staging row (row t & 63 of chunk ch) in two steps: row_req
+  // issues the load its row depends on (the selected id, or the SWA row's
+  // scale), clamped into range, and row_res turns it into the flat row
+  // (-1 = none) and the row scale, so other loads can be issued in between.
+  struct RowReq { int e; float s; };
+  auto row_req = [&](int ch) __attribute__((always_inline)) {
+    RowReq rq{-1, 1.f};
+    const bool main_ch = ch < nmc;             // uniform
+    const int r = (main_ch ? ch * CH_ROWS : (ch - nmc) * CH_ROWS) + (tid & 63);
+    if (main_ch) {
+      rq.e = idx[(int64_t)q * k + (r < k ? r : k - 1)];
+    } else {
+      const int rr = r < sl ? r : sl - 1;       // an SWA chunk exists only when sl >= 1
+      rq.s = swa_scale[seq * T_swa + (sst + rr < T_swa ? sst + rr : sst + rr - T_swa)];
+    }
+    return rq;
+  };
+  auto row_res = [&](int ch, const RowReq& rq, float& sg) __attribute__((always_inline)) {
     const bool main_ch = ch < nmc;
     const int r = (main_ch ? ch * CH_ROWS : (ch - nmc) * CH_ROWS) + (tid & 63);
     int64_t off = -1;
     sg = 1.f;
     if (main_ch) {
-      if (r < k) {
-        const int e = idx[(int64_t)q * k + r];
-        if (e >= 0) off = seq * cap + e;
-      }
+      if (r < k && rq.e >= 0) off = seq * cap + rq.e;
     } else if (r < sl) {
       off = seq * T_swa + (sst + r < T_swa ? sst + r : sst + r - T_swa);
-      sg = swa_scale[off];
+      sg = rq.s;
     }
     return off;
   };
-  // the first chunk's row id is in flight before the query work
+  auto row_of = [&](int ch, float& sg) __attribute__((always_inline)) {
+    return row_res(ch, row_req(ch), sg);
+  };
+  // a readable row of chunk ch in place of a missing one
+  auto readable = [&](int64_t off, bool main_ch) __attribute__((always_inline)) {
+    return off >= 0 ? off : (main_ch ? seq * cap : seq * T_swa + sst);
+  };
+  // the first chunk's row id, then its raw bytes, are in flight before the
+  // query work (the query bytes are requested in between)
+  const RowReq rq0 = row_req(ch_beg < ch_end ? ch_beg : 0);
   float nsg = 1.f;
-  int64_t noff = ch_beg < ch_end ? row_of(ch_beg, nsg) : -1;
+  int64_t noff = -1;
+  RawShare<256> raw;
 
   // ---- query: thread t converts head t >> 4, dims 32 (t & 15) .. +31
   {
@@ -99,6 +122,14 @@ __global__ __launch_bounds__(256, 1) void k_attend(
     bf16x8_t x[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) x[i] = qp[i];
+    // keep the query loads ahead of the wait for the row id (the scheduler
+    // would otherwise issue them after it)
+    __builtin_amdgcn_sched_barrier(0);
+    if (ch_beg < ch_end) {
+      noff = row_res(ch_beg, rq0, nsg);
+      load_share<256>(raw, ch_beg < nmc, readable(noff, ch_beg < nmc), tid >> 6, kv_codes, kv_scales,
+                      swa_codes);
+    }
     rope_table<256>(rp, q, rcs);                   // while the query bytes are in flight
     float xf[32];
 #pragma unroll
@@ -145,9 +176,9 @@ __global__ __launch_bounds__(256, 1) void k_attend(
       float sg = nsg;
       const int64_t off = ch == ch_beg ? noff : row_of(ch, sg);
       const bool valid = off >= 0;
-      const int64_t rd = valid ? off : (is_main ? seq * cap : seq * T_swa + sst);   // a readable row
-      RawShare<256> raw;
-      load_share<256>(raw, is_main, rd, tid >> 6, kv_codes, kv_scales, swa_codes);
+      if (ch != ch_beg)
+        load_share<256>(raw, is_main, readable(off, is_main), tid >> 6, kv_codes, kv_scales,
+                        swa_codes);
       if (tid < CH_ROWS) { rowoff[tid] = off; rowsig[tid] = sg; }
       store_share<256>(raw, is_main, valid, sg, kv[0], kv[1], tid & 63, tid >> 6);
     }
@@ -196,8 +227,8 @@ __global__ __launch_bounds__(256, 1) void k_attend(
         alpha[j] = 1.f;
         p[j] = 0.f;
       } else {
-        alpha[j] = expf(m_run[j] - m_new);            // 0 when m_run is -inf
-        p[j] = valid ? expf(sacc[j] - m_new) : 0.f;
+        alpha[j] = exp_hw(m_run[j] - m_new);            // 0 when m_run is -inf
+        p[j] = valid ? exp_hw(sacc[j] - m_new) : 0.f;
       }
       m_run[j] = m_new;
       pl[hh][lr] = (_Float16)p[j];
@@ -298,12 +329,12 @@ __global__ __launch_bounds__(128) void k_attend_combine(const float* __restrict_
       if (s0 + i < nsplit && ml[i][1] > 0.f) bm = fmaxf(bm, ml[i][0]);
     const float nM = fmaxf(M, bm);
     if (nM == -INFINITY) continue;                      // nothing attended so far
-    const float sc = expf(M - nM);                      // 0 while M is -inf
+    const float sc = exp_hw(M - nM);                      // 0 while M is -inf
     L *= sc;
     acc *= sc;
 #pragma unroll
     for (int i = 0; i < AT_MERGE_BATCH; ++i) {
-      const float w = (s0 + i < nsplit && ml[i][1] > 0.f) ? expf(ml[i][0] - nM) : 0.f;
+      const float w = (s0 + i < nsplit && ml[i][1] > 0.f) ? exp_hw(ml[i][0] - nM) : 0.f;
       L += ml[i][1] * w;
       acc += ov[i] * w;
     }

@@ -28,6 +28,11 @@
 
 namespace csa2 {
 
+// e^x on the hardware exponential, 2^(x log2 e) by v_exp_f32.  Rounding
+// x log2 e adds at most |x| 2^-24 relative error, far below the fp16
+// rounding the softmax weights get before the P V product; e^-inf = 0.
+__device__ __forceinline__ float exp_hw(float x) { return __expf(x); }
+
 typedef short i16x4_t __attribute__((ext_vector_type(4)));
 typedef _Float16 f16x4_t __attribute__((ext_vector_type(4)));
 

@@ -211,10 +211,10 @@ __global__ __launch_bounds__(AW_THREADS, 1) void k_attend_wide(
 #pragma unroll
         for (int rt = 0; rt < 2; ++rt) pl[hh][half * 32 + rt * 16 + r16] = (_Float16)0.f;
       } else {
-        alpha[j] = expf(m_run[j] - m_new);          // 0 when m_run is -inf
+        alpha[j] = exp_hw(m_run[j] - m_new);          // 0 when m_run is -inf
 #pragma unroll
         for (int rt = 0; rt < 2; ++rt) {
-          const float p = expf(sacc[rt][j] - m_new); // masked rows: exp(-inf) = 0
+          const float p = exp_hw(sacc[rt][j] - m_new); // masked rows: exp(-inf) = 0
           psum += p;
           pl[hh][half * 32 + rt * 16 + r16] = (_Float16)p;
         }
