@@ -363,12 +363,14 @@ __device__ __forceinline__ RoundOut select_round(const uint32_t (&kr)[PER], bool
   return RoundOut{kept, lo, mn, mx, all};
 }
 
+// The 256-thread selector runs many queries per CU (prefill): five waves
+// per SIMD keep five workgroups resident.
 template <int NT, int PER>
-__global__ __launch_bounds__(NT) void k_select(
+__global__ __launch_bounds__(NT, (NT <= 256 ? 5 : 1)) void k_select(
     const float* __restrict__ scores, int64_t ld, const int64_t* __restrict__ n_valid,
     const int32_t* __restrict__ col_ids, int64_t n_cols, LevelDesc d,
     const uint32_t* __restrict__ ws, int kk, int mode, int32_t* __restrict__ out, int64_t out_ld,
-    int64_t* __restrict__ out_len, int k2, int32_t* __restrict__ out2, int vec_out) {
+    int64_t* __restrict__ out_len, int k2, int32_t* __restrict__ out2, int vec_out, int spec) {
   __shared__ SelShared<NT> sh;
   const int q = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -379,8 +381,11 @@ __global__ __launch_bounds__(NT) void k_select(
   const int cap = NT * PER;
   const int cbase = 64 * PER * wave + lane;          // candidate of slot 0
 
-  // first round's level as n_cols gives it; its loads go out before n_valid
-  // arrives (every index is clamped into the level's row)
+  // spec (few queries, latency-bound): the first round's loads go out before
+  // n_valid arrives, at the level n_cols gives, every index clamped into the
+  // level's row; otherwise (many queries: causal prefill rows hold fewer
+  // valid columns than n_cols) they wait for n_valid and stop at the valid
+  // groups
   auto level_of = [&](int64_t n) {
     int l = 0;
     while (groups_at(n, l) > (int64_t)cap) ++l;
@@ -391,9 +396,9 @@ __global__ __launch_bounds__(NT) void k_select(
   };
   int lvl = level_of(n_cols);
   uint32_t kr[PER];
-  auto load_first = [&](int l) {
+  auto load_first = [&](int l, int64_t nn) {
     const uint32_t* src = src_of(l);
-    const int64_t len64 = groups_at(n_cols, l);
+    const int64_t len64 = groups_at(nn, l);
     const int last = (int)(len64 < cap ? len64 : cap) - 1;
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
@@ -401,7 +406,7 @@ __global__ __launch_bounds__(NT) void k_select(
       kr[i] = src[c < last ? c : last];
     }
   };
-  if (n_cols > 0) load_first(lvl);
+  if (spec && n_cols > 0) load_first(lvl, n_cols);
   const int64_t n0 = n_valid[q];
   const int64_t n = n0 < 0 ? 0 : (n0 < n_cols ? n0 : n_cols);
   if (n == 0) {
@@ -412,9 +417,17 @@ __global__ __launch_bounds__(NT) void k_select(
     }
     return;
   }
+  if (mode == 0 && n <= kk) {              // every valid column is kept, in id order
+    for (int i = tid; i < kk; i += NT) {
+      int32_t o = -1;
+      if (i < n) o = col_ids ? col_ids[(int64_t)q * ld + i] : i;
+      orow[i] = o;
+    }
+    return;
+  }
   {
     const int ln = level_of(n);
-    if (ln != lvl) { lvl = ln; load_first(lvl); }
+    if (!spec || ln != lvl) { lvl = ln; load_first(lvl, n); }
   }
 #pragma unroll
   for (int j = 0; j < (SEL_BINS / NT); ++j) sh.hist[(SEL_BINS / NT) * tid + j] = 0u;
@@ -568,6 +581,7 @@ hipError_t launch_select(const float* scores, int64_t ld, int Q, const int64_t* 
   const bool al16 = ((uintptr_t)scores & 15) == 0;
   const int vec_max = (ld % 4 == 0) && al16;    // 16-byte row starts
   const int vec_out = ((uintptr_t)out & 15) == 0 && out_ld % 4 == 0;   // 16-byte output rows
+  const int spec = Q <= 64;                      // first loads ahead of n_valid
   if (d.nlev > 0 && nchunk > 0) {
     hipLaunchKernelGGL(k_maxima, dim3((unsigned)(nchunk * Q)), dim3(256), 0, stream, scores, ld,
                        n_valid, n_cols, nchunk, d, (uint32_t*)ws, vec_max);
@@ -576,11 +590,11 @@ hipError_t launch_select(const float* scores, int64_t ld, int Q, const int64_t* 
   if (mode == 0 && n_cols <= 256 * SEL_PER) {
     hipLaunchKernelGGL((k_select<256, SEL_PER>), dim3((unsigned)Q), dim3(256), 0, stream, scores, ld, n_valid,
                        col_ids, n_cols, d, (const uint32_t*)ws, kk, mode, out, out_ld, out_len, k2,
-                       out2, vec_out);
+                       out2, vec_out, spec);
   } else
     hipLaunchKernelGGL((k_select<SEL_NT, SEL_CAP / SEL_NT>), dim3((unsigned)Q), dim3(SEL_NT), 0, stream, scores, ld,
                        n_valid, col_ids, n_cols, d, (const uint32_t*)ws, kk, mode, out, out_ld,
-                       out_len, k2, out2, vec_out);
+                       out_len, k2, out2, vec_out, spec);
   return hipGetLastError();
 }
 
