@@ -294,6 +294,64 @@ def test_select_topk_col_ids(n):
         checks.check_topk_exact(out[i], s[i, :nv[i]], 512, ids[i, :nv[i]])
 
 
+@pytest.mark.parametrize("n", [3000, 20000, 70000])
+def test_select_topk_extremes(n):
+    """Infinities, signed zeros and subnormals among the scores (ordered as
+    fp32 values, +0 == -0, ties to the lower id), in one- and multi-round
+    selections."""
+    Q = 2
+    rng = np.random.default_rng(n)
+    s = rng.standard_normal((Q, n)).astype(np.float32)
+    s[:, ::97] = np.inf
+    s[:, 5::89] = -np.inf
+    s[:, 7::13] = -0.0
+    s[:, 9::17] = 0.0
+    s[:, 11::19] = np.float32(1e-40)          # subnormal
+    s[1, :] = np.where(s[1, :] > 0, np.float32(3.0), s[1, :])   # a huge tie block
+    nv = [n, n - 3]
+    out = _topk(s, nv, 512)
+    for i in range(Q):
+        checks.check_topk_exact(out[i], s[i, :nv[i]], 512)
+
+
+@pytest.mark.parametrize("n", [1, 300, 512])
+def test_select_topk_keep_all(n):
+    """At most k valid columns: every one is kept, in id order, mapped
+    through col_ids when given."""
+    Q = 2
+    rng = np.random.default_rng(7)
+    s = _rand_scores(Q, max(n, 600), seed=8)
+    ids = np.stack([np.sort(rng.choice(1 << 20, s.shape[1], replace=False)) for _ in range(Q)]).astype(np.int32)
+    nv = [n, max(0, n - 1)]
+    for col in (None, ids):
+        out = _topk(s, nv, 512, col)
+        for i in range(Q):
+            checks.check_topk_exact(out[i], s[i, :nv[i]], 512, None if col is None else ids[i, :nv[i]])
+
+
+@pytest.mark.parametrize("n", [300000, 16384 * 8 + 5])
+def test_block_pool_heavy_ties(n):
+    """Scores on a coarse grid (thousands of exact ties at every threshold)
+    and an all-equal row: the pool and top-k still follow the (score desc,
+    id asc) order in every round of the pyramid."""
+    Q = 2
+    rng = np.random.default_rng(n)
+    s = (np.floor(rng.standard_normal((Q, n)) * 4) / 4).astype(np.float32)
+    s[1, :] = 1.0
+    nv = [n, n - 7]
+    ws = C.workspace(C.CSA2_OP_POOL, Q, n, 2048, DEV)
+    pool = torch.empty(Q, 16384, dtype=torch.int32, device=DEV)
+    plen = torch.empty(Q, dtype=torch.int64, device=DEV)
+    topk = torch.empty(Q, 512, dtype=torch.int32, device=DEV)
+    C.csa2_block_pool(torch.from_numpy(s).to(DEV), torch.tensor(nv, dtype=torch.int64).to(DEV), n,
+                      2048, pool, plen, ws, topk=topk)
+    torch.cuda.synchronize()
+    for i in range(Q):
+        checks.check_pool_exact(checks.host(pool[i]), checks.host(plen[i]), s[i, :nv[i]], 8, 2048)
+        checks.check_topk_exact(checks.host(topk[i]), s[i, :nv[i]], 512)
+    assert np.array_equal(checks.host(topk[1]), np.arange(512))
+
+
 @pytest.mark.parametrize("n", [3, 2048, 16384 + 3, 16384 * 8 + 5, 300000])
 def test_block_pool(n):
     Q = 2
