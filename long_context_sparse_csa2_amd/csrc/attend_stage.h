@@ -91,11 +91,12 @@ __device__ __forceinline__ f16x8_t fp8x8_f16(uint32_t lo, uint32_t hi) {
   return f16x8_t{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
 }
 
-// Dequantise one share into row `row` of kv (and, for SWA rows, the scaled
-// copy into kv2).  An invalid main row is written as zeros and an invalid
-// SWA row gets a zero V copy: the caller masks their scores, and zero values
-// keep P V finite whatever bytes the row held.
-template <int NT>
+// Dequantise one share into row `row` of kv (and, for SWA rows with
+// V_COPY, the copy scaled by the row scale into kv2; without it the caller
+// applies the row scale to P instead).  An invalid main row is written as
+// zeros and an invalid SWA row gets a zero V (copy): the caller masks their
+// scores, and zero values keep P V finite whatever bytes the row held.
+template <int NT, bool V_COPY = true>
 __device__ __forceinline__ void store_share(const RawShare<NT>& r, bool is_main, bool valid,
                                             float sig, _Float16* __restrict__ kv,
                                             _Float16* __restrict__ kv2, int row, int part) {
@@ -118,6 +119,13 @@ __device__ __forceinline__ void store_share(const RawShare<NT>& r, bool is_main,
         *(f16x8_t*)(dst + 16 * g) = fp4x8_f16(w0, s2);
         *(f16x8_t*)(dst + 16 * g + 8) = fp4x8_f16(w1, s2);
       }
+    }
+  } else if (!V_COPY) {
+    const uint32_t keep = valid ? 0xFFFFFFFFu : 0u;   // code 0 is +0
+#pragma unroll
+    for (int i = 0; i < R::SW; ++i) {                 // 16 dims per word
+      *(f16x8_t*)(dst + 16 * i) = fp8x8_f16(r.c[i][0] & keep, r.c[i][1] & keep);
+      *(f16x8_t*)(dst + 16 * i + 8) = fp8x8_f16(r.c[i][2] & keep, r.c[i][3] & keep);
     }
   } else {
     _Float16* dst2 = kv2 + row * KV_LD + part * R::DIMS;

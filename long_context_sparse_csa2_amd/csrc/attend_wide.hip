@@ -1,4 +1,4 @@
-// Steps a8 + a9 for many queries at once (prefill): one 512-thread
+// Steps a8 + a9 for many queries at once (prefill): one 256-thread
 // workgroup per query covering all 64 heads, so every gathered row is read
 // and dequantised once for the whole query.
 //
@@ -7,50 +7,59 @@
 // being both key and value; section 2.4.4: FP4 main KV dequantised before
 // attention, FP8 SWA KV.
 //
-// Per 64-row chunk (main-KV chunks first, then SWA chunks, so each chunk has
-// one row type):
-//   staging  thread t holds the raw bytes of row t & 63, dims 64 (t >> 6)
-//            .. +63, loaded one chunk ahead (the row ids two chunks ahead),
-//            and writes them dequantised to fp16 in LDS (attend_stage.h)
-//   S        64 heads x 64 rows, fp16 MFMA 16x16x32; wave w = (head group
-//            w & 3, row half w >> 2); the query tile sits in registers as
-//            fp16, each head scaled by a power of two (undone on S)
-//   softmax  running max per head shared through LDS; each wave keeps the
-//            sum of its own rows (same reference max), added at the end; the
-//            reference max only moves when a chunk beats it by more than
-//            e^8, so the rescaling of O is skipped in most chunks
-//   O += P V fp16 MFMA 16x16x32; wave w = (head group, 256-dim half); V
-//            columns through transposing LDS reads of the staged rows
+// The workgroup holds about 80 KB of LDS, so two queries' workgroups share
+// a CU and their phases interleave: one's softmax and staging run while the
+// other's MFMAs and LDS reads do.  Per 64-row chunk (main-KV chunks first,
+// then SWA chunks, so each chunk has one row type):
+//   staging  thread t loads the raw bytes of row t & 63, dims 128 (t >> 6)
+//            .. +127 (its row id one chunk ahead) and writes them
+//            dequantised to fp16 in LDS (attend_stage.h);
+//            SWA rows are staged unscaled, once: their row scale multiplies
+//            the scores and P
+//   S^T      64 rows x 16 heads per wave (wave w: heads 16w .. +15), fp16
+//            MFMA 16x16x32 with the staged rows as A and the query, in
+//            registers as fp16 (each head scaled by a power of two, undone
+//            on S), as B; a lane then holds one head's scores for 16 rows
+//   softmax  per head within the wave (in-lane, then the lanes xor 16 and
+//            32); the reference max only moves when a chunk beats it by more
+//            than e^8, so O is rescaled in few chunks; P^T and the per-head
+//            rescale factors go to LDS
+//   O^T += V^T P^T  512 dims x 64 heads, wave w: dims 128w .. +127 for all
+//            heads, so every staged value is read once; V^T through
+//            transposing LDS reads of the staged rows, P^T from LDS
 #include "common.h"
 #include "launch.h"
 #include "attend_stage.h"
 
 namespace csa2 {
 
-constexpr int AW_THREADS = 512;
-constexpr int AW_PAD = 8;              // fp16 padding of pl rows
+constexpr int AW_THREADS = 256;
+constexpr int AW_PAD = 8;              // fp16 padding of a P^T row
 constexpr int AW_MAX_SWA = 128;        // largest SWA window per query
 constexpr float AW_LAZY = 8.f;         // slack of the softmax reference max (natural log)
 
-__global__ __launch_bounds__(AW_THREADS, 1) void k_attend_wide(
+// ROPE: the query is turned before QK^T and the output turned back (the
+// variant without it leaves the low query terms out of the registers).
+template <bool ROPE>
+__global__ __launch_bounds__(AW_THREADS, 2) void k_attend_wide(
     const uint16_t* __restrict__ qv, const int32_t* __restrict__ q_seq,
     const uint8_t* __restrict__ kv_codes, const uint8_t* __restrict__ kv_scales, int64_t cap,
     const int32_t* __restrict__ idx, int k, const uint8_t* __restrict__ swa_codes,
     const float* __restrict__ swa_scale, int64_t T_swa, const int64_t* __restrict__ swa_start,
     const int32_t* __restrict__ swa_len, float* __restrict__ out, float* __restrict__ lse,
     RopeArgs rp) {
-  __shared__ __align__(16) _Float16 kv[2][CH_ROWS * KV_LD];        // K (+ V of main rows), V of SWA rows
-  __shared__ __align__(16) _Float16 pl[H_ATT][CH_ROWS + AW_PAD];  // P of the chunk
-  __shared__ int64_t rowoff[CH_ROWS];
-  __shared__ float rowsig[CH_ROWS];
-  __shared__ float red_m[2][H_ATT];
-  __shared__ float red_l[2][H_ATT];
+  __shared__ __align__(16) _Float16 kv[CH_ROWS * KV_LD];           // the chunk's rows (K = V)
+  __shared__ __align__(16) _Float16 pt[H_ATT][CH_ROWS + AW_PAD];   // P^T (SWA rows: times the row scale)
+  __shared__ __align__(16) float rowsc[CH_ROWS];                   // score scale of a row; -1 = no row
+  __shared__ float head_a[H_ATT];                                  // this chunk's O rescale per head
+  __shared__ float head_l[H_ATT];                                  // softmax sums at the end
+  __shared__ int moved_w[4];                                       // a wave's heads moved their max
   __shared__ f32x2_t rcs[ROPE_MAX_PAIRS];                          // RoPE (cos, sin) per pair
 
   const int q = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int r16 = lane & 15, qd = lane >> 4;
-  const int hg = wave & 3, half = wave >> 2;
+  const int head = 16 * wave + r16;                      // S^T and softmax: this lane's head
   const int64_t seq = q_seq[q];
   const int64_t sst = swa_start[q];
   int64_t sl64 = swa_len[q];
@@ -82,22 +91,26 @@ __global__ __launch_bounds__(AW_THREADS, 1) void k_attend_wide(
     return off;
   };
 
-  // ---- query tile of head group hg (head 16 hg + r16, dims 32 s + 8 qd .. +7)
+  // ---- row ids one chunk ahead (the raw bytes are loaded at staging: the
+  // other workgroup on the CU computes meanwhile)
+  int cur_e = entry_of(0);
+
+  // ---- query of head `head` as the B operand: dims 32 s + 8 qd .. +7 for step s
   f16x8_t a[16];
   f16x8_t alo[2];                 // with RoPE: low terms of steps 14 and 15
-  float hinv[4];
+  float hinv;
   {
-    const uint16_t* qp = qv + ((int64_t)q * H_ATT + hg * 16 + r16) * D_LAT + 8 * qd;
+    const uint16_t* qp = qv + ((int64_t)q * H_ATT + head) * D_LAT + 8 * qd;
     bf16x8_t x[16];
 #pragma unroll
     for (int s = 0; s < 16; ++s) x[s] = *(const bf16x8_t*)(qp + 32 * s);
-    rope_table<AW_THREADS>(rp, q, rcs);            // while the query bytes are in flight
+    if (ROPE) rope_table<AW_THREADS>(rp, q, rcs);  // while the query bytes are in flight
     float xf[16][8];
 #pragma unroll
     for (int s = 0; s < 16; ++s)
 #pragma unroll
       for (int j = 0; j < 8; ++j) xf[s][j] = (float)x[s][j];
-    if (rp.dims > 0) {
+    if (ROPE && rp.dims > 0) {
 #pragma unroll
       for (int s = 0; s < 16; ++s)
 #pragma unroll
@@ -123,151 +136,137 @@ __global__ __launch_bounds__(AW_THREADS, 1) void k_attend_wide(
     for (int s = 0; s < 2; ++s)
 #pragma unroll
       for (int j = 0; j < 8; ++j) alo[s][j] = (_Float16)(xf[14 + s][j] * f - (float)a[14 + s][j]);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) hinv[j] = ldexpf(1.f, -__shfl(e, 4 * qd + j));
+    hinv = ldexpf(1.f, -e);
   }
-  f32x4_t o[16];
+  // O^T tiles: dims 128 wave + 16 t + 4 qd + j, head 16 g + r16
+  f32x4_t o[8][4];
 #pragma unroll
-  for (int t = 0; t < 16; ++t) o[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  float m_run[4], l_run[4];
+  for (int t = 0; t < 8; ++t)
 #pragma unroll
-  for (int j = 0; j < 4; ++j) { m_run[j] = -INFINITY; l_run[j] = 0.f; }
-
-  // ---- pipeline: raw bytes of chunk 0 in flight, entry of chunk 1 in flight
-  RawShare<AW_THREADS> raw;
-  int64_t cur_off = -1;
-  int nxt_e = -1;
-  if (nch > 0) {
-    cur_off = row_of(0, entry_of(0));
-    const bool m0 = 0 < nmc;
-    load_share<AW_THREADS>(raw, m0, cur_off >= 0 ? cur_off : (m0 ? seq * cap : seq * T_swa + sst),
-                           spart, kv_codes, kv_scales, swa_codes);
-    nxt_e = entry_of(1);
-  }
+    for (int g = 0; g < 4; ++g) o[t][g] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY, l_run = 0.f;                 // of head `head` (equal in its 4 lanes)
 
   for (int ch = 0; ch < nch; ++ch) {
     const bool is_main = ch < nmc;
     // ---- this chunk's rows, dequantised, into LDS
     {
-      const bool valid = cur_off >= 0;
-      const float sg = (!is_main && valid) ? swa_scale[cur_off] : 1.f;
-      if (tid < CH_ROWS) { rowoff[tid] = cur_off; rowsig[tid] = sg; }
-      store_share<AW_THREADS>(raw, is_main, valid, sg, kv[0], kv[1], srow, spart);
+      const int64_t off = row_of(ch, cur_e);
+      cur_e = entry_of(ch + 1);
+      const bool valid = off >= 0;
+      RawShare<AW_THREADS> raw;
+      load_share<AW_THREADS>(raw, is_main, valid ? off : (is_main ? seq * cap : seq * T_swa + sst),
+                             spart, kv_codes, kv_scales, swa_codes);
+      const float sg = (!is_main && valid) ? swa_scale[off] : 1.f;
+      if (tid < CH_ROWS) rowsc[tid] = valid ? sg : -1.f;
+      store_share<AW_THREADS, false>(raw, is_main, valid, sg, kv, nullptr, srow, spart);
     }
     __syncthreads();
-    // ---- next chunk's bytes and the entry after it, in flight during the compute
-    if (ch + 1 < nch) {
-      cur_off = row_of(ch + 1, nxt_e);
-      const bool mn = ch + 1 < nmc;
-      load_share<AW_THREADS>(raw, mn, cur_off >= 0 ? cur_off : (mn ? seq * cap : seq * T_swa + sst),
-                             spart, kv_codes, kv_scales, swa_codes);
-      nxt_e = entry_of(ch + 2);
-    }
 
-    // ---- S = Q K^T: rows 32*half .. +31 (two 16-row tiles), heads of group hg
-    f32x4_t sacc[2];
+    // ---- S^T for rows 16 rt + 4 qd + j, head `head`
+    float s[4][4];
 #pragma unroll
-    for (int rt = 0; rt < 2; ++rt) {
-      const int row = half * 32 + rt * 16 + r16;
+    for (int rt = 0; rt < 4; ++rt) {
       f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int s = 0; s < 16; ++s) acc = mfma16_f16(a[s], qk_b(kv[0], row, s, qd), acc);
-      if (rp.dims > 0) {
+      for (int st = 0; st < 16; ++st) acc = mfma16_f16(qk_b(kv, 16 * rt + r16, st, qd), a[st], acc);
+      if (ROPE && rp.dims > 0) {
 #pragma unroll
-        for (int s = 0; s < 2; ++s) acc = mfma16_f16(alo[s], qk_b(kv[0], row, 14 + s, qd), acc);
+        for (int st = 0; st < 2; ++st) acc = mfma16_f16(qk_b(kv, 16 * rt + r16, 14 + st, qd), alo[st], acc);
       }
-      const bool valid = rowoff[row] >= 0;
-      const float rs = is_main ? 1.f : rowsig[row];
+      const f32x4_t rs = *(const f32x4_t*)&rowsc[16 * rt + 4 * qd];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) acc[j] = valid ? acc[j] * hinv[j] * rs : -INFINITY;
-      sacc[rt] = acc;
+      for (int j = 0; j < 4; ++j) s[rt][j] = rs[j] >= 0.f ? acc[j] * hinv * rs[j] : -INFINITY;
     }
 
-    // ---- online softmax: chunk max per head over both row halves
-    float cm[4];
+    // ---- online softmax of head `head` over the chunk's 64 rows
+    float cm = -INFINITY;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      cm[j] = row16_max(fmaxf(sacc[0][j], sacc[1][j]));
-    }
-    if (r16 == 0) {
+    for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) red_m[half][hg * 16 + 4 * qd + j] = cm[j];
-    }
-    __syncthreads();
-    float alpha[4];
-    bool moved = false;
+      for (int j = 0; j < 4; ++j) cm = fmaxf(cm, s[rt][j]);
+    cm = fmaxf(cm, __shfl_xor(cm, 16));
+    cm = fmaxf(cm, __shfl_xor(cm, 32));
+    // the reference max moves only when a chunk exceeds it by more than
+    // AW_LAZY (P then stays below e^AW_LAZY, far inside fp16)
+    const float m_new = cm > m_run + AW_LAZY ? cm : m_run;
+    const bool moved = m_new != m_run;
+    float alpha = 1.f, psum = 0.f;
+    const f32x4_t* rsv = (const f32x4_t*)rowsc;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int hh = hg * 16 + 4 * qd + j;
-      // the reference max of a head moves only when a chunk exceeds it by
-      // more than AW_LAZY (P then stays below e^AW_LAZY, far inside fp16), so
-      // O is rescaled only in the few chunks where some max moved
-      const float m_chunk = fmaxf(red_m[0][hh], red_m[1][hh]);
-      const float m_new = m_chunk > m_run[j] + AW_LAZY ? m_chunk : m_run[j];
-      moved |= m_new != m_run[j];
-      float psum = 0.f;
-      if (m_new == -INFINITY) {
-        alpha[j] = 1.f;
+    for (int rt = 0; rt < 4; ++rt) {
+      const f32x4_t rs = rsv[4 * rt + qd];
+      f16x4_t pv;
 #pragma unroll
-        for (int rt = 0; rt < 2; ++rt) pl[hh][half * 32 + rt * 16 + r16] = (_Float16)0.f;
-      } else {
-        alpha[j] = exp_hw(m_run[j] - m_new);          // 0 when m_run is -inf
-#pragma unroll
-        for (int rt = 0; rt < 2; ++rt) {
-          const float p = exp_hw(sacc[rt][j] - m_new); // masked rows: exp(-inf) = 0
-          psum += p;
-          pl[hh][half * 32 + rt * 16 + r16] = (_Float16)p;
-        }
+      for (int j = 0; j < 4; ++j) {
+        const float p = m_new == -INFINITY ? 0.f : exp_hw(s[rt][j] - m_new);   // masked rows: 0
+        psum += p;
+        pv[j] = (_Float16)(is_main ? p : p * fmaxf(rs[j], 0.f));     // SWA: V is unscaled
       }
-      l_run[j] = l_run[j] * alpha[j] + row16_sum(psum);   // this wave's rows only
-      m_run[j] = m_new;
+      *(f16x4_t*)&pt[head][16 * rt + 4 * qd] = pv;
     }
+    if (m_new != -INFINITY) alpha = exp_hw(m_run - m_new);          // 0 when m_run is -inf
+    psum += __shfl_xor(psum, 16);
+    psum += __shfl_xor(psum, 32);
+    l_run = l_run * alpha + psum;
+    m_run = m_new;
+    if (qd == 0) head_a[head] = alpha;
+    const uint64_t mv = __ballot(moved);
+    if (lane == 0) moved_w[wave] = mv != 0;
     __syncthreads();
 
-    // ---- O += P V: heads of group hg, dims 256*half .. +255 (16 tiles)
-    // (the O rows of this lane are the same heads as its S rows: 16hg + 4qd + j)
-    if (__builtin_amdgcn_ballot_w64(moved) != 0) {        // uniform over the wave
+    // ---- O^T += V^T P^T: dims 128 wave .. +127, all 64 heads
+    if (moved_w[0] | moved_w[1] | moved_w[2] | moved_w[3]) {     // uniform
 #pragma unroll
-      for (int t = 0; t < 16; ++t) {
+      for (int g = 0; g < 4; ++g) {
+        const float al = head_a[16 * g + r16];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) o[t][j] *= alpha[j];
+        for (int t = 0; t < 8; ++t) o[t][g] *= al;
       }
     }
-    const _Float16* vrows = is_main ? kv[0] : kv[1];
-    const f16x8_t pa0 = *(const f16x8_t*)&pl[hg * 16 + r16][qd * 8];
-    const f16x8_t pa1 = *(const f16x8_t*)&pl[hg * 16 + r16][32 + qd * 8];
 #pragma unroll
-    for (int t = 0; t < 16; ++t) {
-      const int n0 = half * 256 + 16 * t;
-      o[t] = mfma16_f16(pa0, pv_b(vrows, 0, n0, lane), o[t]);
-      o[t] = mfma16_f16(pa1, pv_b(vrows, 32, n0, lane), o[t]);
+    for (int kk = 0; kk < 2; ++kk) {                 // rows 32 kk .. +31
+      f16x8_t pb[4];
+#pragma unroll
+      for (int g = 0; g < 4; ++g) pb[g] = *(const f16x8_t*)&pt[16 * g + r16][32 * kk + 8 * qd];
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        const f16x8_t va = pv_b(kv, 32 * kk, 128 * wave + 16 * t, lane);
+#pragma unroll
+        for (int g = 0; g < 4; ++g) o[t][g] = mfma16_f16(va, pb[g], o[t][g]);
+      }
     }
     __syncthreads();
   }
 
-  // ---- totals: the two row-half waves of a head group hold partial sums
-  if (r16 == 0) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) red_l[half][hg * 16 + 4 * qd + j] = l_run[j];
-  }
+  // ---- normalise by each head's sum and write (RoPE channels turned back)
+  if (qd == 0) head_l[head] = l_run;
+  if (lse && qd == 0)
+    lse[(int64_t)q * H_ATT + head] = l_run > 0.f ? m_run + logf(l_run) : -INFINITY;
   __syncthreads();
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int hh = hg * 16 + 4 * qd + j;
-    const float L = red_l[0][hh] + red_l[1][hh];
+  for (int g = 0; g < 4; ++g) {
+    const int hh = 16 * g + r16;
+    const float L = head_l[hh];
     const float inv = L > 0.f ? 1.f / L : 0.f;
-    const int64_t row = ((int64_t)q * H_ATT + hh) * D_LAT + half * 256 + r16;
+    const int64_t row = ((int64_t)q * H_ATT + hh) * D_LAT;
 #pragma unroll
-    for (int t = 0; t < 16; ++t) {
-      float v = o[t][j] * inv;
-      const int d = half * 256 + 16 * t + r16;
-      if (rp.dims > 0 && half * 256 + 16 * t + 15 >= D_LAT - rp.dims)   // uniform per wave
-        v = rope_out_lane(v, d, rp.dims, rcs);
-      if (rp.out_bf16) rp.out_bf16[row + 16 * t] = bf16_rne(v);
-      else out[row + 16 * t] = v;
+    for (int t = 0; t < 8; ++t) {
+      const int d0 = 128 * wave + 16 * t + 4 * qd;
+      float v[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) v[j] = o[t][g][j] * inv;
+      if (ROPE && rp.dims > 0 && 128 * wave + 16 * t + 15 >= D_LAT - rp.dims) {   // uniform per wave
+        rope_pair(v[0], v[1], d0, rp.dims, rcs, -1.f);
+        rope_pair(v[2], v[3], d0 + 2, rp.dims, rcs, -1.f);
+      }
+      if (rp.out_bf16) {
+        const uint32_t lo = (uint32_t)bf16_rne(v[0]) | ((uint32_t)bf16_rne(v[1]) << 16);
+        const uint32_t hi = (uint32_t)bf16_rne(v[2]) | ((uint32_t)bf16_rne(v[3]) << 16);
+        *(uint2*)(rp.out_bf16 + row + d0) = make_uint2(lo, hi);
+      } else {
+        *(f32x4_t*)(out + row + d0) = f32x4_t{v[0], v[1], v[2], v[3]};
+      }
     }
-    if (lse && half == 0 && r16 == 0)
-      lse[(int64_t)q * H_ATT + hh] = L > 0.f ? m_run[j] + logf(L) : -INFINITY;
   }
 }
 
@@ -277,9 +276,14 @@ hipError_t launch_attend_wide(const uint16_t* q, const int32_t* q_seq, int Q,
                               const float* swa_scale, int64_t T_swa, const int64_t* swa_start,
                               const int32_t* swa_len, float* out, float* lse, const RopeArgs& rp,
                               hipStream_t stream) {
-  hipLaunchKernelGGL(k_attend_wide, dim3((unsigned)Q), dim3(AW_THREADS), 0, stream, q, q_seq,
-                     kv_codes, kv_scales, cap, idx, k, swa_codes, swa_scale, T_swa, swa_start,
-                     swa_len, out, lse, rp);
+  if (rp.dims > 0)
+    hipLaunchKernelGGL(k_attend_wide<true>, dim3((unsigned)Q), dim3(AW_THREADS), 0, stream, q,
+                       q_seq, kv_codes, kv_scales, cap, idx, k, swa_codes, swa_scale, T_swa,
+                       swa_start, swa_len, out, lse, rp);
+  else
+    hipLaunchKernelGGL(k_attend_wide<false>, dim3((unsigned)Q), dim3(AW_THREADS), 0, stream, q,
+                       q_seq, kv_codes, kv_scales, cap, idx, k, swa_codes, swa_scale, T_swa,
+                       swa_start, swa_len, out, lse, rp);
   return hipGetLastError();
 }
 
