@@ -184,8 +184,9 @@ def time_attend_rope(step, dev, calls=20):
 
 def cpu_baseline_prefill(wl, step, seconds_target=15.0):
     """The fp64 oracle on a sample of a prefill's queries, spread over the
-    causal range: per query, every layer (scores over its visible entries,
-    top-512, attention with its SWA window).  One query stands for m raw
+    causal range: per query, its entry compressed from its m raw tokens, then
+    every layer (scores over its visible entries, top-512, attention with its
+    SWA window).  One query stands for m raw
     tokens, so tokens/s = m x queries / s (the work grows with the position,
     and the sample is spread evenly, so its mean matches the whole run's)."""
     from threadpoolctl import threadpool_info
@@ -199,10 +200,15 @@ def cpu_baseline_prefill(wl, step, seconds_target=15.0):
     khat = R.dequant_mxfp4(ik_c, ik_s)
     scores = R.index_scores_fp4q if step.fp4q else R.index_scores
     order = np.random.default_rng(0).permutation(wl.Q)     # spread over the causal range
+    m = wl.m
+    w_ik = step.w_ik.float().cpu().numpy().astype(np.float64)
     done, t_total = 0, 0.0
     while t_total < seconds_target and done < len(order):
         q = int(order[done])
+        hq = step.h[0, q * m:(q + 1) * m].float().cpu().numpy().astype(np.float64)
+        zq = None if step.z is None else step.z[0, q * m:(q + 1) * m].float().cpu().numpy().astype(np.float64)
         t0 = time.perf_counter()
+        R.build_entries(hq, zq, m, w_ik)          # the query's own entry from its m raw tokens
         idx = None
         for li, mode in enumerate(wl.layers):
             L = step.layers[li]
@@ -218,8 +224,8 @@ def cpu_baseline_prefill(wl, step, seconds_target=15.0):
         done += 1
     threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
     return {"value": wl.m * done / t_total, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": f"{done} of {wl.Q} queries drawn evenly over the causal range, all "
-                      f"{len(wl.layers)} layers each, {t_total:.1f} s; m = {wl.m} raw tokens per "
+            "sample": f"{done} of {wl.Q} queries drawn evenly over the causal range, each its "
+                      f"entry's compression and all {len(wl.layers)} layers, {t_total:.1f} s; m = {wl.m} raw tokens per "
                       f"query; numpy fp64 (BLAS matmul on {threads} threads)"}
 
 
@@ -333,6 +339,8 @@ def main():
     whole = None if graphs is None else step.capture(split_first=False)[0]
     ops = step.ops()                      # built before any timed loop: the host only enqueues
     n_scans = sum(op.name == "index_score_full" for op in ops)
+    i_scan = step.scan_index()
+    g_pre = graphs[0] if graphs and i_scan > 0 else None     # calls before the scan (compressor)
 
     def scan_pass():
         """K steps with the Full-layer scans between HIP events; returns
@@ -347,7 +355,9 @@ def main():
             pairs = evs[si]
             if graphs:
                 e0, e1 = pairs[0]
-                e0.record(); ops[0].fn(); e1.record(); graphs[1].replay()
+                if g_pre is not None:
+                    g_pre.replay()
+                e0.record(); ops[i_scan].fn(); e1.record(); graphs[-1].replay()
             else:
                 j = 0
                 for op in ops:

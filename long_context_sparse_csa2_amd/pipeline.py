@@ -9,6 +9,10 @@ layer attends with the latest top-k indices and runs no indexer.  Section
 pool that the Reindex layers search.  Layers run one after another (layer
 l + 1's queries would depend on layer l's output in the model).
 
+A prefill step starts each chunk of queries by compressing the chunk's own
+raw tokens into its entries (steps a1-a3; query i is entry i and sees
+entries 0..i), so the compressor is timed with the rest of the step.
+
 A long encoder prefill (the commentary, section 4 item 4: the encoder's
 indexer stays quadratic, outside the hierarchy) runs its queries in chunks
 of `q_chunk`: per chunk, every layer scores the chunk's queries against
@@ -56,8 +60,16 @@ class Step:
         self.device = device
         self.fp4q = fp4q
         if cache is None:
-            cache, _ = build_cache(wl, device)
+            cache, w_ik = build_cache(wl, device)
+        else:
+            w_ik = wl.w_ik(device)
         self.cache = cache
+        self.w_ik = w_ik
+        # a prefill keeps its raw latents: each chunk compresses its own tokens
+        self.h = self.z = None
+        if wl.prefill:
+            assert wl.B == 1, "a prefill workload is one sequence"
+            self.h, self.z = wl.latents(device)
         g = wl.query_geometry()
         self.q_seq = g["q_seq"].to(device)
         self.n_vis = g["n_vis"].to(device)
@@ -100,6 +112,11 @@ class Step:
             swa_start, swa_len = self.swa_start[rows], self.swa_len[rows]
             scores, idx_full = self.scores[:n], self.idx[:n]
             idx = idx_full
+            if wl.prefill:
+                m = wl.m
+                out.append(Op("compress", -1, lambda i0=i0, i1=i1: csa2_compress_quant(
+                    self.h[:, i0 * m:i1 * m], None if self.z is None else self.z[:, i0 * m:i1 * m],
+                    m, self.w_ik, self.cache, e0=i0), (i0, i1)))
             for li, mode in enumerate(wl.layers):
                 L = {key: v[rows] if key in ("q_idx", "w", "q_attn") else v
                      for key, v in self.layers[li].items()}
@@ -172,12 +189,21 @@ class Step:
                                                                 device=self.device)
                     self.scores_per_layer[li][dst] = src.index_select(0, src_rows)
 
+    def scan_index(self):
+        """Position of the (first) Full-layer scan among the step's calls."""
+        return next(i for i, op in enumerate(self.ops()) if op.name == "index_score_full")
+
     def capture(self, split_first=True):
-        """Capture the step into HIP graphs: [first call] and [the rest]
-        (split_first) or one graph.  Returns the list of graphs; replaying
-        them in order is one step."""
+        """Capture the step into HIP graphs: [the calls before the first
+        scan] (when there are any), [that scan] and [the rest] (split_first),
+        or one graph.  Returns the list of graphs; replaying them in order is
+        one step."""
         ops = self.ops()
-        groups = [ops[:1], ops[1:]] if split_first else [ops]
+        if split_first:
+            i = self.scan_index()
+            groups = ([ops[:i]] if i > 0 else []) + [ops[i:i + 1], ops[i + 1:]]
+        else:
+            groups = [ops]
         graphs = []
         side = torch.cuda.Stream()
         side.wait_stream(torch.cuda.current_stream())
