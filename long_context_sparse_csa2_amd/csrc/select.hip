@@ -102,18 +102,20 @@ __global__ __launch_bounds__(256) void k_maxima(const float* __restrict__ scores
 // The candidates of one round (PER slots per lane, at most NT * PER, in id
 // order) live in registers slot-major: slot i of lane l in wave w holds
 // candidate c = 64 PER w + 64 i + l, with key 0 for "no candidate" (no fp32
-// value maps to key 0).  The candidates of one slot across a wave are then consecutive,
-// so an order-preserving compaction is a ballot and a masked bit count per
-// slot, and the only block-wide step is a prefix over per-wave totals.  A
-// round's block-wide bookkeeping (histogram scans) runs in one wave while
-// the others wait at the barrier.
+// value maps to key 0).  The candidates of one slot across a wave are then
+// consecutive, so an order-preserving compaction is a ballot and a masked
+// bit count per slot, and the only block-wide step is a prefix over per-wave
+// totals.  A round's block-wide bookkeeping (histogram scans) runs in one
+// wave while the others wait at the barrier.
 //
 // Floor.  A round keeps its best kk parents; each kept parent's maximum
 // child has the parent's key, so when the next round wants at most as many
 // as were kept, its answer lies among the children whose key is at least
-// the smallest kept key (the floor), and the children below it are dropped
-// before the threshold search.  The children's keys then lie between the
-// floor and the best parent's key, so that round needs no min / max pass.
+// the smallest kept key (the floor).  That round searches its threshold
+// between the floor and the best parent's key: those bounds are known, so it
+// needs no min / max pass, and children below the floor keep their keys but
+// fall outside the bounds, so neither the histogram nor the compaction
+// counts them.
 constexpr int SEL_PER = 16;                        // candidate slots per lane (small rounds)
 #ifndef SEL_NT
 #define SEL_NT 1024                                // threads of the 16,384-candidate selector
