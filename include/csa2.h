@@ -149,7 +149,7 @@ csa2_status csa2_compress_quant(const uint16_t* h, const uint16_t* z, int B, int
  *          cand[q][c] (c < n_vis[q]); entries must be in [0, cap).
  *   ld_cand  row stride of cand (ignored when cand is NULL)
  *   Q      queries
- *   n_cols (host) upper bound of n_vis[q], sets the launch size
+ *   n_cols (host) upper bound of n_vis[q], sets the launch size; < 2^29
  *   src    the cache
  *   scores [Q][ld] fp32; columns >= n_vis[q] are not written
  */

@@ -157,7 +157,8 @@ static csa2_status index_score_common(const uint16_t* q_idx, const float* w,
   const csa2_status cs = check_cache(src);
   if (cs != CSA2_OK) return cs;
   REQ(Q > 0, "Q=%d must be > 0", Q);
-  REQ(n_cols >= 0, "n_cols=%lld must be >= 0", (long long)n_cols);
+  REQ(n_cols >= 0 && n_cols < ((int64_t)1 << 29), "n_cols=%lld must be in [0, 2^29)",
+      (long long)n_cols);
   REQ(ld >= n_cols, "ld=%lld < n_cols=%lld", (long long)ld, (long long)n_cols);
   REQ(!cand || ld_cand >= n_cols, "ld_cand=%lld < n_cols=%lld", (long long)ld_cand,
       (long long)n_cols);

@@ -16,8 +16,8 @@
 // power-of-two E8M0 scales).  The ReLU, the
 // head weights and the head sum are applied to the accumulator in registers
 // and the two lane halves are summed with one cross-lane exchange, so only
-// 4 bytes per entry are written.  The next tile's bytes are loaded before
-// the current tile's MFMAs issue.
+// 4 bytes per entry are written.  Each wave keeps the bytes of its next two
+// tiles in flight while it converts and multiplies the current one.
 //
 // MXFP4-query variant (report section 2.4.4: V4 trains the indexer Q and K
 // for OCP MXFP4 so that the index product is an FP4 matrix multiply): the
@@ -144,6 +144,18 @@ __global__ __launch_bounds__(256) void k_index_score(
     scw = *(const uint32_t*)(ik_scales + (seq_base + e) * 4);
   };
 
+  // The score row as a buffer resource over its nv valid columns: the
+  // hardware drops a buffer store at an offset past nv * 4 bytes, so the
+  // lanes without a column of their own (the second lane half, and columns
+  // past the end) store without a branch, to offset 2^31 (nv * 4 < 2^31 is
+  // checked on the host).
+  // (readfirstlane: the resource must sit in scalar registers)
+  const uint64_t sp = (uint64_t)(uintptr_t)srow;
+  const uint64_t sp_u = (uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)sp) |
+                        ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(sp >> 32)) << 32);
+  const __amdgpu_buffer_rsrc_t srs = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(uintptr_t)sp_u, (short)0, __builtin_amdgcn_readfirstlane((int)(nv * 4)), 0x00020000);
+
   // ring of DEPTH + 1 tiles: slot t % (DEPTH + 1) holds tile t
   u32x4_t r0[DEPTH + 1], r1[DEPTH + 1];
   uint32_t rs[DEPTH + 1];
@@ -154,15 +166,15 @@ __global__ __launch_bounds__(256) void k_index_score(
     const int64_t c0 = col_first + t * step;
     if (t < TPW) load(c0, r0[t], r1[t], rs[t]);
   }
-#pragma unroll
-  for (int t = 0; t < TPW; ++t) {
+  auto tile = [&](int t) __attribute__((always_inline)) {
     const int64_t col0 = col_first + t * step;
-    if (col0 >= nv) break;
     {
       const int tn = t + DEPTH;
       const int64_t cn = col_first + tn * step;
       if (tn < TPW) load(cn, r0[tn % (DEPTH + 1)], r1[tn % (DEPTH + 1)], rs[tn % (DEPTH + 1)]);
     }
+    // keep those loads ahead of this tile's work
+    __builtin_amdgcn_sched_barrier(0);
     const int sl = t % (DEPTH + 1);
     const u32x4_t c0 = r0[sl], c1 = r1[sl];
     const uint32_t scw = rs[sl];
@@ -195,7 +207,22 @@ __global__ __launch_bounds__(256) void k_index_score(
     for (int j = 0; j < 16; ++j) part += wr[j] * relu_f32(acc[j]);
     part += __shfl_xor(part, 32);
     const int64_t c = col0 + r;
-    if (half == 0 && c < nv) srow[c] = part;
+    const int off = half == 0 && c < nv ? (int)(c * 4) : (int)0x80000000;
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(part), srs, off, 0, 0);
+  };
+  // A wave whose every tile starts before nv runs them with no branch in
+  // between, so the wait before each tile covers exactly that tile's loads
+  // (a branch per tile lets the compiler sink each tile's loads down to
+  // their use, and makes the waits conservative).
+  if (col_first + (int64_t)(TPW - 1) * step < nv) {
+#pragma unroll
+    for (int t = 0; t < TPW; ++t) tile(t);
+  } else {
+#pragma unroll
+    for (int t = 0; t < TPW; ++t) {
+      if (col_first + t * step >= nv) break;
+      tile(t);
+    }
   }
 }
 

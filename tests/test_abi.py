@@ -70,6 +70,10 @@ def test_index_score_validation(entry):
     assert f(P, P, P, P, None, 0, 1, 10, ctypes.byref(cs), P, 9, None) == 1
     assert f(P, P, P, P, None, 0, 1, 101, ctypes.byref(cs), P, 101, None) == 1
     assert f(P, P, P, P, P, 5, 1, 10, ctypes.byref(cs), P, 10, None) == 1
+    # a score row of 2^29 columns or more (the row is addressed in 32-bit bytes)
+    big = _cache(cap=1 << 30)
+    assert f(P, P, P, P, None, 0, 1, 1 << 29, ctypes.byref(big), P, 1 << 29, None) == 1
+    assert b"2^29" in L.csa2_last_error()
     # nothing to score: returns OK without launching
     assert f(P, P, P, P, None, 0, 1, 0, ctypes.byref(cs), P, 10, None) == 0
 
