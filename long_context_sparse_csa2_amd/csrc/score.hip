@@ -101,7 +101,10 @@ __global__ __launch_bounds__(256) void k_index_score(
   const int64_t cbase = (int64_t)(blockIdx.x % nchunk) * chunk_stride;
   const int64_t nv0 = n_vis[q];
   const int64_t nv = nv0 < n_cols ? nv0 : n_cols;     // never past the launch's columns
-  if (cbase >= nv) return;
+  // A candidate scan has no early exit: its candidate ids, sequence and query
+  // are then requested together with n_vis instead of one after the other
+  // (a workgroup past n_vis scores entry 0 and its stores are dropped).
+  if (!CAND && cbase >= nv) return;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int r = lane & 31, half = lane >> 5;
   const int64_t seq_base = (int64_t)q_seq[q] * cap;
@@ -136,8 +139,13 @@ __global__ __launch_bounds__(256) void k_index_score(
 
   auto load = [&](int64_t col0, u32x4_t& c0, u32x4_t& c1, uint32_t& scw) {
     const int64_t c = col0 + r;
-    const int64_t cc = c < nv ? c : nv - 1;           // past the end: re-read the last entry
-    const int64_t e = CAND ? (int64_t)crow[cc] : cc;
+    int64_t e;
+    if constexpr (CAND) {                             // id read within the launch's columns
+      const int32_t id = crow[c < n_cols ? c : n_cols - 1];
+      e = c < nv ? id : 0;                            // past n_vis: entry 0
+    } else {
+      e = c < nv ? c : nv - 1;                        // past the end: re-read the last entry
+    }
     const uint8_t* cp = ik_codes + (seq_base + e) * 64 + half * 32;
     c0 = *(const u32x4_t*)cp;
     c1 = *(const u32x4_t*)(cp + 16);
@@ -213,8 +221,9 @@ __global__ __launch_bounds__(256) void k_index_score(
   // A wave whose every tile starts before nv runs them with no branch in
   // between, so the wait before each tile covers exactly that tile's loads
   // (a branch per tile lets the compiler sink each tile's loads down to
-  // their use, and makes the waits conservative).
-  if (col_first + (int64_t)(TPW - 1) * step < nv) {
+  // their use, and makes the waits conservative).  A candidate scan always
+  // does: a branch on n_vis would hold its loads back until n_vis arrives.
+  if (CAND || col_first + (int64_t)(TPW - 1) * step < nv) {
 #pragma unroll
     for (int t = 0; t < TPW; ++t) tile(t);
   } else {
