@@ -59,15 +59,31 @@ __global__ __launch_bounds__(256, 1) void k_attend(
   const int hg = hq & 3, q = hq >> 2;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int r16 = lane & 15, qd = lane >> 4;
+  const int nmc = (k + CH_ROWS - 1) / CH_ROWS;
+  const int ch_beg = sp * cps;
+  // The first chunk's selected id (when it is a main-KV chunk) and the query
+  // rows go out before the query's sequence and window arrive: neither
+  // depends on them.
+  int id0 = -1;
+  if (ch_beg < nmc) {
+    const int r0 = ch_beg * CH_ROWS + (tid & 63);
+    id0 = idx[(int64_t)q * k + (r0 < k ? r0 : k - 1)];
+  }
+  const int qh = tid >> 4, qpart = tid & 15;     // query conversion: head, 32-dim part
+  bf16x8_t x[4];
+  {
+    const bf16x8_t* qp = (const bf16x8_t*)(qv + ((int64_t)q * H_ATT + hg * AT_HG + qh) * D_LAT +
+                                           qpart * 32);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) x[i] = qp[i];
+  }
   const int64_t seq = q_seq[q];
   const int64_t sst = swa_start[q];
   int64_t sl64 = swa_len[q];
   if (sst < 0 || sst >= T_swa) sl64 = 0;                     // ring: start must be a slot
   else if (sl64 > T_swa) sl64 = T_swa;                       // at most one lap
   const int sl = sl64 < 0 ? 0 : (sl64 > AT_MAX_SWA ? AT_MAX_SWA : (int)sl64);
-  const int nmc = (k + CH_ROWS - 1) / CH_ROWS;
   const int nch = nmc + (sl + CH_ROWS - 1) / CH_ROWS;
-  const int ch_beg = sp * cps;
   const int ch_end = min(ch_beg + cps, nch);
 
   // This thread's staging row (row t & 63 of chunk ch) in two steps: row_req
@@ -108,22 +124,17 @@ __global__ __launch_bounds__(256, 1) void k_attend(
     return off >= 0 ? off : (main_ch ? seq * cap : seq * T_swa + sst);
   };
   // the first chunk's row id, then its raw bytes, are in flight before the
-  // query work (the query bytes are requested in between)
-  const RowReq rq0 = row_req(ch_beg < ch_end ? ch_beg : 0);
+  // query work
+  const RowReq rq0 = ch_beg < nmc ? RowReq{id0, 1.f} : row_req(ch_beg < ch_end ? ch_beg : 0);
   float nsg = 1.f;
   int64_t noff = -1;
   RawShare<256> raw;
 
   // ---- query: thread t converts head t >> 4, dims 32 (t & 15) .. +31
   {
-    const int hh = tid >> 4, part = tid & 15;
-    const bf16x8_t* qp = (const bf16x8_t*)(qv + ((int64_t)q * H_ATT + hg * AT_HG + hh) * D_LAT +
-                                           part * 32);
-    bf16x8_t x[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) x[i] = qp[i];
-    // keep the query loads ahead of the wait for the row id (the scheduler
-    // would otherwise issue them after it)
+    const int hh = qh, part = qpart;
+    // keep the wait for the row id below the query loads (the scheduler
+    // would otherwise move the loads after it)
     __builtin_amdgcn_sched_barrier(0);
     if (ch_beg < ch_end) {
       noff = row_res(ch_beg, rq0, nsg);

@@ -36,24 +36,34 @@ struct LevelDesc {
 };
 
 // ------------------------------------------------------------ maxima
-// One workgroup per (query, 4096 columns): levels 1..4 of that span.
+// One workgroup per (query, 4096 columns): levels 1..4 of that span.  With
+// spec (few queries) a thread's 16 scores are requested before n_valid
+// arrives, when they lie within the launch's columns.
 __global__ __launch_bounds__(256) void k_maxima(const float* __restrict__ scores, int64_t ld,
                                                 const int64_t* __restrict__ n_valid,
                                                 int64_t n_cols, int64_t nchunk, LevelDesc d,
-                                                uint32_t* __restrict__ ws, int vec) {
+                                                uint32_t* __restrict__ ws, int vec, int spec) {
   __shared__ uint32_t wmax[4];
   const int q = (int)(blockIdx.x / nchunk);
   const int64_t chunk = blockIdx.x % nchunk;
-  const int64_t n0 = n_valid[q];
-  const int64_t n = n0 < n_cols ? n0 : n_cols;
-  if (chunk * 4096 >= n) return;
   const int tid = threadIdx.x;
   const int64_t c0 = chunk * 4096 + (int64_t)tid * 16;
   const float* sp = scores + (int64_t)q * ld;
+  const bool pre = spec && vec && c0 + 16 <= n_cols;
+  f32x4_t v0 = {}, v1 = {}, v2 = {}, v3 = {};
+  if (pre) {
+    const f32x4_t* vp = (const f32x4_t*)(sp + c0);
+    v0 = vp[0]; v1 = vp[1]; v2 = vp[2]; v3 = vp[3];
+  }
+  const int64_t n0 = n_valid[q];
+  const int64_t n = n0 < n_cols ? n0 : n_cols;
+  if (chunk * 4096 >= n) return;
   uint32_t k1a = 0, k1b = 0;
   if (vec && c0 + 16 <= n) {
-    const f32x4_t* vp = (const f32x4_t*)(sp + c0);
-    const f32x4_t v0 = vp[0], v1 = vp[1], v2 = vp[2], v3 = vp[3];
+    if (!pre) {
+      const f32x4_t* vp = (const f32x4_t*)(sp + c0);
+      v0 = vp[0]; v1 = vp[1]; v2 = vp[2]; v3 = vp[3];
+    }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       k1a = max(k1a, max(f32_key(v0[i]), f32_key(v1[i])));
@@ -586,7 +596,7 @@ hipError_t launch_select(const float* scores, int64_t ld, int Q, const int64_t* 
   const int spec = Q <= 64;                      // first loads ahead of n_valid
   if (d.nlev > 0 && nchunk > 0) {
     hipLaunchKernelGGL(k_maxima, dim3((unsigned)(nchunk * Q)), dim3(256), 0, stream, scores, ld,
-                       n_valid, n_cols, nchunk, d, (uint32_t*)ws, vec_max);
+                       n_valid, n_cols, nchunk, d, (uint32_t*)ws, vec_max, spec);
   }
   // one round over at most 4096 candidates: 256-thread workgroups, several per CU
   if (mode == 0 && n_cols <= 256 * SEL_PER) {
