@@ -114,6 +114,78 @@ def test_index_score_full_and_pool():
         assert np.all(p[i, lens[i]:] == -7.0)
 
 
+def _random_indexer_cache(B, cap, seed):
+    """A cache whose indexer K holds random E2M1 codes and E8M0 scales in
+    2^-7 .. 2^7 (the scan reads nothing else)."""
+    g = torch.Generator().manual_seed(seed)
+    cache = C.Cache(B, cap, DEV)
+    cache.ik_codes.copy_(torch.randint(0, 256, (B, cap, 64), generator=g, dtype=torch.uint8))
+    cache.ik_scales.copy_(torch.randint(120, 135, (B, cap, 4), generator=g, dtype=torch.uint8))
+    return cache
+
+
+@pytest.mark.parametrize("fp4q", [False, True])
+def test_index_score_long_ragged(fp4q):
+    # 600,000 columns for 3 queries: 8 tiles per wave and workgroups that
+    # interleave 128-column slices over the whole row, so a query whose
+    # visible count ends mid-row has waves with tiles on both sides of it
+    # (and one query sees nothing)
+    B, cap, Q, N = 2, 600_000, 3, 600_000
+    cache = _random_indexer_cache(B, cap, 91)
+    q, w = _scores_inputs(Q, 92)
+    q_seq = torch.tensor([0, 1, 0], dtype=torch.int32)
+    n_vis = [N - 13, 250_001, 0]
+    scores = torch.full((Q, N), -7.0, device=DEV)
+    C.csa2_index_score(q.to(DEV), w.to(DEV), q_seq.to(DEV), torch.tensor(n_vis, dtype=torch.int64).to(DEV),
+                       None, N, cache, scores, fp4q=fp4q)
+    torch.cuda.synchronize()
+    s = checks.host(scores)
+    codes, scl = checks.host(cache.ik_codes), checks.host(cache.ik_scales)
+    q64, w64 = checks.bf16_to_f64(q), w.double().numpy()
+    rng = np.random.default_rng(93)
+    for i in range(Q):
+        nv, b = n_vis[i], int(q_seq[i])
+        assert np.all(s[i, nv:] == -7.0)                 # columns past n_vis untouched
+        if nv == 0:
+            continue
+        cols = np.unique(np.concatenate([rng.choice(nv, 3000, replace=False), np.arange(min(nv, 64)),
+                                         np.arange(max(0, nv - 64), nv)]))
+        khat = R.dequant_mxfp4(codes[b][cols], scl[b][cols])
+        ref = (_oracle_scores_fp4q(q64[i], w64[i], khat) if fp4q
+               else R.index_scores(q64[i], w64[i], khat))
+        checks.check_scores(s[i, cols], ref)
+
+
+def test_index_score_candidates_multi_tile():
+    # 64 queries over 4,096 candidate columns: two tiles per wave, so
+    # workgroups and tiles past a query's candidate count score entry 0 and
+    # drop their stores; the padding ids past the count are -1
+    B, cap, Q, N = 2, 5000, 64, 4096
+    cache = _random_indexer_cache(B, cap, 94)
+    q, w = _scores_inputs(Q, 95)
+    rng = np.random.default_rng(96)
+    q_seq = (np.arange(Q) % B).astype(np.int32)
+    lens = rng.integers(0, N + 1, Q)
+    lens[:4] = [N, 0, 1, 33]
+    cand = np.full((Q, N), -1, dtype=np.int32)
+    for i in range(Q):
+        cand[i, :lens[i]] = rng.choice(cap, lens[i], replace=False)
+    ps = torch.full((Q, N), -7.0, device=DEV)
+    C.csa2_index_score(q.to(DEV), w.to(DEV), torch.from_numpy(q_seq).to(DEV),
+                       torch.from_numpy(lens.astype(np.int64)).to(DEV), torch.from_numpy(cand).to(DEV),
+                       N, cache, ps)
+    torch.cuda.synchronize()
+    p = checks.host(ps)
+    codes, scl = checks.host(cache.ik_codes), checks.host(cache.ik_scales)
+    q64, w64 = checks.bf16_to_f64(q), w.double().numpy()
+    for i in range(Q):
+        n, b = int(lens[i]), int(q_seq[i])
+        assert np.all(p[i, n:] == -7.0)
+        if n:
+            ids = cand[i, :n]
+            checks.check_scores(p[i, :n], R.index_scores(q64[i], w64[i], R.dequant_mxfp4(codes[b][ids], scl[b][ids])))
+
+
 def _fp4q_special_queries(Q, seed):
     """Indexer queries that exercise the MXFP4 query quantiser: per-block
     magnitudes spread over 2^-30 .. 2^20, exact E2M1 ties (0.25, 0.75, 1.25,
