@@ -307,6 +307,13 @@ def test_index_score_many_queries():
         if nv:
             checks.check_scores(s[i, :nv], R.index_scores(q64[i], w64[i], khat[q_seq[i]][:nv]))
         assert np.all(s[i, nv:] == -7.0)
+    # a query's scores do not depend on the other queries of the launch
+    for lo, hi in ((0, 200), (100, 300)):
+        part = torch.full((hi - lo, 1008), -7.0, device=DEV)
+        C.csa2_index_score(q[lo:hi].to(DEV), w[lo:hi].to(DEV), torch.from_numpy(q_seq[lo:hi]).to(DEV),
+                           torch.from_numpy(n_vis[lo:hi]).to(DEV), None, T, cache, part)
+        torch.cuda.synchronize()
+        assert np.array_equal(checks.host(part).view(np.uint32), s[lo:hi].view(np.uint32))
 
 
 def _rand_scores(Q, n, seed, ties=True):
