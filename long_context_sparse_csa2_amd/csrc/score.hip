@@ -174,16 +174,17 @@ __global__ __launch_bounds__(256) void k_index_score(
     const int64_t c0 = col_first + t * step;
     if (t < TPW) load(c0, r0[t], r1[t], rs[t]);
   }
-  auto tile = [&](int t) __attribute__((always_inline)) {
+  // tile t from ring slot sl (= t mod (DEPTH + 1), a constant wherever this
+  // is called); pf: first request tile t + DEPTH into its slot (a column
+  // past nv re-reads the last entry, so any tile index is safe to request)
+  auto tile = [&](int t, int sl, bool pf) __attribute__((always_inline)) {
     const int64_t col0 = col_first + t * step;
-    {
-      const int tn = t + DEPTH;
-      const int64_t cn = col_first + tn * step;
-      if (tn < TPW) load(cn, r0[tn % (DEPTH + 1)], r1[tn % (DEPTH + 1)], rs[tn % (DEPTH + 1)]);
+    if (pf) {
+      const int sn = (sl + DEPTH) % (DEPTH + 1);
+      load(col_first + (int64_t)(t + DEPTH) * step, r0[sn], r1[sn], rs[sn]);
     }
     // keep those loads ahead of this tile's work
     __builtin_amdgcn_sched_barrier(0);
-    const int sl = t % (DEPTH + 1);
     const u32x4_t c0 = r0[sl], c1 = r1[sl];
     const uint32_t scw = rs[sl];
     f32x16_t acc = {};
@@ -223,15 +224,26 @@ __global__ __launch_bounds__(256) void k_index_score(
   // (a branch per tile lets the compiler sink each tile's loads down to
   // their use, and makes the waits conservative).  A candidate scan always
   // does: a branch on n_vis would hold its loads back until n_vis arrives.
+  // A wave that reaches nv (a causal prefill row) runs its ntv tiles in
+  // branch-free groups of DEPTH + 1 (one turn of the ring, so the slots stay
+  // constants), then the last ntv mod (DEPTH + 1) tiles one by one; those
+  // were requested within the groups already.
   if (CAND || col_first + (int64_t)(TPW - 1) * step < nv) {
 #pragma unroll
-    for (int t = 0; t < TPW; ++t) tile(t);
+    for (int t = 0; t < TPW; ++t) tile(t, t % (DEPTH + 1), t + DEPTH < TPW);
   } else {
+    constexpr int G = DEPTH + 1;
+    const int64_t rem = nv - col_first;
+    const int64_t nt64 = rem <= 0 ? 0 : (rem + step - 1) / step;
+    const int ntv = nt64 < TPW ? (int)nt64 : TPW;
+    int t0 = 0;
+    for (; t0 + G <= ntv; t0 += G) {
 #pragma unroll
-    for (int t = 0; t < TPW; ++t) {
-      if (col_first + t * step >= nv) break;
-      tile(t);
+      for (int i = 0; i < G; ++i) tile(t0 + i, i, true);
     }
+#pragma unroll
+    for (int i = 0; i + 1 < G; ++i)
+      if (t0 + i < ntv) tile(t0 + i, i, false);
   }
 }
 
