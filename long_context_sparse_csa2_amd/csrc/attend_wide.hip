@@ -56,7 +56,7 @@ __global__ __launch_bounds__(AW_THREADS, 2) void k_attend_wide(
   __shared__ int moved_w[4];                                       // a wave's heads moved their max
   __shared__ f32x2_t rcs[ROPE_MAX_PAIRS];                          // RoPE (cos, sin) per pair
 
-  const int q = blockIdx.x;
+  const int q = gridDim.x - 1 - blockIdx.x;        // last queries (most rows when causal) first
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int r16 = lane & 15, qd = lane >> 4;
   const int head = 16 * wave + r16;                      // S^T and softmax: this lane's head

@@ -97,7 +97,10 @@ __global__ __launch_bounds__(256) void k_index_score(
     int64_t tile_stride, int64_t n_cols,
     const uint8_t* __restrict__ ik_codes, const uint8_t* __restrict__ ik_scales, int64_t cap,
     float* __restrict__ scores, int64_t ld) {
-  const int q = (int)(blockIdx.x / nchunk);
+  // the first workgroups take the last queries: in a causal prefill chunk
+  // they see the most entries, and starting the longest work first keeps it
+  // out of the kernel's tail
+  const int q = (int)(gridDim.x / nchunk - 1 - blockIdx.x / nchunk);
   const int64_t cbase = (int64_t)(blockIdx.x % nchunk) * chunk_stride;
   const int64_t nv0 = n_vis[q];
   const int64_t nv = nv0 < n_cols ? nv0 : n_cols;     // never past the launch's columns

@@ -44,7 +44,7 @@ __global__ __launch_bounds__(256) void k_maxima(const float* __restrict__ scores
                                                 int64_t n_cols, int64_t nchunk, LevelDesc d,
                                                 uint32_t* __restrict__ ws, int vec, int spec) {
   __shared__ uint32_t wmax[4];
-  const int q = (int)(blockIdx.x / nchunk);
+  const int q = (int)(gridDim.x / nchunk - 1 - blockIdx.x / nchunk);   // last queries first
   const int64_t chunk = blockIdx.x % nchunk;
   const int tid = threadIdx.x;
   const int64_t c0 = chunk * 4096 + (int64_t)tid * 16;
@@ -384,7 +384,7 @@ __global__ __launch_bounds__(NT, (NT <= 256 ? 5 : 1)) void k_select(
     const uint32_t* __restrict__ ws, int kk, int mode, int32_t* __restrict__ out, int64_t out_ld,
     int64_t* __restrict__ out_len, int k2, int32_t* __restrict__ out2, int vec_out, int spec) {
   __shared__ SelShared<NT> sh;
-  const int q = blockIdx.x;
+  const int q = gridDim.x - 1 - blockIdx.x;        // last queries (most columns when causal) first
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const float* srow = scores + (int64_t)q * ld;
   int32_t* orow = out + (int64_t)q * out_ld;
