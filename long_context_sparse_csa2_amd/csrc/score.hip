@@ -13,11 +13,11 @@
 // scan; each lane streams 32 contiguous bytes of one entry's MXFP4 codes
 // (its half of the 128 dims) plus the entry's 4 scale bytes, and converts
 // them to bf16 with the gfx950 scaled FP4 conversion (exact for the
-// power-of-two E8M0 scales).  The ReLU, the
-// head weights and the head sum are applied to the accumulator in registers
-// and the two lane halves are summed with one cross-lane exchange, so only
-// 4 bytes per entry are written.  Each wave keeps the bytes of its next two
-// tiles in flight while it converts and multiplies the current one.
+// power-of-two E8M0 scales).  The ReLU, the head weights and the head sum
+// are applied to the accumulator in registers and the two lane halves are
+// summed with one cross-lane exchange, so only 4 bytes per entry are
+// written.  Each wave keeps the bytes of its next two tiles in flight while
+// it converts and multiplies the current one.
 //
 // MXFP4-query variant (report section 2.4.4: V4 trains the indexer Q and K
 // for OCP MXFP4 so that the index product is an FP4 matrix multiply): the
@@ -38,6 +38,10 @@
 namespace csa2 {
 
 constexpr int SC_WAVES = 4;
+// Fourth word of a raw (unformatted, stride 0) buffer resource on gfx9:
+// 32-bit data format, so a store is range-checked in bytes against the
+// resource's record count.
+constexpr int SC_RSRC_WORD3 = 0x00020000;
 
 typedef int i32x8_t __attribute__((ext_vector_type(8)));
 
@@ -165,7 +169,7 @@ __global__ __launch_bounds__(256) void k_index_score(
   const uint64_t sp_u = (uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)sp) |
                         ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(sp >> 32)) << 32);
   const __amdgpu_buffer_rsrc_t srs = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(uintptr_t)sp_u, (short)0, __builtin_amdgcn_readfirstlane((int)(nv * 4)), 0x00020000);
+      (void*)(uintptr_t)sp_u, (short)0, __builtin_amdgcn_readfirstlane((int)(nv * 4)), SC_RSRC_WORD3);
 
   // ring of DEPTH + 1 tiles: slot t % (DEPTH + 1) holds tile t
   u32x4_t r0[DEPTH + 1], r1[DEPTH + 1];
