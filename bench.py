@@ -294,8 +294,8 @@ def main():
                     help="only run a plain 1 GiB device copy (reference for HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
-              "the path would shard by sequence across GPUs, which is not built here",
+        print(f"bench.py: the library runs on one GPU only (asked for --gpus {args.gpus}); "
+              "the path would shard by sequence across GPUs, which is not implemented",
               file=sys.stderr)
         sys.exit(2)
 
