@@ -448,6 +448,36 @@ def test_block_pool(n):
         checks.check_topk_exact(checks.host(topk[i]), s[i, :nv[i]], 512)
 
 
+def test_select_and_pool_many_queries():
+    # more than 64 queries: the selection waits for n_valid before its first
+    # loads and the maxima pyramid is built without speculation; ragged
+    # visible counts on both sides of the one-round capacity (16,384), an
+    # empty row and a full one; the workgroups take the rows last-first
+    Q, n = 80, 40000
+    s = _rand_scores(Q, n, seed=81)
+    rng = np.random.default_rng(82)
+    nv = rng.integers(1, n + 1, Q)
+    nv[:4] = [n, 0, 16384, 16385]
+    nv = [int(x) for x in nv]
+    out = _topk(s, nv, 512)
+    for i in range(Q):
+        if nv[i] == 0:
+            assert np.all(out[i] == -1)
+        else:
+            checks.check_topk_exact(out[i], s[i, :nv[i]], 512)
+    nvp = [max(1, x) for x in nv]
+    ws = C.workspace(C.CSA2_OP_POOL, Q, n, 2048, DEV)
+    pool = torch.empty(Q, 16384, dtype=torch.int32, device=DEV)
+    plen = torch.empty(Q, dtype=torch.int64, device=DEV)
+    topk = torch.empty(Q, 512, dtype=torch.int32, device=DEV)
+    C.csa2_block_pool(torch.from_numpy(s).to(DEV), torch.tensor(nvp, dtype=torch.int64).to(DEV), n,
+                      2048, pool, plen, ws, topk=topk)
+    torch.cuda.synchronize()
+    for i in range(Q):
+        checks.check_pool_exact(checks.host(pool[i]), checks.host(plen[i]), s[i, :nvp[i]], 8, 2048)
+        checks.check_topk_exact(checks.host(topk[i]), s[i, :nvp[i]], 512)
+
+
 def test_block_pool_small_blocks_and_topk():
     # few blocks, k equal to the block count, heavy ties
     Q, n = 2, 5000
