@@ -146,7 +146,9 @@ csa2_status csa2_compress_quant(const uint16_t* h, const uint16_t* z, int B, int
  *   n_vis  [Q] int64           columns to score for each query (<= n_cols)
  *   cand   NULL: column c scores entry c (c < n_vis[q]).
  *          else [Q][ld_cand] int32 entry ids: column c scores entry
- *          cand[q][c] (c < n_vis[q]); entries must be in [0, cap).
+ *          cand[q][c] (c < n_vis[q]); entries must be in [0, cap).  Ids at
+ *          columns n_vis[q] .. n_cols-1 may hold anything (e.g. -1 padding):
+ *          they may be read but are never used.
  *   ld_cand  row stride of cand (ignored when cand is NULL)
  *   Q      queries
  *   n_cols (host) upper bound of n_vis[q], sets the launch size; < 2^29
