@@ -248,16 +248,18 @@ def quant_swa_row(x):
     """FP8 SWA row: E4M3FN codes with one fp32 scale per row.  The V4 page
     (Fig. 6, KV cache layout) keeps the SWA entries of the most recent
     n_win tokens in each request's state block; the pages name the format
-    only as FP8.  Reading: sigma = max|x| / 448 and code = RNE_E4M3FN(x /
-    sigma), both quotients rounded to fp32 (the precision the kernel takes
-    this decision in); an all-zero row stores sigma = 0 and +0 codes.
+    only as FP8.  Reading: the row scale sigma = max|x| / 448 is stored as
+    an fp32 number (the exact quotient rounded to nearest, ties to even),
+    and each code is RNE_E4M3FN(x / sigma) of the exact quotient by that
+    stored scale, saturating at 448, so that sigma * e best approximates x;
+    an all-zero row stores sigma = 0 and +0 codes.  Evaluated in fp64.
     x [.., 512] -> (codes [.., 512] u8, sigma [..] fp32)."""
-    x32 = np.asarray(x, dtype=np.float32)
-    amax = np.abs(x32).max(axis=-1)
-    sig = (amax / np.float32(448.0)).astype(np.float32)
-    safe = np.where(sig > 0, sig, np.float32(1.0)).astype(np.float32)
-    v = (x32 / safe[..., None]).astype(np.float32)
-    codes = np.where(sig[..., None] > 0, F.e4m3fn_encode(v.astype(np.float64)), 0)
+    x = np.asarray(x, dtype=np.float64)
+    amax = np.abs(x).max(axis=-1)
+    sig = np.asarray(amax / 448.0).astype(np.float32)        # the stored fp32 scale
+    s64 = sig.astype(np.float64)
+    safe = np.where(s64 > 0, s64, 1.0)
+    codes = np.where(s64[..., None] > 0, F.e4m3fn_encode(x / safe[..., None]), 0)
     return codes.astype(np.uint8), sig
 
 

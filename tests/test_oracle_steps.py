@@ -256,7 +256,8 @@ def test_fp4q_error_bound():
 
 # ------------------------------------------------------------------ f2
 def test_swa_row_worked_example():
-    """FP8 SWA row: sigma = max|x| / 448 in fp32, codes RNE_E4M3FN(x / sigma)."""
+    """FP8 SWA row: sigma = max|x| / 448 stored in fp32, codes
+    RNE_E4M3FN(x / sigma) of the exact quotient."""
     x = np.zeros(512)
     x[:5] = [3.5, -1.75, 2.0 ** -7, 0.3, -0.0]
     c, sg = R.quant_swa_row(x)
@@ -277,8 +278,9 @@ def test_swa_row_worked_example():
 
 
 def test_swa_row_nearest_brute_force():
-    """Every code is a nearest E4M3FN value of fp32(x / sigma), ties to the
-    even code, with sigma = fp32(max|x| / 448)."""
+    """Every code is a nearest E4M3FN value of the exact quotient x / sigma,
+    ties to the even code, with sigma the fp32 number nearest max|x| / 448
+    (numpy's fp32 division of fp32 inputs is correctly rounded)."""
     rng = np.random.default_rng(22)
     rows = rng.standard_normal((8, 512)).astype(np.float32)
     c, sg = R.quant_swa_row(rows)
@@ -286,12 +288,33 @@ def test_swa_row_nearest_brute_force():
     allv = F.e4m3fn_value(allc)
     fin = ~np.isnan(allv)
     for r in range(8):
-        assert sg[r] == np.float32(np.abs(rows[r]).max() / np.float32(448))
-        v = (rows[r] / sg[r]).astype(np.float32).astype(np.float64)
-        d = np.abs(v[:, None] - allv[None, fin])
+        assert sg[r] == np.abs(rows[r]).max() / np.float32(448)
+        v = rows[r].astype(np.float64) / np.float64(sg[r])
+        d = np.abs(np.abs(v)[:, None] - np.abs(allv[None, fin]))
         best = d.min(axis=1)
-        got = np.abs(v - F.e4m3fn_value(c[r]))
+        got = np.abs(np.abs(v) - np.abs(F.e4m3fn_value(c[r])))
         assert np.array_equal(got, best)
+        assert np.all((c[r] >= 0x80) == (v < 0))
+
+
+def test_swa_row_exact_quotient():
+    """The code is taken from the exact quotient, not from a rounded one:
+    with sigma = 2^-7 (a row maximum of 3.5) the element 2^-7 * (38 - 2^-20)
+    lies just below the midpoint 38 of the E4M3 values 36 (code 0x61) and 40
+    (code 0x62), so it rounds down to 36, although its quotient rounded to
+    fp32 (a precision of 2^-18 there) would be exactly 38, which goes to the
+    even code, 40."""
+    x = np.zeros(512)
+    x[0] = 3.5
+    x[1] = 2.0 ** -7 * (38.0 - 2.0 ** -20)
+    c, sg = R.quant_swa_row(x)
+    assert sg == np.float32(2.0 ** -7)
+    assert c[1] == 0x61
+    assert np.float32(x[1] / 2.0 ** -7) == 38.0       # what an fp32 quotient would see
+    x[1] = 2.0 ** -7 * 38.0                           # the midpoint itself: even code
+    assert R.quant_swa_row(x)[0][1] == 0x62
+    x[1] = 2.0 ** -7 * (38.0 + 2.0 ** -20)            # just above it
+    assert R.quant_swa_row(x)[0][1] == 0x62
 
 
 def test_append_matches_batch_build():
@@ -503,3 +526,44 @@ def test_gather_rows_skips_padding_and_appends_swa():
     assert rows.shape == (5, 512)
     assert np.array_equal(rows[0], R.dequant_main_kv(c[4], s[4]))
     assert np.array_equal(rows[3], F.e4m3fn_value(swa_c[1]) * 2.0)
+
+
+# --------------------------------------------------- a1-a3 together
+def test_build_entries_projects_the_stored_entry():
+    """Hand-worked entry (tests/golden/xhat_projection_example.json): the
+    indexer K is projected from the dequantised main KV, whose channel 1 is
+    1.0 where the raw latent holds 0.9, and the two readings give different
+    MXFP4 bytes."""
+    import json
+    import os
+    G = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "xhat_projection_example.json")))
+    h = np.zeros((1, 512))
+    for c, v in G["h_nonzero"].items():
+        h[0, int(c)] = v
+    w_ik = np.zeros((128, 512))
+    for d, c, v in G["w_ik_nonzero"]:
+        w_ik[d, c] = v
+    e = R.build_entries(h, None, 1, w_ik)
+    assert e["kv_codes"][0, 0] == G["kv_codes_byte0"] and np.all(e["kv_codes"][0, 1:] == 0)
+    assert e["kv_scales"][0, 0] == G["kv_scales_byte0"] and np.all(e["kv_scales"][0, 1:] == 0)
+    want_ik = np.zeros(64, np.uint8)
+    for b, v in G["ik_codes"].items():
+        want_ik[int(b)] = v
+    assert np.array_equal(e["ik_codes"][0], want_ik)
+    assert e["ik_scales"][0].tolist() == G["ik_scales"]
+    khat = R.dequant_mxfp4(e["ik_codes"], e["ik_scales"])
+    assert khat[0, 0] == G["khat0"] and np.all(khat[0, 1:] == 0)
+    assert khat[0, 0] != G["khat0_if_x_were_projected"]
+
+
+def test_kth_score_by_hand():
+    """The k-th best score of small lists worked by hand: ties count once per
+    candidate, and k beyond the list gives its smallest score."""
+    s = [3.0, 1.0, 4.0, 1.0, 5.0, 9.0, 2.0, 6.0]
+    assert R.kth_score(s, 1) == 9.0
+    assert R.kth_score(s, 3) == 5.0            # 9, 6, 5
+    assert R.kth_score(s, 7) == 1.0            # 9 6 5 4 3 2 1
+    assert R.kth_score(s, 100) == 1.0
+    assert R.kth_score([2.0, 2.0, 2.0, 1.0], 2) == 2.0
+    assert R.kth_score([2.0, 2.0, 2.0, 1.0], 4) == 1.0
+    assert R.kth_score([-1.0, 0.5, -3.0], 2) == -1.0
