@@ -23,8 +23,9 @@
  *     and sets csa2_last_error().  Launch failures return CSA2_EHIP.
  *   - The contents of device arrays (indices, cache bytes) are not checked;
  *     out-of-range indices are undefined behaviour.  With CSA2_CHECK=1 in
- *     the environment, csa2_index_score (q_seq >= 0, candidate ids in
- *     [0, cap)) and csa2_sparse_attend (q_seq >= 0, idx in [-1, cap)) first
+ *     the environment, csa2_index_score (q_seq in [0, batch), or >= 0 when
+ *     batch is 0; candidate ids in [0, cap)) and csa2_sparse_attend (q_seq
+ *     likewise, idx in [-1, cap)) first
  *     range-check their index arrays on the device, synchronise the stream
  *     and return CSA2_EINVAL naming the array if any value is out of range
  *     (checked calls are synchronous and must not be graph-captured).
@@ -80,6 +81,8 @@ typedef struct {
   uint8_t* ik_codes;
   uint8_t* ik_scales;
   int64_t cap;            /* entries per sequence (the batch stride) */
+  int64_t batch;          /* sequences the arrays hold; 0 = not stated.  Used
+                             only by the CSA2_CHECK range check of q_seq.  */
 } csa2_cache;
 
 /* Per-sequence decode state of one KV-producing layer (host struct holding

@@ -32,7 +32,7 @@ class Csa2Error(RuntimeError):
 class _Cache(ctypes.Structure):
     _fields_ = [("kv_codes", ctypes.c_void_p), ("kv_scales", ctypes.c_void_p),
                 ("ik_codes", ctypes.c_void_p), ("ik_scales", ctypes.c_void_p),
-                ("cap", ctypes.c_int64)]
+                ("cap", ctypes.c_int64), ("batch", ctypes.c_int64)]
 
 
 class _Rope(ctypes.Structure):
@@ -127,7 +127,7 @@ class Cache:
 
     def c_struct(self):
         return _Cache(self.kv_codes.data_ptr(), self.kv_scales.data_ptr(),
-                      self.ik_codes.data_ptr(), self.ik_scales.data_ptr(), self.cap)
+                      self.ik_codes.data_ptr(), self.ik_scales.data_ptr(), self.cap, self.B)
 
     def view(self, b0, b1):
         """The same cache restricted to sequences b0..b1-1 (no copy)."""

@@ -41,6 +41,7 @@ csa2_status check_cache(const csa2_cache* c) {
       !al(c->ik_scales, 16))
     return fail(CSA2_EINVAL, "cache arrays must be 16-byte aligned");
   if (c->cap <= 0) return fail(CSA2_EINVAL, "cache cap=%lld must be > 0", (long long)c->cap);
+  if (c->batch < 0) return fail(CSA2_EINVAL, "cache batch=%lld must be >= 0", (long long)c->batch);
   return CSA2_OK;
 }
 
@@ -168,7 +169,8 @@ static csa2_status index_score_common(const uint16_t* q_idx, const float* w,
   if (n_cols == 0) return CSA2_OK;
   REQ((n_cols + 1023) / 1024 * (int64_t)Q < (int64_t)1 << 31, "launch too large");
   if (device_checks()) {
-    CHECKED(check_indices("q_seq", q_seq, 1, Q, nullptr, Q, 0, INT32_MAX, stream));
+    CHECKED(check_indices("q_seq", q_seq, 1, Q, nullptr, Q, 0,
+                          src->batch > 0 ? src->batch : (int64_t)INT32_MAX, stream));
     if (cand)
       CHECKED(check_indices("cand", cand, Q, ld_cand, n_vis, n_cols, 0, src->cap, stream));
   }
@@ -262,7 +264,8 @@ static csa2_status attend_common(const uint16_t* q, const int32_t* q_seq, int Q,
   REQ(!ws || al(ws, 16), "ws must be 16-byte aligned");
   REQ(Q > 0 && Q <= (1 << 24), "Q=%d must be in [1, 2^24]", Q);
   if (device_checks()) {
-    CHECKED(check_indices("q_seq", q_seq, 1, Q, nullptr, Q, 0, INT32_MAX, stream));
+    CHECKED(check_indices("q_seq", q_seq, 1, Q, nullptr, Q, 0,
+                          src->batch > 0 ? src->batch : (int64_t)INT32_MAX, stream));
     if (k > 0) CHECKED(check_indices("idx", idx, Q, k, nullptr, k, -1, src->cap, stream));
   }
   return hip_status(csa2::launch_attend(q, q_seq, Q, src->kv_codes, src->kv_scales, src->cap, idx,

@@ -107,7 +107,9 @@ __global__ __launch_bounds__(256) void k_index_score(
   const int q = (int)(gridDim.x / nchunk - 1 - blockIdx.x / nchunk);
   const int64_t cbase = (int64_t)(blockIdx.x % nchunk) * chunk_stride;
   const int64_t nv0 = n_vis[q];
-  const int64_t nv = nv0 < n_cols ? nv0 : n_cols;     // never past the launch's columns
+  // within [0, n_cols]: never past the launch's columns, and a negative
+  // count scores nothing
+  const int64_t nv = nv0 < 0 ? 0 : (nv0 < n_cols ? nv0 : n_cols);
   // A candidate scan has no early exit: its candidate ids, sequence and query
   // are then requested together with n_vis instead of one after the other
   // (a workgroup past n_vis scores entry 0 and its stores are dropped).

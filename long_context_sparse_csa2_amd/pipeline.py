@@ -78,6 +78,10 @@ class Step:
         Q, N, k = wl.Q, wl.N, wl.k
         qc = wl.q_chunk if (wl.prefill and 0 < wl.q_chunk < Q) else Q
         self.chunks = [(i0, min(Q, i0 + qc)) for i0 in range(0, Q, qc)]
+        # the pool and its Reindex layers use whole-step arrays (one pool row
+        # per query), so a hierarchical workload runs as one chunk
+        assert not (wl.hierarchical and len(self.chunks) > 1), \
+            "a hierarchical workload cannot run in query chunks"
         self.layers = [wl.layer_inputs(li, device) for li in range(len(wl.layers))]
         self.scores = torch.empty(qc, N, dtype=torch.float32, device=device)
         self.idx = torch.empty(qc, k, dtype=torch.int32, device=device)

@@ -34,8 +34,8 @@ def test_status_strings():
     assert L.csa2_status_string(99) == b"CSA2_UNKNOWN"
 
 
-def _cache(cap=100, ptr=0x10000):
-    return C._Cache(ptr, ptr, ptr, ptr, cap)
+def _cache(cap=100, ptr=0x10000, batch=0):
+    return C._Cache(ptr, ptr, ptr, ptr, cap, batch)
 
 
 def test_compress_validation():
@@ -57,6 +57,10 @@ def test_compress_validation():
     assert b"aligned" in L.csa2_last_error()
     # m out of range
     assert L.csa2_compress_quant(FAKE, FAKE, 1, 34, 17, FAKE, ctypes.byref(cs), 0, None) == 1
+    # a negative batch count in the cache struct
+    neg = _cache(batch=-1)
+    assert L.csa2_compress_quant(FAKE, None, 1, 8, 1, FAKE, ctypes.byref(neg), 0, None) == 1
+    assert b"batch" in L.csa2_last_error()
 
 
 @pytest.mark.parametrize("entry", ["csa2_index_score", "csa2_index_score_fp4q"])

@@ -1,17 +1,20 @@
 """The five workloads at their full sizes, in the launch configuration
-bench.py times, checked against the fp64 oracle: every output the oracle
-can afford at that size is compared element by element, the rest on a
-seeded sample of entries / queries, stage by stage (each oracle stage takes
-the GPU's previous-stage result as input).
+bench.py times, checked against the fp64 oracle stage by stage (each oracle
+stage takes the GPU's previous-stage result as input).  Every score, every
+selection and every attention output is compared; only the compression of
+the decode caches (built before the step, not timed) is checked on a seeded
+sample of entries.
 
-c0  N = 2048, batch 1: everything, with full fp64 scores.
-c1  batch 32 x N = 65,536: full fp64 scores of every query.
-c2  batch 4 x N = 2^20, Full + pool + 4 Reindex: sampled Full-layer scores,
-    exact selections, every Reindex score, every attention output.
+c0  N = 2048, batch 1.
+c1  batch 32 x N = 65,536.
+c2  batch 4 x N = 2^20, Full + pool + 4 Reindex: all 2^20 fp64 scores of
+    every query, the Full top-512 and the 2048-block pool against the fp64
+    ranking (near-ties only may swap), every Reindex score and selection.
 c3  prefill, 8192 raw -> 4096 entries (m = 2), 4096 causal queries: every
     score and every top-k; attention on a sample of queries.
-c4  batch 8 x 2^19 entries from 2^20 raw (m = 2), Full + 5 Reuse: sampled
-    compression and scores, exact selections, every attention output.
+c4  batch 8 x 2^19 entries from 2^20 raw (m = 2), Full + 5 Reuse: all fp64
+    scores, the Full top-512 against the fp64 ranking, every attention
+    output.
 """
 import numpy as np
 import pytest
@@ -61,13 +64,13 @@ def _run(name):
 def test_c1_batched_full_decode():
     wl, step = _run("c1")
     _check_compression_sample(wl, step.cache, wl.w_ik(DEV), 512, seed=1)
-    checks.check_step(step, full_scores=True)
+    checks.check_step(step)
 
 
 def test_c2_hierarchical_1m_decode():
     wl, step = _run("c2")
     _check_compression_sample(wl, step.cache, wl.w_ik(DEV), 512, seed=2)
-    checks.check_step(step, full_scores=False, entry_sample=65536)
+    checks.check_step(step)
     # the Full layer's own top-512 lies inside its pool (report section 2.3.2)
     pool = checks.host(step.pool)
     full_idx = checks.host(step.idx_per_layer[0])
@@ -95,13 +98,13 @@ def test_c3_prefill_m2():
             checks.check_topk_exact(idx[q], s_gpu[q, :nv], wl.k)
             checks.check_topk_tolerance(idx[q], ref[i, :nv], wl.k)
     sample = sorted({0, 1, 2, 63, 64, 511, 512, 513, wl.Q - 1} | set(np.random.default_rng(3).integers(0, wl.Q, 24).tolist()))
-    checks.check_step(step, full_scores=True, q_sample=sample)
+    checks.check_step(step, q_sample=sample)
 
 
 def test_c4_reuse_decode_m2():
     wl, step = _run("c4")
     _check_compression_sample(wl, step.cache, wl.w_ik(DEV), 512, seed=4)
-    checks.check_step(step, full_scores=False, entry_sample=32768)
+    checks.check_step(step)
     # Reuse layers attend over the Full layer's indices
     for li in range(1, len(wl.layers)):
         assert torch.equal(step.idx_per_layer[li], step.idx_per_layer[0])
