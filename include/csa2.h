@@ -13,7 +13,8 @@
  * Conventions for every entry point
  *   - All array arguments are DEVICE pointers unless marked (host).  The
  *     caller owns every buffer; the library never allocates or frees device
- *     memory and keeps no state except a thread-local error string.
+ *     memory and keeps no state except a thread-local error string (and
+ *     the static scratch of csa2_select_topk_noalloc, one per GPU).
  *   - Every call enqueues its kernels on `stream` (a hipStream_t, may be 0
  *     for the null stream) and returns without synchronising.
  *   - bf16 values are passed as uint16_t bit patterns.
@@ -207,6 +208,25 @@ csa2_status csa2_index_score_fp4q(const uint16_t* q_idx, const float* w, const i
 csa2_status csa2_select_topk(const float* scores, int64_t ld, int Q, const int64_t* n_valid,
                              const int32_t* col_ids, int64_t n_cols, int k, int32_t* out,
                              void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * (3a') Per-query top-k without a workspace, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation).  Same selection, arguments,
+ * layouts and errors as csa2_select_topk; the maxima the selection keeps
+ * between its kernels go to a static scratch array of
+ * CSA2_NOALLOC_SCRATCH_BYTES inside the library, one per GPU, held until
+ * the process ends.  Calls whose Q x n_cols needs more scratch than that
+ * (csa2_workspace_bytes(CSA2_OP_TOPK, Q, n_cols, k) > the limit; e.g. up to
+ * 4 x 2^20 or 32 x 2^19 columns fit) return CSA2_EUNSUPPORTED.  The call
+ * allocates nothing.  Every call on one GPU shares that GPU's scratch:
+ * calls that overlap on one GPU (on different streams, or from several
+ * threads) race and must be ordered by the caller.
+ */
+#define CSA2_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)
+csa2_status csa2_select_topk_noalloc(const float* scores, int64_t ld, int Q,
+                                     const int64_t* n_valid, const int32_t* col_ids,
+                                     int64_t n_cols, int k, int32_t* out, void* stream);
 
 /*
  * (3b) Hierarchical candidate pool: step a6.

@@ -20,7 +20,7 @@ STATUS = {0: "CSA2_OK", 1: "CSA2_EINVAL", 2: "CSA2_EUNSUPPORTED", 3: "CSA2_EWORK
 EXPORTS = ("csa2_status_string", "csa2_last_error", "csa2_compress_quant", "csa2_index_score",
            "csa2_index_score_fp4q", "csa2_select_topk", "csa2_block_pool", "csa2_sparse_attend",
            "csa2_sparse_attend_rope", "csa2_decode_append", "csa2_workspace_bytes",
-           "csa2_selftest")
+           "csa2_selftest", "csa2_select_topk_noalloc")
 
 
 class Csa2Error(RuntimeError):
@@ -68,6 +68,8 @@ def lib():
             fn.argtypes = [P, P, P, P, P, I64, I, I64, ctypes.POINTER(_Cache), P, I64, P]
         L.csa2_select_topk.restype = I
         L.csa2_select_topk.argtypes = [P, I64, I, P, P, I64, I, P, P, SZ, P]
+        L.csa2_select_topk_noalloc.restype = I
+        L.csa2_select_topk_noalloc.argtypes = [P, I64, I, P, P, I64, I, P, P]
         L.csa2_block_pool.restype = I
         L.csa2_block_pool.argtypes = [P, I64, I, P, I64, I, I, P, P, I, P, P, SZ, P]
         L.csa2_sparse_attend.restype = I
@@ -216,6 +218,16 @@ def csa2_select_topk(scores, n_valid, col_ids, n_cols, k, out, ws=None, stream=N
     st = lib().csa2_select_topk(_ptr(scores), scores.shape[1], Q, _ptr(n_valid), _ptr(col_ids),
                                 n_cols, k, _ptr(out), _ptr(ws), wsb, _stream(stream, scores))
     _check("csa2_select_topk", st)
+
+
+def csa2_select_topk_noalloc(scores, n_valid, col_ids, n_cols, k, out, stream=None):
+    """csa2_select_topk without a workspace (the library's static scratch)."""
+    _dtype(scores, torch.float32, "scores"); _dtype(n_valid, torch.int64, "n_valid")
+    _dtype(col_ids, torch.int32, "col_ids"); _dtype(out, torch.int32, "out")
+    Q = scores.shape[0]
+    st = lib().csa2_select_topk_noalloc(_ptr(scores), scores.shape[1], Q, _ptr(n_valid),
+                                        _ptr(col_ids), n_cols, k, _ptr(out), _stream(stream, scores))
+    _check("csa2_select_topk_noalloc", st)
 
 
 def csa2_block_pool(scores, n_valid, n_cols, n_blocks, pool, pool_len, ws=None, block=8,

@@ -14,6 +14,9 @@
 
 #include "launch.h"
 
+static_assert(CSA2_NOALLOC_SCRATCH_BYTES == csa2::SEL_SCRATCH_BYTES,
+              "the header states the static scratch size");
+
 namespace {
 
 thread_local char g_err[512];
@@ -225,6 +228,35 @@ csa2_status csa2_select_topk(const float* scores, int64_t ld, int Q, const int64
   return hip_status(csa2::launch_select(scores, ld, Q, n_valid, col_ids, n_cols, k, 0, out, k,
                                         nullptr, 0, nullptr, ws, (hipStream_t)stream),
                     "csa2_select_topk launch");
+}
+
+csa2_status csa2_select_topk_noalloc(const float* scores, int64_t ld, int Q,
+                                     const int64_t* n_valid, const int32_t* col_ids,
+                                     int64_t n_cols, int k, int32_t* out, void* stream) {
+  g_err[0] = 0;
+  REQ(out, "out must not be NULL");
+  REQ(scores && n_valid, "scores and n_valid must not be NULL");
+  REQ(Q > 0, "Q=%d must be > 0", Q);
+  REQ(k >= 1 && k <= CSA2_MAX_K, "k=%d must be in [1, %d]", k, CSA2_MAX_K);
+  REQ(n_cols >= 0 && n_cols <= CSA2_MAX_COLS, "n_cols=%lld must be in [0, %d]",
+      (long long)n_cols, CSA2_MAX_COLS);
+  REQ(ld >= n_cols && ld > 0, "ld=%lld < n_cols=%lld", (long long)ld, (long long)n_cols);
+  REQ(al(scores, 4), "scores must be 4-byte aligned");
+  const size_t need = csa2::select_ws_bytes(Q, n_cols, 0);
+  if (need > csa2::SEL_SCRATCH_BYTES)
+    return fail(CSA2_EUNSUPPORTED,
+                "Q=%d x n_cols=%lld needs %zu bytes of scratch, more than the %zu-byte static "
+                "scratch of csa2_select_topk_noalloc (use csa2_select_topk with a workspace)",
+                Q, (long long)n_cols, need, csa2::SEL_SCRATCH_BYTES);
+  void* ptr = nullptr;
+  if (need > 0) {
+    const hipError_t e = csa2::select_scratch(&ptr);
+    if (e != hipSuccess)
+      return fail(CSA2_EHIP, "csa2_select_topk_noalloc scratch lookup: %s", hipGetErrorString(e));
+  }
+  return hip_status(csa2::launch_select(scores, ld, Q, n_valid, col_ids, n_cols, k, 0, out, k,
+                                        nullptr, 0, nullptr, ptr, (hipStream_t)stream),
+                    "csa2_select_topk_noalloc launch");
 }
 
 csa2_status csa2_block_pool(const float* scores, int64_t ld, int Q, const int64_t* n_valid,

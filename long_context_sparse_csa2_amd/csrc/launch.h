@@ -44,6 +44,10 @@ hipError_t launch_index_score(const uint16_t* q_idx, const float* w, const int32
 // Selection: mode 0 = top-k of columns (levels down to 0), mode 1 = block
 // pool (levels down to 1, blocks of 8).
 size_t select_ws_bytes(int Q, int64_t n_cols, int mode);
+// Bytes of the static scratch behind csa2_select_topk_noalloc, and its
+// device address on the current device (looked up on the first call there).
+constexpr size_t SEL_SCRATCH_BYTES = (size_t)16 << 20;
+hipError_t select_scratch(void** ptr);
 hipError_t launch_select(const float* scores, int64_t ld, int Q, const int64_t* n_valid,
                          const int32_t* col_ids, int64_t n_cols, int kk, int mode, int32_t* out,
                          int64_t out_ld, int64_t* out_len, int k2, int32_t* out2, void* ws,

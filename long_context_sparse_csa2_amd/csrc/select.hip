@@ -25,6 +25,8 @@
 #include "common.h"
 #include "launch.h"
 
+#include <mutex>
+
 namespace csa2 {
 
 constexpr int SEL_KK_MAX = 2048;
@@ -559,6 +561,37 @@ __global__ __launch_bounds__(NT, (NT <= 256 ? 5 : 1)) void k_select(
     const int want_next = (lvl == 0 && mode == 1) ? k2 : kk;
     floor_key = kept >= want_next ? (ro.all ? ro.mn : ro.lo) : 0u;
   }
+}
+
+// ------------------------------------------------------------ scratch
+// Static scratch of the allocation-free top-k entry point: the maxima
+// pyramid lives here instead of in a caller's workspace.  Every GPU the
+// library runs on holds its own copy until the process ends; its address is
+// looked up once per device (the host-side name is only a stand-in and must
+// never be passed to a kernel).  Nothing in it has to start at zero: the
+// maxima kernel writes every group a selection reads.
+static __device__ __align__(256) uint8_t scratch[SEL_SCRATCH_BYTES];
+
+namespace {
+constexpr int SEL_MAX_DEVICES = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[SEL_MAX_DEVICES] = {};
+}  // namespace
+
+hipError_t select_scratch(void** ptr) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= SEL_MAX_DEVICES) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return hipSuccess;
 }
 
 // ------------------------------------------------------------ host side

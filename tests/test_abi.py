@@ -102,6 +102,20 @@ def test_select_and_pool_validation():
     assert L.csa2_block_pool(P, 100, 1, P, 100, 8, 4, P, P, 3, None, P, 1 << 20, None) == 1
 
 
+def test_select_noalloc_validation():
+    """The allocation-free top-k validates like csa2_select_topk and refuses,
+    before any HIP call, a size whose maxima exceed its static scratch."""
+    L = C.lib()
+    P = FAKE
+    assert L.csa2_select_topk_noalloc(P, 100, 1, P, None, 100, 5, None, None) == 1
+    assert L.csa2_select_topk_noalloc(P, 100, 1, P, None, 100, 0, P, None) == 1
+    assert L.csa2_select_topk_noalloc(P, 100, 1, P, None, 101, 5, P, None) == 1
+    Q, n = 64, 1 << 19
+    assert C.csa2_workspace_bytes(C.CSA2_OP_TOPK, Q, n, 512) > 16 << 20
+    assert L.csa2_select_topk_noalloc(P, n, Q, P, None, n, 512, P, None) == 2
+    assert b"static" in L.csa2_last_error()
+
+
 def test_attend_validation():
     L = C.lib()
     cs = _cache()
