@@ -73,6 +73,8 @@ typedef enum {
 #define CSA2_OP_TOPK 1
 #define CSA2_OP_POOL 2
 #define CSA2_OP_ATTEND 3
+#define CSA2_OP_SELECT_ATTEND 4   /* csa2_select_attend, n_blocks == 0 */
+#define CSA2_OP_POOL_ATTEND 5     /* csa2_select_attend, n_blocks > 0  */
 
 /* One KV-producing layer's cache for B sequences (host struct holding device
  * pointers).  Every pointer must be 16-byte aligned. */
@@ -306,6 +308,40 @@ csa2_status csa2_sparse_attend(const uint16_t* q, const int32_t* q_seq, int Q, c
                                const int32_t* swa_len, float* out, float* lse, void* ws,
                                size_t ws_bytes, void* stream);
 
+/*
+ * (3 + 4 + 5) Selection fused with the gather and the attention, for decode
+ * batches: csa2_select_topk (n_blocks == 0) or csa2_block_pool with its
+ * top-k (n_blocks > 0) followed by csa2_sparse_attend over the selected
+ * entries, in one call whose kernels keep the selected ids on chip.  The
+ * report (section 3.2) fuses each layer's steps into few kernels; here
+ * every attention workgroup of a query repeats the query's (deterministic)
+ * selection instead of reading the ids back from memory.
+ *
+ * Outputs are those of the separate calls on the same inputs: idx (and
+ * pool, pool_len) exactly as csa2_select_topk / csa2_block_pool write them,
+ * out and lse as csa2_sparse_attend computes them over idx.
+ *
+ *   scores, ld, Q, n_valid, n_cols   as for csa2_select_topk; Q < 256
+ *   col_ids    as for csa2_select_topk; must be NULL when n_blocks > 0
+ *   k          1 <= k <= CSA2_MAX_K (and k <= n_blocks when n_blocks > 0)
+ *   idx        [Q][k] int32 selected entry ids, ascending, -1 padded
+ *   n_blocks   0 (plain top-k) or the pool's block count (blocks of 8)
+ *   pool, pool_len  as for csa2_block_pool (NULL when n_blocks == 0)
+ *   q, q_seq, src, swa_codes, swa_scale, T_swa, swa_start, swa_len, out,
+ *   lse        as for csa2_sparse_attend (the attended rows are idx)
+ *   ws         256-byte aligned, csa2_workspace_bytes(CSA2_OP_SELECT_ATTEND or
+ *              CSA2_OP_POOL_ATTEND, Q, n_cols, k) bytes (maxima levels and
+ *              the attention's partial states); calls sharing a workspace
+ *              must not overlap
+ */
+csa2_status csa2_select_attend(const float* scores, int64_t ld, int Q, const int64_t* n_valid,
+                               const int32_t* col_ids, int64_t n_cols, int k, int32_t* idx,
+                               int n_blocks, int32_t* pool, int64_t* pool_len, const uint16_t* q,
+                               const int32_t* q_seq, const csa2_cache* src,
+                               const uint8_t* swa_codes, const float* swa_scale, int64_t T_swa,
+                               const int64_t* swa_start, const int32_t* swa_len, float* out,
+                               float* lse, void* ws, size_t ws_bytes, void* stream);
+
 /* Rotary position embedding of csa2_sparse_attend_rope (host struct). */
 typedef struct {
   const int64_t* q_pos;   /* [Q] position of each query (device); may be NULL iff dims == 0 */
@@ -383,7 +419,8 @@ csa2_status csa2_decode_append(const uint16_t* h_new, const uint16_t* z_new,
 
 /* Workspace bytes an operation needs (0 if it needs none).
  *   op      CSA2_OP_TOPK (n_cols, k), CSA2_OP_POOL (n_cols, k = n_blocks),
- *           CSA2_OP_ATTEND (k = entries per query)
+ *           CSA2_OP_ATTEND (k = entries per query), CSA2_OP_SELECT_ATTEND and
+ *           CSA2_OP_POOL_ATTEND (n_cols, k = the top-k)
  */
 size_t csa2_workspace_bytes(int op, int Q, int64_t n_cols, int k);
 

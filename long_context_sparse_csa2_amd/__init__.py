@@ -16,11 +16,12 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libcsa2.so")
 
 CSA2_OP_TOPK, CSA2_OP_POOL, CSA2_OP_ATTEND = 1, 2, 3
+CSA2_OP_SELECT_ATTEND, CSA2_OP_POOL_ATTEND = 4, 5
 STATUS = {0: "CSA2_OK", 1: "CSA2_EINVAL", 2: "CSA2_EUNSUPPORTED", 3: "CSA2_EWORKSPACE", 4: "CSA2_EHIP"}
 EXPORTS = ("csa2_status_string", "csa2_last_error", "csa2_compress_quant", "csa2_index_score",
            "csa2_index_score_fp4q", "csa2_select_topk", "csa2_block_pool", "csa2_sparse_attend",
            "csa2_sparse_attend_rope", "csa2_decode_append", "csa2_workspace_bytes",
-           "csa2_selftest", "csa2_select_topk_noalloc")
+           "csa2_selftest", "csa2_select_topk_noalloc", "csa2_select_attend")
 
 
 class Csa2Error(RuntimeError):
@@ -68,6 +69,9 @@ def lib():
             fn.argtypes = [P, P, P, P, P, I64, I, I64, ctypes.POINTER(_Cache), P, I64, P]
         L.csa2_select_topk.restype = I
         L.csa2_select_topk.argtypes = [P, I64, I, P, P, I64, I, P, P, SZ, P]
+        L.csa2_select_attend.restype = I
+        L.csa2_select_attend.argtypes = [P, I64, I, P, P, I64, I, P, I, P, P, P, P,
+                                         ctypes.POINTER(_Cache), P, P, I64, P, P, P, P, P, SZ, P]
         L.csa2_select_topk_noalloc.restype = I
         L.csa2_select_topk_noalloc.argtypes = [P, I64, I, P, P, I64, I, P, P]
         L.csa2_block_pool.restype = I
@@ -228,6 +232,32 @@ def csa2_select_topk_noalloc(scores, n_valid, col_ids, n_cols, k, out, stream=No
     st = lib().csa2_select_topk_noalloc(_ptr(scores), scores.shape[1], Q, _ptr(n_valid),
                                         _ptr(col_ids), n_cols, k, _ptr(out), _stream(stream, scores))
     _check("csa2_select_topk_noalloc", st)
+
+
+def csa2_select_attend(scores, n_valid, col_ids, n_cols, k, idx, q, q_seq, cache, swa_codes,
+                       swa_scale, swa_start, swa_len, out, lse=None, ws=None, n_blocks=0,
+                       pool=None, pool_len=None, stream=None):
+    """Top-k (n_blocks == 0, col_ids optional) or pool + top-k (n_blocks > 0)
+    fused with the attention over the selected rows; idx [Q, k] i32, out
+    [Q, 64, 512] f32; ws from workspace(CSA2_OP_SELECT_ATTEND or
+    CSA2_OP_POOL_ATTEND, Q, n_cols, k)."""
+    _dtype(scores, torch.float32, "scores"); _dtype(n_valid, torch.int64, "n_valid")
+    _dtype(col_ids, torch.int32, "col_ids"); _dtype(idx, torch.int32, "idx")
+    _dtype(pool, torch.int32, "pool"); _dtype(pool_len, torch.int64, "pool_len")
+    _dtype(q, torch.bfloat16, "q"); _dtype(q_seq, torch.int32, "q_seq")
+    _dtype(swa_codes, torch.uint8, "swa_codes"); _dtype(swa_scale, torch.float32, "swa_scale")
+    _dtype(swa_start, torch.int64, "swa_start"); _dtype(swa_len, torch.int32, "swa_len")
+    _dtype(out, torch.float32, "out"); _dtype(lse, torch.float32, "lse")
+    Q = scores.shape[0]
+    T_swa = swa_codes.shape[1] if swa_codes is not None else 0
+    wsb = ws.numel() * ws.element_size() if ws is not None else 0
+    cs = cache.c_struct()
+    st = lib().csa2_select_attend(_ptr(scores), scores.shape[1], Q, _ptr(n_valid), _ptr(col_ids),
+                                  n_cols, k, _ptr(idx), n_blocks, _ptr(pool), _ptr(pool_len),
+                                  _ptr(q), _ptr(q_seq), ctypes.byref(cs), _ptr(swa_codes),
+                                  _ptr(swa_scale), T_swa, _ptr(swa_start), _ptr(swa_len),
+                                  _ptr(out), _ptr(lse), _ptr(ws), wsb, _stream(stream, scores))
+    _check("csa2_select_attend", st)
 
 
 def csa2_block_pool(scores, n_valid, n_cols, n_blocks, pool, pool_len, ws=None, block=8,

@@ -276,6 +276,49 @@ csa2_status csa2_block_pool(const float* scores, int64_t ld, int Q, const int64_
                     "csa2_block_pool launch");
 }
 
+csa2_status csa2_select_attend(const float* scores, int64_t ld, int Q, const int64_t* n_valid,
+                               const int32_t* col_ids, int64_t n_cols, int k, int32_t* idx,
+                               int n_blocks, int32_t* pool, int64_t* pool_len, const uint16_t* q,
+                               const int32_t* q_seq, const csa2_cache* src,
+                               const uint8_t* swa_codes, const float* swa_scale, int64_t T_swa,
+                               const int64_t* swa_start, const int32_t* swa_len, float* out,
+                               float* lse, void* ws, size_t ws_bytes, void* stream) {
+  g_err[0] = 0;
+  REQ(scores && n_valid && idx && q && q_seq && out && swa_start && swa_len,
+      "scores, n_valid, idx, q, q_seq, out, swa_start, swa_len must not be NULL");
+  REQ(Q > 0 && Q < 256, "Q=%d must be in [1, 255] (larger batches: the separate calls)", Q);
+  REQ(k >= 1 && k <= CSA2_MAX_K, "k=%d must be in [1, %d]", k, CSA2_MAX_K);
+  REQ(n_blocks >= 0 && n_blocks <= CSA2_MAX_K, "n_blocks=%d must be in [0, %d]", n_blocks,
+      CSA2_MAX_K);
+  REQ(n_blocks == 0 || (pool && pool_len && !col_ids && k <= n_blocks),
+      "with n_blocks > 0: pool and pool_len given, col_ids NULL, k <= n_blocks");
+  REQ(n_cols >= 0 && n_cols <= CSA2_MAX_COLS, "n_cols=%lld must be in [0, %d]",
+      (long long)n_cols, CSA2_MAX_COLS);
+  REQ(ld >= n_cols && ld > 0, "ld=%lld < n_cols=%lld", (long long)ld, (long long)n_cols);
+  const csa2_status cs = check_cache(src);
+  if (cs != CSA2_OK) return cs;
+  REQ(T_swa >= 0, "T_swa must be >= 0");
+  REQ(T_swa == 0 || (swa_codes && swa_scale), "swa_codes / swa_scale NULL with T_swa > 0");
+  REQ(al(scores, 4) && al(q, 16) && al(out, 16) && (!swa_codes || al(swa_codes, 16)) &&
+          (!pool || al(pool, 16)),
+      "scores must be 4-byte aligned, q, out, swa_codes and pool 16-byte aligned");
+  const int mode = n_blocks > 0 ? 1 : 0;
+  const size_t need = csa2::select_attend_ws_bytes(Q, n_cols, mode, k);
+  if (!ws || ws_bytes < need)
+    return fail(CSA2_EWORKSPACE, "workspace %zu bytes < %zu needed", ws ? ws_bytes : (size_t)0,
+                need);
+  REQ(al(ws, 256), "ws must be 256-byte aligned");
+  if (device_checks())
+    CHECKED(check_indices("q_seq", q_seq, 1, Q, nullptr, Q, 0,
+                          src->batch > 0 ? src->batch : (int64_t)INT32_MAX, stream));
+  return hip_status(csa2::launch_select_attend(scores, ld, Q, n_valid, col_ids, n_cols, mode,
+                                               mode == 1 ? n_blocks : k, k, idx, pool, pool_len,
+                                               q, q_seq, src->kv_codes, src->kv_scales, src->cap,
+                                               swa_codes, swa_scale, T_swa, swa_start, swa_len,
+                                               out, lse, ws, (hipStream_t)stream),
+                    "csa2_select_attend launch");
+}
+
 static csa2_status attend_common(const uint16_t* q, const int32_t* q_seq, int Q,
                                  const csa2_cache* src, const int32_t* idx, int k,
                                  const uint8_t* swa_codes, const float* swa_scale, int64_t T_swa,
@@ -346,6 +389,11 @@ size_t csa2_workspace_bytes(int op, int Q, int64_t n_cols, int k) {
     case CSA2_OP_TOPK: return csa2::select_ws_bytes(Q, n_cols < 0 ? 0 : n_cols, 0);
     case CSA2_OP_POOL: return csa2::select_ws_bytes(Q, n_cols < 0 ? 0 : n_cols, 1);
     case CSA2_OP_ATTEND: return csa2::attend_ws_bytes(Q, k < 0 ? 0 : k);
+    case CSA2_OP_SELECT_ATTEND:
+    case CSA2_OP_POOL_ATTEND:
+      if (k < 1) return 0;
+      return csa2::select_attend_ws_bytes(Q, n_cols < 0 ? 0 : n_cols,
+                                          op == CSA2_OP_POOL_ATTEND ? 1 : 0, k);
     default: return 0;
   }
 }

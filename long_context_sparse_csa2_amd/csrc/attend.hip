@@ -28,6 +28,7 @@
 #include "common.h"
 #include "launch.h"
 #include "attend_stage.h"
+#include "select_core.h"
 
 namespace csa2 {
 
@@ -37,52 +38,95 @@ constexpr int AT_MAX_SWA = 128;
 constexpr int AT_TARGET_WG = 1024; // workgroups a decode launch aims for
 constexpr int AT_WIDE_MIN_Q = 256;  // from this many queries on, one workgroup per query
 
-__global__ __launch_bounds__(256, 1) void k_attend(
-    const uint16_t* __restrict__ qv, const int32_t* __restrict__ q_seq,
-    const uint8_t* __restrict__ kv_codes, const uint8_t* __restrict__ kv_scales, int64_t cap,
-    const int32_t* __restrict__ idx, int k, const uint8_t* __restrict__ swa_codes,
-    const float* __restrict__ swa_scale, int64_t T_swa, const int64_t* __restrict__ swa_start,
-    const int32_t* __restrict__ swa_len, float* __restrict__ out, float* __restrict__ lse,
-    float* __restrict__ part_o, float* __restrict__ part_ml, int nsplit, int cps, RopeArgs rp) {
-  __shared__ __align__(16) _Float16 kv[2][CH_ROWS * KV_LD];         // K (+ V of main rows), V of SWA rows
-  __shared__ __align__(16) _Float16 qs[AT_HG][D_LAT + AT_PAD];     // fp16 query rows
-  __shared__ __align__(16) _Float16 pl[AT_HG][CH_ROWS + AT_PAD];   // P of the chunk
-  __shared__ float red_m[4][AT_HG], red_l[4][AT_HG];
-  __shared__ int64_t rowoff[CH_ROWS];                               // entry / SWA row, -1 = none
-  __shared__ float rowsig[CH_ROWS];
-  __shared__ float qinv[AT_HG];                                     // 2^-e of each head
-  __shared__ f32x2_t rcs[ROPE_MAX_PAIRS];                           // RoPE (cos, sin) per pair
-  __shared__ __align__(16) _Float16 qs_lo[AT_HG][ROPE_MAX_DIMS + AT_PAD];  // low fp16 terms, last 64 dims
+// LDS of one 256-thread attention workgroup, except the SWA rows' scaled V
+// copy (kv1), which the fused selection kernel overlays on its selection
+// state.
+struct AttendLds {
+  alignas(16) _Float16 kv[CH_ROWS * KV_LD];             // K (and V of main rows) of the chunk
+  alignas(16) _Float16 qs[AT_HG][D_LAT + AT_PAD];       // fp16 query rows
+  alignas(16) _Float16 pl[AT_HG][CH_ROWS + AT_PAD];     // P of the chunk
+  float red_m[4][AT_HG], red_l[4][AT_HG];
+  int64_t rowoff[CH_ROWS];                               // entry / SWA row, -1 = none
+  float rowsig[CH_ROWS];
+  float qinv[AT_HG];                                     // 2^-e of each head
+  f32x2_t rcs[ROPE_MAX_PAIRS];                           // RoPE (cos, sin) per pair
+  alignas(16) _Float16 qs_lo[AT_HG][ROPE_MAX_DIMS + AT_PAD];  // low fp16 terms, last 64 dims
+};
 
-  const int sp = blockIdx.x % nsplit;
-  const int hq = blockIdx.x / nsplit;
-  const int hg = hq & 3, q = hq >> 2;
+// A query's sequence and SWA window (ring start, length clamped to one lap
+// and to AT_MAX_SWA rows; a start outside the ring gives no rows).
+struct AttendQuery {
+  int64_t seq, sst;
+  int sl;
+};
+
+__device__ __forceinline__ AttendQuery attend_query(int q, const int32_t* __restrict__ q_seq,
+                                                    const int64_t* __restrict__ swa_start,
+                                                    const int32_t* __restrict__ swa_len,
+                                                    int64_t T_swa) {
+  AttendQuery a;
+  a.seq = q_seq[q];
+  a.sst = swa_start[q];
+  int64_t sl64 = swa_len[q];
+  if (a.sst < 0 || a.sst >= T_swa) sl64 = 0;                 // ring: start must be a slot
+  else if (sl64 > T_swa) sl64 = T_swa;                       // at most one lap
+  a.sl = sl64 < 0 ? 0 : (sl64 > AT_MAX_SWA ? AT_MAX_SWA : (int)sl64);
+  return a;
+}
+
+// This thread's share of the query rows of head group hg: head tid >> 4,
+// dims 32 (tid & 15) .. +31 (threads 0..255).
+__device__ __forceinline__ void attend_query_rows(bf16x8_t (&x)[4], const uint16_t* __restrict__ qv,
+                                                  int q, int hg) {
+  const int tid = threadIdx.x;
+  const bf16x8_t* qp = (const bf16x8_t*)(qv + ((int64_t)q * H_ATT + hg * AT_HG + (tid >> 4)) * D_LAT +
+                                         (tid & 15) * 32);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) x[i] = qp[i];
+}
+
+// Workgroup b -> (unit, head group): the four head-group workgroups of one
+// unit (query, split) get indices 8 apart, so the round-robin dispatch over
+// the 8 XCDs puts them on one XCD and its L2 serves the rows all four
+// gather.  A launch has ceil(units / 8) * 32 workgroups; those past the
+// last unit return at once.
+__device__ __forceinline__ void unit_of(int b, int& u, int& hg) {
+  u = (b >> 5) * 8 + (b & 7);
+  hg = (b >> 3) & 3;
+}
+static inline unsigned unit_grid(int units) { return (unsigned)((units + 7) / 8 * 32); }
+
+// One workgroup's part of a query's attention: head group hg (16 heads),
+// chunks sp * cps .. of the query's main-KV chunks followed by its SWA
+// chunks; id_of(r) is the selected entry of main row r (r < k); id0 that of
+// this thread's row of the first chunk (when it is a main chunk), requested
+// by the caller before the query rows x and the scalars aq.  Writes the
+// final output when nsplit == 1, else the partial (max, sum, O) state.
+template <typename IdOf>
+__device__ __forceinline__ void attend_body(
+    int q, int hg, int sp, int nsplit, int cps, IdOf id_of, int id0, const bf16x8_t (&x)[4],
+    const AttendQuery& aq, const uint8_t* __restrict__ kv_codes,
+    const uint8_t* __restrict__ kv_scales, int64_t cap, int k,
+    const uint8_t* __restrict__ swa_codes, const float* __restrict__ swa_scale, int64_t T_swa,
+    float* __restrict__ out, float* __restrict__ lse, float* __restrict__ part_o,
+    float* __restrict__ part_ml, const RopeArgs& rp, AttendLds& L, _Float16* kv1) {
+  _Float16* const kv0 = L.kv;
+  auto& qs = L.qs;
+  auto& pl = L.pl;
+  auto& red_m = L.red_m;
+  auto& red_l = L.red_l;
+  auto& rowoff = L.rowoff;
+  auto& rowsig = L.rowsig;
+  auto& qinv = L.qinv;
+  auto& rcs = L.rcs;
+  auto& qs_lo = L.qs_lo;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int r16 = lane & 15, qd = lane >> 4;
   const int nmc = (k + CH_ROWS - 1) / CH_ROWS;
   const int ch_beg = sp * cps;
-  // The first chunk's selected id (when it is a main-KV chunk) and the query
-  // rows go out before the query's sequence and window arrive: neither
-  // depends on them.
-  int id0 = -1;
-  if (ch_beg < nmc) {
-    const int r0 = ch_beg * CH_ROWS + (tid & 63);
-    id0 = idx[(int64_t)q * k + (r0 < k ? r0 : k - 1)];
-  }
   const int qh = tid >> 4, qpart = tid & 15;     // query conversion: head, 32-dim part
-  bf16x8_t x[4];
-  {
-    const bf16x8_t* qp = (const bf16x8_t*)(qv + ((int64_t)q * H_ATT + hg * AT_HG + qh) * D_LAT +
-                                           qpart * 32);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) x[i] = qp[i];
-  }
-  const int64_t seq = q_seq[q];
-  const int64_t sst = swa_start[q];
-  int64_t sl64 = swa_len[q];
-  if (sst < 0 || sst >= T_swa) sl64 = 0;                     // ring: start must be a slot
-  else if (sl64 > T_swa) sl64 = T_swa;                       // at most one lap
-  const int sl = sl64 < 0 ? 0 : (sl64 > AT_MAX_SWA ? AT_MAX_SWA : (int)sl64);
+  const int64_t seq = aq.seq, sst = aq.sst;
+  const int sl = aq.sl;
   const int nch = nmc + (sl + CH_ROWS - 1) / CH_ROWS;
   const int ch_end = min(ch_beg + cps, nch);
 
@@ -96,7 +140,7 @@ __global__ __launch_bounds__(256, 1) void k_attend(
     const bool main_ch = ch < nmc;             // uniform
     const int r = (main_ch ? ch * CH_ROWS : (ch - nmc) * CH_ROWS) + (tid & 63);
     if (main_ch) {
-      rq.e = idx[(int64_t)q * k + (r < k ? r : k - 1)];
+      rq.e = id_of(r < k ? r : k - 1);
     } else {
       const int rr = r < sl ? r : sl - 1;       // an SWA chunk exists only when sl >= 1
       rq.s = swa_scale[seq * T_swa + (sst + rr < T_swa ? sst + rr : sst + rr - T_swa)];
@@ -191,7 +235,7 @@ __global__ __launch_bounds__(256, 1) void k_attend(
         load_share<256>(raw, is_main, readable(off, is_main), tid >> 6, kv_codes, kv_scales,
                         swa_codes);
       if (tid < CH_ROWS) { rowoff[tid] = off; rowsig[tid] = sg; }
-      store_share<256>(raw, is_main, valid, sg, kv[0], kv[1], tid & 63, tid >> 6);
+      store_share<256>(raw, is_main, valid, sg, kv0, kv1, tid & 63, tid >> 6);
     }
     __syncthreads();
     if (ch == ch_beg) {
@@ -209,10 +253,10 @@ __global__ __launch_bounds__(256, 1) void k_attend(
     const int lr = wave * 16 + r16;
     f32x4_t sacc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int s = 0; s < 16; ++s) sacc = mfma16_f16(a[s], qk_b(kv[0], lr, s, qd), sacc);
+    for (int s = 0; s < 16; ++s) sacc = mfma16_f16(a[s], qk_b(kv0, lr, s, qd), sacc);
     if (rp.dims > 0) {                             // the rotated query's low terms
 #pragma unroll
-      for (int s = 0; s < 2; ++s) sacc = mfma16_f16(alo[s], qk_b(kv[0], lr, 14 + s, qd), sacc);
+      for (int s = 0; s < 2; ++s) sacc = mfma16_f16(alo[s], qk_b(kv0, lr, 14 + s, qd), sacc);
     }
     const bool valid = rowoff[lr] >= 0;
     const float rs = is_main ? 1.f : rowsig[lr];
@@ -259,7 +303,7 @@ __global__ __launch_bounds__(256, 1) void k_attend(
     }
 
     // ---- O += P V for dims 128*wave .. +127
-    const _Float16* vrows = is_main ? kv[0] : kv[1];
+    const _Float16* vrows = is_main ? kv0 : kv1;
     const f16x8_t pa0 = *(const f16x8_t*)&pl[r16][qd * 8];
     const f16x8_t pa1 = *(const f16x8_t*)&pl[r16][32 + qd * 8];
 #pragma unroll
@@ -303,6 +347,39 @@ __global__ __launch_bounds__(256, 1) void k_attend(
       part_ml[2 * slot + 1] = l_run[j];
     }
   }
+}
+
+__global__ __launch_bounds__(256, 1) void k_attend(
+    const uint16_t* __restrict__ qv, const int32_t* __restrict__ q_seq,
+    const uint8_t* __restrict__ kv_codes, const uint8_t* __restrict__ kv_scales, int64_t cap,
+    const int32_t* __restrict__ idx, int k, const uint8_t* __restrict__ swa_codes,
+    const float* __restrict__ swa_scale, int64_t T_swa, const int64_t* __restrict__ swa_start,
+    const int32_t* __restrict__ swa_len, float* __restrict__ out, float* __restrict__ lse,
+    float* __restrict__ part_o, float* __restrict__ part_ml, int nsplit, int cps, int Q,
+    RopeArgs rp) {
+  __shared__ AttendLds L;
+  __shared__ __align__(16) _Float16 kv1[CH_ROWS * KV_LD];          // V of SWA rows
+  int u, hg;
+  unit_of(blockIdx.x, u, hg);
+  if (u >= Q * nsplit) return;
+  const int q = u / nsplit, sp = u % nsplit;
+  const int tid = threadIdx.x;
+  const int nmc = (k + CH_ROWS - 1) / CH_ROWS;
+  // The first chunk's selected id (when it is a main-KV chunk) and the query
+  // rows go out before the query's sequence and window arrive: neither
+  // depends on them.
+  const int32_t* irow = idx + (int64_t)q * k;
+  int id0 = -1;
+  if (sp * cps < nmc) {
+    const int r0 = sp * cps * CH_ROWS + (tid & 63);
+    id0 = irow[r0 < k ? r0 : k - 1];
+  }
+  bf16x8_t x[4];
+  attend_query_rows(x, qv, q, hg);
+  const AttendQuery aq = attend_query(q, q_seq, swa_start, swa_len, T_swa);
+  attend_body(q, hg, sp, nsplit, cps, [&](int r) __attribute__((always_inline)) { return irow[r]; },
+              id0, x, aq, kv_codes, kv_scales, cap, k, swa_codes, swa_scale, T_swa, out, lse,
+              part_o, part_ml, rp, L, kv1);
 }
 
 // Merge the per-split partial states of one (query, head) by log-sum-exp.
@@ -375,6 +452,76 @@ __global__ __launch_bounds__(128) void k_attend_combine(const float* __restrict_
   if (lse && threadIdx.x == 0) lse[qh] = L > 0.f ? M + logf(L) : -INFINITY;
 }
 
+
+// ------------------------------------------------------------ fused
+// Selection and attention in one kernel (decode): every main-chunk
+// workgroup of a query runs the query's whole selection itself (the
+// selection is deterministic, so they all agree), keeps the entries of its
+// own 64 rows, and attends over them at once; the workgroup of head group 0
+// and split 0 also writes the selection out.  This removes the kernel
+// boundary and the round trip of the ids through memory between the two
+// steps (cross-workgroup hand-offs inside a kernel measured slower on
+// MI355X than a kernel boundary).  SWA-chunk workgroups skip the selection.
+// 512 threads: the selection runs on all eight waves, the attention on the
+// first four (the other four end after the selection; a barrier waits only
+// for the waves that have not ended).
+constexpr int SA_NT = 512;
+
+template <int MODE>
+__global__ __launch_bounds__(SA_NT, 1) void k_select_attend(
+    const float* __restrict__ scores, int64_t ld, const int64_t* __restrict__ n_valid,
+    const int32_t* __restrict__ col_ids, int64_t n_cols, LevelDesc d,
+    const uint32_t* __restrict__ lv, int kk, int k, int32_t* __restrict__ idx_out,
+    int32_t* __restrict__ pool, int64_t* __restrict__ pool_len, int vec_out, int spec,
+    const uint16_t* __restrict__ qv, const int32_t* __restrict__ q_seq,
+    const uint8_t* __restrict__ kv_codes, const uint8_t* __restrict__ kv_scales, int64_t cap,
+    const uint8_t* __restrict__ swa_codes, const float* __restrict__ swa_scale, int64_t T_swa,
+    const int64_t* __restrict__ swa_start, const int32_t* __restrict__ swa_len,
+    float* __restrict__ out, float* __restrict__ lse, float* __restrict__ part_o,
+    float* __restrict__ part_ml, int nsplit, int Q) {
+  __shared__ AttendLds L;
+  __shared__ union alignas(16) SaOverlay {
+    SelShared<SA_NT> sel;                       // main chunks: the selection state
+    _Float16 kv1[CH_ROWS * KV_LD];              // SWA chunks: V of the SWA rows
+  } U;
+  __shared__ int32_t cid[CH_ROWS];              // entries of this workgroup's 64 rows
+  int u, hg;
+  unit_of(blockIdx.x, u, hg);
+  if (u >= Q * nsplit) return;
+  const int q = u / nsplit, sp = u % nsplit;
+  const int tid = threadIdx.x;
+  const int nmc = (k + CH_ROWS - 1) / CH_ROWS;
+  const bool main_ch = sp < nmc;                // uniform over the workgroup
+  // the query rows and scalars go out before the selection
+  bf16x8_t x[4];
+  if (tid < 256) attend_query_rows(x, qv, q, hg);
+  const AttendQuery aq = attend_query(q, q_seq, swa_start, swa_len, T_swa);
+  if (main_ch) {
+    const bool writer = hg == 0 && sp == 0;
+    const SelResult r = select_query<SA_NT, SEL_CAP / SA_NT>(
+        q, scores, ld, n_valid, col_ids, n_cols, d, lv, kk, MODE, MODE == 0 ? idx_out : pool,
+        MODE == 0 ? (int64_t)kk : (int64_t)kk * 8, pool_len, MODE == 1 ? k : 0,
+        MODE == 1 ? idx_out : nullptr, vec_out, spec, writer, U.sel);
+    if (tid < CH_ROWS) {
+      const int rr = sp * CH_ROWS + tid;
+      int32_t e = -1;
+      if (rr < r.kept && rr < k) {
+        const uint32_t c = r.identity ? (uint32_t)rr : r.list[rr];
+        e = (MODE == 0 && col_ids) ? col_ids[(int64_t)q * ld + c] : (int32_t)c;
+      }
+      cid[tid] = e;
+    }
+    __syncthreads();
+  }
+  if (tid >= 256) return;                       // whole waves: the attention uses waves 0-3
+  const int id0 = main_ch ? cid[tid & 63] : -1;
+  const RopeArgs none = {nullptr, 0, 0.f, nullptr, {}};
+  attend_body(q, hg, sp, nsplit, 1,
+              [&](int r) __attribute__((always_inline)) { return cid[r - sp * CH_ROWS]; }, id0, x,
+              aq, kv_codes, kv_scales, cap, k, swa_codes, swa_scale, T_swa, out, lse, part_o,
+              part_ml, none, L, U.kv1);
+}
+
 // ------------------------------------------------------------ host side
 static void attend_plan(int Q, int k, int& nsplit, int& cps) {
   const int nch = (k + CH_ROWS - 1) / CH_ROWS + AT_MAX_SWA / CH_ROWS;
@@ -420,12 +567,55 @@ hipError_t launch_attend(const uint16_t* q, const int32_t* q_seq, int Q, const u
   if (nsplit <= 1) { nsplit = 1; cps = nch; }
   float* part_o = (float*)ws;
   float* part_ml = nsplit > 1 ? part_o + (size_t)Q * nsplit * H_ATT * D_LAT : nullptr;
-  hipLaunchKernelGGL(k_attend, dim3((unsigned)(Q * (H_ATT / AT_HG) * nsplit)), dim3(256), 0,
-                     stream, q, q_seq, kv_codes, kv_scales, cap, idx, k, swa_codes, swa_scale,
-                     T_swa, swa_start, swa_len, out, lse, part_o, part_ml, nsplit, cps, rp);
+  hipLaunchKernelGGL(k_attend, dim3(unit_grid(Q * nsplit)), dim3(256), 0, stream, q, q_seq,
+                     kv_codes, kv_scales, cap, idx, k, swa_codes, swa_scale, T_swa, swa_start,
+                     swa_len, out, lse, part_o, part_ml, nsplit, cps, Q, rp);
   if (nsplit > 1)
     hipLaunchKernelGGL(k_attend_combine, dim3((unsigned)(Q * H_ATT)), dim3(128), 0, stream,
                        (const float*)part_o, (const float*)part_ml, nsplit, out, lse, rp);
+  return hipGetLastError();
+}
+
+// ---- fused selection + attention
+// One split per 64-row chunk: the main chunks of the top-k, then two for a
+// window of up to 128 SWA rows.
+static int sa_splits(int k) { return (k + CH_ROWS - 1) / CH_ROWS + AT_MAX_SWA / CH_ROWS; }
+static size_t align256(size_t b) { return (b + 255) / 256 * 256; }
+
+size_t select_attend_ws_bytes(int Q, int64_t n_cols, int mode, int k) {
+  return align256(select_ws_bytes(Q, n_cols, mode)) + attend_ws_for(Q, sa_splits(k));
+}
+
+hipError_t launch_select_attend(const float* scores, int64_t ld, int Q, const int64_t* n_valid,
+                                const int32_t* col_ids, int64_t n_cols, int mode, int kk, int k,
+                                int32_t* idx_out, int32_t* pool, int64_t* pool_len,
+                                const uint16_t* q, const int32_t* q_seq, const uint8_t* kv_codes,
+                                const uint8_t* kv_scales, int64_t cap, const uint8_t* swa_codes,
+                                const float* swa_scale, int64_t T_swa, const int64_t* swa_start,
+                                const int32_t* swa_len, float* out, float* lse, void* ws,
+                                hipStream_t stream) {
+  const LevelDesc d = select_levels(Q, n_cols, mode);
+  uint32_t* lv = (uint32_t*)ws;
+  const int nsplit = sa_splits(k);
+  float* part_o = (float*)((char*)ws + align256(select_ws_bytes(Q, n_cols, mode)));
+  float* part_ml = part_o + (size_t)Q * nsplit * H_ATT * D_LAT;
+  hipError_t e = launch_maxima(scores, ld, Q, n_valid, n_cols, d, lv, stream);
+  if (e != hipSuccess) return e;
+  const int spec = Q <= 64;
+  const int vec_out = mode == 1 && ((uintptr_t)pool & 15) == 0;
+  if (mode == 0)
+    hipLaunchKernelGGL(k_select_attend<0>, dim3(unit_grid(Q * nsplit)), dim3(SA_NT), 0, stream,
+                       scores, ld, n_valid, col_ids, n_cols, d, (const uint32_t*)lv, kk, k, idx_out,
+                       pool, pool_len, vec_out, spec, q, q_seq, kv_codes, kv_scales, cap, swa_codes,
+                       swa_scale, T_swa, swa_start, swa_len, out, lse, part_o, part_ml, nsplit, Q);
+  else
+    hipLaunchKernelGGL(k_select_attend<1>, dim3(unit_grid(Q * nsplit)), dim3(SA_NT), 0, stream,
+                       scores, ld, n_valid, col_ids, n_cols, d, (const uint32_t*)lv, kk, k, idx_out,
+                       pool, pool_len, vec_out, spec, q, q_seq, kv_codes, kv_scales, cap, swa_codes,
+                       swa_scale, T_swa, swa_start, swa_len, out, lse, part_o, part_ml, nsplit, Q);
+  const RopeArgs none = {nullptr, 0, 0.f, nullptr, {}};
+  hipLaunchKernelGGL(k_attend_combine, dim3((unsigned)(Q * H_ATT)), dim3(128), 0, stream,
+                     (const float*)part_o, (const float*)part_ml, nsplit, out, lse, none);
   return hipGetLastError();
 }
 

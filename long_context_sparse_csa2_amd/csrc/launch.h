@@ -60,6 +60,20 @@ hipError_t launch_attend(const uint16_t* q, const int32_t* q_seq, int Q, const u
                          const int64_t* swa_start, const int32_t* swa_len, float* out, float* lse,
                          void* ws, size_t ws_bytes, const RopeArgs& rp, hipStream_t stream);
 
+// Selection (mode 0: top-k of kk = k columns, col_ids optional; mode 1: the
+// pool of kk blocks of 8 and the top-k inside it) fused with the attention
+// over the top-k rows (decode batches, Q < 256); ws holds the maxima levels
+// and the attention's partial states.
+size_t select_attend_ws_bytes(int Q, int64_t n_cols, int mode, int k);
+hipError_t launch_select_attend(const float* scores, int64_t ld, int Q, const int64_t* n_valid,
+                                const int32_t* col_ids, int64_t n_cols, int mode, int kk, int k,
+                                int32_t* idx_out, int32_t* pool, int64_t* pool_len,
+                                const uint16_t* q, const int32_t* q_seq, const uint8_t* kv_codes,
+                                const uint8_t* kv_scales, int64_t cap, const uint8_t* swa_codes,
+                                const float* swa_scale, int64_t T_swa, const int64_t* swa_start,
+                                const int32_t* swa_len, float* out, float* lse, void* ws,
+                                hipStream_t stream);
+
 hipError_t launch_attend_wide(const uint16_t* q, const int32_t* q_seq, int Q,
                               const uint8_t* kv_codes, const uint8_t* kv_scales, int64_t cap,
                               const int32_t* idx, int k, const uint8_t* swa_codes,

@@ -27,13 +27,15 @@ from collections import namedtuple
 
 import torch
 
-from . import (Cache, CSA2_OP_ATTEND, CSA2_OP_POOL, CSA2_OP_TOPK, csa2_block_pool,
-               csa2_compress_quant, csa2_index_score, csa2_select_topk, csa2_sparse_attend,
-               workspace)
+from . import (Cache, CSA2_OP_ATTEND, CSA2_OP_POOL, CSA2_OP_POOL_ATTEND, CSA2_OP_SELECT_ATTEND,
+               CSA2_OP_TOPK, csa2_block_pool, csa2_compress_quant, csa2_index_score,
+               csa2_select_attend, csa2_select_topk, csa2_sparse_attend, workspace)
 from .synth import Workload
 
 # one C-ABI call of a step: its name, layer, thunk and query rows [i0, i1)
 Op = namedtuple("Op", "name layer fn rows")
+# the calls that end a layer (its attention)
+ATTEND_OPS = ("sparse_attend", "select_attend_full", "select_attend_pool")
 
 
 def build_cache(wl: Workload, device, seq_chunk=1):
@@ -53,9 +55,12 @@ def build_cache(wl: Workload, device, seq_chunk=1):
 class Step:
     """All layers of one step of a workload over a built cache."""
 
-    def __init__(self, wl: Workload, device, cache=None, fp4q=False):
+    def __init__(self, wl: Workload, device, cache=None, fp4q=False, fused=None):
         """fp4q=True scores with the MXFP4 indexer query
-        (csa2_index_score_fp4q) instead of the bf16 one."""
+        (csa2_index_score_fp4q) instead of the bf16 one.  fused=True runs
+        each selection together with its attention (csa2_select_attend);
+        the default does so for decode batches (fewer than 256 queries) and
+        uses the separate calls for prefill chunks."""
         self.wl = wl
         self.device = device
         self.fp4q = fp4q
@@ -82,6 +87,8 @@ class Step:
         # per query), so a hierarchical workload runs as one chunk
         assert not (wl.hierarchical and len(self.chunks) > 1), \
             "a hierarchical workload cannot run in query chunks"
+        self.fused = (qc < 256) if fused is None else bool(fused)
+        assert not (self.fused and qc >= 256), "the fused selection + attention takes < 256 queries"
         self.layers = [wl.layer_inputs(li, device) for li in range(len(wl.layers))]
         self.scores = torch.empty(qc, N, dtype=torch.float32, device=device)
         self.idx = torch.empty(qc, k, dtype=torch.int32, device=device)
@@ -100,6 +107,11 @@ class Step:
             self.pool_scores = torch.empty(Q, P, dtype=torch.float32, device=device)
             self.ws_topk_pool = workspace(CSA2_OP_TOPK, Q, P, k, device)
             self.idx_r = [torch.empty(Q, k, dtype=torch.int32, device=device) for _ in wl.layers]
+        if self.fused:
+            self.ws_sa_full = workspace(CSA2_OP_POOL_ATTEND if wl.hierarchical else CSA2_OP_SELECT_ATTEND,
+                                        qc, N, k, device)
+            if wl.hierarchical:
+                self.ws_sa_pool = workspace(CSA2_OP_SELECT_ATTEND, Q, self.P, k, device)
 
     def ops(self):
         """The step as an ordered list of Op(name, layer, thunk, rows); each
@@ -129,6 +141,20 @@ class Step:
                                   n_cols=n_cols, scores=scores: csa2_index_score(
                         L["q_idx"], L["w"], q_seq, n_vis, None, n_cols, self.cache, scores,
                         fp4q=self.fp4q), (i0, i1)))
+                    idx = idx_full
+                    if self.fused:
+                        # the pool (hierarchical) or the top-k, and the attention, in one call
+                        nb = wl.n_blocks if wl.hierarchical else 0
+                        out.append(Op("select_attend_full", li, lambda L=L, li=li, q_seq=q_seq,
+                                      n_vis=n_vis, n_cols=n_cols, scores=scores, idx=idx_full,
+                                      swa_start=swa_start, swa_len=swa_len, rows=rows, nb=nb:
+                                      csa2_select_attend(
+                            scores, n_vis, None, n_cols, wl.k, idx, L["q_attn"], q_seq, self.cache,
+                            L["swa_codes"], L["swa_scale"], swa_start, swa_len,
+                            self.out[li][rows], self.lse[li][rows], self.ws_sa_full, n_blocks=nb,
+                            pool=self.pool if nb else None, pool_len=self.pool_len if nb else None),
+                            (i0, i1)))
+                        continue
                     if wl.hierarchical:
                         # the pool and the layer's own top-k in one selection pass
                         out.append(Op("block_pool_topk", li, lambda: csa2_block_pool(
@@ -138,12 +164,19 @@ class Step:
                         out.append(Op("select_topk_full", li, lambda n_vis=n_vis, n_cols=n_cols,
                                       scores=scores, idx=idx_full: csa2_select_topk(
                             scores, n_vis, None, n_cols, wl.k, idx, self.ws_topk), (i0, i1)))
-                    idx = idx_full
                 elif mode == "reindex":
                     idx = self.idx_r[li]
                     out.append(Op("index_score_pool", li, lambda L=L: csa2_index_score(
                         L["q_idx"], L["w"], self.q_seq, self.pool_len, self.pool, self.P,
                         self.cache, self.pool_scores, fp4q=self.fp4q), (i0, i1)))
+                    if self.fused:
+                        out.append(Op("select_attend_pool", li, lambda L=L, li=li, idx=idx:
+                                      csa2_select_attend(
+                            self.pool_scores, self.pool_len, self.pool, self.P, wl.k, idx,
+                            L["q_attn"], self.q_seq, self.cache, L["swa_codes"], L["swa_scale"],
+                            self.swa_start, self.swa_len, self.out[li], self.lse[li],
+                            self.ws_sa_pool), (i0, i1)))
+                        continue
                     out.append(Op("select_topk_pool", li, lambda idx=idx: csa2_select_topk(
                         self.pool_scores, self.pool_len, self.pool, self.P, wl.k, idx,
                         self.ws_topk_pool), (i0, i1)))
@@ -176,7 +209,7 @@ class Step:
                 op.fn()
                 e1.record()
                 events.setdefault(name, []).append((e0, e1))
-            if keep and name == "sparse_attend":
+            if keep and name in ATTEND_OPS:
                 mode = wl.layers[li]
                 src_idx = self.idx_r[li] if mode == "reindex" else self.idx
                 sel = ((kept >= i0) & (kept < i1)).nonzero().flatten()   # kept rows in this chunk
