@@ -101,6 +101,69 @@ def scan_roofline(wl, step, scan_us):
             "traffic": scan_traffic(wl.name, step.fp4q), "flops_per_launch": flops, **base}
 
 
+def measure_peaks(dev, read_bytes=2 << 30, mfma_iters=4000, reps=5):
+    """The device's practical ceilings, timed here with HIP events around
+    single launches (median of reps): a streaming read of read_bytes by a
+    grid-stride kernel (csa2_peak_read) and dense bf16 32x32x16 MFMA chains
+    (csa2_peak_mfma).  Reported beside the datasheet peaks, which the
+    roofline fractions use."""
+    from long_context_sparse_csa2_amd import lib
+    L = lib()
+    st = torch.cuda.current_stream().cuda_stream
+    buf = torch.ones(read_bytes, dtype=torch.uint8, device=dev)
+    sink = torch.zeros(4096, dtype=torch.int32, device=dev)
+    fsink = torch.zeros(1024, dtype=torch.float32, device=dev)
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(reps):
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(); fn(); e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1) * 1e-3)
+        return float(np.median(ts))
+
+    t_read = timed(lambda: L.csa2_peak_read(buf.data_ptr(), read_bytes, sink.data_ptr(), st))
+    flops = [0.0]
+
+    def mf():
+        flops[0] = L.csa2_peak_mfma(mfma_iters, fsink.data_ptr(), st)
+    t_mfma = timed(mf)
+    del buf
+    return {"hbm_read_GBs": round(read_bytes / t_read / 1e9, 1),
+            "bf16_mfma_TFLOPs": round(flops[0] / t_mfma / 1e12, 1),
+            "datasheet_hbm_GBs": HBM_PEAK_GBS, "datasheet_bf16_TFLOPs": MFMA_BF16_PEAK_TFLOPS,
+            "method": f"csa2_peak_read over {read_bytes >> 20} MiB and csa2_peak_mfma "
+                      f"({mfma_iters} iterations of 4 bf16 32x32x16 MFMA chains in 4096 waves), "
+                      f"HIP events around single launches, median of {reps}"}
+
+
+def time_scan_cold(step, dev, reps=10, sweep_bytes=512 << 20):
+    """The Full-layer scan timed right after a streaming read of sweep_bytes
+    of other memory (which evicts what the 256 MB memory-side cache held of
+    the scan's bytes from the previous step): HIP events on the current
+    stream, median of reps, microseconds."""
+    from long_context_sparse_csa2_amd import lib
+    L = lib()
+    st = torch.cuda.current_stream().cuda_stream
+    buf = torch.ones(sweep_bytes, dtype=torch.uint8, device=dev)
+    sink = torch.zeros(4096, dtype=torch.int32, device=dev)
+    op = step.ops()[step.scan_index()]
+    ts = []
+    for _ in range(reps):
+        L.csa2_peak_read(buf.data_ptr(), sweep_bytes, sink.data_ptr(), st)
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(); op.fn(); e1.record()
+        torch.cuda.synchronize()
+        ts.append(e0.elapsed_time(e1) * 1e3)
+    del buf
+    return float(np.median(ts))
+
+
 def time_append(wl, dev, calls=64):
     """Decode-time append (csa2_decode_append) of one token per sequence for
     the workload's batch and m, into a fresh state and a cache with room for
@@ -182,6 +245,17 @@ def time_attend_rope(step, dev, calls=20):
     return res
 
 
+def blas_threads():
+    """Threads the oracle's numpy BLAS runs on (its matmuls; the elementwise
+    steps run on one)."""
+    from threadpoolctl import threadpool_info
+    return max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+
+
+def host_cpus():
+    return {"host_cpus": os.cpu_count(), "cpus_in_affinity": len(os.sched_getaffinity(0))}
+
+
 def cpu_baseline_prefill(wl, step, seconds_target=15.0):
     """The fp64 oracle on a sample of a prefill's queries, spread over the
     causal range: per query, its entry compressed from its m raw tokens, then
@@ -189,7 +263,6 @@ def cpu_baseline_prefill(wl, step, seconds_target=15.0):
     SWA window).  One query stands for m raw
     tokens, so tokens/s = m x queries / s (the work grows with the position,
     and the sample is spread evenly, so its mean matches the whole run's)."""
-    from threadpoolctl import threadpool_info
     from oracle import csa2_ref as R
     ik_c = step.cache.ik_codes[0].cpu().numpy()
     ik_s = step.cache.ik_scales[0].cpu().numpy()
@@ -222,8 +295,9 @@ def cpu_baseline_prefill(wl, step, seconds_target=15.0):
             R.attend(L["q_attn"][q].float().cpu().numpy().astype(np.float64), rows)
         t_total += time.perf_counter() - t0
         done += 1
-    threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    threads = blas_threads()
     return {"value": wl.m * done / t_total, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            **host_cpus(),
             "sample": f"{done} of {wl.Q} queries drawn evenly over the causal range, each its "
                       f"entry's compression and all {len(wl.layers)} layers, {t_total:.1f} s; m = {wl.m} raw tokens per "
                       f"query; numpy fp64 (BLAS matmul on {threads} threads)"}
@@ -233,7 +307,6 @@ def cpu_baseline(wl, step, seconds_target=15.0):
     """The fp64 oracle, as it stands, on one sequence of the workload: the
     whole step (Full scan, pool, top-512, attention, every Reindex layer).
     Returns tokens/s for that one-sequence sample."""
-    from threadpoolctl import threadpool_info
     from oracle import csa2_ref as R
     if wl.prefill:
         return cpu_baseline_prefill(wl, step, seconds_target)
@@ -271,8 +344,9 @@ def cpu_baseline(wl, step, seconds_target=15.0):
             R.attend(L["q_attn"], rows)
         t_total += time.perf_counter() - t0
         runs += 1
-    threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    threads = blas_threads()
     return {"value": runs / t_total, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            **host_cpus(),
             "sample": f"one of {wl.B} sequences, whole {len(wl.layers)}-layer step, "
                       f"{runs} run(s) in {t_total:.1f} s; numpy fp64 (BLAS matmul on "
                       f"{threads} threads, elementwise steps on 1)"}
@@ -393,6 +467,10 @@ def main():
           flush=True)
 
     roofline = scan_roofline(wl, step, scan_us)
+    if not chunked:
+        # the same scan right after a 512 MiB read sweep of other memory
+        roofline["avg_launch_us_after_read_sweep"] = round(time_scan_cold(step, dev), 2)
+    peaks = measure_peaks(dev)
     step_b = step_bytes(wl)
     out = {
         "metric": PREFILL_METRIC if wl.prefill else METRIC,
@@ -415,6 +493,7 @@ def main():
         "step_roofline": None if step_b is None else {
             "bytes": step_b, "us_at_peak": round(step_b / (HBM_PEAK_GBS * 1e3), 2),
             "frac": round(step_b / (HBM_PEAK_GBS * 1e9) / (ms * 1e-3), 4)},
+        "peaks_measured": peaks,
         "launch": "eager" if graphs is None else "the step replayed as one hip graph",
         "scan_timing": ("HIP events around each Full-layer scan inside the timed region"
                         if graphs is None else
@@ -436,6 +515,12 @@ def main():
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(wl, step)
+        if wl.name in ("c0", "c1"):
+            # the same oracle on one host thread
+            from threadpoolctl import threadpool_limits
+            with threadpool_limits(limits=1):
+                one = cpu_baseline(wl, step)
+            out["cpu_baseline_1thread"] = {k: one[k] for k in ("value", "unit", "cores", "sample")}
     print(json.dumps(out), flush=True)
 
 

@@ -13,7 +13,9 @@ import os
 import torch
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "libcsa2.so")
+# CSA2_LIB selects another build of the library (the sanitizer build of the
+# host code that a CPU test loads); by default the in-tree libcsa2.so.
+LIB_PATH = os.environ.get("CSA2_LIB") or os.path.join(_PKG, "libcsa2.so")
 
 CSA2_OP_TOPK, CSA2_OP_POOL, CSA2_OP_ATTEND = 1, 2, 3
 CSA2_OP_SELECT_ATTEND, CSA2_OP_POOL_ATTEND = 4, 5
@@ -21,7 +23,8 @@ STATUS = {0: "CSA2_OK", 1: "CSA2_EINVAL", 2: "CSA2_EUNSUPPORTED", 3: "CSA2_EWORK
 EXPORTS = ("csa2_status_string", "csa2_last_error", "csa2_compress_quant", "csa2_index_score",
            "csa2_index_score_fp4q", "csa2_select_topk", "csa2_block_pool", "csa2_sparse_attend",
            "csa2_sparse_attend_rope", "csa2_decode_append", "csa2_workspace_bytes",
-           "csa2_selftest", "csa2_select_topk_noalloc", "csa2_select_attend")
+           "csa2_selftest", "csa2_select_topk_noalloc", "csa2_select_attend",
+           "csa2_peak_read", "csa2_peak_mfma")
 
 
 class Csa2Error(RuntimeError):
@@ -87,6 +90,10 @@ def lib():
                                          ctypes.POINTER(_State), P, P, P, P]
         L.csa2_workspace_bytes.restype = SZ
         L.csa2_workspace_bytes.argtypes = [I, I, I64, I]
+        L.csa2_peak_read.restype = I
+        L.csa2_peak_read.argtypes = [P, SZ, P, P]
+        L.csa2_peak_mfma.restype = ctypes.c_double
+        L.csa2_peak_mfma.argtypes = [I, P, P]
         L.csa2_selftest.restype = I
         L.csa2_selftest.argtypes = [P, I, P]
         _lib = L

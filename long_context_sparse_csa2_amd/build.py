@@ -10,7 +10,7 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libcsa2.so")
 SOURCES = ["compress.hip", "score.hip", "select.hip", "attend.hip", "attend_wide.hip",
-           "selftest.hip", "check.hip", "api.cpp"]
+           "selftest.hip", "check.hip", "peaks.hip", "api.cpp"]
 ARCH = "gfx950"
 FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-x", "hip",

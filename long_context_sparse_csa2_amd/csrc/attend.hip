@@ -577,6 +577,20 @@ hipError_t launch_attend(const uint16_t* q, const int32_t* q_seq, int Q, const u
 }
 
 // ---- fused selection + attention
+// Compute units of the current device (looked up once per device).
+static int device_cus() {
+  static int cus[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cus[dev] <= 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
+    cus[dev] = n;
+  }
+  return cus[dev];
+}
+
 // One split per 64-row chunk: the main chunks of the top-k, then two for a
 // window of up to 128 SWA rows.
 static int sa_splits(int k) { return (k + CH_ROWS - 1) / CH_ROWS + AT_MAX_SWA / CH_ROWS; }
@@ -597,8 +611,23 @@ hipError_t launch_select_attend(const float* scores, int64_t ld, int Q, const in
   const LevelDesc d = select_levels(Q, n_cols, mode);
   uint32_t* lv = (uint32_t*)ws;
   const int nsplit = sa_splits(k);
-  float* part_o = (float*)((char*)ws + align256(select_ws_bytes(Q, n_cols, mode)));
+  char* part = (char*)ws + align256(select_ws_bytes(Q, n_cols, mode));
+  float* part_o = (float*)part;
   float* part_ml = part_o + (size_t)Q * nsplit * H_ATT * D_LAT;
+  // The fused kernel pays for repeating the selection in every workgroup
+  // only while its workgroups fit on the device at once (one per CU); past
+  // that, the separate kernels (same results) are faster.
+  if (unit_grid(Q * nsplit) > (unsigned)device_cus()) {
+    hipError_t e = launch_select(scores, ld, Q, n_valid, col_ids, n_cols, kk, mode,
+                                 mode == 0 ? idx_out : pool, mode == 0 ? kk : (int64_t)kk * 8,
+                                 pool_len, mode == 1 ? k : 0, mode == 1 ? idx_out : nullptr, lv,
+                                 stream);
+    if (e != hipSuccess) return e;
+    const RopeArgs none = {nullptr, 0, 0.f, nullptr, {}};
+    return launch_attend(q, q_seq, Q, kv_codes, kv_scales, cap, idx_out, k, swa_codes, swa_scale,
+                         T_swa, swa_start, swa_len, out, lse, part, attend_ws_for(Q, nsplit),
+                         none, stream);
+  }
   hipError_t e = launch_maxima(scores, ld, Q, n_valid, n_cols, d, lv, stream);
   if (e != hipSuccess) return e;
   const int spec = Q <= 64;

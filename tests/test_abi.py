@@ -9,14 +9,17 @@ import pytest
 import long_context_sparse_csa2_amd as C
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "csa2.h")
+HEADERS = [os.path.join(ROOT, "include", h) for h in sorted(os.listdir(os.path.join(ROOT, "include")))
+           if h.endswith(".h")]
 FAKE = ctypes.c_void_p(0x10000)      # aligned, never dereferenced: every call below fails validation
 
 
 def declared():
-    src = open(HEADER).read()
-    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"\b(csa2_[a-z0-9_]+)\s*\(", src)))
+    names = set()
+    for h in HEADERS:
+        src = re.sub(r"/\*.*?\*/", "", open(h).read(), flags=re.S)
+        names |= set(re.findall(r"\b(csa2_[a-z0-9_]+)\s*\(", src))
+    return sorted(names)
 
 
 def test_exports_every_declared_symbol():
