@@ -316,6 +316,36 @@ def test_index_score_many_queries():
         assert np.array_equal(checks.host(part).view(np.uint32), s[lo:hi].view(np.uint32))
 
 
+def test_index_score_launch_composition():
+    """A 1000-query causal launch over 5000 entries and the same queries in
+    launches of 125 (which pick another tile count per wave and another
+    workgroup layout): the same score bits, and sampled rows (around the
+    tile and block edges) match the oracle."""
+    B, T, Q = 2, 5000, 1000
+    _, _, _, cache = _build(B, T, 1, seed=27)
+    q, w = _scores_inputs(Q, 28)
+    q_seq = np.ones(Q, np.int32)
+    q_seq[997] = 0                                     # one query of the last block elsewhere
+    n_vis = np.minimum(np.arange(Q) * 5 + 1, T).astype(np.int64)
+    full = torch.full((Q, T), -7.0, device=DEV)
+    C.csa2_index_score(q.to(DEV), w.to(DEV), torch.from_numpy(q_seq).to(DEV),
+                       torch.from_numpy(n_vis).to(DEV), None, T, cache, full)
+    parts = torch.full((Q, T), -7.0, device=DEV)
+    for lo in range(0, Q, 125):
+        hi = lo + 125
+        C.csa2_index_score(q[lo:hi].to(DEV), w[lo:hi].to(DEV), torch.from_numpy(q_seq[lo:hi]).to(DEV),
+                           torch.from_numpy(n_vis[lo:hi]).to(DEV), None, T, cache, parts[lo:hi])
+    torch.cuda.synchronize()
+    a, b = checks.host(full), checks.host(parts)
+    assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+    q64, w64 = checks.bf16_to_f64(q), w.double().numpy()
+    khat = [R.dequant_mxfp4(checks.host(cache.ik_codes[x]), checks.host(cache.ik_scales[x])) for x in range(B)]
+    for i in (0, 1, 7, 8, 204, 205, 206, 511, 996, 997, 998, 999):
+        nv = int(n_vis[i])
+        checks.check_scores(a[i, :nv], R.index_scores(q64[i], w64[i], khat[q_seq[i]][:nv]))
+        assert np.all(a[i, nv:] == -7.0)
+
+
 def _rand_scores(Q, n, seed, ties=True):
     rng = np.random.default_rng(seed)
     s = (rng.standard_normal((Q, n)) ** 2).astype(np.float32)
