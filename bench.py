@@ -278,6 +278,7 @@ def cpu_baseline_prefill(wl, step, seconds_target=15.0):
     done, t_total = 0, 0.0
     while t_total < seconds_target and done < len(order):
         q = int(order[done])
+        qi = q % wl.q_chunk if step.reuse else q        # row of the per-layer inputs
         hq = step.h[0, q * m:(q + 1) * m].float().cpu().numpy().astype(np.float64)
         zq = None if step.z is None else step.z[0, q * m:(q + 1) * m].float().cpu().numpy().astype(np.float64)
         t0 = time.perf_counter()
@@ -286,13 +287,13 @@ def cpu_baseline_prefill(wl, step, seconds_target=15.0):
         for li, mode in enumerate(wl.layers):
             L = step.layers[li]
             if mode == "full":
-                s = scores(L["q_idx"][q].float().cpu().numpy().astype(np.float64),
-                           L["w"][q].cpu().numpy().astype(np.float64), khat[:int(n_vis[q])])
+                s = scores(L["q_idx"][qi].float().cpu().numpy().astype(np.float64),
+                           L["w"][qi].cpu().numpy().astype(np.float64), khat[:int(n_vis[q])])
                 idx = R.topk(s, wl.k)
             sc = L["swa_codes"][0, int(s0[q]):int(s0[q]) + int(sl[q])].cpu().numpy()
             ss = L["swa_scale"][0, int(s0[q]):int(s0[q]) + int(sl[q])].cpu().numpy().astype(np.float64)
             rows = R.gather_rows(kv_c, kv_s, idx, sc, ss)
-            R.attend(L["q_attn"][q].float().cpu().numpy().astype(np.float64), rows)
+            R.attend(L["q_attn"][qi].float().cpu().numpy().astype(np.float64), rows)
         t_total += time.perf_counter() - t0
         done += 1
     threads = blas_threads()

@@ -94,8 +94,13 @@ class Step:
         self.idx = torch.empty(qc, k, dtype=torch.int32, device=device)
         self.ws_topk = workspace(CSA2_OP_TOPK, qc, N, k, device)
         self.ws_attend = workspace(CSA2_OP_ATTEND, qc, 0, k, device)
-        self.out = [torch.empty(Q, 64, 512, dtype=torch.float32, device=device) for _ in wl.layers]
-        self.lse = [torch.empty(Q, 64, dtype=torch.float32, device=device) for _ in wl.layers]
+        # per-layer inputs and outputs: every query's, or (reuse_chunk_inputs)
+        # one chunk's worth that each chunk reuses
+        self.reuse = wl.reuse_chunk_inputs and len(self.chunks) > 1
+        R = wl.input_rows if self.reuse else Q
+        self.out = [torch.empty(R, 64, 512, dtype=torch.float32, device=device) for _ in wl.layers]
+        self.lse = [torch.empty(R, 64, dtype=torch.float32, device=device) for _ in wl.layers]
+        self.out_kept = self.lse_kept = None
         self.idx_per_layer = [None] * len(wl.layers)
         self.scores_per_layer = [None] * len(wl.layers)
         if wl.hierarchical:
@@ -122,6 +127,7 @@ class Step:
         for (i0, i1) in self.chunks:
             n = i1 - i0
             rows = slice(i0, i1)
+            loc = slice(0, n) if self.reuse else rows     # rows of the inputs and outputs
             # columns the chunk can see: causal prefill query i sees i + 1 entries
             n_cols = i1 if wl.prefill else wl.N
             q_seq, n_vis = self.q_seq[rows], self.n_vis[rows]
@@ -134,7 +140,7 @@ class Step:
                     self.h[:, i0 * m:i1 * m], None if self.z is None else self.z[:, i0 * m:i1 * m],
                     m, self.w_ik, self.cache, e0=i0), (i0, i1)))
             for li, mode in enumerate(wl.layers):
-                L = {key: v[rows] if key in ("q_idx", "w", "q_attn") else v
+                L = {key: v[loc] if key in ("q_idx", "w", "q_attn") else v
                      for key, v in self.layers[li].items()}
                 if mode == "full":
                     out.append(Op("index_score_full", li, lambda L=L, q_seq=q_seq, n_vis=n_vis,
@@ -147,7 +153,7 @@ class Step:
                         nb = wl.n_blocks if wl.hierarchical else 0
                         out.append(Op("select_attend_full", li, lambda L=L, li=li, q_seq=q_seq,
                                       n_vis=n_vis, n_cols=n_cols, scores=scores, idx=idx_full,
-                                      swa_start=swa_start, swa_len=swa_len, rows=rows, nb=nb:
+                                      swa_start=swa_start, swa_len=swa_len, rows=loc, nb=nb:
                                       csa2_select_attend(
                             scores, n_vis, None, n_cols, wl.k, idx, L["q_attn"], q_seq, self.cache,
                             L["swa_codes"], L["swa_scale"], swa_start, swa_len,
@@ -181,7 +187,7 @@ class Step:
                         self.pool_scores, self.pool_len, self.pool, self.P, wl.k, idx,
                         self.ws_topk_pool), (i0, i1)))
                 out.append(Op("sparse_attend", li, lambda L=L, li=li, idx=idx, q_seq=q_seq,
-                              swa_start=swa_start, swa_len=swa_len, rows=rows: csa2_sparse_attend(
+                              swa_start=swa_start, swa_len=swa_len, rows=loc: csa2_sparse_attend(
                     L["q_attn"], q_seq, self.cache, idx, L["swa_codes"], L["swa_scale"],
                     swa_start, swa_len, self.out[li][rows], self.lse[li][rows], self.ws_attend),
                     (i0, i1)))
@@ -219,6 +225,12 @@ class Step:
                     self.idx_per_layer[li] = torch.empty(nk, wl.k, dtype=torch.int32,
                                                          device=self.device)
                 self.idx_per_layer[li][dst] = src_idx.index_select(0, src_rows)
+                if self.reuse:                  # outputs are overwritten by the next chunk
+                    if self.out_kept is None:
+                        self.out_kept = [torch.empty(nk, 64, 512, device=self.device) for _ in wl.layers]
+                        self.lse_kept = [torch.empty(nk, 64, device=self.device) for _ in wl.layers]
+                    self.out_kept[li][dst] = self.out[li].index_select(0, src_rows)
+                    self.lse_kept[li][dst] = self.lse[li].index_select(0, src_rows)
                 if mode in ("full", "reindex"):
                     src = self.scores if mode == "full" else self.pool_scores
                     if self.scores_per_layer[li] is None:

@@ -47,6 +47,11 @@ class Workload:
                 one decode query per sequence
     q_chunk     prefill queries per chunk (0: all at once)
     draw_device draw the per-layer inputs on the device (large prefills)
+    reuse_chunk_inputs  the per-layer queries are drawn for one chunk of
+                q_chunk queries and every chunk uses them (and writes its
+                outputs into one chunk-sized buffer): at 2^19 queries the
+                full-size query and output tensors would not fit in memory,
+                and the work of a chunk does not depend on the values
     """
     name: str
     seed: int
@@ -62,6 +67,7 @@ class Workload:
     n_blocks: int = 2048
     q_chunk: int = 0
     draw_device: bool = False
+    reuse_chunk_inputs: bool = False
     note: str = ""
 
     @property
@@ -96,9 +102,14 @@ class Workload:
         w = torch.randn(128, 512, dtype=torch.float32, generator=g) / math.sqrt(512.0)
         return w.to(torch.bfloat16).to(device)
 
+    @property
+    def input_rows(self):
+        """Rows of the per-layer query tensors (and of the step's outputs)."""
+        return self.q_chunk if (self.reuse_chunk_inputs and self.q_chunk) else self.Q
+
     def layer_inputs(self, layer, device="cpu"):
         """Per-layer queries and SWA rows (drawn on the CPU, then moved)."""
-        Q = self.Q
+        Q = self.input_rows
         out = {}
         dd = device if self.draw_device else "cpu"
         g = _gen(self.seed, "q_idx", layer, dd)
@@ -161,6 +172,11 @@ WORKLOADS = {
                      layers=["full", "reuse", "reuse", "reuse", "reuse", "reuse"], prefill=True,
                      q_chunk=4096, draw_device=True,
                      note="encoder group prefill of 65,536 raw tokens (m=2) in 4096-query chunks"),
+    "p1m": Workload("p1m", 6, B=1, T=1 << 20, m=2,
+                    layers=["full", "reuse", "reuse", "reuse", "reuse", "reuse"], prefill=True,
+                    q_chunk=4096, draw_device=True, reuse_chunk_inputs=True,
+                    note="encoder group prefill of 1,048,576 raw tokens (m=2) in 4096-query "
+                         "chunks, one chunk's queries reused by every chunk"),
 }
 
 

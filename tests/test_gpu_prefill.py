@@ -83,3 +83,42 @@ def test_p64k_sampled_against_oracle():
             rows = R.gather_rows(kv_c, kv_s, idx[j], sc, ss)
             checks.check_attention(checks.host(step.out[li][q]), checks.host(step.lse[li][q]),
                                    checks.bf16_to_f64(L["q_attn"][q]), rows)
+
+
+def test_p1m_sampled_against_oracle():
+    """The 1,048,576-raw-token end of the chunked prefill (2^19 queries in
+    128 chunks of 4096; one chunk's queries reused by every chunk): sampled
+    queries across the causal range -- scores against the oracle over all
+    their visible entries (up to 2^19), the exact top-512 of the GPU's
+    scores and its fp64 ranking within the tie bar, and every layer's
+    attention over the GPU's selection."""
+    wl = synth.WORKLOADS["p1m"]
+    step = Step(wl, DEV)
+    assert step.reuse and len(step.chunks) == 128
+    keep = sorted({0, 511, 4095, 4096, 262143, 262144, wl.Q - 1} |
+                  set(np.random.default_rng(7).integers(0, wl.Q, 4).tolist()))
+    print(f"[p1m] step with {len(step.chunks)} chunks, checking queries {keep}", flush=True)
+    step.run(keep=True, keep_rows=keep)
+    torch.cuda.synchronize()
+    ik_c, ik_s = checks.host(step.cache.ik_codes[0]), checks.host(step.cache.ik_scales[0])
+    kv_c, kv_s = checks.host(step.cache.kv_codes[0]), checks.host(step.cache.kv_scales[0])
+    s0, sl = checks.host(step.swa_start), checks.host(step.swa_len)
+    s_gpu = checks.host(step.scores_per_layer[0])
+    idx = checks.host(step.idx_per_layer[0])
+    L0 = step.layers[0]
+    for j, q in enumerate(keep):
+        qi = q % wl.q_chunk
+        nv = q + 1
+        ref = checks.full_index_scores(checks.bf16_to_f64(L0["q_idx"][qi]),
+                                       checks.host(L0["w"][qi]).astype(np.float64), ik_c, ik_s, nv)
+        checks.check_scores(s_gpu[j, :nv], ref)
+        checks.check_topk_exact(idx[j], s_gpu[j, :nv], wl.k)
+        checks.check_topk_tolerance(idx[j], ref, wl.k)
+        for li in range(len(wl.layers)):
+            assert np.array_equal(checks.host(step.idx_per_layer[li])[j], idx[j])   # Reuse layers
+            L = step.layers[li]
+            sc, ss = checks.swa_rows(checks.host(L["swa_codes"][0]), checks.host(L["swa_scale"][0]).astype(np.float64),
+                                     int(s0[q]), int(sl[q]))
+            rows = R.gather_rows(kv_c, kv_s, idx[j], sc, ss)
+            checks.check_attention(checks.host(step.out_kept[li][j]), checks.host(step.lse_kept[li][j]),
+                                   checks.bf16_to_f64(L["q_attn"][qi]), rows)
