@@ -21,9 +21,9 @@
 //            registers as fp16 (each head scaled by a power of two, undone
 //            on S), as B; a lane then holds one head's scores for 16 rows
 //   softmax  per head within the wave (in-lane, then the lanes xor 16 and
-//            32); the reference max only moves when a chunk beats it by more
-//            than e^8, so O is rescaled in few chunks; P^T and the per-head
-//            rescale factors go to LDS
+//            32 by row-swapping permutes); the reference max only moves
+//            when a chunk beats it by more than e^8, so O is rescaled in
+//            few chunks; P^T and the per-head rescale factors go to LDS
 //   O^T += V^T P^T  512 dims x 64 heads, wave w: dims 128w .. +127 for all
 //            heads, so every staged value is read once; V^T through
 //            transposing LDS reads of the staged rows, P^T from LDS
@@ -122,8 +122,7 @@ __global__ __launch_bounds__(AW_THREADS, 2) void k_attend_wide(
     for (int s = 0; s < 16; ++s)
 #pragma unroll
       for (int j = 0; j < 8; ++j) mx = fmaxf(mx, fabsf(xf[s][j]));
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    mx = lanes_max32(lanes_max16(mx));
     const int e = q_exponent(mx);
     const float f = ldexpf(1.f, e);
 #pragma unroll
@@ -184,8 +183,7 @@ __global__ __launch_bounds__(AW_THREADS, 2) void k_attend_wide(
     for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
       for (int j = 0; j < 4; ++j) cm = fmaxf(cm, s[rt][j]);
-    cm = fmaxf(cm, __shfl_xor(cm, 16));
-    cm = fmaxf(cm, __shfl_xor(cm, 32));
+    cm = lanes_max32(lanes_max16(cm));
     // the reference max moves only when a chunk exceeds it by more than
     // AW_LAZY (P then stays below e^AW_LAZY, far inside fp16)
     const float m_new = cm > m_run + AW_LAZY ? cm : m_run;
@@ -205,8 +203,7 @@ __global__ __launch_bounds__(AW_THREADS, 2) void k_attend_wide(
       *(f16x4_t*)&pt[head][16 * rt + 4 * qd] = pv;
     }
     if (m_new != -INFINITY) alpha = exp_hw(m_run - m_new);          // 0 when m_run is -inf
-    psum += __shfl_xor(psum, 16);
-    psum += __shfl_xor(psum, 32);
+    psum = lanes_sum32(lanes_sum16(psum));
     l_run = l_run * alpha + psum;
     m_run = m_new;
     if (qd == 0) head_a[head] = alpha;

@@ -192,6 +192,28 @@ __device__ __forceinline__ f32x4_t mfma16_f16(f16x8_t a, f16x8_t b, f32x4_t c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }
 
+// ----------------------------------------------------- lane-pair sums / maxima
+// x combined with the value of lane l ^ 16 (or l ^ 32), by the gfx950
+// row-swapping permutes (VALU, no LDS round trip); both lanes of a pair get
+// the same result, bit for bit, since max and a two-term sum do not depend
+// on the operand order.  Every lane must be active.
+__device__ __forceinline__ float lanes_max16(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float lanes_max32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float lanes_sum16(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float lanes_sum32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // ------------------------------------------------------------ wave scans
 // Inclusive scan over the 64 lanes of a wave with DPP: Hillis-Steele shifts
 // inside each 16-lane row, then the row_bcast:15 / row_bcast:31 steps carry

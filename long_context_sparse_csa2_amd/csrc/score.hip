@@ -15,9 +15,10 @@
 // them to bf16 with the gfx950 scaled FP4 conversion (exact for the
 // power-of-two E8M0 scales).  The ReLU, the head weights and the head sum
 // are applied to the accumulator in registers and the two lane halves are
-// summed with one cross-lane exchange, so only 4 bytes per entry are
-// written.  Each wave keeps the bytes of its next two tiles in flight while
-// it converts and multiplies the current one.
+// summed with one cross-lane exchange (a row-swapping permute, no LDS round
+// trip), so only 4 bytes per entry are written.  Each wave keeps the bytes
+// of its next two tiles in flight while it converts and multiplies the
+// current one.
 //
 // MXFP4-query variant (report section 2.4.4: V4 trains the indexer Q and K
 // for OCP MXFP4 so that the index product is an FP4 matrix multiply): the
@@ -223,7 +224,7 @@ __global__ __launch_bounds__(256) void k_index_score(
     float part = 0.f;
 #pragma unroll
     for (int j = 0; j < 16; ++j) part += wr[j] * relu_f32(acc[j]);
-    part += __shfl_xor(part, 32);
+    part = lanes_sum32(part);
     const int64_t c = col0 + r;
     const int off = half == 0 && c < nv ? (int)(c * 4) : (int)0x80000000;
     __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(part), srs, off, 0, 0);
