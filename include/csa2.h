@@ -342,6 +342,50 @@ csa2_status csa2_select_attend(const float* scores, int64_t ld, int Q, const int
                                const int64_t* swa_start, const int32_t* swa_len, float* out,
                                float* lse, void* ws, size_t ws_bytes, void* stream);
 
+/*
+ * (4b) Full scan that also lays down the selection's block maxima, and the
+ * fused selection + attention that starts from them.
+ *
+ * The report runs each layer as a few fused kernels (section 3.2); here the
+ * first pass of the top-k / block-pool selection (the maximum score of
+ * every 8 and every 64 consecutive columns, the lowest levels of its 8-way
+ * maxima pyramid) moves into the scan's epilogue, so the selection that
+ * follows does not read the scores once more before it starts.
+ *
+ * csa2_index_score_levels = csa2_index_score (or _fp4q with fp4q != 0) with
+ * cand = NULL, plus the maxima levels of those scores written into ws, laid
+ * out for a selection of mode n_blocks > 0 (block pool) or n_blocks == 0
+ * (top-k) over Q x n_cols (levels the scan epilogue cannot produce are
+ * computed by a maxima pass after the scan; the contents are the same).
+ *   n_cols   <= CSA2_MAX_COLS (and as for csa2_index_score)
+ *   n_blocks 0 or the block count of the csa2_select_attend_levels call that
+ *            follows (only its sign matters here)
+ *   ws       256-byte aligned, at least csa2_workspace_bytes(CSA2_OP_TOPK or
+ *            CSA2_OP_POOL, Q, n_cols, 1) bytes: normally the workspace of the
+ *            csa2_select_attend_levels call that follows, whose first part
+ *            holds the levels
+ *
+ * csa2_select_attend_levels = csa2_select_attend (same arguments, outputs,
+ * workspace and errors) without its own maxima pass: ws must hold the
+ * levels a csa2_index_score_levels call wrote for these scores with
+ * n_vis == n_valid, the same Q, n_cols and the same sign of n_blocks, and
+ * col_ids must be NULL.  Levels from other scores give a wrong (though
+ * in-bounds) selection.
+ */
+csa2_status csa2_index_score_levels(const uint16_t* q_idx, const float* w, const int32_t* q_seq,
+                                    const int64_t* n_vis, int Q, int64_t n_cols,
+                                    const csa2_cache* src, float* scores, int64_t ld, int fp4q,
+                                    int n_blocks, void* ws, size_t ws_bytes, void* stream);
+csa2_status csa2_select_attend_levels(const float* scores, int64_t ld, int Q,
+                                      const int64_t* n_valid, const int32_t* col_ids,
+                                      int64_t n_cols, int k, int32_t* idx, int n_blocks,
+                                      int32_t* pool, int64_t* pool_len, const uint16_t* q,
+                                      const int32_t* q_seq, const csa2_cache* src,
+                                      const uint8_t* swa_codes, const float* swa_scale,
+                                      int64_t T_swa, const int64_t* swa_start,
+                                      const int32_t* swa_len, float* out, float* lse, void* ws,
+                                      size_t ws_bytes, void* stream);
+
 /* Rotary position embedding of csa2_sparse_attend_rope (host struct). */
 typedef struct {
   const int64_t* q_pos;   /* [Q] position of each query (device); may be NULL iff dims == 0 */

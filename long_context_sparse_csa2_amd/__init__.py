@@ -24,6 +24,7 @@ EXPORTS = ("csa2_status_string", "csa2_last_error", "csa2_compress_quant", "csa2
            "csa2_index_score_fp4q", "csa2_select_topk", "csa2_block_pool", "csa2_sparse_attend",
            "csa2_sparse_attend_rope", "csa2_decode_append", "csa2_workspace_bytes",
            "csa2_selftest", "csa2_select_topk_noalloc", "csa2_select_attend",
+           "csa2_index_score_levels", "csa2_select_attend_levels",
            "csa2_peak_read", "csa2_peak_mfma")
 
 
@@ -72,9 +73,13 @@ def lib():
             fn.argtypes = [P, P, P, P, P, I64, I, I64, ctypes.POINTER(_Cache), P, I64, P]
         L.csa2_select_topk.restype = I
         L.csa2_select_topk.argtypes = [P, I64, I, P, P, I64, I, P, P, SZ, P]
-        L.csa2_select_attend.restype = I
-        L.csa2_select_attend.argtypes = [P, I64, I, P, P, I64, I, P, I, P, P, P, P,
-                                         ctypes.POINTER(_Cache), P, P, I64, P, P, P, P, P, SZ, P]
+        for fn in (L.csa2_select_attend, L.csa2_select_attend_levels):
+            fn.restype = I
+            fn.argtypes = [P, I64, I, P, P, I64, I, P, I, P, P, P, P,
+                           ctypes.POINTER(_Cache), P, P, I64, P, P, P, P, P, SZ, P]
+        L.csa2_index_score_levels.restype = I
+        L.csa2_index_score_levels.argtypes = [P, P, P, P, I, I64, ctypes.POINTER(_Cache), P, I64,
+                                              I, I, P, SZ, P]
         L.csa2_select_topk_noalloc.restype = I
         L.csa2_select_topk_noalloc.argtypes = [P, I64, I, P, P, I64, I, P, P]
         L.csa2_block_pool.restype = I
@@ -219,6 +224,24 @@ def csa2_index_score(q_idx, w, q_seq, n_vis, cand, n_cols, cache, scores, stream
     _check(name, st)
 
 
+def csa2_index_score_levels(q_idx, w, q_seq, n_vis, n_cols, cache, scores, ws, n_blocks=0,
+                            fp4q=False, stream=None):
+    """csa2_index_score over all columns (no candidate list) that also writes
+    the selection's maxima levels into ws (the workspace of the
+    csa2_select_attend(..., levels=True) call that follows, of the same
+    n_blocks sign)."""
+    _dtype(q_idx, torch.bfloat16, "q_idx"); _dtype(w, torch.float32, "w")
+    _dtype(q_seq, torch.int32, "q_seq"); _dtype(n_vis, torch.int64, "n_vis")
+    _dtype(scores, torch.float32, "scores")
+    Q = q_idx.shape[0]
+    wsb = ws.numel() * ws.element_size() if ws is not None else 0
+    cs = cache.c_struct()
+    st = lib().csa2_index_score_levels(_ptr(q_idx), _ptr(w), _ptr(q_seq), _ptr(n_vis), Q, n_cols,
+                                       ctypes.byref(cs), _ptr(scores), scores.shape[1], int(fp4q),
+                                       n_blocks, _ptr(ws), wsb, _stream(stream, q_idx))
+    _check("csa2_index_score_levels", st)
+
+
 def csa2_select_topk(scores, n_valid, col_ids, n_cols, k, out, ws=None, stream=None):
     """scores [Q, ld] f32, n_valid [Q] i64, col_ids None or [Q, ld] i32,
     out [Q, k] i32; ws a uint8 tensor of csa2_workspace_bytes(TOPK, ...)."""
@@ -243,11 +266,13 @@ def csa2_select_topk_noalloc(scores, n_valid, col_ids, n_cols, k, out, stream=No
 
 def csa2_select_attend(scores, n_valid, col_ids, n_cols, k, idx, q, q_seq, cache, swa_codes,
                        swa_scale, swa_start, swa_len, out, lse=None, ws=None, n_blocks=0,
-                       pool=None, pool_len=None, stream=None):
+                       pool=None, pool_len=None, stream=None, levels=False):
     """Top-k (n_blocks == 0, col_ids optional) or pool + top-k (n_blocks > 0)
     fused with the attention over the selected rows; idx [Q, k] i32, out
     [Q, 64, 512] f32; ws from workspace(CSA2_OP_SELECT_ATTEND or
-    CSA2_OP_POOL_ATTEND, Q, n_cols, k)."""
+    CSA2_OP_POOL_ATTEND, Q, n_cols, k).  levels=True calls
+    csa2_select_attend_levels: ws already holds the maxima levels that
+    csa2_index_score_levels wrote for these scores."""
     _dtype(scores, torch.float32, "scores"); _dtype(n_valid, torch.int64, "n_valid")
     _dtype(col_ids, torch.int32, "col_ids"); _dtype(idx, torch.int32, "idx")
     _dtype(pool, torch.int32, "pool"); _dtype(pool_len, torch.int64, "pool_len")
@@ -259,12 +284,13 @@ def csa2_select_attend(scores, n_valid, col_ids, n_cols, k, idx, q, q_seq, cache
     T_swa = swa_codes.shape[1] if swa_codes is not None else 0
     wsb = ws.numel() * ws.element_size() if ws is not None else 0
     cs = cache.c_struct()
-    st = lib().csa2_select_attend(_ptr(scores), scores.shape[1], Q, _ptr(n_valid), _ptr(col_ids),
-                                  n_cols, k, _ptr(idx), n_blocks, _ptr(pool), _ptr(pool_len),
-                                  _ptr(q), _ptr(q_seq), ctypes.byref(cs), _ptr(swa_codes),
-                                  _ptr(swa_scale), T_swa, _ptr(swa_start), _ptr(swa_len),
-                                  _ptr(out), _ptr(lse), _ptr(ws), wsb, _stream(stream, scores))
-    _check("csa2_select_attend", st)
+    name = "csa2_select_attend_levels" if levels else "csa2_select_attend"
+    st = getattr(lib(), name)(_ptr(scores), scores.shape[1], Q, _ptr(n_valid), _ptr(col_ids),
+                              n_cols, k, _ptr(idx), n_blocks, _ptr(pool), _ptr(pool_len),
+                              _ptr(q), _ptr(q_seq), ctypes.byref(cs), _ptr(swa_codes),
+                              _ptr(swa_scale), T_swa, _ptr(swa_start), _ptr(swa_len),
+                              _ptr(out), _ptr(lse), _ptr(ws), wsb, _stream(stream, scores))
+    _check(name, st)
 
 
 def csa2_block_pool(scores, n_valid, n_cols, n_blocks, pool, pool_len, ws=None, block=8,

@@ -13,6 +13,7 @@
 #include <cstring>
 
 #include "launch.h"
+#include "select_core.h"
 
 static_assert(CSA2_NOALLOC_SCRATCH_BYTES == csa2::SEL_SCRATCH_BYTES,
               "the header states the static scratch size");
@@ -156,7 +157,9 @@ static csa2_status index_score_common(const uint16_t* q_idx, const float* w,
                                       const int32_t* q_seq, const int64_t* n_vis,
                                       const int32_t* cand, int64_t ld_cand, int Q, int64_t n_cols,
                                       const csa2_cache* src, float* scores, int64_t ld,
-                                      void* stream, bool fp4q) {
+                                      void* stream, bool fp4q,
+                                      const csa2::LevelDesc* levels = nullptr,
+                                      uint32_t* lv = nullptr) {
   REQ(q_idx && w && q_seq && n_vis && scores, "q_idx, w, q_seq, n_vis, scores must not be NULL");
   const csa2_status cs = check_cache(src);
   if (cs != CSA2_OK) return cs;
@@ -179,8 +182,9 @@ static csa2_status index_score_common(const uint16_t* q_idx, const float* w,
   }
   return hip_status(csa2::launch_index_score(q_idx, w, q_seq, n_vis, cand, ld_cand, Q, n_cols,
                                              src->ik_codes, src->ik_scales, src->cap, scores, ld,
-                                             fp4q, (hipStream_t)stream),
-                    fp4q ? "csa2_index_score_fp4q launch" : "csa2_index_score launch");
+                                             fp4q, (hipStream_t)stream, levels, lv),
+                    levels ? "csa2_index_score_levels launch"
+                           : fp4q ? "csa2_index_score_fp4q launch" : "csa2_index_score launch");
 }
 
 csa2_status csa2_index_score(const uint16_t* q_idx, const float* w, const int32_t* q_seq,
@@ -199,6 +203,27 @@ csa2_status csa2_index_score_fp4q(const uint16_t* q_idx, const float* w, const i
   g_err[0] = 0;
   return index_score_common(q_idx, w, q_seq, n_vis, cand, ld_cand, Q, n_cols, src, scores, ld,
                             stream, true);
+}
+
+csa2_status csa2_index_score_levels(const uint16_t* q_idx, const float* w, const int32_t* q_seq,
+                                    const int64_t* n_vis, int Q, int64_t n_cols,
+                                    const csa2_cache* src, float* scores, int64_t ld, int fp4q,
+                                    int n_blocks, void* ws, size_t ws_bytes, void* stream) {
+  g_err[0] = 0;
+  REQ(Q > 0, "Q=%d must be > 0", Q);
+  REQ(n_blocks >= 0 && n_blocks <= CSA2_MAX_K, "n_blocks=%d must be in [0, %d]", n_blocks,
+      CSA2_MAX_K);
+  REQ(n_cols >= 0 && n_cols <= CSA2_MAX_COLS, "n_cols=%lld must be in [0, %d]",
+      (long long)n_cols, CSA2_MAX_COLS);
+  const int mode = n_blocks > 0 ? 1 : 0;
+  const size_t need = csa2::select_ws_bytes(Q, n_cols, mode);
+  if (!ws || ws_bytes < need)
+    return fail(CSA2_EWORKSPACE, "workspace %zu bytes < %zu needed", ws ? ws_bytes : (size_t)0,
+                need);
+  REQ(al(ws, 256), "ws must be 256-byte aligned");
+  const csa2::LevelDesc d = csa2::select_levels(Q, n_cols, mode);
+  return index_score_common(q_idx, w, q_seq, n_vis, nullptr, 0, Q, n_cols, src, scores, ld,
+                            stream, fp4q != 0, &d, (uint32_t*)ws);
 }
 
 static csa2_status select_common(const float* scores, int64_t ld, int Q, const int64_t* n_valid,
@@ -276,14 +301,15 @@ csa2_status csa2_block_pool(const float* scores, int64_t ld, int Q, const int64_
                     "csa2_block_pool launch");
 }
 
-csa2_status csa2_select_attend(const float* scores, int64_t ld, int Q, const int64_t* n_valid,
-                               const int32_t* col_ids, int64_t n_cols, int k, int32_t* idx,
-                               int n_blocks, int32_t* pool, int64_t* pool_len, const uint16_t* q,
-                               const int32_t* q_seq, const csa2_cache* src,
-                               const uint8_t* swa_codes, const float* swa_scale, int64_t T_swa,
-                               const int64_t* swa_start, const int32_t* swa_len, float* out,
-                               float* lse, void* ws, size_t ws_bytes, void* stream) {
-  g_err[0] = 0;
+static csa2_status select_attend_common(const float* scores, int64_t ld, int Q,
+                                        const int64_t* n_valid, const int32_t* col_ids,
+                                        int64_t n_cols, int k, int32_t* idx, int n_blocks,
+                                        int32_t* pool, int64_t* pool_len, const uint16_t* q,
+                                        const int32_t* q_seq, const csa2_cache* src,
+                                        const uint8_t* swa_codes, const float* swa_scale,
+                                        int64_t T_swa, const int64_t* swa_start,
+                                        const int32_t* swa_len, float* out, float* lse, void* ws,
+                                        size_t ws_bytes, void* stream, bool levels_ready) {
   REQ(scores && n_valid && idx && q && q_seq && out && swa_start && swa_len,
       "scores, n_valid, idx, q, q_seq, out, swa_start, swa_len must not be NULL");
   REQ(Q > 0 && Q < 256, "Q=%d must be in [1, 255] (larger batches: the separate calls)", Q);
@@ -315,8 +341,37 @@ csa2_status csa2_select_attend(const float* scores, int64_t ld, int Q, const int
                                                mode == 1 ? n_blocks : k, k, idx, pool, pool_len,
                                                q, q_seq, src->kv_codes, src->kv_scales, src->cap,
                                                swa_codes, swa_scale, T_swa, swa_start, swa_len,
-                                               out, lse, ws, (hipStream_t)stream),
-                    "csa2_select_attend launch");
+                                               out, lse, ws, (hipStream_t)stream, levels_ready),
+                    levels_ready ? "csa2_select_attend_levels launch" : "csa2_select_attend launch");
+}
+
+csa2_status csa2_select_attend(const float* scores, int64_t ld, int Q, const int64_t* n_valid,
+                               const int32_t* col_ids, int64_t n_cols, int k, int32_t* idx,
+                               int n_blocks, int32_t* pool, int64_t* pool_len, const uint16_t* q,
+                               const int32_t* q_seq, const csa2_cache* src,
+                               const uint8_t* swa_codes, const float* swa_scale, int64_t T_swa,
+                               const int64_t* swa_start, const int32_t* swa_len, float* out,
+                               float* lse, void* ws, size_t ws_bytes, void* stream) {
+  g_err[0] = 0;
+  return select_attend_common(scores, ld, Q, n_valid, col_ids, n_cols, k, idx, n_blocks, pool,
+                              pool_len, q, q_seq, src, swa_codes, swa_scale, T_swa, swa_start,
+                              swa_len, out, lse, ws, ws_bytes, stream, false);
+}
+
+csa2_status csa2_select_attend_levels(const float* scores, int64_t ld, int Q,
+                                      const int64_t* n_valid, const int32_t* col_ids,
+                                      int64_t n_cols, int k, int32_t* idx, int n_blocks,
+                                      int32_t* pool, int64_t* pool_len, const uint16_t* q,
+                                      const int32_t* q_seq, const csa2_cache* src,
+                                      const uint8_t* swa_codes, const float* swa_scale,
+                                      int64_t T_swa, const int64_t* swa_start,
+                                      const int32_t* swa_len, float* out, float* lse, void* ws,
+                                      size_t ws_bytes, void* stream) {
+  g_err[0] = 0;
+  REQ(!col_ids, "col_ids must be NULL (the levels are those of a full scan)");
+  return select_attend_common(scores, ld, Q, n_valid, col_ids, n_cols, k, idx, n_blocks, pool,
+                              pool_len, q, q_seq, src, swa_codes, swa_scale, T_swa, swa_start,
+                              swa_len, out, lse, ws, ws_bytes, stream, true);
 }
 
 static csa2_status attend_common(const uint16_t* q, const int32_t* q_seq, int Q,

@@ -607,7 +607,7 @@ hipError_t launch_select_attend(const float* scores, int64_t ld, int Q, const in
                                 const uint8_t* kv_scales, int64_t cap, const uint8_t* swa_codes,
                                 const float* swa_scale, int64_t T_swa, const int64_t* swa_start,
                                 const int32_t* swa_len, float* out, float* lse, void* ws,
-                                hipStream_t stream) {
+                                hipStream_t stream, bool levels_ready) {
   const LevelDesc d = select_levels(Q, n_cols, mode);
   uint32_t* lv = (uint32_t*)ws;
   const int nsplit = sa_splits(k);
@@ -621,15 +621,17 @@ hipError_t launch_select_attend(const float* scores, int64_t ld, int Q, const in
     hipError_t e = launch_select(scores, ld, Q, n_valid, col_ids, n_cols, kk, mode,
                                  mode == 0 ? idx_out : pool, mode == 0 ? kk : (int64_t)kk * 8,
                                  pool_len, mode == 1 ? k : 0, mode == 1 ? idx_out : nullptr, lv,
-                                 stream);
+                                 stream, levels_ready);
     if (e != hipSuccess) return e;
     const RopeArgs none = {nullptr, 0, 0.f, nullptr, {}};
     return launch_attend(q, q_seq, Q, kv_codes, kv_scales, cap, idx_out, k, swa_codes, swa_scale,
                          T_swa, swa_start, swa_len, out, lse, part, attend_ws_for(Q, nsplit),
                          none, stream);
   }
-  hipError_t e = launch_maxima(scores, ld, Q, n_valid, n_cols, d, lv, stream);
-  if (e != hipSuccess) return e;
+  if (!levels_ready) {
+    hipError_t e = launch_maxima(scores, ld, Q, n_valid, n_cols, d, lv, stream);
+    if (e != hipSuccess) return e;
+  }
   const int spec = Q <= 64;
   const int vec_out = mode == 1 && ((uintptr_t)pool & 15) == 0;
   if (mode == 0)

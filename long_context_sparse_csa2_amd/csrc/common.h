@@ -213,6 +213,10 @@ __device__ __forceinline__ float lanes_sum32(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
+__device__ __forceinline__ uint32_t lanes_max16u(uint32_t x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+  return max((uint32_t)r[0], (uint32_t)r[1]);
+}
 
 // ------------------------------------------------------------ wave scans
 // Inclusive scan over the 64 lanes of a wave with DPP: Hillis-Steele shifts
@@ -248,6 +252,10 @@ __device__ __forceinline__ uint32_t wave_min_all(uint32_t v) {
 template <int CTRL>
 __device__ __forceinline__ float dpp_mov(float v) {
   return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xf, 0xf, false));
+}
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_movu(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xf, 0xf, false);
 }
 __device__ __forceinline__ float row16_max(float v) {
   v = fmaxf(v, dpp_mov<0xb1>(v));     // quad_perm [1,0,3,2]

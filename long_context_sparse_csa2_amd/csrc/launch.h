@@ -35,11 +35,16 @@ hipError_t launch_append(const uint16_t* h_new, const uint16_t* z_new, const uin
                          float* swa_scale, int64_t W, int64_t* n_vis, int64_t* swa_start,
                          int32_t* swa_len, hipStream_t stream);
 
+struct LevelDesc;
+// levels != nullptr (full scans only): also writes the selection's maxima
+// levels (laid out by `levels`) into lv, from the scan's epilogue when levels
+// 1-2 are all there are, else by the maxima kernel after the scan.
 hipError_t launch_index_score(const uint16_t* q_idx, const float* w, const int32_t* q_seq,
                               const int64_t* n_vis, const int32_t* cand, int64_t ld_cand, int Q,
                               int64_t n_cols, const uint8_t* ik_codes, const uint8_t* ik_scales,
                               int64_t cap, float* scores, int64_t ld, bool fp4q,
-                              hipStream_t stream);
+                              hipStream_t stream, const LevelDesc* levels = nullptr,
+                              uint32_t* lv = nullptr);
 
 // Selection: mode 0 = top-k of columns (levels down to 0), mode 1 = block
 // pool (levels down to 1, blocks of 8).
@@ -48,10 +53,12 @@ size_t select_ws_bytes(int Q, int64_t n_cols, int mode);
 // device address on the current device (looked up on the first call there).
 constexpr size_t SEL_SCRATCH_BYTES = (size_t)16 << 20;
 hipError_t select_scratch(void** ptr);
+// levels_ready: ws already holds the maxima levels of these scores (a scan
+// with levels wrote them), so the maxima kernel is skipped.
 hipError_t launch_select(const float* scores, int64_t ld, int Q, const int64_t* n_valid,
                          const int32_t* col_ids, int64_t n_cols, int kk, int mode, int32_t* out,
                          int64_t out_ld, int64_t* out_len, int k2, int32_t* out2, void* ws,
-                         hipStream_t stream);
+                         hipStream_t stream, bool levels_ready = false);
 
 size_t attend_ws_bytes(int Q, int k);
 hipError_t launch_attend(const uint16_t* q, const int32_t* q_seq, int Q, const uint8_t* kv_codes,
@@ -72,7 +79,7 @@ hipError_t launch_select_attend(const float* scores, int64_t ld, int Q, const in
                                 const uint8_t* kv_scales, int64_t cap, const uint8_t* swa_codes,
                                 const float* swa_scale, int64_t T_swa, const int64_t* swa_start,
                                 const int32_t* swa_len, float* out, float* lse, void* ws,
-                                hipStream_t stream);
+                                hipStream_t stream, bool levels_ready = false);
 
 hipError_t launch_attend_wide(const uint16_t* q, const int32_t* q_seq, int Q,
                               const uint8_t* kv_codes, const uint8_t* kv_scales, int64_t cap,

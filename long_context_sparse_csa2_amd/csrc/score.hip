@@ -33,8 +33,17 @@
 // exactly one MX block with one scale byte per operand.  Products of E2M1
 // values with power-of-two scales are exact; only the fp32 accumulation
 // rounds.
+//
+// Level variant (LV): the scan also writes the first two levels of the
+// selection's 8-way maxima pyramid (the maximum score key of every 8 and
+// every 64 consecutive columns), so the top-k / block-pool selection that
+// follows starts without a pass of its own over the scores.  A wave then
+// scores its tiles in adjacent pairs (64 columns, one level-2 group); the
+// 8-column maxima come from DPP lane permutations inside the tile, the
+// 64-column maximum from the tile pair.
 #include "common.h"
 #include "launch.h"
+#include "select_core.h"
 
 namespace csa2 {
 
@@ -43,6 +52,17 @@ constexpr int SC_WAVES = 4;
 // 32-bit data format, so a store is range-checked in bytes against the
 // resource's record count.
 constexpr int SC_RSRC_WORD3 = 0x00020000;
+
+// A raw buffer resource over `bytes` bytes at p (both uniform, so the
+// resource sits in scalar registers): a store at an offset past `bytes` is
+// dropped by the hardware.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, int64_t bytes) {
+  const uint64_t a = (uint64_t)(uintptr_t)p;
+  const uint64_t au = (uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)a) |
+                      ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(a >> 32)) << 32);
+  return __builtin_amdgcn_make_buffer_rsrc((void*)(uintptr_t)au, (short)0,
+                                           __builtin_amdgcn_readfirstlane((int)bytes), SC_RSRC_WORD3);
+}
 
 typedef int i32x8_t __attribute__((ext_vector_type(8)));
 
@@ -93,15 +113,17 @@ __device__ __forceinline__ void quant_query_fp4(const uint16_t* __restrict__ qro
 // TPW: 32-entry tiles per wave; DEPTH: tiles whose bytes are in flight ahead
 // of the one being multiplied.  Workgroup chunk c starts at column
 // c * chunk_stride (+ 32 per wave) and a wave's consecutive tiles are
-// tile_stride columns apart.
-template <bool CAND, bool FP4Q, int TPW, int DEPTH>
-__global__ __launch_bounds__(256) void k_index_score(
+// tile_stride columns apart; with LV (+ 64 per wave) a wave's tiles 2p and
+// 2p + 1 are adjacent and its pairs tile_stride columns apart.
+template <bool CAND, bool FP4Q, int TPW, int DEPTH, bool LV>
+__global__ __launch_bounds__(256, 4) void k_index_score(
     const uint16_t* __restrict__ q_idx, const float* __restrict__ w,
     const int32_t* __restrict__ q_seq, const int64_t* __restrict__ n_vis,
     const int32_t* __restrict__ cand, int64_t ld_cand, int64_t nchunk, int64_t chunk_stride,
     int64_t tile_stride, int64_t n_cols,
     const uint8_t* __restrict__ ik_codes, const uint8_t* __restrict__ ik_scales, int64_t cap,
-    float* __restrict__ scores, int64_t ld) {
+    float* __restrict__ scores, int64_t ld, LevelDesc lvd, uint32_t* __restrict__ lv) {
+  static_assert(!LV || (!CAND && TPW % 2 == 0), "levels: full scans, tiles in pairs");
   // the first workgroups take the last queries: in a causal prefill chunk
   // they see the most entries, and starting the longest work first keeps it
   // out of the kernel's tail
@@ -178,20 +200,32 @@ __global__ __launch_bounds__(256) void k_index_score(
   u32x4_t r0[DEPTH + 1], r1[DEPTH + 1];
   uint32_t rs[DEPTH + 1];
   const int64_t step = tile_stride;
-  const int64_t col_first = cbase + (int64_t)wave * 32;
+  const int64_t col_first = cbase + (int64_t)wave * (LV ? 64 : 32);
+  auto col_of = [&](int t) __attribute__((always_inline)) {
+    return LV ? col_first + (int64_t)(t >> 1) * step + (t & 1) * 32 : col_first + (int64_t)t * step;
+  };
 #pragma unroll
   for (int t = 0; t < DEPTH; ++t) {
-    const int64_t c0 = col_first + t * step;
-    if (t < TPW) load(c0, r0[t], r1[t], rs[t]);
+    if (t < TPW) load(col_of(t), r0[t], r1[t], rs[t]);
   }
+  // LV: the query's level-1 and level-2 rows as buffer resources over their
+  // groups that hold a visible column (a store past them is dropped), and
+  // the key maximum of the first tile of the current pair
+  const __amdgpu_buffer_rsrc_t lr1 =
+      make_rsrc(LV ? lv + lvd.off[1] + (int64_t)q * lvd.stride[1] : nullptr,
+                LV ? groups_at(nv, 1) * 4 : 0);
+  const __amdgpu_buffer_rsrc_t lr2 =
+      make_rsrc(LV ? lv + lvd.off[2] + (int64_t)q * lvd.stride[2] : nullptr,
+                LV && lvd.nlev >= 2 ? groups_at(nv, 2) * 4 : 0);
+  uint32_t pair_key = 0;
   // tile t from ring slot sl (= t mod (DEPTH + 1), a constant wherever this
   // is called); pf: first request tile t + DEPTH into its slot (a column
   // past nv re-reads the last entry, so any tile index is safe to request)
   auto tile = [&](int t, int sl, bool pf) __attribute__((always_inline)) {
-    const int64_t col0 = col_first + t * step;
+    const int64_t col0 = col_of(t);
     if (pf) {
       const int sn = (sl + DEPTH) % (DEPTH + 1);
-      load(col_first + (int64_t)(t + DEPTH) * step, r0[sn], r1[sn], rs[sn]);
+      load(col_of(t + DEPTH), r0[sn], r1[sn], rs[sn]);
     }
     // keep those loads ahead of this tile's work
     __builtin_amdgcn_sched_barrier(0);
@@ -225,9 +259,28 @@ __global__ __launch_bounds__(256) void k_index_score(
 #pragma unroll
     for (int j = 0; j < 16; ++j) part += wr[j] * relu_f32(acc[j]);
     part = lanes_sum32(part);
-    const int64_t c = col0 + r;
-    const int off = half == 0 && c < nv ? (int)(c * 4) : (int)0x80000000;
+    // (columns and their byte offsets fit 32 bits: n_cols < 2^29)
+    const int c = (int)col0 + r;
+    const bool vis = c < (int)nv;
+    const int off = half == 0 && vis ? c * 4 : (int)0x80000000;
     __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(part), srs, off, 0, 0);
+    if constexpr (LV) {
+      // both lane halves hold the tile's 32 scores; columns past nv count
+      // as key 0, below every score's key
+      uint32_t key = vis ? f32_key(part) : 0u;
+      key = max(key, dpp_movu<0xb1>(key));               // quad_perm [1,0,3,2]
+      key = max(key, dpp_movu<0x4e>(key));               // quad_perm [2,3,0,1]
+      key = max(key, dpp_movu<0x141>(key));              // row_half_mirror: 8 columns
+      const int o1 = half == 0 && (r & 7) == 0 ? (((int)col0 >> 3) + (r >> 3)) * 4 : (int)0x80000000;
+      __builtin_amdgcn_raw_buffer_store_b32(key, lr1, o1, 0, 0);
+      key = max(key, dpp_movu<0x140>(key));              // row_mirror: 16 columns
+      key = max(key, lanes_max16u(key));                 // the tile's 32 columns
+      // the pair's second tile stores max(first, second) for its 64 columns
+      const bool second = (t & 1) != 0;
+      const int o2 = second && lane == 0 ? ((int)col0 >> 6) * 4 : (int)0x80000000;
+      __builtin_amdgcn_raw_buffer_store_b32(max(pair_key, key), lr2, o2, 0, 0);
+      pair_key = second ? pair_key : key;
+    }
   };
   // A wave whose every tile starts before nv runs them with no branch in
   // between, so the wait before each tile covers exactly that tile's loads
@@ -238,14 +291,21 @@ __global__ __launch_bounds__(256) void k_index_score(
   // branch-free groups of DEPTH + 1 (one turn of the ring, so the slots stay
   // constants), then the last ntv mod (DEPTH + 1) tiles one by one; those
   // were requested within the groups already.
-  if (CAND || col_first + (int64_t)(TPW - 1) * step < nv) {
+  if (CAND || col_of(TPW - 1) < nv) {
 #pragma unroll
     for (int t = 0; t < TPW; ++t) tile(t, t % (DEPTH + 1), t + DEPTH < TPW);
   } else {
     constexpr int G = DEPTH + 1;
     const int64_t rem = nv - col_first;
-    const int64_t nt64 = rem <= 0 ? 0 : (rem + step - 1) / step;
-    const int ntv = nt64 < TPW ? (int)nt64 : TPW;
+    int ntv;
+    if constexpr (LV) {                 // tiles before nv: first tiles p < P0, second p < P1
+      const int64_t P0 = rem <= 0 ? 0 : (rem + step - 1) / step;
+      const int64_t P1 = rem <= 32 ? 0 : (rem - 32 + step - 1) / step;
+      ntv = (int)((P0 < TPW / 2 ? P0 : TPW / 2) + (P1 < TPW / 2 ? P1 : TPW / 2));
+    } else {
+      const int64_t nt64 = rem <= 0 ? 0 : (rem + step - 1) / step;
+      ntv = nt64 < TPW ? (int)nt64 : TPW;
+    }
     int t0 = 0;
     for (; t0 + G <= ntv; t0 += G) {
 #pragma unroll
@@ -254,32 +314,37 @@ __global__ __launch_bounds__(256) void k_index_score(
 #pragma unroll
     for (int i = 0; i + 1 < G; ++i)
       if (t0 + i < ntv) tile(t0 + i, i, false);
+    // a pair whose second tile starts past nv: its level-2 group
+    if (LV && (ntv & 1))
+      __builtin_amdgcn_raw_buffer_store_b32(pair_key, lr2,
+                                            lane == 0 ? (int)((col_of(ntv - 1) >> 6) * 4) : (int)0x80000000,
+                                            0, 0);
   }
 }
 
-template <bool CAND, int TPW, int DEPTH>
+template <bool CAND, int TPW, int DEPTH, bool LV>
 static void launch_variant(bool fp4q, dim3 grid, hipStream_t stream, const uint16_t* q_idx,
                            const float* w,
                            const int32_t* q_seq, const int64_t* n_vis, const int32_t* cand,
                            int64_t ld_cand, int64_t nchunk, int64_t chunk_stride,
                            int64_t tile_stride, int64_t n_cols,
                            const uint8_t* ik_codes, const uint8_t* ik_scales, int64_t cap,
-                           float* scores, int64_t ld) {
+                           float* scores, int64_t ld, const LevelDesc& lvd, uint32_t* lv) {
   if (fp4q)
-    hipLaunchKernelGGL((k_index_score<CAND, true, TPW, DEPTH>), grid, dim3(256), 0, stream, q_idx,
-                       w, q_seq, n_vis, cand, ld_cand, nchunk, chunk_stride, tile_stride, n_cols, ik_codes,
-                       ik_scales, cap, scores, ld);
+    hipLaunchKernelGGL((k_index_score<CAND, true, TPW, DEPTH, LV>), grid, dim3(256), 0, stream,
+                       q_idx, w, q_seq, n_vis, cand, ld_cand, nchunk, chunk_stride, tile_stride,
+                       n_cols, ik_codes, ik_scales, cap, scores, ld, lvd, lv);
   else
-    hipLaunchKernelGGL((k_index_score<CAND, false, TPW, DEPTH>), grid, dim3(256), 0, stream, q_idx,
-                       w, q_seq, n_vis, cand, ld_cand, nchunk, chunk_stride, tile_stride, n_cols, ik_codes,
-                       ik_scales, cap, scores, ld);
+    hipLaunchKernelGGL((k_index_score<CAND, false, TPW, DEPTH, LV>), grid, dim3(256), 0, stream,
+                       q_idx, w, q_seq, n_vis, cand, ld_cand, nchunk, chunk_stride, tile_stride,
+                       n_cols, ik_codes, ik_scales, cap, scores, ld, lvd, lv);
 }
 
 hipError_t launch_index_score(const uint16_t* q_idx, const float* w, const int32_t* q_seq,
                               const int64_t* n_vis, const int32_t* cand, int64_t ld_cand, int Q,
                               int64_t n_cols, const uint8_t* ik_codes, const uint8_t* ik_scales,
                               int64_t cap, float* scores, int64_t ld, bool fp4q,
-                              hipStream_t stream) {
+                              hipStream_t stream, const LevelDesc* levels, uint32_t* lv) {
   // Tiles per wave: the largest of 32, 16, 8, 2, 1 that still launches at
   // least 1024 workgroups (4 per CU); long scans keep two tiles in flight.
   // (Swept on MI355X: 1M-entry scans want 32 tiles x 2 in flight, 64K-entry
@@ -292,24 +357,37 @@ hipError_t launch_index_score(const uint16_t* q_idx, const float* w, const int32
   const int64_t cols = (int64_t)SC_WAVES * tpw * 32;
   const int64_t nchunk = (n_cols + cols - 1) / cols;
   const dim3 grid((unsigned)(nchunk * Q));
+  // The scan writes the selection's levels 1 and 2 itself when they are all
+  // the selection needs and its waves take tiles in pairs; otherwise the
+  // maxima kernel derives them from the scores afterwards.
+  const LevelDesc none = {};
+  const bool lv_scan = levels && !cand && tpw >= 2 && levels->nlev <= 2;
+  const LevelDesc& lvd = levels ? *levels : none;
   // Long scans (>= 128 chunks per query) interleave the workgroups' tiles:
-  // workgroup g takes 128-column slices g, g + nchunk, g + 2 nchunk, ..., so
-  // at any moment the workgroups of a query read one contiguous window
-  // instead of nchunk windows a fixed power-of-two stride apart (measured on
-  // MI355X: 2-7 % faster at 512K-1M entries, 3-5 % slower at 64K).
+  // workgroup g takes 128-column slices g, g + nchunk, g + 2 nchunk, ...
+  // (256-column slices of tile pairs with levels), so at any moment the
+  // workgroups of a query read one contiguous window instead of nchunk
+  // windows a fixed power-of-two stride apart (measured on MI355X: 2-7 %
+  // faster at 512K-1M entries, 3-5 % slower at 64K).
   const bool inter = nchunk >= 128;
-  const int64_t cs = inter ? (int64_t)SC_WAVES * 32 : cols;
-  const int64_t ts = inter ? nchunk * SC_WAVES * 32 : (int64_t)SC_WAVES * 32;
+  const int64_t slice = (int64_t)SC_WAVES * 32 * (lv_scan ? 2 : 1);
+  const int64_t cs = inter ? slice : cols;
+  const int64_t ts = inter ? nchunk * slice : slice;
 #define CSA2_SCORE_CASE(T, D)                                                          \
   case T:                                                                             \
     if (cand)                                                                         \
-      launch_variant<true, T, D>(fp4q, grid, stream, q_idx, w, q_seq, n_vis, cand,    \
-                                 ld_cand, nchunk, cs, ts, n_cols, ik_codes, ik_scales, \
-                                 cap, scores, ld);                                    \
+      launch_variant<true, T, D, false>(fp4q, grid, stream, q_idx, w, q_seq, n_vis, cand, \
+                                        ld_cand, nchunk, cs, ts, n_cols, ik_codes,    \
+                                        ik_scales, cap, scores, ld, lvd, lv);         \
+    else if (lv_scan)                                                                 \
+      launch_variant<false, T, D, (T % 2 == 0)>(fp4q, grid, stream, q_idx, w, q_seq,  \
+                                                n_vis, cand, ld_cand, nchunk, cs, ts, \
+                                                n_cols, ik_codes, ik_scales, cap,     \
+                                                scores, ld, lvd, lv);                 \
     else                                                                              \
-      launch_variant<false, T, D>(fp4q, grid, stream, q_idx, w, q_seq, n_vis, cand,   \
-                                  ld_cand, nchunk, cs, ts, n_cols, ik_codes, ik_scales, \
-                                  cap, scores, ld);                                   \
+      launch_variant<false, T, D, false>(fp4q, grid, stream, q_idx, w, q_seq, n_vis,  \
+                                         cand, ld_cand, nchunk, cs, ts, n_cols,       \
+                                         ik_codes, ik_scales, cap, scores, ld, lvd, lv); \
     break;
   switch (tpw) {
     CSA2_SCORE_CASE(32, 2)
@@ -320,7 +398,11 @@ hipError_t launch_index_score(const uint16_t* q_idx, const float* w, const int32
     CSA2_SCORE_CASE(1, 1)
   }
 #undef CSA2_SCORE_CASE
-  return hipGetLastError();
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if (levels && !lv_scan && levels->nlev > 0)
+    e = launch_maxima(scores, ld, Q, n_vis, n_cols, *levels, lv, stream);
+  return e;
 }
 
 }  // namespace csa2

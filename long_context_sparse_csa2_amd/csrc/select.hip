@@ -176,11 +176,11 @@ hipError_t launch_maxima(const float* scores, int64_t ld, int Q, const int64_t* 
 hipError_t launch_select(const float* scores, int64_t ld, int Q, const int64_t* n_valid,
                          const int32_t* col_ids, int64_t n_cols, int kk, int mode, int32_t* out,
                          int64_t out_ld, int64_t* out_len, int k2, int32_t* out2, void* ws,
-                         hipStream_t stream) {
+                         hipStream_t stream, bool levels_ready) {
   const LevelDesc d = make_levels(Q, n_cols, mode);
   const int vec_out = ((uintptr_t)out & 15) == 0 && out_ld % 4 == 0;   // 16-byte output rows
   const int spec = Q <= 64;                      // first loads ahead of n_valid
-  launch_maxima(scores, ld, Q, n_valid, n_cols, d, (uint32_t*)ws, stream);
+  if (!levels_ready) launch_maxima(scores, ld, Q, n_valid, n_cols, d, (uint32_t*)ws, stream);
   // one round over at most 4096 candidates: 256-thread workgroups, several per CU
   if (mode == 0 && n_cols <= 256 * SEL_PER) {
     hipLaunchKernelGGL((k_select<256, SEL_PER>), dim3((unsigned)Q), dim3(256), 0, stream, scores, ld, n_valid,

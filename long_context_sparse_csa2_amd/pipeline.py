@@ -29,7 +29,8 @@ import torch
 
 from . import (Cache, CSA2_OP_ATTEND, CSA2_OP_POOL, CSA2_OP_POOL_ATTEND, CSA2_OP_SELECT_ATTEND,
                CSA2_OP_TOPK, csa2_block_pool, csa2_compress_quant, csa2_index_score,
-               csa2_select_attend, csa2_select_topk, csa2_sparse_attend, workspace)
+               csa2_index_score_levels, csa2_select_attend, csa2_select_topk, csa2_sparse_attend,
+               workspace)
 from .synth import Workload
 
 # one C-ABI call of a step: its name, layer, thunk and query rows [i0, i1)
@@ -58,9 +59,11 @@ class Step:
     def __init__(self, wl: Workload, device, cache=None, fp4q=False, fused=None):
         """fp4q=True scores with the MXFP4 indexer query
         (csa2_index_score_fp4q) instead of the bf16 one.  fused=True runs
-        each selection together with its attention (csa2_select_attend);
-        the default does so for decode batches (fewer than 256 queries) and
-        uses the separate calls for prefill chunks."""
+        each selection together with its attention (csa2_select_attend),
+        the Full layer's scan also writing the selection's lowest maxima
+        levels (csa2_index_score_levels); the default does so for decode
+        batches (fewer than 256 queries) and uses the separate calls for
+        prefill chunks."""
         self.wl = wl
         self.device = device
         self.fp4q = fp4q
@@ -143,14 +146,16 @@ class Step:
                 L = {key: v[loc] if key in ("q_idx", "w", "q_attn") else v
                      for key, v in self.layers[li].items()}
                 if mode == "full":
-                    out.append(Op("index_score_full", li, lambda L=L, q_seq=q_seq, n_vis=n_vis,
-                                  n_cols=n_cols, scores=scores: csa2_index_score(
-                        L["q_idx"], L["w"], q_seq, n_vis, None, n_cols, self.cache, scores,
-                        fp4q=self.fp4q), (i0, i1)))
                     idx = idx_full
                     if self.fused:
-                        # the pool (hierarchical) or the top-k, and the attention, in one call
+                        # the scan also lays down the selection's lowest maxima
+                        # levels; then the pool (hierarchical) or the top-k, and
+                        # the attention, in one call
                         nb = wl.n_blocks if wl.hierarchical else 0
+                        out.append(Op("index_score_full", li, lambda L=L, q_seq=q_seq, n_vis=n_vis,
+                                      n_cols=n_cols, scores=scores, nb=nb: csa2_index_score_levels(
+                            L["q_idx"], L["w"], q_seq, n_vis, n_cols, self.cache, scores,
+                            self.ws_sa_full, n_blocks=nb, fp4q=self.fp4q), (i0, i1)))
                         out.append(Op("select_attend_full", li, lambda L=L, li=li, q_seq=q_seq,
                                       n_vis=n_vis, n_cols=n_cols, scores=scores, idx=idx_full,
                                       swa_start=swa_start, swa_len=swa_len, rows=loc, nb=nb:
@@ -158,9 +163,13 @@ class Step:
                             scores, n_vis, None, n_cols, wl.k, idx, L["q_attn"], q_seq, self.cache,
                             L["swa_codes"], L["swa_scale"], swa_start, swa_len,
                             self.out[li][rows], self.lse[li][rows], self.ws_sa_full, n_blocks=nb,
-                            pool=self.pool if nb else None, pool_len=self.pool_len if nb else None),
-                            (i0, i1)))
+                            pool=self.pool if nb else None, pool_len=self.pool_len if nb else None,
+                            levels=True), (i0, i1)))
                         continue
+                    out.append(Op("index_score_full", li, lambda L=L, q_seq=q_seq, n_vis=n_vis,
+                                  n_cols=n_cols, scores=scores: csa2_index_score(
+                        L["q_idx"], L["w"], q_seq, n_vis, None, n_cols, self.cache, scores,
+                        fp4q=self.fp4q), (i0, i1)))
                     if wl.hierarchical:
                         # the pool and the layer's own top-k in one selection pass
                         out.append(Op("block_pool_topk", li, lambda: csa2_block_pool(
