@@ -208,20 +208,42 @@ __global__ __launch_bounds__(256, 4) void k_index_score(
   for (int t = 0; t < DEPTH; ++t) {
     if (t < TPW) load(col_of(t), r0[t], r1[t], rs[t]);
   }
-  // LV: the query's level-1 and level-2 rows as buffer resources over their
-  // groups that hold a visible column (a store past them is dropped), and
-  // the key maximum of the first tile of the current pair
-  const __amdgpu_buffer_rsrc_t lr1 =
-      make_rsrc(LV ? lv + lvd.off[1] + (int64_t)q * lvd.stride[1] : nullptr,
-                LV ? groups_at(nv, 1) * 4 : 0);
-  const __amdgpu_buffer_rsrc_t lr2 =
-      make_rsrc(LV ? lv + lvd.off[2] + (int64_t)q * lvd.stride[2] : nullptr,
-                LV && lvd.nlev >= 2 ? groups_at(nv, 2) * 4 : 0);
-  uint32_t pair_key = 0;
+  // LV: the levels region as one buffer resource (its byte size fits 31
+  // bits, checked on the host), the query's level-1 / level-2 rows in it
+  // (uint32 units), their groups that hold a visible column, and the first
+  // tile's level-1 keys and key maximum while the pair's second tile runs.
+  // One store per pair writes the pair's 8 level-1 groups (lanes 8j: the
+  // second tile's groups from the first lane half, the first tile's from the
+  // second, both halves holding the same scores) and its level-2 group
+  // (lane 1).
+  const int Qn = (int)(gridDim.x / nchunk);
+  const int L2 = LV && lvd.nlev >= 2;
+  const __amdgpu_buffer_rsrc_t lrs = make_rsrc(
+      LV ? (const void*)lv : nullptr,
+      LV ? (lvd.off[1 + L2] + (int64_t)Qn * lvd.stride[1 + L2]) * 4 : 0);
+  const int b1 = LV ? (int)(lvd.off[1] + (int64_t)q * lvd.stride[1]) : 0;
+  const int b2 = L2 ? (int)(lvd.off[2] + (int64_t)q * lvd.stride[2]) : 0;
+  const int G1 = LV ? (int)groups_at(nv, 1) : 0;
+  const int G2 = L2 ? (int)groups_at(nv, 2) : 0;
+  uint32_t pair_l1 = 0, pair_max = 0;
+  // the level store of the pair whose first tile starts at column colA (has_b:
+  // its second tile ran, its keys l1b)
+  auto pair_store = [&](uint32_t l1a, uint32_t l1b, uint32_t m2, int colA, bool has_b)
+      __attribute__((always_inline)) {
+    const int g = (colA >> 3) + (r >> 3) + (half ? 0 : 4);
+    uint32_t v = half ? l1a : l1b;
+    int o = (r & 7) == 0 && g < G1 && (half || has_b) ? (b1 + g) * 4 : (int)0x80000000;
+    if (lane == 1) {
+      v = m2;
+      o = (colA >> 6) < G2 ? (b2 + (colA >> 6)) * 4 : (int)0x80000000;
+    }
+    __builtin_amdgcn_raw_buffer_store_b32(v, lrs, o, 0, 0);
+  };
   // tile t from ring slot sl (= t mod (DEPTH + 1), a constant wherever this
   // is called); pf: first request tile t + DEPTH into its slot (a column
   // past nv re-reads the last entry, so any tile index is safe to request)
-  auto tile = [&](int t, int sl, bool pf) __attribute__((always_inline)) {
+  // tail: a call from the ragged-row loop, where t is not a constant
+  auto tile = [&](int t, int sl, bool pf, bool tail) __attribute__((always_inline)) {
     const int64_t col0 = col_of(t);
     if (pf) {
       const int sn = (sl + DEPTH) % (DEPTH + 1);
@@ -271,15 +293,23 @@ __global__ __launch_bounds__(256, 4) void k_index_score(
       key = max(key, dpp_movu<0xb1>(key));               // quad_perm [1,0,3,2]
       key = max(key, dpp_movu<0x4e>(key));               // quad_perm [2,3,0,1]
       key = max(key, dpp_movu<0x141>(key));              // row_half_mirror: 8 columns
-      const int o1 = half == 0 && (r & 7) == 0 ? (((int)col0 >> 3) + (r >> 3)) * 4 : (int)0x80000000;
-      __builtin_amdgcn_raw_buffer_store_b32(key, lr1, o1, 0, 0);
+      const uint32_t l1 = key;
       key = max(key, dpp_movu<0x140>(key));              // row_mirror: 16 columns
       key = max(key, lanes_max16u(key));                 // the tile's 32 columns
-      // the pair's second tile stores max(first, second) for its 64 columns
-      const bool second = (t & 1) != 0;
-      const int o2 = second && lane == 0 ? ((int)col0 >> 6) * 4 : (int)0x80000000;
-      __builtin_amdgcn_raw_buffer_store_b32(max(pair_key, key), lr2, o2, 0, 0);
-      pair_key = second ? pair_key : key;
+      const bool first = (t & 1) == 0;
+      if (!tail) {                                       // t is a constant here: no branch
+        if (first) {
+          pair_l1 = l1;
+          pair_max = key;
+        } else {
+          pair_store(pair_l1, l1, max(pair_max, key), (int)col0 - 32, true);
+        }
+      } else {                                           // branch-free: a first tile stores nothing
+        const int colA = (int)col0 - (first ? 0 : 32);
+        pair_store(pair_l1, l1, max(pair_max, key), first ? (1 << 30) : colA, true);
+        pair_l1 = first ? l1 : pair_l1;
+        pair_max = first ? key : pair_max;
+      }
     }
   };
   // A wave whose every tile starts before nv runs them with no branch in
@@ -293,7 +323,7 @@ __global__ __launch_bounds__(256, 4) void k_index_score(
   // were requested within the groups already.
   if (CAND || col_of(TPW - 1) < nv) {
 #pragma unroll
-    for (int t = 0; t < TPW; ++t) tile(t, t % (DEPTH + 1), t + DEPTH < TPW);
+    for (int t = 0; t < TPW; ++t) tile(t, t % (DEPTH + 1), t + DEPTH < TPW, false);
   } else {
     constexpr int G = DEPTH + 1;
     const int64_t rem = nv - col_first;
@@ -309,16 +339,13 @@ __global__ __launch_bounds__(256, 4) void k_index_score(
     int t0 = 0;
     for (; t0 + G <= ntv; t0 += G) {
 #pragma unroll
-      for (int i = 0; i < G; ++i) tile(t0 + i, i, true);
+      for (int i = 0; i < G; ++i) tile(t0 + i, i, true, true);
     }
 #pragma unroll
     for (int i = 0; i + 1 < G; ++i)
-      if (t0 + i < ntv) tile(t0 + i, i, false);
-    // a pair whose second tile starts past nv: its level-2 group
-    if (LV && (ntv & 1))
-      __builtin_amdgcn_raw_buffer_store_b32(pair_key, lr2,
-                                            lane == 0 ? (int)((col_of(ntv - 1) >> 6) * 4) : (int)0x80000000,
-                                            0, 0);
+      if (t0 + i < ntv) tile(t0 + i, i, false, true);
+    // a pair whose second tile starts past nv: its first tile's groups
+    if (LV && (ntv & 1)) pair_store(pair_l1, 0u, pair_max, (int)col_of(ntv - 1), false);
   }
 }
 
@@ -361,7 +388,9 @@ hipError_t launch_index_score(const uint16_t* q_idx, const float* w, const int32
   // the selection needs and its waves take tiles in pairs; otherwise the
   // maxima kernel derives them from the scores afterwards.
   const LevelDesc none = {};
-  const bool lv_scan = levels && !cand && tpw >= 2 && levels->nlev <= 2;
+  const bool lv_scan = levels && !cand && tpw >= 2 && levels->nlev >= 1 && levels->nlev <= 2 &&
+                       (levels->off[levels->nlev] + (int64_t)Q * levels->stride[levels->nlev]) * 4 <
+                           ((int64_t)1 << 31);
   const LevelDesc& lvd = levels ? *levels : none;
   // Long scans (>= 128 chunks per query) interleave the workgroups' tiles:
   // workgroup g takes 128-column slices g, g + nchunk, g + 2 nchunk, ...
