@@ -17,6 +17,67 @@ constexpr int CQ_ENT = 32;          // entries per workgroup
 constexpr int CQ_XPAD = 8;          // bf16 padding of an LDS latent row
 constexpr int CQ_KPAD = 4;          // fp32 padding of an LDS indexer-K row
 
+// Phase 1 of the compressor for a wave's 8 entries when an entry has M <= 2
+// raw rows: every row is requested first, then each entry is pooled (per
+// channel, softmax over the M rows of z weighting the rows of h; M == 1:
+// the row itself) and handed to quant(x, jl, j).  Entries past n_ent get
+// zero rows in xs and nothing stored.
+template <int M, typename HRow, typename ZRow, typename Quant>
+__device__ __forceinline__ void pool_rows_8(HRow hrow, ZRow zrow, int64_t n_ent, int64_t j0,
+                                            int wave, int lane, Quant quant,
+                                            uint16_t (*xs)[D_LAT + CQ_XPAD]) {
+  u32x4_t hv[8][M], zv[8][M];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int64_t jr = j0 + wave * 8 + i;
+    const int64_t j = jr < n_ent ? jr : n_ent - 1;
+#pragma unroll
+    for (int t = 0; t < M; ++t) {
+      hv[i][t] = *(const u32x4_t*)(hrow(j, t) + lane * 8);
+      if (M > 1) zv[i][t] = *(const u32x4_t*)(zrow(j, t) + lane * 8);
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int jl = wave * 8 + i;
+    const int64_t j = j0 + jl;
+    float x[8];
+    if constexpr (M == 1) {
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        x[2 * c] = __uint_as_float(hv[i][0][c] << 16);
+        x[2 * c + 1] = __uint_as_float(hv[i][0][c] & 0xFFFF0000u);
+      }
+    } else {
+      float zmax[8], num[8], den[8];
+#pragma unroll
+      for (int c = 0; c < 8; ++c) { zmax[c] = -INFINITY; num[c] = 0.f; den[c] = 0.f; }
+#pragma unroll
+      for (int t = 0; t < M; ++t)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          zmax[2 * c] = fmaxf(zmax[2 * c], __uint_as_float(zv[i][t][c] << 16));
+          zmax[2 * c + 1] = fmaxf(zmax[2 * c + 1], __uint_as_float(zv[i][t][c] & 0xFFFF0000u));
+        }
+#pragma unroll
+      for (int t = 0; t < M; ++t)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const float e0v = expf(__uint_as_float(zv[i][t][c] << 16) - zmax[2 * c]);
+          const float e1v = expf(__uint_as_float(zv[i][t][c] & 0xFFFF0000u) - zmax[2 * c + 1]);
+          num[2 * c] += e0v * __uint_as_float(hv[i][t][c] << 16);
+          num[2 * c + 1] += e1v * __uint_as_float(hv[i][t][c] & 0xFFFF0000u);
+          den[2 * c] += e0v;
+          den[2 * c + 1] += e1v;
+        }
+#pragma unroll
+      for (int c = 0; c < 8; ++c) x[c] = num[c] / den[c];
+    }
+    if (j < n_ent) quant(x, jl, j);                     // uniform per wave
+    else *(u32x4_t*)&xs[jl][lane * 8] = u32x4_t{0u, 0u, 0u, 0u};
+  }
+}
+
 // The compressor for entries j0 .. j0 + 31 of sequence b (those below
 // n_ent), written at entries e0 + j.  hrow(j, t) / zrow(j, t) give raw row
 // t (< m) of entry j.  ONE_ENTRY (the decode append, one valid entry) loads
@@ -43,49 +104,8 @@ __device__ __forceinline__ void compress_entries(HRow hrow, ZRow zrow, int m, in
 
   // ---- phase 1: pooling + main-KV quantisation; wave w owns entries 8w..8w+7,
   //      lane l owns channels 8l..8l+7 (two lanes per 16-channel scale group).
-  for (int i = 0; i < 8; ++i) {
-    const int jl = wave * 8 + i;
-    const int64_t j = j0 + jl;
-    if (j >= n_ent) {
-      *(u32x4_t*)&xs[jl][lane * 8] = u32x4_t{0u, 0u, 0u, 0u};
-      continue;
-    }
-    float x[8];
-    if (m == 1) {
-      const u32x4_t v = *(const u32x4_t*)(hrow(j, 0) + lane * 8);
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        x[2 * c] = __uint_as_float(v[c] << 16);
-        x[2 * c + 1] = __uint_as_float(v[c] & 0xFFFF0000u);
-      }
-    } else {
-      float zmax[8], num[8], den[8];
-#pragma unroll
-      for (int c = 0; c < 8; ++c) { zmax[c] = -INFINITY; num[c] = 0.f; den[c] = 0.f; }
-      for (int t = 0; t < m; ++t) {
-        const u32x4_t zv = *(const u32x4_t*)(zrow(j, t) + lane * 8);
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          zmax[2 * c] = fmaxf(zmax[2 * c], __uint_as_float(zv[c] << 16));
-          zmax[2 * c + 1] = fmaxf(zmax[2 * c + 1], __uint_as_float(zv[c] & 0xFFFF0000u));
-        }
-      }
-      for (int t = 0; t < m; ++t) {
-        const u32x4_t zv = *(const u32x4_t*)(zrow(j, t) + lane * 8);
-        const u32x4_t hv = *(const u32x4_t*)(hrow(j, t) + lane * 8);
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          const float e0v = expf(__uint_as_float(zv[c] << 16) - zmax[2 * c]);
-          const float e1v = expf(__uint_as_float(zv[c] & 0xFFFF0000u) - zmax[2 * c + 1]);
-          num[2 * c] += e0v * __uint_as_float(hv[c] << 16);
-          num[2 * c + 1] += e1v * __uint_as_float(hv[c] & 0xFFFF0000u);
-          den[2 * c] += e0v;
-          den[2 * c + 1] += e1v;
-        }
-      }
-#pragma unroll
-      for (int c = 0; c < 8; ++c) x[c] = num[c] / den[c];
-    }
+  // FP4 codes and E4M3 scales of entry j (local jl) from its pooled channels
+  auto quantise = [&](const float (&x)[8], int jl, int64_t j) __attribute__((always_inline)) {
     float amax = 0.f;
 #pragma unroll
     for (int c = 0; c < 8; ++c) amax = fmaxf(amax, fabsf(x[c]));
@@ -108,6 +128,58 @@ __device__ __forceinline__ void compress_entries(HRow hrow, ZRow zrow, int m, in
     if ((lane & 7) == 0)
       *(uint32_t*)(kv_scales + ent * 32 + lane / 2) = sc | (s1 << 8) | (s2 << 16) | (s3 << 24);
     *(u32x4_t*)&xs[jl][lane * 8] = u32x4_t{xb[0], xb[1], xb[2], xb[3]};
+  };
+  if (!ONE_ENTRY && (m == 1 || m == 2)) {
+    // the rows of all 8 entries requested before any pooling (rows past
+    // n_ent re-read the last entry; their results are not stored)
+    if (m == 1) pool_rows_8<1>(hrow, zrow, n_ent, j0, wave, lane, quantise, xs);
+    else pool_rows_8<2>(hrow, zrow, n_ent, j0, wave, lane, quantise, xs);
+  } else {
+    for (int i = 0; i < 8; ++i) {
+      const int jl = wave * 8 + i;
+      const int64_t j = j0 + jl;
+      if (j >= n_ent) {
+        *(u32x4_t*)&xs[jl][lane * 8] = u32x4_t{0u, 0u, 0u, 0u};
+        continue;
+      }
+      float x[8];
+      if (m == 1) {
+        const u32x4_t v = *(const u32x4_t*)(hrow(j, 0) + lane * 8);
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          x[2 * c] = __uint_as_float(v[c] << 16);
+          x[2 * c + 1] = __uint_as_float(v[c] & 0xFFFF0000u);
+        }
+      } else {
+        float zmax[8], num[8], den[8];
+#pragma unroll
+        for (int c = 0; c < 8; ++c) { zmax[c] = -INFINITY; num[c] = 0.f; den[c] = 0.f; }
+        for (int t = 0; t < m; ++t) {
+          const u32x4_t zv = *(const u32x4_t*)(zrow(j, t) + lane * 8);
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            zmax[2 * c] = fmaxf(zmax[2 * c], __uint_as_float(zv[c] << 16));
+            zmax[2 * c + 1] = fmaxf(zmax[2 * c + 1], __uint_as_float(zv[c] & 0xFFFF0000u));
+          }
+        }
+        for (int t = 0; t < m; ++t) {
+          const u32x4_t zv = *(const u32x4_t*)(zrow(j, t) + lane * 8);
+          const u32x4_t hv = *(const u32x4_t*)(hrow(j, t) + lane * 8);
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            const float e0v = expf(__uint_as_float(zv[c] << 16) - zmax[2 * c]);
+            const float e1v = expf(__uint_as_float(zv[c] & 0xFFFF0000u) - zmax[2 * c + 1]);
+            num[2 * c] += e0v * __uint_as_float(hv[c] << 16);
+            num[2 * c + 1] += e1v * __uint_as_float(hv[c] & 0xFFFF0000u);
+            den[2 * c] += e0v;
+            den[2 * c + 1] += e1v;
+          }
+        }
+#pragma unroll
+        for (int c = 0; c < 8; ++c) x[c] = num[c] / den[c];
+      }
+      quantise(x, jl, j);
+    }
   }
   __syncthreads();
 
