@@ -371,6 +371,11 @@ csa2_status csa2_select_attend(const float* scores, int64_t ld, int Q, const int
  * n_vis == n_valid, the same Q, n_cols and the same sign of n_blocks, and
  * col_ids must be NULL.  Levels from other scores give a wrong (though
  * in-bounds) selection.
+ *
+ * csa2_select_topk_levels = csa2_select_topk (same arguments, outputs,
+ * workspace and errors) likewise without its maxima pass, after a
+ * csa2_index_score_levels call with n_blocks == 0 into the same ws (its
+ * csa2_workspace_bytes(CSA2_OP_TOPK, Q, n_cols, k) bytes); col_ids NULL.
  */
 csa2_status csa2_index_score_levels(const uint16_t* q_idx, const float* w, const int32_t* q_seq,
                                     const int64_t* n_vis, int Q, int64_t n_cols,
@@ -385,6 +390,10 @@ csa2_status csa2_select_attend_levels(const float* scores, int64_t ld, int Q,
                                       int64_t T_swa, const int64_t* swa_start,
                                       const int32_t* swa_len, float* out, float* lse, void* ws,
                                       size_t ws_bytes, void* stream);
+csa2_status csa2_select_topk_levels(const float* scores, int64_t ld, int Q,
+                                    const int64_t* n_valid, const int32_t* col_ids,
+                                    int64_t n_cols, int k, int32_t* out, void* ws,
+                                    size_t ws_bytes, void* stream);
 
 /* Rotary position embedding of csa2_sparse_attend_rope (host struct). */
 typedef struct {

@@ -24,7 +24,7 @@ EXPORTS = ("csa2_status_string", "csa2_last_error", "csa2_compress_quant", "csa2
            "csa2_index_score_fp4q", "csa2_select_topk", "csa2_block_pool", "csa2_sparse_attend",
            "csa2_sparse_attend_rope", "csa2_decode_append", "csa2_workspace_bytes",
            "csa2_selftest", "csa2_select_topk_noalloc", "csa2_select_attend",
-           "csa2_index_score_levels", "csa2_select_attend_levels",
+           "csa2_index_score_levels", "csa2_select_attend_levels", "csa2_select_topk_levels",
            "csa2_peak_read", "csa2_peak_mfma")
 
 
@@ -71,8 +71,9 @@ def lib():
         for fn in (L.csa2_index_score, L.csa2_index_score_fp4q):
             fn.restype = I
             fn.argtypes = [P, P, P, P, P, I64, I, I64, ctypes.POINTER(_Cache), P, I64, P]
-        L.csa2_select_topk.restype = I
-        L.csa2_select_topk.argtypes = [P, I64, I, P, P, I64, I, P, P, SZ, P]
+        for fn in (L.csa2_select_topk, L.csa2_select_topk_levels):
+            fn.restype = I
+            fn.argtypes = [P, I64, I, P, P, I64, I, P, P, SZ, P]
         for fn in (L.csa2_select_attend, L.csa2_select_attend_levels):
             fn.restype = I
             fn.argtypes = [P, I64, I, P, P, I64, I, P, I, P, P, P, P,
@@ -242,16 +243,20 @@ def csa2_index_score_levels(q_idx, w, q_seq, n_vis, n_cols, cache, scores, ws, n
     _check("csa2_index_score_levels", st)
 
 
-def csa2_select_topk(scores, n_valid, col_ids, n_cols, k, out, ws=None, stream=None):
+def csa2_select_topk(scores, n_valid, col_ids, n_cols, k, out, ws=None, stream=None,
+                     levels=False):
     """scores [Q, ld] f32, n_valid [Q] i64, col_ids None or [Q, ld] i32,
-    out [Q, k] i32; ws a uint8 tensor of csa2_workspace_bytes(TOPK, ...)."""
+    out [Q, k] i32; ws a uint8 tensor of csa2_workspace_bytes(TOPK, ...).
+    levels=True calls csa2_select_topk_levels: ws already holds the maxima
+    levels that csa2_index_score_levels (n_blocks=0) wrote for these scores."""
     _dtype(scores, torch.float32, "scores"); _dtype(n_valid, torch.int64, "n_valid")
     _dtype(col_ids, torch.int32, "col_ids"); _dtype(out, torch.int32, "out")
     Q = scores.shape[0]
     wsb = ws.numel() * ws.element_size() if ws is not None else 0
-    st = lib().csa2_select_topk(_ptr(scores), scores.shape[1], Q, _ptr(n_valid), _ptr(col_ids),
-                                n_cols, k, _ptr(out), _ptr(ws), wsb, _stream(stream, scores))
-    _check("csa2_select_topk", st)
+    name = "csa2_select_topk_levels" if levels else "csa2_select_topk"
+    st = getattr(lib(), name)(_ptr(scores), scores.shape[1], Q, _ptr(n_valid), _ptr(col_ids),
+                              n_cols, k, _ptr(out), _ptr(ws), wsb, _stream(stream, scores))
+    _check(name, st)
 
 
 def csa2_select_topk_noalloc(scores, n_valid, col_ids, n_cols, k, out, stream=None):

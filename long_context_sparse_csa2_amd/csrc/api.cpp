@@ -216,11 +216,12 @@ csa2_status csa2_index_score_levels(const uint16_t* q_idx, const float* w, const
   REQ(n_cols >= 0 && n_cols <= CSA2_MAX_COLS, "n_cols=%lld must be in [0, %d]",
       (long long)n_cols, CSA2_MAX_COLS);
   const int mode = n_blocks > 0 ? 1 : 0;
+  // (no levels at all when the selection takes the scores directly)
   const size_t need = csa2::select_ws_bytes(Q, n_cols, mode);
-  if (!ws || ws_bytes < need)
+  if (need > 0 && (!ws || ws_bytes < need))
     return fail(CSA2_EWORKSPACE, "workspace %zu bytes < %zu needed", ws ? ws_bytes : (size_t)0,
                 need);
-  REQ(al(ws, 256), "ws must be 256-byte aligned");
+  REQ(!ws || al(ws, 256), "ws must be 256-byte aligned");
   const csa2::LevelDesc d = csa2::select_levels(Q, n_cols, mode);
   return index_score_common(q_idx, w, q_seq, n_vis, nullptr, 0, Q, n_cols, src, scores, ld,
                             stream, fp4q != 0, &d, (uint32_t*)ws);
@@ -253,6 +254,20 @@ csa2_status csa2_select_topk(const float* scores, int64_t ld, int Q, const int64
   return hip_status(csa2::launch_select(scores, ld, Q, n_valid, col_ids, n_cols, k, 0, out, k,
                                         nullptr, 0, nullptr, ws, (hipStream_t)stream),
                     "csa2_select_topk launch");
+}
+
+csa2_status csa2_select_topk_levels(const float* scores, int64_t ld, int Q,
+                                    const int64_t* n_valid, const int32_t* col_ids,
+                                    int64_t n_cols, int k, int32_t* out, void* ws,
+                                    size_t ws_bytes, void* stream) {
+  g_err[0] = 0;
+  REQ(out, "out must not be NULL");
+  REQ(!col_ids, "col_ids must be NULL (the levels are those of a full scan)");
+  const csa2_status st = select_common(scores, ld, Q, n_valid, n_cols, k, ws, ws_bytes, 0);
+  if (st != CSA2_OK) return st;
+  return hip_status(csa2::launch_select(scores, ld, Q, n_valid, col_ids, n_cols, k, 0, out, k,
+                                        nullptr, 0, nullptr, ws, (hipStream_t)stream, true),
+                    "csa2_select_topk_levels launch");
 }
 
 csa2_status csa2_select_topk_noalloc(const float* scores, int64_t ld, int Q,

@@ -166,6 +166,9 @@ class Step:
                             pool=self.pool if nb else None, pool_len=self.pool_len if nb else None,
                             levels=True), (i0, i1)))
                         continue
+                    # (a prefill chunk's scan is bound by its MFMA and conversion
+                    # work, and the maxima epilogue costs it about what the
+                    # separate maxima pass does: the plain scan here)
                     out.append(Op("index_score_full", li, lambda L=L, q_seq=q_seq, n_vis=n_vis,
                                   n_cols=n_cols, scores=scores: csa2_index_score(
                         L["q_idx"], L["w"], q_seq, n_vis, None, n_cols, self.cache, scores,

@@ -130,3 +130,38 @@ def test_levels_validation():
     with pytest.raises(C.Csa2Error, match="CSA2_EINVAL"):
         C.csa2_select_attend(scores, nv, ids, n, 512, idx, q, q_seq, cache, swa_c, swa_s, start,
                              slen, out, None, ws, levels=True)
+
+
+@pytest.mark.parametrize("Q,n_cols", [(512, 200000), (64, 1 << 19), (300, 70000)])
+def test_topk_levels_equal_separate(Q, n_cols):
+    """csa2_index_score_levels + csa2_select_topk_levels against
+    csa2_index_score + csa2_select_topk (the prefill path, many queries with
+    causal visible counts): scores, maxima groups and top-k ids bit for bit."""
+    B, k = 1, 512
+    cache = _cache(B, n_cols, seed=Q + 11)
+    q_idx, w, *_ = _inputs(Q, B, seed=Q + 12)
+    q_seq = torch.zeros(Q, dtype=torch.int32, device=DEV)
+    nv_h = [max(1, n_cols - (Q - 1 - i) * (n_cols // Q) - (i % 5)) for i in range(Q)]
+    nv = torch.tensor(nv_h, dtype=torch.int64, device=DEV)
+    res = {}
+    for levels in (False, True):
+        scores = torch.full((Q, n_cols), -5.0, device=DEV)
+        idx = torch.full((Q, k), -9, dtype=torch.int32, device=DEV)
+        ws = C.workspace(C.CSA2_OP_TOPK, Q, n_cols, k, DEV)
+        ws.fill_(0xAB)
+        if levels:
+            C.csa2_index_score_levels(q_idx, w, q_seq, nv, n_cols, cache, scores, ws)
+        else:
+            C.csa2_index_score(q_idx, w, q_seq, nv, None, n_cols, cache, scores)
+        C.csa2_select_topk(scores, nv, None, n_cols, k, idx, ws, levels=levels)
+        torch.cuda.synchronize()
+        res[levels] = (scores, idx, ws.view(torch.int32))
+    a, b = res[False], res[True]
+    for i in range(Q):
+        assert torch.equal(a[0][i, :nv_h[i]], b[0][i, :nv_h[i]]), f"scores of query {i}"
+    for l, (off, stride) in _layout(Q, n_cols, 0).items():
+        for i in range(Q):
+            g = _groups(nv_h[i], l)
+            assert torch.equal(a[2][off + i * stride: off + i * stride + g],
+                               b[2][off + i * stride: off + i * stride + g]), f"level {l} of query {i}"
+    assert torch.equal(a[1], b[1])
