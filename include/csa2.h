@@ -18,6 +18,12 @@
  *   - Every call enqueues its kernels on `stream` (a hipStream_t, may be 0
  *     for the null stream) and returns without synchronising.
  *   - bf16 values are passed as uint16_t bit patterns.
+ *   - Every array must be aligned to at least its element size (8 bytes for
+ *     int64, 4 for int32 and fp32); where an entry point states a stronger
+ *     alignment (16 bytes for bf16 / byte arrays the kernels read as
+ *     vectors and for fp32 attention outputs, 256 for workspaces that hold
+ *     maxima levels) that one applies.  A misaligned pointer returns
+ *     CSA2_EINVAL.
  *   - Arguments are validated on the host before anything is launched.  A
  *     bad argument returns CSA2_EINVAL (or CSA2_EUNSUPPORTED for a size the
  *     library does not implement, CSA2_EWORKSPACE for a short workspace)

@@ -31,6 +31,8 @@ csa2_status fail(csa2_status st, const char* fmt, ...) {
 }
 
 bool al(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+// an optional array (NULL allowed) aligned to `a` bytes when given
+bool al0(const void* p, uintptr_t a) { return !p || al(p, a); }
 
 csa2_status hip_status(hipError_t e, const char* what) {
   if (e == hipSuccess) return CSA2_OK;
@@ -143,6 +145,8 @@ csa2_status csa2_decode_append(const uint16_t* h_new, const uint16_t* z_new,
           (!state->swa_codes || al(state->swa_codes, 16)) &&
           (!state->swa_scale || al(state->swa_scale, 4)),
       "h_new, z_new, swa_new, w_ik and the state arrays must be 16-byte aligned");
+  REQ(al0(n_vis, 8) && al0(swa_start, 8) && al0(swa_len, 4),
+      "n_vis and swa_start must be 8-byte aligned, swa_len 4-byte aligned");
   hipStream_t st = (hipStream_t)stream;
   const uint16_t* zn = m == 1 ? nullptr : z_new;
   return hip_status(csa2::launch_append(h_new, zn, W > 0 ? swa_new : nullptr, B, m,
@@ -171,7 +175,10 @@ static csa2_status index_score_common(const uint16_t* q_idx, const float* w,
       (long long)n_cols);
   REQ(cand || n_cols <= src->cap, "n_cols=%lld exceeds cap=%lld", (long long)n_cols,
       (long long)src->cap);
-  REQ(al(q_idx, 16) && al(w, 4) && al(scores, 4), "q_idx must be 16-byte aligned");
+  REQ(al(q_idx, 16) && al(w, 4) && al(q_seq, 4) && al(n_vis, 8) && al0(cand, 4) &&
+          al(scores, 4),
+      "q_idx must be 16-byte aligned, n_vis 8-byte aligned, w, q_seq, cand and scores "
+      "4-byte aligned");
   if (n_cols == 0) return CSA2_OK;
   REQ((n_cols + 1023) / 1024 * (int64_t)Q < (int64_t)1 << 31, "launch too large");
   if (device_checks()) {
@@ -228,14 +235,16 @@ csa2_status csa2_index_score_levels(const uint16_t* q_idx, const float* w, const
 }
 
 static csa2_status select_common(const float* scores, int64_t ld, int Q, const int64_t* n_valid,
-                                 int64_t n_cols, int kk, void* ws, size_t ws_bytes, int mode) {
+                                 const int32_t* col_ids, int64_t n_cols, int kk, void* ws,
+                                 size_t ws_bytes, int mode) {
   REQ(scores && n_valid, "scores and n_valid must not be NULL");
   REQ(Q > 0, "Q=%d must be > 0", Q);
   REQ(kk >= 1 && kk <= CSA2_MAX_K, "k=%d must be in [1, %d]", kk, CSA2_MAX_K);
   REQ(n_cols >= 0 && n_cols <= CSA2_MAX_COLS, "n_cols=%lld must be in [0, %d]",
       (long long)n_cols, CSA2_MAX_COLS);
   REQ(ld >= n_cols && ld > 0, "ld=%lld < n_cols=%lld", (long long)ld, (long long)n_cols);
-  REQ(al(scores, 4), "scores must be 4-byte aligned");
+  REQ(al(scores, 4) && al(n_valid, 8) && al0(col_ids, 4),
+      "scores and col_ids must be 4-byte aligned, n_valid 8-byte aligned");
   const size_t need = csa2::select_ws_bytes(Q, n_cols, mode);
   if (need > 0 && (!ws || ws_bytes < need))
     return fail(CSA2_EWORKSPACE, "workspace %zu bytes < %zu needed", ws ? ws_bytes : (size_t)0,
@@ -248,8 +257,9 @@ csa2_status csa2_select_topk(const float* scores, int64_t ld, int Q, const int64
                              const int32_t* col_ids, int64_t n_cols, int k, int32_t* out,
                              void* ws, size_t ws_bytes, void* stream) {
   g_err[0] = 0;
-  REQ(out, "out must not be NULL");
-  const csa2_status st = select_common(scores, ld, Q, n_valid, n_cols, k, ws, ws_bytes, 0);
+  REQ(out && al(out, 4), "out must not be NULL and 4-byte aligned");
+  const csa2_status st =
+      select_common(scores, ld, Q, n_valid, col_ids, n_cols, k, ws, ws_bytes, 0);
   if (st != CSA2_OK) return st;
   return hip_status(csa2::launch_select(scores, ld, Q, n_valid, col_ids, n_cols, k, 0, out, k,
                                         nullptr, 0, nullptr, ws, (hipStream_t)stream),
@@ -261,9 +271,10 @@ csa2_status csa2_select_topk_levels(const float* scores, int64_t ld, int Q,
                                     int64_t n_cols, int k, int32_t* out, void* ws,
                                     size_t ws_bytes, void* stream) {
   g_err[0] = 0;
-  REQ(out, "out must not be NULL");
+  REQ(out && al(out, 4), "out must not be NULL and 4-byte aligned");
   REQ(!col_ids, "col_ids must be NULL (the levels are those of a full scan)");
-  const csa2_status st = select_common(scores, ld, Q, n_valid, n_cols, k, ws, ws_bytes, 0);
+  const csa2_status st =
+      select_common(scores, ld, Q, n_valid, col_ids, n_cols, k, ws, ws_bytes, 0);
   if (st != CSA2_OK) return st;
   return hip_status(csa2::launch_select(scores, ld, Q, n_valid, col_ids, n_cols, k, 0, out, k,
                                         nullptr, 0, nullptr, ws, (hipStream_t)stream, true),
@@ -274,14 +285,15 @@ csa2_status csa2_select_topk_noalloc(const float* scores, int64_t ld, int Q,
                                      const int64_t* n_valid, const int32_t* col_ids,
                                      int64_t n_cols, int k, int32_t* out, void* stream) {
   g_err[0] = 0;
-  REQ(out, "out must not be NULL");
+  REQ(out && al(out, 4), "out must not be NULL and 4-byte aligned");
   REQ(scores && n_valid, "scores and n_valid must not be NULL");
   REQ(Q > 0, "Q=%d must be > 0", Q);
   REQ(k >= 1 && k <= CSA2_MAX_K, "k=%d must be in [1, %d]", k, CSA2_MAX_K);
   REQ(n_cols >= 0 && n_cols <= CSA2_MAX_COLS, "n_cols=%lld must be in [0, %d]",
       (long long)n_cols, CSA2_MAX_COLS);
   REQ(ld >= n_cols && ld > 0, "ld=%lld < n_cols=%lld", (long long)ld, (long long)n_cols);
-  REQ(al(scores, 4), "scores must be 4-byte aligned");
+  REQ(al(scores, 4) && al(n_valid, 8) && al0(col_ids, 4),
+      "scores and col_ids must be 4-byte aligned, n_valid 8-byte aligned");
   const size_t need = csa2::select_ws_bytes(Q, n_cols, 0);
   if (need > csa2::SEL_SCRATCH_BYTES)
     return fail(CSA2_EUNSUPPORTED,
@@ -307,8 +319,11 @@ csa2_status csa2_block_pool(const float* scores, int64_t ld, int Q, const int64_
   REQ(pool && pool_len, "pool and pool_len must not be NULL");
   REQ(k >= 0 && k <= n_blocks, "k=%d must be in [0, n_blocks=%d]", k, n_blocks);
   REQ(k == 0 || topk, "topk must not be NULL when k > 0");
+  REQ(al(pool, 4) && al(pool_len, 8) && al0(topk, 4),
+      "pool and topk must be 4-byte aligned, pool_len 8-byte aligned");
   if (block != 8) return fail(CSA2_EUNSUPPORTED, "block=%d: only blocks of 8 positions", block);
-  const csa2_status st = select_common(scores, ld, Q, n_valid, n_cols, n_blocks, ws, ws_bytes, 1);
+  const csa2_status st =
+      select_common(scores, ld, Q, n_valid, nullptr, n_cols, n_blocks, ws, ws_bytes, 1);
   if (st != CSA2_OK) return st;
   return hip_status(csa2::launch_select(scores, ld, Q, n_valid, nullptr, n_cols, n_blocks, 1, pool,
                                         (int64_t)n_blocks * 8, pool_len, k, topk, ws,
@@ -340,9 +355,13 @@ static csa2_status select_attend_common(const float* scores, int64_t ld, int Q,
   if (cs != CSA2_OK) return cs;
   REQ(T_swa >= 0, "T_swa must be >= 0");
   REQ(T_swa == 0 || (swa_codes && swa_scale), "swa_codes / swa_scale NULL with T_swa > 0");
-  REQ(al(scores, 4) && al(q, 16) && al(out, 16) && (!swa_codes || al(swa_codes, 16)) &&
-          (!pool || al(pool, 16)),
-      "scores must be 4-byte aligned, q, out, swa_codes and pool 16-byte aligned");
+  REQ(al(q, 16) && al(out, 16) && al0(swa_codes, 16),
+      "q, out and swa_codes must be 16-byte aligned");
+  REQ(al(scores, 4) && al(n_valid, 8) && al0(col_ids, 4) && al(idx, 4) && al0(pool, 4) &&
+          al0(pool_len, 8) && al(q_seq, 4) && al0(swa_scale, 4) && al(swa_start, 8) &&
+          al(swa_len, 4) && al0(lse, 4),
+      "n_valid, pool_len and swa_start must be 8-byte aligned, the other int32 / fp32 "
+      "arrays 4-byte aligned");
   const int mode = n_blocks > 0 ? 1 : 0;
   const size_t need = csa2::select_attend_ws_bytes(Q, n_cols, mode, k);
   if (!ws || ws_bytes < need)
@@ -406,6 +425,9 @@ static csa2_status attend_common(const uint16_t* q, const int32_t* q_seq, int Q,
   REQ(al(q, 16) && (!out || al(out, 16)) && (!rp.out_bf16 || al(rp.out_bf16, 16)) &&
           (!swa_codes || al(swa_codes, 16)),
       "q, out, swa_codes must be 16-byte aligned");
+  REQ(al(q_seq, 4) && al0(idx, 4) && al0(swa_scale, 4) && al(swa_start, 8) && al(swa_len, 4) &&
+          al0(lse, 4),
+      "swa_start must be 8-byte aligned, q_seq, idx, swa_scale, swa_len, lse 4-byte aligned");
   REQ(!ws || al(ws, 16), "ws must be 16-byte aligned");
   REQ(Q > 0 && Q <= (1 << 24), "Q=%d must be in [1, 2^24]", Q);
   if (device_checks()) {

@@ -198,3 +198,98 @@ def test_workspace_sizes():
 
 def test_selftest_counter_query():
     assert C.lib().csa2_selftest(None, 0, None) == 8
+
+
+def test_alignment_validation():
+    """Every array must be aligned to at least its element size: a pointer
+    off by 4 bytes for an int64 array, or by 2 bytes for an int32 / fp32 one,
+    is refused on the host with CSA2_EINVAL.  Each call below is otherwise
+    one that stops before any launch (a short workspace, nothing to score,
+    an empty batch), so a missing check shows as a status other than EINVAL."""
+    L = C.lib()
+    P = FAKE
+    A4 = ctypes.c_void_p(0x10004)        # 4-byte aligned, not 8
+    A2 = ctypes.c_void_p(0x10002)        # 2-byte aligned, not 4
+    cs = _cache(cap=1 << 20)
+
+    def einval(st):
+        assert st == 1, st
+        assert b"aligned" in L.csa2_last_error(), L.csa2_last_error()
+
+    # index scores (n_cols = 0: returns before any launch once validated)
+    for entry in ("csa2_index_score", "csa2_index_score_fp4q"):
+        f = getattr(L, entry)
+        assert f(P, P, P, P, None, 0, 1, 0, ctypes.byref(cs), P, 10, None) == 0
+        einval(f(P, P, A2, P, None, 0, 1, 0, ctypes.byref(cs), P, 10, None))    # q_seq
+        einval(f(P, P, P, A4, None, 0, 1, 0, ctypes.byref(cs), P, 10, None))    # n_vis
+        einval(f(P, P, P, P, A2, 10, 1, 0, ctypes.byref(cs), P, 10, None))      # cand
+        einval(f(P, A2, P, P, None, 0, 1, 0, ctypes.byref(cs), P, 10, None))    # w
+        einval(f(P, P, P, P, None, 0, 1, 0, ctypes.byref(cs), A2, 10, None))    # scores
+    # top-k (20000 columns with no workspace: CSA2_EWORKSPACE once validated)
+    n = 20000
+    assert L.csa2_select_topk(P, n, 1, P, None, n, 5, P, None, 0, None) == 3
+    einval(L.csa2_select_topk(P, n, 1, P, None, n, 5, A2, None, 0, None))       # out
+    einval(L.csa2_select_topk(P, n, 1, A4, None, n, 5, P, None, 0, None))       # n_valid
+    einval(L.csa2_select_topk(P, n, 1, P, A2, n, 5, P, None, 0, None))          # col_ids
+    einval(L.csa2_select_topk(A2, n, 1, P, None, n, 5, P, None, 0, None))       # scores
+    assert L.csa2_select_topk_levels(P, n, 1, P, None, n, 5, P, None, 0, None) == 3
+    einval(L.csa2_select_topk_levels(P, n, 1, P, None, n, 5, A2, None, 0, None))
+    einval(L.csa2_select_topk_levels(P, n, 1, A4, None, n, 5, P, None, 0, None))
+    # the allocation-free top-k (a size past its static scratch: EUNSUPPORTED)
+    Q, m = 64, 1 << 19
+    assert L.csa2_select_topk_noalloc(P, m, Q, P, None, m, 512, P, None) == 2
+    einval(L.csa2_select_topk_noalloc(P, m, Q, P, None, m, 512, A2, None))
+    einval(L.csa2_select_topk_noalloc(P, m, Q, A4, None, m, 512, P, None))
+    einval(L.csa2_select_topk_noalloc(P, m, Q, P, A2, m, 512, P, None))
+    # block pool with its top-k
+    assert L.csa2_block_pool(P, n, 1, P, n, 8, 4, P, P, 4, P, None, 0, None) == 3
+    einval(L.csa2_block_pool(P, n, 1, P, n, 8, 4, A2, P, 4, P, None, 0, None))  # pool
+    einval(L.csa2_block_pool(P, n, 1, P, n, 8, 4, P, A4, 4, P, None, 0, None))  # pool_len
+    einval(L.csa2_block_pool(P, n, 1, P, n, 8, 4, P, P, 4, A2, None, 0, None))  # topk
+    einval(L.csa2_block_pool(P, n, 1, A4, n, 8, 4, P, P, 4, P, None, 0, None))  # n_valid
+
+    # fused selection + attention (no workspace: CSA2_EWORKSPACE once validated)
+    def sa(entry="csa2_select_attend", **kw):
+        a = dict(scores=P, n_valid=P, col_ids=None, idx=P, pool=P, pool_len=P, q=P, q_seq=P,
+                 swa_codes=P, swa_scale=P, swa_start=P, swa_len=P, out=P, lse=P)
+        a.update(kw)
+        return getattr(L, entry)(a["scores"], n, 1, a["n_valid"], a["col_ids"], n, 4, a["idx"], 4,
+                                 a["pool"], a["pool_len"], a["q"], a["q_seq"], ctypes.byref(cs),
+                                 a["swa_codes"], a["swa_scale"], 8, a["swa_start"], a["swa_len"],
+                                 a["out"], a["lse"], None, 0, None)
+
+    assert sa() == 3 and sa("csa2_select_attend_levels") == 3
+    for name, bad in (("n_valid", A4), ("idx", A2), ("pool", A2), ("pool_len", A4),
+                      ("q_seq", A2), ("swa_scale", A2), ("swa_start", A4), ("swa_len", A2),
+                      ("lse", A2), ("scores", A2), ("out", ctypes.c_void_p(0x10008)),
+                      ("q", ctypes.c_void_p(0x10008))):
+        einval(sa(**{name: bad}))
+        einval(sa("csa2_select_attend_levels", **{name: bad}))
+    assert sa(pool=ctypes.c_void_p(0x10004)) == 3    # the pool needs only 4-byte alignment
+
+    # attention (Q = 0: refused after the alignment checks, for another reason)
+    def at(**kw):
+        a = dict(q=P, q_seq=P, idx=P, swa_codes=P, swa_scale=P, swa_start=P, swa_len=P, out=P,
+                 lse=P)
+        a.update(kw)
+        return L.csa2_sparse_attend(a["q"], a["q_seq"], 0, ctypes.byref(cs), a["idx"], 8,
+                                    a["swa_codes"], a["swa_scale"], 4, a["swa_start"],
+                                    a["swa_len"], a["out"], a["lse"], None, 0, None)
+
+    assert at() == 1 and b"aligned" not in L.csa2_last_error()
+    for name, bad in (("q_seq", A2), ("idx", A2), ("swa_scale", A2), ("swa_start", A4),
+                      ("swa_len", A2), ("lse", A2), ("out", ctypes.c_void_p(0x10008))):
+        einval(at(**{name: bad}))
+
+
+def test_decode_append_output_alignment():
+    L = C.lib()
+    cs = _cache()
+    P = FAKE
+    st = C._State(0x10000, 0x10000, 0x10000, 0x10000, 0x10000, 8, 2)
+    for nv, ss, sl in ((0x10004, None, None), (None, 0x10004, None), (None, None, 0x10002)):
+        r = L.csa2_decode_append(P, P, P, 2, P, ctypes.byref(cs), ctypes.byref(st),
+                                 None if nv is None else ctypes.c_void_p(nv),
+                                 None if ss is None else ctypes.c_void_p(ss),
+                                 None if sl is None else ctypes.c_void_p(sl), None)
+        assert r == 1 and b"aligned" in L.csa2_last_error()
