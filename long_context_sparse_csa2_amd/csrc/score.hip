@@ -11,8 +11,8 @@
 // (rows = the query's 32 heads, columns = entries, K = the 128 dims in 8
 // bf16 32x32x16 steps).  The query tile stays in registers for the whole
 // scan; each lane streams 32 contiguous bytes of one entry's MXFP4 codes
-// (its half of the 128 dims) plus the entry's 4 scale bytes, and converts
-// them to bf16 with the gfx950 scaled FP4 conversion (exact for the
+// (its half of the 128 dims) plus the 2 scale bytes of those dims, and
+// converts them to bf16 with the gfx950 scaled FP4 conversion (exact for the
 // power-of-two E8M0 scales).  The ReLU, the head weights and the head sum
 // are applied to the accumulator in registers and the two lane halves are
 // summed with one cross-lane exchange (a row-swapping permute, no LDS round
@@ -137,7 +137,8 @@ __global__ __launch_bounds__(256, 4) void k_index_score(
   // are then requested together with n_vis instead of one after the other
   // (a workgroup past n_vis scores entry 0 and its stores are dropped).
   if (!CAND && cbase >= nv) return;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
   const int r = lane & 31, half = lane >> 5;
   const int64_t seq_base = (int64_t)q_seq[q] * cap;
 
@@ -168,20 +169,43 @@ __global__ __launch_bounds__(256, 4) void k_index_score(
 
   const int32_t* crow = CAND ? cand + (int64_t)q * ld_cand : nullptr;
   float* srow = scores + (int64_t)q * ld;
+  const int code_off = r * 64 + half * 32, scale_off = r * 4 + half * 2;
+  // score store offset within a tile: the first lane half writes column r,
+  // the second an offset past any resource (dropped)
+  const int st_off = half == 0 ? r * 4 : (int)0x80000000;
 
+  // Tile loads.  Each lane reads 32 code bytes of entry col0 + r (its lane
+  // half's two MX blocks) and those blocks' two scale bytes (block 2 half in
+  // bits 0-7, 2 half + 1 in bits 8-15 of scw).  A contiguous scan reads
+  // through two buffer resources over the workgroup's visible entries from
+  // its first column cbase on (codes and scales), so a tile's addresses are
+  // one add of a wave-uniform offset per array and lanes past the row's end
+  // read zeros (their scores are never stored).  The offsets fit 31 bits:
+  // the host interleaves the workgroups' tiles across a row only for rows of
+  // fewer than 2^24 columns (a tile requested ahead lies at most two tile
+  // strides past the row), otherwise a workgroup's tiles (and the tiles it
+  // requests ahead) lie within its own chunk and the next one.
+  const int64_t vis_wg = nv - cbase;                  // > 0 (the workgroup has columns)
+  const __amdgpu_buffer_rsrc_t rcodes = make_rsrc(
+      ik_codes + (seq_base + cbase) * 64, vis_wg < ((int64_t)1 << 25) ? vis_wg * 64 : 0x7FFFFFFFll);
+  const __amdgpu_buffer_rsrc_t rscales =
+      make_rsrc(ik_scales + (seq_base + cbase) * 4, vis_wg * 4);
   auto load = [&](int64_t col0, u32x4_t& c0, u32x4_t& c1, uint32_t& scw) {
-    const int64_t c = col0 + r;
-    int64_t e;
-    if constexpr (CAND) {                             // id read within the launch's columns
-      const int32_t id = crow[c < n_cols ? c : n_cols - 1];
-      e = c < nv ? id : 0;                            // past n_vis: entry 0
+    if constexpr (CAND) {
+      const int64_t c = col0 + r;
+      const int32_t id = crow[c < n_cols ? c : n_cols - 1];   // read within the launch's columns
+      const int64_t e = c < nv ? id : 0;                      // past n_vis: entry 0
+      const uint8_t* cp = ik_codes + (seq_base + e) * 64 + half * 32;
+      c0 = *(const u32x4_t*)cp;
+      c1 = *(const u32x4_t*)(cp + 16);
+      scw = *(const uint16_t*)(ik_scales + (seq_base + e) * 4 + half * 2);
     } else {
-      e = c < nv ? c : nv - 1;                        // past the end: re-read the last entry
+      const int d = (int)(col0 - cbase);              // < 2^25 (see above)
+      const int oc = code_off + d * 64;
+      c0 = __builtin_amdgcn_raw_buffer_load_b128(rcodes, oc, 0, 0);
+      c1 = __builtin_amdgcn_raw_buffer_load_b128(rcodes, oc + 16, 0, 0);
+      scw = __builtin_amdgcn_raw_buffer_load_b16(rscales, scale_off + d * 4, 0, 0);
     }
-    const uint8_t* cp = ik_codes + (seq_base + e) * 64 + half * 32;
-    c0 = *(const u32x4_t*)cp;
-    c1 = *(const u32x4_t*)(cp + 16);
-    scw = *(const uint32_t*)(ik_scales + (seq_base + e) * 4);
   };
 
   // The score row as a buffer resource over its nv valid columns: the
@@ -255,19 +279,19 @@ __global__ __launch_bounds__(256, 4) void k_index_score(
     const uint32_t scw = rs[sl];
     f32x16_t acc = {};
     if constexpr (FP4Q) {
-      const uint32_t ksc = scw >> (16 * half);
       const i32x8_t b0 = {(int)c0[0], (int)c0[1], (int)c0[2], (int)c0[3], 0, 0, 0, 0};
       const i32x8_t b1 = {(int)c1[0], (int)c1[1], (int)c1[2], (int)c1[3], 0, 0, 0, 0};
-      // format 4 (E2M1) for both operands; scale operands are E8M0 bytes
-      acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(qa0, b0, acc, 4, 4, 0,
-                                                            (int)(qsc & 0xFFu), 0,
-                                                            (int)(ksc & 0xFFu));
-      acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(qa1, b1, acc, 4, 4, 0,
-                                                            (int)((qsc >> 8) & 0xFFu), 0,
-                                                            (int)((ksc >> 8) & 0xFFu));
+      // format 4 (E2M1) for both operands; the scale operands are E8M0
+      // bytes, byte 0 of qsc / scw for MFMA 0 and byte 1 for MFMA 1
+      acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(qa0, b0, acc, 4, 4, 0, (int)qsc, 0,
+                                                            (int)scw);
+      acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(qa1, b1, acc, 4, 4, 1, (int)qsc, 1,
+                                                            (int)scw);
     } else {
-      const float s_lo = e8m0_val((scw >> (16 * half)) & 0xFFu);
-      const float s_hi = e8m0_val((scw >> (16 * half + 8)) & 0xFFu);
+      // 2^(c - 127) of each E8M0 byte c: c moved into the exponent field,
+      // 2^-127 (a subnormal) for c = 0
+      const float s_lo = __uint_as_float(max((scw << 23) & 0x7F800000u, 0x00400000u));
+      const float s_hi = __uint_as_float(max((scw << 15) & 0x7F800000u, 0x00400000u));
       acc = mfma32_bf16(a[0], fp4x8_to_bf16_pow2(c0[0], s_lo), acc);
       acc = mfma32_bf16(a[1], fp4x8_to_bf16_pow2(c0[1], s_lo), acc);
       acc = mfma32_bf16(a[2], fp4x8_to_bf16_pow2(c0[2], s_lo), acc);
@@ -282,10 +306,14 @@ __global__ __launch_bounds__(256, 4) void k_index_score(
     for (int j = 0; j < 16; ++j) part += wr[j] * relu_f32(acc[j]);
     part = lanes_sum32(part);
     // (columns and their byte offsets fit 32 bits: n_cols < 2^29)
-    const int c = (int)col0 + r;
-    const bool vis = c < (int)nv;
-    const int off = half == 0 && vis ? c * 4 : (int)0x80000000;
-    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(part), srs, off, 0, 0);
+    const bool vis = r < (int)(nv - col0);
+    if constexpr (CAND) {
+      const int off = half == 0 && vis ? ((int)col0 + r) * 4 : (int)0x80000000;
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(part), srs, off, 0, 0);
+    } else {                  // the second lane half at 2^31 + col0 * 4 >= nv * 4: dropped
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(part), srs, st_off + (int)col0 * 4, 0,
+                                            0);
+    }
     if constexpr (LV) {
       // both lane halves hold the tile's 32 scores; columns past nv count
       // as key 0, below every score's key
@@ -398,7 +426,7 @@ hipError_t launch_index_score(const uint16_t* q_idx, const float* w, const int32
   // workgroups of a query read one contiguous window instead of nchunk
   // windows a fixed power-of-two stride apart (measured on MI355X: 2-7 %
   // faster at 512K-1M entries, 3-5 % slower at 64K).
-  const bool inter = nchunk >= 128;
+  const bool inter = nchunk >= 128 && n_cols < ((int64_t)1 << 24);
   const int64_t slice = (int64_t)SC_WAVES * 32 * (lv_scan ? 2 : 1);
   const int64_t cs = inter ? slice : cols;
   const int64_t ts = inter ? nchunk * slice : slice;
