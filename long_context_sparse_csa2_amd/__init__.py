@@ -19,6 +19,7 @@ LIB_PATH = os.environ.get("CSA2_LIB") or os.path.join(_PKG, "libcsa2.so")
 
 CSA2_OP_TOPK, CSA2_OP_POOL, CSA2_OP_ATTEND = 1, 2, 3
 CSA2_OP_SELECT_ATTEND, CSA2_OP_POOL_ATTEND = 4, 5
+CSA2_MAX_K, CSA2_MAX_COLS = 2048, 1 << 24          # as include/csa2.h
 STATUS = {0: "CSA2_OK", 1: "CSA2_EINVAL", 2: "CSA2_EUNSUPPORTED", 3: "CSA2_EWORKSPACE", 4: "CSA2_EHIP"}
 EXPORTS = ("csa2_status_string", "csa2_last_error", "csa2_compress_quant", "csa2_index_score",
            "csa2_index_score_fp4q", "csa2_select_topk", "csa2_block_pool", "csa2_sparse_attend",

@@ -30,6 +30,15 @@ def test_exports_every_declared_symbol():
         assert hasattr(L, n), n
 
 
+def test_constants_match_the_header():
+    src = open(os.path.join(ROOT, "include", "csa2.h")).read()
+    for name in ("CSA2_MAX_K", "CSA2_MAX_COLS", "CSA2_OP_TOPK", "CSA2_OP_POOL", "CSA2_OP_ATTEND",
+                 "CSA2_OP_SELECT_ATTEND", "CSA2_OP_POOL_ATTEND"):
+        m = re.search(r"#define\s+" + name + r"\s+(\(1 << \d+\)|\d+)", src)
+        assert m, name
+        assert eval(m.group(1)) == getattr(C, name), name
+
+
 def test_status_strings():
     L = C.lib()
     assert L.csa2_status_string(0) == b"CSA2_OK"

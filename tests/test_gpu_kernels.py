@@ -156,6 +156,78 @@ def test_index_score_long_ragged(fp4q):
         checks.check_scores(s[i, cols], ref)
 
 
+def _device_indexer_cache(cap, seed):
+    """One sequence of random MXFP4 indexer keys generated on the device (the
+    scan reads only the indexer arrays; the main-KV arrays are one entry)."""
+    g = torch.Generator(device=DEV).manual_seed(seed)
+    cache = C.Cache.__new__(C.Cache)
+    cache.B, cache.cap = 1, cap
+    cache.kv_codes = torch.zeros(1, 1, 256, dtype=torch.uint8, device=DEV)
+    cache.kv_scales = torch.zeros(1, 1, 32, dtype=torch.uint8, device=DEV)
+    cache.ik_codes = torch.randint(0, 256, (1, cap, 64), generator=g, dtype=torch.uint8, device=DEV)
+    cache.ik_scales = torch.randint(120, 135, (1, cap, 4), generator=g, dtype=torch.uint8, device=DEV)
+    return cache
+
+
+@pytest.mark.parametrize("fp4q", [False, True])
+@pytest.mark.parametrize("N", [(1 << 24) + 4100, (1 << 25) + 4100])
+def test_index_score_longest_rows(N, fp4q):
+    # rows past the length up to which workgroups interleave their tiles
+    # (2^24 columns) and past 2^25 columns, where a workgroup addresses its
+    # keys from its own first column: sampled columns at the row's start and
+    # end, around those lengths and the workgroup chunk edges, against the
+    # oracle; a query that ends mid-row leaves the rest of its row untouched
+    Q = 2
+    print(f"[longest rows] N={N} fp4q={fp4q}", flush=True)
+    cache = _device_indexer_cache(N, 95)
+    q, w = _scores_inputs(Q, 96)
+    n_vis = [N, N - 4133]
+    scores = torch.full((Q, N), -7.0, device=DEV)
+    C.csa2_index_score(q.to(DEV), w.to(DEV), torch.zeros(Q, dtype=torch.int32, device=DEV),
+                       torch.tensor(n_vis, dtype=torch.int64).to(DEV), None, N, cache, scores,
+                       fp4q=fp4q)
+    torch.cuda.synchronize()
+    q64, w64 = checks.bf16_to_f64(q), w.double().numpy()
+    rng = np.random.default_rng(97)
+    for i in range(Q):
+        nv = n_vis[i]
+        edges = [0, 4096, (1 << 24) - 64, 1 << 24, (1 << 25) - 64, 1 << 25, nv - 4096 - 64, nv - 128]
+        cols = np.unique(np.concatenate([rng.choice(nv, 2000, replace=False)] +
+                                        [np.arange(e, e + 128) for e in edges]))
+        cols = cols[(cols >= 0) & (cols < nv)]
+        idx = torch.from_numpy(cols).to(DEV)
+        got = checks.host(scores[i].index_select(0, idx))
+        khat = R.dequant_mxfp4(checks.host(cache.ik_codes[0].index_select(0, idx)),
+                               checks.host(cache.ik_scales[0].index_select(0, idx)))
+        ref = (_oracle_scores_fp4q(q64[i], w64[i], khat) if fp4q
+               else R.index_scores(q64[i], w64[i], khat))
+        checks.check_scores(got, ref)
+        assert bool((scores[i, nv:] == -7.0).all())
+
+
+def test_select_at_max_columns():
+    # CSA2_MAX_COLS columns (the largest selection row), full and ragged:
+    # top-512, top-2048 and the 2048-block pool with its top-512
+    n = C.CSA2_MAX_COLS
+    Q = 2
+    s = _rand_scores(Q, n, seed=98)
+    nv = [n, n - 1001]
+    for k, rows in ((512, (0, 1)), (2048, (1,))):     # (the oracle's ranking of 2^24 takes seconds)
+        out = _topk(s, nv, k)
+        for i in rows:
+            checks.check_topk_exact(out[i], s[i, :nv[i]], k)
+    ws = C.workspace(C.CSA2_OP_POOL, Q, n, 2048, DEV)
+    pool = torch.empty(Q, 16384, dtype=torch.int32, device=DEV)
+    plen = torch.empty(Q, dtype=torch.int64, device=DEV)
+    topk = torch.empty(Q, 512, dtype=torch.int32, device=DEV)
+    C.csa2_block_pool(torch.from_numpy(s).to(DEV), torch.tensor(nv, dtype=torch.int64).to(DEV), n,
+                      2048, pool, plen, ws, topk=topk)
+    torch.cuda.synchronize()
+    for i in range(Q):
+        checks.check_pool_exact(checks.host(pool[i]), checks.host(plen[i]), s[i, :nv[i]], 8, 2048)
+        checks.check_topk_exact(checks.host(topk[i]), s[i, :nv[i]], 512)
+
+
 def test_index_score_candidates_multi_tile():
     # 64 queries over 4,096 candidate columns: two tiles per wave, so
     # workgroups and tiles past a query's candidate count score entry 0 and
