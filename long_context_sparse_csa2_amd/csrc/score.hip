@@ -48,6 +48,16 @@
 namespace csa2 {
 
 constexpr int SC_WAVES = 4;
+// Two-query prefill scan (k_index_score_pair): used for launches of at
+// least SC_PAIR_MIN_Q queries over more than SC_PAIR_MIN_COLS columns, 32
+// tiles per wave, one tile's bytes in flight.  Measured on MI355X against
+// the one-query scan: 65,536-token prefill chunk scans 4.02 -> 3.81 ms per
+// group, 1,048,576-token 1.175 -> 1.038 s; at 4,096 columns (one chunk of
+// 4,096 queries) 76 -> 79 us, so short rows keep the one-query scan; two
+// tiles in flight or 16 tiles per wave ran 2-10 % slower.
+constexpr int SC_PAIR_MIN_Q = 2048;
+constexpr int64_t SC_PAIR_MIN_COLS = 4096;
+constexpr int SC_PAIR_TPW = 32, SC_PAIR_DEPTH = 1;
 // Fourth word of a raw (unformatted, stride 0) buffer resource on gfx9:
 // 32-bit data format, so a store is range-checked in bytes against the
 // resource's record count.
@@ -377,6 +387,128 @@ __global__ __launch_bounds__(256, 4) void k_index_score(
   }
 }
 
+// Two queries per wave (long prefill rows, bf16 query): the queries 2p and
+// 2p + 1 of a causal prefill chunk see (nearly) the same entries, so a wave
+// converts each 32-entry key tile to bf16 once and feeds it to the MFMAs of
+// both: half the FP4 conversions per (query, entry), which with the epilogue
+// bound the single-query scan of long rows.  Each query's accumulator sees
+// the same operands in the same order as in the single-query scan, so the
+// scores are the same bits.  Loads run to the longer of the two rows, each
+// query's stores stop at its own.  A pair on two sequences (or the last,
+// unpaired query) is scored one query at a time, the wave then scoring that
+// query for both of its slots (the same value stored twice).
+template <int TPW, int DEPTH>
+__global__ __launch_bounds__(256, 2) void k_index_score_pair(
+    const uint16_t* __restrict__ q_idx, const float* __restrict__ w,
+    const int32_t* __restrict__ q_seq, const int64_t* __restrict__ n_vis, int Q, int64_t nchunk,
+    int64_t chunk_stride, int64_t tile_stride, int64_t n_cols,
+    const uint8_t* __restrict__ ik_codes, const uint8_t* __restrict__ ik_scales, int64_t cap,
+    float* __restrict__ scores, int64_t ld) {
+  const int p = (int)(gridDim.x / nchunk - 1 - blockIdx.x / nchunk);   // last pairs first
+  const int64_t cbase = (int64_t)(blockIdx.x % nchunk) * chunk_stride;
+  const int q0 = 2 * p, q1 = 2 * p + 1 < Q ? 2 * p + 1 : 2 * p;
+  const bool joint = q1 != q0 && q_seq[q0] == q_seq[q1];
+  const int npass = q1 != q0 && !joint ? 2 : 1;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  const int r = lane & 31, half = lane >> 5;
+  const int code_off = r * 64 + half * 32, scale_off = r * 4 + half * 2;
+  const int st_off = half == 0 ? r * 4 : (int)0x80000000;
+  for (int pass = 0; pass < npass; ++pass) {
+    const int qa = pass == 0 ? q0 : q1;
+    const int qb = joint ? q1 : qa;
+    const int64_t na0 = n_vis[qa], nb0 = n_vis[qb];
+    const int64_t nva = na0 < 0 ? 0 : (na0 < n_cols ? na0 : n_cols);
+    const int64_t nvb = nb0 < 0 ? 0 : (nb0 < n_cols ? nb0 : n_cols);
+    const int64_t nv = nva > nvb ? nva : nvb;
+    if (cbase >= nv) continue;                            // uniform
+    const int64_t seq_base = (int64_t)q_seq[qa] * cap;
+    bf16x8_t a0[8], a1[8];
+    float w0[16], w1[16];
+    {
+      const uint16_t* pa = q_idx + ((int64_t)qa * H_IDX + r) * D_IDX + half * 64;
+      const uint16_t* pb = q_idx + ((int64_t)qb * H_IDX + r) * D_IDX + half * 64;
+#pragma unroll
+      for (int s = 0; s < 8; ++s) {
+        a0[s] = *(const bf16x8_t*)(pa + 8 * s);
+        a1[s] = *(const bf16x8_t*)(pb + 8 * s);
+      }
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const int h = 8 * (j >> 2) + 4 * half + (j & 3);
+        w0[j] = w[qa * H_IDX + h];
+        w1[j] = w[qb * H_IDX + h];
+      }
+    }
+    const __amdgpu_buffer_rsrc_t sra = make_rsrc(scores + (int64_t)qa * ld, nva * 4);
+    const __amdgpu_buffer_rsrc_t srb = make_rsrc(scores + (int64_t)qb * ld, nvb * 4);
+    const int64_t vis_wg = nv - cbase;
+    const __amdgpu_buffer_rsrc_t rcodes = make_rsrc(
+        ik_codes + (seq_base + cbase) * 64, vis_wg < ((int64_t)1 << 25) ? vis_wg * 64 : 0x7FFFFFFFll);
+    const __amdgpu_buffer_rsrc_t rscales = make_rsrc(ik_scales + (seq_base + cbase) * 4, vis_wg * 4);
+
+    u32x4_t r0[DEPTH + 1], r1[DEPTH + 1];
+    uint32_t rs[DEPTH + 1];
+    const int64_t step = tile_stride;
+    const int64_t col_first = cbase + (int64_t)wave * 32;
+    auto load = [&](int t, int sl) __attribute__((always_inline)) {
+      const int d = (int)(col_first + (int64_t)t * step - cbase);   // < 2^25, as in the single scan
+      const int oc = code_off + d * 64;
+      r0[sl] = __builtin_amdgcn_raw_buffer_load_b128(rcodes, oc, 0, 0);
+      r1[sl] = __builtin_amdgcn_raw_buffer_load_b128(rcodes, oc + 16, 0, 0);
+      rs[sl] = __builtin_amdgcn_raw_buffer_load_b16(rscales, scale_off + d * 4, 0, 0);
+    };
+#pragma unroll
+    for (int t = 0; t < DEPTH; ++t)
+      if (t < TPW) load(t, t);
+    auto tile = [&](int t, int sl, bool pf) __attribute__((always_inline)) {
+      if (pf) load(t + DEPTH, (sl + DEPTH) % (DEPTH + 1));
+      __builtin_amdgcn_sched_barrier(0);
+      const u32x4_t c0 = r0[sl], c1 = r1[sl];
+      const uint32_t scw = rs[sl];
+      const float s_lo = __uint_as_float(max((scw << 23) & 0x7F800000u, 0x00400000u));
+      const float s_hi = __uint_as_float(max((scw << 15) & 0x7F800000u, 0x00400000u));
+      f32x16_t acc0 = {}, acc1 = {};
+#pragma unroll
+      for (int st = 0; st < 8; ++st) {
+        const bf16x8_t kb = fp4x8_to_bf16_pow2(st < 4 ? c0[st] : c1[st - 4], st < 4 ? s_lo : s_hi);
+        acc0 = mfma32_bf16(a0[st], kb, acc0);
+        acc1 = mfma32_bf16(a1[st], kb, acc1);
+      }
+      float pa = 0.f, pb = 0.f;
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        pa += w0[j] * relu_f32(acc0[j]);
+        pb += w1[j] * relu_f32(acc1[j]);
+      }
+      pa = lanes_sum32(pa);
+      pb = lanes_sum32(pb);
+      const int so = st_off + (int)(col_first + (int64_t)t * step) * 4;
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(pa), sra, so, 0, 0);
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(pb), srb, so, 0, 0);
+    };
+    // the single-query scan's loop shape: all tiles branch-free when the
+    // wave's last tile starts before nv, else ring-turn groups of DEPTH + 1
+    if (col_first + (int64_t)(TPW - 1) * step < nv) {
+#pragma unroll
+      for (int t = 0; t < TPW; ++t) tile(t, t % (DEPTH + 1), t + DEPTH < TPW);
+    } else {
+      constexpr int G = DEPTH + 1;
+      const int64_t rem = nv - col_first;
+      const int64_t nt64 = rem <= 0 ? 0 : (rem + step - 1) / step;
+      const int ntv = nt64 < TPW ? (int)nt64 : TPW;
+      int t0 = 0;
+      for (; t0 + G <= ntv; t0 += G) {
+#pragma unroll
+        for (int i = 0; i < G; ++i) tile(t0 + i, i, true);
+      }
+#pragma unroll
+      for (int i = 0; i + 1 < G; ++i)
+        if (t0 + i < ntv) tile(t0 + i, i, false);
+    }
+  }
+}
+
 template <bool CAND, int TPW, int DEPTH, bool LV>
 static void launch_variant(bool fp4q, dim3 grid, hipStream_t stream, const uint16_t* q_idx,
                            const float* w,
@@ -446,7 +578,26 @@ hipError_t launch_index_score(const uint16_t* q_idx, const float* w, const int32
                                          cand, ld_cand, nchunk, cs, ts, n_cols,       \
                                          ik_codes, ik_scales, cap, scores, ld, lvd, lv); \
     break;
+  // Long prefill rows with a bf16 query: two queries per wave share each
+  // key tile's conversion (same scores, bit for bit)
+  const int64_t P = ((int64_t)Q + 1) / 2;
+  constexpr int64_t pcols = (int64_t)SC_WAVES * SC_PAIR_TPW * 32;
+  const int64_t pchunk = (n_cols + pcols - 1) / pcols;
+  const bool pairs = !cand && !fp4q && !lv_scan && Q >= SC_PAIR_MIN_Q &&
+                     n_cols > SC_PAIR_MIN_COLS && P * pchunk >= 1024;
+  if (pairs) {
+    const bool pinter = pchunk >= 128 && n_cols < ((int64_t)1 << 24);
+    const int64_t pslice = (int64_t)SC_WAVES * 32;
+    hipLaunchKernelGGL((k_index_score_pair<SC_PAIR_TPW, SC_PAIR_DEPTH>),
+                       dim3((unsigned)(pchunk * P)), dim3(256), 0, stream, q_idx, w, q_seq, n_vis,
+                       Q, pchunk, pinter ? pslice : pcols,
+                       pinter ? pchunk * pslice : pslice, n_cols, ik_codes, ik_scales, cap,
+                       scores, ld);
+    tpw = 0;                                                    // launched
+  }
   switch (tpw) {
+    case 0:
+      break;
     CSA2_SCORE_CASE(32, 2)
     CSA2_SCORE_CASE(16, 2)
     CSA2_SCORE_CASE(8, 2)

@@ -388,6 +388,42 @@ def test_index_score_many_queries():
         assert np.array_equal(checks.host(part).view(np.uint32), s[lo:hi].view(np.uint32))
 
 
+def test_index_score_query_pairs():
+    """A 2049-query prefill launch over 40,000 entries (long rows: the scan
+    scores two queries per wave, sharing each key tile's conversion) against
+    the same queries in launches of 512 (one query per wave): the same score
+    bits.  Pairs across a sequence boundary, the last unpaired query, rows of
+    different lengths within a pair and empty rows included; sampled rows
+    against the oracle."""
+    B, T, Q = 2, 40000, 2049
+    _, _, _, cache = _build(B, T, 1, seed=31)
+    q, w = _scores_inputs(Q, 32)
+    q_seq = np.ones(Q, np.int32)
+    q_seq[1001] = 0                                    # pair (1000, 1001) on two sequences
+    q_seq[1500:1504] = 0                               # a run of pairs on the other one
+    n_vis = np.minimum(np.arange(Q) * 19 + 1, T).astype(np.int64)
+    n_vis[7] = 0                                       # an empty row beside a full one
+    n_vis[40] = T
+    n_vis[2048] = T - 3
+    full = torch.full((Q, T), -7.0, device=DEV)
+    C.csa2_index_score(q.to(DEV), w.to(DEV), torch.from_numpy(q_seq).to(DEV),
+                       torch.from_numpy(n_vis).to(DEV), None, T, cache, full)
+    parts = torch.full((Q, T), -7.0, device=DEV)
+    for lo in range(0, Q, 512):
+        hi = min(lo + 512, Q)
+        C.csa2_index_score(q[lo:hi].to(DEV), w[lo:hi].to(DEV), torch.from_numpy(q_seq[lo:hi]).to(DEV),
+                           torch.from_numpy(n_vis[lo:hi]).to(DEV), None, T, cache, parts[lo:hi])
+    torch.cuda.synchronize()
+    assert bool(torch.equal(full.view(torch.int32), parts.view(torch.int32)))
+    a = checks.host(full)
+    q64, w64 = checks.bf16_to_f64(q), w.double().numpy()
+    khat = [R.dequant_mxfp4(checks.host(cache.ik_codes[x]), checks.host(cache.ik_scales[x])) for x in range(B)]
+    for i in (0, 1, 6, 7, 40, 41, 1000, 1001, 1500, 1503, 2047, 2048):
+        nv = int(n_vis[i])
+        checks.check_scores(a[i, :nv], R.index_scores(q64[i], w64[i], khat[q_seq[i]][:nv]))
+        assert np.all(a[i, nv:] == -7.0)
+
+
 def test_index_score_launch_composition():
     """A 1000-query causal launch over 5000 entries and the same queries in
     launches of 125 (which pick another tile count per wave and another
