@@ -1,5 +1,5 @@
 // Steps a1-a3: m-to-1 softmax pooling, FP4 main-KV quantisation, indexer-K
-// projection and MXFP4 quantisation, one workgroup per 32 entries; and the
+// projection and MXFP4 quantisation, one workgroup per 8 entries; and the
 // decode-time append, which runs the same steps on the group a new token
 // completes.
 //
@@ -13,23 +13,27 @@
 
 namespace csa2 {
 
-constexpr int CQ_ENT = 32;          // entries per workgroup
+// entries per workgroup of the batch compressor: 8 (two per wave) keeps each
+// wave's serial pooling and quantisation short and launches enough
+// workgroups to cover the device (4,096 entries at m = 2 on MI355X: 44 us
+// with 32 per workgroup, 30 with 16, 28 with 8)
+constexpr int CQ_ENT = 8;
 constexpr int CQ_XPAD = 8;          // bf16 padding of an LDS latent row
 constexpr int CQ_KPAD = 4;          // fp32 padding of an LDS indexer-K row
 
-// Phase 1 of the compressor for a wave's 8 entries when an entry has M <= 2
+// Phase 1 of the compressor for a wave's E entries when an entry has M <= 2
 // raw rows: every row is requested first, then each entry is pooled (per
 // channel, softmax over the M rows of z weighting the rows of h; M == 1:
 // the row itself) and handed to quant(x, jl, j).  Entries past n_ent get
 // zero rows in xs and nothing stored.
-template <int M, typename HRow, typename ZRow, typename Quant>
-__device__ __forceinline__ void pool_rows_8(HRow hrow, ZRow zrow, int64_t n_ent, int64_t j0,
-                                            int wave, int lane, Quant quant,
-                                            uint16_t (*xs)[D_LAT + CQ_XPAD]) {
-  u32x4_t hv[8][M], zv[8][M];
+template <int M, int E, typename HRow, typename ZRow, typename Quant>
+__device__ __forceinline__ void pool_rows(HRow hrow, ZRow zrow, int64_t n_ent, int64_t j0,
+                                          int wave, int lane, Quant quant,
+                                          uint16_t (*xs)[D_LAT + CQ_XPAD]) {
+  u32x4_t hv[E][M], zv[E][M];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int64_t jr = j0 + wave * 8 + i;
+  for (int i = 0; i < E; ++i) {
+    const int64_t jr = j0 + wave * E + i;
     const int64_t j = jr < n_ent ? jr : n_ent - 1;
 #pragma unroll
     for (int t = 0; t < M; ++t) {
@@ -38,8 +42,8 @@ __device__ __forceinline__ void pool_rows_8(HRow hrow, ZRow zrow, int64_t n_ent,
     }
   }
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int jl = wave * 8 + i;
+  for (int i = 0; i < E; ++i) {
+    const int jl = wave * E + i;
     const int64_t j = j0 + jl;
     float x[8];
     if constexpr (M == 1) {
@@ -78,11 +82,13 @@ __device__ __forceinline__ void pool_rows_8(HRow hrow, ZRow zrow, int64_t n_ent,
   }
 }
 
-// The compressor for entries j0 .. j0 + 31 of sequence b (those below
+// The compressor for entries j0 .. j0 + ENT - 1 of sequence b (those below
 // n_ent), written at entries e0 + j.  hrow(j, t) / zrow(j, t) give raw row
-// t (< m) of entry j.  ONE_ENTRY (the decode append, one valid entry) loads
-// the whole projection operand at once instead of eight steps at a time.
-template <bool ONE_ENTRY, typename HRow, typename ZRow>
+// t (< m) of entry j.  ONE_ENTRY (the decode append, one valid entry, ENT =
+// 32) loads the whole projection operand at once instead of eight steps at
+// a time.  The batch compressor runs ENT = 8 (its projection on 16x16x32
+// MFMAs whose rows past ENT are discarded).
+template <bool ONE_ENTRY, int ENT, typename HRow, typename ZRow>
 __device__ __forceinline__ void compress_entries(HRow hrow, ZRow zrow, int m, int64_t n_ent,
                                                  int64_t j0, int b, int64_t e0,
                                                  const uint16_t* __restrict__ w_ik,
@@ -90,8 +96,11 @@ __device__ __forceinline__ void compress_entries(HRow hrow, ZRow zrow, int m, in
                                                  uint8_t* __restrict__ kv_scales,
                                                  uint8_t* __restrict__ ik_codes,
                                                  uint8_t* __restrict__ ik_scales, int64_t cap) {
-  __shared__ __align__(16) uint16_t xs[CQ_ENT][D_LAT + CQ_XPAD];   // dequantised main KV, bf16
-  __shared__ __align__(16) float ks[CQ_ENT][D_IDX + CQ_KPAD];      // projected indexer K
+  static_assert(ENT == 8 || ENT == 16 || ENT == 32, "8, 16 or 32 entries per workgroup");
+  static_assert(!ONE_ENTRY || ENT == 32, "the append path keeps 32");
+  constexpr int EPW = ENT / 4;                                     // entries per wave
+  __shared__ __align__(16) uint16_t xs[ENT][D_LAT + CQ_XPAD];     // dequantised main KV, bf16
+  __shared__ __align__(16) float ks[ENT][D_IDX + CQ_KPAD];        // projected indexer K
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   // the projection operand (wave w: output dims 32w..32w+31), for a single
   // entry loaded up front so that its latency overlaps the pooling
@@ -102,7 +111,7 @@ __device__ __forceinline__ void compress_entries(HRow hrow, ZRow zrow, int m, in
     for (int s = 0; s < D_LAT / 16; ++s) wpre[s] = *(const bf16x8_t*)(wrow + 16 * s);
   }
 
-  // ---- phase 1: pooling + main-KV quantisation; wave w owns entries 8w..8w+7,
+  // ---- phase 1: pooling + main-KV quantisation; wave w owns entries EPW w ..,
   //      lane l owns channels 8l..8l+7 (two lanes per 16-channel scale group).
   // FP4 codes and E4M3 scales of entry j (local jl) from its pooled channels
   auto quantise = [&](const float (&x)[8], int jl, int64_t j) __attribute__((always_inline)) {
@@ -132,11 +141,11 @@ __device__ __forceinline__ void compress_entries(HRow hrow, ZRow zrow, int m, in
   if (!ONE_ENTRY && (m == 1 || m == 2)) {
     // the rows of all 8 entries requested before any pooling (rows past
     // n_ent re-read the last entry; their results are not stored)
-    if (m == 1) pool_rows_8<1>(hrow, zrow, n_ent, j0, wave, lane, quantise, xs);
-    else pool_rows_8<2>(hrow, zrow, n_ent, j0, wave, lane, quantise, xs);
+    if (m == 1) pool_rows<1, EPW>(hrow, zrow, n_ent, j0, wave, lane, quantise, xs);
+    else pool_rows<2, EPW>(hrow, zrow, n_ent, j0, wave, lane, quantise, xs);
   } else {
-    for (int i = 0; i < 8; ++i) {
-      const int jl = wave * 8 + i;
+    for (int i = 0; i < EPW; ++i) {
+      const int jl = wave * EPW + i;
       const int64_t j = j0 + jl;
       if (j >= n_ent) {
         *(u32x4_t*)&xs[jl][lane * 8] = u32x4_t{0u, 0u, 0u, 0u};
@@ -183,9 +192,29 @@ __device__ __forceinline__ void compress_entries(HRow hrow, ZRow zrow, int m, in
   }
   __syncthreads();
 
-  // ---- phase 2: k[32 entries][128] = xhat[32][512] . w_ik^T with 32x32x16 bf16
-  //      MFMA; wave w computes output dims 32w..32w+31.
-  {
+  // ---- phase 2: k[ENT entries][128] = xhat[ENT][512] . w_ik^T, wave w
+  //      computing output dims 32w..32w+31: 32x32x16 bf16 MFMA for 32
+  //      entries, two 16x16x32 column blocks for 16
+  if constexpr (ENT <= 16) {
+    const int r16 = lane & 15, kq = lane >> 4;
+    const int ra = r16 < ENT ? r16 : 0;           // rows past ENT: any row, results unused
+    const uint16_t* w0 = w_ik + (int64_t)(wave * 32 + r16) * D_LAT + kq * 8;
+    const uint16_t* w1 = w0 + 16 * D_LAT;
+    f32x4_t acc0 = {}, acc1 = {};
+#pragma unroll 8
+    for (int s = 0; s < D_LAT / 32; ++s) {
+      const bf16x8_t a = *(const bf16x8_t*)&xs[ra][32 * s + kq * 8];
+      acc0 = mfma16_bf16(a, *(const bf16x8_t*)(w0 + 32 * s), acc0);
+      acc1 = mfma16_bf16(a, *(const bf16x8_t*)(w1 + 32 * s), acc1);
+    }
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      if (4 * kq + jj < ENT) {
+        ks[4 * kq + jj][wave * 32 + r16] = acc0[jj];
+        ks[4 * kq + jj][wave * 32 + 16 + r16] = acc1[jj];
+      }
+    }
+  } else {
     const int r = lane & 31, kh = lane >> 5;
     f32x16_t acc = {};
     if constexpr (ONE_ENTRY) {
@@ -205,20 +234,22 @@ __device__ __forceinline__ void compress_entries(HRow hrow, ZRow zrow, int m, in
   }
   __syncthreads();
 
-  // ---- phase 3: MXFP4, one (entry, 32-dim group) per thread pair, 16 dims each
+  // ---- phase 3: MXFP4, one (entry, 32-dim group) per TPT threads, VPT dims each
   {
+    constexpr int TPT = 256 / (ENT * 4), VPT = 32 / TPT;
     const int tid = threadIdx.x;
-    const int task = tid >> 1, sub = tid & 1;
+    const int task = tid / TPT, sub = tid % TPT;
     const int jl = task >> 2, g = task & 3;
     const int64_t j = j0 + jl;
-    float v[16];
+    float v[VPT];
     float amax = 0.f;
 #pragma unroll
-    for (int c = 0; c < 16; ++c) {
-      v[c] = ks[jl][g * 32 + sub * 16 + c];
+    for (int c = 0; c < VPT; ++c) {
+      v[c] = ks[jl][g * 32 + sub * VPT + c];
       amax = fmaxf(amax, fabsf(v[c]));
     }
-    amax = fmaxf(amax, __shfl_xor(amax, 1));
+#pragma unroll
+    for (int o = 1; o < TPT; o <<= 1) amax = fmaxf(amax, __shfl_xor(amax, o));
     int E = -127;
     if (amax > 0.f) {
       int ex;
@@ -228,13 +259,16 @@ __device__ __forceinline__ void compress_entries(HRow hrow, ZRow zrow, int m, in
     }
     uint64_t word = 0;
 #pragma unroll
-    for (int c = 0; c < 16; ++c) {
+    for (int c = 0; c < VPT; ++c) {
       const uint32_t n = amax > 0.f ? e2m1_encode(ldexpf(v[c], -E), 1.0f) : 0u;
       word |= (uint64_t)n << (4 * c);
     }
     if (j < n_ent) {
       const int64_t ent = (int64_t)b * cap + e0 + j;
-      *(uint64_t*)(ik_codes + ent * 64 + g * 16 + sub * 8) = word;
+      uint8_t* dst = ik_codes + ent * 64 + g * 16 + sub * (VPT / 2);
+      if constexpr (VPT == 16) *(uint64_t*)dst = word;
+      else if constexpr (VPT == 8) *(uint32_t*)dst = (uint32_t)word;
+      else *(uint16_t*)dst = (uint16_t)word;
       if (sub == 0) ik_scales[ent * 4 + g] = (uint8_t)(E + 127);
     }
   }
@@ -246,7 +280,7 @@ __global__ __launch_bounds__(256) void k_compress_quant(
     uint8_t* __restrict__ kv_scales, uint8_t* __restrict__ ik_codes,
     uint8_t* __restrict__ ik_scales, int64_t cap, int64_t e0) {
   const int b = blockIdx.y;
-  compress_entries<false>(
+  compress_entries<false, CQ_ENT>(
       [&](int64_t j, int t) { return h + ((int64_t)b * T + j * m + t) * D_LAT; },
       [&](int64_t j, int t) { return z + ((int64_t)b * T + j * m + t) * D_LAT; }, m, n_ent,
       (int64_t)blockIdx.x * CQ_ENT, b, e0, w_ik, kv_codes, kv_scales, ik_codes, ik_scales, cap);
@@ -346,7 +380,7 @@ __global__ __launch_bounds__(256) void k_append(
   if ((t + 1) % m == 0 && (t + 1) / m <= cap) {
     const uint16_t* th = tail_h;
     const uint16_t* tz = tail_z;
-    compress_entries<true>(
+    compress_entries<true, 32>(
         [&](int64_t, int r) {
           return r == m - 1 ? h_new + (int64_t)b * D_LAT : th + ((int64_t)b * (m - 1) + r) * D_LAT;
         },
