@@ -13,11 +13,15 @@
 
 namespace csa2 {
 
-// entries per workgroup of the batch compressor: 8 (two per wave) keeps each
-// wave's serial pooling and quantisation short and launches enough
-// workgroups to cover the device (4,096 entries at m = 2 on MI355X: 44 us
-// with 32 per workgroup, 30 with 16, 28 with 8)
-constexpr int CQ_ENT = 8;
+// Entries per workgroup of the batch compressor.  A small launch takes 8
+// (two per wave): each wave's pooling and quantisation are serial work, and
+// more workgroups cover the device (4,096 entries at m = 2 on MI355X: 44 us
+// with 32 per workgroup, 30 with 16, 28 with 8).  A launch that fills the
+// device with 32 per workgroup keeps 32: every workgroup reads the whole
+// 128 KB projection matrix, so 8 per workgroup quadruples that traffic
+// (4 x 2^20 entries at m = 1: 1.30 ms with 32, 1.95 ms with 8).
+constexpr int CQ_ENT_SMALL = 8, CQ_ENT_LARGE = 32;
+constexpr int64_t CQ_LARGE_WGS = 1024;
 constexpr int CQ_XPAD = 8;          // bf16 padding of an LDS latent row
 constexpr int CQ_KPAD = 4;          // fp32 padding of an LDS indexer-K row
 
@@ -86,8 +90,8 @@ __device__ __forceinline__ void pool_rows(HRow hrow, ZRow zrow, int64_t n_ent, i
 // n_ent), written at entries e0 + j.  hrow(j, t) / zrow(j, t) give raw row
 // t (< m) of entry j.  ONE_ENTRY (the decode append, one valid entry, ENT =
 // 32) loads the whole projection operand at once instead of eight steps at
-// a time.  The batch compressor runs ENT = 8 (its projection on 16x16x32
-// MFMAs whose rows past ENT are discarded).
+// a time.  With ENT < 32 the projection runs on 16x16x32 MFMAs whose rows
+// past ENT are discarded.
 template <bool ONE_ENTRY, int ENT, typename HRow, typename ZRow>
 __device__ __forceinline__ void compress_entries(HRow hrow, ZRow zrow, int m, int64_t n_ent,
                                                  int64_t j0, int b, int64_t e0,
@@ -274,16 +278,17 @@ __device__ __forceinline__ void compress_entries(HRow hrow, ZRow zrow, int m, in
   }
 }
 
+template <int ENT>
 __global__ __launch_bounds__(256) void k_compress_quant(
     const uint16_t* __restrict__ h, const uint16_t* __restrict__ z, int64_t T, int m,
     int64_t n_ent, const uint16_t* __restrict__ w_ik, uint8_t* __restrict__ kv_codes,
     uint8_t* __restrict__ kv_scales, uint8_t* __restrict__ ik_codes,
     uint8_t* __restrict__ ik_scales, int64_t cap, int64_t e0) {
   const int b = blockIdx.y;
-  compress_entries<false, CQ_ENT>(
+  compress_entries<false, ENT>(
       [&](int64_t j, int t) { return h + ((int64_t)b * T + j * m + t) * D_LAT; },
       [&](int64_t j, int t) { return z + ((int64_t)b * T + j * m + t) * D_LAT; }, m, n_ent,
-      (int64_t)blockIdx.x * CQ_ENT, b, e0, w_ik, kv_codes, kv_scales, ik_codes, ik_scales, cap);
+      (int64_t)blockIdx.x * ENT, b, e0, w_ik, kv_codes, kv_scales, ik_codes, ik_scales, cap);
 }
 
 hipError_t launch_compress_quant(const uint16_t* h, const uint16_t* z, int B, int64_t T, int m,
@@ -291,9 +296,16 @@ hipError_t launch_compress_quant(const uint16_t* h, const uint16_t* z, int B, in
                                  uint8_t* ik_codes, uint8_t* ik_scales, int64_t cap, int64_t e0,
                                  hipStream_t stream) {
   const int64_t n_ent = T / m;
-  const dim3 grid((unsigned)((n_ent + CQ_ENT - 1) / CQ_ENT), (unsigned)B);
-  hipLaunchKernelGGL(k_compress_quant, grid, dim3(256), 0, stream, h, z, T, m, n_ent, w_ik,
-                     kv_codes, kv_scales, ik_codes, ik_scales, cap, e0);
+  const int64_t wgs_large = (n_ent + CQ_ENT_LARGE - 1) / CQ_ENT_LARGE * B;
+  if (wgs_large >= CQ_LARGE_WGS) {
+    const dim3 grid((unsigned)((n_ent + CQ_ENT_LARGE - 1) / CQ_ENT_LARGE), (unsigned)B);
+    hipLaunchKernelGGL(k_compress_quant<CQ_ENT_LARGE>, grid, dim3(256), 0, stream, h, z, T, m,
+                       n_ent, w_ik, kv_codes, kv_scales, ik_codes, ik_scales, cap, e0);
+  } else {
+    const dim3 grid((unsigned)((n_ent + CQ_ENT_SMALL - 1) / CQ_ENT_SMALL), (unsigned)B);
+    hipLaunchKernelGGL(k_compress_quant<CQ_ENT_SMALL>, grid, dim3(256), 0, stream, h, z, T, m,
+                       n_ent, w_ik, kv_codes, kv_scales, ik_codes, ik_scales, cap, e0);
+  }
   return hipGetLastError();
 }
 
