@@ -143,7 +143,7 @@ __device__ __forceinline__ void compress_entries(HRow hrow, ZRow zrow, int m, in
     *(u32x4_t*)&xs[jl][lane * 8] = u32x4_t{xb[0], xb[1], xb[2], xb[3]};
   };
   if (!ONE_ENTRY && (m == 1 || m == 2)) {
-    // the rows of all 8 entries requested before any pooling (rows past
+    // the rows of all the wave's entries requested before any pooling (rows past
     // n_ent re-read the last entry; their results are not stored)
     if (m == 1) pool_rows<1, EPW>(hrow, zrow, n_ent, j0, wave, lane, quantise, xs);
     else pool_rows<2, EPW>(hrow, zrow, n_ent, j0, wave, lane, quantise, xs);
@@ -198,7 +198,7 @@ __device__ __forceinline__ void compress_entries(HRow hrow, ZRow zrow, int m, in
 
   // ---- phase 2: k[ENT entries][128] = xhat[ENT][512] . w_ik^T, wave w
   //      computing output dims 32w..32w+31: 32x32x16 bf16 MFMA for 32
-  //      entries, two 16x16x32 column blocks for 16
+  //      entries, two 16x16x32 column blocks for 8 or 16
   if constexpr (ENT <= 16) {
     const int r16 = lane & 15, kq = lane >> 4;
     const int ra = r16 < ENT ? r16 : 0;           // rows past ENT: any row, results unused
