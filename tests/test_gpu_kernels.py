@@ -424,6 +424,44 @@ def test_index_score_query_pairs():
         assert np.all(a[i, nv:] == -7.0)
 
 
+def test_index_score_pairs_long_interleaved():
+    """2048 queries over 524,388 columns: the two-query scan with workgroups
+    interleaving 128-column slices across the row, against the same queries
+    in launches of 512 (one query per wave, also interleaved): the same
+    score bits; ragged rows ending mid-slice; sampled columns against the
+    oracle."""
+    Q, N = 2048, (1 << 19) + 100
+    print(f"[pairs interleaved] Q={Q} N={N}", flush=True)
+    cache = _device_indexer_cache(N, 35)
+    q, w = _scores_inputs(Q, 36)
+    n_vis = (N - 37 * np.arange(Q)).astype(np.int64)
+    n_vis[5] = 0
+    q_seq = torch.zeros(Q, dtype=torch.int32, device=DEV)
+    nv_d = torch.from_numpy(n_vis).to(DEV)
+    full = torch.full((Q, N), -7.0, device=DEV)
+    C.csa2_index_score(q.to(DEV), w.to(DEV), q_seq, nv_d, None, N, cache, full)
+    parts = torch.full((Q, N), -7.0, device=DEV)
+    for lo in range(0, Q, 512):
+        C.csa2_index_score(q[lo:lo + 512].to(DEV), w[lo:lo + 512].to(DEV), q_seq[lo:lo + 512],
+                           nv_d[lo:lo + 512], None, N, cache, parts[lo:lo + 512])
+    torch.cuda.synchronize()
+    assert bool(torch.equal(full.view(torch.int32), parts.view(torch.int32)))
+    del parts
+    q64, w64 = checks.bf16_to_f64(q), w.double().numpy()
+    rng = np.random.default_rng(37)
+    for i in (0, 1, 4, 5, 1023, 2046, 2047):
+        nv = int(n_vis[i])
+        assert bool((full[i, nv:] == -7.0).all())
+        if nv == 0:
+            continue
+        cols = np.unique(np.concatenate([rng.choice(nv, 1500, replace=False), np.arange(nv - 200, nv)]))
+        idx = torch.from_numpy(cols).to(DEV)
+        got = checks.host(full[i].index_select(0, idx))
+        khat = R.dequant_mxfp4(checks.host(cache.ik_codes[0].index_select(0, idx)),
+                               checks.host(cache.ik_scales[0].index_select(0, idx)))
+        checks.check_scores(got, R.index_scores(q64[i], w64[i], khat))
+
+
 def test_index_score_launch_composition():
     """A 1000-query causal launch over 5000 entries and the same queries in
     launches of 125 (which pick another tile count per wave and another
