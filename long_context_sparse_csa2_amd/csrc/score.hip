@@ -49,15 +49,19 @@ namespace csa2 {
 
 constexpr int SC_WAVES = 4;
 // Two-query prefill scan (k_index_score_pair): used for launches of at
-// least SC_PAIR_MIN_Q queries over more than SC_PAIR_MIN_COLS columns, 32
-// tiles per wave, one tile's bytes in flight.  Measured on MI355X against
-// the one-query scan: 65,536-token prefill chunk scans 4.02 -> 3.81 ms per
-// group, 1,048,576-token 1.175 -> 1.038 s; at 4,096 columns (one chunk of
-// 4,096 queries) 76 -> 79 us, so short rows keep the one-query scan; two
-// tiles in flight or 16 tiles per wave ran 2-10 % slower.
+// least SC_PAIR_MIN_Q queries, 32 tiles per wave, one tile's bytes in
+// flight; bf16 queries over more than SC_PAIR_MIN_COLS columns, MXFP4
+// queries over any.  Measured on MI355X against the one-query scan:
+// 65,536-token prefill chunk scans 4.02 -> 3.81 ms per group (MXFP4 query
+// 2.71 -> 2.13 ms), 1,048,576-token 1.175 -> 1.038 s; at 4,096 columns (one
+// chunk of 4,096 queries) 76 -> 79 us with bf16 queries, so their short rows
+// keep the one-query scan, and 60 -> 54 us with MXFP4 queries; two tiles in
+// flight or 16 tiles per wave ran 2-10 % slower, and the MXFP4 variant
+// spills at three or four waves per SIMD.
 constexpr int SC_PAIR_MIN_Q = 2048;
 constexpr int64_t SC_PAIR_MIN_COLS = 4096;
 constexpr int SC_PAIR_TPW = 32, SC_PAIR_DEPTH = 1;
+
 // Fourth word of a raw (unformatted, stride 0) buffer resource on gfx9:
 // 32-bit data format, so a store is range-checked in bytes against the
 // resource's record count.
@@ -387,17 +391,19 @@ __global__ __launch_bounds__(256, 4) void k_index_score(
   }
 }
 
-// Two queries per wave (long prefill rows, bf16 query): the queries 2p and
-// 2p + 1 of a causal prefill chunk see (nearly) the same entries, so a wave
-// converts each 32-entry key tile to bf16 once and feeds it to the MFMAs of
-// both: half the FP4 conversions per (query, entry), which with the epilogue
-// bound the single-query scan of long rows.  Each query's accumulator sees
+// Two queries per wave (prefill rows): the queries 2p and 2p + 1 of a causal
+// prefill chunk see (nearly) the same entries, so a wave converts each
+// 32-entry key tile to bf16 once and feeds it to the MFMAs of both: half the
+// FP4 conversions per (query, entry), which with the epilogue bound the
+// single-query scan of long rows.  With MXFP4 queries (no conversion) each
+// tile's key bytes feed both queries' scaled FP4 MFMAs: half the loads per
+// (query, entry) and twice the MFMA work between the waits for them.  Each query's accumulator sees
 // the same operands in the same order as in the single-query scan, so the
 // scores are the same bits.  Loads run to the longer of the two rows, each
 // query's stores stop at its own.  A pair on two sequences (or the last,
 // unpaired query) is scored one query at a time, the wave then scoring that
 // query for both of its slots (the same value stored twice).
-template <int TPW, int DEPTH>
+template <int TPW, int DEPTH, bool FP4Q>
 __global__ __launch_bounds__(256, 2) void k_index_score_pair(
     const uint16_t* __restrict__ q_idx, const float* __restrict__ w,
     const int32_t* __restrict__ q_seq, const int64_t* __restrict__ n_vis, int Q, int64_t nchunk,
@@ -423,15 +429,35 @@ __global__ __launch_bounds__(256, 2) void k_index_score_pair(
     const int64_t nv = nva > nvb ? nva : nvb;
     if (cbase >= nv) continue;                            // uniform
     const int64_t seq_base = (int64_t)q_seq[qa] * cap;
-    bf16x8_t a0[8], a1[8];
+    bf16x8_t a0[FP4Q ? 1 : 8], a1[FP4Q ? 1 : 8];
+    i32x8_t qa0[2] = {}, qa1[2] = {};           // MXFP4: the two queries' codes
+    uint32_t qsc0 = 0, qsc1 = 0;
     float w0[16], w1[16];
     {
-      const uint16_t* pa = q_idx + ((int64_t)qa * H_IDX + r) * D_IDX + half * 64;
-      const uint16_t* pb = q_idx + ((int64_t)qb * H_IDX + r) * D_IDX + half * 64;
+      if constexpr (FP4Q) {
+        __shared__ QFp4Lds ql[2];
+        quant_query_fp4(q_idx + (int64_t)qa * H_IDX * D_IDX, ql[0]);
+        quant_query_fp4(q_idx + (int64_t)qb * H_IDX * D_IDX, ql[1]);
+        __syncthreads();
 #pragma unroll
-      for (int s = 0; s < 8; ++s) {
-        a0[s] = *(const bf16x8_t*)(pa + 8 * s);
-        a1[s] = *(const bf16x8_t*)(pb + 8 * s);
+        for (int i = 0; i < 2; ++i) {
+          const u32x4_t* cp = (const u32x4_t*)&ql[i].codes[r][32 * half];
+          const u32x4_t c0 = cp[0], c1 = cp[1];
+          i32x8_t* dst = i == 0 ? qa0 : qa1;
+          dst[0] = i32x8_t{(int)c0[0], (int)c0[1], (int)c0[2], (int)c0[3], 0, 0, 0, 0};
+          dst[1] = i32x8_t{(int)c1[0], (int)c1[1], (int)c1[2], (int)c1[3], 0, 0, 0, 0};
+        }
+        qsc0 = ql[0].scales[r] >> (16 * half);
+        qsc1 = ql[1].scales[r] >> (16 * half);
+        __syncthreads();                    // read before a second pass rewrites them
+      } else {
+        const uint16_t* pa = q_idx + ((int64_t)qa * H_IDX + r) * D_IDX + half * 64;
+        const uint16_t* pb = q_idx + ((int64_t)qb * H_IDX + r) * D_IDX + half * 64;
+#pragma unroll
+        for (int s = 0; s < 8; ++s) {
+          a0[s] = *(const bf16x8_t*)(pa + 8 * s);
+          a1[s] = *(const bf16x8_t*)(pb + 8 * s);
+        }
       }
 #pragma unroll
       for (int j = 0; j < 16; ++j) {
@@ -466,14 +492,27 @@ __global__ __launch_bounds__(256, 2) void k_index_score_pair(
       __builtin_amdgcn_sched_barrier(0);
       const u32x4_t c0 = r0[sl], c1 = r1[sl];
       const uint32_t scw = rs[sl];
-      const float s_lo = __uint_as_float(max((scw << 23) & 0x7F800000u, 0x00400000u));
-      const float s_hi = __uint_as_float(max((scw << 15) & 0x7F800000u, 0x00400000u));
       f32x16_t acc0 = {}, acc1 = {};
+      if constexpr (FP4Q) {                 // the single scan's two scaled FP4 MFMAs per query
+        const i32x8_t b0 = {(int)c0[0], (int)c0[1], (int)c0[2], (int)c0[3], 0, 0, 0, 0};
+        const i32x8_t b1 = {(int)c1[0], (int)c1[1], (int)c1[2], (int)c1[3], 0, 0, 0, 0};
+        acc0 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(qa0[0], b0, acc0, 4, 4, 0, (int)qsc0,
+                                                               0, (int)scw);
+        acc1 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(qa1[0], b0, acc1, 4, 4, 0, (int)qsc1,
+                                                               0, (int)scw);
+        acc0 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(qa0[1], b1, acc0, 4, 4, 1, (int)qsc0,
+                                                               1, (int)scw);
+        acc1 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(qa1[1], b1, acc1, 4, 4, 1, (int)qsc1,
+                                                               1, (int)scw);
+      } else {
+        const float s_lo = __uint_as_float(max((scw << 23) & 0x7F800000u, 0x00400000u));
+        const float s_hi = __uint_as_float(max((scw << 15) & 0x7F800000u, 0x00400000u));
 #pragma unroll
-      for (int st = 0; st < 8; ++st) {
-        const bf16x8_t kb = fp4x8_to_bf16_pow2(st < 4 ? c0[st] : c1[st - 4], st < 4 ? s_lo : s_hi);
-        acc0 = mfma32_bf16(a0[st], kb, acc0);
-        acc1 = mfma32_bf16(a1[st], kb, acc1);
+        for (int st = 0; st < 8; ++st) {
+          const bf16x8_t kb = fp4x8_to_bf16_pow2(st < 4 ? c0[st] : c1[st - 4], st < 4 ? s_lo : s_hi);
+          acc0 = mfma32_bf16(a0[st], kb, acc0);
+          acc1 = mfma32_bf16(a1[st], kb, acc1);
+        }
       }
       float pa = 0.f, pb = 0.f;
 #pragma unroll
@@ -583,16 +622,23 @@ hipError_t launch_index_score(const uint16_t* q_idx, const float* w, const int32
   const int64_t P = ((int64_t)Q + 1) / 2;
   constexpr int64_t pcols = (int64_t)SC_WAVES * SC_PAIR_TPW * 32;
   const int64_t pchunk = (n_cols + pcols - 1) / pcols;
-  const bool pairs = !cand && !fp4q && !lv_scan && Q >= SC_PAIR_MIN_Q &&
-                     n_cols > SC_PAIR_MIN_COLS && P * pchunk >= 1024;
+  const bool pairs = !cand && !lv_scan && Q >= SC_PAIR_MIN_Q &&
+                     n_cols > (fp4q ? 0 : SC_PAIR_MIN_COLS) && P * pchunk >= 1024;
   if (pairs) {
     const bool pinter = pchunk >= 128 && n_cols < ((int64_t)1 << 24);
     const int64_t pslice = (int64_t)SC_WAVES * 32;
-    hipLaunchKernelGGL((k_index_score_pair<SC_PAIR_TPW, SC_PAIR_DEPTH>),
-                       dim3((unsigned)(pchunk * P)), dim3(256), 0, stream, q_idx, w, q_seq, n_vis,
-                       Q, pchunk, pinter ? pslice : pcols,
-                       pinter ? pchunk * pslice : pslice, n_cols, ik_codes, ik_scales, cap,
-                       scores, ld);
+    if (fp4q)
+      hipLaunchKernelGGL((k_index_score_pair<SC_PAIR_TPW, SC_PAIR_DEPTH, true>),
+                         dim3((unsigned)(pchunk * P)), dim3(256), 0, stream, q_idx, w, q_seq,
+                         n_vis, Q, pchunk, pinter ? pslice : pcols,
+                         pinter ? pchunk * pslice : pslice, n_cols, ik_codes, ik_scales, cap,
+                         scores, ld);
+    else
+      hipLaunchKernelGGL((k_index_score_pair<SC_PAIR_TPW, SC_PAIR_DEPTH, false>),
+                         dim3((unsigned)(pchunk * P)), dim3(256), 0, stream, q_idx, w, q_seq,
+                         n_vis, Q, pchunk, pinter ? pslice : pcols,
+                         pinter ? pchunk * pslice : pslice, n_cols, ik_codes, ik_scales, cap,
+                         scores, ld);
     tpw = 0;                                                    // launched
   }
   switch (tpw) {

@@ -388,9 +388,10 @@ def test_index_score_many_queries():
         assert np.array_equal(checks.host(part).view(np.uint32), s[lo:hi].view(np.uint32))
 
 
-def test_index_score_query_pairs():
-    """A 2049-query prefill launch over 40,000 entries (long rows: the scan
-    scores two queries per wave, sharing each key tile's conversion) against
+@pytest.mark.parametrize("fp4q", [False, True])
+def test_index_score_query_pairs(fp4q):
+    """A 2049-query prefill launch over 40,000 entries (the scan scores two
+    queries per wave, sharing each key tile's conversion or loads) against
     the same queries in launches of 512 (one query per wave): the same score
     bits.  Pairs across a sequence boundary, the last unpaired query, rows of
     different lengths within a pair and empty rows included; sampled rows
@@ -407,12 +408,13 @@ def test_index_score_query_pairs():
     n_vis[2048] = T - 3
     full = torch.full((Q, T), -7.0, device=DEV)
     C.csa2_index_score(q.to(DEV), w.to(DEV), torch.from_numpy(q_seq).to(DEV),
-                       torch.from_numpy(n_vis).to(DEV), None, T, cache, full)
+                       torch.from_numpy(n_vis).to(DEV), None, T, cache, full, fp4q=fp4q)
     parts = torch.full((Q, T), -7.0, device=DEV)
     for lo in range(0, Q, 512):
         hi = min(lo + 512, Q)
         C.csa2_index_score(q[lo:hi].to(DEV), w[lo:hi].to(DEV), torch.from_numpy(q_seq[lo:hi]).to(DEV),
-                           torch.from_numpy(n_vis[lo:hi]).to(DEV), None, T, cache, parts[lo:hi])
+                           torch.from_numpy(n_vis[lo:hi]).to(DEV), None, T, cache, parts[lo:hi],
+                           fp4q=fp4q)
     torch.cuda.synchronize()
     assert bool(torch.equal(full.view(torch.int32), parts.view(torch.int32)))
     a = checks.host(full)
@@ -420,18 +422,21 @@ def test_index_score_query_pairs():
     khat = [R.dequant_mxfp4(checks.host(cache.ik_codes[x]), checks.host(cache.ik_scales[x])) for x in range(B)]
     for i in (0, 1, 6, 7, 40, 41, 1000, 1001, 1500, 1503, 2047, 2048):
         nv = int(n_vis[i])
-        checks.check_scores(a[i, :nv], R.index_scores(q64[i], w64[i], khat[q_seq[i]][:nv]))
+        k = khat[q_seq[i]][:nv]
+        ref = _oracle_scores_fp4q(q64[i], w64[i], k) if fp4q else R.index_scores(q64[i], w64[i], k)
+        checks.check_scores(a[i, :nv], ref)
         assert np.all(a[i, nv:] == -7.0)
 
 
-def test_index_score_pairs_long_interleaved():
+@pytest.mark.parametrize("fp4q", [False, True])
+def test_index_score_pairs_long_interleaved(fp4q):
     """2048 queries over 524,388 columns: the two-query scan with workgroups
     interleaving 128-column slices across the row, against the same queries
     in launches of 512 (one query per wave, also interleaved): the same
     score bits; ragged rows ending mid-slice; sampled columns against the
     oracle."""
     Q, N = 2048, (1 << 19) + 100
-    print(f"[pairs interleaved] Q={Q} N={N}", flush=True)
+    print(f"[pairs interleaved] Q={Q} N={N} fp4q={fp4q}", flush=True)
     cache = _device_indexer_cache(N, 35)
     q, w = _scores_inputs(Q, 36)
     n_vis = (N - 37 * np.arange(Q)).astype(np.int64)
@@ -439,11 +444,11 @@ def test_index_score_pairs_long_interleaved():
     q_seq = torch.zeros(Q, dtype=torch.int32, device=DEV)
     nv_d = torch.from_numpy(n_vis).to(DEV)
     full = torch.full((Q, N), -7.0, device=DEV)
-    C.csa2_index_score(q.to(DEV), w.to(DEV), q_seq, nv_d, None, N, cache, full)
+    C.csa2_index_score(q.to(DEV), w.to(DEV), q_seq, nv_d, None, N, cache, full, fp4q=fp4q)
     parts = torch.full((Q, N), -7.0, device=DEV)
     for lo in range(0, Q, 512):
         C.csa2_index_score(q[lo:lo + 512].to(DEV), w[lo:lo + 512].to(DEV), q_seq[lo:lo + 512],
-                           nv_d[lo:lo + 512], None, N, cache, parts[lo:lo + 512])
+                           nv_d[lo:lo + 512], None, N, cache, parts[lo:lo + 512], fp4q=fp4q)
     torch.cuda.synchronize()
     assert bool(torch.equal(full.view(torch.int32), parts.view(torch.int32)))
     del parts
@@ -459,7 +464,8 @@ def test_index_score_pairs_long_interleaved():
         got = checks.host(full[i].index_select(0, idx))
         khat = R.dequant_mxfp4(checks.host(cache.ik_codes[0].index_select(0, idx)),
                                checks.host(cache.ik_scales[0].index_select(0, idx)))
-        checks.check_scores(got, R.index_scores(q64[i], w64[i], khat))
+        ref = _oracle_scores_fp4q(q64[i], w64[i], khat) if fp4q else R.index_scores(q64[i], w64[i], khat)
+        checks.check_scores(got, ref)
 
 
 def test_index_score_launch_composition():
