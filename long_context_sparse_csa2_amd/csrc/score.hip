@@ -114,12 +114,21 @@ __device__ __forceinline__ void quant_query_fp4(const uint16_t* __restrict__ qro
     E = ex - 1 - 2;                                   // minus emax of E2M1
     E = E < -127 ? -127 : (E > 127 ? 127 : E);
   }
+  // E2M1(v / 2^E), round to nearest even, saturating: the gfx950 scaled
+  // conversion, two values per instruction into byte sel of the word (it
+  // reads only the exponent field of its scale operand, so 2^-127 is passed
+  // as the subnormal with that field 0; checked against the software rule
+  // on ties, saturation and the extreme scales)
+  const float sc = __uint_as_float(E == -127 ? 0x00400000u : (uint32_t)(E + 127) << 23);
   uint32_t lo = 0, hi = 0;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    lo |= e2m1_encode(ldexpf(v[i], -E), 1.0f) << (4 * i);
-    hi |= e2m1_encode(ldexpf(v[8 + i], -E), 1.0f) << (4 * i);
-  }
+  lo = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(lo, v[0], v[1], sc, 0);
+  lo = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(lo, v[2], v[3], sc, 1);
+  lo = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(lo, v[4], v[5], sc, 2);
+  lo = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(lo, v[6], v[7], sc, 3);
+  hi = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(hi, v[8], v[9], sc, 0);
+  hi = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(hi, v[10], v[11], sc, 1);
+  hi = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(hi, v[12], v[13], sc, 2);
+  hi = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(hi, v[14], v[15], sc, 3);
   *(uint2*)&ql.codes[head][16 * g + 8 * sub] = make_uint2(lo, hi);
   if (sub == 0) ((uint8_t*)&ql.scales[head])[g] = (uint8_t)(E + 127);
 }
