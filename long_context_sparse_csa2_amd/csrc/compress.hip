@@ -261,12 +261,24 @@ __device__ __forceinline__ void compress_entries(HRow hrow, ZRow zrow, int m, in
       E = ex - 1 - 2;                 // minus emax of E2M1
       E = E < -127 ? -127 : (E > 127 ? 127 : E);
     }
-    uint64_t word = 0;
+    // E2M1(v / 2^E), round to nearest even, saturating, by the gfx950 scaled
+    // conversion (two values into byte sel of a word; it reads only the
+    // exponent field of its scale, so 2^-127 goes in as the subnormal with
+    // that field 0); an all-zero group stores +0 codes
+    const float sc = __uint_as_float(E == -127 ? 0x00400000u : (uint32_t)(E + 127) << 23);
+    uint32_t wd[2] = {0u, 0u};
 #pragma unroll
-    for (int c = 0; c < VPT; ++c) {
-      const uint32_t n = amax > 0.f ? e2m1_encode(ldexpf(v[c], -E), 1.0f) : 0u;
-      word |= (uint64_t)n << (4 * c);
+    for (int c = 0; c < VPT; c += 8) {
+      uint32_t x = 0u;
+      x = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(x, v[c], v[c + 1], sc, 0);
+      x = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(x, v[c + 2 < VPT ? c + 2 : c], v[c + 3 < VPT ? c + 3 : c + 1], sc, 1);
+      if constexpr (VPT >= 8) {
+        x = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(x, v[c + 4 < VPT ? c + 4 : c], v[c + 5 < VPT ? c + 5 : c], sc, 2);
+        x = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(x, v[c + 6 < VPT ? c + 6 : c], v[c + 7 < VPT ? c + 7 : c], sc, 3);
+      }
+      wd[c / 8] = amax > 0.f ? x : 0u;
     }
+    const uint64_t word = (uint64_t)wd[0] | ((uint64_t)wd[1] << 32);
     if (j < n_ent) {
       const int64_t ent = (int64_t)b * cap + e0 + j;
       uint8_t* dst = ik_codes + ent * 64 + g * 16 + sub * (VPT / 2);
