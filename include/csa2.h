@@ -485,8 +485,9 @@ size_t csa2_workspace_bytes(int op, int Q, int64_t n_cols, int k);
 
 /*
  * Device self-test of the hardware conversion and matrix instructions the
- * kernels rely on (FP4 -> bf16/fp16 scaled conversion, MFMA operand
- * layouts), against plain integer/bit code on the same device.  Writes
+ * kernels rely on (FP4 -> bf16/fp16 and fp32 -> FP4 scaled conversions,
+ * FP8 decoding, MFMA operand layouts, wave scans), against plain
+ * integer/bit code on the same device.  Writes
  * `n` int32 failure counters to `counts` (device); all zero means pass.
  * Returns the number of counters it writes when counts is NULL.
  */

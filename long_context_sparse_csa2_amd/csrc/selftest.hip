@@ -8,13 +8,16 @@
 //   5  FP4 -> fp16 times each E4M3 scale (packed fp16 multiply)
 //   6  DPP wave scan / max / min against a lane loop
 //   7  E4M3FN -> bf16 / fp16 (times scales) for all 256 codes but NaN
+//   8  fp32 -> E2M1 with a power-of-two scale (the MXFP4 quantisation of
+//      the indexer K and query): round to nearest even, saturating at 6,
+//      against the compare-based encoder, ties and the extreme scales
 // Each counter holds the number of mismatching values (0 = pass).
 #include "common.h"
 #include "launch.h"
 
 namespace csa2 {
 
-constexpr int ST_COUNT = 8;
+constexpr int ST_COUNT = 9;
 
 __device__ __forceinline__ int st_a(int m, int k) { return ((m * 7 + k * 3) % 9) - 4; }
 __device__ __forceinline__ int st_b(int k, int n) { return ((k * 5 + n * 11) % 7) - 3; }
@@ -86,6 +89,24 @@ __global__ __launch_bounds__(64) void k_selftest(int32_t* counts) {
   atomicAdd(&counts[0], bad_pow2);
   atomicAdd(&counts[1], bad_bf);
   atomicAdd(&counts[5], bad_f16);
+
+  {  // fp32 -> E2M1 scaled: magnitudes v / 32 (0 .. 7.97, every tie) times 2^e
+    const int exps[7] = {-127, -126, -20, -3, 0, 20, 125};   // the range the MX rule produces
+    int bad4 = 0;
+    for (int ei = 0; ei < 7; ++ei) {
+      const int e = exps[ei];
+      const float s = e == -127 ? __uint_as_float(0x00400000u) : __uint_as_float((uint32_t)(e + 127) << 23);
+      for (int v = 1; v < 256; ++v) {
+        const int u = ((v ^ l) & 255) | 1;           // nonzero: -0 and +0 codes need no care
+        const float x0 = (l & 1 ? -1.f : 1.f) * ((float)v / 32.f) * s;
+        const float x1 = (l & 2 ? -1.f : 1.f) * ((float)u / 32.f) * s;
+        const uint32_t w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, x0, x1, s, 1);
+        const uint32_t want = (e2m1_encode(x0, s) | (e2m1_encode(x1, s) << 4)) << 8;
+        bad4 += w != want;
+      }
+    }
+    atomicAdd(&counts[8], bad4);
+  }
 
   {  // 32x32x16 bf16
     bf16x8_t a, b;

@@ -206,7 +206,7 @@ def test_workspace_sizes():
 
 
 def test_selftest_counter_query():
-    assert C.lib().csa2_selftest(None, 0, None) == 8
+    assert C.lib().csa2_selftest(None, 0, None) == 9
 
 
 def test_alignment_validation():

@@ -37,7 +37,7 @@ def _build(B, T, m, seed):
 
 
 def test_selftest():
-    assert C.csa2_selftest(DEV) == [0] * 8
+    assert C.csa2_selftest(DEV) == [0] * 9
 
 
 @pytest.mark.parametrize("m,T", [(1, 1000), (2, 2000), (4, 4 * 77)])
