@@ -777,6 +777,54 @@ def test_sparse_attend_rope(Q, dims, split):
                                     lse_scale=True)
 
 
+def test_sparse_attend_wide_trailing_empty_chunks():
+    """The one-workgroup-per-query kernel on rows whose selected ids stop
+    early (a causal query that sees fewer than k entries: -1 after its last
+    id, also -1 inside): against the oracle, and bit for bit the same when
+    the id rows are padded with 512 more -1 columns."""
+    B, N, Q, k = 2, 1500, 272, 512
+    _, _, _, cache = _build(B, N, 1, seed=83)
+    rng = np.random.default_rng(83)
+    g = torch.Generator().manual_seed(83)
+    q = (torch.randn(Q, 64, 512, generator=g) / math.sqrt(512)).to(torch.bfloat16)
+    q_seq = rng.integers(0, B, Q).astype(np.int32)
+    idx = np.full((Q, k), -1, dtype=np.int32)
+    counts = [0, 1, 2, 63, 64, 65, 127, 128, 129, 200, 448, 449, 511, 512]
+    nv = np.array([counts[i % len(counts)] for i in range(Q)])
+    for i in range(Q):
+        idx[i, :nv[i]] = np.sort(rng.choice(N, nv[i], replace=False))
+        if nv[i] > 100 and i % 3 == 0:
+            idx[i, 5:70] = -1                       # a whole empty chunk before the last ids
+    T_swa = 200
+    swa_c, swa_s = _swa(B, T_swa, 13)
+    start = rng.integers(0, T_swa, Q).astype(np.int64)
+    slen = rng.integers(0, 129, Q).astype(np.int32)
+    slen[::5] = 0                                   # some queries without a window
+    args = (q.to(DEV), torch.from_numpy(q_seq).to(DEV), cache)
+    swa = (swa_c.to(DEV), swa_s.to(DEV), torch.from_numpy(start).to(DEV), torch.from_numpy(slen).to(DEV))
+    out = torch.empty(Q, 64, 512, device=DEV)
+    lse = torch.empty(Q, 64, device=DEV)
+    C.csa2_sparse_attend(*args, torch.from_numpy(idx).to(DEV), *swa, out, lse, None)
+    wide = np.concatenate([idx, np.full((Q, 512), -1, dtype=np.int32)], axis=1)
+    out2 = torch.empty_like(out)
+    lse2 = torch.empty_like(lse)
+    C.csa2_sparse_attend(*args, torch.from_numpy(wide).to(DEV), *swa, out2, lse2, None)
+    torch.cuda.synchronize()
+    assert torch.equal(out, out2) and torch.equal(lse, lse2)
+    o, l = checks.host(out), checks.host(lse)
+    q64 = checks.bf16_to_f64(q)
+    kv_c, kv_s = checks.host(cache.kv_codes), checks.host(cache.kv_scales)
+    sc_np, ss_np = swa_c.numpy(), swa_s.double().numpy()
+    for i in sorted(set(range(2 * len(counts))) | {Q - 1}):
+        b = q_seq[i]
+        wc, ws_ = checks.swa_rows(sc_np[b], ss_np[b], int(start[i]), int(slen[i]))
+        rows = R.gather_rows(kv_c[b], kv_s[b], idx[i], wc, ws_)
+        if len(rows) == 0:
+            assert np.all(o[i] == 0) and np.all(np.isneginf(l[i]))
+            continue
+        checks.check_attention(o[i], l[i], q64[i], rows, lse_scale=True)
+
+
 @pytest.mark.parametrize("Q", [1, 256])
 def test_sparse_attend_no_rows(Q):
     _, _, _, cache = _build(1, 64, 1, seed=2)
