@@ -825,6 +825,57 @@ def test_sparse_attend_wide_trailing_empty_chunks():
         checks.check_attention(o[i], l[i], q64[i], rows, lse_scale=True)
 
 
+@pytest.mark.parametrize("Q,split", [(2, True), (2, False), (260, False)])
+def test_sparse_attend_rising_scores(Q, split):
+    """Logits up to a few hundred that grow chunk after chunk (rows ordered
+    by their score along the query's direction), so the running softmax
+    maximum moves past its slack many times and every rescale path of the
+    online softmax runs; heads of odd index see the reverse order (their
+    maximum comes first).  Decode kernel with and without its split merge,
+    and the one-workgroup-per-query kernel, against the oracle."""
+    B, N, k = 1, 1500, 512
+    _, _, _, cache = _build(B, N, 1, seed=91)
+    rng = np.random.default_rng(91 + Q)
+    kv_c, kv_s = checks.host(cache.kv_codes), checks.host(cache.kv_scales)
+    K = R.dequant_main_kv(kv_c[0], kv_s[0])                       # [N, 512] fp64
+    e_u = int(rng.integers(0, N))
+    u = K[e_u]                                                       # the queries' direction
+    r = K @ u
+    order = np.argsort(r, kind="stable")
+    order = order[order != e_u]                                      # the other rows, by r
+    r_sd = np.std(r[order])
+    idx = np.empty((Q, k), dtype=np.int32)
+    q = np.empty((Q, 64, 512))
+    sign = np.where(np.arange(64) % 2 == 0, 1.0, -1.0)
+    for i in range(Q):
+        sel = np.sort(rng.choice(len(order), k, replace=False))      # ranks, ascending
+        idx[i] = order[sel]                                          # rows by rising score
+        amp = rng.uniform(100.0, 400.0, 64) * sign / (4.0 * r_sd)   # logits over about +-amp
+        q[i] = amp[:, None] * u[None, :]
+    qb = torch.from_numpy(q).to(torch.bfloat16)
+    T_swa = 200
+    swa_c, swa_s = _swa(B, T_swa, 17)
+    start = rng.integers(0, T_swa, Q).astype(np.int64)
+    slen = rng.integers(0, 129, Q).astype(np.int32)
+    q_seq = np.zeros(Q, dtype=np.int32)
+    out = torch.empty(Q, 64, 512, device=DEV)
+    lse = torch.empty(Q, 64, device=DEV)
+    ws = C.workspace(C.CSA2_OP_ATTEND, Q, 0, k, DEV) if split else None
+    C.csa2_sparse_attend(qb.to(DEV), torch.from_numpy(q_seq).to(DEV), cache,
+                         torch.from_numpy(idx).to(DEV), swa_c.to(DEV), swa_s.to(DEV),
+                         torch.from_numpy(start).to(DEV), torch.from_numpy(slen).to(DEV), out, lse, ws)
+    torch.cuda.synchronize()
+    o, l = checks.host(out), checks.host(lse)
+    q64 = checks.bf16_to_f64(qb)
+    sc_np, ss_np = swa_c.numpy(), swa_s.double().numpy()
+    for i in sorted(set(range(min(Q, 6))) | {Q - 1}):
+        wc, ws_ = checks.swa_rows(sc_np[0], ss_np[0], int(start[i]), int(slen[i]))
+        rows = R.gather_rows(kv_c[0], kv_s[0], idx[i], wc, ws_)
+        lg = q64[i] @ rows.T
+        assert np.abs(lg).max() > 50.0                              # the test's premise
+        checks.check_attention(o[i], l[i], q64[i], rows, lse_scale=True)
+
+
 @pytest.mark.parametrize("Q", [1, 256])
 def test_sparse_attend_no_rows(Q):
     _, _, _, cache = _build(1, 64, 1, seed=2)
