@@ -100,8 +100,12 @@ static inline unsigned unit_grid(int units) { return (unsigned)((units + 7) / 8 
 // chunks; id_of(r) is the selected entry of main row r (r < k); id0 that of
 // this thread's row of the first chunk (when it is a main chunk), requested
 // by the caller before the query rows x and the scalars aq.  Writes the
-// final output when nsplit == 1, else the partial (max, sum, O) state.
-template <typename IdOf>
+// final output when nsplit == 1, else the partial (max, sum, O) state; NT:
+// through nontemporal stores (the merge kernel reads them from another
+// XCD, so keeping them in this XCD's L2 gains nothing: measured on MI355X,
+// the 8-sequence decode step with five Reuse layers 2.4 % faster; the fused
+// selection kernel measured no faster with them and keeps plain stores).
+template <bool NT = false, typename IdOf>
 __device__ __forceinline__ void attend_body(
     int q, int hg, int sp, int nsplit, int cps, IdOf id_of, int id0, const bf16x8_t (&x)[4],
     const AttendQuery& aq, const uint8_t* __restrict__ kv_codes,
@@ -340,10 +344,18 @@ __device__ __forceinline__ void attend_body(
     const int64_t slot = ((int64_t)q * nsplit + sp) * H_ATT + head0 + j;
     float* op = part_o + slot * D_LAT + wave * 128 + r16;
 #pragma unroll
-    for (int t = 0; t < 8; ++t) op[16 * t] = o[t][j];
+    for (int t = 0; t < 8; ++t) {
+      if constexpr (NT) __builtin_nontemporal_store(o[t][j], op + 16 * t);
+      else op[16 * t] = o[t][j];
+    }
     if (wave == 0 && r16 == 0) {
-      part_ml[2 * slot] = m_run[j];
-      part_ml[2 * slot + 1] = l_run[j];
+      if constexpr (NT) {
+        __builtin_nontemporal_store(m_run[j], part_ml + 2 * slot);
+        __builtin_nontemporal_store(l_run[j], part_ml + 2 * slot + 1);
+      } else {
+        part_ml[2 * slot] = m_run[j];
+        part_ml[2 * slot + 1] = l_run[j];
+      }
     }
   }
 }
@@ -376,7 +388,7 @@ __global__ __launch_bounds__(256, 1) void k_attend(
   bf16x8_t x[4];
   attend_query_rows(x, qv, q, hg);
   const AttendQuery aq = attend_query(q, q_seq, swa_start, swa_len, T_swa);
-  attend_body(q, hg, sp, nsplit, cps, [&](int r) __attribute__((always_inline)) { return irow[r]; },
+  attend_body<true>(q, hg, sp, nsplit, cps, [&](int r) __attribute__((always_inline)) { return irow[r]; },
               id0, x, aq, kv_codes, kv_scales, cap, k, swa_codes, swa_scale, T_swa, out, lse,
               part_o, part_ml, rp, L, kv1);
 }
