@@ -66,10 +66,12 @@ constexpr int SC_PAIR_TPW = 32, SC_PAIR_DEPTH = 1;
 // 32-bit data format, so a store is range-checked in bytes against the
 // resource's record count.
 constexpr int SC_RSRC_WORD3 = 0x00020000;
-// Cache policy of the score and level stores: nontemporal.  The selection
-// reads them in the next kernel, mostly from other XCDs, so they gain
-// nothing from staying in this XCD's L2 (measured on MI355X: the 4 x 2^20
-// decode scan 60-64 -> 55-56 us, 58 -> 51 us after a read sweep).
+// Cache policy of the score stores: nontemporal.  The selection reads a
+// small part of them in the next kernel, mostly from other XCDs, so they
+// gain nothing from staying in this XCD's L2 (measured on MI355X: the
+// 4 x 2^20 decode scan 60-64 -> 55-56 us, 58 -> 51 us after a read sweep).
+// The maxima levels, which the selection reads whole and first, keep the
+// default policy (nontemporal there made the decode step 1 % slower).
 constexpr int SC_ST_NT = 2;
 
 // A raw buffer resource over `bytes` bytes at p (both uniform, so the
@@ -289,7 +291,7 @@ __global__ __launch_bounds__(256, 4) void k_index_score(
       v = m2;
       o = (colA >> 6) < G2 ? (b2 + (colA >> 6)) * 4 : (int)0x80000000;
     }
-    __builtin_amdgcn_raw_buffer_store_b32(v, lrs, o, 0, SC_ST_NT);
+    __builtin_amdgcn_raw_buffer_store_b32(v, lrs, o, 0, 0);       // cached: read first
   };
   // tile t from ring slot sl (= t mod (DEPTH + 1), a constant wherever this
   // is called); pf: first request tile t + DEPTH into its slot (a column
