@@ -163,9 +163,6 @@ __device__ __forceinline__ void attend_body(
     }
     return off;
   };
-  auto row_of = [&](int ch, float& sg) __attribute__((always_inline)) {
-    return row_res(ch, row_req(ch), sg);
-  };
   // a readable row of chunk ch in place of a missing one
   auto readable = [&](int64_t off, bool main_ch) __attribute__((always_inline)) {
     return off >= 0 ? off : (main_ch ? seq * cap : seq * T_swa + sst);
@@ -229,16 +226,24 @@ __device__ __forceinline__ void attend_body(
 
   for (int ch = ch_beg; ch < ch_end; ++ch) {
     const bool is_main = ch < nmc;                 // uniform over the workgroup
-    // ---- stage: thread t takes row t & 63, quarter t >> 6
+    // ---- stage: thread t takes row t & 63, quarter t >> 6.  The chunk's
+    // raw bytes (row noff, scale nsg) are in flight in `raw`; once they are
+    // in LDS the next chunk's row id and then its bytes are requested into
+    // the same registers, so they arrive during this chunk's MFMAs.
     {
-      float sg = nsg;
-      const int64_t off = ch == ch_beg ? noff : row_of(ch, sg);
-      const bool valid = off >= 0;
-      if (ch != ch_beg)
-        load_share<256>(raw, is_main, readable(off, is_main), tid >> 6, kv_codes, kv_scales,
-                        swa_codes);
+      const bool more = ch + 1 < ch_end;          // uniform
+      RowReq rqn{-1, 1.f};
+      if (more) rqn = row_req(ch + 1);
+      const int64_t off = noff;
+      const float sg = nsg;
       if (tid < CH_ROWS) { rowoff[tid] = off; rowsig[tid] = sg; }
-      store_share<256>(raw, is_main, valid, sg, kv0, kv1, tid & 63, tid >> 6);
+      store_share<256>(raw, is_main, off >= 0, sg, kv0, kv1, tid & 63, tid >> 6);
+      if (more) {
+        const bool nmain = ch + 1 < nmc;
+        noff = row_res(ch + 1, rqn, nsg);
+        load_share<256>(raw, nmain, readable(noff, nmain), tid >> 6, kv_codes, kv_scales,
+                        swa_codes);
+      }
     }
     __syncthreads();
     if (ch == ch_beg) {
