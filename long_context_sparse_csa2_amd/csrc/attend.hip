@@ -400,9 +400,10 @@ __global__ __launch_bounds__(256, 1) void k_attend(
 
 // Merge the per-split partial states of one (query, head) by log-sum-exp.
 // Every split wrote its state (an empty split: max -inf, sum 0, O = 0).  A
-// thread owns 4 dims; it loads the states of 16 splits at a time, all
-// loads in flight together (indices past the last split re-read the last
-// one with weight 0), then folds them into a running (max, sum, O).
+// thread owns 4 dims; it loads the states of up to 16 splits at a time,
+// all loads in flight together (slots past the last split are not read:
+// re-reading the last split there cost the 4 x 2^20 decode step 4 %), then
+// folds them into a running (max, sum, O).
 constexpr int AT_MAX_SPLITS = 64;
 constexpr int AT_MERGE_BATCH = 16;
 
@@ -422,10 +423,15 @@ __global__ __launch_bounds__(128) void k_attend_combine(const float* __restrict_
     f32x4_t ov[AT_MERGE_BATCH];
 #pragma unroll
     for (int i = 0; i < AT_MERGE_BATCH; ++i) {
-      const int si = s0 + i < nsplit ? s0 + i : nsplit - 1;
-      const int64_t slot = slot0 + (int64_t)si * H_ATT;
-      ml[i] = *(const f32x2_t*)(part_ml + 2 * slot);
-      ov[i] = *(const f32x4_t*)(part_o + slot * D_LAT + d0);
+      const int64_t slot = slot0 + (int64_t)(s0 + i) * H_ATT;
+      ml[i] = f32x2_t{-INFINITY, 0.f};
+      ov[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      // only the splits that exist (no clamped re-reads of the last one);
+      // the partial rows with the nontemporal policy: each is read once
+      if (s0 + i < nsplit) {
+        ml[i] = *(const f32x2_t*)(part_ml + 2 * slot);
+        ov[i] = __builtin_nontemporal_load((const f32x4_t*)(part_o + slot * D_LAT + d0));
+      }
     }
     float bm = -INFINITY;
 #pragma unroll
