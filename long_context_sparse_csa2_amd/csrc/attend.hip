@@ -486,8 +486,11 @@ __global__ __launch_bounds__(128) void k_attend_combine(const float* __restrict_
 // MI355X than a kernel boundary).  SWA-chunk workgroups skip the selection.
 // 512 threads: the selection runs on all eight waves, the attention on the
 // first four (the other four end after the selection; a barrier waits only
-// for the waves that have not ended).
+// for the waves that have not ended).  A workgroup attends over cps
+// consecutive chunks (more than one when one chunk per workgroup would not
+// fit the device's CUs in one round).
 constexpr int SA_NT = 512;
+constexpr int SA_MAX_CPS = 8;                   // SA_MAX_CPS * 64 <= SA_NT
 
 template <int MODE>
 __global__ __launch_bounds__(SA_NT, 1) void k_select_attend(
@@ -500,20 +503,21 @@ __global__ __launch_bounds__(SA_NT, 1) void k_select_attend(
     const uint8_t* __restrict__ swa_codes, const float* __restrict__ swa_scale, int64_t T_swa,
     const int64_t* __restrict__ swa_start, const int32_t* __restrict__ swa_len,
     float* __restrict__ out, float* __restrict__ lse, float* __restrict__ part_o,
-    float* __restrict__ part_ml, int nsplit, int Q) {
+    float* __restrict__ part_ml, int nsplit, int cps, int Q) {
   __shared__ AttendLds L;
   __shared__ union alignas(16) SaOverlay {
     SelShared<SA_NT> sel;                       // main chunks: the selection state
     _Float16 kv1[CH_ROWS * KV_LD];              // SWA chunks: V of the SWA rows
   } U;
-  __shared__ int32_t cid[CH_ROWS];              // entries of this workgroup's 64 rows
+  __shared__ int32_t cid[SA_MAX_CPS * CH_ROWS];  // entries of this workgroup's rows
   int u, hg;
   unit_of(blockIdx.x, u, hg);
   if (u >= Q * nsplit) return;
   const int q = u / nsplit, sp = u % nsplit;
   const int tid = threadIdx.x;
   const int nmc = (k + CH_ROWS - 1) / CH_ROWS;
-  const bool main_ch = sp < nmc;                // uniform over the workgroup
+  const int row0 = sp * cps * CH_ROWS;          // first row of the workgroup's chunks
+  const bool main_ch = sp * cps < nmc;          // uniform over the workgroup
   // the query rows and scalars go out before the selection
   bf16x8_t x[4];
   if (tid < 256) attend_query_rows(x, qv, q, hg);
@@ -524,8 +528,8 @@ __global__ __launch_bounds__(SA_NT, 1) void k_select_attend(
         q, scores, ld, n_valid, col_ids, n_cols, d, lv, kk, MODE, MODE == 0 ? idx_out : pool,
         MODE == 0 ? (int64_t)kk : (int64_t)kk * 8, pool_len, MODE == 1 ? k : 0,
         MODE == 1 ? idx_out : nullptr, vec_out, spec, writer, U.sel);
-    if (tid < CH_ROWS) {
-      const int rr = sp * CH_ROWS + tid;
+    if (tid < cps * CH_ROWS) {
+      const int rr = row0 + tid;
       int32_t e = -1;
       if (rr < r.kept && rr < k) {
         const uint32_t c = r.identity ? (uint32_t)rr : r.list[rr];
@@ -538,8 +542,8 @@ __global__ __launch_bounds__(SA_NT, 1) void k_select_attend(
   if (tid >= 256) return;                       // whole waves: the attention uses waves 0-3
   const int id0 = main_ch ? cid[tid & 63] : -1;
   const RopeArgs none = {nullptr, 0, 0.f, nullptr, {}};
-  attend_body(q, hg, sp, nsplit, 1,
-              [&](int r) __attribute__((always_inline)) { return cid[r - sp * CH_ROWS]; }, id0, x,
+  attend_body(q, hg, sp, nsplit, cps,
+              [&](int r) __attribute__((always_inline)) { return cid[r - row0]; }, id0, x,
               aq, kv_codes, kv_scales, cap, k, swa_codes, swa_scale, T_swa, out, lse, part_o,
               part_ml, none, L, U.kv1);
 }
@@ -640,13 +644,17 @@ hipError_t launch_select_attend(const float* scores, int64_t ld, int Q, const in
                                 hipStream_t stream, bool levels_ready) {
   const LevelDesc d = select_levels(Q, n_cols, mode);
   uint32_t* lv = (uint32_t*)ws;
-  const int nsplit = sa_splits(k);
+  const int nch = sa_splits(k);                 // one split per chunk at most
   char* part = (char*)ws + align256(select_ws_bytes(Q, n_cols, mode));
   float* part_o = (float*)part;
-  float* part_ml = part_o + (size_t)Q * nsplit * H_ATT * D_LAT;
   // The fused kernel pays for repeating the selection in every workgroup
-  // only while its workgroups fit on the device at once (one per CU); past
-  // that, the separate kernels (same results) are faster.
+  // only while its workgroups fit on the device at once (one per CU): each
+  // takes the fewest consecutive chunks that make them fit; past
+  // SA_MAX_CPS chunks the separate kernels (same results) are faster.
+  int cps = 1;
+  while (cps < SA_MAX_CPS && unit_grid(Q * ((nch + cps - 1) / cps)) > (unsigned)device_cus()) ++cps;
+  const int nsplit = (nch + cps - 1) / cps;
+  float* part_ml = part_o + (size_t)Q * nsplit * H_ATT * D_LAT;
   if (unit_grid(Q * nsplit) > (unsigned)device_cus()) {
     hipError_t e = launch_select(scores, ld, Q, n_valid, col_ids, n_cols, kk, mode,
                                  mode == 0 ? idx_out : pool, mode == 0 ? kk : (int64_t)kk * 8,
@@ -655,7 +663,7 @@ hipError_t launch_select_attend(const float* scores, int64_t ld, int Q, const in
     if (e != hipSuccess) return e;
     const RopeArgs none = {nullptr, 0, 0.f, nullptr, {}};
     return launch_attend(q, q_seq, Q, kv_codes, kv_scales, cap, idx_out, k, swa_codes, swa_scale,
-                         T_swa, swa_start, swa_len, out, lse, part, attend_ws_for(Q, nsplit),
+                         T_swa, swa_start, swa_len, out, lse, part, attend_ws_for(Q, nch),
                          none, stream);
   }
   if (!levels_ready) {
@@ -668,12 +676,12 @@ hipError_t launch_select_attend(const float* scores, int64_t ld, int Q, const in
     hipLaunchKernelGGL(k_select_attend<0>, dim3(unit_grid(Q * nsplit)), dim3(SA_NT), 0, stream,
                        scores, ld, n_valid, col_ids, n_cols, d, (const uint32_t*)lv, kk, k, idx_out,
                        pool, pool_len, vec_out, spec, q, q_seq, kv_codes, kv_scales, cap, swa_codes,
-                       swa_scale, T_swa, swa_start, swa_len, out, lse, part_o, part_ml, nsplit, Q);
+                       swa_scale, T_swa, swa_start, swa_len, out, lse, part_o, part_ml, nsplit, cps, Q);
   else
     hipLaunchKernelGGL(k_select_attend<1>, dim3(unit_grid(Q * nsplit)), dim3(SA_NT), 0, stream,
                        scores, ld, n_valid, col_ids, n_cols, d, (const uint32_t*)lv, kk, k, idx_out,
                        pool, pool_len, vec_out, spec, q, q_seq, kv_codes, kv_scales, cap, swa_codes,
-                       swa_scale, T_swa, swa_start, swa_len, out, lse, part_o, part_ml, nsplit, Q);
+                       swa_scale, T_swa, swa_start, swa_len, out, lse, part_o, part_ml, nsplit, cps, Q);
   const RopeArgs none = {nullptr, 0, 0.f, nullptr, {}};
   hipLaunchKernelGGL(k_attend_combine, dim3((unsigned)(Q * H_ATT)), dim3(128), 0, stream,
                      (const float*)part_o, (const float*)part_ml, nsplit, out, lse, none);

@@ -57,8 +57,12 @@ def _check_rows(c, i, idx_row, o, l):
 
 @pytest.mark.parametrize("Q,n_cols,k,pool_ids", [(4, 16384, 512, True), (3, 16384, 512, False),
                                                  (5, 3000, 100, True), (2, 65536, 512, False),
-                                                 (7, 700, 512, False), (1, 20000, 2048, True)])
+                                                 (7, 700, 512, False), (1, 20000, 2048, True),
+                                                 (11, 3000, 300, True), (24, 4096, 512, False)])
 def test_select_attend_topk(Q, n_cols, k, pool_ids):
+    """One chunk per workgroup while the workgroups fit the CUs; Q = 7, 11
+    and 24 take 2, 2 and 5 consecutive chunks per workgroup (11 and 24 with
+    a workgroup whose chunks are main rows followed by SWA rows)."""
     c = _case(Q, max(4096, n_cols + 100), n_cols, seed=Q * 7 + k, pool_ids=pool_ids)
     nv = torch.tensor([n_cols - 3 * i for i in range(Q)], dtype=torch.int64)
     nv[-1] = min(n_cols, 300) if Q > 1 else nv[-1]          # fewer valid columns than k
