@@ -50,16 +50,18 @@ namespace csa2 {
 constexpr int SC_WAVES = 4;
 // Two-query prefill scan (k_index_score_pair): used for launches of at
 // least SC_PAIR_MIN_Q queries, 32 tiles per wave, one tile's bytes in
-// flight; bf16 queries over more than SC_PAIR_MIN_COLS columns, MXFP4
-// queries over any.  Measured on MI355X against the one-query scan:
-// 65,536-token prefill chunk scans 4.02 -> 3.81 ms per group (MXFP4 query
-// 2.71 -> 2.13 ms), 1,048,576-token 1.175 -> 1.038 s; at 4,096 columns (one
-// chunk of 4,096 queries) 76 -> 79 us with bf16 queries, so their short rows
-// keep the one-query scan, and 60 -> 54 us with MXFP4 queries; two tiles in
-// flight or 16 tiles per wave ran 2-10 % slower, and the MXFP4 variant
-// spills at three or four waves per SIMD.
+// flight.  Measured on MI355X against the one-query scan, at two waves per
+// SIMD: 65,536-token prefill chunk scans 4.02 -> 3.81 ms per group (MXFP4
+// query 2.71 -> 2.13 ms), 1,048,576-token 1.175 -> 1.038 s; at 4,096
+// columns (one chunk of 4,096 queries) 76 -> 79 us with bf16 queries, which
+// then kept the one-query scan, and 60 -> 54 us with MXFP4 queries; two tiles in
+// flight or 16 tiles per wave ran 2-10 % slower.  Three waves per SIMD
+// (tile offsets added where they are used, head weights in LDS: 145 and 116
+// registers instead of 256 with spills) then took the 1,048,576-token chunk
+// scans 1.04 -> 0.96 s, the 65,536-token ones 3.84 -> 3.72 ms and the
+// 4,096-query MXFP4 scan 48.6 -> 45.3 us, and bf16 queries at 4,096
+// columns went to pairs as well (76 -> 71 us).
 constexpr int SC_PAIR_MIN_Q = 2048;
-constexpr int64_t SC_PAIR_MIN_COLS = 4096;
 constexpr int SC_PAIR_TPW = 32, SC_PAIR_DEPTH = 1;
 
 // Fourth word of a raw (unformatted, stride 0) buffer resource on gfx9:
@@ -419,8 +421,21 @@ __global__ __launch_bounds__(256, 4) void k_index_score(
 // query's stores stop at its own.  A pair on two sequences (or the last,
 // unpaired query) is scored one query at a time, the wave then scoring that
 // query for both of its slots (the same value stored twice).
+// A lane offset plus a wave-uniform tile offset, as one vector add issued
+// where the load or store that uses it is: left to itself the compiler
+// computes the offsets of all unrolled tiles up front and keeps them in
+// registers (about 80 of them at 32 tiles per wave), which limited this
+// kernel to two waves per SIMD.  The sum stays in the vector offset, which
+// the buffer range check covers (a uniform part passed as the scalar offset
+// would not be checked).
+__device__ __forceinline__ int tile_off(int lane_off, int uniform_off) {
+  int o;
+  asm volatile("v_add_u32 %0, %1, %2" : "=v"(o) : "v"(lane_off), "s"(uniform_off));
+  return o;
+}
+
 template <int TPW, int DEPTH, bool FP4Q>
-__global__ __launch_bounds__(256, 2) void k_index_score_pair(
+__global__ __launch_bounds__(256, 3) void k_index_score_pair(
     const uint16_t* __restrict__ q_idx, const float* __restrict__ w,
     const int32_t* __restrict__ q_seq, const int64_t* __restrict__ n_vis, int Q, int64_t nchunk,
     int64_t chunk_stride, int64_t tile_stride, int64_t n_cols,
@@ -448,7 +463,13 @@ __global__ __launch_bounds__(256, 2) void k_index_score_pair(
     bf16x8_t a0[FP4Q ? 1 : 8], a1[FP4Q ? 1 : 8];
     i32x8_t qa0[2] = {}, qa1[2] = {};           // MXFP4: the two queries' codes
     uint32_t qsc0 = 0, qsc1 = 0;
-    float w0[16], w1[16];
+    // the two queries' head weights, read from LDS in the epilogue (in
+    // registers they took 32 of the 168 a lane has at three waves per SIMD)
+    __shared__ __align__(16) float wl[2][H_IDX];
+    if (pass > 0) __syncthreads();                  // pass 0's weights read
+    if (threadIdx.x < 2 * H_IDX)
+      wl[threadIdx.x / H_IDX][threadIdx.x % H_IDX] =
+          w[(threadIdx.x < H_IDX ? qa : qb) * H_IDX + threadIdx.x % H_IDX];
     {
       if constexpr (FP4Q) {
         __shared__ QFp4Lds ql[2];
@@ -475,13 +496,8 @@ __global__ __launch_bounds__(256, 2) void k_index_score_pair(
           a1[s] = *(const bf16x8_t*)(pb + 8 * s);
         }
       }
-#pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        const int h = 8 * (j >> 2) + 4 * half + (j & 3);
-        w0[j] = w[qa * H_IDX + h];
-        w1[j] = w[qb * H_IDX + h];
-      }
     }
+    __syncthreads();
     const __amdgpu_buffer_rsrc_t sra = make_rsrc(scores + (int64_t)qa * ld, nva * 4);
     const __amdgpu_buffer_rsrc_t srb = make_rsrc(scores + (int64_t)qb * ld, nvb * 4);
     const int64_t vis_wg = nv - cbase;
@@ -495,10 +511,10 @@ __global__ __launch_bounds__(256, 2) void k_index_score_pair(
     const int64_t col_first = cbase + (int64_t)wave * 32;
     auto load = [&](int t, int sl) __attribute__((always_inline)) {
       const int d = (int)(col_first + (int64_t)t * step - cbase);   // < 2^25, as in the single scan
-      const int oc = code_off + d * 64;
+      const int oc = tile_off(code_off, d * 64), os = tile_off(scale_off, d * 4);
       r0[sl] = __builtin_amdgcn_raw_buffer_load_b128(rcodes, oc, 0, 0);
       r1[sl] = __builtin_amdgcn_raw_buffer_load_b128(rcodes, oc + 16, 0, 0);
-      rs[sl] = __builtin_amdgcn_raw_buffer_load_b16(rscales, scale_off + d * 4, 0, 0);
+      rs[sl] = __builtin_amdgcn_raw_buffer_load_b16(rscales, os, 0, 0);
     };
 #pragma unroll
     for (int t = 0; t < DEPTH; ++t)
@@ -532,13 +548,18 @@ __global__ __launch_bounds__(256, 2) void k_index_score_pair(
       }
       float pa = 0.f, pb = 0.f;
 #pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        pa += w0[j] * relu_f32(acc0[j]);
-        pb += w1[j] * relu_f32(acc1[j]);
+      for (int m = 0; m < 4; ++m) {
+        const f32x4_t wa = *(const f32x4_t*)&wl[0][8 * m + 4 * half];
+        const f32x4_t wb = *(const f32x4_t*)&wl[1][8 * m + 4 * half];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          pa += wa[i] * relu_f32(acc0[4 * m + i]);
+          pb += wb[i] * relu_f32(acc1[4 * m + i]);
+        }
       }
       pa = lanes_sum32(pa);
       pb = lanes_sum32(pb);
-      const int so = st_off + (int)(col_first + (int64_t)t * step) * 4;
+      const int so = tile_off(st_off, (int)(col_first + (int64_t)t * step) * 4);
       __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(pa), sra, so, 0, SC_ST_NT);
       __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(pb), srb, so, 0, SC_ST_NT);
     };
@@ -633,13 +654,13 @@ hipError_t launch_index_score(const uint16_t* q_idx, const float* w, const int32
                                          cand, ld_cand, nchunk, cs, ts, n_cols,       \
                                          ik_codes, ik_scales, cap, scores, ld, lvd, lv); \
     break;
-  // Long prefill rows with a bf16 query: two queries per wave share each
-  // key tile's conversion (same scores, bit for bit)
+  // Prefill chunks: two queries per wave share each key tile's conversion
+  // (bf16 query) or its loads (MXFP4 query); same scores, bit for bit
   const int64_t P = ((int64_t)Q + 1) / 2;
   constexpr int64_t pcols = (int64_t)SC_WAVES * SC_PAIR_TPW * 32;
   const int64_t pchunk = (n_cols + pcols - 1) / pcols;
   const bool pairs = !cand && !lv_scan && Q >= SC_PAIR_MIN_Q &&
-                     n_cols > (fp4q ? 0 : SC_PAIR_MIN_COLS) && P * pchunk >= 1024;
+                     n_cols > 0 && P * pchunk >= 1024;
   if (pairs) {
     const bool pinter = pchunk >= 128 && n_cols < ((int64_t)1 << 24);
     const int64_t pslice = (int64_t)SC_WAVES * 32;
