@@ -147,6 +147,19 @@ __device__ __forceinline__ void quant_query_fp4(const uint16_t* __restrict__ qro
 // c * chunk_stride (+ 32 per wave) and a wave's consecutive tiles are
 // tile_stride columns apart; with LV (+ 64 per wave) a wave's tiles 2p and
 // 2p + 1 are adjacent and its pairs tile_stride columns apart.
+// A lane offset plus a wave-uniform tile offset, as one vector add issued
+// where the load or store that uses it is: left to itself the compiler
+// computes the offsets of all unrolled tiles up front and keeps them in
+// registers (about 80 of them at 32 tiles per wave), which limited the
+// two-query scan below to two waves per SIMD.  The sum stays in the vector
+// offset, which the buffer range check covers (a uniform part passed as the
+// scalar offset would not be checked).
+__device__ __forceinline__ int tile_off(int lane_off, int uniform_off) {
+  int o;
+  asm volatile("v_add_u32 %0, %1, %2" : "=v"(o) : "v"(lane_off), "s"(uniform_off));
+  return o;
+}
+
 template <bool CAND, bool FP4Q, int TPW, int DEPTH, bool LV>
 __global__ __launch_bounds__(256, 4) void k_index_score(
     const uint16_t* __restrict__ q_idx, const float* __restrict__ w,
@@ -421,19 +434,6 @@ __global__ __launch_bounds__(256, 4) void k_index_score(
 // query's stores stop at its own.  A pair on two sequences (or the last,
 // unpaired query) is scored one query at a time, the wave then scoring that
 // query for both of its slots (the same value stored twice).
-// A lane offset plus a wave-uniform tile offset, as one vector add issued
-// where the load or store that uses it is: left to itself the compiler
-// computes the offsets of all unrolled tiles up front and keeps them in
-// registers (about 80 of them at 32 tiles per wave), which limited this
-// kernel to two waves per SIMD.  The sum stays in the vector offset, which
-// the buffer range check covers (a uniform part passed as the scalar offset
-// would not be checked).
-__device__ __forceinline__ int tile_off(int lane_off, int uniform_off) {
-  int o;
-  asm volatile("v_add_u32 %0, %1, %2" : "=v"(o) : "v"(lane_off), "s"(uniform_off));
-  return o;
-}
-
 template <int TPW, int DEPTH, bool FP4Q>
 __global__ __launch_bounds__(256, 3) void k_index_score_pair(
     const uint16_t* __restrict__ q_idx, const float* __restrict__ w,
