@@ -142,11 +142,6 @@ __device__ __forceinline__ void quant_query_fp4(const uint16_t* __restrict__ qro
   if (sub == 0) ((uint8_t*)&ql.scales[head])[g] = (uint8_t)(E + 127);
 }
 
-// TPW: 32-entry tiles per wave; DEPTH: tiles whose bytes are in flight ahead
-// of the one being multiplied.  Workgroup chunk c starts at column
-// c * chunk_stride (+ 32 per wave) and a wave's consecutive tiles are
-// tile_stride columns apart; with LV (+ 64 per wave) a wave's tiles 2p and
-// 2p + 1 are adjacent and its pairs tile_stride columns apart.
 // A lane offset plus a wave-uniform tile offset, as one vector add issued
 // where the load or store that uses it is: left to itself the compiler
 // computes the offsets of all unrolled tiles up front and keeps them in
@@ -160,6 +155,11 @@ __device__ __forceinline__ int tile_off(int lane_off, int uniform_off) {
   return o;
 }
 
+// TPW: 32-entry tiles per wave; DEPTH: tiles whose bytes are in flight ahead
+// of the one being multiplied.  Workgroup chunk c starts at column
+// c * chunk_stride (+ 32 per wave) and a wave's consecutive tiles are
+// tile_stride columns apart; with LV (+ 64 per wave) a wave's tiles 2p and
+// 2p + 1 are adjacent and its pairs tile_stride columns apart.
 template <bool CAND, bool FP4Q, int TPW, int DEPTH, bool LV>
 __global__ __launch_bounds__(256, 4) void k_index_score(
     const uint16_t* __restrict__ q_idx, const float* __restrict__ w,
