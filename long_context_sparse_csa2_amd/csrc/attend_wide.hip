@@ -57,7 +57,8 @@ __global__ __launch_bounds__(AW_THREADS, 2) void k_attend_wide(
   __shared__ f32x2_t rcs[ROPE_MAX_PAIRS];                          // RoPE (cos, sin) per pair
 
   const int q = gridDim.x - 1 - blockIdx.x;        // last queries (most rows when causal) first
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);      // uniform: scalar registers
   const int r16 = lane & 15, qd = lane >> 4;
   const int head = 16 * wave + r16;                      // S^T and softmax: this lane's head
   const int64_t seq = q_seq[q];
@@ -68,7 +69,7 @@ __global__ __launch_bounds__(AW_THREADS, 2) void k_attend_wide(
   const int sl = sl64 < 0 ? 0 : (sl64 > AW_MAX_SWA ? AW_MAX_SWA : (int)sl64);
   const int nmc = (k + CH_ROWS - 1) / CH_ROWS;
   const int nch = nmc + (sl + CH_ROWS - 1) / CH_ROWS;
-  const int srow = tid & 63, spart = tid >> 6;          // this thread's staging share
+  const int srow = tid & 63, spart = wave;              // this thread's staging share
 
   // selected entry of this thread's row in chunk ch (main chunks; -1 = none)
   auto entry_of = [&](int ch) __attribute__((always_inline)) {
