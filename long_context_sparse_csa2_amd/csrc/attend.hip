@@ -123,7 +123,8 @@ __device__ __forceinline__ void attend_body(
   auto& qinv = L.qinv;
   auto& rcs = L.rcs;
   auto& qs_lo = L.qs_lo;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);      // uniform: scalar registers
   const int r16 = lane & 15, qd = lane >> 4;
   const int nmc = (k + CH_ROWS - 1) / CH_ROWS;
   const int ch_beg = sp * cps;
@@ -182,7 +183,7 @@ __device__ __forceinline__ void attend_body(
     __builtin_amdgcn_sched_barrier(0);
     if (ch_beg < ch_end) {
       noff = row_res(ch_beg, rq0, nsg);
-      load_share<256>(raw, ch_beg < nmc, readable(noff, ch_beg < nmc), tid >> 6, kv_codes, kv_scales,
+      load_share<256>(raw, ch_beg < nmc, readable(noff, ch_beg < nmc), wave, kv_codes, kv_scales,
                       swa_codes);
     }
     rope_table<256>(rp, q, rcs);                   // while the query bytes are in flight
@@ -237,11 +238,11 @@ __device__ __forceinline__ void attend_body(
       const int64_t off = noff;
       const float sg = nsg;
       if (tid < CH_ROWS) { rowoff[tid] = off; rowsig[tid] = sg; }
-      store_share<256>(raw, is_main, off >= 0, sg, kv0, kv1, tid & 63, tid >> 6);
+      store_share<256>(raw, is_main, off >= 0, sg, kv0, kv1, tid & 63, wave);
       if (more) {
         const bool nmain = ch + 1 < nmc;
         noff = row_res(ch + 1, rqn, nsg);
-        load_share<256>(raw, nmain, readable(noff, nmain), tid >> 6, kv_codes, kv_scales,
+        load_share<256>(raw, nmain, readable(noff, nmain), wave, kv_codes, kv_scales,
                         swa_codes);
       }
     }
