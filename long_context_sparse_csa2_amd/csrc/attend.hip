@@ -480,16 +480,16 @@ __global__ __launch_bounds__(128) void k_attend_combine(const float* __restrict_
 // Selection and attention in one kernel (decode): every main-chunk
 // workgroup of a query runs the query's whole selection itself (the
 // selection is deterministic, so they all agree), keeps the entries of its
-// own 64 rows, and attends over them at once; the workgroup of head group 0
-// and split 0 also writes the selection out.  This removes the kernel
-// boundary and the round trip of the ids through memory between the two
-// steps (cross-workgroup hand-offs inside a kernel measured slower on
-// MI355X than a kernel boundary).  SWA-chunk workgroups skip the selection.
-// 512 threads: the selection runs on all eight waves, the attention on the
-// first four (the other four end after the selection; a barrier waits only
-// for the waves that have not ended).  A workgroup attends over cps
-// consecutive chunks (more than one when one chunk per workgroup would not
-// fit the device's CUs in one round).
+// own rows (cps consecutive 64-row chunks: more than one when one chunk per
+// workgroup would not fit the device's CUs in one round) and attends over
+// them; the workgroup of head group 0 and split 0 also writes the selection
+// out.  This removes the kernel boundary and the round trip of the ids
+// through memory between the two steps (cross-workgroup hand-offs inside a
+// kernel measured slower on MI355X than a kernel boundary).  Workgroups
+// whose chunks are all SWA chunks skip the selection.  512 threads: the
+// selection runs on all eight waves, the attention on the first four (the
+// other four end after the selection; a barrier waits only for the waves
+// that have not ended).
 constexpr int SA_NT = 512;
 constexpr int SA_MAX_CPS = 8;                   // SA_MAX_CPS * 64 <= SA_NT
 
