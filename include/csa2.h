@@ -325,7 +325,9 @@ csa2_status csa2_sparse_attend(const uint16_t* q, const int32_t* q_seq, int Q, c
  *
  * Outputs are those of the separate calls on the same inputs: idx (and
  * pool, pool_len) exactly as csa2_select_topk / csa2_block_pool write them,
- * out and lse as csa2_sparse_attend computes them over idx.
+ * out and lse the attention csa2_sparse_attend computes over idx (its rows
+ * may be split over workgroups differently, so the fp32 rounding of the
+ * merge can differ).
  *
  *   scores, ld, Q, n_valid, n_cols   as for csa2_select_topk; Q < 256
  *   col_ids    as for csa2_select_topk; must be NULL when n_blocks > 0
