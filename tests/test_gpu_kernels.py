@@ -388,15 +388,16 @@ def test_index_score_many_queries():
         assert np.array_equal(checks.host(part).view(np.uint32), s[lo:hi].view(np.uint32))
 
 
-@pytest.mark.parametrize("fp4q", [False, True])
-def test_index_score_query_pairs(fp4q):
-    """A 2049-query prefill launch over 40,000 entries (the scan scores two
-    queries per wave, sharing each key tile's conversion or loads) against
-    the same queries in launches of 512 (one query per wave): the same score
-    bits.  Pairs across a sequence boundary, the last unpaired query, rows of
+@pytest.mark.parametrize("fp4q,T", [(False, 40000), (True, 40000), (False, 3000), (True, 3000)])
+def test_index_score_query_pairs(fp4q, T):
+    """A 2049-query prefill launch over T entries (the scan scores two
+    queries per wave, sharing each key tile's conversion or loads; 3000
+    entries is one workgroup per pair, short causal rows) against the same
+    queries in launches of 512 (one query per wave): the same score bits.
+    Pairs across a sequence boundary, the last unpaired query, rows of
     different lengths within a pair and empty rows included; sampled rows
     against the oracle."""
-    B, T, Q = 2, 40000, 2049
+    B, Q = 2, 2049
     _, _, _, cache = _build(B, T, 1, seed=31)
     q, w = _scores_inputs(Q, 32)
     q_seq = np.ones(Q, np.int32)
