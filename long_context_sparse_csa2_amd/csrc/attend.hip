@@ -491,7 +491,8 @@ __global__ __launch_bounds__(128) void k_attend_combine(const float* __restrict_
 // other four end after the selection; a barrier waits only for the waves
 // that have not ended).
 constexpr int SA_NT = 512;
-constexpr int SA_MAX_CPS = 8;                   // SA_MAX_CPS * 64 <= SA_NT
+constexpr int SA_MAX_CPS = 8;                   // a thread per row id of the workgroup's chunks
+static_assert(SA_MAX_CPS * CH_ROWS <= SA_NT, "one thread per kept row id");
 
 template <int MODE>
 __global__ __launch_bounds__(SA_NT, 1) void k_select_attend(
